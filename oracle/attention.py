@@ -1,0 +1,293 @@
+"""fp64 CPU oracle for the fused attention forward.
+
+TEST INFRASTRUCTURE. Only the tests, the package's smoke check and the bench's
+CPU-baseline leg may import this module. It shares no code with the HIP path:
+it is the plain definition written out, slow and explicit, so that a reader can
+check it against the pages by eye.
+
+What it computes, and the passage each part follows:
+
+* The attention forward returns the output together with the per-row
+  log-sum-exp (pith-train page, "Issues resolved" item 1: FA4's forward returns
+  ``(out, lse)``).
+* GQA/MQA: the K/V heads are expanded by ``repeat_kv`` with kv-major heads,
+  ``y[b, kv*n_rep + rep] = x[b, kv]`` (ArcFlash page, "What rung 0 does"). The
+  oracle performs that expansion as an explicit copy.
+* Sinks: a per-head constant that enters each row's softmax denominator and
+  nothing else (ArcFlash page, "What rung 0 does", last paragraph; the "sink
+  dropped from the softmax denominator" mutation under "Mutations").
+* Query-row tiling under a byte budget is exact because each output row is an
+  independent softmax (ArcFlash page, "What rung 0 does").
+* MLA asymmetric head dims: q and k carry d_qk, v carries d_v (pith-train page,
+  "Issues resolved" item 2: the no-rope/rope concatenation is done by the
+  caller and fed to the attention directly).
+* Sparse top-k: each query attends only to the rows of one shared KV pool that
+  its index list names (TensorRT-LLM page, "Description": 13312 queries x 64
+  heads x 2176 top-k rows, d_qk 512).
+
+Readings where the pages are silent (each one stated again where it is used):
+
+* The sink is a logit in the scaled-score space: it is not multiplied by
+  ``scale``.
+* ``lse`` is the natural log of the full denominator, so it includes the sink
+  term when sinks are given.
+* Causal masks are bottom-right aligned: key j is visible to query t iff
+  ``j <= t + (Tk - Tq)``.
+* A row with no visible key has O = 0 and lse = -inf (lse = sink with a sink).
+* Sparse: ``V = kv[:, :d_v]`` of the one pool (V == K when d_v == d_qk); an
+  index outside [0, N) is skipped; duplicates count with multiplicity.
+
+Every function here is pinned by tests against brute force, closed forms,
+library routines and invariants. Two conventions are readings that the pages
+do not fix at all: the sink term inside lse, and the skipped out-of-range
+sparse index. Their closed-form tests pin the code to the stated reading, not
+to the pages, so those two conventions are "parity unpinned" as far as the
+pages go; the configurations exercise neither of them except the sink in lse.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast to fp64 (bf16 and fp32 values are representable)."""
+    if hasattr(x, "detach"):  # a torch tensor
+        x = x.detach().to("cpu")
+        import torch
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def repeat_kv(x: np.ndarray, n_rep: int) -> np.ndarray:
+    """Explicit GQA expansion with kv-major heads: ``y[b, kv*n_rep + rep] = x[b, kv]``.
+
+    ArcFlash page, "What rung 0 does" (the repeat_kv mapping). This is the copy
+    that the fused path avoids; the oracle performs it on purpose.
+    """
+    B, Hkv, T, D = x.shape
+    y = np.empty((B, Hkv * n_rep, T, D), dtype=x.dtype)
+    for kv in range(Hkv):
+        for rep in range(n_rep):
+            y[:, kv * n_rep + rep] = x[:, kv]
+    return y
+
+
+def causal_visible(t: int, j: int, Tq: int, Tk: int) -> bool:
+    """Bottom-right aligned causal mask: key j visible to query row t."""
+    return j <= t + (Tk - Tq)
+
+
+def _causal_mask(ts, Tq: int, Tk: int) -> np.ndarray:
+    """Boolean [len(ts), Tk]: True where key j is visible to query token t."""
+    j = np.arange(Tk)[None, :]
+    t = np.asarray(ts)[:, None]
+    return j <= t + (Tk - Tq)
+
+
+def _tile_row_token(f: np.ndarray, f0: int, Tq: int) -> np.ndarray:
+    """Token index of folded rows ``f`` (a tile starting at folded row ``f0``).
+
+    The token depends on the folded row alone, never on where the tile starts:
+    "the mask follows the tile" (ArcFlash page, "Mutations").
+    """
+    return f % Tq
+
+
+def _value_rows(G: np.ndarray, d_v: int) -> np.ndarray:
+    """V rows of gathered pool rows: the first d_v columns (V == K when d_v == d_qk)."""
+    return G[:, :d_v]
+
+
+def _softmax_rows(S: np.ndarray, sink: Optional[float]) -> Tuple[np.ndarray, np.ndarray]:
+    """Row softmax of an explicit score matrix ``S`` [R, n] (masked entries = -inf).
+
+    Returns the probabilities P [R, n] and lse [R]. With a sink s, the row
+    denominator gains exp(s) and nothing else does (ArcFlash page, sinks).
+    """
+    R = S.shape[0]
+    m = S.max(axis=1) if S.shape[1] > 0 else np.full(R, NEG_INF)
+    if sink is not None:
+        m = np.maximum(m, sink)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    E = np.exp(S - m_safe[:, None])          # exp(-inf) = 0 for masked keys
+    denom = E.sum(axis=1)
+    if sink is not None:
+        denom = denom + np.exp(sink - m_safe)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        P = np.where(denom[:, None] > 0, E / np.where(denom > 0, denom, 1.0)[:, None], 0.0)
+        lse = np.where(denom > 0, m_safe + np.log(np.where(denom > 0, denom, 1.0)), NEG_INF)
+    return P, lse
+
+
+def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
+                    rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Dense attention forward in fp64.
+
+    q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v], sinks [H] or None.
+    Returns (out [B,H,Tq,d_v], lse [B,H,Tq]) -- or, when ``rows`` lists
+    (b, h, t) triples, (out [n, d_v], lse [n]) for those rows only.
+
+    Steps (explicit, in the order of the definition):
+      1. K, V expanded to H heads by repeat_kv (kv-major).
+      2. S = scale * q . K^T, an explicit [Tq, Tk] score matrix per (b, h).
+      3. Causal: S[t, j] = -inf where j > t + (Tk - Tq).
+      4. Row softmax with the sink (if any) added to the denominator only.
+      5. O = P . V;  lse = m + ln(denominator).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Tq, Dqk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    Dv = v.shape[-1]
+    assert H % Hkv == 0, "H must be a multiple of Hkv"
+    g = H // Hkv
+    K = repeat_kv(k, g)
+    V = repeat_kv(v, g)
+    sk = None if sinks is None else _f64(sinks)
+
+    def head(b, h, ts):
+        S = scale * (q[b, h, ts] @ K[b, h].T)
+        if causal:
+            S = np.where(_causal_mask(ts, Tq, Tk), S, NEG_INF)
+        P, lse = _softmax_rows(S, None if sk is None else float(sk[h]))
+        return P @ V[b, h], lse
+
+    if rows is None:
+        out = np.empty((B, H, Tq, Dv))
+        lse = np.empty((B, H, Tq))
+        all_t = np.arange(Tq)
+        for b in range(B):
+            for h in range(H):
+                out[b, h], lse[b, h] = head(b, h, all_t)
+        return out, lse
+
+    rows = list(rows)
+    out = np.empty((len(rows), Dv))
+    lse = np.empty(len(rows))
+    # group the requested rows by (b, h) so each head's scores are formed once
+    by_head = {}
+    for i, (b, h, t) in enumerate(rows):
+        by_head.setdefault((b, h), []).append((i, t))
+    for (b, h), lst in by_head.items():
+        ts = np.array([t for _, t in lst])
+        o, l = head(b, h, ts)
+        for r, (i, _) in enumerate(lst):
+            out[i], lse[i] = o[r], l[r]
+    return out, lse
+
+
+def tile_rows_for_budget(tile_bytes: int, Tk: int, elt_bytes: int) -> int:
+    """Folded query rows per tile so that one tile's [rows, Tk] scores fit the budget.
+
+    ArcFlash page, "What rung 0 does": the score matrix is bounded to one
+    query tile of ``tile_bytes`` (32 MiB by default).
+    """
+    return max(1, tile_bytes // (Tk * elt_bytes))
+
+
+def dense_attention_tiled(q, k, v, *, scale: float, causal: bool, sinks=None,
+                          tile_bytes: int = 32 << 20):
+    """The same forward computed over query-row tiles of the folded view.
+
+    GQA fold: q [B,H,Tq,D] is viewed as [B,Hkv,g*Tq,D] (kv-major heads, so a
+    contiguous reshape, ArcFlash page "What rung 0 does"); folded row f of kv
+    head ``kv`` is head ``kv*g + f // Tq`` at token ``t = f % Tq``. Tiles of
+    ``tile_rows`` folded rows may straddle heads; each row's causal bound uses
+    its own ``t`` ("the mask follows the tile") and its own head's sink.
+    K and V are used per kv head, without expansion. fp64 scores are 8 bytes.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Tq, Dqk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    Dv = v.shape[-1]
+    g = H // Hkv
+    qf = q.reshape(B, Hkv, g * Tq, Dqk)       # the fold: a view, no copy
+    sk = None if sinks is None else _f64(sinks)
+    rows_per_tile = tile_rows_for_budget(tile_bytes, Tk, 8)
+    out = np.empty((B, Hkv, g * Tq, Dv))
+    lse = np.empty((B, Hkv, g * Tq))
+    for b in range(B):
+        for kv in range(Hkv):
+            for f0 in range(0, g * Tq, rows_per_tile):
+                f = np.arange(f0, min(f0 + rows_per_tile, g * Tq))
+                t = _tile_row_token(f, f0, Tq)
+                h = kv * g + f // Tq
+                S = scale * (qf[b, kv, f] @ k[b, kv].T)
+                if causal:
+                    S = np.where(_causal_mask(t, Tq, Tk), S, NEG_INF)
+                # rows of one tile can belong to different heads: softmax per head
+                P = np.empty_like(S)
+                L = np.empty(len(f))
+                for hh in np.unique(h):
+                    sel = h == hh
+                    P[sel], L[sel] = _softmax_rows(S[sel], None if sk is None else float(sk[hh]))
+                out[b, kv, f] = P @ v[b, kv]
+                lse[b, kv, f] = L
+    return out.reshape(B, H, Tq, Dv), lse.reshape(B, H, Tq)
+
+
+def gather_rows(pool: np.ndarray, idx: Sequence[int]) -> np.ndarray:
+    """Explicit gather ``pool[idx]`` that skips indices outside [0, N)."""
+    N = pool.shape[0]
+    keep = [int(i) for i in idx if 0 <= int(i) < N]
+    return pool[np.asarray(keep, dtype=np.int64)] if keep else pool[:0]
+
+
+def sparse_topk_attention(q, kv, idx, *, d_v: int, scale: float, sinks=None,
+                          queries: Optional[Iterable[int]] = None):
+    """Sparse top-k forward in fp64.
+
+    q [Sq,Hq,d_qk], kv [N,d_qk] (one shared pool), idx [Sq,topk] integer.
+    V is the first d_v columns of the same pool (V == K when d_v == d_qk).
+    For query s: G = kv[idx[s]] (explicit gather), S = scale * q[s] . G^T
+    ([Hq, topk], no mask), row softmax (sink in the denominator only),
+    O = P . G[:, :d_v]. Returns (out [Sq,Hq,d_v], lse [Sq,Hq]) or, with
+    ``queries``, (out [n,Hq,d_v], lse [n,Hq]) for those queries.
+    """
+    q, kv = _f64(q), _f64(kv)
+    idx = np.asarray(idx.numpy() if hasattr(idx, "numpy") else idx)
+    Sq, Hq, Dqk = q.shape
+    sk = None if sinks is None else _f64(sinks)
+    qs = list(range(Sq)) if queries is None else list(queries)
+    out = np.empty((len(qs), Hq, d_v))
+    lse = np.empty((len(qs), Hq))
+    for i, s in enumerate(qs):
+        G = gather_rows(kv, idx[s])
+        S = scale * (q[s] @ G.T)                      # [Hq, n]
+        Vg = _value_rows(G, d_v)
+        for h in range(Hq):
+            P, L = _softmax_rows(S[h:h + 1], None if sk is None else float(sk[h]))
+            out[i, h] = P[0] @ Vg
+            lse[i, h] = L[0]
+    return out, lse
+
+
+def merge_partials(parts, sink: Optional[float] = None):
+    """Merge (O_i, lse_i) computed over disjoint key sets into the full result.
+
+    lse = log(sum_i exp(lse_i) [+ exp(sink)]), O = sum_i exp(lse_i - lse) O_i.
+    Each part must have been computed without the sink. This is the output
+    merge of context-parallel attention (TransformerEngine page, flowchart:
+    "ring communication and output merge"), done on one device.
+    """
+    lses = np.stack([p[1] for p in parts])            # [n, R]
+    terms = list(lses)
+    if sink is not None:
+        terms.append(np.full_like(lses[0], sink))
+    allt = np.stack(terms)
+    m = allt.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    tot = np.exp(allt - m_safe).sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), NEG_INF)
+    lse_safe = np.where(np.isfinite(lse), lse, 0.0)
+    out = np.zeros_like(parts[0][0])
+    for o, l in parts:
+        w = np.where(np.isfinite(l), np.exp(l - lse_safe), 0.0)
+        out = out + w[..., None] * o
+    return out, lse

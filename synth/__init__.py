@@ -1,0 +1,168 @@
+"""Seeded synthetic workloads for the attention forward.
+
+This module only draws random numbers and fixes shapes. It holds none of the
+attention arithmetic, so both the fp64 oracle (through the tests) and the HIP
+path (through the binding) can take their inputs from here without sharing any
+part of the computation.
+
+The five workloads restate the shapes that the pages measure or discuss:
+
+* ``tiny``   -- dense causal GQA, B=1 H=4 Hkv=1 T=128 d=64, fp32 inputs.
+* ``gqa``    -- dense causal GQA prefill, B=2 H=32 Hkv=8 T=4096 d=128, bf16.
+* ``mla``    -- MLA-shaped causal prefill (DeepSeek-V2-Lite-like, the q/k
+  concatenation of a 128-wide no-rope part and a 64-wide rope part that the
+  pith-train page, "Issues resolved" item 2, moves into the model), B=4 H=16
+  Hkv=16 T=4096 d_qk=192 d_v=128, bf16.
+* ``mqa512`` -- MQA with d=512 and per-head attention sinks, the DeepSeek-V4
+  prefill layer shape of the ArcFlash page ("Numbers, labelled": B=1 H=64
+  D=512 T=1400), bf16, sinks fp32.
+* ``sparse`` -- sparse top-k MLA-style forward: 13312 queries x 64 heads x
+  2176 gathered rows with d_qk=512, the FlashMLA shape of the TensorRT-LLM
+  page ("Description"), over one shared pool of 65536 rows, bf16.
+
+Generation recipe (fixed so that every consumer sees identical bits):
+``torch.Generator('cpu').manual_seed(seed)`` with seed = workload number (1..5);
+draw order q, k, v, sinks, each ``torch.randn(shape, dtype=float32)``; cast to
+bf16 (round to nearest even) for the bf16 workloads. Sparse indices come from
+``numpy.random.default_rng(seed)``, one ``choice(N, topk, replace=False)`` per
+query, in query order, as int32 and unsorted.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class DenseSpec:
+    name: str
+    seed: int
+    B: int
+    H: int
+    Hkv: int
+    Tq: int
+    Tk: int
+    d_qk: int
+    d_v: int
+    dtype: str          # "bf16" or "f32"
+    causal: bool
+    sinks: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d_qk))
+
+    @property
+    def kind(self) -> str:
+        return "dense"
+
+
+
+@dataclasses.dataclass(frozen=True)
+class SparseSpec:
+    name: str
+    seed: int
+    Sq: int
+    Hq: int
+    N: int
+    d_qk: int
+    d_v: int
+    topk: int
+    sinks: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d_qk))
+
+    @property
+    def kind(self) -> str:
+        return "sparse"
+
+    @property
+    def dtype(self) -> str:
+        return "bf16"
+
+
+
+WORKLOADS = {
+    1: DenseSpec("tiny", 1, B=1, H=4, Hkv=1, Tq=128, Tk=128, d_qk=64, d_v=64,
+                 dtype="f32", causal=True, sinks=False),
+    2: DenseSpec("gqa", 2, B=2, H=32, Hkv=8, Tq=4096, Tk=4096, d_qk=128, d_v=128,
+                 dtype="bf16", causal=True, sinks=False),
+    3: DenseSpec("mla", 3, B=4, H=16, Hkv=16, Tq=4096, Tk=4096, d_qk=192, d_v=128,
+                 dtype="bf16", causal=True, sinks=False),
+    4: DenseSpec("mqa512", 4, B=1, H=64, Hkv=1, Tq=1400, Tk=1400, d_qk=512, d_v=512,
+                 dtype="bf16", causal=True, sinks=True),
+    5: SparseSpec("sparse", 5, Sq=13312, Hq=64, N=65536, d_qk=512, d_v=512, topk=2176),
+}
+
+
+def spec(n: int):
+    return WORKLOADS[n]
+
+
+def _torch_dtype(name: str):
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def make_dense(s: DenseSpec, *, seed: Optional[int] = None) -> dict:
+    """CPU tensors q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v], sinks [H] or None."""
+    g = torch.Generator("cpu").manual_seed(s.seed if seed is None else seed)
+    dt = _torch_dtype(s.dtype)
+    q = torch.randn((s.B, s.H, s.Tq, s.d_qk), generator=g, dtype=torch.float32).to(dt)
+    k = torch.randn((s.B, s.Hkv, s.Tk, s.d_qk), generator=g, dtype=torch.float32).to(dt)
+    v = torch.randn((s.B, s.Hkv, s.Tk, s.d_v), generator=g, dtype=torch.float32).to(dt)
+    sinks = None
+    if s.sinks:
+        sinks = torch.randn((s.H,), generator=g, dtype=torch.float32)
+    return {"q": q, "k": k, "v": v, "sinks": sinks}
+
+
+def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:
+    """[Sq, topk] int32, each row topk distinct values of [0, N), unsorted."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((Sq, topk), dtype=np.int32)
+    for s in range(Sq):
+        out[s] = rng.choice(N, topk, replace=False)
+    return out
+
+
+def make_sparse(s: SparseSpec, *, seed: Optional[int] = None) -> dict:
+    """CPU tensors q [Sq,Hq,d_qk], kv [N,d_qk] (V = kv[:, :d_v]), idx [Sq,topk] int32."""
+    sd = s.seed if seed is None else seed
+    g = torch.Generator("cpu").manual_seed(sd)
+    q = torch.randn((s.Sq, s.Hq, s.d_qk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    kv = torch.randn((s.N, s.d_qk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    sinks = None
+    if s.sinks:
+        sinks = torch.randn((s.Hq,), generator=g, dtype=torch.float32)
+    idx = torch.from_numpy(make_indices(s.Sq, s.N, s.topk, sd))
+    return {"q": q, "kv": kv, "idx": idx, "sinks": sinks}
+
+
+def make(n: int) -> dict:
+    s = spec(n)
+    return make_dense(s) if s.kind == "dense" else make_sparse(s)
+
+
+def sha256(t: torch.Tensor) -> str:
+    """Digest of a tensor's bytes, for reproducibility records."""
+    a = t.contiguous()
+    if a.dtype == torch.bfloat16:
+        a = a.view(torch.int16)
+    return hashlib.sha256(a.numpy().tobytes()).hexdigest()
+
+
+def randn_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype="bf16", sinks=False, seed=0):
+    """Ad-hoc dense inputs for sweeps and edge cases (same recipe, any shape)."""
+    s = DenseSpec("adhoc", seed, B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, True, sinks)
+    return make_dense(s)
+
+
+def randn_sparse(Sq, Hq, N, d_qk, topk, *, seed=0, sinks=False):
+    s = SparseSpec("adhoc", seed, Sq, Hq, N, d_qk, d_qk, topk, sinks)
+    return make_sparse(s)

@@ -1,0 +1,70 @@
+"""Brute-force attention in pure Python, for pinning the oracle on tiny inputs.
+
+Written independently of ``oracle/``: scores by explicit loops with
+``math.fsum``, the GQA head mapping as ``kv = h // g`` (no expansion), and the
+softmax in a different algebraic form -- the weight of key j is
+``1 / (sum_i exp(s_i - s_j) + exp(sink - s_j))`` -- with lse taken unshifted as
+``log(fsum(exp(s_i)) + exp(sink))`` (inputs are kept small so nothing
+overflows). Mask: key j visible to token t iff j <= t + (Tk - Tq).
+"""
+import math
+
+
+def _attend(scores, values, sink):
+    """scores: list of floats; values: list of rows. Returns (o, lse)."""
+    dv = len(values[0]) if values else 0
+    if not scores:
+        return None, (sink if sink is not None else -math.inf)
+    w = []
+    for sj in scores:
+        terms = [math.exp(si - sj) for si in scores]
+        if sink is not None:
+            terms.append(math.exp(sink - sj))
+        w.append(1.0 / math.fsum(terms))
+    o = [math.fsum(w[j] * values[j][d] for j in range(len(scores))) for d in range(dv)]
+    tot = [math.exp(si) for si in scores]
+    if sink is not None:
+        tot.append(math.exp(sink))
+    return o, math.log(math.fsum(tot))
+
+
+def brute_dense(q, k, v, scale, causal, sinks=None):
+    """q [B][H][Tq][Dqk], k [B][Hkv][Tk][Dqk], v [B][Hkv][Tk][Dv] (nested lists or arrays)."""
+    B, H, Tq, Dqk = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, Tk, Dv = len(k[0]), len(k[0][0]), len(v[0][0][0])
+    g = H // Hkv
+    out = [[[[0.0] * Dv for _ in range(Tq)] for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * Tq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            kvh = h // g
+            for t in range(Tq):
+                sc, vals = [], []
+                for j in range(Tk):
+                    if causal and j > t + (Tk - Tq):
+                        continue
+                    sc.append(scale * math.fsum(float(q[b][h][t][d]) * float(k[b][kvh][j][d])
+                                                for d in range(Dqk)))
+                    vals.append([float(x) for x in v[b][kvh][j]])
+                o, l = _attend(sc, vals, None if sinks is None else float(sinks[h]))
+                out[b][h][t] = o if o is not None else [0.0] * Dv
+                lse[b][h][t] = l
+    return out, lse
+
+
+def brute_sparse(q, kv, idx, d_v, scale, sinks=None):
+    """q [Sq][Hq][Dqk], kv [N][Dqk], idx [Sq][topk]; out-of-range indices skipped."""
+    Sq, Hq, Dqk = len(q), len(q[0]), len(q[0][0])
+    N = len(kv)
+    out = [[[0.0] * d_v for _ in range(Hq)] for _ in range(Sq)]
+    lse = [[0.0] * Hq for _ in range(Sq)]
+    for s in range(Sq):
+        rows = [int(i) for i in idx[s] if 0 <= int(i) < N]
+        for h in range(Hq):
+            sc = [scale * math.fsum(float(q[s][h][d]) * float(kv[r][d]) for d in range(Dqk))
+                  for r in rows]
+            vals = [[float(kv[r][d]) for d in range(d_v)] for r in rows]
+            o, l = _attend(sc, vals, None if sinks is None else float(sinks[h]))
+            out[s][h] = o if o is not None else [0.0] * d_v
+            lse[s][h] = l
+    return out, lse

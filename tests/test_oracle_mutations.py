@@ -1,0 +1,76 @@
+"""Planted mistakes in the oracle must each be caught by some pin.
+
+The four mutations of the ArcFlash page ("Mutations": rep-major heads, mask not
+following the tile, sink dropped from the denominator, and a disabled fast path
+-- the last one is covered by the dispatch-record tests of the library) plus
+causal switched off, scale applied twice, lse in base 2 and V taken from the
+wrong columns of the sparse pool. Mistakes are planted on the CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as OA
+from tests import pins
+
+
+def _caught(checks):
+    return {n: pins.ALL_CHECKS[n]() for n in checks}
+
+
+def _assert_caught(results):
+    assert any(v > pins.TOL for v in results.values()), f"mutation not caught: {results}"
+
+
+def test_rep_major_heads_caught(monkeypatch):
+    def rep_major(x, n_rep):
+        B, Hkv, T, D = x.shape
+        y = np.empty((B, Hkv * n_rep, T, D), dtype=x.dtype)
+        for kv in range(Hkv):
+            for rep in range(n_rep):
+                y[:, rep * Hkv + kv] = x[:, kv]
+        return y
+
+    monkeypatch.setattr(OA, "repeat_kv", rep_major)
+    _assert_caught(_caught(["fold_matches_repeat_kv", "brute_dense"]))
+
+
+def test_mask_not_following_tile_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_tile_row_token", lambda f, f0, Tq: (f - f0) % Tq)
+    _assert_caught(_caught(["tiling_exact"]))
+
+
+def test_sink_dropped_caught(monkeypatch):
+    orig = OA._softmax_rows
+    monkeypatch.setattr(OA, "_softmax_rows", lambda S, sink: orig(S, None))
+    _assert_caught(_caught(["closed_forms", "brute_dense", "lse_logsumexp"]))
+
+
+def test_causal_off_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_causal_mask", lambda ts, Tq, Tk: np.ones((len(ts), Tk), dtype=bool))
+    _assert_caught(_caught(["closed_forms", "causal_differs"]))
+
+
+def test_scale_twice_caught(monkeypatch):
+    orig = OA.dense_attention
+    monkeypatch.setattr(oracle, "dense_attention",
+                        lambda q, k, v, *, scale, **kw: orig(q, k, v, scale=scale * scale, **kw))
+    _assert_caught(_caught(["brute_dense", "library_dense"]))
+
+
+def test_lse_base2_caught(monkeypatch):
+    orig = OA.dense_attention
+
+    def log2_lse(*a, **kw):
+        o, l = orig(*a, **kw)
+        return o, l / math.log(2.0)
+
+    monkeypatch.setattr(oracle, "dense_attention", log2_lse)
+    _assert_caught(_caught(["library_dense", "lse_logsumexp"]))
+
+
+def test_sparse_value_columns_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_value_rows", lambda G, d_v: G[:, G.shape[1] - d_v:][:, ::-1])
+    _assert_caught(_caught(["brute_sparse", "sparse_equals_dense_mqa"]))
