@@ -1,0 +1,320 @@
+"""Python binding of the gfx950 fused attention forward (C ABI in include/attn_fwd.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn_fwd.so``. PyTorch supplies device memory and the stream.
+There is no CPU fallback; if the library is missing, importing the binding's
+entry points raises.
+
+    out, lse = dense(q, k, v, causal=True, scale=None, sinks=None)
+    out, lse = sparse_topk(q, kv, idx, d_v=512, scale=None, sinks=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
+
+ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
+ATTN_BF16, ATTN_F32 = 0, 1
+ABI_VERSION = 1
+
+
+class AttnDenseArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_st", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_sb", ctypes.c_int64), ("v_sh", ctypes.c_int64), ("v_st", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_st", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
+class AttnSparseArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Hq", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_ss", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("kv", ctypes.c_void_p), ("kv_sn", ctypes.c_int64),
+        ("indices", ctypes.c_void_p), ("idx_ss", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_ss", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
+class AttnPlan(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("path", ctypes.c_char * 64),
+        ("block_rows", ctypes.c_int32), ("block_keys", ctypes.c_int32), ("waves", ctypes.c_int32),
+        ("grid", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("fold_g", ctypes.c_int32),
+        ("folded_rows", ctypes.c_int64),
+        ("hbm_score_bytes", ctypes.c_int64),
+        ("budget_bytes", ctypes.c_int64),
+        ("score_elt_bytes", ctypes.c_int32),
+        ("budget_tile_rows", ctypes.c_int64),
+        ("budget_tiles", ctypes.c_int64),
+    ]
+
+
+EXPORTS = (
+    "attn_abi_version", "attn_fwd_dense", "attn_fwd_sparse_topk", "attn_plan_dense",
+    "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
+    "attn_reset_dispatch_counts", "attn_budget_tile_rows",
+)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn_fwd.so (built by attention_forward_attn_amd.build). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m attention_forward_attn_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    lib.attn_abi_version.restype = ctypes.c_int
+    lib.attn_fwd_dense.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_void_p]
+    lib.attn_fwd_dense.restype = ctypes.c_int
+    lib.attn_fwd_sparse_topk.argtypes = [ctypes.POINTER(AttnSparseArgs), ctypes.c_void_p]
+    lib.attn_fwd_sparse_topk.restype = ctypes.c_int
+    lib.attn_plan_dense.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.POINTER(AttnPlan)]
+    lib.attn_plan_dense.restype = ctypes.c_int
+    lib.attn_plan_sparse_topk.argtypes = [ctypes.POINTER(AttnSparseArgs), ctypes.POINTER(AttnPlan)]
+    lib.attn_plan_sparse_topk.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_dispatch_count.argtypes = [ctypes.c_char_p]
+    lib.attn_dispatch_count.restype = ctypes.c_uint64
+    lib.attn_reset_dispatch_counts.restype = None
+    lib.attn_budget_tile_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.attn_budget_tile_rows.restype = ctypes.c_int64
+    v = lib.attn_abi_version()
+    if v != ABI_VERSION:
+        raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class AttnInvalidArgument(AttnError, ValueError):
+    pass
+
+
+class AttnUnsupported(AttnError, NotImplementedError):
+    pass
+
+
+def _check(status: int):
+    if status == ATTN_OK:
+        return
+    lib = load_library()
+    msg = f"{lib.attn_status_string(status).decode()}: {lib.attn_last_error().decode()}"
+    if status == ATTN_INVALID_ARGUMENT:
+        raise AttnInvalidArgument(status, msg)
+    if status == ATTN_UNSUPPORTED:
+        raise AttnUnsupported(status, msg)
+    raise AttnError(status, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise AttnUnsupported(ATTN_UNSUPPORTED, f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None) -> AttnDenseArgs:
+    """Fill the C argument struct from tensors (BHSD or any strided view with unit last stride)."""
+    B, H, Tq, dqk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    dv = v.shape[-1]
+    a = AttnDenseArgs()
+    a.struct_size = ctypes.sizeof(AttnDenseArgs)
+    a.dtype = _dtype_code(q)
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, dqk, dv
+    a.causal = 1 if causal else 0
+    a.scale = float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    a.q, (a.q_sb, a.q_sh, a.q_st) = q.data_ptr(), q.stride()[:3]
+    a.k, (a.k_sb, a.k_sh, a.k_st) = k.data_ptr(), k.stride()[:3]
+    a.v, (a.v_sb, a.v_sh, a.v_st) = v.data_ptr(), v.stride()[:3]
+    a.out, (a.o_sb, a.o_sh, a.o_st) = out.data_ptr(), out.stride()[:3]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    return a
+
+
+def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
+          out=None, lse=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Fused dense attention forward on the GPU.
+
+    q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v] (bf16, or fp32 for the
+    split-bf16 path), sinks [H] fp32 or None. Returns (out [B,H,Tq,d_v] in the
+    input dtype, lse [B,H,Tq] fp32). Launches on ``stream`` (default: torch's
+    current stream) and does not synchronise.
+    """
+    import torch
+
+    lib = load_library()
+    B, H, Tq, dqk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
+    if not lse.is_contiguous():
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks)
+    _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+def sparse_args(q, kv, idx, out, lse, *, d_v: int, scale: float, sinks=None) -> AttnSparseArgs:
+    Sq, Hq, dqk = q.shape
+    N = kv.shape[0]
+    a = AttnSparseArgs()
+    a.struct_size = ctypes.sizeof(AttnSparseArgs)
+    a.dtype = _dtype_code(q)
+    a.Sq, a.Hq, a.N, a.d_qk, a.d_v, a.topk = Sq, Hq, N, dqk, d_v, idx.shape[1]
+    a.scale = float(scale)
+    for name, t in (("q", q), ("kv", kv), ("indices", idx), ("out", out)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    a.q, (a.q_ss, a.q_sh) = q.data_ptr(), q.stride()[:2]
+    a.kv, a.kv_sn = kv.data_ptr(), kv.stride(0)
+    a.indices, a.idx_ss = idx.data_ptr(), idx.stride(0)
+    a.out, (a.o_ss, a.o_sh) = out.data_ptr(), out.stride()[:2]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    return a
+
+
+def sparse_topk(q, kv, idx, *, d_v: Optional[int] = None, scale: Optional[float] = None, sinks=None,
+                out=None, lse=None, stream=None):
+    """Sparse top-k attention forward on the GPU.
+
+    q [Sq,Hq,d_qk] bf16, kv [N,d_qk] bf16 (one pool; values = kv[:, :d_v]),
+    idx [Sq,topk] int32 (entries outside [0, N) skipped). Returns
+    (out [Sq,Hq,d_v] bf16, lse [Sq,Hq] fp32).
+    """
+    import torch
+
+    lib = load_library()
+    Sq, Hq, dqk = q.shape
+    d_v = dqk if d_v is None else d_v
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if idx.dtype != torch.int32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "indices must be int32")
+    if out is None:
+        out = torch.empty((Sq, Hq, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((Sq, Hq), dtype=torch.float32, device=q.device)
+    a = sparse_args(q, kv, idx, out, lse, d_v=d_v, scale=scale, sinks=sinks)
+    _check(lib.attn_fwd_sparse_topk(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+_FAKE_PTR = 1 << 12  # never dereferenced: plans are computed on the host only
+
+
+def _plan_to_dict(p: AttnPlan) -> dict:
+    return {f: (getattr(p, f).decode() if f == "path" else getattr(p, f)) for f, _ in AttnPlan._fields_
+            if f != "struct_size"}
+
+
+def plan_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype: str = "bf16", causal: bool = True,
+               sinks: bool = False, scale: Optional[float] = None) -> dict:
+    """The launch plan for a contiguous BHSD problem of this shape (host only)."""
+    lib = load_library()
+    a = AttnDenseArgs()
+    a.struct_size = ctypes.sizeof(AttnDenseArgs)
+    a.dtype = ATTN_BF16 if dtype == "bf16" else ATTN_F32
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, d_qk, d_v
+    a.causal = 1 if causal else 0
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d_qk))
+    a.q, a.q_sb, a.q_sh, a.q_st = _FAKE_PTR, H * Tq * d_qk, Tq * d_qk, d_qk
+    a.k, a.k_sb, a.k_sh, a.k_st = _FAKE_PTR, Hkv * Tk * d_qk, Tk * d_qk, d_qk
+    a.v, a.v_sb, a.v_sh, a.v_st = _FAKE_PTR, Hkv * Tk * d_v, Tk * d_v, d_v
+    a.out, a.o_sb, a.o_sh, a.o_st = _FAKE_PTR, H * Tq * d_v, Tq * d_v, d_v
+    a.lse = _FAKE_PTR
+    a.sinks = _FAKE_PTR if sinks else None
+    p = AttnPlan()
+    p.struct_size = ctypes.sizeof(AttnPlan)
+    _check(lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p)))
+    return _plan_to_dict(p)
+
+
+def plan_sparse_topk(Sq, Hq, N, d_qk, d_v, topk, *, scale: Optional[float] = None) -> dict:
+    lib = load_library()
+    a = AttnSparseArgs()
+    a.struct_size = ctypes.sizeof(AttnSparseArgs)
+    a.dtype = ATTN_BF16
+    a.Sq, a.Hq, a.N, a.d_qk, a.d_v, a.topk = Sq, Hq, N, d_qk, d_v, topk
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d_qk))
+    a.q, a.q_ss, a.q_sh = _FAKE_PTR, Hq * d_qk, d_qk
+    a.kv, a.kv_sn = _FAKE_PTR, d_qk
+    a.indices, a.idx_ss = _FAKE_PTR, topk
+    a.out, a.o_ss, a.o_sh = _FAKE_PTR, Hq * d_v, d_v
+    a.lse = _FAKE_PTR
+    p = AttnPlan()
+    p.struct_size = ctypes.sizeof(AttnPlan)
+    _check(lib.attn_plan_sparse_topk(ctypes.byref(a), ctypes.byref(p)))
+    return _plan_to_dict(p)
+
+
+def dispatch_count(path: str) -> int:
+    return int(load_library().attn_dispatch_count(path.encode()))
+
+
+def reset_dispatch_counts() -> None:
+    load_library().attn_reset_dispatch_counts()
+
+
+def budget_tile_rows(budget_bytes: int, Tk: int, elt_bytes: int) -> int:
+    return int(load_library().attn_budget_tile_rows(budget_bytes, Tk, elt_bytes))
+
+
+def abi_version() -> int:
+    return int(load_library().attn_abi_version())

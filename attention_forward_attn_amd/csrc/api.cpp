@@ -1,0 +1,301 @@
+// Host side of the C ABI declared in include/attn_fwd.h: argument validation,
+// the planner (shape -> one kernel path, grid, tile order) and the dispatch
+// record. Nothing here allocates or synchronises device memory.
+//
+// The dispatch record follows the engagement idea of the ArcFlash pull
+// request (section "D18 -- engagement asserted, both directions"): every
+// launch of a kernel path increments that path's counter, so a test can show
+// that the path it meant to exercise really ran, and that a path it did not
+// exercise did not.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/attn_fwd.h"
+#include "attn_params.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr int kMaxPaths = 64;
+std::atomic<uint64_t> g_counts[kMaxPaths];
+std::atomic<int> g_logged[kMaxPaths];
+
+int path_index(const char* path) {
+  int n = 0;
+  const attn::KernelConfig* t = attn::kernel_table(&n);
+  for (int i = 0; i < n && i < kMaxPaths; ++i)
+    if (std::strcmp(t[i].path, path) == 0) return i;
+  return -1;
+}
+
+void note_dispatch(int i, const char* path) {
+  g_counts[i].fetch_add(1, std::memory_order_relaxed);
+  const char* env = std::getenv("ATTN_LOG_DISPATCH");
+  if (env && env[0] == '1' && g_logged[i].exchange(1) == 0)
+    std::fprintf(stderr, "attn_fwd: first dispatch on %s\n", path);
+}
+
+int64_t tile_budget_bytes() {
+  const char* env = std::getenv("ATTN_TILE_BYTES");
+  if (env && *env) {
+    char* end = nullptr;
+    long long v = std::strtoll(env, &end, 10);
+    if (end && *end == '\0' && v > 0) return (int64_t)v;
+  }
+  return (int64_t)32 << 20;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }  // NULL passes
+
+const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse) {
+  int n = 0;
+  const attn::KernelConfig* t = attn::kernel_table(&n);
+  for (int i = 0; i < n; ++i)
+    if (t[i].dtype == dtype && t[i].d_qk == d_qk && t[i].d_v == d_v && t[i].sparse == sparse) return &t[i];
+  return nullptr;
+}
+
+struct DensePlan {
+  const attn::KernelConfig* cfg;
+  attn::KernelParams kp;
+};
+
+attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_dense_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_dense_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_dense_args));
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F32) return fail(ATTN_UNSUPPORTED, "dtype %d unsupported", a->dtype);
+  if (a->B < 1 || a->H < 1 || a->Hkv < 1) return fail(ATTN_INVALID_ARGUMENT, "B, H, Hkv must be >= 1");
+  if (a->Tq < 0 || a->Tk < 0) return fail(ATTN_INVALID_ARGUMENT, "Tq, Tk must be >= 0");
+  if (a->H % a->Hkv != 0) return fail(ATTN_INVALID_ARGUMENT, "H (%d) must be a multiple of Hkv (%d)", a->H, a->Hkv);
+  if (a->d_qk < 1 || a->d_v < 1) return fail(ATTN_INVALID_ARGUMENT, "head dims must be >= 1");
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const attn::KernelConfig* cfg = find_config(a->dtype, a->d_qk, a->d_v, 0);
+  if (!cfg)
+    return fail(ATTN_UNSUPPORTED, "no compiled dense kernel for dtype %d with (d_qk, d_v) = (%d, %d)", a->dtype,
+                a->d_qk, a->d_v);
+  // empty operands (Tq == 0 or Tk == 0) may come with NULL pointers; they are never read
+  if (a->Tq > 0 && (!a->q || !a->out || !a->lse))
+    return fail(ATTN_INVALID_ARGUMENT, "q, out, lse must be non-NULL when Tq > 0");
+  if (a->Tk > 0 && (!a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "k, v must be non-NULL when Tk > 0");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) || !aligned16(a->lse) ||
+      !aligned16(a->sinks))
+    return fail(ATTN_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const int64_t vec = (a->dtype == ATTN_BF16) ? 8 : 4;  // elements per 16 bytes
+  const int64_t strides[] = {a->q_sb, a->q_sh, a->q_st, a->k_sb, a->k_sh, a->k_st,
+                             a->v_sb, a->v_sh, a->v_st, a->o_sb, a->o_sh, a->o_st};
+  for (int64_t s : strides)
+    if (s < 0 || s % vec != 0)
+      return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and keep rows 16-byte aligned (multiple of %lld elements)",
+                  (long long)vec);
+  if (a->Tq > 1 && a->q_st < a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "q token stride smaller than d_qk");
+  if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v))
+    return fail(ATTN_INVALID_ARGUMENT, "k/v token stride smaller than the head dim");
+  if (a->Tq > 1 && a->o_st < a->d_v) return fail(ATTN_INVALID_ARGUMENT, "out token stride smaller than d_v");
+
+  out->cfg = cfg;
+  attn::KernelParams& p = out->kp;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse; p.sinks = a->sinks; p.idx = nullptr;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_st = a->q_st;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
+  p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_st = a->o_st;
+  p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
+  p.npool = 0;
+  p.causal = a->causal;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  const int BM = cfg->block_rows;
+  p.block_rows = BM;
+  p.n_groups = a->B * a->Hkv;
+  // Tiles never straddle heads when a head has at least one full block of
+  // rows; otherwise the rows of several heads of one group share a tile
+  // (the folded view), which is what makes small Tq (decode) efficient.
+  const int64_t folded = (int64_t)p.g * a->Tq;
+  if (a->Tq >= BM) {
+    p.aligned = 1;
+    p.tiles_per_head = (a->Tq + BM - 1) / BM;
+    p.tiles_per_group = p.tiles_per_head * p.g;
+  } else {
+    p.aligned = 0;
+    p.tiles_per_head = 0;
+    p.tiles_per_group = (int)((folded + BM - 1) / BM);
+  }
+  const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
+  if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
+  p.n_tiles = (int)tiles;
+  return ATTN_OK;
+}
+
+attn_status validate_sparse(const attn_sparse_args* a, DensePlan* out) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_sparse_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_sparse_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_sparse_args));
+  if (a->dtype != ATTN_BF16) return fail(ATTN_UNSUPPORTED, "sparse path supports bf16 only");
+  if (a->Sq < 0 || a->Hq < 1 || a->N < 1 || a->topk < 0) return fail(ATTN_INVALID_ARGUMENT, "bad Sq/Hq/N/topk");
+  if (a->d_v > a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "d_v must not exceed d_qk (V is a prefix of each pool row)");
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  const attn::KernelConfig* cfg = find_config(ATTN_BF16, a->d_qk, a->d_v, 1);
+  if (!cfg) return fail(ATTN_UNSUPPORTED, "no compiled sparse kernel for (d_qk, d_v) = (%d, %d)", a->d_qk, a->d_v);
+  if (a->Hq > cfg->block_rows)
+    return fail(ATTN_UNSUPPORTED, "sparse kernel handles up to %d heads per query, got %d", cfg->block_rows, a->Hq);
+  if (a->Sq > 0 && (!a->q || !a->out || !a->lse))
+    return fail(ATTN_INVALID_ARGUMENT, "q, out, lse must be non-NULL when Sq > 0");
+  if (a->Sq > 0 && a->topk > 0 && (!a->kv || !a->indices))
+    return fail(ATTN_INVALID_ARGUMENT, "kv, indices must be non-NULL when Sq > 0 and topk > 0");
+  if (!aligned16(a->q) || !aligned16(a->kv) || !aligned16(a->out) || !aligned16(a->lse) ||
+      ((uintptr_t)a->indices & 3u) || !aligned16(a->sinks))
+    return fail(ATTN_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (indices 4-byte)");
+  const int64_t strides[] = {a->q_ss, a->q_sh, a->kv_sn, a->o_ss, a->o_sh};
+  for (int64_t s : strides)
+    if (s < 0 || s % 8 != 0)
+      return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and multiples of 8 elements");
+  if (a->kv_sn < a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "kv row stride smaller than d_qk");
+  if (a->idx_ss < a->topk) return fail(ATTN_INVALID_ARGUMENT, "index row stride smaller than topk");
+
+  out->cfg = cfg;
+  attn::KernelParams& p = out->kp;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->kv; p.v = a->kv; p.out = a->out; p.lse = a->lse; p.sinks = a->sinks; p.idx = a->indices;
+  p.q_sb = a->q_ss; p.q_sh = a->q_sh;
+  p.k_st = a->kv_sn; p.v_st = a->kv_sn;
+  p.o_sb = a->o_ss; p.o_sh = a->o_sh;
+  p.idx_ss = a->idx_ss;
+  p.B = a->Sq; p.H = a->Hq; p.Hkv = 1; p.Tq = 1; p.Tk = a->topk; p.g = 1;
+  p.npool = a->N;
+  p.causal = 0;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  p.block_rows = cfg->block_rows;
+  p.n_groups = a->Sq;
+  p.n_tiles = a->Sq;
+  return ATTN_OK;
+}
+
+void fill_plan(const DensePlan& dp, int fold_g, int64_t folded_rows, int64_t Tk, int score_elt, attn_plan* p) {
+  std::memset(reinterpret_cast<char*>(p) + sizeof(p->struct_size), 0, sizeof(*p) - sizeof(p->struct_size));
+  std::snprintf(p->path, sizeof(p->path), "%s", dp.cfg->path);
+  p->block_rows = dp.cfg->block_rows;
+  p->block_keys = dp.cfg->block_keys;
+  p->waves = dp.cfg->waves;
+  p->grid = dp.kp.n_tiles;
+  p->lds_bytes = dp.cfg->lds_bytes;
+  p->fold_g = fold_g;
+  p->folded_rows = folded_rows;
+  p->hbm_score_bytes = 0;  // scores and probabilities never leave the CU
+  p->budget_bytes = tile_budget_bytes();
+  p->score_elt_bytes = score_elt;
+  p->budget_tile_rows = attn_budget_tile_rows(p->budget_bytes, Tk > 0 ? Tk : 1, score_elt);
+  p->budget_tiles = p->budget_tile_rows > 0 ? (folded_rows + p->budget_tile_rows - 1) / p->budget_tile_rows : 0;
+}
+
+attn_status do_launch(const DensePlan& dp, void* stream) {
+  if (dp.kp.n_tiles <= 0) return ATTN_OK;  // nothing to compute (Tq == 0 or Sq == 0)
+  const int err = dp.cfg->launch(dp.kp, stream);
+  if (err != 0)
+    return fail(ATTN_HIP_ERROR, "launch of %s failed: %s", dp.cfg->path, hipGetErrorString((hipError_t)err));
+  note_dispatch(path_index(dp.cfg->path), dp.cfg->path);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+attn_status attn_fwd_dense(const attn_dense_args* a, void* stream) {
+  g_last_error.clear();
+  DensePlan dp;
+  attn_status s = validate_dense(a, &dp);
+  if (s != ATTN_OK) return s;
+  if (a->Tq == 0) return ATTN_OK;
+  return do_launch(dp, stream);
+}
+
+attn_status attn_fwd_sparse_topk(const attn_sparse_args* a, void* stream) {
+  g_last_error.clear();
+  DensePlan dp;
+  attn_status s = validate_sparse(a, &dp);
+  if (s != ATTN_OK) return s;
+  return do_launch(dp, stream);
+}
+
+attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p) {
+  g_last_error.clear();
+  if (!p) return fail(ATTN_INVALID_ARGUMENT, "plan is NULL");
+  if (p->struct_size != sizeof(attn_plan))
+    return fail(ATTN_ABI_MISMATCH, "attn_plan.struct_size = %u, library expects %zu", p->struct_size, sizeof(attn_plan));
+  DensePlan dp;
+  attn_status s = validate_dense(a, &dp);
+  if (s != ATTN_OK) return s;
+  if (a->Tq == 0) dp.kp.n_tiles = 0;
+  fill_plan(dp, a->H / a->Hkv, (int64_t)(a->H / a->Hkv) * a->Tq, a->Tk, a->dtype == ATTN_BF16 ? 2 : 4, p);
+  return ATTN_OK;
+}
+
+attn_status attn_plan_sparse_topk(const attn_sparse_args* a, attn_plan* p) {
+  g_last_error.clear();
+  if (!p) return fail(ATTN_INVALID_ARGUMENT, "plan is NULL");
+  if (p->struct_size != sizeof(attn_plan))
+    return fail(ATTN_ABI_MISMATCH, "attn_plan.struct_size = %u, library expects %zu", p->struct_size, sizeof(attn_plan));
+  DensePlan dp;
+  attn_status s = validate_sparse(a, &dp);
+  if (s != ATTN_OK) return s;
+  fill_plan(dp, 1, a->Hq, a->topk, 2, p);
+  return ATTN_OK;
+}
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_UNSUPPORTED: return "unsupported";
+    case ATTN_ABI_MISMATCH: return "ABI mismatch";
+    case ATTN_HIP_ERROR: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t attn_dispatch_count(const char* path) {
+  if (!path) return 0;
+  const int i = path_index(path);
+  return i < 0 ? 0 : g_counts[i].load(std::memory_order_relaxed);
+}
+
+void attn_reset_dispatch_counts(void) {
+  for (int i = 0; i < kMaxPaths; ++i) g_counts[i].store(0, std::memory_order_relaxed);
+}
+
+int64_t attn_budget_tile_rows(int64_t budget_bytes, int64_t Tk, int64_t elt_bytes) {
+  if (budget_bytes <= 0 || Tk <= 0 || elt_bytes <= 0) return 0;
+  const int64_t r = budget_bytes / (Tk * elt_bytes);
+  return r > 0 ? r : 1;
+}
+
+}  // extern "C"

@@ -1,0 +1,672 @@
+// Fused attention forward for AMD CDNA4 (gfx950 / MI355X).
+//
+// One workgroup owns a block of query rows and streams keys through LDS:
+//
+//   S^T = K Q^T      on v_mfma_f32_32x32x16_bf16 (fp32 accumulate)
+//   online softmax   row max / row sum kept in registers, exp2 with the
+//                    scale*log2(e) factor folded into one FMA
+//   O^T += V^T P^T   on the same MFMA, P taken straight from the S^T
+//                    accumulators after bf16 packing
+//
+// The scores are computed transposed (keys along the MFMA M dimension,
+// queries along N) so that every lane owns exactly one query row: lane l holds
+// query column l%32 and 16 of the 32 keys of a 32x32 tile, the other 16 being
+// in lane l^32. Row max and row sum are therefore in-lane reductions plus one
+// exchange with the partner half-wave, the rescale of the output accumulator
+// is a per-lane multiply, and the accumulator layout of S^T is already the B
+// operand layout that O^T = V^T P^T needs (no shuffle of P).
+//
+// K is staged in LDS row-major ([key][d], rows padded by 16 bytes so that the
+// 32 rows read by one A-operand load fall in distinct banks). V is staged
+// transposed ([d][key]) because the PV contraction runs over keys: each
+// thread loads a 4-key x 8-d block with 16-byte global loads and transposes
+// it in registers before writing 8-byte rows. Keys inside each 16-key group
+// are stored in the order {0-3, 8-11, 4-7, 12-15}, which is the order in which
+// the S^T accumulator hands them to the B operand, so one lane's eight V^T
+// values are contiguous.
+//
+// Tiles are double-buffered in LDS with a register prefetch: the global loads
+// of tile i+2 are in flight while tile i is being multiplied.
+//
+// GQA/MQA: the query rows of one (batch, kv head) are the folded view
+// [g*Tq, d] of q[B,H,Tq,d] with kv-major heads (ArcFlash pull request,
+// "What rung 0 does"): folded row f is head kv*g + f/Tq at token f%Tq. The
+// fold is pure index arithmetic; nothing is copied.
+//
+// d = 512: a group of DS waves shares each 32-row query block; wave i of the
+// group computes a partial S over d_qk/DS columns, the partials are summed
+// through LDS, and the wave keeps the output columns [i*d_v/DS, (i+1)*d_v/DS).
+// This keeps the fp32 output accumulator at 128 registers per lane.
+//
+// Sparse top-k (TensorRT-LLM pull request 22028, "Description"): the rows of a
+// workgroup are the heads of one query; the keys are pool rows named by the
+// query's index list, gathered with 16-byte loads into the same LDS tiles. The
+// value rows are the first d_v columns of the same gathered rows, so every
+// gathered row is read from memory once and serves both products.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_params.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16_t;
+typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// value held by lane l ^ 32
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16_t a = (bf16_t)lo, b = (bf16_t)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Note: reinterpret single vector elements with __uint_as_float, never with
+// __builtin_bit_cast(float, vec[i]) -- this compiler lowers the latter to a
+// read of element 0 of the vector.
+
+// split 8 floats into high and low bfloat16 parts: x ~= hi + lo with ~16 bits
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16_t h0 = (bf16_t)x[2 * i], h1 = (bf16_t)x[2 * i + 1];
+    float r0 = x[2 * i] - (float)h0, r1 = x[2 * i + 1] - (float)h1;
+    h[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+// position of key-quad kq (4 keys) inside a V^T row: quads {0,2,1,3} of each 16-key group
+__device__ __forceinline__ int vquad_pos(int kq) {
+  const int q = kq & 3;
+  return (kq & ~3) | ((q & 1) << 1) | (q >> 1);
+}
+
+template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int NQG = NW / DS;           // query groups per workgroup
+  static constexpr int BM = NQG * QT * 32;      // query rows per workgroup
+  static constexpr int DQW = DQK / DS;          // d_qk columns per wave
+  static constexpr int DVW = DV / DS;           // d_v columns per wave
+  static constexpr int KS = DQW / 16;           // MFMA k-steps of S per wave
+  static constexpr int MT = BN / 32;            // 32-key tiles per block
+  static constexpr int DT = DVW / 32;           // 32-column output tiles per wave
+  static constexpr int PKS = BN / 16;           // MFMA k-steps of PV
+  static constexpr int K_LD = DQK + 8;          // K row stride in LDS (elements)
+  static constexpr int V_LD = BN + 4;           // V^T row stride in LDS (elements)
+  static constexpr int NSPLIT = F32 ? 2 : 1;    // hi/lo bf16 parts for fp32 inputs
+  static constexpr int K_ELEMS = BN * K_LD;
+  static constexpr int V_ELEMS = DV * V_LD;
+  static constexpr int STAGE_ELEMS = NSPLIT * (K_ELEMS + V_ELEMS);
+  static constexpr int SX_FLOATS = (DS > 1) ? NW * QT * MT * 16 * 64 : 0;
+  static constexpr int FLAG_BYTES = SPARSE ? 2 * BN : 0;
+  static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * 2 + SX_FLOATS * 4 + FLAG_BYTES;
+  // dense K tile loading: 8-element chunks, consecutive threads along a row
+  static constexpr int KCH = BN * DQK / 8;
+  static constexpr int KCH_PT = (KCH + NT - 1) / NT;
+  // V loading (and all sparse loading): units of 4 keys x 8 columns
+  static constexpr int UCOLS = SPARSE ? DQK : DV;
+  static constexpr int VU = (BN / 4) * (UCOLS / 8);
+  static constexpr int VU_PT = (VU + NT - 1) / NT;
+  static constexpr int WORDS = F32 ? 8 : 4;     // 32-bit words per 8-element chunk
+  static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0, "head dims must tile");
+  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+  static_assert(!(SPARSE && F32), "sparse path is bf16 only");
+  static_assert(!SPARSE || DV <= DQK, "sparse value columns are a prefix of the row");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
+__global__ void __launch_bounds__(NW * 64)
+attn_fwd_kernel(const KernelParams p) {
+  using C = Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>;
+  using in_t = typename std::conditional<F32, float, bf16_t>::type;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
+  bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
+  float* const sx = reinterpret_cast<float*>(smem + 2 * C::STAGE_ELEMS * 2);
+  unsigned char* const flags = smem + 2 * C::STAGE_ELEMS * 2 + C::SX_FLOATS * 4;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int qg = wave / DS, dsi = wave % DS;
+
+  // ---------------------------------------------------------------- tile
+  int b = 0, kvh = 0, f0 = 0, nrows = 0, t_lo = 0, t_hi = 0, sq = 0;
+  if constexpr (SPARSE) {
+    sq = blockIdx.x;
+    nrows = p.H;
+  } else {
+    const int tile = blockIdx.x;
+    if (p.aligned) {
+      // largest causal row blocks first (longest-processing-time order)
+      const int per_tb = p.n_groups * p.g;
+      const int tb = (p.tiles_per_head - 1) - tile / per_tb;
+      const int rest = tile % per_tb;
+      const int grp = rest / p.g, hl = rest % p.g;
+      b = grp / p.Hkv;
+      kvh = grp % p.Hkv;
+      const int t0 = tb * C::BM;
+      f0 = hl * p.Tq + t0;
+      nrows = min(C::BM, p.Tq - t0);
+      t_lo = t0;
+      t_hi = t0 + nrows - 1;
+    } else {
+      const int grp = tile / p.tiles_per_group;
+      f0 = (tile % p.tiles_per_group) * C::BM;
+      nrows = min(C::BM, p.g * p.Tq - f0);
+      b = grp / p.Hkv;
+      kvh = grp % p.Hkv;
+      const int tf = f0 % p.Tq;
+      if (nrows >= p.Tq || tf + nrows > p.Tq) {
+        t_lo = 0;
+        t_hi = p.Tq - 1;
+      } else {
+        t_lo = tf;
+        t_hi = tf + nrows - 1;
+      }
+    }
+  }
+
+  // keys [0, kend) are needed; below kfull no row of the tile is masked
+  int kend = p.Tk, kfull = p.Tk;
+  if (!SPARSE && p.causal) {
+    const int off = p.Tk - p.Tq;
+    kend = min(p.Tk, max(0, t_hi + off + 1));
+    kfull = min(p.Tk, max(0, t_lo + off + 1));
+  }
+  const int nblk = (kend + BN - 1) / BN;
+
+  // ---------------------------------------------------------------- rows of this lane
+  bool row_ok[QT];
+  int row_lim[QT];        // last visible key (dense)
+  int row_h[QT];
+  int64_t q_off[QT], o_off[QT], l_off[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = (qg * QT + qt) * 32 + lq;
+    row_ok[qt] = r < nrows;
+    const int rr = row_ok[qt] ? r : 0;
+    if constexpr (SPARSE) {
+      row_h[qt] = rr;
+      row_lim[qt] = p.Tk - 1;
+      q_off[qt] = (int64_t)sq * p.q_sb + (int64_t)rr * p.q_sh;
+      o_off[qt] = (int64_t)sq * p.o_sb + (int64_t)rr * p.o_sh;
+      l_off[qt] = (int64_t)sq * p.H + rr;
+    } else {
+      const int f = f0 + rr;
+      const int h = kvh * p.g + f / p.Tq;
+      const int t = f % p.Tq;
+      row_h[qt] = h;
+      row_lim[qt] = p.causal ? min(p.Tk - 1, t + p.Tk - p.Tq) : p.Tk - 1;
+      q_off[qt] = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)t * p.q_st;
+      o_off[qt] = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)t * p.o_st;
+      l_off[qt] = ((int64_t)b * p.H + h) * p.Tq + t;
+    }
+  }
+
+  // ---------------------------------------------------------------- Q fragments (B operand of S^T)
+  bf16x8 qf[QT][C::KS];
+  bf16x8 qlo[F32 ? QT : 1][F32 ? C::KS : 1];
+  {
+    const in_t* qb = reinterpret_cast<const in_t*>(p.q);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int d0 = dsi * C::DQW + s * 16 + lh * 8;
+        if constexpr (F32) {
+          float x[8];
+          if (row_ok[qt]) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(qb + q_off[qt] + d0);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(qb + q_off[qt] + d0 + 4);
+            x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+            x[4] = c[0]; x[5] = c[1]; x[6] = c[2]; x[7] = c[3];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
+          }
+          u32x4 hi, lo;
+          split8(x, hi, lo);
+          qf[qt][s] = as_bf16x8(hi);
+          qlo[qt][s] = as_bf16x8(lo);
+        } else {
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (row_ok[qt]) w = *reinterpret_cast<const u32x4*>(qb + q_off[qt] + d0);
+          qf[qt][s] = as_bf16x8(w);
+        }
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- tile loader
+  const in_t* kbase;
+  const in_t* vbase;
+  if constexpr (SPARSE) {
+    kbase = reinterpret_cast<const in_t*>(p.k);
+    vbase = kbase;
+  } else {
+    kbase = reinterpret_cast<const in_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    vbase = reinterpret_cast<const in_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  }
+  const int32_t* idx_row = SPARSE ? p.idx + (int64_t)sq * p.idx_ss : nullptr;
+
+  u32x4 kst[SPARSE ? 1 : C::KCH_PT][C::WORDS / 4];
+  u32x4 vst[C::VU_PT][4][C::WORDS / 4];
+  int32_t sidx[4];        // sparse: pool rows of this thread's 4 keys for the next load
+  uint32_t svalid = 0;    // sparse: validity bits of the staged keys
+
+  auto load_idx = [&](int blk) {
+    // this thread's key quad is the same for all its units (unit stride NT is a multiple of BN/4)
+    const int kq = tid % (BN / 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kk = blk * BN + 4 * kq + r;
+      sidx[r] = (kk < p.Tk) ? idx_row[kk] : -1;
+    }
+  };
+
+  auto load_tile = [&](int blk) {
+    const int key0 = blk * BN;
+    if constexpr (!SPARSE) {
+#pragma unroll
+      for (int i = 0; i < C::KCH_PT; ++i) {
+        const int c = tid + i * C::NT;
+        const int key = c / (DQK / 8), dc = c % (DQK / 8);
+        const int kk = key0 + key;
+        const bool ok = (c < C::KCH) && (kk < kend);
+        const in_t* src = kbase + (int64_t)kk * p.k_st + dc * 8;
+#pragma unroll
+        for (int w = 0; w < C::WORDS / 4; ++w)
+          kst[i][w] = ok ? *reinterpret_cast<const u32x4*>(src + w * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < C::VU_PT; ++i) {
+        const int u = tid + i * C::NT;
+        const int kq = u % (BN / 4), dc = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = key0 + 4 * kq + r;
+          const bool ok = (u < C::VU) && (kk < kend);
+          const in_t* src = vbase + (int64_t)kk * p.v_st + dc * 8;
+#pragma unroll
+          for (int w = 0; w < C::WORDS / 4; ++w)
+            vst[i][r][w] = ok ? *reinterpret_cast<const u32x4*>(src + w * 4) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    } else {
+      (void)key0;
+      uint32_t vb = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vb |= (sidx[r] >= 0 && sidx[r] < p.npool) ? (1u << r) : 0u;
+      svalid = vb;
+#pragma unroll
+      for (int i = 0; i < C::VU_PT; ++i) {
+        const int u = tid + i * C::NT;
+        const int dc = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (u < C::VU) && ((vb >> r) & 1u);
+          const in_t* src = kbase + (int64_t)(ok ? sidx[r] : 0) * p.k_st + dc * 8;
+          vst[i][r][0] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      if (blk + 1 < nblk) load_idx(blk + 1);
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    bf16_t* Kb = lds + buf * C::STAGE_ELEMS;
+    bf16_t* Vb = Kb + C::NSPLIT * C::K_ELEMS;
+    if constexpr (!SPARSE) {
+#pragma unroll
+      for (int i = 0; i < C::KCH_PT; ++i) {
+        const int c = tid + i * C::NT;
+        if (c < C::KCH) {
+          const int key = c / (DQK / 8), dc = c % (DQK / 8);
+          bf16_t* dst = Kb + key * C::K_LD + dc * 8;
+          if constexpr (F32) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(kst[i][e / 4][e % 4]);
+            u32x4 hi, lo;
+            split8(x, hi, lo);
+            *reinterpret_cast<u32x4*>(dst) = hi;
+            *reinterpret_cast<u32x4*>(dst + C::K_ELEMS) = lo;
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = kst[i][0];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VU_PT; ++i) {
+      const int u = tid + i * C::NT;
+      if (u < C::VU) {
+        const int kq = u % (BN / 4), dc = u / (BN / 4);
+        // rows as bf16 words: hv[part][r] = 4 words (8 elements) of key r
+        u32x4 hv[C::NSPLIT][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (F32) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(vst[i][r][e / 4][e % 4]);
+            split8(x, hv[0][r], hv[C::NSPLIT - 1][r]);
+          } else {
+            hv[0][r] = vst[i][r][0];
+          }
+        }
+        if constexpr (SPARSE) {
+          // row-major K tile from the same gathered rows
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<u32x4*>(Kb + (4 * kq + r) * C::K_LD + dc * 8) = hv[0][r];
+        }
+        if (!SPARSE || dc < DV / 8) {
+          // transpose 4 keys x 8 columns into 8 V^T rows of 4 keys
+          const int col = vquad_pos(kq) * 4;
+#pragma unroll
+          for (int part = 0; part < C::NSPLIT; ++part) {
+            bf16_t* vdst = Vb + part * C::V_ELEMS + (dc * 8) * C::V_LD + col;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int w = j >> 1;
+              uint32_t x0, x1;
+              if (j & 1) {
+                x0 = (hv[part][0][w] >> 16) | (hv[part][1][w] & 0xffff0000u);
+                x1 = (hv[part][2][w] >> 16) | (hv[part][3][w] & 0xffff0000u);
+              } else {
+                x0 = (hv[part][0][w] & 0xffffu) | (hv[part][1][w] << 16);
+                x1 = (hv[part][2][w] & 0xffffu) | (hv[part][3][w] << 16);
+              }
+              *reinterpret_cast<u32x2*>(vdst + j * C::V_LD) = u32x2{x0, x1};
+            }
+          }
+        }
+      }
+    }
+    if constexpr (SPARSE) {
+      if (tid < BN / 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) flags[buf * BN + 4 * tid + r] = (svalid >> r) & 1u;
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- state
+  f32x16 acc[QT][C::DT];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qt][dt][i] = 0.f;
+  }
+
+  if (nblk > 0) {
+    if constexpr (SPARSE) load_idx(0);
+    load_tile(0);
+    store_tile(0);
+    if (nblk > 1) load_tile(1);
+  }
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    __syncthreads();
+    const int buf = blk & 1;
+    const bf16_t* Kb = lds + buf * C::STAGE_ELEMS;
+    const bf16_t* Vb = Kb + C::NSPLIT * C::K_ELEMS;
+    const int key0 = blk * BN;
+
+    // ---- S^T = K Q^T (partial over this wave's d_qk columns)
+    f32x16 S[QT][C::MT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[qt][mt][i] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int off = (mt * 32 + lq) * C::K_LD + dsi * C::DQW + s * 16 + lh * 8;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + off);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[qt][mt] = mfma32(a, qf[qt][s], S[qt][mt]);
+        if constexpr (F32) {
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(Kb + C::K_ELEMS + off);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            S[qt][mt] = mfma32(alo, qf[qt][s], S[qt][mt]);
+            S[qt][mt] = mfma32(a, qlo[qt][s], S[qt][mt]);
+          }
+        }
+      }
+    }
+
+    // ---- sum the partial scores of the DS waves sharing these rows
+    if constexpr (DS > 1) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float* dst = sx + ((((wave * QT + qt) * C::MT + mt) * 4 + g4) * 64 + lane) * 4;
+            *reinterpret_cast<f32x4*>(dst) =
+                f32x4{S[qt][mt][g4 * 4], S[qt][mt][g4 * 4 + 1], S[qt][mt][g4 * 4 + 2], S[qt][mt][g4 * 4 + 3]};
+          }
+      __syncthreads();
+#pragma unroll
+      for (int o = 1; o < DS; ++o) {
+        const int w2 = qg * DS + (dsi + o) % DS;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const float* src = sx + ((((w2 * QT + qt) * C::MT + mt) * 4 + g4) * 64 + lane) * 4;
+              const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) S[qt][mt][g4 * 4 + e] += v[e];
+            }
+      }
+    }
+
+    // ---- masks: causal / ragged tail (dense) or skipped indices (sparse)
+    if constexpr (SPARSE) {
+      const unsigned char* fl = flags + buf * BN;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const uint32_t f4 = *reinterpret_cast<const uint32_t*>(fl + mt * 32 + g4 * 8 + lh * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (((f4 >> (8 * e)) & 0xffu) == 0u)
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt) S[qt][mt][g4 * 4 + e] = -INFINITY;
+        }
+    } else {
+      if (key0 + BN > kfull) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + mt * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+              if (key > row_lim[qt]) S[qt][mt][i] = -INFINITY;
+            }
+      }
+    }
+
+    // ---- online softmax (base 2, scale folded into the FMA)
+    bf16x8 pb[QT][C::PKS];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qt][mt][i]);
+      mx = fmaxf(mx, other_half(mx));
+      const float mnew = fmaxf(m_run[qt], mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - muse) * p.c);
+      const float mc = muse * p.c;
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(S[qt][mt][i], p.c, -mc));
+          S[qt][mt][i] = e;
+          rs += e;
+        }
+      l_run[qt] = l_run[qt] * alpha + rs;
+      m_run[qt] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[qt][dt][i] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < C::PKS; ++ks) {
+        const int mt = ks >> 1, base = (ks & 1) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(S[qt][mt][base + 2 * e], S[qt][mt][base + 2 * e + 1]);
+        pb[qt][ks] = as_bf16x8(w);
+      }
+    }
+
+    // ---- O^T += V^T P^T over this wave's d_v columns
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < C::PKS; ++ks) {
+        const int off = (dsi * C::DVW + dt * 32 + lq) * C::V_LD + ks * 16 + lh * 8;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(Vb + off);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(Vb + off + 4);
+        const bf16x8 a = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32(a, pb[qt][ks], acc[qt][dt]);
+        if constexpr (F32) {
+          const u32x2 b0 = *reinterpret_cast<const u32x2*>(Vb + C::V_ELEMS + off);
+          const u32x2 b1 = *reinterpret_cast<const u32x2*>(Vb + C::V_ELEMS + off + 4);
+          const bf16x8 alo = as_bf16x8(u32x4{b0[0], b0[1], b1[0], b1[1]});
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma32(alo, pb[qt][ks], acc[qt][dt]);
+        }
+      }
+    }
+
+    // ---- stage the next tile, prefetch the one after
+    if (blk + 1 < nblk) {
+      store_tile(buf ^ 1);
+      if (blk + 2 < nblk) load_tile(blk + 2);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  in_t* ob = reinterpret_cast<in_t*>(p.out);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float lt = l_run[qt] + other_half(l_run[qt]);
+    const float ms = (m_run[qt] == -INFINITY) ? -INFINITY : m_run[qt] * p.scale;  // natural units
+    float inv, lse;
+    if (p.sinks != nullptr) {
+      const float sk = p.sinks[row_h[qt]];
+      const float M = fmaxf(ms, sk);
+      if (M == -INFINITY) {
+        inv = 0.f;
+        lse = -INFINITY;
+      } else {
+        const float fac = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - M) * kLog2e);
+        const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - M) * kLog2e);
+        const float den = lt * fac + es;
+        inv = den > 0.f ? fac / den : 0.f;
+        lse = den > 0.f ? M + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+      }
+    } else {
+      inv = lt > 0.f ? 1.f / lt : 0.f;
+      lse = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
+    }
+    if (row_ok[qt]) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = dsi * C::DVW + dt * 32 + g4 * 8 + lh * 4;
+          const float v0 = acc[qt][dt][g4 * 4] * inv, v1 = acc[qt][dt][g4 * 4 + 1] * inv;
+          const float v2 = acc[qt][dt][g4 * 4 + 2] * inv, v3 = acc[qt][dt][g4 * 4 + 3] * inv;
+          if constexpr (F32) {
+            *reinterpret_cast<f32x4*>(ob + o_off[qt] + d) = f32x4{v0, v1, v2, v3};
+          } else {
+            *reinterpret_cast<u32x2*>(ob + o_off[qt] + d) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          }
+        }
+      }
+      if (lh == 0 && dsi == 0) p.lse[l_off[qt]] = lse;
+    }
+  }
+}
+
+template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
+int launch(const KernelParams& p, void* stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, QT, DS, NW, BN, F32, SPARSE>), dim3(p.n_tiles), dim3(NW * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
+  return (int)hipGetLastError();
+}
+
+#define CFG_ENTRY(NAME, DT, DQK, DV, QT, DS, NW, BN, F32, SPARSE)                                          \
+  KernelConfig {                                                                                          \
+    NAME, DT, DQK, DV, SPARSE, Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::BM, BN, NW,                    \
+        Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::LDS_BYTES, &launch<DQK, DV, QT, DS, NW, BN, F32, SPARSE> \
+  }
+
+const KernelConfig kTable[] = {
+    CFG_ENTRY("dense_bf16_d64", 0, 64, 64, 1, 1, 4, 64, false, false),
+    CFG_ENTRY("dense_bf16_d128", 0, 128, 128, 1, 1, 4, 64, false, false),
+    CFG_ENTRY("dense_bf16_d192_v128", 0, 192, 128, 1, 1, 4, 64, false, false),
+    CFG_ENTRY("dense_bf16_d256", 0, 256, 256, 1, 1, 4, 32, false, false),
+    CFG_ENTRY("dense_bf16_d512", 0, 512, 512, 1, 2, 4, 32, false, false),
+    CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
+    CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
+    CFG_ENTRY("sparse_bf16_d512", 0, 512, 512, 1, 2, 4, 32, false, true),
+};
+
+}  // namespace
+
+const KernelConfig* kernel_table(int* n) {
+  *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
+  return kTable;
+}
+
+}  // namespace attn

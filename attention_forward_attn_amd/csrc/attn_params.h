@@ -1,0 +1,55 @@
+// Launch parameters shared by the host planner (api.cpp) and the gfx950
+// kernels (attn_kernels.hip). Plain data only.
+#pragma once
+#include <stdint.h>
+
+namespace attn {
+
+struct KernelParams {
+  const void* q;
+  const void* k;        // dense: K; sparse: the shared KV pool
+  const void* v;        // dense: V; sparse: same pool (value = first d_v columns)
+  void* out;
+  float* lse;
+  const float* sinks;   // [H] or nullptr
+  const int32_t* idx;   // sparse only: [Sq, topk]
+
+  // element strides. dense: (b, h, t); sparse: q (s, h, -), kv row stride in k_st
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t o_sb, o_sh, o_st;
+  int64_t idx_ss;
+
+  int32_t B, H, Hkv, Tq, Tk, g;  // sparse: B = Sq, H = Hq, Hkv = 1, Tk = topk
+  int32_t npool;                 // sparse: rows in the pool
+  int32_t causal;
+  float scale;                   // softmax scale
+  float c;                       // scale * log2(e)
+
+  // workgroup -> tile decode (dense)
+  int32_t aligned;        // 1: tiles never straddle heads (tiles_per_head per head)
+  int32_t block_rows;     // folded rows per workgroup
+  int32_t tiles_per_head; // aligned mode
+  int32_t tiles_per_group;// tiles per (b, kv head)
+  int32_t n_groups;       // B * Hkv
+  int32_t n_tiles;        // grid size
+};
+
+// Host-side launchers, one per compiled kernel configuration.
+// Return 0 on success, else the hipError_t of the launch.
+typedef int (*launch_fn)(const KernelParams& p, void* stream);
+
+struct KernelConfig {
+  const char* path;
+  int dtype;         // 0 bf16, 1 f32 split
+  int d_qk, d_v;
+  int sparse;
+  int block_rows, block_keys, waves, lds_bytes;
+  launch_fn launch;
+};
+
+// Table of compiled configurations (defined in attn_kernels.hip).
+const KernelConfig* kernel_table(int* n);
+
+}  // namespace attn

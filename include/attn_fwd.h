@@ -1,0 +1,200 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ * The library computes, in one kernel launch per call,
+ *
+ *     O   = softmax(scale * Q K^T + mask [+ per-head sink in the denominator]) V
+ *     lse = log of each row's softmax denominator (natural log)
+ *
+ * i.e. the attention forward that returns the output together with the per-row
+ * log-sum-exp (pith-train pull request 65, "Issues resolved" item 1: FA4's
+ * forward returns (out, lse)). Variants covered:
+ *
+ *   - GQA/MQA: H query heads share Hkv K/V heads, heads kv-major, so query head
+ *     h reads K/V head h / (H/Hkv). The query tensor is used as the folded view
+ *     [B, Hkv, g*Tq, D] with g = H/Hkv, a reshape and never a copy (ArcFlash
+ *     pull request, "What rung 0 does").
+ *   - MLA asymmetric head dims d_qk != d_v, the no-rope/rope concatenation done
+ *     by the caller (pith-train pull request 65, "Issues resolved" item 2).
+ *   - d = 512 heads with attention sinks: a per-head logit that enters each
+ *     row's denominator only (ArcFlash pull request, "What rung 0 does").
+ *   - A sparse top-k forward in which each query attends to the rows of one
+ *     shared KV pool named by its index list (TensorRT-LLM pull request 22028,
+ *     "Description": flash_mla_sparse_fwd, 13312 queries x 64 heads x 2176
+ *     rows, d_qk 512).
+ *
+ * Conventions (all calls):
+ *   - Ownership: the caller owns every buffer. The library never allocates,
+ *     frees or synchronises device memory; it only launches on `stream`.
+ *   - Device pointers: q, k, v, kv, out, lse, sinks and indices are device
+ *     addresses (hipMalloc or equivalent) and must be 16-byte aligned. Strides
+ *     are in ELEMENTS of the tensor's own type; the last dimension is always
+ *     contiguous (stride 1). Row strides must keep every row 16-byte aligned.
+ *   - Streams: `stream` is a hipStream_t passed as void*. NULL is valid and
+ *     means the legacy default stream, as in HIP itself. Calls are
+ *     asynchronous with respect to the host.
+ *   - Errors: every call returns an attn_status. Argument errors are detected
+ *     on the host before anything is launched and leave all buffers untouched;
+ *     attn_last_error() then holds a message naming the offending argument.
+ *     There is no fallback path: an unsupported shape returns
+ *     ATTN_UNSUPPORTED, never a slower kernel.
+ *   - Aliasing: out and lse must not overlap any input.
+ *   - Thread safety: calls may be made from several host threads; the error
+ *     message is per thread and the dispatch counters are atomic.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_INVALID_ARGUMENT = 1, /* null pointer, bad size/stride/alignment, H % Hkv != 0, scale not finite > 0 */
+  ATTN_UNSUPPORTED = 2,      /* valid arguments outside the compiled set (head dims, dtype) */
+  ATTN_ABI_MISMATCH = 3,     /* struct_size does not match this library */
+  ATTN_HIP_ERROR = 4         /* the HIP runtime refused the launch */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_BF16 = 0, /* bfloat16 inputs and output */
+  ATTN_F32 = 1   /* float32 inputs and output (QK^T in split-bf16, see below) */
+} attn_dtype;
+
+/*
+ * Dense forward arguments.
+ *
+ *   q   [B, H,   Tq, d_qk]  element strides q_sb, q_sh, q_st (last dim contiguous)
+ *   k   [B, Hkv, Tk, d_qk]  strides k_sb, k_sh, k_st
+ *   v   [B, Hkv, Tk, d_v]   strides v_sb, v_sh, v_st
+ *   out [B, H,   Tq, d_v]   strides o_sb, o_sh, o_st (written)
+ *   lse [B, H,   Tq]        float32, contiguous (written)
+ *   sinks [H] float32 or NULL. The sink of head h is a logit in the same
+ *        space as scale*q.k (it is not multiplied by scale); it adds
+ *        exp(sink[h]) to every row's denominator and is included in lse.
+ *   causal: 0 or 1. The mask is bottom-right aligned: key j is visible to
+ *        query token t iff j <= t + (Tk - Tq). A row that sees no key
+ *        gets out = 0 and lse = -inf (lse = sink[h] when sinks are given).
+ *   dtype: ATTN_BF16, or ATTN_F32 where q and k are split into a high and
+ *        a low bfloat16 part on load so that QK^T keeps ~16 mantissa bits.
+ *   Compiled head dims (d_qk, d_v): (64,64), (128,128), (192,128),
+ *        (256,256), (512,512) in bf16; (64,64) and (128,128) in f32.
+ *   Sizes: B, H, Hkv >= 1, H % Hkv == 0; Tq, Tk >= 0 (Tq == 0 launches nothing;
+ *        Tk == 0 writes out = 0 and lse = -inf, or sink).
+ */
+typedef struct attn_dense_args {
+  uint32_t struct_size; /* = sizeof(attn_dense_args) */
+  int32_t dtype;        /* attn_dtype of q, k, v, out */
+  int32_t B, H, Hkv, Tq, Tk, d_qk, d_v;
+  int32_t causal;
+  float scale;          /* finite, > 0 */
+  const void* q;
+  int64_t q_sb, q_sh, q_st;
+  const void* k;
+  int64_t k_sb, k_sh, k_st;
+  const void* v;
+  int64_t v_sb, v_sh, v_st;
+  void* out;
+  int64_t o_sb, o_sh, o_st;
+  float* lse;
+  const float* sinks;
+} attn_dense_args;
+
+/*
+ * Sparse top-k forward arguments.
+ *
+ *   q       [Sq, Hq, d_qk] bf16, strides q_ss, q_sh
+ *   kv      [N, d_qk] bf16, row stride kv_sn: ONE shared pool. The value rows
+ *           are its first d_v columns (V == K when d_v == d_qk), so d_v <= d_qk.
+ *   indices [Sq, topk] int32, row stride idx_ss. An index outside [0, N)
+ *           (canonically -1) is skipped; duplicates count with multiplicity.
+ *   out     [Sq, Hq, d_v] bf16, strides o_ss, o_sh (written)
+ *   lse     [Sq, Hq] float32, contiguous (written)
+ *   sinks   [Hq] float32 or NULL (same meaning as in the dense call)
+ *   No mask beyond the index list. Compiled: d_qk = 512, d_v = 512, Hq = 64.
+ */
+typedef struct attn_sparse_args {
+  uint32_t struct_size; /* = sizeof(attn_sparse_args) */
+  int32_t dtype;        /* ATTN_BF16 */
+  int32_t Sq, Hq, N, d_qk, d_v, topk;
+  float scale;
+  const void* q;
+  int64_t q_ss, q_sh;
+  const void* kv;
+  int64_t kv_sn;
+  const int32_t* indices;
+  int64_t idx_ss;
+  void* out;
+  int64_t o_ss, o_sh;
+  float* lse;
+  const float* sinks;
+} attn_sparse_args;
+
+/*
+ * A launch plan, filled on the host without touching the GPU.
+ *   path        kernel path name (one path per shape; also the dispatch key)
+ *   block_rows  query rows per workgroup (folded rows for dense, heads for sparse)
+ *   block_keys  keys per pipeline step
+ *   waves       wavefronts per workgroup
+ *   grid        workgroups launched
+ *   lds_bytes   LDS per workgroup
+ *   fold_g      H / Hkv (1 for sparse)
+ *   folded_rows g * Tq rows per (b, kv head) of the folded query view
+ *   hbm_score_bytes  score bytes written to HBM: 0, the scores stay on chip
+ *   budget_tile_rows folded rows per tile if scores of element size
+ *               score_elt_bytes were materialised under ATTN_TILE_BYTES
+ *               (default 32 MiB): floor(budget / (Tk * elt)) (ArcFlash pull
+ *               request, "What rung 0 does": query-row tiling under a budget)
+ *   budget_tiles     tiles of that size over all folded rows of one kv head
+ */
+typedef struct attn_plan {
+  uint32_t struct_size; /* = sizeof(attn_plan), set by the caller */
+  char path[64];
+  int32_t block_rows, block_keys, waves, grid, lds_bytes, fold_g;
+  int64_t folded_rows;
+  int64_t hbm_score_bytes;
+  int64_t budget_bytes;
+  int32_t score_elt_bytes;
+  int64_t budget_tile_rows;
+  int64_t budget_tiles;
+} attn_plan;
+
+/* ABI version of the loaded library (ATTN_ABI_VERSION at build time). */
+int attn_abi_version(void);
+
+/* Dense forward. Validates, plans and launches one kernel on `stream`. */
+attn_status attn_fwd_dense(const attn_dense_args* a, void* stream);
+
+/* Sparse top-k forward. Validates, plans and launches one kernel on `stream`. */
+attn_status attn_fwd_sparse_topk(const attn_sparse_args* a, void* stream);
+
+/* The plan attn_fwd_dense / attn_fwd_sparse_topk would launch; host only. */
+attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p);
+attn_status attn_plan_sparse_topk(const attn_sparse_args* a, attn_plan* p);
+
+/* Static text for a status code. */
+const char* attn_status_string(attn_status s);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Number of launches of kernel path `path` in this process (engagement
+ * record: a path that never launched reads 0). */
+uint64_t attn_dispatch_count(const char* path);
+
+/* Reset every dispatch counter to 0. */
+void attn_reset_dispatch_counts(void);
+
+/* Folded query rows per tile when [rows, Tk] scores of elt_bytes each must fit
+ * budget_bytes: floor(budget / (Tk * elt)), at least 1; 0 on bad arguments. */
+int64_t attn_budget_tile_rows(int64_t budget_bytes, int64_t Tk, int64_t elt_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,149 @@
+"""The C-ABI library on the host: loads, exports every declared symbol, plans and
+validates without a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_forward_attn_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn_fwd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.load_library()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/attn_fwd.h but not exported"
+    assert set(names) == set(A.EXPORTS)
+
+
+def test_abi_version_and_struct_sizes():
+    assert A.abi_version() == A.ABI_VERSION
+    # the library checks struct_size; a plan call with the binding's structs must succeed
+    A.plan_dense(1, 4, 1, 128, 128, 64, 64)
+
+
+def test_abi_mismatch_is_reported():
+    lib = A.load_library()
+    a = A.AttnDenseArgs()
+    a.struct_size = ctypes.sizeof(A.AttnDenseArgs) + 8
+    p = A.AttnPlan()
+    p.struct_size = ctypes.sizeof(A.AttnPlan)
+    st = lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p))
+    assert st == A.ATTN_ABI_MISMATCH
+    assert b"struct_size" in lib.attn_last_error()
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(B=1, H=3, Hkv=2, Tq=16, Tk=16, d_qk=128, d_v=128), A.AttnInvalidArgument),   # H % Hkv
+    (dict(B=1, H=4, Hkv=1, Tq=16, Tk=16, d_qk=96, d_v=96), A.AttnUnsupported),         # head dim
+    (dict(B=1, H=4, Hkv=1, Tq=16, Tk=16, d_qk=128, d_v=64), A.AttnUnsupported),        # pair
+    (dict(B=0, H=4, Hkv=1, Tq=16, Tk=16, d_qk=128, d_v=128), A.AttnInvalidArgument),   # B
+    (dict(B=1, H=4, Hkv=1, Tq=-1, Tk=16, d_qk=128, d_v=128), A.AttnInvalidArgument),   # Tq
+])
+def test_dense_validation_errors(kw, exc):
+    with pytest.raises(exc):
+        A.plan_dense(**kw)
+
+
+def test_dense_scale_and_dtype_errors():
+    with pytest.raises(A.AttnInvalidArgument):
+        A.plan_dense(1, 4, 1, 16, 16, 128, 128, scale=float("nan"))
+    with pytest.raises(A.AttnInvalidArgument):
+        A.plan_dense(1, 4, 1, 16, 16, 128, 128, scale=-1.0)
+    with pytest.raises(A.AttnUnsupported):
+        A.plan_dense(1, 4, 1, 16, 16, 512, 512, dtype="f32")
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = A.load_library()
+    a = A.AttnDenseArgs()
+    a.struct_size = ctypes.sizeof(A.AttnDenseArgs)
+    a.dtype = A.ATTN_BF16
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = 1, 4, 1, 8, 8, 128, 128
+    a.scale = 0.1
+    a.q_sb, a.q_sh, a.q_st = 4 * 8 * 128, 8 * 128, 128
+    a.k_sb, a.k_sh, a.k_st = 8 * 128, 8 * 128, 128
+    a.v_sb, a.v_sh, a.v_st = 8 * 128, 8 * 128, 128
+    a.o_sb, a.o_sh, a.o_st = 4 * 8 * 128, 8 * 128, 128
+    # NULL q
+    a.k = a.v = a.out = a.lse = 4096
+    assert lib.attn_fwd_dense(ctypes.byref(a), None) == A.ATTN_INVALID_ARGUMENT
+    assert b"non-NULL" in lib.attn_last_error()
+    # NULL k/v are fine when there are no keys (nothing is read) -- plan only, no launch
+    a.q = 4096
+    a.k = a.v = None
+    a.Tk = 0
+    p = A.AttnPlan()
+    p.struct_size = ctypes.sizeof(A.AttnPlan)
+    assert lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p)) == A.ATTN_OK
+    a.k = a.v = 4096
+    a.Tk = 8
+    a.q = None
+    # misaligned q (8-byte aligned only)
+    a.q = 4096 + 8
+    assert lib.attn_fwd_dense(ctypes.byref(a), None) == A.ATTN_INVALID_ARGUMENT
+    assert b"aligned" in lib.attn_last_error()
+    # a stride that breaks row alignment
+    a.q = 4096
+    a.q_st = 130
+    assert lib.attn_fwd_dense(ctypes.byref(a), None) == A.ATTN_INVALID_ARGUMENT
+
+
+def test_sparse_validation_errors():
+    with pytest.raises(A.AttnInvalidArgument):
+        A.plan_sparse_topk(4, 64, 100, 512, 513, 16)           # d_v > d_qk
+    with pytest.raises(A.AttnUnsupported):
+        A.plan_sparse_topk(4, 128, 100, 512, 512, 16)          # too many heads per query
+    with pytest.raises(A.AttnUnsupported):
+        A.plan_sparse_topk(4, 64, 100, 256, 256, 16)           # head dim
+
+
+def test_plans_for_the_five_workloads():
+    p1 = A.plan_dense(1, 4, 1, 128, 128, 64, 64, dtype="f32")
+    assert p1["path"] == "dense_f32split_d64" and p1["fold_g"] == 4 and p1["folded_rows"] == 512
+    p2 = A.plan_dense(2, 32, 8, 4096, 4096, 128, 128)
+    assert p2["path"] == "dense_bf16_d128" and p2["folded_rows"] == 4 * 4096
+    assert p2["grid"] == 2 * 8 * 4 * (4096 // p2["block_rows"])
+    p3 = A.plan_dense(4, 16, 16, 4096, 4096, 192, 128)
+    assert p3["path"] == "dense_bf16_d192_v128" and p3["fold_g"] == 1
+    p4 = A.plan_dense(1, 64, 1, 1400, 1400, 512, 512, sinks=True)
+    assert p4["path"] == "dense_bf16_d512" and p4["fold_g"] == 64 and p4["folded_rows"] == 89600
+    p5 = A.plan_sparse_topk(13312, 64, 65536, 512, 512, 2176)
+    assert p5["path"] == "sparse_bf16_d512" and p5["grid"] == 13312
+    for p in (p1, p2, p3, p4, p5):
+        assert p["hbm_score_bytes"] == 0            # scores never leave the chip
+        assert p["lds_bytes"] <= 160 * 1024
+
+
+def test_budget_tiling_reproduces_arcflash_arithmetic():
+    """The planner's byte-budget tiling at the DeepSeek-V4 prefill shape of the
+    ArcFlash page (B=1 H=64 D=512 T=1400 bf16, 32 MiB): 11,983 folded rows per
+    tile, 8 tiles, tile boundaries straddling heads."""
+    p4 = A.plan_dense(1, 64, 1, 1400, 1400, 512, 512, sinks=True)
+    assert p4["budget_bytes"] == 32 << 20
+    assert p4["budget_tile_rows"] == 11983 and p4["budget_tiles"] == 8
+    assert p4["budget_tile_rows"] % 1400 != 0
+    assert A.budget_tile_rows(32 << 20, 1400, 8) == 2995
+    assert A.budget_tile_rows(0, 1400, 2) == 0
+
+
+def test_tile_budget_env(monkeypatch):
+    monkeypatch.setenv("ATTN_TILE_BYTES", str(16 << 20))
+    p = A.plan_dense(1, 64, 1, 1400, 1400, 512, 512)
+    assert p["budget_tile_rows"] == (16 << 20) // (1400 * 2)
+
+
+def test_dispatch_counts_start_at_zero():
+    A.reset_dispatch_counts()
+    assert A.dispatch_count("dense_bf16_d128") == 0
+    assert A.dispatch_count("no_such_path") == 0

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Tolerances (stated for bf16 inputs): max |O - O_ref| <= 2e-2 and
+max |lse - lse_ref| <= 1e-3; the same bar is applied to the fp32-input path.
+Rows where both lse values are -inf agree.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_attn_amd as A
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-3
+
+
+def announce(msg):
+    sys.stderr.write(f"[gpu-case] {msg}\n")
+    sys.stderr.flush()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _lse_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        d = np.where(same_inf, 0.0, np.abs(a - b))
+    return float(np.nan_to_num(d, nan=np.inf).max()) if d.size else 0.0
+
+
+def _o_err(a, b):
+    d = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    return float(np.nan_to_num(d, nan=np.inf).max()) if d.size else 0.0
+
+
+def run_dense(inp, *, causal, scale, poison=True, stream=None):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    B, H, Tq, _ = q.shape
+    out = torch.full((B, H, Tq, v.shape[-1]), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((B, H, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    A.dense(q, k, v, causal=causal, scale=scale, sinks=sk, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_dense_full(inp, *, causal, scale, label):
+    announce(f"dense {label} q{tuple(inp['q'].shape)} k{tuple(inp['k'].shape)} v{tuple(inp['v'].shape)} "
+             f"causal={causal} sinks={inp['sinks'] is not None}")
+    out, lse = run_dense(inp, causal=causal, scale=scale)
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=scale, causal=causal,
+                                    sinks=inp["sinks"])
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"{label}: max|dO|={eo:.3e} max|dlse|={el:.3e}"
+    return eo, el
+
+
+# ------------------------------------------------------------------ small shapes, full outputs
+HEAD_DIMS = [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]
+
+
+@pytest.mark.parametrize("dqk,dv", HEAD_DIMS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_bf16_head_dims(dqk, dv, causal):
+    # T = 200: several 64/128-row tiles and several key blocks, ragged in both
+    inp = synth.randn_dense(2, 4, 2, 200, 200, dqk, dv, dtype="bf16", sinks=False, seed=dqk + dv)
+    check_dense_full(inp, causal=causal, scale=1 / math.sqrt(dqk), label=f"bf16 d{dqk}/{dv}")
+
+
+@pytest.mark.parametrize("dqk,dv", HEAD_DIMS)
+def test_dense_bf16_sinks(dqk, dv):
+    inp = synth.randn_dense(1, 8, 2, 150, 150, dqk, dv, dtype="bf16", sinks=True, seed=7 + dqk)
+    check_dense_full(inp, causal=True, scale=1 / math.sqrt(dqk), label=f"sinks d{dqk}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_f32_split(d, causal):
+    inp = synth.randn_dense(1, 4, 1, 150, 150, d, d, dtype="f32", seed=11 + d)
+    check_dense_full(inp, causal=causal, scale=1 / math.sqrt(d), label=f"f32 d{d}")
+
+
+@pytest.mark.parametrize("g,Hkv,T", [(1, 3, 70), (4, 2, 5), (8, 1, 17), (64, 1, 3), (16, 2, 1)])
+def test_gqa_fold_packed_rows(g, Hkv, T):
+    """Small Tq: rows of several heads share one workgroup tile (folded view)."""
+    inp = synth.randn_dense(2, g * Hkv, Hkv, T, T, 128, 128, dtype="bf16", sinks=True, seed=100 + g)
+    check_dense_full(inp, causal=True, scale=1 / math.sqrt(128), label=f"fold g{g}")
+
+
+@pytest.mark.parametrize("Tq,Tk", [(1, 300), (37, 300), (300, 37), (130, 129), (64, 64)])
+@pytest.mark.parametrize("sinks", [False, True])
+def test_causal_bottom_right_unequal_lengths(Tq, Tk, sinks):
+    inp = synth.randn_dense(1, 8, 2, Tq, Tk, 128, 128, dtype="bf16", sinks=sinks, seed=Tq * 1000 + Tk)
+    check_dense_full(inp, causal=True, scale=1 / math.sqrt(128), label=f"Tq{Tq} Tk{Tk}")
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_no_keys(sinks):
+    inp = synth.randn_dense(1, 4, 2, 9, 0, 64, 64, dtype="bf16", sinks=sinks, seed=5)
+    announce(f"dense Tk=0 sinks={sinks}")
+    out, lse = run_dense(inp, causal=False, scale=0.125)
+    assert torch.all(out.float() == 0)
+    if sinks:
+        assert torch.allclose(lse.cpu(), inp["sinks"].repeat_interleave(1).view(1, 4, 1).expand(1, 4, 9))
+    else:
+        assert torch.all(torch.isneginf(lse))
+
+
+def test_no_queries_launches_nothing():
+    inp = synth.randn_dense(1, 4, 2, 0, 16, 64, 64, dtype="bf16", seed=6)
+    announce("dense Tq=0")
+    A.reset_dispatch_counts()
+    out, lse = A.dense(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and lse.numel() == 0
+    assert A.dispatch_count("dense_bf16_d64") == 0
+
+
+def test_strided_bshd_view():
+    """A BSHD tensor passed as a strided BHSD view gives the same result."""
+    inp = synth.randn_dense(2, 8, 2, 96, 96, 128, 128, dtype="bf16", seed=21)
+    announce("dense strided BSHD view")
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    assert qs.stride(-1) == 1 and not qs.is_contiguous()
+    o1, l1 = A.dense(q, k, v, causal=True)
+    o2, l2 = A.dense(qs, ks, vs, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_streams_default_and_side():
+    """The legacy NULL stream and a side stream both work (stream 0 is valid)."""
+    inp = synth.randn_dense(1, 4, 1, 128, 128, 64, 64, dtype="bf16", seed=31)
+    announce("dense on NULL stream and on a side stream")
+    o0, l0 = run_dense(inp, causal=True, scale=0.125, stream=torch.cuda.default_stream())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1, l1 = run_dense(inp, causal=True, scale=0.125, stream=s)
+    s.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+# ------------------------------------------------------------------ sparse, small
+@pytest.mark.parametrize("Hq,sinks", [(64, False), (64, True), (16, False)])
+def test_sparse_small(Hq, sinks):
+    Sq, N, topk = 7, 300, 100
+    inp = synth.randn_sparse(Sq, Hq, N, 512, topk, seed=40 + Hq, sinks=sinks)
+    idx = inp["idx"].clone()
+    idx[0, 5] = -1           # skipped
+    idx[1, 0] = N + 5        # out of range: skipped
+    idx[2, 7] = idx[2, 8]    # duplicate: counted twice
+    idx[3, :] = -1           # a query with no valid key
+    announce(f"sparse Sq={Sq} Hq={Hq} N={N} topk={topk} sinks={sinks}")
+    q, kv, ix = inp["q"].cuda(), inp["kv"].cuda(), idx.cuda()
+    sk = inp["sinks"].cuda() if sinks else None
+    out, lse = A.sparse_topk(q, kv, ix, d_v=512, sinks=sk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], idx, d_v=512, scale=1 / math.sqrt(512),
+                                          sinks=inp["sinks"])
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"sparse: max|dO|={eo:.3e} max|dlse|={el:.3e}"
+
+
+# ------------------------------------------------------------------ the five workloads
+def _sample_rows(B, H, Tq, rng, n_rand=24):
+    ts = sorted({0, 1, 2, 31, 32, 63, 64, 127, 128, 129, Tq // 2, Tq - 129, Tq - 2, Tq - 1}
+                | set(rng.integers(0, Tq, n_rand).tolist()))
+    ts = [t for t in ts if 0 <= t < Tq]
+    hs = sorted({0, H - 1, H // 2} | set(rng.integers(0, H, 3).tolist()))
+    return [(b, h, t) for b in range(B) for h in hs for t in ts]
+
+
+def test_workload_tiny_full():
+    s = synth.spec(1)
+    inp = synth.make(1)
+    check_dense_full(inp, causal=True, scale=s.scale, label="tiny (fp32, B1 H4 Hkv1 T128 d64)")
+
+
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_workload_dense_sampled(n):
+    s = synth.spec(n)
+    inp = synth.make(n)
+    announce(f"workload {s.name}: B{s.B} H{s.H} Hkv{s.Hkv} T{s.Tq} d{s.d_qk}/{s.d_v} sinks={s.sinks}")
+    A.reset_dispatch_counts()
+    out, lse = run_dense(inp, causal=True, scale=s.scale)
+    path = A.plan_dense(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v, sinks=s.sinks)["path"]
+    assert A.dispatch_count(path) == 1
+    # every element written (outputs were poisoned with NaN)
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
+    rows = _sample_rows(s.B, s.H, s.Tq, np.random.default_rng(n))
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=s.scale, causal=True,
+                                    sinks=inp["sinks"], rows=rows)
+    bi, hi, ti = (torch.tensor([r[i] for r in rows]) for i in range(3))
+    go = _np(out[bi, hi, ti])
+    gl = _np(lse[bi, hi, ti])
+    eo, el = _o_err(go, ro), _lse_err(gl, rl)
+    announce(f"workload {s.name}: {len(rows)} sampled rows, max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+    # run-to-run bitwise determinism
+    out2, lse2 = run_dense(inp, causal=True, scale=s.scale)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_workload_sparse_sampled():
+    s = synth.spec(5)
+    inp = synth.make(5)
+    announce(f"workload sparse: Sq{s.Sq} Hq{s.Hq} N{s.N} d{s.d_qk} topk{s.topk}")
+    q, kv, ix = inp["q"].cuda(), inp["kv"].cuda(), inp["idx"].cuda()
+    out = torch.full((s.Sq, s.Hq, s.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((s.Sq, s.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    A.reset_dispatch_counts()
+    A.sparse_topk(q, kv, ix, d_v=s.d_v, scale=s.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert A.dispatch_count("sparse_bf16_d512") == 1 and A.dispatch_count("dense_bf16_d512") == 0
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
+    rng = np.random.default_rng(5)
+    qs = sorted({0, 1, s.Sq - 1} | set(rng.integers(0, s.Sq, 13).tolist()))
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], inp["idx"], d_v=s.d_v, scale=s.scale,
+                                          queries=qs)
+    go, gl = _np(out[qs]), _np(lse[qs])
+    eo, el = _o_err(go, ro), _lse_err(gl, rl)
+    announce(f"workload sparse: {len(qs)} sampled queries, max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    A.sparse_topk(q, kv, ix, d_v=s.d_v, scale=s.scale, out=out2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
