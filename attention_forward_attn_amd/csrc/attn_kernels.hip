@@ -60,6 +60,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -638,6 +639,482 @@ attn_fwd_kernel(const KernelParams p) {
   }
 }
 
+// ===========================================================================
+// bf16 kernel family with direct-to-LDS staging.
+//
+// K and V tiles travel from global memory straight into LDS with
+// global_load_lds_dwordx4 (16 bytes per lane, no staging registers, no LDS
+// store instructions). A wave instruction fills 64 consecutive 16-byte LDS
+// slots, so the bank-conflict swizzle is applied on the global side: the lane
+// that owns slot (row r, physical chunk p) fetches logical chunk p ^ swz(r).
+// V^T operands of the PV product are read from the row-major V tile with
+// ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements across
+// each 16-lane group; no transposed copy of V exists. In the sparse path the
+// gathered pool rows form one tile that serves both products (V == K).
+//
+// The direct-to-LDS loads are issued from inline asm so that the compiler
+// does not insert a conservative vmcnt(0) before every LDS read; the kernel
+// waits for exactly the loads of the tile it is about to use and synchronises
+// with a plain s_barrier. With NSTAGE = 3 the loads of tile i+2 are in flight
+// while tile i is multiplied and one barrier per tile suffices.
+//
+// Online softmax with a lazy rescale: the running row max only moves when a
+// new score exceeds it by more than kRescaleLog2 (in log2 units), so the
+// output accumulator is rescaled on the first key blocks and almost never
+// afterwards; exp2 arguments stay <= kRescaleLog2, far from fp32 overflow.
+// ===========================================================================
+
+constexpr float kRescaleLog2 = 8.f;
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// vmcnt wait with a wave-uniform count (0..31)
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    case 21: wait_vmcnt<21>(); break;
+    case 22: wait_vmcnt<22>(); break;
+    case 23: wait_vmcnt<23>(); break;
+    case 24: wait_vmcnt<24>(); break;
+    case 25: wait_vmcnt<25>(); break;
+    case 26: wait_vmcnt<26>(); break;
+    case 27: wait_vmcnt<27>(); break;
+    case 28: wait_vmcnt<28>(); break;
+    case 29: wait_vmcnt<29>(); break;
+    case 30: wait_vmcnt<30>(); break;
+    default: wait_vmcnt<31>(); break;
+  }
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// chunk swizzle of a tile row: rows r..r+7 send one logical chunk to 8 bank
+// groups; rows 4k..4k+3 send an aligned chunk pair to 4 distinct pairs
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+struct DCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int NQG = NW / DS;
+  static constexpr int BM = NQG * 32;
+  static constexpr int DQW = DQK / DS;
+  static constexpr int DVW = DV / DS;
+  static constexpr int KS = DQW / 16;
+  static constexpr int MT = BN / 32;
+  static constexpr int DT = DVW / 32;
+  static constexpr int PKS = BN / 16;
+  static constexpr int CPRK = DQK / 8;
+  static constexpr int CPRV = DV / 8;
+  static constexpr int VLD = SPARSE ? DQK : DV;  // row length of the tile V is read from
+  static constexpr int K_ELEMS = BN * DQK;
+  static constexpr int V_ELEMS = SPARSE ? 0 : BN * DV;
+  static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int NIK = BN * CPRK / 64;     // wave instructions per K tile
+  static constexpr int NIV = SPARSE ? 0 : BN * CPRV / 64;
+  static constexpr int NIK_W = (NIK + NW - 1) / NW;  // per wave (the first NIK % NW waves carry one more)
+  static constexpr int NIV_W = (NIV + NW - 1) / NW;
+  static constexpr int SX_BYTES = (DS > 1) ? NW * MT * 16 * 64 * 4 : 0;
+  static constexpr int IDX_CAP = SPARSE ? 4096 : 0;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_ELEMS * 2 + SX_BYTES + IDX_CAP * 4;
+  static_assert(NIK_W + NIV_W <= 31, "vmcnt wait range");
+  static_assert(CPRK >= 8 && (SPARSE || CPRV >= 8), "swizzle needs 8 chunks per row");
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
+  static_assert(!SPARSE || (IDX_CAP % BN == 0), "index segments hold whole key blocks");
+  static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0, "head dims must tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+__global__ void __launch_bounds__(NW * 64)
+attn_fwd_dma_kernel(const KernelParams p) {
+  using C = DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  bf16_t* const tiles = reinterpret_cast<bf16_t*>(smem);
+  float* const sx = reinterpret_cast<float*>(smem + NSTAGE * C::STAGE_ELEMS * 2);
+  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + NSTAGE * C::STAGE_ELEMS * 2 + C::SX_BYTES);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int qg = wave / DS, dsi = wave % DS;
+
+  // ---------------------------------------------------------------- tile of this workgroup
+  int b = 0, kvh = 0, f0 = 0, nrows = 0, t_lo = 0, t_hi = 0, sq = 0;
+  if constexpr (SPARSE) {
+    sq = blockIdx.x;
+    nrows = p.H;
+  } else {
+    const int tile = blockIdx.x;
+    if (p.aligned) {
+      const int per_tb = p.n_groups * p.g;
+      const int tb = (p.tiles_per_head - 1) - tile / per_tb;  // longest causal blocks first
+      const int rest = tile % per_tb;
+      const int grp = rest / p.g, hl = rest % p.g;
+      b = grp / p.Hkv;
+      kvh = grp % p.Hkv;
+      const int t0 = tb * C::BM;
+      f0 = hl * p.Tq + t0;
+      nrows = min(C::BM, p.Tq - t0);
+      t_lo = t0;
+      t_hi = t0 + nrows - 1;
+    } else {
+      const int grp = tile / p.tiles_per_group;
+      f0 = (tile % p.tiles_per_group) * C::BM;
+      nrows = min(C::BM, p.g * p.Tq - f0);
+      b = grp / p.Hkv;
+      kvh = grp % p.Hkv;
+      const int tf = f0 % p.Tq;
+      if (nrows >= p.Tq || tf + nrows > p.Tq) {
+        t_lo = 0;
+        t_hi = p.Tq - 1;
+      } else {
+        t_lo = tf;
+        t_hi = tf + nrows - 1;
+      }
+    }
+  }
+  int kend = p.Tk, kfull = p.Tk;
+  if (!SPARSE && p.causal) {
+    const int off = p.Tk - p.Tq;
+    kend = min(p.Tk, max(0, t_hi + off + 1));
+    kfull = min(p.Tk, max(0, t_lo + off + 1));
+  }
+
+  // ---------------------------------------------------------------- the query row of this lane
+  const int r = qg * 32 + lq;
+  const bool row_ok = r < nrows;
+  const int rr = row_ok ? r : 0;
+  int row_lim, row_h;
+  int64_t q_off, o_off, l_off;
+  if constexpr (SPARSE) {
+    row_h = rr;
+    row_lim = p.Tk - 1;
+    q_off = (int64_t)sq * p.q_sb + (int64_t)rr * p.q_sh;
+    o_off = (int64_t)sq * p.o_sb + (int64_t)rr * p.o_sh;
+    l_off = (int64_t)sq * p.H + rr;
+  } else {
+    const int f = f0 + rr;
+    row_h = kvh * p.g + f / p.Tq;
+    const int t = f % p.Tq;
+    row_lim = p.causal ? min(p.Tk - 1, t + p.Tk - p.Tq) : p.Tk - 1;
+    q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (int64_t)t * p.q_st;
+    o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (int64_t)t * p.o_st;
+    l_off = ((int64_t)b * p.H + row_h) * p.Tq + t;
+  }
+
+  // ---------------------------------------------------------------- Q fragments (B operand of S^T)
+  bf16x8 qf[C::KS];
+  {
+    const bf16_t* qb = reinterpret_cast<const bf16_t*>(p.q) + q_off;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok) w = *reinterpret_cast<const u32x4*>(qb + dsi * C::DQW + s * 16 + lh * 8);
+      qf[s] = as_bf16x8(w);
+    }
+  }
+
+  const bf16_t* kbase;
+  const bf16_t* vbase;
+  if constexpr (SPARSE) {
+    kbase = reinterpret_cast<const bf16_t*>(p.k);
+    vbase = kbase;
+  } else {
+    kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  }
+
+  // ---------------------------------------------------------------- loads of one key block
+  // blk is the block index inside the current segment (sparse) or the key range (dense)
+  auto issue = [&](int blk, int st) {
+    bf16_t* Kb = tiles + st * C::STAGE_ELEMS;
+    const int key0 = blk * BN;
+#pragma unroll
+    for (int m = 0; m < C::NIK_W; ++m) {
+      const int j = wave + NW * m;
+      if (C::NIK % NW != 0 && j >= C::NIK) break;
+      const int s = 64 * j + lane;
+      const int rw = s / C::CPRK, c = (s % C::CPRK) ^ swz(rw);
+      const bf16_t* src;
+      if constexpr (SPARSE) {
+        const int ix = sidx[key0 + rw];
+        const bool ok = ix >= 0 && ix < p.npool;
+        src = kbase + (int64_t)(ok ? ix : 0) * p.k_st + c * 8;
+      } else {
+        const int kk = min(key0 + rw, kend - 1);
+        src = kbase + (int64_t)kk * p.k_st + c * 8;
+      }
+      dma16(src, lds_u32(Kb + 64 * j * 8));
+    }
+    if constexpr (!SPARSE) {
+      bf16_t* Vb = Kb + C::K_ELEMS;
+#pragma unroll
+      for (int m = 0; m < C::NIV_W; ++m) {
+        const int j = wave + NW * m;
+        if (C::NIV % NW != 0 && j >= C::NIV) break;
+        const int s = 64 * j + lane;
+        const int rw = s / C::CPRV, c = (s % C::CPRV) ^ swz(rw);
+        const int kk = min(key0 + rw, kend - 1);
+        dma16(vbase + (int64_t)kk * p.v_st + c * 8, lds_u32(Vb + 64 * j * 8));
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- state
+  f32x16 acc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // per-lane parts of the LDS addresses
+  const int kswz = swz(lq);                                   // rows mt*32 + lq
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = (vg >> 1) * 4 + (vi >> 2);                 // + 16*ks (+8 for the second read)
+  const int vswz = swz(vrow);
+  const int vcol0 = dsi * C::DVW + (vg & 1) * 16 + 4 * (vi & 3);  // + 32*dt
+
+  auto compute = [&](int blk, const bf16_t* Kb) {
+    const bf16_t* Vb = SPARSE ? Kb : Kb + C::K_ELEMS;
+    const int key0 = blk * BN;
+    // ---- S^T = K Q^T over this wave's d_qk columns
+    f32x16 S[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const bf16_t* krow = Kb + (mt * 32 + lq) * DQK;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int c = ((dsi * C::DQW + s * 16) >> 3) + lh;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ((c ^ kswz) << 3));
+        S[mt] = mfma32(a, qf[s], S[mt]);
+      }
+    }
+    // ---- partial scores of the DS waves sharing these rows
+    if constexpr (DS > 1) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(sx + (((wave * C::MT + mt) * 4 + g4) * 64 + lane) * 4) =
+              f32x4{S[mt][g4 * 4], S[mt][g4 * 4 + 1], S[mt][g4 * 4 + 2], S[mt][g4 * 4 + 3]};
+      lds_barrier();
+#pragma unroll
+      for (int o = 1; o < DS; ++o) {
+        const int w2 = qg * DS + (dsi + o) % DS;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sx + (((w2 * C::MT + mt) * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[mt][g4 * 4 + e] += v[e];
+          }
+      }
+    }
+    // ---- masks
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int4 ix = *reinterpret_cast<const int4*>(sidx + key0 + mt * 32 + g4 * 8 + lh * 4);
+          const int v4[4] = {ix.x, ix.y, ix.z, ix.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v4[e] < 0 || v4[e] >= p.npool) S[mt][g4 * 4 + e] = -INFINITY;
+        }
+    } else {
+      if (key0 + BN > kfull) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + mt * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
+            if (key > row_lim) S[mt][i] = -INFINITY;
+          }
+      }
+    }
+    // ---- online softmax with a lazy rescale
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mt][i]);
+    mx = fmaxf(mx, other_half(mx));
+    const float mnew = fmaxf(m_run, mx);
+    const bool grow = (mnew - m_run) * p.c > kRescaleLog2;  // false when both are -inf
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mnew) * p.c) : 1.f;
+      if (grow) m_run = mnew;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -mc));
+        S[mt][i] = e;
+        rs += e;
+      }
+    l_run += rs;
+    bf16x8 pb[C::PKS];
+#pragma unroll
+    for (int ks = 0; ks < C::PKS; ++ks) {
+      const int mt = ks >> 1, base = (ks & 1) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(S[mt][base + 2 * e], S[mt][base + 2 * e + 1]);
+      pb[ks] = as_bf16x8(w);
+    }
+    // ---- O^T += V^T P^T, V^T fragments by transposed LDS reads
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int col = vcol0 + dt * 32;
+      const int choff = (((col >> 3) ^ vswz) << 3) + (col & 7);
+#pragma unroll
+      for (int ks = 0; ks < C::PKS; ++ks) {
+        const bf16_t* p0 = Vb + (ks * 16 + vrow) * C::VLD + choff;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + 8 * C::VLD));
+        const u32x4 w = {(uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
+                         (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
+                         (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
+                         (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16)};
+        acc[dt] = mfma32(as_bf16x8(w), pb[ks], acc[dt]);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- key loop
+  // direct-to-LDS loads this wave issues per key block
+  const int my_loads = C::NIK / NW + (wave < C::NIK % NW ? 1 : 0) + C::NIV / NW + (wave < C::NIV % NW ? 1 : 0);
+  const int nseg = SPARSE ? (p.Tk + C::IDX_CAP - 1) / max(C::IDX_CAP, 1) : 1;
+  for (int sg = 0; sg < nseg; ++sg) {
+    int nb;
+    if constexpr (SPARSE) {
+      const int seg0 = sg * C::IDX_CAP;
+      const int segn = min(C::IDX_CAP, p.Tk - seg0);
+      nb = (segn + BN - 1) / BN;
+      if (sg > 0) block_barrier();  // everyone is done with the previous segment's indices
+      const int32_t* irow = p.idx + (int64_t)sq * p.idx_ss + seg0;
+      for (int e = tid; e < nb * BN; e += C::NT) sidx[e] = (e < segn) ? irow[e] : -1;
+      lds_barrier();
+    } else {
+      nb = (kend + BN - 1) / BN;
+    }
+    if (nb > 0) issue(0, 0);
+    if (NSTAGE == 3 && nb > 1) issue(1, 1);
+    for (int blk = 0; blk < nb; ++blk) {
+      if (NSTAGE == 3 && blk + 1 < nb)
+        wait_vmcnt_dyn(my_loads);
+      else
+        wait_vmcnt<0>();
+      block_barrier();
+      if (NSTAGE == 3) {
+        if (blk + 2 < nb) issue(blk + 2, (blk + 2) % 3);
+      } else {
+        if (blk + 1 < nb) issue(blk + 1, (blk + 1) & 1);
+      }
+      compute(blk, tiles + (blk % NSTAGE) * C::STAGE_ELEMS);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const float lt = l_run + other_half(l_run);
+  const float ms = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
+  float inv, lse;
+  if (p.sinks != nullptr) {
+    const float sk = p.sinks[row_h];
+    const float M = fmaxf(ms, sk);
+    if (M == -INFINITY) {
+      inv = 0.f;
+      lse = -INFINITY;
+    } else {
+      const float fac = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - M) * kLog2e);
+      const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - M) * kLog2e);
+      const float den = lt * fac + es;
+      inv = den > 0.f ? fac / den : 0.f;
+      lse = den > 0.f ? M + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+    }
+  } else {
+    inv = lt > 0.f ? 1.f / lt : 0.f;
+    lse = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
+  }
+  if (row_ok) {
+    bf16_t* ob = reinterpret_cast<bf16_t*>(p.out) + o_off;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dsi * C::DVW + dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(ob + d) =
+            u32x2{pack_bf16x2(acc[dt][g4 * 4] * inv, acc[dt][g4 * 4 + 1] * inv),
+                  pack_bf16x2(acc[dt][g4 * 4 + 2] * inv, acc[dt][g4 * 4 + 3] * inv)};
+      }
+    if (lh == 0 && dsi == 0) p.lse[l_off] = lse;
+  }
+}
+
+template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+int launch_dma(const KernelParams& p, void* stream) {
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>), dim3(p.n_tiles), dim3(NW * 64), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
+  return (int)hipGetLastError();
+}
+
+#define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NSTAGE, SPARSE)                                                  \
+  KernelConfig {                                                                                             \
+    NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>::BM, BN, NW,                         \
+        DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NSTAGE, SPARSE> \
+  }
+
 template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
 int launch(const KernelParams& p, void* stream) {
   hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, QT, DS, NW, BN, F32, SPARSE>), dim3(p.n_tiles), dim3(NW * 64), 0,
@@ -652,14 +1129,14 @@ int launch(const KernelParams& p, void* stream) {
   }
 
 const KernelConfig kTable[] = {
-    CFG_ENTRY("dense_bf16_d64", 0, 64, 64, 1, 1, 4, 64, false, false),
-    CFG_ENTRY("dense_bf16_d128", 0, 128, 128, 1, 1, 4, 64, false, false),
-    CFG_ENTRY("dense_bf16_d192_v128", 0, 192, 128, 1, 1, 4, 64, false, false),
-    CFG_ENTRY("dense_bf16_d256", 0, 256, 256, 1, 1, 4, 32, false, false),
-    CFG_ENTRY("dense_bf16_d512", 0, 512, 512, 1, 2, 4, 32, false, false),
+    DMA_ENTRY("dense_bf16_d64", 64, 64, 1, 8, 64, 3, false),
+    DMA_ENTRY("dense_bf16_d128", 128, 128, 1, 8, 64, 3, false),
+    DMA_ENTRY("dense_bf16_d192_v128", 192, 128, 1, 8, 32, 3, false),
+    DMA_ENTRY("dense_bf16_d256", 256, 256, 2, 4, 32, 3, false),
+    DMA_ENTRY("dense_bf16_d512", 512, 512, 2, 4, 32, 2, false),
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
     CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
-    CFG_ENTRY("sparse_bf16_d512", 0, 512, 512, 1, 2, 4, 32, false, true),
+    DMA_ENTRY("sparse_bf16_d512", 512, 512, 2, 4, 32, 3, true),
 };
 
 }  // namespace
