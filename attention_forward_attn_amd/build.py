@@ -34,12 +34,13 @@ def sources():
     return [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "api.cpp")]
 
 
-def build(verbose: bool = False, resource_report: bool = False) -> str:
+def build(verbose: bool = False, resource_report: bool = False, defines=(), out: str = LIB) -> str:
     objs = []
     os.makedirs(os.path.join(ROOT, "_build"), exist_ok=True)
     for src in sources():
-        obj = os.path.join(ROOT, "_build", os.path.basename(src) + ".o")
-        cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+        tag = str(abs(hash(tuple(defines)))) if defines else ""
+        obj = os.path.join(ROOT, "_build", os.path.basename(src) + tag + ".o")
+        cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + ["-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", src, "-o", obj]
         if resource_report and src.endswith(".hip"):
@@ -47,21 +48,21 @@ def build(verbose: bool = False, resource_report: bool = False) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
-        out = (r.stdout or "") + (r.stderr or "")
-        lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+        text = (r.stdout or "") + (r.stderr or "")
+        lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
         if r.returncode != 0:
             sys.stderr.write("\n".join(lines) + "\n")
             raise RuntimeError(f"hipcc failed on {src}")
         if verbose or resource_report:
             print("\n".join(lines))
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

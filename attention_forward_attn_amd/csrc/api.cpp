@@ -109,6 +109,8 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
     if (s < 0 || s % vec != 0)
       return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and keep rows 16-byte aligned (multiple of %lld elements)",
                   (long long)vec);
+  if (a->k_st >= (1 << 24) || a->v_st >= (1 << 24))
+    return fail(ATTN_INVALID_ARGUMENT, "k/v token strides must be below 2^24 elements");
   if (a->Tq > 1 && a->q_st < a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "q token stride smaller than d_qk");
   if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v))
     return fail(ATTN_INVALID_ARGUMENT, "k/v token stride smaller than the head dim");

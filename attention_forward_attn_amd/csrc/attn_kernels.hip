@@ -72,9 +72,12 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // value held by lane l ^ 32
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
 
+typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16_t a = (bf16_t)lo, b = (bf16_t)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -666,6 +669,15 @@ attn_fwd_kernel(const KernelParams p) {
 
 constexpr float kRescaleLog2 = 8.f;
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+#ifndef ATTN_LDS_PREFETCH
+#define ATTN_LDS_PREFETCH 4
+#endif
+constexpr int kPrefetch = ATTN_LDS_PREFETCH;  // MFMA operands read from LDS ahead of use
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -723,11 +735,24 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// chunk swizzle of a tile row: rows r..r+7 send one logical chunk to 8 bank
-// groups; rows 4k..4k+3 send an aligned chunk pair to 4 distinct pairs
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk swizzle of a tile row with CPR 16-byte chunks. LDS serves 256 bytes
+// (16 chunks, 64 banks) per cycle. Rows whose length is a multiple of 256
+// bytes start on the same bank, so the swizzle is a 4-bit XOR: 16 consecutive
+// rows send one logical chunk to 16 distinct bank groups (A-operand reads of
+// K), and rows 4k..4k+3 send an aligned 4-chunk group to 4 distinct groups
+// (transposed V reads). Rows of 128 + 256n bytes alternate between the two
+// halves of the banks, so a 3-bit XOR inside aligned 8-chunk groups gives the
+// same two properties and keeps every chunk inside the row.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR % 8 == 0, "rows are whole 8-chunk groups");
+  if constexpr (CPR % 16 == 0)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
-template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG>
 struct DCfg {
   static constexpr int NT = NW * 64;
   static constexpr int NQG = NW / DS;
@@ -743,35 +768,46 @@ struct DCfg {
   static constexpr int VLD = SPARSE ? DQK : DV;  // row length of the tile V is read from
   static constexpr int K_ELEMS = BN * DQK;
   static constexpr int V_ELEMS = SPARSE ? 0 : BN * DV;
-  static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
+  // Two wave groups (one wave of each per SIMD with 8 waves) or one.
+  static constexpr bool PP = PINGPONG;
+  // With two groups, K block j is read in the two halves of key step j and
+  // V block j in the two halves of step j+1; with one group both are read in
+  // step j. K block j+KD (V block j+VD) is loaded while step j runs, into the
+  // ring slot of a block nobody reads any more.
+  static constexpr int KD = (PP && SPARSE) ? NBUF - 2 : NBUF - 1;
+  static constexpr int VD = PP ? NBUF - 2 : NBUF - 1;
   static constexpr int NIK = BN * CPRK / 64;     // wave instructions per K tile
   static constexpr int NIV = SPARSE ? 0 : BN * CPRV / 64;
-  static constexpr int NIK_W = (NIK + NW - 1) / NW;  // per wave (the first NIK % NW waves carry one more)
-  static constexpr int NIV_W = (NIV + NW - 1) / NW;
   static constexpr int SX_BYTES = (DS > 1) ? NW * MT * 16 * 64 * 4 : 0;
   static constexpr int IDX_CAP = SPARSE ? 4096 : 0;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_ELEMS * 2 + SX_BYTES + IDX_CAP * 4;
-  static_assert(NIK_W + NIV_W <= 31, "vmcnt wait range");
+  static constexpr int KRING_BYTES = NBUF * K_ELEMS * 2;
+  static constexpr int VRING_BYTES = NBUF * V_ELEMS * 2;
+  static constexpr int LDS_BYTES = KRING_BYTES + VRING_BYTES + SX_BYTES + IDX_CAP * 4;
+  static_assert(KD >= 1, "at least one key step of prefetch");
+  static constexpr int NLOADW = PP ? NW / 2 : NW;  // waves sharing one tile's loads
+  static_assert((KD - 1) * ((NIK + NLOADW - 1) / NLOADW + (NIV + NLOADW - 1) / NLOADW) <= 31, "vmcnt wait range");
   static_assert(CPRK >= 8 && (SPARSE || CPRV >= 8), "swizzle needs 8 chunks per row");
-  static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
   static_assert(!SPARSE || (IDX_CAP % BN == 0), "index segments hold whole key blocks");
   static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0, "head dims must tile");
+  static_assert(!PP || (NW / 2) % DS == 0, "a query group stays inside one wave group");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_dma_kernel(const KernelParams p) {
-  using C = DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>;
+  using C = DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
-  bf16_t* const tiles = reinterpret_cast<bf16_t*>(smem);
-  float* const sx = reinterpret_cast<float*>(smem + NSTAGE * C::STAGE_ELEMS * 2);
-  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + NSTAGE * C::STAGE_ELEMS * 2 + C::SX_BYTES);
+  bf16_t* const kring = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* const vring = reinterpret_cast<bf16_t*>(smem + C::KRING_BYTES);
+  float* const sx = reinterpret_cast<float*>(smem + C::KRING_BYTES + C::VRING_BYTES);
+  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + C::KRING_BYTES + C::VRING_BYTES + C::SX_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, lh = lane >> 5;
   const int qg = wave / DS, dsi = wave % DS;
+  const int wgrp = C::PP ? (wave >= NW / 2 ? 1 : 0) : 0;  // wave group
 
   // ---------------------------------------------------------------- tile of this workgroup
   int b = 0, kvh = 0, f0 = 0, nrows = 0, t_lo = 0, t_hi = 0, sq = 0;
@@ -847,6 +883,11 @@ attn_fwd_dma_kernel(const KernelParams p) {
       if (row_ok) w = *reinterpret_cast<const u32x4*>(qb + dsi * C::DQW + s * 16 + lh * 8);
       qf[s] = as_bf16x8(w);
     }
+    // use the fragments here so that the compiler waits for these loads before
+    // the key loop, not inside it (where the wait would also drain the tile
+    // loads in flight)
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) asm volatile("" ::"v"(qf[s]));
   }
 
   const bf16_t* kbase;
@@ -861,36 +902,84 @@ attn_fwd_dma_kernel(const KernelParams p) {
 
   // ---------------------------------------------------------------- loads of one key block
   // blk is the block index inside the current segment (sparse) or the key range (dense)
-  auto issue = [&](int blk, int st) {
-    bf16_t* Kb = tiles + st * C::STAGE_ELEMS;
+  constexpr int NLW_ = C::NLOADW;  // waves that share the loads of one tile
+  constexpr int NIK_L = (C::NIK + NLW_ - 1) / NLW_, NIV_L = (C::NIV + NLW_ - 1) / NLW_;
+  const int lw_ = wave % NLW_;
+  // per-lane element offsets of the rows and chunks a wave loads, relative
+  // to the first key of the block (the swizzle is applied on the global side);
+  // 32-bit because the host limits key-row strides to 2^24 elements
+  auto koffg_at = [&](int m) -> int32_t {
+    const int sl = 64 * (lw_ + NLW_ * m) + lane;
+    const int rw = sl / C::CPRK, c = (sl % C::CPRK) ^ swz<C::CPRK>(rw);
+    return SPARSE ? c * 8 : rw * (int32_t)p.k_st + c * 8;
+  };
+  auto voffg_at = [&](int m) -> int32_t {
+    const int sl = 64 * (lw_ + NLW_ * m) + lane;
+    const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
+    return rw * (int32_t)p.v_st + c * 8;
+  };
+  // narrow slices keep the offsets in registers; wide ones (d_qk/DS >= 256)
+  // recompute them, which is a few integer ops per load
+  constexpr bool KEEP_OFFS = C::DQW < 256;
+  int32_t koffg[KEEP_OFFS ? NIK_L : 1], voffg[(KEEP_OFFS && NIV_L > 0) ? NIV_L : 1];
+  if constexpr (KEEP_OFFS) {
+#pragma unroll
+    for (int m = 0; m < NIK_L; ++m) koffg[m] = koffg_at(m);
+#pragma unroll
+    for (int m = 0; m < NIV_L; ++m) voffg[m] = voffg_at(m);
+  }
+  auto issueK = [&](int blk) {
+    bf16_t* Kb = kring + (blk % NBUF) * C::K_ELEMS;
     const int key0 = blk * BN;
+    if constexpr (SPARSE) {
+      // one LDS read per lane for the block's indices; each wave instruction
+      // loads one pool row (64 chunks) whose index is broadcast by readlane
+      static_assert(C::CPRK == 64 && BN <= 64, "one gathered row per wave instruction");
+      const int myix = sidx[key0 + (lane & (BN - 1))];
 #pragma unroll
-    for (int m = 0; m < C::NIK_W; ++m) {
-      const int j = wave + NW * m;
-      if (C::NIK % NW != 0 && j >= C::NIK) break;
-      const int s = 64 * j + lane;
-      const int rw = s / C::CPRK, c = (s % C::CPRK) ^ swz(rw);
-      const bf16_t* src;
-      if constexpr (SPARSE) {
-        const int ix = sidx[key0 + rw];
-        const bool ok = ix >= 0 && ix < p.npool;
-        src = kbase + (int64_t)(ok ? ix : 0) * p.k_st + c * 8;
-      } else {
-        const int kk = min(key0 + rw, kend - 1);
-        src = kbase + (int64_t)kk * p.k_st + c * 8;
+      for (int m = 0; m < NIK_L; ++m) {
+        const int j = lw_ + NLW_ * m;
+        if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
+        const int ix = __builtin_amdgcn_readlane(myix, j);
+        const int row = (ix >= 0 && ix < p.npool) ? ix : 0;
+        dma16(kbase + (int64_t)row * p.k_st + (KEEP_OFFS ? koffg[m] : koffg_at(m)), lds_u32(Kb + 64 * j * 8));
       }
-      dma16(src, lds_u32(Kb + 64 * j * 8));
-    }
-    if constexpr (!SPARSE) {
-      bf16_t* Vb = Kb + C::K_ELEMS;
+    } else {
+      const bool tail = key0 + BN > kend;  // rows past kend are clamped onto row kend-1
 #pragma unroll
-      for (int m = 0; m < C::NIV_W; ++m) {
-        const int j = wave + NW * m;
-        if (C::NIV % NW != 0 && j >= C::NIV) break;
-        const int s = 64 * j + lane;
-        const int rw = s / C::CPRV, c = (s % C::CPRV) ^ swz(rw);
-        const int kk = min(key0 + rw, kend - 1);
-        dma16(vbase + (int64_t)kk * p.v_st + c * 8, lds_u32(Vb + 64 * j * 8));
+      for (int m = 0; m < NIK_L; ++m) {
+        const int j = lw_ + NLW_ * m;
+        if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
+        const bf16_t* src;
+        if (!tail) {
+          src = kbase + (int64_t)key0 * p.k_st + (KEEP_OFFS ? koffg[m] : koffg_at(m));
+        } else {
+          const int sl = 64 * j + lane;
+          const int rw = sl / C::CPRK, c = (sl % C::CPRK) ^ swz<C::CPRK>(rw);
+          src = kbase + (int64_t)min(key0 + rw, kend - 1) * p.k_st + c * 8;
+        }
+        dma16(src, lds_u32(Kb + 64 * j * 8));
+      }
+    }
+  };
+  auto issueV = [&](int blk) {
+    if constexpr (!SPARSE) {
+      bf16_t* Vb = vring + (blk % NBUF) * C::V_ELEMS;
+      const int key0 = blk * BN;
+      const bool tail = key0 + BN > kend;
+#pragma unroll
+      for (int m = 0; m < NIV_L; ++m) {
+        const int j = lw_ + NLW_ * m;
+        if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
+        const bf16_t* src;
+        if (!tail) {
+          src = vbase + (int64_t)key0 * p.v_st + (KEEP_OFFS ? voffg[m] : voffg_at(m));
+        } else {
+          const int sl = 64 * j + lane;
+          const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
+          src = vbase + (int64_t)min(key0 + rw, kend - 1) * p.v_st + c * 8;
+        }
+        dma16(src, lds_u32(Vb + 64 * j * 8));
       }
     }
   };
@@ -903,41 +992,114 @@ attn_fwd_dma_kernel(const KernelParams p) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // per-lane parts of the LDS addresses
-  const int kswz = swz(lq);                                   // rows mt*32 + lq
-  const int vg = lane >> 4, vi = lane & 15;
-  const int vrow = (vg >> 1) * 4 + (vi >> 2);                 // + 16*ks (+8 for the second read)
-  const int vswz = swz(vrow);
-  const int vcol0 = dsi * C::DVW + (vg & 1) * 16 + 4 * (vi & 3);  // + 32*dt
-
-  auto compute = [&](int blk, const bf16_t* Kb) {
-    const bf16_t* Vb = SPARSE ? Kb : Kb + C::K_ELEMS;
-    const int key0 = blk * BN;
-    // ---- S^T = K Q^T over this wave's d_qk columns
-    f32x16 S[C::MT];
+  // per-lane LDS offsets (elements) inside a stage; the swizzle depends on the
+  // row modulo 16 only, so the mt (32 rows) and ks (16 rows) steps are
+  // compile-time offsets
+  constexpr int CPRVT = SPARSE ? C::CPRK : C::CPRV;  // chunks per row of the tile V is read from
+  // The XOR swizzle only touches the low 4 chunk bits, so the offsets repeat
+  // every 8 K steps (16 chunks) and every 4 output tiles (16 chunks) up to a
+  // compile-time shift of 128 elements: keep 8 + 8 per-lane offsets.
+  constexpr int NKO = C::KS < 8 ? C::KS : 8;
+  constexpr int NVO = C::DT < 4 ? C::DT : 4;
+  int koff[NKO];
+  {
+    const int sw = swz<C::CPRK>(lq);
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
+    for (int s = 0; s < NKO; ++s)
+      koff[s] = lq * DQK + (((((dsi * C::DQW + s * 16) >> 3) + lh) ^ sw) << 3);
+  }
+  int voff[NVO][2];
+  {
+    const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = (vg >> 1) * 4 + (vi >> 2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
+    for (int dt = 0; dt < NVO; ++dt)
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      const bf16_t* krow = Kb + (mt * 32 + lq) * DQK;
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const int c = ((dsi * C::DQW + s * 16) >> 3) + lh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ((c ^ kswz) << 3));
-        S[mt] = mfma32(a, qf[s], S[mt]);
+      for (int h = 0; h < 2; ++h) {
+        const int row = vrow + 8 * h;
+        const int col = dsi * C::DVW + dt * 32 + (vg & 1) * 16 + 4 * (vi & 3);
+        voff[dt][h] = row * C::VLD + (((col >> 3) ^ swz<CPRVT>(row)) << 3) + (col & 7);
       }
-    }
-    // ---- partial scores of the DS waves sharing these rows
-    if constexpr (DS > 1) {
+  }
+
+  f32x16 S[C::MT];
+  bf16x8 pb[C::PKS];
+
+  // S(blk) = K(blk) Q^T, partial over this wave's d_qk columns and published
+  // through LDS when DS > 1
+  auto doS = [&](int blk) {
+    {
+      const bf16_t* Kb = kring + (blk % NBUF) * C::K_ELEMS;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<f32x4*>(sx + (((wave * C::MT + mt) * 4 + g4) * 64 + lane) * 4) =
-              f32x4{S[mt][g4 * 4], S[mt][g4 * 4 + 1], S[mt][g4 * 4 + 2], S[mt][g4 * 4 + 3]};
-      lds_barrier();
+        for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + koff[s % NKO] + (s / NKO) * 128 + mt * 32 * DQK);
+          S[mt] = mfma32(a, qf[s], S[mt]);
+        }
+      }
+      if constexpr (DS > 1) {
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(sx + (((wave * C::MT + mt) * 4 + g4) * 64 + lane) * 4) =
+                f32x4{S[mt][g4 * 4], S[mt][g4 * 4 + 1], S[mt][g4 * 4 + 2], S[mt][g4 * 4 + 3]};
+      }
+      // keep kPrefetch operand reads in flight ahead of the MFMAs
+      constexpr int PF = C::DQW >= 256 ? 2 : kPrefetch;
+      constexpr int NM = C::MT * C::KS, PD = NM < PF ? NM : PF;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PD, 0);
+#pragma unroll
+      for (int k = 0; k < NM - PD; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, PD, 0);
+      if constexpr (DS > 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4 * C::MT, 0);
+    }
+  };
+
+  // O += V(blk)^T P(blk), V^T fragments by transposed LDS reads
+  auto doPV = [&](int blk) {
+    {
+      const bf16_t* Vb = SPARSE ? kring + (blk % NBUF) * C::K_ELEMS : vring + (blk % NBUF) * C::V_ELEMS;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+        for (int ks = 0; ks < C::PKS; ++ks) {
+          const bf16_t* p0 = Vb + voff[dt % NVO][0] + (dt / NVO) * 128 + ks * 16 * C::VLD;
+          const bf16_t* p1 = Vb + voff[dt % NVO][1] + (dt / NVO) * 128 + ks * 16 * C::VLD;
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+          const u32x4 w = {(uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
+                           (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
+                           (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
+                           (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16)};
+          acc[dt] = mfma32(as_bf16x8(w), pb[ks], acc[dt]);
+        }
+      }
+      // two transposed reads per MFMA; keep kPrefetch MFMAs' operands in flight
+      constexpr int PF = C::DVW >= 256 ? 2 : kPrefetch;
+      constexpr int NM = C::DT * C::PKS, PD = NM < PF ? NM : PF;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PD, 0);
+#pragma unroll
+      for (int k = 0; k < NM - PD; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, PD, 0);
+    }
+  };
+
+  // VALU half of a key step: full scores, masks, online softmax -> P(blk)
+  auto phase2 = [&](int blk) {
+    const int key0 = blk * BN;
+    if constexpr (DS > 1) {
 #pragma unroll
       for (int o = 1; o < DS; ++o) {
         const int w2 = qg * DS + (dsi + o) % DS;
@@ -951,7 +1113,6 @@ attn_fwd_dma_kernel(const KernelParams p) {
           }
       }
     }
-    // ---- masks
     if constexpr (SPARSE) {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
@@ -965,16 +1126,14 @@ attn_fwd_dma_kernel(const KernelParams p) {
         }
     } else {
       if (key0 + BN > kfull) {
+        const int lim = row_lim - key0 - lh * 4;  // mask keys whose in-block offset exceeds lim
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + mt * 32 + (i >> 2) * 8 + lh * 4 + (i & 3);
-            if (key > row_lim) S[mt][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (mt * 32 + (i >> 2) * 8 + (i & 3) > lim) S[mt][i] = -INFINITY;
       }
     }
-    // ---- online softmax with a lazy rescale
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
@@ -1003,7 +1162,6 @@ attn_fwd_dma_kernel(const KernelParams p) {
         rs += e;
       }
     l_run += rs;
-    bf16x8 pb[C::PKS];
 #pragma unroll
     for (int ks = 0; ks < C::PKS; ++ks) {
       const int mt = ks >> 1, base = (ks & 1) * 8;
@@ -1012,29 +1170,17 @@ attn_fwd_dma_kernel(const KernelParams p) {
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(S[mt][base + 2 * e], S[mt][base + 2 * e + 1]);
       pb[ks] = as_bf16x8(w);
     }
-    // ---- O^T += V^T P^T, V^T fragments by transposed LDS reads
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int col = vcol0 + dt * 32;
-      const int choff = (((col >> 3) ^ vswz) << 3) + (col & 7);
-#pragma unroll
-      for (int ks = 0; ks < C::PKS; ++ks) {
-        const bf16_t* p0 = Vb + (ks * 16 + vrow) * C::VLD + choff;
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-        const i16x4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + 8 * C::VLD));
-        const u32x4 w = {(uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
-                         (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
-                         (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
-                         (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16)};
-        acc[dt] = mfma32(as_bf16x8(w), pb[ks], acc[dt]);
-      }
-    }
   };
 
   // ---------------------------------------------------------------- key loop
-  // direct-to-LDS loads this wave issues per key block
-  const int my_loads = C::NIK / NW + (wave < C::NIK % NW ? 1 : 0) + C::NIV / NW + (wave < C::NIV % NW ? 1 : 0);
+  // Key step i spans barriers B(2i) .. B(2i+2). With two groups, group 0 runs
+  // its MFMA half (S(i), PV(i-1)) then its softmax half (phase2(i)); group 1
+  // runs phase2(i-1) then S(i), PV(i-1), so on every SIMD one wave multiplies
+  // while the other does the softmax; step nb only drains the last PV
+  // product. With one group a step is S(i), [exchange], phase2(i), PV(i).
+  // with two groups each group's waves load one tile kind (K: group 0, V: group 1)
+  const int myK = C::NIK / NLW_ + (lw_ < C::NIK % NLW_ ? 1 : 0);
+  const int myV = C::NIV / NLW_ + (lw_ < C::NIV % NLW_ ? 1 : 0);
   const int nseg = SPARSE ? (p.Tk + C::IDX_CAP - 1) / max(C::IDX_CAP, 1) : 1;
   for (int sg = 0; sg < nseg; ++sg) {
     int nb;
@@ -1042,27 +1188,85 @@ attn_fwd_dma_kernel(const KernelParams p) {
       const int seg0 = sg * C::IDX_CAP;
       const int segn = min(C::IDX_CAP, p.Tk - seg0);
       nb = (segn + BN - 1) / BN;
-      if (sg > 0) block_barrier();  // everyone is done with the previous segment's indices
+      if (sg > 0) lds_barrier();  // everyone is done with the previous segment's indices and tiles
       const int32_t* irow = p.idx + (int64_t)sq * p.idx_ss + seg0;
       for (int e = tid; e < nb * BN; e += C::NT) sidx[e] = (e < segn) ? irow[e] : -1;
       lds_barrier();
     } else {
       nb = (kend + BN - 1) / BN;
     }
-    if (nb > 0) issue(0, 0);
-    if (NSTAGE == 3 && nb > 1) issue(1, 1);
-    for (int blk = 0; blk < nb; ++blk) {
-      if (NSTAGE == 3 && blk + 1 < nb)
-        wait_vmcnt_dyn(my_loads);
-      else
-        wait_vmcnt<0>();
-      block_barrier();
-      if (NSTAGE == 3) {
-        if (blk + 2 < nb) issue(blk + 2, (blk + 2) % 3);
-      } else {
-        if (blk + 1 < nb) issue(blk + 1, (blk + 1) & 1);
+    // Loads of key step i: K block i+KD and V block i+VD. With two groups the
+    // V block is loaded by group 1 right after B(2i) and the K block by group
+    // 0 right after B(2i+1), each at the start of its softmax half, so the
+    // issue never delays an MFMA half; with one group both follow B(2i).
+    auto issue_k = [&](int i) {
+      const int kj = i + C::KD;
+      if (kj >= 0 && kj < nb) issueK(kj);
+    };
+    auto issue_v = [&](int i) {
+      const int vj = i + C::VD;
+      if (!SPARSE && vj >= 0 && vj < nb) issueV(vj);
+    };
+    // loads of step i that this wave issued (it only counts its own)
+    auto step_loads = [&](int i) {
+      const int kj = i + C::KD, vj = i + C::VD;
+      const bool doesK = !C::PP || wgrp == 0, doesV = !C::PP || wgrp == 1 || SPARSE;
+      return ((doesK && kj >= 0 && kj < nb) ? myK : 0) + ((doesV && !SPARSE && vj >= 0 && vj < nb) ? myV : 0);
+    };
+    auto issue_step = [&](int i) {
+      issue_k(i);
+      issue_v(i);
+    };
+    for (int i = -C::KD; i < 0; ++i) {
+      if (!C::PP || wgrp == 0) issue_k(i);
+      if (!C::PP || wgrp == 1) issue_v(i);
+    }
+    // wait until K block i and V block i-1 (two groups) or V block i (one
+    // group) have landed: they were issued at B(2(i-KD)), later loads may
+    // stay in flight
+    auto wait_step = [&](int i) {
+      int allow = 0;
+#pragma unroll
+      for (int g = 1; g < C::KD; ++g) allow += step_loads(i - g);
+      wait_vmcnt_dyn(allow);
+    };
+    if constexpr (C::PP) {
+      // half-step t: barrier B(t); one call site per phase keeps register
+      // allocation to a single path
+      for (int t = 0; t <= 2 * nb + 1; ++t) {
+        if ((t & 1) == 0) wait_step(t >> 1);
+        lds_barrier();
+        const int u = t - wgrp;
+        if (u < 0) {
+          issue_v(t >> 1);  // group 1, half-step 0
+          continue;
+        }
+        const int j = u >> 1;
+        if ((u & 1) == 0) {
+          // MFMA half: S(j) and the PV product of block j-1
+          if (j < nb) doS(j);
+          // keep the V reads below the S product (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
+          if (j >= 1) doPV(j - 1);
+        } else {
+          // softmax half; this group's loads of step t/2 go first
+          if (wgrp == 0)
+            issue_k(t >> 1);
+          else
+            issue_v(t >> 1);
+          if (j < nb) phase2(j);
+        }
       }
-      compute(blk, tiles + (blk % NSTAGE) * C::STAGE_ELEMS);
+    } else {
+      for (int j = 0; j < nb; ++j) {
+        wait_step(j);
+        lds_barrier();
+        issue_step(j);
+        doS(j);
+        if constexpr (DS > 1) lds_barrier();  // publishes the partial scores
+        phase2(j);
+        doPV(j);
+      }
     }
   }
 
@@ -1102,17 +1306,17 @@ attn_fwd_dma_kernel(const KernelParams p) {
   }
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NSTAGE, bool SPARSE>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
 int launch_dma(const KernelParams& p, void* stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>), dim3(p.n_tiles), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>), dim3(p.n_tiles), dim3(NW * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
-#define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NSTAGE, SPARSE)                                                  \
-  KernelConfig {                                                                                             \
-    NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>::BM, BN, NW,                         \
-        DCfg<DQK, DV, DS, NW, BN, NSTAGE, SPARSE>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NSTAGE, SPARSE> \
+#define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
+  KernelConfig {                                                                                                 \
+    NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::BM, BN, NW,                           \
+        DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, SPARSE> \
   }
 
 template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
@@ -1128,15 +1332,37 @@ int launch(const KernelParams& p, void* stream) {
         Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::LDS_BYTES, &launch<DQK, DV, QT, DS, NW, BN, F32, SPARSE> \
   }
 
+// (DS, waves, BN, LDS ring slots, two wave groups) per head-dim configuration;
+// DMA_ENTRY_X expands them first
+#define DMA_ENTRY_X(...) DMA_ENTRY(__VA_ARGS__)
+#ifndef ATTN_CFG_D64
+#define ATTN_CFG_D64 1, 8, 64, 3, true
+#endif
+#ifndef ATTN_CFG_D128
+#define ATTN_CFG_D128 1, 8, 64, 3, true
+#endif
+#ifndef ATTN_CFG_D192
+#define ATTN_CFG_D192 1, 8, 64, 3, true
+#endif
+#ifndef ATTN_CFG_D256
+#define ATTN_CFG_D256 2, 4, 32, 3, false
+#endif
+#ifndef ATTN_CFG_D512
+#define ATTN_CFG_D512 2, 4, 32, 2, false
+#endif
+#ifndef ATTN_CFG_SPARSE
+#define ATTN_CFG_SPARSE 2, 4, 32, 4, false
+#endif
+
 const KernelConfig kTable[] = {
-    DMA_ENTRY("dense_bf16_d64", 64, 64, 1, 8, 64, 3, false),
-    DMA_ENTRY("dense_bf16_d128", 128, 128, 1, 8, 64, 3, false),
-    DMA_ENTRY("dense_bf16_d192_v128", 192, 128, 1, 8, 32, 3, false),
-    DMA_ENTRY("dense_bf16_d256", 256, 256, 2, 4, 32, 3, false),
-    DMA_ENTRY("dense_bf16_d512", 512, 512, 2, 4, 32, 2, false),
+    DMA_ENTRY_X("dense_bf16_d64", 64, 64, ATTN_CFG_D64, false),
+    DMA_ENTRY_X("dense_bf16_d128", 128, 128, ATTN_CFG_D128, false),
+    DMA_ENTRY_X("dense_bf16_d192_v128", 192, 128, ATTN_CFG_D192, false),
+    DMA_ENTRY_X("dense_bf16_d256", 256, 256, ATTN_CFG_D256, false),
+    DMA_ENTRY_X("dense_bf16_d512", 512, 512, ATTN_CFG_D512, false),
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
     CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
-    DMA_ENTRY("sparse_bf16_d512", 512, 512, 2, 4, 32, 3, true),
+    DMA_ENTRY_X("sparse_bf16_d512", 512, 512, ATTN_CFG_SPARSE, true),
 };
 
 }  // namespace
