@@ -244,6 +244,76 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp}
 
 
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain device copy of known size, to scale the HBM byte counters."""
+    import torch
+
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {mib} MiB x {reps}")
+
+
+def _counter_means(csv_path: str, counter: str) -> dict:
+    """Mean value of one counter per dispatch, keyed by kernel name."""
+    import collections
+    import csv
+
+    tot, disp = collections.defaultdict(float), collections.defaultdict(set)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def _workload_of_kernel(name: str):
+    """Map a kernel's template arguments to the workload it serves (None if not ours)."""
+    if "attn_fwd" not in name or "<" not in name:
+        return None
+    args = [a.strip() for a in name[name.index("<") + 1:name.index(">")].split(",")]
+    dqk, dv = int(args[0]), int(args[1])
+    if "attn_fwd_dma_kernel" in name:
+        sparse = args[6] == "true"
+        if sparse:
+            return 5
+        return {(128, 128): 2, (192, 128): 3, (512, 512): 4}.get((dqk, dv))
+    return 1 if (dqk, dv) == (64, 64) else None
+
+
+def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, commands):
+    """Write profiles/traffic.json: HBM bytes per launch for each workload kernel."""
+    cf = _counter_means(copy_fetch_csv, "FETCH_SIZE")
+    cw = _counter_means(copy_write_csv, "WRITE_SIZE")
+    # the plain copy (the calibration run also has the fill that creates its source)
+    ck = [k for k in cf if "copy" in k.lower()]
+    if not ck:
+        raise SystemExit("no copy kernel in the calibration profile")
+    copy_kib = copy_mib * 1024.0
+    sf = copy_kib / max(cf[ck[0]], 1.0)
+    sw = copy_kib / max(cw[ck[0]], 1.0)
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    out = {"kernel_source_hash": kernel_source_hash(), "copy_calibration_mib": copy_mib,
+           "fetch_scale": round(sf, 4), "write_scale": round(sw, 4), "commands": commands, "workloads": {}}
+    for k in fetch:
+        n = _workload_of_kernel(k)
+        if n is None or k not in write:
+            continue
+        b = (fetch[k] * sf + write[k] * sw) * 1024.0
+        out["workloads"][str(n)] = {"kernel": k, "fetch_kib_raw": round(fetch[k], 1),
+                                    "write_kib_raw": round(write[k], 1), "hbm_bytes_per_launch": int(b),
+                                    "algorithmic_bytes": work(n)["bytes"]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,7 +322,16 @@ def main():
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOAD_IDS))
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--commands", default="", help="the profiling commands, recorded in traffic.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from, args.copy_mib, args.commands)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention forward "
               "of this library runs on one device. Run with --gpus 1.", file=sys.stderr)
@@ -263,6 +342,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import attention_forward_attn_amd as A
 
     A.load_library()
