@@ -148,6 +148,27 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
   if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   p.n_tiles = (int)tiles;
+  // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
+  // with its own L2. When the (batch, kv head) groups split evenly, every XCD
+  // takes whole groups so that a group's K/V stays in one L2.
+  p.xcd_groups = (p.aligned && p.n_groups % 8 == 0) ? 1 : 0;
+  if (p.xcd_groups) {
+    // An XCD runs 32 workgroups at once (one per CU); it works through its
+    // groups a chunk at a time, the chunk just large enough to fill its CUs,
+    // so that concurrent workgroups share their K/V in that XCD's L2.
+    const int gpx = p.n_groups / 8;
+    const int per_group = p.g * p.tiles_per_head;
+    const int want = (32 + per_group - 1) / per_group;
+    int chunk = gpx;
+    for (int c = 1; c <= gpx; ++c)
+      if (gpx % c == 0 && c >= want) {
+        chunk = c;
+        break;
+      }
+    p.xcd_chunk = chunk;
+  } else {
+    p.xcd_chunk = 0;
+  }
   return ATTN_OK;
 }
 

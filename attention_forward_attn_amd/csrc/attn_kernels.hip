@@ -817,10 +817,25 @@ attn_fwd_dma_kernel(const KernelParams p) {
   } else {
     const int tile = blockIdx.x;
     if (p.aligned) {
-      const int per_tb = p.n_groups * p.g;
-      const int tb = (p.tiles_per_head - 1) - tile / per_tb;  // longest causal blocks first
-      const int rest = tile % per_tb;
-      const int grp = rest / p.g, hl = rest % p.g;
+      int tb, grp, hl;
+      if (p.xcd_groups) {
+        // XCD x (= tile % 8) owns groups x, x+8, ...; it takes them xcd_chunk
+        // at a time, longest causal blocks first inside a chunk
+        const int x = tile & 7, i = tile >> 3;
+        const int per_tb = p.xcd_chunk * p.g;
+        const int per_chunk = per_tb * p.tiles_per_head;
+        const int c = i / per_chunk, r = i % per_chunk;
+        tb = (p.tiles_per_head - 1) - r / per_tb;
+        const int rest = r % per_tb;
+        grp = (c * p.xcd_chunk + rest / p.g) * 8 + x;
+        hl = rest % p.g;
+      } else {
+        const int per_tb = p.n_groups * p.g;
+        tb = (p.tiles_per_head - 1) - tile / per_tb;  // longest causal blocks first
+        const int rest = tile % per_tb;
+        grp = rest / p.g;
+        hl = rest % p.g;
+      }
       b = grp / p.Hkv;
       kvh = grp % p.Hkv;
       const int t0 = tb * C::BM;

@@ -34,6 +34,8 @@ struct KernelParams {
   int32_t tiles_per_group;// tiles per (b, kv head)
   int32_t n_groups;       // B * Hkv
   int32_t n_tiles;        // grid size
+  int32_t xcd_groups;     // 1: workgroup i runs on XCD i % 8; give each XCD whole (b, kv) groups
+  int32_t xcd_chunk;      // groups an XCD works on at a time (divides n_groups / 8)
 };
 
 // Host-side launchers, one per compiled kernel configuration.
