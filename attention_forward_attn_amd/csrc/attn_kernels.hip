@@ -70,7 +70,17 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 // value held by lane l ^ 32
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// v_permlane32_swap leaves lanes 0-31 of both halves in one register and
+// lanes 32-63 in the other, so one VALU op combines the two row halves held
+// by lanes l and l ^ 32 (no LDS round trip).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -540,7 +550,7 @@ attn_fwd_kernel(const KernelParams p) {
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qt][mt][i]);
-      mx = fmaxf(mx, other_half(mx));
+      mx = halves_max(mx);
       const float mnew = fmaxf(m_run[qt], mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - muse) * p.c);
@@ -602,7 +612,7 @@ attn_fwd_kernel(const KernelParams p) {
   in_t* ob = reinterpret_cast<in_t*>(p.out);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float lt = l_run[qt] + other_half(l_run[qt]);
+    const float lt = halves_sum(l_run[qt]);
     const float ms = (m_run[qt] == -INFINITY) ? -INFINITY : m_run[qt] * p.scale;  // natural units
     float inv, lse;
     if (p.sinks != nullptr) {
@@ -682,11 +692,21 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16 bytes per lane from global memory into LDS at m0 + 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+// 16 bytes per lane from global memory into LDS at m0 + 16 * lane, read
+// from a wave-uniform base plus a per-lane 32-bit byte offset (the SGPR-base
+// form of the instruction: no 64-bit address arithmetic per load).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
+}
+
+// a pointer that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int N>
@@ -919,32 +939,37 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // blk is the block index inside the current segment (sparse) or the key range (dense)
   constexpr int NLW_ = C::NLOADW;  // waves that share the loads of one tile
   constexpr int NIK_L = (C::NIK + NLW_ - 1) / NLW_, NIV_L = (C::NIV + NLW_ - 1) / NLW_;
-  const int lw_ = wave % NLW_;
-  // per-lane element offsets of the rows and chunks a wave loads, relative
-  // to the first key of the block (the swizzle is applied on the global side);
+  const int lw_ = __builtin_amdgcn_readfirstlane(wave % NLW_);
+  // per-lane byte offsets of the rows and chunks a wave loads, relative to
+  // the first key of the block (the swizzle is applied on the global side);
   // 32-bit because the host limits key-row strides to 2^24 elements
-  auto koffg_at = [&](int m) -> int32_t {
+  auto koffg_at = [&](int m) -> uint32_t {
     const int sl = 64 * (lw_ + NLW_ * m) + lane;
     const int rw = sl / C::CPRK, c = (sl % C::CPRK) ^ swz<C::CPRK>(rw);
-    return SPARSE ? c * 8 : rw * (int32_t)p.k_st + c * 8;
+    return 2u * (uint32_t)(SPARSE ? c * 8 : rw * (int32_t)p.k_st + c * 8);
   };
-  auto voffg_at = [&](int m) -> int32_t {
+  auto voffg_at = [&](int m) -> uint32_t {
     const int sl = 64 * (lw_ + NLW_ * m) + lane;
     const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
-    return rw * (int32_t)p.v_st + c * 8;
+    return 2u * (uint32_t)(rw * (int32_t)p.v_st + c * 8);
   };
   // narrow slices keep the offsets in registers; wide ones (d_qk/DS >= 256)
   // recompute them, which is a few integer ops per load
   constexpr bool KEEP_OFFS = C::DQW < 256;
-  int32_t koffg[KEEP_OFFS ? NIK_L : 1], voffg[(KEEP_OFFS && NIV_L > 0) ? NIV_L : 1];
+  uint32_t koffg[KEEP_OFFS ? NIK_L : 1], voffg[(KEEP_OFFS && NIV_L > 0) ? NIV_L : 1];
   if constexpr (KEEP_OFFS) {
 #pragma unroll
     for (int m = 0; m < NIK_L; ++m) koffg[m] = koffg_at(m);
 #pragma unroll
     for (int m = 0; m < NIV_L; ++m) voffg[m] = voffg_at(m);
   }
-  auto issueK = [&](int blk) {
-    bf16_t* Kb = kring + (blk % NBUF) * C::K_ELEMS;
+  // The block index is the same in every lane; taking it into a scalar
+  // register keeps the ring slot, the LDS address and the global base of the
+  // block in scalar arithmetic.
+  const uint32_t kring_s = lds_u32(kring), vring_s = lds_u32(vring);
+  auto issueK = [&](int blk_in) {
+    const int blk = __builtin_amdgcn_readfirstlane(blk_in);
+    const uint32_t Kb = kring_s + (uint32_t)((blk % NBUF) * C::K_ELEMS * 2);
     const int key0 = blk * BN;
     if constexpr (SPARSE) {
       // one LDS read per lane for the block's indices; each wave instruction
@@ -957,44 +982,54 @@ attn_fwd_dma_kernel(const KernelParams p) {
         if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
         const int ix = __builtin_amdgcn_readlane(myix, j);
         const int row = (ix >= 0 && ix < p.npool) ? ix : 0;
-        dma16(kbase + (int64_t)row * p.k_st + (KEEP_OFFS ? koffg[m] : koffg_at(m)), lds_u32(Kb + 64 * j * 8));
+        dma16s(uniform_ptr(kbase + (int64_t)row * p.k_st), KEEP_OFFS ? koffg[m] : koffg_at(m), Kb + 1024u * j);
       }
     } else {
-      const bool tail = key0 + BN > kend;  // rows past kend are clamped onto row kend-1
+      const void* sb = uniform_ptr(kbase + (int64_t)key0 * p.k_st);
+      if (key0 + BN <= kend) {
 #pragma unroll
-      for (int m = 0; m < NIK_L; ++m) {
-        const int j = lw_ + NLW_ * m;
-        if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
-        const bf16_t* src;
-        if (!tail) {
-          src = kbase + (int64_t)key0 * p.k_st + (KEEP_OFFS ? koffg[m] : koffg_at(m));
-        } else {
+        for (int m = 0; m < NIK_L; ++m) {
+          const int j = lw_ + NLW_ * m;
+          if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
+          dma16s(sb, KEEP_OFFS ? koffg[m] : koffg_at(m), Kb + 1024u * j);
+        }
+      } else {
+        // last block: rows past kend are clamped onto row kend-1
+#pragma unroll
+        for (int m = 0; m < NIK_L; ++m) {
+          const int j = lw_ + NLW_ * m;
+          if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
           const int sl = 64 * j + lane;
           const int rw = sl / C::CPRK, c = (sl % C::CPRK) ^ swz<C::CPRK>(rw);
-          src = kbase + (int64_t)min(key0 + rw, kend - 1) * p.k_st + c * 8;
+          const int rr = min(rw, kend - 1 - key0);
+          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.k_st + c * 8), Kb + 1024u * j);
         }
-        dma16(src, lds_u32(Kb + 64 * j * 8));
       }
     }
   };
-  auto issueV = [&](int blk) {
+  auto issueV = [&](int blk_in) {
     if constexpr (!SPARSE) {
-      bf16_t* Vb = vring + (blk % NBUF) * C::V_ELEMS;
+      const int blk = __builtin_amdgcn_readfirstlane(blk_in);
+      const uint32_t Vb = vring_s + (uint32_t)((blk % NBUF) * C::V_ELEMS * 2);
       const int key0 = blk * BN;
-      const bool tail = key0 + BN > kend;
+      const void* sb = uniform_ptr(vbase + (int64_t)key0 * p.v_st);
+      if (key0 + BN <= kend) {
 #pragma unroll
-      for (int m = 0; m < NIV_L; ++m) {
-        const int j = lw_ + NLW_ * m;
-        if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
-        const bf16_t* src;
-        if (!tail) {
-          src = vbase + (int64_t)key0 * p.v_st + (KEEP_OFFS ? voffg[m] : voffg_at(m));
-        } else {
+        for (int m = 0; m < NIV_L; ++m) {
+          const int j = lw_ + NLW_ * m;
+          if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
+          dma16s(sb, KEEP_OFFS ? voffg[m] : voffg_at(m), Vb + 1024u * j);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < NIV_L; ++m) {
+          const int j = lw_ + NLW_ * m;
+          if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
           const int sl = 64 * j + lane;
           const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
-          src = vbase + (int64_t)min(key0 + rw, kend - 1) * p.v_st + c * 8;
+          const int rr = min(rw, kend - 1 - key0);
+          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.v_st + c * 8), Vb + 1024u * j);
         }
-        dma16(src, lds_u32(Vb + 64 * j * 8));
       }
     }
   };
@@ -1149,12 +1184,13 @@ attn_fwd_dma_kernel(const KernelParams p) {
             if (mt * 32 + (i >> 2) * 8 + (i & 3) > lim) S[mt][i] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    // four partial maxima and sums keep the dependency chains short
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mt][i]);
-    mx = fmaxf(mx, other_half(mx));
+      for (int i = 0; i < 16; ++i) mx4[i & 3] = fmaxf(mx4[i & 3], S[mt][i]);
+    const float mx = halves_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
     const float mnew = fmaxf(m_run, mx);
     const bool grow = (mnew - m_run) * p.c > kRescaleLog2;  // false when both are -inf
     if (__any(grow)) {
@@ -1167,16 +1203,16 @@ attn_fwd_dma_kernel(const KernelParams p) {
         for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
-    float rs = 0.f;
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -mc));
         S[mt][i] = e;
-        rs += e;
+        rs4[i & 3] += e;
       }
-    l_run += rs;
+    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 #pragma unroll
     for (int ks = 0; ks < C::PKS; ++ks) {
       const int mt = ks >> 1, base = (ks & 1) * 8;
@@ -1286,7 +1322,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   }
 
   // ---------------------------------------------------------------- epilogue
-  const float lt = l_run + other_half(l_run);
+  const float lt = halves_sum(l_run);
   const float ms = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
   float inv, lse;
   if (p.sinks != nullptr) {
