@@ -1164,16 +1164,19 @@ attn_fwd_dma_kernel(const KernelParams p) {
       }
     }
     if constexpr (SPARSE) {
+      // lane k tests key k of the block; the ballot has a set bit per key
+      // whose index is out of range (padding of a short list, or invalid)
+      static_assert(BN <= 64, "one key per lane");
+      const int ixl = sidx[key0 + (lane & (BN - 1))];
+      uint64_t bad = __ballot(ixl < 0 || ixl >= p.npool);
+      if constexpr (BN < 64) bad &= (uint64_t(1) << BN) - 1;
+      if (bad != 0) {
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+        for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int4 ix = *reinterpret_cast<const int4*>(sidx + key0 + mt * 32 + g4 * 8 + lh * 4);
-          const int v4[4] = {ix.x, ix.y, ix.z, ix.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (v4[e] < 0 || v4[e] >= p.npool) S[mt][g4 * 4 + e] = -INFINITY;
-        }
+          for (int i = 0; i < 16; ++i)
+            if ((bad >> (mt * 32 + (i >> 2) * 8 + lh * 4 + (i & 3))) & 1) S[mt][i] = -INFINITY;
+      }
     } else {
       if (key0 + BN > kfull) {
         const int lim = row_lim - key0 - lh * 4;  // mask keys whose in-block offset exceeds lim
@@ -1249,7 +1252,8 @@ attn_fwd_dma_kernel(const KernelParams p) {
     // Loads of key step i: K block i+KD and V block i+VD. With two groups the
     // V block is loaded by group 1 right after B(2i) and the K block by group
     // 0 right after B(2i+1), each at the start of its softmax half, so the
-    // issue never delays an MFMA half; with one group both follow B(2i).
+    // issue never delays an MFMA half; with one group both are issued right
+    // after the S product of step i, while its MFMAs drain.
     auto issue_k = [&](int i) {
       const int kj = i + C::KD;
       if (kj >= 0 && kj < nb) issueK(kj);
@@ -1312,8 +1316,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
       for (int j = 0; j < nb; ++j) {
         wait_step(j);
         lds_barrier();
-        issue_step(j);
         doS(j);
+        // the loads go out while the queued S products execute
+        issue_step(j);
         if constexpr (DS > 1) lds_barrier();  // publishes the partial scores
         phase2(j);
         doPV(j);
@@ -1402,7 +1407,7 @@ int launch(const KernelParams& p, void* stream) {
 #define ATTN_CFG_D512 2, 4, 32, 2, false
 #endif
 #ifndef ATTN_CFG_SPARSE
-#define ATTN_CFG_SPARSE 2, 4, 32, 4, false
+#define ATTN_CFG_SPARSE 4, 8, 32, 3, false
 #endif
 
 const KernelConfig kTable[] = {
