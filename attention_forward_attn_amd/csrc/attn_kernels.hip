@@ -953,9 +953,16 @@ attn_fwd_dma_kernel(const KernelParams p) {
     const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
     return 2u * (uint32_t)(rw * (int32_t)p.v_st + c * 8);
   };
-  // narrow slices keep the offsets in registers; wide ones (d_qk/DS >= 256)
-  // recompute them, which is a few integer ops per load
-  constexpr bool KEEP_OFFS = C::DQW < 256;
+  // Rows of 64 chunks (d = 512): one wave instruction loads one row, the row
+  // goes into the scalar base and the per-lane part of the offset is
+  // (lane ^ swizzle(row)) * 16 bytes, one XOR of lane * 16 per load. The
+  // empty asm in the issue functions keeps these XORs inside the key loop
+  // (hoisted, they would pin one register per load).
+  constexpr bool ROWK = C::CPRK == 64, ROWV = !SPARSE && C::CPRV == 64;
+  uint32_t lane16 = (uint32_t)lane << 4;
+  // other narrow slices keep the offsets in registers; wide ones
+  // (d_qk/DS >= 256) recompute them, which is a few integer ops per load
+  constexpr bool KEEP_OFFS = C::DQW < 256 && !ROWK;
   uint32_t koffg[KEEP_OFFS ? NIK_L : 1], voffg[(KEEP_OFFS && NIV_L > 0) ? NIV_L : 1];
   if constexpr (KEEP_OFFS) {
 #pragma unroll
@@ -976,13 +983,25 @@ attn_fwd_dma_kernel(const KernelParams p) {
       // loads one pool row (64 chunks) whose index is broadcast by readlane
       static_assert(C::CPRK == 64 && BN <= 64, "one gathered row per wave instruction");
       const int myix = sidx[key0 + (lane & (BN - 1))];
+      asm volatile("" : "+v"(lane16));
 #pragma unroll
       for (int m = 0; m < NIK_L; ++m) {
         const int j = lw_ + NLW_ * m;
         if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
         const int ix = __builtin_amdgcn_readlane(myix, j);
         const int row = (ix >= 0 && ix < p.npool) ? ix : 0;
-        dma16s(uniform_ptr(kbase + (int64_t)row * p.k_st), KEEP_OFFS ? koffg[m] : koffg_at(m), Kb + 1024u * j);
+        dma16s(uniform_ptr(kbase + (int64_t)row * p.k_st), lane16 ^ (uint32_t)(swz<64>(j) << 4), Kb + 1024u * j);
+      }
+    } else if constexpr (ROWK) {
+      asm volatile("" : "+v"(lane16));
+      const int last = kend - 1 - key0;  // rows past kend are clamped onto row kend-1
+#pragma unroll
+      for (int m = 0; m < NIK_L; ++m) {
+        const int j = lw_ + NLW_ * m;
+        if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
+        const int rr = min(j, last);
+        dma16s(uniform_ptr(kbase + (int64_t)(key0 + rr) * p.k_st), lane16 ^ (uint32_t)(swz<64>(j) << 4),
+               Kb + 1024u * j);
       }
     } else {
       const void* sb = uniform_ptr(kbase + (int64_t)key0 * p.k_st);
@@ -1012,6 +1031,19 @@ attn_fwd_dma_kernel(const KernelParams p) {
       const int blk = __builtin_amdgcn_readfirstlane(blk_in);
       const uint32_t Vb = vring_s + (uint32_t)((blk % NBUF) * C::V_ELEMS * 2);
       const int key0 = blk * BN;
+      if constexpr (ROWV) {
+        asm volatile("" : "+v"(lane16));
+        const int last = kend - 1 - key0;
+#pragma unroll
+        for (int m = 0; m < NIV_L; ++m) {
+          const int j = lw_ + NLW_ * m;
+          if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
+          const int rr = min(j, last);
+          dma16s(uniform_ptr(vbase + (int64_t)(key0 + rr) * p.v_st), lane16 ^ (uint32_t)(swz<64>(j) << 4),
+                 Vb + 1024u * j);
+        }
+        return;
+      }
       const void* sb = uniform_ptr(vbase + (int64_t)key0 * p.v_st);
       if (key0 + BN <= kend) {
 #pragma unroll
@@ -1051,15 +1083,38 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // compile-time shift of 128 elements: keep 8 + 8 per-lane offsets.
   constexpr int NKO = C::KS < 8 ? C::KS : 8;
   constexpr int NVO = C::DT < 4 ? C::DT : 4;
-  int koff[NKO];
-  {
+  // With one wave group (wide slices, one wave per SIMD) registers are
+  // scarce: for 128-aligned slices the 8 + 8 offsets are rebuilt per read
+  // from a base and an XOR term (a logical K step s of a row moves to chunk
+  // 2s + lh; XOR with the row swizzle sw gives ((s ^ sw/2) << 1) | ((lh ^ sw)
+  // & 1) inside each 16-chunk group, and likewise for the V^T quads).
+  constexpr bool LEAN = !C::PP && C::DQW % 128 == 0 && C::DVW % 128 == 0;
+  int koff[LEAN ? 1 : NKO];
+  int k0 = 0, kx = 0;
+  if constexpr (LEAN) {
+    const int sw = swz<C::CPRK>(lq);
+    k0 = lq * DQK + dsi * C::DQW + (((lh ^ sw) & 1) << 3);
+    kx = (sw >> 1) << 4;
+  } else {
     const int sw = swz<C::CPRK>(lq);
 #pragma unroll
     for (int s = 0; s < NKO; ++s)
       koff[s] = lq * DQK + (((((dsi * C::DQW + s * 16) >> 3) + lh) ^ sw) << 3);
   }
-  int voff[NVO][2];
-  {
+  int voff[LEAN ? 1 : NVO][2];
+  int v0[2] = {0, 0}, vx[2] = {0, 0};
+  if constexpr (LEAN) {
+    const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = (vg >> 1) * 4 + (vi >> 2);
+    const int r = (vg & 1) * 2 + ((vi >> 1) & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = vrow + 8 * h;
+      const int sw = swz<CPRVT>(row);
+      v0[h] = row * C::VLD + dsi * C::DVW + (((r ^ sw) & 3) << 3) + 4 * (vi & 1);
+      vx[h] = (sw >> 2) << 5;
+    }
+  } else {
     const int vg = lane >> 4, vi = lane & 15;
     const int vrow = (vg >> 1) * 4 + (vi >> 2);
 #pragma unroll
@@ -1084,11 +1139,13 @@ attn_fwd_dma_kernel(const KernelParams p) {
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
+      if constexpr (LEAN) asm volatile("" : "+v"(k0), "+v"(kx));  // rebuild the offsets every step
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + koff[s % NKO] + (s / NKO) * 128 + mt * 32 * DQK);
+          const int ko = LEAN ? k0 + ((((s % 8) << 4) ^ kx) + (s / 8) * 128) : koff[s % NKO] + (s / NKO) * 128;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + ko + mt * 32 * DQK);
           S[mt] = mfma32(a, qf[s], S[mt]);
         }
       }
@@ -1101,7 +1158,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
                 f32x4{S[mt][g4 * 4], S[mt][g4 * 4 + 1], S[mt][g4 * 4 + 2], S[mt][g4 * 4 + 3]};
       }
       // keep kPrefetch operand reads in flight ahead of the MFMAs
-      constexpr int PF = C::DQW >= 256 ? 2 : kPrefetch;
+      constexpr int PF = C::DQW >= 256 ? 3 : kPrefetch;
       constexpr int NM = C::MT * C::KS, PD = NM < PF ? NM : PF;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PD, 0);
 #pragma unroll
@@ -1118,12 +1175,15 @@ attn_fwd_dma_kernel(const KernelParams p) {
   auto doPV = [&](int blk) {
     {
       const bf16_t* Vb = SPARSE ? kring + (blk % NBUF) * C::K_ELEMS : vring + (blk % NBUF) * C::V_ELEMS;
+      if constexpr (LEAN) asm volatile("" : "+v"(v0[0]), "+v"(v0[1]), "+v"(vx[0]), "+v"(vx[1]));
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
         for (int ks = 0; ks < C::PKS; ++ks) {
-          const bf16_t* p0 = Vb + voff[dt % NVO][0] + (dt / NVO) * 128 + ks * 16 * C::VLD;
-          const bf16_t* p1 = Vb + voff[dt % NVO][1] + (dt / NVO) * 128 + ks * 16 * C::VLD;
+          const int o0 = LEAN ? v0[0] + ((((dt % 4) << 5) ^ vx[0]) + (dt / 4) * 128) : voff[dt % NVO][0] + (dt / NVO) * 128;
+          const int o1 = LEAN ? v0[1] + ((((dt % 4) << 5) ^ vx[1]) + (dt / 4) * 128) : voff[dt % NVO][1] + (dt / NVO) * 128;
+          const bf16_t* p0 = Vb + o0 + ks * 16 * C::VLD;
+          const bf16_t* p1 = Vb + o1 + ks * 16 * C::VLD;
           const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
           const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
           const u32x4 w = {(uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
@@ -1404,7 +1464,7 @@ int launch(const KernelParams& p, void* stream) {
 #define ATTN_CFG_D256 2, 4, 32, 3, false
 #endif
 #ifndef ATTN_CFG_D512
-#define ATTN_CFG_D512 2, 4, 32, 2, false
+#define ATTN_CFG_D512 2, 8, 32, 2, false
 #endif
 #ifndef ATTN_CFG_SPARSE
 #define ATTN_CFG_SPARSE 4, 8, 32, 3, false
