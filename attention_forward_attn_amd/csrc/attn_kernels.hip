@@ -960,23 +960,39 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // (hoisted, they would pin one register per load).
   constexpr bool ROWK = C::CPRK == 64, ROWV = !SPARSE && C::CPRV == 64;
   uint32_t lane16 = (uint32_t)lane << 4;
+  // Rows of 8, 16 or 32 chunks: when the rows one wave's successive
+  // instructions start on are a whole number of 16-row swizzle periods apart,
+  // every load of the wave has the same per-lane offset and the rest is a
+  // scalar step of STEPK (STEPV) rows.
+  constexpr int RPIK = 64 / C::CPRK, RPIV = SPARSE ? 1 : 64 / C::CPRV;  // rows per wave instruction
+  constexpr bool STRK = !ROWK && 64 % C::CPRK == 0 && (RPIK * NLW_) % 16 == 0;
+  constexpr bool STRV = !SPARSE && !ROWV && 64 % C::CPRV == 0 && (RPIV * NLW_) % 16 == 0;
+  constexpr int STEPK = RPIK * NLW_, STEPV = RPIV * NLW_;
   // other narrow slices keep the offsets in registers; wide ones
   // (d_qk/DS >= 256) recompute them, which is a few integer ops per load
-  constexpr bool KEEP_OFFS = C::DQW < 256 && !ROWK;
-  uint32_t koffg[KEEP_OFFS ? NIK_L : 1], voffg[(KEEP_OFFS && NIV_L > 0) ? NIV_L : 1];
-  if constexpr (KEEP_OFFS) {
+  constexpr bool KEEPK = STRK || (C::DQW < 256 && !ROWK), KEEPV = STRV || (C::DQW < 256 && !ROWV);
+  constexpr int NKG = STRK ? 1 : NIK_L, NVG = STRV ? 1 : (NIV_L > 0 ? NIV_L : 1);
+  uint32_t koffg[KEEPK ? NKG : 1], voffg[KEEPV ? NVG : 1];
+  if constexpr (KEEPK) {
 #pragma unroll
-    for (int m = 0; m < NIK_L; ++m) koffg[m] = koffg_at(m);
+    for (int m = 0; m < NKG; ++m) koffg[m] = koffg_at(m);
+  }
+  if constexpr (KEEPV && NIV_L > 0) {
 #pragma unroll
-    for (int m = 0; m < NIV_L; ++m) voffg[m] = voffg_at(m);
+    for (int m = 0; m < NVG; ++m) voffg[m] = voffg_at(m);
   }
   // The block index is the same in every lane; taking it into a scalar
   // register keeps the ring slot, the LDS address and the global base of the
   // block in scalar arithmetic.
+  // (The empty asm statements below stop the per-instruction LDS addresses
+  // from being hoisted out of the key loop, which would pin one scalar
+  // register each.)
   const uint32_t kring_s = lds_u32(kring), vring_s = lds_u32(vring);
   auto issueK = [&](int blk_in) {
     const int blk = __builtin_amdgcn_readfirstlane(blk_in);
-    const uint32_t Kb = kring_s + (uint32_t)((blk % NBUF) * C::K_ELEMS * 2);
+    uint32_t kr = kring_s + 1024u * lw_;  // this wave's first instruction slot
+    asm volatile("" : "+s"(kr));
+    const uint32_t Kb = kr + (uint32_t)((blk % NBUF) * C::K_ELEMS * 2);
     const int key0 = blk * BN;
     if constexpr (SPARSE) {
       // one LDS read per lane for the block's indices; each wave instruction
@@ -990,7 +1006,8 @@ attn_fwd_dma_kernel(const KernelParams p) {
         if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
         const int ix = __builtin_amdgcn_readlane(myix, j);
         const int row = (ix >= 0 && ix < p.npool) ? ix : 0;
-        dma16s(uniform_ptr(kbase + (int64_t)row * p.k_st), lane16 ^ (uint32_t)(swz<64>(j) << 4), Kb + 1024u * j);
+        dma16s(uniform_ptr(kbase + (int64_t)row * p.k_st), lane16 ^ (uint32_t)(swz<64>(j) << 4), Kb + 1024u * NLW_ * m);
+        static_assert(ROWK, "sparse rows are 64 chunks");
       }
     } else if constexpr (ROWK) {
       asm volatile("" : "+v"(lane16));
@@ -1001,16 +1018,21 @@ attn_fwd_dma_kernel(const KernelParams p) {
         if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
         const int rr = min(j, last);
         dma16s(uniform_ptr(kbase + (int64_t)(key0 + rr) * p.k_st), lane16 ^ (uint32_t)(swz<64>(j) << 4),
-               Kb + 1024u * j);
+               Kb + 1024u * NLW_ * m);
       }
     } else {
       const void* sb = uniform_ptr(kbase + (int64_t)key0 * p.k_st);
       if (key0 + BN <= kend) {
+        int64_t kstep = (int64_t)STEPK * p.k_st;
+        asm volatile("" : "+s"(kstep));
 #pragma unroll
         for (int m = 0; m < NIK_L; ++m) {
           const int j = lw_ + NLW_ * m;
           if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
-          dma16s(sb, KEEP_OFFS ? koffg[m] : koffg_at(m), Kb + 1024u * j);
+          if constexpr (STRK)
+            dma16s(uniform_ptr(static_cast<const bf16_t*>(sb) + m * kstep), koffg[0], Kb + 1024u * NLW_ * m);
+          else
+            dma16s(sb, KEEPK ? koffg[m] : koffg_at(m), Kb + 1024u * NLW_ * m);
         }
       } else {
         // last block: rows past kend are clamped onto row kend-1
@@ -1021,7 +1043,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
           const int sl = 64 * j + lane;
           const int rw = sl / C::CPRK, c = (sl % C::CPRK) ^ swz<C::CPRK>(rw);
           const int rr = min(rw, kend - 1 - key0);
-          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.k_st + c * 8), Kb + 1024u * j);
+          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.k_st + c * 8), Kb + 1024u * NLW_ * m);
         }
       }
     }
@@ -1029,7 +1051,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
   auto issueV = [&](int blk_in) {
     if constexpr (!SPARSE) {
       const int blk = __builtin_amdgcn_readfirstlane(blk_in);
-      const uint32_t Vb = vring_s + (uint32_t)((blk % NBUF) * C::V_ELEMS * 2);
+      uint32_t vr = vring_s + 1024u * lw_;
+      asm volatile("" : "+s"(vr));
+      const uint32_t Vb = vr + (uint32_t)((blk % NBUF) * C::V_ELEMS * 2);
       const int key0 = blk * BN;
       if constexpr (ROWV) {
         asm volatile("" : "+v"(lane16));
@@ -1040,17 +1064,22 @@ attn_fwd_dma_kernel(const KernelParams p) {
           if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
           const int rr = min(j, last);
           dma16s(uniform_ptr(vbase + (int64_t)(key0 + rr) * p.v_st), lane16 ^ (uint32_t)(swz<64>(j) << 4),
-                 Vb + 1024u * j);
+                 Vb + 1024u * NLW_ * m);
         }
         return;
       }
       const void* sb = uniform_ptr(vbase + (int64_t)key0 * p.v_st);
       if (key0 + BN <= kend) {
+        int64_t vstep = (int64_t)STEPV * p.v_st;
+        asm volatile("" : "+s"(vstep));
 #pragma unroll
         for (int m = 0; m < NIV_L; ++m) {
           const int j = lw_ + NLW_ * m;
           if (C::NIV % NLW_ != 0 && j >= C::NIV) break;
-          dma16s(sb, KEEP_OFFS ? voffg[m] : voffg_at(m), Vb + 1024u * j);
+          if constexpr (STRV)
+            dma16s(uniform_ptr(static_cast<const bf16_t*>(sb) + m * vstep), voffg[0], Vb + 1024u * NLW_ * m);
+          else
+            dma16s(sb, KEEPV ? voffg[m] : voffg_at(m), Vb + 1024u * NLW_ * m);
         }
       } else {
 #pragma unroll
@@ -1060,7 +1089,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
           const int sl = 64 * j + lane;
           const int rw = sl / C::CPRV, c = (sl % C::CPRV) ^ swz<C::CPRV>(rw);
           const int rr = min(rw, kend - 1 - key0);
-          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.v_st + c * 8), Vb + 1024u * j);
+          dma16s(sb, 2u * (uint32_t)(rr * (int32_t)p.v_st + c * 8), Vb + 1024u * NLW_ * m);
         }
       }
     }
@@ -1083,12 +1112,13 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // compile-time shift of 128 elements: keep 8 + 8 per-lane offsets.
   constexpr int NKO = C::KS < 8 ? C::KS : 8;
   constexpr int NVO = C::DT < 4 ? C::DT : 4;
-  // With one wave group (wide slices, one wave per SIMD) registers are
-  // scarce: for 128-aligned slices the 8 + 8 offsets are rebuilt per read
-  // from a base and an XOR term (a logical K step s of a row moves to chunk
-  // 2s + lh; XOR with the row swizzle sw gives ((s ^ sw/2) << 1) | ((lh ^ sw)
-  // & 1) inside each 16-chunk group, and likewise for the V^T quads).
-  constexpr bool LEAN = !C::PP && C::DQW % 128 == 0 && C::DVW % 128 == 0;
+  // With one wave group (wide slices, one wave per SIMD) or 128-key blocks
+  // registers are scarce: for 128-aligned slices the 8 + 8 offsets are
+  // rebuilt per read from a base and an XOR term (a logical K step s of a
+  // row moves to chunk 2s + lh; XOR with the row swizzle sw gives
+  // ((s ^ sw/2) << 1) | ((lh ^ sw) & 1) inside each 16-chunk group, and
+  // likewise for the V^T quads).
+  constexpr bool LEAN = (!C::PP || BN >= 128) && C::DQW % 128 == 0 && C::DVW % 128 == 0;
   int koff[LEAN ? 1 : NKO];
   int k0 = 0, kx = 0;
   if constexpr (LEAN) {
@@ -1240,11 +1270,16 @@ attn_fwd_dma_kernel(const KernelParams p) {
     } else {
       if (key0 + BN > kfull) {
         const int lim = row_lim - key0 - lh * 4;  // mask keys whose in-block offset exceeds lim
+        // branch-free select from the sign of lim - offset (v_sub, v_ashr,
+        // v_bfi); compares against the 16 * MT constants would each hold a
+        // 64-bit lane mask in scalar registers
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (mt * 32 + (i >> 2) * 8 + (i & 3) > lim) S[mt][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int over = (lim - (mt * 32 + (i >> 2) * 8 + (i & 3))) >> 31;  // all ones past the limit
+            S[mt][i] = __int_as_float((__float_as_int(S[mt][i]) & ~over) | (int)(0xff800000u & (uint32_t)over));
+          }
       }
     }
     // four partial maxima and sums keep the dependency chains short
@@ -1455,7 +1490,7 @@ int launch(const KernelParams& p, void* stream) {
 #define ATTN_CFG_D64 1, 8, 64, 3, true
 #endif
 #ifndef ATTN_CFG_D128
-#define ATTN_CFG_D128 1, 8, 64, 3, true
+#define ATTN_CFG_D128 1, 8, 128, 2, true
 #endif
 #ifndef ATTN_CFG_D192
 #define ATTN_CFG_D192 1, 8, 64, 3, true
