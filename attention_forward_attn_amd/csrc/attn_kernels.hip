@@ -1171,9 +1171,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
         for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
       if constexpr (LEAN) asm volatile("" : "+v"(k0), "+v"(kx));  // rebuild the offsets every step
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
+      for (int s = 0; s < C::KS; ++s) {
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+        for (int mt = 0; mt < C::MT; ++mt) {
           const int ko = LEAN ? k0 + ((((s % 8) << 4) ^ kx) + (s / 8) * 128) : koff[s % NKO] + (s / NKO) * 128;
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + ko + mt * 32 * DQK);
           S[mt] = mfma32(a, qf[s], S[mt]);
@@ -1201,25 +1201,27 @@ attn_fwd_dma_kernel(const KernelParams p) {
     }
   };
 
-  // O += V(blk)^T P(blk), V^T fragments by transposed LDS reads
+  // O += V(blk)^T P(blk), V^T fragments by transposed LDS reads; the output
+  // tiles go innermost (consecutive transposed reads cover different columns,
+  // measured faster for the wide slices)
   auto doPV = [&](int blk) {
     {
       const bf16_t* Vb = SPARSE ? kring + (blk % NBUF) * C::K_ELEMS : vring + (blk % NBUF) * C::V_ELEMS;
       if constexpr (LEAN) asm volatile("" : "+v"(v0[0]), "+v"(v0[1]), "+v"(vx[0]), "+v"(vx[1]));
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
+      for (int ks = 0; ks < C::PKS; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < C::PKS; ++ks) {
+        for (int dt = 0; dt < C::DT; ++dt) {
           const int o0 = LEAN ? v0[0] + ((((dt % 4) << 5) ^ vx[0]) + (dt / 4) * 128) : voff[dt % NVO][0] + (dt / NVO) * 128;
           const int o1 = LEAN ? v0[1] + ((((dt % 4) << 5) ^ vx[1]) + (dt / 4) * 128) : voff[dt % NVO][1] + (dt / NVO) * 128;
           const bf16_t* p0 = Vb + o0 + ks * 16 * C::VLD;
           const bf16_t* p1 = Vb + o1 + ks * 16 * C::VLD;
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
-          const u32x4 w = {(uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
-                           (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
-                           (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
-                           (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16)};
+          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+          const u32x4 w = {(uint32_t)(uint16_t)t0[0] | ((uint32_t)(uint16_t)t0[1] << 16),
+                           (uint32_t)(uint16_t)t0[2] | ((uint32_t)(uint16_t)t0[3] << 16),
+                           (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
+                           (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16)};
           acc[dt] = mfma32(as_bf16x8(w), pb[ks], acc[dt]);
         }
       }
