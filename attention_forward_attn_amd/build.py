@@ -2,7 +2,9 @@
 
     python -m attention_forward_attn_amd.build [--verbose]
 
-Produces ``attention_forward_attn_amd/libattn_fwd.so`` (HIP kernels + C ABI).
+Produces ``attention_forward_attn_amd/libattn_fwd.so`` (HIP kernels + C ABI) and
+``libattn_ceiling.so`` (the benchmark's measured-ceiling diagnostics, not part of
+the attention boundary).
 Whole-program compilation (no -fgpu-rdc), so the compiler sees every kernel
 in one translation unit and nothing spills to scratch because of separate
 device linking.
@@ -17,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_fwd.so")
+CEILING_LIB = os.path.join(HERE, "libattn_ceiling.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,7 +65,24 @@ def build(verbose: bool = False, resource_report: bool = False, defines=(), out:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    if out == LIB:
+        build_ceiling(verbose)
     return out
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """The MFMA-loop and copy diagnostics bench.py measures ceilings with."""
+    src = os.path.join(CSRC, "ceiling.hip")
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-shared", src, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
 
 
 if __name__ == "__main__":

@@ -2,7 +2,7 @@
 """Benchmark of the gfx950 fused attention forward (one GPU).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|mla|mqa512|sparse|tiny]
-                    [--primary-only] [--no-cpu-baseline]
+                    [--primary-only] [--no-cpu-baseline] [--no-ceilings]
 
 A step is one call of the library on one batch of synthetic, already
 device-resident inputs: validation + plan + one kernel launch that runs the
@@ -19,6 +19,10 @@ Algorithmic work (what the method must do, not what the kernel happens to do):
   sparse: flops = 2 * Sq*Hq*topk * (d_qk + d_v); bytes = Sq*topk*d_qk*2 (each gathered
           pool row once, V == K) + q + out + indices + lse
 Peaks (MI355X published): bf16 dense MFMA 2.5 PFLOP/s, HBM3E 8 TB/s.
+Measured ceilings (context, not the metric): an MFMA-only 32x32x16 bf16 loop
+and a 2 GiB streaming copy from libattn_ceiling.so, plus the peak computed from
+the device's CU count and maximum clock; each roofline also reports its
+fraction of the measured ceiling.
 """
 from __future__ import annotations
 
@@ -244,6 +248,74 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp}
 
 
+def ceilings() -> dict:
+    """Achievable MFMA and copy rates on this device (best of a few launches)."""
+    import ctypes
+
+    import torch
+
+    from attention_forward_attn_amd import build as B
+
+    if not os.path.exists(B.CEILING_LIB):
+        raise RuntimeError(f"{B.CEILING_LIB} is missing: build with `python -m attention_forward_attn_amd.build`")
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    lib.attn_ceiling_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    lib.attn_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    cus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    if lib.attn_ceiling_device_info(ctypes.byref(cus), ctypes.byref(clk)) != 0:
+        raise RuntimeError("hipDeviceGetAttribute failed")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_ms(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    blocks, iters = cus.value, 20000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        if lib.attn_ceiling_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, sp) != 0:
+            raise RuntimeError("MFMA loop launch failed")
+
+    mfma_flops = blocks * 8 * iters * 8 * (2 * 32 * 32 * 16)
+    mfma_tflops = mfma_flops / (best_ms(mfma) * 1e-3) / 1e12
+    del out
+    nbytes = 1 << 30  # 1 GiB read + 1 GiB written
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copy():
+        if lib.attn_ceiling_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 nbytes, cus.value * 64, sp) != 0:
+            raise RuntimeError("copy launch failed")
+
+    copy_gbs = 2 * nbytes / (best_ms(copy) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    res = {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(copy_gbs, 1), "cus": cus.value,
+           "max_clock_mhz": round(clk.value / 1e3), "computed_bf16_peak_tflops":
+           round(cus.value * 4 * 1024 * clk.value * 1e3 / 1e12, 1)}
+    log(f"[bench] ceilings: {res}")
+    return res
+
+
+def add_ceiling_fraction(roof: dict, ceil: dict) -> None:
+    c = ceil["mfma_bf16_tflops"] if roof["bound"] == "mfma" else ceil["copy_gbs"]
+    roof["ceiling"] = c
+    roof["frac_of_ceiling"] = round(roof["achieved"] / c, 4) if c > 0 else None
+
+
 def copy_calibration(mib: int, reps: int = 5):
     """A plain device copy of known size, to scale the HBM byte counters."""
     import torch
@@ -322,6 +394,7 @@ def main():
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOAD_IDS))
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / copy ceilings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -361,6 +434,12 @@ def main():
                            "roofline": r["roofline"]})
             del r
             torch.cuda.empty_cache()
+    ceil = None
+    if not args.no_ceilings:
+        ceil = ceilings()
+        add_ceiling_fraction(prim["roofline"], ceil)
+        for o in others:
+            add_ceiling_fraction(o["roofline"], ceil)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(n, prim["inp"])
@@ -384,6 +463,7 @@ def main():
         "config": {"workload": describe(n), "path": prim["path"], "kernel_ms": round(prim["timing"]["kernel_ms_mean"], 5)},
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "workloads": others,
     }
     print(json.dumps(line), flush=True)

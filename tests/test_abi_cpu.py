@@ -26,6 +26,18 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(A.EXPORTS)
 
 
+def test_ceiling_library_exports():
+    """The benchmark's ceiling diagnostics live in their own library."""
+    from attention_forward_attn_amd import build as B
+
+    assert os.path.exists(B.CEILING_LIB), "build with python -m attention_forward_attn_amd.build"
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    for n in ("attn_ceiling_device_info", "attn_ceiling_mfma", "attn_ceiling_copy"):
+        assert hasattr(lib, n), n
+    # the attention library does not carry them
+    assert not hasattr(A.load_library(), "attn_ceiling_mfma")
+
+
 def test_abi_version_and_struct_sizes():
     assert A.abi_version() == A.ABI_VERSION
     # the library checks struct_size; a plan call with the binding's structs must succeed
