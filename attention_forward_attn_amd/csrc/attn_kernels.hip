@@ -1386,8 +1386,13 @@ attn_fwd_dma_kernel(const KernelParams p) {
       // half-step t: barrier B(t); one call site per phase keeps register
       // allocation to a single path
       for (int t = 0; t <= 2 * nb + 1; ++t) {
-        if ((t & 1) == 0) wait_step(t >> 1);
-        lds_barrier();
+        // Only even half steps synchronise: every load's landing (waited
+        // just before) and every ring-slot reuse is separated from its
+        // readers by one of them, so the groups need not meet in between.
+        if ((t & 1) == 0) {
+          wait_step(t >> 1);
+          lds_barrier();
+        }
         const int u = t - wgrp;
         if (u < 0) {
           issue_v(t >> 1);  // group 1, half-step 0
