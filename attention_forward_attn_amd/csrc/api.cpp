@@ -154,11 +154,12 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   p.xcd_groups = (p.aligned && p.n_groups % 8 == 0) ? 1 : 0;
   if (p.xcd_groups) {
     // An XCD runs 32 workgroups at once (one per CU); it works through its
-    // groups a chunk at a time, the chunk just large enough to fill its CUs,
-    // so that concurrent workgroups share their K/V in that XCD's L2.
+    // groups a chunk at a time, the chunk holding at least two rounds of its
+    // CUs (so the longest-first order inside a chunk can balance them), so
+    // that concurrent workgroups share their K/V in that XCD's L2.
     const int gpx = p.n_groups / 8;
     const int per_group = p.g * p.tiles_per_head;
-    const int want = (32 + per_group - 1) / per_group;
+    const int want = (64 + per_group - 1) / per_group;
     int chunk = gpx;
     for (int c = 1; c <= gpx; ++c)
       if (gpx % c == 0 && c >= want) {
