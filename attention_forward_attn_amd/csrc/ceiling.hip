@@ -60,6 +60,19 @@ __global__ void __launch_bounds__(256) copy16(const u32x4* __restrict__ src, u32
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Timer self-test: one wave spins until the constant 100 MHz real-time
+// counter has advanced by `ticks`, so the kernel's duration is known
+// independently of the event timer being checked. The wait always ends.
+__global__ void __launch_bounds__(64) spin(unsigned long long ticks, unsigned long long* out) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long t = t0;
+  while (t - t0 < ticks) {
+    __builtin_amdgcn_s_sleep(1);
+    t = __builtin_amdgcn_s_memrealtime();
+  }
+  if (threadIdx.x == 0) out[0] = t - t0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,6 +103,16 @@ int attn_ceiling_copy(const void* src, void* dst, int64_t bytes, int blocks, voi
   if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// Launches the timer self-test kernel for `us` microseconds (measured on the
+// device's 100 MHz real-time counter); `out` (one uint64, device memory)
+// receives the ticks that actually elapsed. Asynchronous on `stream`.
+int attn_ceiling_spin(int us, unsigned long long* out, void* stream) {
+  if (out == nullptr || us <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(spin, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), (unsigned long long)us * 100ull,
+                     out);
   return (int)hipGetLastError();
 }
 

@@ -235,7 +235,10 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     A.reset_dispatch_counts()
     t = time_steps(step, steps, warmup)
     launched = A.dispatch_count(path)
-    assert launched == steps + warmup, f"expected {steps + warmup} launches of {path}, saw {launched}"
+    # engagement census: the expected kernel path ran exactly once per step,
+    # otherwise the numbers are not this path's and the run stops
+    if launched != steps + warmup:
+        raise RuntimeError(f"NotEngaged: expected {steps + warmup} launches of {path}, saw {launched}")
     w = work(n)
     rl = roofline(n, t["kernel_ms_mean"])
     if w["kind"] == "dense":
@@ -245,7 +248,8 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     log(f"[bench] {describe(n)} | path {path} | kernel {t['kernel_ms_mean']:.4f} ms (median "
         f"{t['kernel_ms_median']:.4f}) | step {t['ms_per_step']:.4f} ms | {rl['achieved']} {rl['unit']} "
         f"= {100 * rl['frac']:.1f}% of peak")
-    return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp}
+    return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp,
+            "verdict": "Measured"}
 
 
 def ceilings() -> dict:
@@ -262,6 +266,7 @@ def ceilings() -> dict:
     lib.attn_ceiling_device_info.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.attn_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_ceiling_spin.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     cus, clk = ctypes.c_int(0), ctypes.c_int(0)
     if lib.attn_ceiling_device_info(ctypes.byref(cus), ctypes.byref(clk)) != 0:
         raise RuntimeError("hipDeviceGetAttribute failed")
@@ -303,9 +308,22 @@ def ceilings() -> dict:
     copy_gbs = 2 * nbytes / (best_ms(copy) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
+    # timer self-test: a kernel of known duration (it spins on the device's
+    # 100 MHz real-time counter) must time within 5% with the same events
+    spin_us = 2000
+    ticks = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def spin():
+        if lib.attn_ceiling_spin(spin_us, ctypes.c_void_p(ticks.data_ptr()), sp) != 0:
+            raise RuntimeError("spin launch failed")
+
+    ev_ms = best_ms(spin, reps=3)
+    dev_ms = int(ticks.item()) / 1e5
+    timer = {"expected_ms": spin_us / 1e3, "device_ms": round(dev_ms, 4), "event_ms": round(ev_ms, 4),
+             "ok": abs(ev_ms / (spin_us / 1e3) - 1.0) <= 0.05}
     res = {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(copy_gbs, 1), "cus": cus.value,
            "max_clock_mhz": round(clk.value / 1e3), "computed_bf16_peak_tflops":
-           round(cus.value * 4 * 1024 * clk.value * 1e3 / 1e12, 1)}
+           round(cus.value * 4 * 1024 * clk.value * 1e3 / 1e12, 1), "timer_selftest": timer}
     log(f"[bench] ceilings: {res}")
     return res
 
@@ -431,7 +449,7 @@ def main():
             r = measure(m, max(10, args.steps // 2), max(3, args.warmup // 2))
             others.append({"workload": describe(m), "path": r["path"], "value": round(r["value"], 3),
                            "unit": r["unit"], "kernel_ms": round(r["timing"]["kernel_ms_mean"], 5),
-                           "roofline": r["roofline"]})
+                           "roofline": r["roofline"], "verdict": r["verdict"]})
             del r
             torch.cuda.empty_cache()
     ceil = None
@@ -460,7 +478,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if s.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes; no dataset)",
-        "config": {"workload": describe(n), "path": prim["path"], "kernel_ms": round(prim["timing"]["kernel_ms_mean"], 5)},
+        "config": {"workload": describe(n), "path": prim["path"], "kernel_ms": round(prim["timing"]["kernel_ms_mean"], 5),
+                   "verdict": prim["verdict"]},
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
         "ceilings": ceil,

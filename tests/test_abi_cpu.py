@@ -32,7 +32,7 @@ def test_ceiling_library_exports():
 
     assert os.path.exists(B.CEILING_LIB), "build with python -m attention_forward_attn_amd.build"
     lib = ctypes.CDLL(B.CEILING_LIB)
-    for n in ("attn_ceiling_device_info", "attn_ceiling_mfma", "attn_ceiling_copy"):
+    for n in ("attn_ceiling_device_info", "attn_ceiling_mfma", "attn_ceiling_copy", "attn_ceiling_spin"):
         assert hasattr(lib, n), n
     # the attention library does not carry them
     assert not hasattr(A.load_library(), "attn_ceiling_mfma")
