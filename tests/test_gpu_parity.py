@@ -237,3 +237,53 @@ def test_workload_sparse_sampled():
     A.sparse_topk(q, kv, ix, d_v=s.d_v, scale=s.scale, out=out2, lse=lse2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+# ------------------------------------------------------------------ seeded random sweeps
+def _sweep_cases(n, seed):
+    """Shapes drawn at random (seeded): head dims, GQA group, lengths with
+    ragged tails on every tile size, causal and sink switches."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dqk, dv = HEAD_DIMS[i % len(HEAD_DIMS)]
+        Hkv = int(rng.integers(1, 3))
+        g = int(rng.choice([1, 2, 4, 8]))
+        Tq = int(rng.integers(1, 300))
+        Tk = Tq if rng.random() < 0.5 else int(rng.integers(1, 300))
+        cases.append(dict(B=int(rng.integers(1, 3)), H=g * Hkv, Hkv=Hkv, Tq=Tq, Tk=Tk, dqk=int(dqk), dv=int(dv),
+                          causal=bool(rng.random() < 0.7), sinks=bool(rng.random() < 0.3), seed=1000 * seed + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(12, 7), ids=lambda c: (
+    f"B{c['B']}H{c['H']}/{c['Hkv']}T{c['Tq']}x{c['Tk']}d{c['dqk']}/{c['dv']}"
+    f"{'c' if c['causal'] else 'n'}{'s' if c['sinks'] else ''}"))
+def test_dense_random_sweep(case):
+    c = case
+    inp = synth.randn_dense(c["B"], c["H"], c["Hkv"], c["Tq"], c["Tk"], c["dqk"], c["dv"], dtype="bf16",
+                            sinks=c["sinks"], seed=c["seed"])
+    check_dense_full(inp, causal=c["causal"], scale=1 / math.sqrt(c["dqk"]), label=f"sweep {c}")
+
+
+@pytest.mark.parametrize("seed", [3, 4, 5, 6])
+def test_sparse_random_sweep(seed):
+    rng = np.random.default_rng(seed)
+    Sq, Hq = int(rng.integers(1, 6)), int(rng.choice([8, 16, 32, 64]))
+    N, topk = int(rng.integers(64, 400)), int(rng.integers(1, 300))
+    sinks = bool(rng.random() < 0.5)
+    inp = synth.randn_sparse(Sq, Hq, N, 512, min(topk, N), seed=500 + seed, sinks=sinks)
+    idx = inp["idx"].clone()
+    # a few skipped (-1) and out-of-range entries at random positions
+    flat = idx.view(-1)
+    pos = torch.from_numpy(rng.choice(flat.numel(), size=min(5, flat.numel()), replace=False))
+    flat[pos[: len(pos) // 2]] = -1
+    flat[pos[len(pos) // 2:]] = N + 7
+    announce(f"sparse sweep Sq={Sq} Hq={Hq} N={N} topk={idx.shape[1]} sinks={sinks}")
+    sk = inp["sinks"].cuda() if sinks else None
+    out, lse = A.sparse_topk(inp["q"].cuda(), inp["kv"].cuda(), idx.cuda(), d_v=512, sinks=sk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], idx, d_v=512, scale=1 / math.sqrt(512),
+                                          sinks=inp["sinks"])
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"sparse sweep: max|dO|={eo:.3e} max|dlse|={el:.3e}"
