@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -75,7 +75,8 @@ class AttnPlan(ctypes.Structure):
 EXPORTS = (
     "attn_abi_version", "attn_fwd_dense", "attn_fwd_sparse_topk", "attn_plan_dense",
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
-    "attn_reset_dispatch_counts", "attn_budget_tile_rows",
+    "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
+    "attn_splitkv_workspace_bytes", "attn_splitkv_choose",
 )
 
 _lib = None
@@ -108,6 +109,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_reset_dispatch_counts.restype = None
     lib.attn_budget_tile_rows.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.attn_budget_tile_rows.restype = ctypes.c_int64
+    lib.attn_fwd_dense_splitkv.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_void_p]
+    lib.attn_fwd_dense_splitkv.restype = ctypes.c_int
+    lib.attn_splitkv_workspace_bytes.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_int32]
+    lib.attn_splitkv_workspace_bytes.restype = ctypes.c_int64
+    lib.attn_splitkv_choose.argtypes = [ctypes.POINTER(AttnDenseArgs)]
+    lib.attn_splitkv_choose.restype = ctypes.c_int32
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -210,6 +218,78 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
     return out, lse
 
 
+def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
+                  n_splits: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Split-KV dense forward (decode and other few-row shapes): same inputs
+    and results as :func:`dense`. The keys are cut into ``n_splits`` ranges
+    (0: the library's choice); the fp32 partials go to ``workspace``, a uint8
+    device tensor of at least :func:`splitkv_workspace_bytes` bytes (allocated
+    here when None). Launches on ``stream`` and does not synchronise.
+    """
+    import torch
+
+    lib = load_library()
+    B, H, Tq, dqk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
+    if not lse.is_contiguous():
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks)
+    need = int(lib.attn_splitkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
+    if need < 0:
+        _check(ATTN_INVALID_ARGUMENT)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_fwd_dense_splitkv(ctypes.byref(a), int(n_splits), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                      ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+def _shape_args(B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, causal, sinks, scale) -> AttnDenseArgs:
+    a = AttnDenseArgs()
+    a.struct_size = ctypes.sizeof(AttnDenseArgs)
+    a.dtype = ATTN_BF16 if dtype == "bf16" else ATTN_F32
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, d_qk, d_v
+    a.causal = 1 if causal else 0
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d_qk))
+    a.q, a.q_sb, a.q_sh, a.q_st = _FAKE_PTR, H * Tq * d_qk, Tq * d_qk, d_qk
+    a.k, a.k_sb, a.k_sh, a.k_st = _FAKE_PTR, Hkv * Tk * d_qk, Tk * d_qk, d_qk
+    a.v, a.v_sb, a.v_sh, a.v_st = _FAKE_PTR, Hkv * Tk * d_v, Tk * d_v, d_v
+    a.out, a.o_sb, a.o_sh, a.o_st = _FAKE_PTR, H * Tq * d_v, Tq * d_v, d_v
+    a.lse = _FAKE_PTR
+    a.sinks = _FAKE_PTR if sinks else None
+    return a
+
+
+def splitkv_workspace_bytes(B, H, Hkv, Tq, Tk, d_qk, d_v, *, n_splits: int = 0, dtype: str = "bf16",
+                            causal: bool = True, sinks: bool = False, scale: Optional[float] = None) -> int:
+    """Workspace bytes of a contiguous BHSD split-KV call (host only); 0 when one range suffices."""
+    a = _shape_args(B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, causal, sinks, scale)
+    n = int(load_library().attn_splitkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
+    if n < 0:
+        _check(ATTN_INVALID_ARGUMENT)
+    return n
+
+
+def splitkv_choose(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype: str = "bf16", causal: bool = True,
+                   sinks: bool = False, scale: Optional[float] = None) -> int:
+    """Key ranges the library picks for this shape on the current device (host only)."""
+    a = _shape_args(B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, causal, sinks, scale)
+    n = int(load_library().attn_splitkv_choose(ctypes.byref(a)))
+    if n < 0:
+        _check(ATTN_INVALID_ARGUMENT)
+    return n
+
+
 def sparse_args(q, kv, idx, out, lse, *, d_v: int, scale: float, sinks=None) -> AttnSparseArgs:
     Sq, Hq, dqk = q.shape
     N = kv.shape[0]
@@ -268,18 +348,7 @@ def plan_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype: str = "bf16", causal: boo
                sinks: bool = False, scale: Optional[float] = None) -> dict:
     """The launch plan for a contiguous BHSD problem of this shape (host only)."""
     lib = load_library()
-    a = AttnDenseArgs()
-    a.struct_size = ctypes.sizeof(AttnDenseArgs)
-    a.dtype = ATTN_BF16 if dtype == "bf16" else ATTN_F32
-    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, d_qk, d_v
-    a.causal = 1 if causal else 0
-    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d_qk))
-    a.q, a.q_sb, a.q_sh, a.q_st = _FAKE_PTR, H * Tq * d_qk, Tq * d_qk, d_qk
-    a.k, a.k_sb, a.k_sh, a.k_st = _FAKE_PTR, Hkv * Tk * d_qk, Tk * d_qk, d_qk
-    a.v, a.v_sb, a.v_sh, a.v_st = _FAKE_PTR, Hkv * Tk * d_v, Tk * d_v, d_v
-    a.out, a.o_sb, a.o_sh, a.o_st = _FAKE_PTR, H * Tq * d_v, Tq * d_v, d_v
-    a.lse = _FAKE_PTR
-    a.sinks = _FAKE_PTR if sinks else None
+    a = _shape_args(B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, causal, sinks, scale)
     p = AttnPlan()
     p.struct_size = ctypes.sizeof(AttnPlan)
     _check(lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p)))

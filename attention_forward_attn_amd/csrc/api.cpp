@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -39,7 +40,12 @@ constexpr int kMaxPaths = 64;
 std::atomic<uint64_t> g_counts[kMaxPaths];
 std::atomic<int> g_logged[kMaxPaths];
 
+// the split-KV merge kernel has a counter of its own, after the kernel paths
+constexpr int kMergeSlot = kMaxPaths - 1;
+constexpr const char* kMergePath = "splitkv_merge";
+
 int path_index(const char* path) {
+  if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
   int n = 0;
   const attn::KernelConfig* t = attn::kernel_table(&n);
   for (int i = 0; i < n && i < kMaxPaths; ++i)
@@ -236,6 +242,57 @@ void fill_plan(const DensePlan& dp, int fold_g, int64_t folded_rows, int64_t Tk,
   p->budget_tiles = p->budget_tile_rows > 0 ? (folded_rows + p->budget_tile_rows - 1) / p->budget_tile_rows : 0;
 }
 
+// ---------------------------------------------------------------- split-KV
+int device_cus() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();  // no device here (host-only planning): assume an MI355X
+    cus = 256;
+  }
+  cached.store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+constexpr int kMaxSplits = 1024;
+
+struct SplitPlan {
+  int n;           // ranges actually launched (1: the plain path)
+  int keys;        // keys per range
+  int64_t rows;    // B * H * Tq
+  int64_t bytes;   // workspace bytes needed (0 when n == 1)
+};
+
+// Ranges of whole key blocks: enough of them that the launch fills the GPU
+// twice over (when n_req == 0), never more than there are key blocks.
+SplitPlan plan_split(const DensePlan& dp, const attn_dense_args* a, int n_req) {
+  SplitPlan sp{1, a->Tk, (int64_t)a->B * a->H * a->Tq, 0};
+  const int BN = dp.cfg->block_keys;
+  const int nblocks = (a->Tk + BN - 1) / BN;
+  if (nblocks <= 1 || a->Tq == 0) return sp;
+  int want = n_req;
+  if (want == 0) {
+    const int64_t target = 2 * (int64_t)device_cus();
+    const int64_t tiles = dp.kp.n_tiles > 0 ? dp.kp.n_tiles : 1;
+    want = (int)std::min<int64_t>(kMaxSplits, (target + tiles - 1) / tiles);
+  }
+  want = std::min(want, nblocks);
+  if (want <= 1) return sp;
+  const int per = (nblocks + want - 1) / want;  // key blocks per range
+  sp.keys = per * BN;
+  sp.n = (a->Tk + sp.keys - 1) / sp.keys;
+  if (sp.n <= 1) {
+    sp.n = 1;
+    sp.keys = a->Tk;
+    return sp;
+  }
+  sp.bytes = (int64_t)sp.n * sp.rows * ((int64_t)a->d_v + 1) * 4;
+  return sp;
+}
+
 attn_status do_launch(const DensePlan& dp, void* stream) {
   if (dp.kp.n_tiles <= 0) return ATTN_OK;  // nothing to compute (Tq == 0 or Sq == 0)
   const int err = dp.cfg->launch(dp.kp, stream);
@@ -278,6 +335,67 @@ attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p) {
   if (s != ATTN_OK) return s;
   if (a->Tq == 0) dp.kp.n_tiles = 0;
   fill_plan(dp, a->H / a->Hkv, (int64_t)(a->H / a->Hkv) * a->Tq, a->Tk, a->dtype == ATTN_BF16 ? 2 : 4, p);
+  return ATTN_OK;
+}
+
+int32_t attn_splitkv_choose(const attn_dense_args* a) {
+  g_last_error.clear();
+  DensePlan dp;
+  if (validate_dense(a, &dp) != ATTN_OK) return -1;
+  if (a->dtype != ATTN_BF16) return 1;
+  return plan_split(dp, a, 0).n;
+}
+
+int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits) {
+  g_last_error.clear();
+  DensePlan dp;
+  if (validate_dense(a, &dp) != ATTN_OK) return -1;
+  if (n_splits < 0 || n_splits > kMaxSplits) {
+    fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+    return -1;
+  }
+  if (a->dtype != ATTN_BF16) return 0;
+  return plan_split(dp, a, n_splits).bytes;
+}
+
+attn_status attn_fwd_dense_splitkv(const attn_dense_args* a, int32_t n_splits, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  DensePlan dp;
+  attn_status s = validate_dense(a, &dp);
+  if (s != ATTN_OK) return s;
+  if (n_splits < 0 || n_splits > kMaxSplits)
+    return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+  if (a->Tq == 0) return ATTN_OK;
+  if (a->dtype != ATTN_BF16) {
+    if (n_splits > 1) return fail(ATTN_UNSUPPORTED, "split-KV is compiled for bf16 inputs only");
+    return do_launch(dp, stream);
+  }
+  const SplitPlan sp = plan_split(dp, a, n_splits);
+  if (sp.n == 1) return do_launch(dp, stream);
+  if (workspace == nullptr || workspace_bytes < sp.bytes)
+    return fail(ATTN_INVALID_ARGUMENT, "split-KV over %d key ranges needs a workspace of %lld bytes, got %lld", sp.n,
+                (long long)sp.bytes, (long long)(workspace ? workspace_bytes : 0));
+  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  attn::KernelParams& p = dp.kp;
+  p.n_splits = sp.n;
+  p.split_keys = sp.keys;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + (int64_t)sp.n * sp.rows * a->d_v;
+  s = do_launch(dp, stream);
+  if (s != ATTN_OK) return s;
+  attn::MergeParams m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.sinks = a->sinks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.o_sb = a->o_sb; m.o_sh = a->o_sh; m.o_st = a->o_st;
+  m.B = a->B; m.H = a->H; m.Tq = a->Tq; m.d_v = a->d_v; m.n_splits = sp.n;
+  m.f32 = 0;
+  const int err = attn::launch_merge(m, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the split-KV merge failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kMergeSlot, kMergePath);
   return ATTN_OK;
 }
 

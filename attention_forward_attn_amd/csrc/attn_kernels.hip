@@ -885,6 +885,15 @@ attn_fwd_dma_kernel(const KernelParams p) {
     kend = min(p.Tk, max(0, t_hi + off + 1));
     kfull = min(p.Tk, max(0, t_lo + off + 1));
   }
+  // split-KV: this workgroup sees keys [k_lo, k_hi) only; from here on key
+  // positions (kend, kfull, the row limits, the K/V bases) are relative to k_lo
+  int k_lo = 0;
+  if (!SPARSE && p.n_splits > 1) {
+    k_lo = blockIdx.y * p.split_keys;
+    const int k_hi = min(p.Tk, k_lo + p.split_keys);
+    kend = max(0, min(kend, k_hi) - k_lo);
+    kfull = max(0, min(kfull, k_hi) - k_lo);
+  }
 
   // ---------------------------------------------------------------- the query row of this lane
   const int r = qg * 32 + lq;
@@ -903,6 +912,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
     row_h = kvh * p.g + f / p.Tq;
     const int t = f % p.Tq;
     row_lim = p.causal ? min(p.Tk - 1, t + p.Tk - p.Tq) : p.Tk - 1;
+    row_lim = min(row_lim - k_lo, kend - 1);  // split-KV: relative to the range
     q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (int64_t)t * p.q_st;
     o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (int64_t)t * p.o_st;
     l_off = ((int64_t)b * p.H + row_h) * p.Tq + t;
@@ -931,8 +941,8 @@ attn_fwd_dma_kernel(const KernelParams p) {
     kbase = reinterpret_cast<const bf16_t*>(p.k);
     vbase = kbase;
   } else {
-    kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-    vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+    kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)k_lo * p.k_st;
+    vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + (int64_t)k_lo * p.v_st;
   }
 
   // ---------------------------------------------------------------- loads of one key block
@@ -1431,6 +1441,25 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // ---------------------------------------------------------------- epilogue
   const float lt = halves_sum(l_run);
   const float ms = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
+  if (!SPARSE && p.n_splits > 1) {
+    // split-KV partial: O over this key range normalised by the range's own
+    // denominator (fp32), lse of the range without the sink
+    if (row_ok) {
+      const float pinv = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
+      float* po = p.part_o + prow * DV;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = dsi * C::DVW + dt * 32 + g4 * 8 + lh * 4;
+          *reinterpret_cast<f32x4*>(po + d) = f32x4{acc[dt][g4 * 4] * pinv, acc[dt][g4 * 4 + 1] * pinv,
+                                                    acc[dt][g4 * 4 + 2] * pinv, acc[dt][g4 * 4 + 3] * pinv};
+        }
+      if (lh == 0 && dsi == 0) p.part_lse[prow] = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   float inv, lse;
   if (p.sinks != nullptr) {
     const float sk = p.sinks[row_h];
@@ -1466,9 +1495,72 @@ attn_fwd_dma_kernel(const KernelParams p) {
 
 template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
 int launch_dma(const KernelParams& p, void* stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>), dim3(p.n_tiles), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>),
+                     dim3(p.n_tiles, p.n_splits > 1 ? p.n_splits : 1), dim3(NW * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
+}
+
+// ===========================================================================
+// Merge of split-KV partials: one wave per query row. Each key range i left
+// (O_i normalised by its own denominator, lse_i without the sink); then
+// lse = log(sum_i exp(lse_i) [+ exp(sink)]) and O = sum_i exp(lse_i - lse) O_i
+// (the output merge of TransformerEngine's context-parallel forward,
+// "Flowchart", done across workgroups of one device). Memory bound: it reads
+// n_splits * d_v floats per row once.
+// ===========================================================================
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) {
+  const int lane = threadIdx.x & 63;
+  const int64_t R = (int64_t)m.B * m.H * m.Tq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int t = (int)(row % m.Tq);
+  const int h = (int)((row / m.Tq) % m.H);
+  const int b = (int)(row / ((int64_t)m.Tq * m.H));
+  float mx = -INFINITY;
+  for (int i = lane; i < m.n_splits; i += 64) mx = fmaxf(mx, m.part_lse[i * R + row]);
+  mx = wave_max(mx);
+  const float sk = m.sinks != nullptr ? m.sinks[h] : -INFINITY;
+  mx = fmaxf(mx, sk);
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    for (int i = lane; i < m.n_splits; i += 64) {
+      const float li = m.part_lse[i * R + row];
+      den += li == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((li - mx) * kLog2e);
+    }
+    den = wave_sum(den);
+    if (sk != -INFINITY) den += __builtin_amdgcn_exp2f((sk - mx) * kLog2e);
+  }
+  const float lse = (den > 0.f) ? mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+  const int64_t obase = (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)t * m.o_st;
+  for (int c = lane; c < m.d_v / 4; c += 64) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < m.n_splits; ++i) {
+      const float li = m.part_lse[i * R + row];
+      if (li == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((li - lse) * kLog2e);
+      const f32x4 oi = *reinterpret_cast<const f32x4*>(m.part_o + (i * R + row) * m.d_v + 4 * c);
+      o += w * oi;
+    }
+    if (m.f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(m.out) + obase + 4 * c) = o;
+    } else {
+      *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(m.out) + obase + 4 * c) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+  if (lane == 0) m.lse[row] = lse;
 }
 
 #define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
@@ -1528,6 +1620,13 @@ const KernelConfig kTable[] = {
 const KernelConfig* kernel_table(int* n) {
   *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
   return kTable;
+}
+
+int launch_merge(const MergeParams& m, void* stream) {
+  const int64_t rows = (int64_t)m.B * m.H * m.Tq;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), m);
+  return (int)hipGetLastError();
 }
 
 }  // namespace attn

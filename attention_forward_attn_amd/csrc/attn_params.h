@@ -36,7 +36,31 @@ struct KernelParams {
   int32_t n_tiles;        // grid size
   int32_t xcd_groups;     // 1: workgroup i runs on XCD i % 8; give each XCD whole (b, kv) groups
   int32_t xcd_chunk;      // groups an XCD works on at a time (divides n_groups / 8)
+
+  // split-KV (dense, bf16 paths): blockIdx.y selects keys
+  // [y * split_keys, min(Tk, (y + 1) * split_keys)); with n_splits > 1 the
+  // kernel writes the partial result of its range (O normalised by its own
+  // denominator, fp32, and lse without the sink) to part_o / part_lse
+  int32_t n_splits;       // 1: no split
+  int32_t split_keys;     // keys per range, a multiple of the kernel's key block
+  float* part_o;          // [n_splits][B*H*Tq][d_v]
+  float* part_lse;        // [n_splits][B*H*Tq]
 };
+
+// Merge of split-KV partials (one launch after the split kernel).
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  const float* sinks;     // [H] or nullptr
+  void* out;              // [B, H, Tq, d_v] with the element strides below
+  float* lse;             // [B, H, Tq] contiguous
+  int64_t o_sb, o_sh, o_st;
+  int32_t B, H, Tq, d_v, n_splits;
+  int32_t f32;            // 1: out is float32, else bfloat16
+};
+
+// Host-side launcher of the merge (defined in attn_kernels.hip).
+int launch_merge(const MergeParams& m, void* stream);
 
 // Host-side launchers, one per compiled kernel configuration.
 // Return 0 on success, else the hipError_t of the launch.

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -176,6 +176,52 @@ attn_status attn_fwd_sparse_topk(const attn_sparse_args* a, void* stream);
 /* The plan attn_fwd_dense / attn_fwd_sparse_topk would launch; host only. */
 attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p);
 attn_status attn_plan_sparse_topk(const attn_sparse_args* a, attn_plan* p);
+
+/*
+ * Split-KV dense forward, for shapes with few query rows (decode, short
+ * prefills) where one workgroup per row block would leave most of the GPU
+ * idle. The keys are cut into n ranges of whole key blocks; one launch
+ * computes, for every (row block, range), the attention of those rows over
+ * that range alone -- O_i normalised by the range's own denominator and
+ * lse_i without the sink -- into `workspace`; a second launch merges them:
+ *
+ *     lse = log(sum_i exp(lse_i) [+ exp(sink[h])]),  O = sum_i exp(lse_i - lse) O_i
+ *
+ * the output merge of context-parallel attention (TransformerEngine pull
+ * request 3259, "Flowchart": ring communication and output merge), here
+ * across the workgroups of one device. The result is the same attention as
+ * attn_fwd_dense computes (same arguments, same out and lse), up to the
+ * rounding of the fp32 partials.
+ *
+ *   n_splits         key ranges to use, 1..1024 (fewer when there are fewer
+ *                    key blocks); 0 lets the library choose enough ranges to
+ *                    fill the device twice over
+ *   workspace        device memory, 16-byte aligned, owned by the caller, of
+ *                    at least attn_splitkv_workspace_bytes(a, n_splits)
+ *                    bytes; its contents on return are unspecified. Calls
+ *                    sharing one workspace must be ordered on one stream.
+ *   workspace_bytes  its size
+ *
+ * When the plan needs one range only (few key blocks, Tk == 0, or a grid that
+ * already fills the device) this is exactly attn_fwd_dense and the workspace
+ * is not touched (NULL allowed). Split ranges are compiled for bf16 inputs:
+ * an f32 call with n_splits > 1 returns ATTN_UNSUPPORTED. A workspace that
+ * is NULL, misaligned or too small returns ATTN_INVALID_ARGUMENT before any
+ * launch. The merge launch is recorded under the dispatch path
+ * "splitkv_merge".
+ */
+attn_status attn_fwd_dense_splitkv(const attn_dense_args* a, int32_t n_splits, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_dense_splitkv needs for these arguments and
+ * n_splits (0 = the library's choice): n * B*H*Tq * (d_v + 1) * 4 for n > 1
+ * ranges, 0 when one range suffices, -1 on invalid arguments. Host only. */
+int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits);
+
+/* The number of key ranges the library would choose (n_splits = 0) for
+ * these arguments on the current device; -1 on invalid arguments. Host only
+ * (it reads the device's compute-unit count once, 256 when there is none). */
+int32_t attn_splitkv_choose(const attn_dense_args* a);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status s);

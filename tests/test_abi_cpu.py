@@ -159,3 +159,46 @@ def test_dispatch_counts_start_at_zero():
     A.reset_dispatch_counts()
     assert A.dispatch_count("dense_bf16_d128") == 0
     assert A.dispatch_count("no_such_path") == 0
+
+
+# ------------------------------------------------------------------ split-KV (host side)
+def test_splitkv_planning():
+    # prefill that already fills the device: one range, no workspace
+    assert A.splitkv_choose(2, 32, 8, 4096, 4096, 128, 128) == 1
+    assert A.splitkv_workspace_bytes(2, 32, 8, 4096, 4096, 128, 128) == 0
+    # decode: ranges of whole 128-key blocks, never more than there are blocks
+    assert A.splitkv_workspace_bytes(1, 8, 2, 1, 1000, 128, 128, n_splits=3) == 3 * 8 * 129 * 4
+    assert A.splitkv_workspace_bytes(1, 8, 2, 1, 1000, 128, 128, n_splits=100) == 8 * 8 * 129 * 4
+    n = A.splitkv_choose(8, 64, 1, 1, 32768, 512, 512, sinks=True)
+    assert 2 <= n <= 1024
+    assert A.splitkv_workspace_bytes(8, 64, 1, 1, 32768, 512, 512, sinks=True) == n * 8 * 64 * 513 * 4
+    # no keys: one range
+    assert A.splitkv_choose(1, 8, 2, 1, 0, 128, 128) == 1
+    with pytest.raises(A.AttnInvalidArgument):
+        A.splitkv_workspace_bytes(1, 8, 2, 1, 1000, 128, 128, n_splits=-1)
+    with pytest.raises(A.AttnInvalidArgument):
+        A.splitkv_workspace_bytes(1, 8, 2, 1, 1000, 128, 128, n_splits=5000)
+
+
+def _fake_dense(dtype=0):
+    a = A._shape_args(1, 8, 2, 1, 1000, 128, 128, "bf16" if dtype == 0 else "f32", True, False, None)
+    return a
+
+
+def test_splitkv_rejects_bad_workspace_before_launch():
+    lib = A.load_library()
+    a = _fake_dense()
+    need = lib.attn_splitkv_workspace_bytes(ctypes.byref(a), 4)
+    assert need > 0
+    st = lib.attn_fwd_dense_splitkv(ctypes.byref(a), 4, None, 0, None)
+    assert st == A.ATTN_INVALID_ARGUMENT and b"workspace" in lib.attn_last_error()
+    st = lib.attn_fwd_dense_splitkv(ctypes.byref(a), 4, ctypes.c_void_p(4096), need - 16, None)
+    assert st == A.ATTN_INVALID_ARGUMENT
+    st = lib.attn_fwd_dense_splitkv(ctypes.byref(a), 4, ctypes.c_void_p(4096 + 8), need, None)
+    assert st == A.ATTN_INVALID_ARGUMENT and b"aligned" in lib.attn_last_error()
+    st = lib.attn_fwd_dense_splitkv(ctypes.byref(a), 2000, ctypes.c_void_p(4096), need, None)
+    assert st == A.ATTN_INVALID_ARGUMENT
+    f = _fake_dense(dtype=1)
+    st = lib.attn_fwd_dense_splitkv(ctypes.byref(f), 4, ctypes.c_void_p(4096), 1 << 30, None)
+    assert st == A.ATTN_UNSUPPORTED
+
