@@ -266,8 +266,24 @@ struct SplitPlan {
   int64_t bytes;   // workspace bytes needed (0 when n == 1)
 };
 
-// Ranges of whole key blocks: enough of them that the launch fills the GPU
-// twice over (when n_req == 0), never more than there are key blocks.
+// Workgroups of `cfg` resident on one CU at once: the runtime's answer when a
+// device is present, else what its LDS allows.
+int resident_per_cu(const attn::KernelConfig* cfg) {
+  static std::atomic<int> cache[kMaxPaths];
+  const int i = path_index(cfg->path);
+  int v = (i >= 0) ? cache[i].load(std::memory_order_relaxed) : 0;
+  if (v > 0) return v;
+  v = cfg->occupancy ? cfg->occupancy() : 0;
+  if (v <= 0) v = std::max(1, (160 * 1024) / std::max(1, cfg->lds_bytes));
+  if (i >= 0) cache[i].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Ranges of whole key blocks, never more than there are key blocks. The
+// library's choice (n_req == 0) is the most ranges whose workgroups all run
+// in one round on the device: a second, partial round costs more than the
+// longer key loop of fewer, larger ranges, and every range adds partials to
+// write and merge.
 SplitPlan plan_split(const DensePlan& dp, const attn_dense_args* a, int n_req) {
   SplitPlan sp{1, a->Tk, (int64_t)a->B * a->H * a->Tq, 0};
   const int BN = dp.cfg->block_keys;
@@ -275,9 +291,9 @@ SplitPlan plan_split(const DensePlan& dp, const attn_dense_args* a, int n_req) {
   if (nblocks <= 1 || a->Tq == 0) return sp;
   int want = n_req;
   if (want == 0) {
-    const int64_t target = 2 * (int64_t)device_cus();
+    const int64_t slots = (int64_t)device_cus() * resident_per_cu(dp.cfg);
     const int64_t tiles = dp.kp.n_tiles > 0 ? dp.kp.n_tiles : 1;
-    want = (int)std::min<int64_t>(kMaxSplits, (target + tiles - 1) / tiles);
+    want = (int)std::min<int64_t>(kMaxSplits, slots / tiles);
   }
   want = std::min(want, nblocks);
   if (want <= 1) return sp;

@@ -1494,6 +1494,18 @@ attn_fwd_dma_kernel(const KernelParams p) {
 }
 
 template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
+int occupancy_dma() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>), NW * 64,
+          0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
 int launch_dma(const KernelParams& p, void* stream) {
   hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>),
                      dim3(p.n_tiles, p.n_splits > 1 ? p.n_splits : 1), dim3(NW * 64), 0,
@@ -1566,8 +1578,21 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) 
 #define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
   KernelConfig {                                                                                                 \
     NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::BM, BN, NW,                           \
-        DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, SPARSE> \
+        DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, SPARSE>, \
+        &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, SPARSE>                                                    \
   }
+
+template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
+int occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, QT, DS, NW, BN, F32, SPARSE>), NW * 64, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
 
 template <int DQK, int DV, int QT, int DS, int NW, int BN, bool F32, bool SPARSE>
 int launch(const KernelParams& p, void* stream) {
@@ -1579,7 +1604,8 @@ int launch(const KernelParams& p, void* stream) {
 #define CFG_ENTRY(NAME, DT, DQK, DV, QT, DS, NW, BN, F32, SPARSE)                                          \
   KernelConfig {                                                                                          \
     NAME, DT, DQK, DV, SPARSE, Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::BM, BN, NW,                    \
-        Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::LDS_BYTES, &launch<DQK, DV, QT, DS, NW, BN, F32, SPARSE> \
+        Cfg<DQK, DV, QT, DS, NW, BN, F32, SPARSE>::LDS_BYTES, &launch<DQK, DV, QT, DS, NW, BN, F32, SPARSE>, \
+        &occupancy<DQK, DV, QT, DS, NW, BN, F32, SPARSE>                                                   \
   }
 
 // (DS, waves, BN, LDS ring slots, two wave groups) per head-dim configuration;

@@ -65,6 +65,8 @@ int launch_merge(const MergeParams& m, void* stream);
 // Host-side launchers, one per compiled kernel configuration.
 // Return 0 on success, else the hipError_t of the launch.
 typedef int (*launch_fn)(const KernelParams& p, void* stream);
+// workgroups of a kernel that fit on one CU at once (0 when the device cannot be asked)
+typedef int (*occupancy_fn)();
 
 struct KernelConfig {
   const char* path;
@@ -73,6 +75,7 @@ struct KernelConfig {
   int sparse;
   int block_rows, block_keys, waves, lds_bytes;
   launch_fn launch;
+  occupancy_fn occupancy;
 };
 
 // Table of compiled configurations (defined in attn_kernels.hip).

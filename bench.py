@@ -41,7 +41,8 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak); sparse top-k GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-WORKLOAD_IDS = {"tiny": 1, "gqa": 2, "mla": 3, "mqa512": 4, "sparse": 5}
+WORKLOAD_IDS = {"tiny": 1, "gqa": 2, "mla": 3, "mqa512": 4, "sparse": 5, "decode512": 6}
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 KERNEL_SOURCES = ("attention_forward_attn_amd/csrc/attn_kernels.hip",
                   "attention_forward_attn_amd/csrc/attn_params.h")
 
@@ -74,7 +75,8 @@ def describe(n: int) -> str:
 
     s = synth.spec(n)
     if s.kind == "dense":
-        return (f"{s.name}: dense causal B={s.B} H={s.H} Hkv={s.Hkv} T={s.Tq} d_qk={s.d_qk} d_v={s.d_v} "
+        t = f"T={s.Tq}" if s.Tq == s.Tk else f"Tq={s.Tq} Tk={s.Tk}"
+        return (f"{s.name}: dense causal B={s.B} H={s.H} Hkv={s.Hkv} {t} d_qk={s.d_qk} d_v={s.d_v} "
                 f"{s.dtype}" + (" sinks" if s.sinks else ""))
     return f"{s.name}: sparse top-k Sq={s.Sq} Hq={s.Hq} N={s.N} d_qk={s.d_qk} d_v={s.d_v} topk={s.topk} bf16"
 
@@ -97,8 +99,9 @@ def work(n: int) -> dict:
     return {"pairs": pairs, "flops": flops, "bytes": nbytes, "kind": s.kind}
 
 
-def make_call(n: int):
-    """Device-resident inputs and outputs for workload n and a closure that runs one step."""
+def make_call(n: int, split: bool = False):
+    """Device-resident inputs and outputs for workload n and a closure that runs one step
+    (split: the split-KV call with a preallocated workspace)."""
     import torch
 
     import attention_forward_attn_amd as A
@@ -112,8 +115,17 @@ def make_call(n: int):
         out = torch.empty((s.B, s.H, s.Tq, s.d_v), dtype=q.dtype, device="cuda")
         lse = torch.empty((s.B, s.H, s.Tq), dtype=torch.float32, device="cuda")
 
+        ws = None
+        if split:
+            nb = A.splitkv_workspace_bytes(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v, dtype=s.dtype,
+                                           causal=s.causal, sinks=s.sinks)
+            ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+
         def step():
-            A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse)
+            if split:
+                A.dense_splitkv(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse, workspace=ws)
+            else:
+                A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse)
 
         path = A.plan_dense(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v, dtype=s.dtype, sinks=s.sinks)["path"]
     else:
@@ -150,7 +162,10 @@ def time_steps(step, steps: int, warmup: int) -> dict:
 
 def roofline(n: int, kernel_ms: float) -> dict:
     w = work(n)
-    if w["kind"] == "dense":
+    # bound by whichever resource the algorithmic work saturates first
+    # (ridge = peak flops / peak bytes = 312.5 flop/B): the prefill layers are
+    # MFMA bound, decode and the sparse gather HBM bound
+    if w["flops"] / w["bytes"] >= RIDGE_FLOP_PER_BYTE:
         ach = w["flops"] / (kernel_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(n)}
@@ -228,10 +243,10 @@ def cpu_baseline(n: int, inp: dict, budget_s: float = 12.0) -> dict:
             "seconds": round(dt, 2)}
 
 
-def measure(n: int, steps: int, warmup: int) -> dict:
+def measure(n: int, steps: int, warmup: int, split: bool = False) -> dict:
     import attention_forward_attn_amd as A
 
-    step, path, inp = make_call(n)
+    step, path, inp = make_call(n, split)
     A.reset_dispatch_counts()
     t = time_steps(step, steps, warmup)
     launched = A.dispatch_count(path)
@@ -239,13 +254,15 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     # otherwise the numbers are not this path's and the run stops
     if launched != steps + warmup:
         raise RuntimeError(f"NotEngaged: expected {steps + warmup} launches of {path}, saw {launched}")
+    if split and A.dispatch_count("splitkv_merge") != steps + warmup:
+        raise RuntimeError("NotEngaged: the split-KV merge did not run once per step")
     w = work(n)
     rl = roofline(n, t["kernel_ms_mean"])
-    if w["kind"] == "dense":
+    if rl["bound"] == "mfma":
         value, unit = w["flops"] / (t["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
     else:
         value, unit = w["bytes"] / (t["ms_per_step"] * 1e-3) / 1e9, "GB/s"
-    log(f"[bench] {describe(n)} | path {path} | kernel {t['kernel_ms_mean']:.4f} ms (median "
+    log(f"[bench] {describe(n)} | path {path}{' split-KV' if split else ''} | kernel {t['kernel_ms_mean']:.4f} ms (median "
         f"{t['kernel_ms_median']:.4f}) | step {t['ms_per_step']:.4f} ms | {rl['achieved']} {rl['unit']} "
         f"= {100 * rl['frac']:.1f}% of peak")
     return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp,
@@ -440,7 +457,7 @@ def main():
 
     A.load_library()
     n = WORKLOAD_IDS[args.workload]
-    prim = measure(n, args.steps, args.warmup)
+    prim = measure(n, args.steps, args.warmup, split=(n == 6))
     others = []
     if not args.primary_only:
         for m in (2, 3, 4, 5):
@@ -452,11 +469,26 @@ def main():
                            "roofline": r["roofline"], "verdict": r["verdict"]})
             del r
             torch.cuda.empty_cache()
+    # rows beyond the five: the split-KV forward on a decode step (Tq = 1),
+    # with the plain one-launch path on the same inputs for context
+    next_rows = []
+    if not args.primary_only and n != 6:
+        st, wu = max(10, args.steps // 2), max(3, args.warmup // 2)
+        r = measure(6, st, wu, split=True)
+        rp = measure(6, st, wu, split=False)
+        next_rows.append({"row": "split-KV forward (attn_fwd_dense_splitkv), decode", "workload": describe(6),
+                          "path": r["path"] + " + splitkv_merge", "value": round(r["value"], 3), "unit": r["unit"],
+                          "kernel_ms": round(r["timing"]["kernel_ms_mean"], 5), "roofline": r["roofline"],
+                          "verdict": r["verdict"],
+                          "plain_path": {"path": rp["path"], "value": round(rp["value"], 3), "unit": rp["unit"],
+                                         "kernel_ms": round(rp["timing"]["kernel_ms_mean"], 5)}})
+        del r, rp
+        torch.cuda.empty_cache()
     ceil = None
     if not args.no_ceilings:
         ceil = ceilings()
         add_ceiling_fraction(prim["roofline"], ceil)
-        for o in others:
+        for o in others + next_rows:
             add_ceiling_fraction(o["roofline"], ceil)
     cpu = None
     if not args.no_cpu_baseline:
@@ -484,6 +516,7 @@ def main():
         "cpu_baseline": cpu,
         "ceilings": ceil,
         "workloads": others,
+        "next_rows": next_rows,
     }
     print(json.dumps(line), flush=True)
 

@@ -194,8 +194,8 @@ attn_status attn_plan_sparse_topk(const attn_sparse_args* a, attn_plan* p);
  * rounding of the fp32 partials.
  *
  *   n_splits         key ranges to use, 1..1024 (fewer when there are fewer
- *                    key blocks); 0 lets the library choose enough ranges to
- *                    fill the device twice over
+ *                    key blocks); 0 lets the library choose: the most
+ *                    ranges whose workgroups all fit on the device at once
  *   workspace        device memory, 16-byte aligned, owned by the caller, of
  *                    at least attn_splitkv_workspace_bytes(a, n_splits)
  *                    bytes; its contents on return are unspecified. Calls
@@ -220,7 +220,8 @@ int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits)
 
 /* The number of key ranges the library would choose (n_splits = 0) for
  * these arguments on the current device; -1 on invalid arguments. Host only
- * (it reads the device's compute-unit count once, 256 when there is none). */
+ * (it reads the device's compute-unit count and the kernel's workgroups per
+ * CU once; without a device it assumes 256 CUs and the LDS limit). */
 int32_t attn_splitkv_choose(const attn_dense_args* a);
 
 /* Static text for a status code. */

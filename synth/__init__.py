@@ -20,6 +20,11 @@ The five workloads restate the shapes that the pages measure or discuss:
   2176 gathered rows with d_qk=512, the FlashMLA shape of the TensorRT-LLM
   page ("Description"), over one shared pool of 65536 rows, bf16.
 
+One more workload measures the split-KV forward (a "next" step beyond the
+five): ``decode512`` -- one new token per sequence (Tq=1) of the MQA d=512
+layer with sinks (the absorbed-MQA decode the ArcFlash page discusses at
+t_q = 1), B=8 sequences, a 32768-token cache, bf16; seed 6, same recipe.
+
 Generation recipe (fixed so that every consumer sees identical bits):
 ``torch.Generator('cpu').manual_seed(seed)`` with seed = workload number (1..5);
 draw order q, k, v, sinks, each ``torch.randn(shape, dtype=float32)``; cast to
@@ -100,9 +105,15 @@ WORKLOADS = {
     5: SparseSpec("sparse", 5, Sq=13312, Hq=64, N=65536, d_qk=512, d_v=512, topk=2176),
 }
 
+# measured beyond the five (split-KV decode)
+NEXT_WORKLOADS = {
+    6: DenseSpec("decode512", 6, B=8, H=64, Hkv=1, Tq=1, Tk=32768, d_qk=512, d_v=512,
+                 dtype="bf16", causal=True, sinks=True),
+}
+
 
 def spec(n: int):
-    return WORKLOADS[n]
+    return WORKLOADS[n] if n in WORKLOADS else NEXT_WORKLOADS[n]
 
 
 def _torch_dtype(name: str):
