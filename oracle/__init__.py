@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward -- test infrastructure only.
+"""fp64 CPU oracle for the attention forward and backward -- test infrastructure only.
 
 Importable by the tests, the package smoke check and the bench's CPU-baseline
 leg; never by the product path.
@@ -6,10 +6,12 @@ leg; never by the product path.
 from .attention import (  # noqa: F401
     causal_visible,
     dense_attention,
+    dense_attention_backward,
     dense_attention_tiled,
     gather_rows,
     merge_partials,
     repeat_kv,
     sparse_topk_attention,
+    sum_kv_groups,
     tile_rows_for_budget,
 )

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the fused attention forward.
+"""fp64 CPU oracle for the fused attention forward and its backward.
 
 TEST INFRASTRUCTURE. Only the tests, the package's smoke check and the bench's
 CPU-baseline leg may import this module. It shares no code with the HIP path:
@@ -24,6 +24,12 @@ What it computes, and the passage each part follows:
 * Sparse top-k: each query attends only to the rows of one shared KV pool that
   its index list names (TensorRT-LLM page, "Description": 13312 queries x 64
   heads x 2176 top-k rows, d_qk 512).
+* Backward: the Q/K/V gradients that a raw attention backward returns after
+  the forward and the output merge (TransformerEngine page, "Flowchart" and
+  "Summary": raw forward/backward wrappers with LSE handling). The pages give
+  no formulas; the oracle is the chain rule through the forward definition
+  above, written out step by step (and the sink's gradient, since the sink is
+  a per-head parameter of the same softmax).
 
 Readings where the pages are silent (each one stated again where it is used):
 
@@ -291,3 +297,80 @@ def merge_partials(parts, sink: Optional[float] = None):
         w = np.where(np.isfinite(l), np.exp(l - lse_safe), 0.0)
         out = out + w[..., None] * o
     return out, lse
+
+
+def _softmax_backward(P: np.ndarray, dP: np.ndarray, dO: np.ndarray, O: np.ndarray) -> np.ndarray:
+    """dS = P * (dP - D) with D = rowsum(dO * O): the softmax Jacobian applied to dP.
+
+    With a sink the rows of P sum to 1 - p_sink; the Jacobian of the visible
+    entries is still P * (dP - sum_j P_j dP_j), and sum_j P_j dP_j = rowsum(dO * O)
+    because O = P . V.
+    """
+    D = (dO * O).sum(axis=1)
+    return P * (dP - D[:, None])
+
+
+def sum_kv_groups(x: np.ndarray, g: int) -> np.ndarray:
+    """Adjoint of ``repeat_kv``: ``y[b, kv] = sum_rep x[b, kv*g + rep]`` (kv-major heads)."""
+    B, H, T, D = x.shape
+    y = np.zeros((B, H // g, T, D), dtype=x.dtype)
+    for kv in range(H // g):
+        for rep in range(g):
+            y[:, kv] += x[:, kv * g + rep]
+    return y
+
+
+def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks=None):
+    """Gradients of the dense forward in fp64: (dq, dk, dv, dsinks).
+
+    ``dout`` = dL/dO [B,H,Tq,d_v] for a scalar loss L of the output; the lse
+    output is a saved statistic and carries no gradient. dsinks is None when
+    ``sinks`` is None. Steps, per (b, h), through the forward's definition:
+
+      1. Recompute the forward: S = scale * q . K_h^T (explicit, masked), the
+         row softmax P with the sink in the denominator, O = P . V_h.
+      2. dV_h = P^T . dO                      (O is linear in V)
+      3. dP = dO . V_h^T                      (O is linear in P)
+      4. D = rowsum(dO * O)                   (= rowsum(P * dP))
+      5. dS = P * (dP - D)                    (softmax Jacobian, sink included:
+                                               the sink only enlarges the
+                                               denominator, so it appears in P
+                                               and D but has no column)
+      6. dq = scale * dS . K_h,  dK_h = scale * dS^T . q
+      7. dsink_h = -sum over rows of p_sink * D, with p_sink = exp(sink - lse)
+      8. dk, dv of kv head kv = sum of dK_h, dV_h over the g heads that read
+         it (the adjoint of repeat_kv's kv-major copy).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Tq, Dqk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    Dv = v.shape[-1]
+    assert H % Hkv == 0, "H must be a multiple of Hkv"
+    g = H // Hkv
+    K = repeat_kv(k, g)
+    V = repeat_kv(v, g)
+    sk = None if sinks is None else _f64(sinks)
+    dq = np.zeros_like(q)
+    dK = np.zeros((B, H, Tk, Dqk))
+    dV = np.zeros((B, H, Tk, Dv))
+    dsk = None if sk is None else np.zeros(H)
+    ts = np.arange(Tq)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ K[b, h].T)
+            if causal:
+                S = np.where(_causal_mask(ts, Tq, Tk), S, NEG_INF)
+            sink = None if sk is None else float(sk[h])
+            P, lse = _softmax_rows(S, sink)
+            O = P @ V[b, h]
+            dO = dout[b, h]
+            dV[b, h] = P.T @ dO
+            dP = dO @ V[b, h].T
+            dS = _softmax_backward(P, dP, dO, O)
+            dq[b, h] = scale * (dS @ K[b, h])
+            dK[b, h] = scale * (dS.T @ q[b, h])
+            if sink is not None:
+                D = (dO * O).sum(axis=1)
+                p_sink = np.where(np.isfinite(lse), np.exp(sink - np.where(np.isfinite(lse), lse, 0.0)), 0.0)
+                dsk[h] -= float((p_sink * D).sum())
+    return dq, sum_kv_groups(dK, g), sum_kv_groups(dV, g), dsk

@@ -1,0 +1,65 @@
+"""The oracle's backward against finite differences, torch autograd, closed forms and
+invariants; planted mistakes in it must each be caught (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as OA
+from tests import pins_bwd
+
+
+@pytest.mark.parametrize("name", sorted(pins_bwd.ALL_CHECKS))
+def test_backward_pin(name):
+    err = pins_bwd.ALL_CHECKS[name]()
+    assert err <= pins_bwd.TOL, f"{name}: discrepancy {err:.3e}"
+
+
+def _assert_caught(names):
+    results = {n: pins_bwd.ALL_CHECKS[n]() for n in names}
+    assert any(v > pins_bwd.TOL for v in results.values()), f"mutation not caught: {results}"
+
+
+def test_dropped_D_term_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_softmax_backward", lambda P, dP, dO, O: P * dP)
+    _assert_caught(["bwd_finite_differences", "bwd_invariants"])
+
+
+def test_wrong_sign_caught(monkeypatch):
+    orig = OA._softmax_backward
+    monkeypatch.setattr(OA, "_softmax_backward", lambda P, dP, dO, O: -orig(P, dP, dO, O))
+    _assert_caught(["bwd_finite_differences", "bwd_library_autograd"])
+
+
+def test_rep_major_head_sum_caught(monkeypatch):
+    def rep_major(x, g):
+        B, H, T, D = x.shape
+        y = np.zeros((B, H // g, T, D))
+        for kv in range(H // g):
+            for rep in range(g):
+                y[:, kv] += x[:, rep * (H // g) + kv]
+        return y
+
+    monkeypatch.setattr(OA, "sum_kv_groups", rep_major)
+    _assert_caught(["bwd_finite_differences", "bwd_library_autograd"])
+
+
+def test_missing_scale_caught(monkeypatch):
+    orig = OA.dense_attention_backward
+
+    def unscaled(q, k, v, dout, *, scale, **kw):
+        dq, dk, dv, ds = orig(q, k, v, dout, scale=scale, **kw)
+        return dq / scale, dk / scale, dv, ds
+
+    monkeypatch.setattr(oracle, "dense_attention_backward", unscaled)
+    _assert_caught(["bwd_finite_differences", "bwd_library_autograd"])
+
+
+def test_sink_gradient_sign_caught(monkeypatch):
+    orig = OA.dense_attention_backward
+
+    def flipped(*a, **kw):
+        dq, dk, dv, ds = orig(*a, **kw)
+        return dq, dk, dv, (None if ds is None else -ds)
+
+    monkeypatch.setattr(oracle, "dense_attention_backward", flipped)
+    _assert_caught(["bwd_finite_differences", "bwd_library_autograd"])
