@@ -7,6 +7,7 @@ entry points raises.
 
     out, lse = dense(q, k, v, causal=True, scale=None, sinks=None)
     out, lse = sparse_topk(q, kv, idx, d_v=512, scale=None, sinks=None)
+    dq, dk, dv, dsinks = dense_backward(q, k, v, out, dout, lse, causal=True, sinks=None)
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -72,11 +73,33 @@ class AttnPlan(ctypes.Structure):
     ]
 
 
+class AttnDenseBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_st", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_sb", ctypes.c_int64), ("v_sh", ctypes.c_int64), ("v_st", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_st", ctypes.c_int64),
+        ("dout", ctypes.c_void_p), ("do_sb", ctypes.c_int64), ("do_sh", ctypes.c_int64), ("do_st", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dq_sb", ctypes.c_int64), ("dq_sh", ctypes.c_int64), ("dq_st", ctypes.c_int64),
+        ("dk", ctypes.c_void_p), ("dk_sb", ctypes.c_int64), ("dk_sh", ctypes.c_int64), ("dk_st", ctypes.c_int64),
+        ("dv", ctypes.c_void_p), ("dv_sb", ctypes.c_int64), ("dv_sh", ctypes.c_int64), ("dv_st", ctypes.c_int64),
+        ("dsinks", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = (
     "attn_abi_version", "attn_fwd_dense", "attn_fwd_sparse_topk", "attn_plan_dense",
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
-    "attn_splitkv_workspace_bytes", "attn_splitkv_choose",
+    "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
 )
 
 _lib = None
@@ -116,6 +139,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.attn_splitkv_choose.argtypes = [ctypes.POINTER(AttnDenseArgs)]
     lib.attn_splitkv_choose.restype = ctypes.c_int32
+    lib.attn_bwd_dense.argtypes = [ctypes.POINTER(AttnDenseBwdArgs), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.attn_bwd_dense.restype = ctypes.c_int
+    lib.attn_bwd_dense_workspace_bytes.argtypes = [ctypes.POINTER(AttnDenseBwdArgs)]
+    lib.attn_bwd_dense_workspace_bytes.restype = ctypes.c_int64
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -387,3 +414,87 @@ def budget_tile_rows(budget_bytes: int, Tk: int, elt_bytes: int) -> int:
 
 def abi_version() -> int:
     return int(load_library().attn_abi_version())
+
+
+def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: float, sinks=None,
+                   dsinks=None) -> AttnDenseBwdArgs:
+    """Fill the backward's C argument struct from tensors (unit last stride)."""
+    B, H, Tq, dqk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    a = AttnDenseBwdArgs()
+    a.struct_size = ctypes.sizeof(AttnDenseBwdArgs)
+    a.dtype = _dtype_code(q)
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, dqk, v.shape[-1]
+    a.causal = 1 if causal else 0
+    a.scale = float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    a.q, (a.q_sb, a.q_sh, a.q_st) = q.data_ptr(), q.stride()[:3]
+    a.k, (a.k_sb, a.k_sh, a.k_st) = k.data_ptr(), k.stride()[:3]
+    a.v, (a.v_sb, a.v_sh, a.v_st) = v.data_ptr(), v.stride()[:3]
+    a.out, (a.o_sb, a.o_sh, a.o_st) = out.data_ptr(), out.stride()[:3]
+    a.dout, (a.do_sb, a.do_sh, a.do_st) = dout.data_ptr(), dout.stride()[:3]
+    a.dq, (a.dq_sb, a.dq_sh, a.dq_st) = dq.data_ptr(), dq.stride()[:3]
+    a.dk, (a.dk_sb, a.dk_sh, a.dk_st) = dk.data_ptr(), dk.stride()[:3]
+    a.dv, (a.dv_sb, a.dv_sh, a.dv_st) = dv.data_ptr(), dv.stride()[:3]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.dsinks = dsinks.data_ptr() if dsinks is not None else None
+    return a
+
+
+def dense_backward(q, k, v, out, dout, lse, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
+                   dq=None, dk=None, dv=None, dsinks=None, workspace=None, stream=None):
+    """Dense attention backward on the GPU (bf16): returns (dq, dk, dv, dsinks).
+
+    ``out`` and ``lse`` are the forward's results for (q, k, v, sinks); ``dout``
+    is dL/dout. dk and dv are summed over the query heads that share each kv
+    head. dsinks (fp32 [H]) is computed when ``sinks`` is given, else None.
+    ``workspace`` is a uint8 device tensor of at least
+    :func:`bwd_workspace_bytes` bytes (allocated here when None). Launches on
+    ``stream`` and does not synchronise.
+    """
+    import torch
+
+    lib = load_library()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or not sinks.is_contiguous():
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
+        if dsinks is None:
+            dsinks = torch.empty_like(sinks)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [B, H, Tq]")
+    a = dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, causal=causal, scale=scale, sinks=sinks,
+                       dsinks=dsinks)
+    # a negative size means invalid sizes or head dims: the call below then
+    # reports the library's own status before launching anything
+    need = int(lib.attn_bwd_dense_workspace_bytes(ctypes.byref(a)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_bwd_dense(ctypes.byref(a), ctypes.c_void_p(ws_ptr), ws_bytes,
+                              ctypes.c_void_p(_stream_handle(stream))))
+    return dq, dk, dv, dsinks
+
+
+def bwd_workspace_bytes(B, H, Hkv, Tq, Tk, d_qk, d_v) -> int:
+    """Workspace bytes of the dense backward for these sizes (host only)."""
+    a = AttnDenseBwdArgs()
+    a.struct_size = ctypes.sizeof(AttnDenseBwdArgs)
+    a.dtype = ATTN_BF16
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, d_qk, d_v
+    a.causal, a.scale = 1, 1.0 / math.sqrt(d_qk)
+    n = int(load_library().attn_bwd_dense_workspace_bytes(ctypes.byref(a)))
+    if n < 0:
+        _check(ATTN_INVALID_ARGUMENT)
+    return n

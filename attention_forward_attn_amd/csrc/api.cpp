@@ -44,8 +44,14 @@ std::atomic<int> g_logged[kMaxPaths];
 constexpr int kMergeSlot = kMaxPaths - 1;
 constexpr const char* kMergePath = "splitkv_merge";
 
+// the dense backward paths have counters of their own, below the merge's
+constexpr const char* kBwdPaths[] = {"dense_bwd_bf16_d64", "dense_bwd_bf16_d128", "dense_bwd_bf16_d192_v128"};
+constexpr int kBwdSlot0 = kMergeSlot - 3;
+
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
+  for (int i = 0; i < 3; ++i)
+    if (std::strcmp(path, kBwdPaths[i]) == 0) return kBwdSlot0 + i;
   int n = 0;
   const attn::KernelConfig* t = attn::kernel_table(&n);
   for (int i = 0; i < n && i < kMaxPaths; ++i)
@@ -439,6 +445,106 @@ const char* attn_status_string(attn_status s) {
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- dense backward
+namespace {
+
+int bwd_path(int d_qk, int d_v) {
+  if (d_qk == 64 && d_v == 64) return 0;
+  if (d_qk == 128 && d_v == 128) return 1;
+  if (d_qk == 192 && d_v == 128) return 2;
+  return -1;
+}
+
+// sizes, dtype and head dims only (what the workspace size depends on)
+attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_dense_bwd_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_dense_bwd_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_dense_bwd_args));
+  if (a->dtype != ATTN_BF16) return fail(ATTN_UNSUPPORTED, "the backward is compiled for bf16 only (dtype %d)", a->dtype);
+  if (a->B < 1 || a->H < 1 || a->Hkv < 1) return fail(ATTN_INVALID_ARGUMENT, "B, H, Hkv must be >= 1");
+  if (a->Tq < 0 || a->Tk < 0) return fail(ATTN_INVALID_ARGUMENT, "Tq, Tk must be >= 0");
+  if (a->H % a->Hkv != 0) return fail(ATTN_INVALID_ARGUMENT, "H (%d) must be a multiple of Hkv (%d)", a->H, a->Hkv);
+  if (a->d_qk < 1 || a->d_v < 1) return fail(ATTN_INVALID_ARGUMENT, "head dims must be >= 1");
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (bwd_path(a->d_qk, a->d_v) < 0)
+    return fail(ATTN_UNSUPPORTED, "no compiled dense backward for (d_qk, d_v) = (%d, %d)", a->d_qk, a->d_v);
+  if ((int64_t)a->B * a->Hkv > 65535) return fail(ATTN_UNSUPPORTED, "B * Hkv above 65535 (grid y)");
+  return ATTN_OK;
+}
+
+attn_status validate_bwd(const attn_dense_bwd_args* a) {
+  const attn_status s = validate_bwd_shape(a);
+  if (s != ATTN_OK) return s;
+  if (a->Tq > 0 && (!a->q || !a->out || !a->dout || !a->lse || !a->dq))
+    return fail(ATTN_INVALID_ARGUMENT, "q, out, dout, lse, dq must be non-NULL when Tq > 0");
+  if (a->Tk > 0 && (!a->k || !a->v || !a->dk || !a->dv))
+    return fail(ATTN_INVALID_ARGUMENT, "k, v, dk, dv must be non-NULL when Tk > 0");
+  if (a->dsinks && !a->sinks) return fail(ATTN_INVALID_ARGUMENT, "dsinks given without sinks");
+  const void* ptrs[] = {a->q, a->k, a->v, a->out, a->dout, a->lse, a->sinks, a->dq, a->dk, a->dv, a->dsinks};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const int64_t strides[] = {a->q_sb,  a->q_sh,  a->q_st,  a->k_sb,  a->k_sh,  a->k_st,  a->v_sb,  a->v_sh,
+                             a->v_st,  a->o_sb,  a->o_sh,  a->o_st,  a->do_sb, a->do_sh, a->do_st, a->dq_sb,
+                             a->dq_sh, a->dq_st, a->dk_sb, a->dk_sh, a->dk_st, a->dv_sb, a->dv_sh, a->dv_st};
+  for (int64_t s : strides)
+    if (s < 0 || s % 8 != 0)
+      return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and keep rows 16-byte aligned (multiple of 8 elements)");
+  if (a->Tq > 1 && (a->q_st < a->d_qk || a->dq_st < a->d_qk || a->o_st < a->d_v || a->do_st < a->d_v))
+    return fail(ATTN_INVALID_ARGUMENT, "query-side token stride smaller than the head dim");
+  if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v || a->dk_st < a->d_qk || a->dv_st < a->d_v))
+    return fail(ATTN_INVALID_ARGUMENT, "key-side token stride smaller than the head dim");
+  return ATTN_OK;
+}
+
+int64_t bwd_workspace(const attn_dense_bwd_args* a) {
+  const int64_t rows = (int64_t)a->B * a->H * a->Tq;
+  return (rows * 4 + 255) / 256 * 256;
+}
+
+}  // namespace
+
+int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a) {
+  g_last_error.clear();
+  if (validate_bwd_shape(a) != ATTN_OK) return -1;
+  return bwd_workspace(a);
+}
+
+attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  attn_status s = validate_bwd(a);
+  if (s != ATTN_OK) return s;
+  const int64_t need = bwd_workspace(a);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_INVALID_ARGUMENT, "the backward needs a workspace of %lld bytes, got %lld", (long long)need,
+                (long long)(workspace ? workspace_bytes : 0));
+  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  attn::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.dout = a->dout; p.lse = a->lse; p.sinks = a->sinks;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv; p.dsinks = a->dsinks;
+  p.D = static_cast<float*>(workspace);
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_st = a->q_st;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
+  p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_st = a->o_st;
+  p.do_sb = a->do_sb; p.do_sh = a->do_sh; p.do_st = a->do_st;
+  p.dq_sb = a->dq_sb; p.dq_sh = a->dq_sh; p.dq_st = a->dq_st;
+  p.dk_sb = a->dk_sb; p.dk_sh = a->dk_sh; p.dk_st = a->dk_st;
+  p.dv_sb = a->dv_sb; p.dv_sh = a->dv_sh; p.dv_st = a->dv_st;
+  p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
+  p.causal = a->causal;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  const int err = attn::launch_bwd(p, a->d_qk, a->d_v, stream);
+  if (err != 0)
+    return fail(ATTN_HIP_ERROR, "launch of the dense backward failed: %s", hipGetErrorString((hipError_t)err));
+  const int bp = bwd_path(a->d_qk, a->d_v);
+  note_dispatch(kBwdSlot0 + bp, kBwdPaths[bp]);
+  return ATTN_OK;
+}
 
 uint64_t attn_dispatch_count(const char* path) {
   if (!path) return 0;

@@ -1,0 +1,530 @@
+// Attention backward for AMD CDNA4 (gfx950 / MI355X), bf16 inputs.
+//
+// Gradients of O = softmax(scale * Q K^T + mask [+ sink in the denominator]) V
+// with respect to q, k, v and the sinks, from the forward's inputs, its
+// output O and lse, and dO = dL/dO. This is the raw attention backward that
+// follows the forward and the output merge in TransformerEngine's
+// context-parallel attention ("Flowchart": raw backward -> Q/K/V gradients;
+// "Summary": raw forward/backward wrappers with LSE handling). With
+// P = exp(scale * q.k - lse) recomputed from the saved lse:
+//
+//   D    = rowsum(dO * O)                       (row dots)
+//   dV   = P^T dO,  dP = dO V^T,  dS = P (dP - D)
+//   dK   = scale dS^T Q,  dQ = scale dS K
+//   dsink_h = -sum over rows of exp(sink_h - lse) D
+//
+// GQA/MQA: the keys of kv head kvh are read by the g query heads kvh*g ..
+// kvh*g + g-1 (kv-major), so dK and dV sum over those heads.
+//
+// Four launches, none with atomics (the result does not depend on timing):
+//
+//  1. bwd_dot_kernel   D for every row, several rows per wave.
+//  2. bwd_dsink_kernel one workgroup per head sums its rows' sink terms.
+//  3. bwd_dkdv_kernel  a workgroup owns 32 keys per wave of one (b, kv head);
+//                      K and V of its keys stay in registers (the B operands
+//                      of S = Q K^T and dP = dO V^T) while it streams the
+//                      query rows of all g heads through LDS (Q and dO tiles);
+//                      dV^T += dO^T P and dK^T += Q^T dS take their A operands
+//                      from the same tiles by transposed LDS reads and their
+//                      B operands straight from the P / dS accumulators.
+//  4. bwd_dq_kernel    a workgroup owns 32 folded query rows per wave (the
+//                      forward's tiling); Q and dO rows stay in registers
+//                      while K and V blocks stream through LDS; S^T and dP^T
+//                      are recomputed and dQ^T += K^T dS^T.
+//
+// Scores and probabilities never leave the CU; the only workspace is D.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_params.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16_t;
+typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// two floats -> two bf16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  const u32x4 w = {pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// bf16 halves of a 32-bit word, widened exactly
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 16-byte chunk swizzle of a tile row with CPR chunks (64 LDS banks): 16
+// consecutive rows send one logical chunk to distinct bank groups, and
+// aligned groups of 4 rows send a 4-chunk group to distinct groups. Rows of
+// 128 + 256n bytes use a 3-bit XOR inside aligned 8-chunk groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR % 8 == 0, "rows are whole 8-chunk groups");
+  if constexpr (CPR % 16 == 0)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// element offset of logical chunk c of tile row r
+template <int CPR>
+__device__ __forceinline__ int chunk_at(int r, int c) {
+  return r * (CPR * 8) + ((c ^ swz<CPR>(r)) << 3);
+}
+
+// A operand (rows of a row-major tile): lane row `row`, columns 16s + 8lh .. +7
+template <int CPR>
+__device__ __forceinline__ bf16x8 row_frag(const bf16_t* tile, int row, int s, int lh) {
+  return *reinterpret_cast<const bf16x8*>(tile + chunk_at<CPR>(row, 2 * s + lh));
+}
+
+// A operand X^T (32 columns of X by 16 rows) from a row-major tile X by two
+// transposed reads. The 16 rows r0..r0+15 (r0 a multiple of 16) arrive in the
+// order {0-3, 8-11} for lanes 0-31 and {4-7, 12-15} for lanes 32-63, which is
+// the order in which a 32x32 accumulator with those rows hands them to the B
+// operand (pack8 of its elements 8ks..8ks+7), so no shuffle is needed.
+template <int CPR>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int r0, int c0, int lane) {
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = (vg >> 1) * 4 + (vi >> 2);
+  const int col = c0 + (vg & 1) * 16 + 4 * (vi & 3);
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = r0 + vrow + 8 * h;
+    const bf16_t* ptr = tile + row * (CPR * 8) + (((col >> 3) ^ swz<CPR>(row)) << 3) + (col & 7);
+    const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)ptr);
+    w[2 * h] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
+    w[2 * h + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+// ---------------------------------------------------------------------------
+// 1. D = rowsum(dO * O): LPR = DV/8 lanes per row, 64/LPR rows per wave
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ void __launch_bounds__(256) bwd_dot_kernel(const BwdParams p) {
+  constexpr int LPR = DV / 8, RPW = 64 / LPR;
+  static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "power-of-two lanes per row");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t R = (int64_t)p.B * p.H * p.Tq;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  const int c = lane % LPR;
+  float s = 0.f;
+  if (row < R) {
+    const int t = (int)(row % p.Tq);
+    const int h = (int)((row / p.Tq) % p.H);
+    const int b = (int)(row / ((int64_t)p.Tq * p.H));
+    const u32x4 o = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.out) + b * p.o_sb +
+                                                    h * p.o_sh + t * p.o_st + c * 8);
+    const u32x4 d = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb +
+                                                    h * p.do_sh + t * p.do_st + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += bf_lo(o[e]) * bf_lo(d[e]) + bf_hi(o[e]) * bf_hi(d[e]);
+  }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (row < R && c == 0) p.D[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dsink_h = -sum_{b,t} exp(sink_h - lse) D
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_dsink_kernel(const BwdParams p) {
+  __shared__ float part[4];
+  const int h = blockIdx.x;
+  const float sk = p.sinks[h];
+  float s = 0.f;
+  const int n = p.B * p.Tq;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int b = i / p.Tq, t = i % p.Tq;
+    const int64_t row = ((int64_t)b * p.H + h) * p.Tq + t;
+    const float l = p.lse[row];
+    if (l != -INFINITY && sk != -INFINITY) s += __expf(sk - l) * p.D[row];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) p.dsinks[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK, dV: one workgroup per 32*NW keys of one (b, kv head)
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int NW, int BQ>
+__global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int BNK = 32 * NW;  // keys per workgroup; BQ query rows per step (32-row sub-blocks)
+  constexpr int NT = NW * 64;
+  constexpr int CPQ = DQK / 8, CPO = DV / 8;
+  constexpr int KS = DQK / 16, VS = DV / 16, DTK = DQK / 32, DTV = DV / 32;
+  constexpr int QCH = BQ * CPQ / NT, OCH = BQ * CPO / NT;  // 16-byte chunks per thread per step
+  static_assert(BQ * CPQ % NT == 0 && BQ * CPO % NT == 0, "tiles split evenly over the threads");
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims are whole 32-column tiles");
+  __shared__ __attribute__((aligned(16))) bf16_t qt[BQ * DQK];
+  __shared__ __attribute__((aligned(16))) bf16_t ot[BQ * DV];
+  __shared__ __attribute__((aligned(16))) float rl[BQ];  // lse * log2(e) (+inf: row sees nothing)
+  __shared__ __attribute__((aligned(16))) float rd[BQ];  // D
+  __shared__ __attribute__((aligned(16))) int rlim[BQ];  // last visible key (-1: padding row)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int grp = blockIdx.y, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int kb0 = blockIdx.x * BNK;
+  const int key = kb0 + wave * 32 + lq;  // the key column this lane holds
+  const int keyc = min(key, p.Tk - 1);
+
+  bf16x8 kf[KS], vf[VS];
+  {
+    const bf16_t* kp = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh + (int64_t)keyc * p.k_st;
+    const bf16_t* vp = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh + (int64_t)keyc * p.v_st;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + s * 16 + lh * 8);
+#pragma unroll
+    for (int s = 0; s < VS; ++s) vf[s] = *reinterpret_cast<const bf16x8*>(vp + s * 16 + lh * 8);
+  }
+  f32x16 ak[DTK], av[DTV];
+#pragma unroll
+  for (int dt = 0; dt < DTK; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ak[dt][i] = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) av[dt][i] = 0.f;
+
+  const int off = p.Tk - p.Tq;
+  // query tokens that can see a key of this block start at kb0 - off (causal)
+  const int t_first = p.causal ? max(0, kb0 - off) : 0;
+  const int ntb = (p.Tq + BQ - 1) / BQ;
+  const int tb0 = min(t_first / BQ, ntb);
+  const int per_head = ntb - tb0;
+  const int n_it = p.g * per_head;
+
+  u32x4 qreg[QCH], oreg[OCH];
+  float rl_r = INFINITY, rd_r = 0.f;
+  int rlim_r = -1;
+  auto load = [&](int it) {
+    const int hl = it / per_head, tb = tb0 + it % per_head;
+    const int h = kvh * p.g + hl;
+    const bf16_t* qb = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
+    const bf16_t* ob = reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPQ, c = sl % CPQ;
+      const int t = min(tb * BQ + r, p.Tq - 1);
+      qreg[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)t * p.q_st + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < OCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPO, c = sl % CPO;
+      const int t = min(tb * BQ + r, p.Tq - 1);
+      oreg[i] = *reinterpret_cast<const u32x4*>(ob + (int64_t)t * p.do_st + c * 8);
+    }
+    if (tid < BQ) {
+      const int t = tb * BQ + tid;
+      if (t < p.Tq) {
+        const int64_t row = ((int64_t)b * p.H + h) * p.Tq + t;
+        const float l = p.lse[row];
+        rl_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        rd_r = p.D[row];
+        rlim_r = p.causal ? min(t + off, p.Tk - 1) : p.Tk - 1;
+      } else {
+        rl_r = INFINITY;
+        rd_r = 0.f;
+        rlim_r = -1;
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPQ, c = sl % CPQ;
+      *reinterpret_cast<u32x4*>(qt + chunk_at<CPQ>(r, c)) = qreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < OCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPO, c = sl % CPO;
+      *reinterpret_cast<u32x4*>(ot + chunk_at<CPO>(r, c)) = oreg[i];
+    }
+    if (tid < BQ) {
+      rl[tid] = rl_r;
+      rd[tid] = rd_r;
+      rlim[tid] = rlim_r;
+    }
+  };
+
+  if (n_it > 0) load(0);
+  for (int it = 0; it < n_it; ++it) {
+    __syncthreads();  // every wave is done with the previous tile
+    store();
+    __syncthreads();
+    if (it + 1 < n_it) load(it + 1);  // in flight while this tile is multiplied
+#pragma unroll
+    for (int qs = 0; qs < BQ / 32; ++qs) {
+      f32x16 S, dP;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        S[i] = 0.f;
+        dP[i] = 0.f;
+      }
+      const int r = qs * 32 + lq;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) S = mfma32(row_frag<CPQ>(qt, r, s, lh), kf[s], S);
+#pragma unroll
+      for (int s = 0; s < VS; ++s) dP = mfma32(row_frag<CPO>(ot, r, s, lh), vf[s], dP);
+      // accumulator element i holds query row qs*32 + lh*4 + 8*(i/4) + i%4 of key `key`
+      float P[16], dS[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = qs * 32 + lh * 4 + 8 * g4;
+        const f32x4 L = *reinterpret_cast<const f32x4*>(rl + r0);
+        const f32x4 Dv = *reinterpret_cast<const f32x4*>(rd + r0);
+        const i32x4 lim = *reinterpret_cast<const i32x4*>(rlim + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = g4 * 4 + j;
+          const float pr = (key <= lim[j]) ? __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j])) : 0.f;
+          P[i] = pr;
+          dS[i] = pr * (dP[i] - Dv[j]);
+        }
+      }
+      const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
+      const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+#pragma unroll
+      for (int dt = 0; dt < DTV; ++dt) {
+        av[dt] = mfma32(tr_frag<CPO>(ot, qs * 32, dt * 32, lane), pb0, av[dt]);
+        av[dt] = mfma32(tr_frag<CPO>(ot, qs * 32 + 16, dt * 32, lane), pb1, av[dt]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DTK; ++dt) {
+        ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32, dt * 32, lane), db0, ak[dt]);
+        ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32 + 16, dt * 32, lane), db1, ak[dt]);
+      }
+    }
+  }
+
+  // dK^T / dV^T tiles: lane holds key `key`, columns dt*32 + 8*g4 + 4*lh .. +3
+  if (key < p.Tk) {
+    bf16_t* dkp = reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st;
+    bf16_t* dvp = reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st;
+#pragma unroll
+    for (int dt = 0; dt < DTK; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dkp + d) = u32x2{pack2(ak[dt][g4 * 4] * p.scale, ak[dt][g4 * 4 + 1] * p.scale),
+                                                   pack2(ak[dt][g4 * 4 + 2] * p.scale, ak[dt][g4 * 4 + 3] * p.scale)};
+      }
+#pragma unroll
+    for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dvp + d) =
+            u32x2{pack2(av[dt][g4 * 4], av[dt][g4 * 4 + 1]), pack2(av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. dQ: one workgroup per 32*NW folded query rows of one (b, kv head)
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int NW, int BN>
+__global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
+  constexpr int BM = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int CPK = DQK / 8, CPV = DV / 8;
+  constexpr int KS = DQK / 16, VS = DV / 16, DT = DQK / 32, MT = BN / 32, PKS = BN / 16;
+  constexpr int KCH = BN * CPK / NT, VCH = BN * CPV / NT;
+  static_assert(BN * CPK % NT == 0 && BN * CPV % NT == 0, "tiles split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) bf16_t kt[BN * DQK];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[BN * DV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int grp = blockIdx.y, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int rows = p.g * p.Tq;  // folded rows of the group
+  const int n_rt = (rows + BM - 1) / BM;
+  const int tb = n_rt - 1 - (int)blockIdx.x;  // longest causal tiles first
+  const int f0 = tb * BM;
+  const int f = f0 + wave * 32 + lq;
+  const bool valid = f < rows;
+  const int fc = valid ? f : rows - 1;
+  const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
+  const int off = p.Tk - p.Tq;
+  const int row_lim = !valid ? -1 : (p.causal ? min(t + off, p.Tk - 1) : p.Tk - 1);
+  const int64_t lrow = ((int64_t)b * p.H + h) * p.Tq + t;
+  const float lse = p.lse[lrow];
+  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  const float Dr = p.D[lrow];
+
+  bf16x8 qf[KS], dof[VS];
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st;
+    const bf16_t* dp = reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)t * p.do_st;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + lh * 8);
+#pragma unroll
+    for (int s = 0; s < VS; ++s) dof[s] = *reinterpret_cast<const bf16x8*>(dp + s * 16 + lh * 8);
+  }
+
+  // keys this tile can see
+  int kend = p.Tk;
+  if (p.causal) {
+    const int f_last = min(f0 + BM, rows) - 1;
+    const int t_hi = (f_last / p.Tq != f0 / p.Tq) ? p.Tq - 1 : f_last % p.Tq;
+    kend = max(0, min(p.Tk, t_hi + off + 1));
+  }
+  const int nb = (kend + BN - 1) / BN;
+
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
+  u32x4 kreg[KCH], vreg[VCH];
+  auto load = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPK, c = sl % CPK;
+      const int kk = min(j * BN + r, p.Tk - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kk * p.k_st + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPV, c = sl % CPV;
+      const int kk = min(j * BN + r, p.Tk - 1);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)kk * p.v_st + c * 8);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPK, c = sl % CPK;
+      *reinterpret_cast<u32x4*>(kt + chunk_at<CPK>(r, c)) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int sl = i * NT + tid, r = sl / CPV, c = sl % CPV;
+      *reinterpret_cast<u32x4*>(vt + chunk_at<CPV>(r, c)) = vreg[i];
+    }
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  if (nb > 0) load(0);
+  for (int j = 0; j < nb; ++j) {
+    __syncthreads();
+    store();
+    __syncthreads();
+    if (j + 1 < nb) load(j + 1);
+    f32x16 S[MT], dP[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        S[mt][i] = 0.f;
+        dP[mt][i] = 0.f;
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) S[mt] = mfma32(row_frag<CPK>(kt, mt * 32 + lq, s, lh), qf[s], S[mt]);
+#pragma unroll
+      for (int s = 0; s < VS; ++s) dP[mt] = mfma32(row_frag<CPV>(vt, mt * 32 + lq, s, lh), dof[s], dP[mt]);
+    }
+    // S^T element i of tile mt is key j*BN + mt*32 + lh*4 + 8*(i/4) + i%4 of this lane's row
+    float dS[MT * 16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
+        const float pr = (kk <= row_lim) ? __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -l2)) : 0.f;
+        dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
+      }
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      const bf16x8 db = pack8(dS + ks * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_frag<CPK>(kt, ks * 16, dt * 32, lane), db, acc[dt]);
+    }
+  }
+
+  if (valid) {
+    bf16_t* qo = reinterpret_cast<bf16_t*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)t * p.dq_st;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(qo + d) = u32x2{pack2(acc[dt][g4 * 4] * p.scale, acc[dt][g4 * 4 + 1] * p.scale),
+                                                  pack2(acc[dt][g4 * 4 + 2] * p.scale, acc[dt][g4 * 4 + 3] * p.scale)};
+      }
+  }
+}
+
+template <int DQK, int DV>
+int launch_bwd_cfg(const BwdParams& p, void* stream) {
+  constexpr int NW_KV = 4, NW_Q = 4, BN_Q = 64;
+  constexpr int BQ_KV = DQK + DV > 256 ? 32 : 64;  // wide heads: one 32-row sub-block per step (registers)
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t R = (int64_t)p.B * p.H * p.Tq;
+  if (R > 0) {
+    constexpr int RPB = 4 * (64 / (DV / 8));  // rows per block of the dot kernel
+    hipLaunchKernelGGL(bwd_dot_kernel<DV>, dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  if (p.sinks != nullptr && p.dsinks != nullptr) {
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(p.H), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  if (p.Tk > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3((p.Tk + 32 * NW_KV - 1) / (32 * NW_KV), p.B * p.Hkv),
+                       dim3(NW_KV * 64), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  if (p.Tq > 0) {
+    const int rows = p.g * p.Tq;
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, NW_Q, BN_Q>), dim3((rows + 32 * NW_Q - 1) / (32 * NW_Q), p.B * p.Hkv),
+                       dim3(NW_Q * 64), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  return 0;
+}
+
+}  // namespace
+
+bool bwd_supported(int d_qk, int d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+}
+
+int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
+  if (d_qk == 64 && d_v == 64) return launch_bwd_cfg<64, 64>(p, stream);
+  if (d_qk == 128 && d_v == 128) return launch_bwd_cfg<128, 128>(p, stream);
+  if (d_qk == 192 && d_v == 128) return launch_bwd_cfg<192, 128>(p, stream);
+  return -1;
+}
+
+}  // namespace attn

@@ -62,6 +62,37 @@ struct MergeParams {
 // Host-side launcher of the merge (defined in attn_kernels.hip).
 int launch_merge(const MergeParams& m, void* stream);
 
+// Dense backward (bf16): gradients of q, k, v (and the sinks) from the
+// forward's inputs, its output and lse, and the output gradient.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;        // forward output O
+  const void* dout;       // dL/dO
+  const float* lse;       // forward lse [B, H, Tq] contiguous (natural log, sink included)
+  const float* sinks;     // [H] or nullptr
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsinks;          // [H] or nullptr
+  float* D;               // workspace: rowsum(dO * O), [B, H, Tq]
+  int64_t q_sb, q_sh, q_st, k_sb, k_sh, k_st, v_sb, v_sh, v_st;
+  int64_t o_sb, o_sh, o_st, do_sb, do_sh, do_st;
+  int64_t dq_sb, dq_sh, dq_st, dk_sb, dk_sh, dk_st, dv_sb, dv_sh, dv_st;
+  int32_t B, H, Hkv, Tq, Tk, g;
+  int32_t causal;
+  float scale;
+  float c;                // scale * log2(e)
+};
+
+// Launches the whole backward (row dots, sink gradients, dK/dV, dQ) on
+// `stream`; 0 or the hipError_t of a failed launch. Returns -1 when no
+// kernel is compiled for (d_qk, d_v).
+int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
+// (d_qk, d_v) pairs with a compiled backward
+bool bwd_supported(int d_qk, int d_v);
+
 // Host-side launchers, one per compiled kernel configuration.
 // Return 0 on success, else the hipError_t of the launch.
 typedef int (*launch_fn)(const KernelParams& p, void* stream);

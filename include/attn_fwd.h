@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -223,6 +223,74 @@ int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits)
  * (it reads the device's compute-unit count and the kernel's workgroups per
  * CU once; without a device it assumes 256 CUs and the LDS limit). */
 int32_t attn_splitkv_choose(const attn_dense_args* a);
+
+/*
+ * Dense backward arguments (bf16). The gradients of the dense forward above
+ * with respect to q, k, v and the sinks: the raw attention backward that runs
+ * after the forward and the output merge in context-parallel training
+ * (TransformerEngine pull request 3259, "Flowchart": raw backward -> Q/K/V
+ * gradients; "Summary": forward/backward wrappers with LSE handling).
+ *
+ *   q, k, v  the forward's inputs, layouts and strides as in attn_dense_args
+ *   out      [B, H, Tq, d_v] the forward's output O, strides o_sb, o_sh, o_st
+ *   dout     [B, H, Tq, d_v] dL/dO, strides do_sb, do_sh, do_st
+ *   lse      [B, H, Tq] float32 contiguous: the forward's lse (natural log,
+ *            sink included), used to recompute P = exp(scale q.k - lse)
+ *   sinks    [H] float32 or NULL, as in the forward
+ *   dq       [B, H, Tq, d_qk]  written, strides dq_sb, dq_sh, dq_st
+ *   dk       [B, Hkv, Tk, d_qk] written (summed over the g query heads that
+ *            read each kv head), strides dk_sb, dk_sh, dk_st
+ *   dv       [B, Hkv, Tk, d_v] written, strides dv_sb, dv_sh, dv_st
+ *   dsinks   [H] float32 written, or NULL (not computed); must be NULL when
+ *            sinks is NULL
+ *   causal, scale, sizes: as in the forward; lse carries no gradient.
+ *
+ * Gradients are accumulated in fp32 and rounded once to bf16 (dq, dk, dv).
+ * No atomics: results are bitwise reproducible. Compiled head dims (d_qk,
+ * d_v): (64,64), (128,128), (192,128); others return ATTN_UNSUPPORTED.
+ */
+typedef struct attn_dense_bwd_args {
+  uint32_t struct_size; /* = sizeof(attn_dense_bwd_args) */
+  int32_t dtype;        /* ATTN_BF16 */
+  int32_t B, H, Hkv, Tq, Tk, d_qk, d_v;
+  int32_t causal;
+  float scale;
+  const void* q;
+  int64_t q_sb, q_sh, q_st;
+  const void* k;
+  int64_t k_sb, k_sh, k_st;
+  const void* v;
+  int64_t v_sb, v_sh, v_st;
+  const void* out;
+  int64_t o_sb, o_sh, o_st;
+  const void* dout;
+  int64_t do_sb, do_sh, do_st;
+  const float* lse;
+  const float* sinks;
+  void* dq;
+  int64_t dq_sb, dq_sh, dq_st;
+  void* dk;
+  int64_t dk_sb, dk_sh, dk_st;
+  void* dv;
+  int64_t dv_sb, dv_sh, dv_st;
+  float* dsinks;
+} attn_dense_bwd_args;
+
+/* Workspace bytes attn_bwd_dense needs: B*H*Tq*4 (the row dots
+ * rowsum(dO * O)), rounded up to 256; -1 on invalid sizes, dtype or head
+ * dims (pointers are not examined). Host only. */
+int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a);
+
+/* Dense backward: four launches on `stream` (row dots, sink gradients when
+ * dsinks != NULL, dK/dV, dQ). `workspace` is caller-owned device memory,
+ * 16-byte aligned, of at least attn_bwd_dense_workspace_bytes(a) bytes; its
+ * contents on return are unspecified and calls sharing it must be ordered on
+ * one stream. Argument errors (NULL or misaligned pointers, bad strides, a
+ * short workspace, dsinks without sinks) return ATTN_INVALID_ARGUMENT before
+ * any launch; dtype or head dims outside the compiled set ATTN_UNSUPPORTED.
+ * Launches are recorded under the dispatch path "dense_bwd_bf16_d<d_qk>" (with
+ * "_v<d_v>" when d_v differs). */
+attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status s);

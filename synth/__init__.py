@@ -30,7 +30,8 @@ Generation recipe (fixed so that every consumer sees identical bits):
 draw order q, k, v, sinks, each ``torch.randn(shape, dtype=float32)``; cast to
 bf16 (round to nearest even) for the bf16 workloads. Sparse indices come from
 ``numpy.random.default_rng(seed)``, one ``choice(N, topk, replace=False)`` per
-query, in query order, as int32 and unsorted.
+query, in query order, as int32 and unsorted. The backward's output gradient
+dL/dO comes from a generator of its own seeded with 1000 + seed (``make_dout``).
 """
 from __future__ import annotations
 
@@ -131,6 +132,19 @@ def make_dense(s: DenseSpec, *, seed: Optional[int] = None) -> dict:
     if s.sinks:
         sinks = torch.randn((s.H,), generator=g, dtype=torch.float32)
     return {"q": q, "k": k, "v": v, "sinks": sinks}
+
+
+def make_dout(s: DenseSpec, *, seed: Optional[int] = None) -> torch.Tensor:
+    """The output gradient dL/dO [B,H,Tq,d_v] for the backward: its own generator,
+    seeded with 1000 + the workload's seed, one ``randn`` in fp32 cast to the
+    workload's dtype (a random linear functional of the output)."""
+    g = torch.Generator("cpu").manual_seed(1000 + (s.seed if seed is None else seed))
+    return torch.randn((s.B, s.H, s.Tq, s.d_v), generator=g, dtype=torch.float32).to(_torch_dtype(s.dtype))
+
+
+def randn_dout(B, H, Tq, d_v, *, dtype="bf16", seed=0) -> torch.Tensor:
+    """make_dout for ad-hoc shapes."""
+    return make_dout(DenseSpec("adhoc", seed, B, H, 1, Tq, 1, 1, d_v, dtype, True, False))
 
 
 def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:

@@ -203,3 +203,46 @@ def test_splitkv_rejects_bad_workspace_before_launch():
     st = lib.attn_fwd_dense_splitkv(ctypes.byref(f), 4, ctypes.c_void_p(4096), 1 << 30, None)
     assert st == A.ATTN_UNSUPPORTED
 
+
+
+# ------------------------------------------------------------------ dense backward (host side)
+def _fake_bwd(**over):
+    a = A.AttnDenseBwdArgs()
+    a.struct_size = ctypes.sizeof(A.AttnDenseBwdArgs)
+    a.dtype = A.ATTN_BF16
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = 1, 8, 2, 16, 16, 128, 128
+    a.causal, a.scale = 1, 0.1
+    fake = 0x10000  # aligned, never dereferenced: validation fails first
+    for n in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"):
+        setattr(a, n, fake)
+    for n in ("q", "dq", "k", "dk"):
+        setattr(a, n + "_st", 128)
+    for n in ("v", "o", "do", "dv"):
+        setattr(a, n + "_st", 128)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_bwd_workspace_and_validation():
+    lib = A.load_library()
+    assert A.bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, 128) == 2 * 32 * 4096 * 4
+    assert A.bwd_workspace_bytes(1, 8, 2, 3, 5, 64, 64) == 256          # rounded up to 256
+    with pytest.raises(A.AttnInvalidArgument):
+        A.bwd_workspace_bytes(1, 8, 3, 3, 5, 64, 64)                    # H % Hkv != 0
+    assert lib.attn_bwd_dense_workspace_bytes(ctypes.byref(_fake_bwd(d_qk=256, d_v=256))) == -1
+    ws = ctypes.c_void_p(0x20000)
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(d_qk=512, d_v=512)), ws, 1 << 20, None)
+    assert st == A.ATTN_UNSUPPORTED
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(dsinks=0x30000)), ws, 1 << 20, None)
+    assert st == A.ATTN_INVALID_ARGUMENT and b"dsinks" in lib.attn_last_error()
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd()), ws, 16, None)
+    assert st == A.ATTN_INVALID_ARGUMENT and b"workspace" in lib.attn_last_error()
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(dq=None)), ws, 1 << 20, None)
+    assert st == A.ATTN_INVALID_ARGUMENT
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(q_st=100)), ws, 1 << 20, None)
+    assert st == A.ATTN_INVALID_ARGUMENT
+    bad = _fake_bwd()
+    bad.struct_size = 8
+    assert lib.attn_bwd_dense(ctypes.byref(bad), ws, 1 << 20, None) == A.ATTN_ABI_MISMATCH
+    assert lib.attn_bwd_dense(ctypes.byref(_fake_bwd(dtype=A.ATTN_F32)), ws, 1 << 20, None) == A.ATTN_UNSUPPORTED

@@ -1,0 +1,163 @@
+"""Dense backward (attn_bwd_dense) against the fp64 oracle's gradients.
+
+The GPU forward supplies out and lse (as in training); the oracle computes the
+exact gradients of the same bf16 inputs from the definition. Tolerance, from
+the arithmetic: P and dS enter the MFMAs as bf16 (relative rounding 2^-9 each)
+and every gradient is rounded once to bf16, so the error of a gradient tensor
+is a few 2^-9 of its largest entry; the bar is max |g - g_ref| <= 2e-2 * max|g_ref|
+(about 10x that), and 1e-2 relative for the fp32 sink gradients (computed from
+the bf16 output through D). Gradients that vanish exactly (one key: P = 1 and
+dS = dP - D = 0) keep the rounding of O in D, a few 2^-9 of |dO.v| ~ 1: the
+scale of the bar never drops below 0.05 (an absolute floor of 1e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_attn_amd as A
+import oracle
+import synth
+from test_gpu_parity import _np, announce
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+TOL_SINK = 1e-2
+
+
+def _rel_err(got, ref):
+    ref = np.asarray(ref, np.float64)
+    scale = max(float(np.abs(ref).max()) if ref.size else 0.0, 0.05)
+    d = np.abs(np.asarray(got, np.float64) - ref)
+    return float(np.nan_to_num(d, nan=np.inf).max()) / scale if d.size else 0.0
+
+
+def run_fwd_bwd(inp, dout, *, causal, scale):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    out, lse = A.dense(q, k, v, causal=causal, scale=scale, sinks=sk)
+    d = dout.cuda()
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    res = A.dense_backward(q, k, v, out, d, lse, causal=causal, scale=scale, sinks=sk, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_bwd(inp, dout, *, causal, scale, label):
+    announce(f"bwd {label} q{tuple(inp['q'].shape)} k{tuple(inp['k'].shape)} v{tuple(inp['v'].shape)} "
+             f"causal={causal} sinks={inp['sinks'] is not None}")
+    dq, dk, dv, ds = run_fwd_bwd(inp, dout, causal=causal, scale=scale)
+    rq, rk, rv, rs = oracle.dense_attention_backward(inp["q"], inp["k"], inp["v"], dout, scale=scale, causal=causal,
+                                                     sinks=inp["sinks"])
+    errs = {"dq": _rel_err(_np(dq), rq), "dk": _rel_err(_np(dk), rk), "dv": _rel_err(_np(dv), rv)}
+    assert max(errs.values()) <= TOL_REL, f"{label}: {errs}"
+    if rs is not None:
+        es = _rel_err(_np(ds), rs)
+        assert es <= TOL_SINK, f"{label}: dsinks rel err {es:.3e}"
+    return errs
+
+
+BWD_DIMS = [(64, 64), (128, 128), (192, 128)]
+
+
+@pytest.mark.parametrize("dqk,dv", BWD_DIMS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_head_dims(dqk, dv, causal):
+    # T = 200: several 64-row query steps and 128-key blocks, ragged in both
+    inp = synth.randn_dense(2, 4, 2, 200, 200, dqk, dv, dtype="bf16", sinks=False, seed=dqk + dv + 7)
+    dout = synth.randn_dout(2, 4, 200, dv, seed=dqk + dv + 7)
+    check_bwd(inp, dout, causal=causal, scale=1 / math.sqrt(dqk), label=f"d{dqk}/{dv}")
+
+
+CASES = [
+    # B, H, Hkv, Tq, Tk, d_qk, d_v, causal, sinks
+    (1, 8, 1, 130, 130, 128, 128, True, True),     # MQA with sinks
+    (1, 8, 2, 33, 300, 128, 128, True, False),     # Tq < Tk: bottom-right causal
+    (1, 4, 4, 150, 40, 64, 64, True, True),        # Tq > Tk: rows that see no key
+    (2, 6, 3, 1, 257, 192, 128, True, True),       # one query row
+    (1, 2, 1, 97, 1, 128, 128, False, False),      # one key: dq = dk = 0
+    (1, 16, 16, 64, 64, 192, 128, True, False),    # MLA shape, exact tiles
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}T{c[3]}x{c[4]}d{c[5]}/{c[6]}"
+                         f"{'c' if c[7] else 'n'}{'s' if c[8] else ''}")
+def test_bwd_cases(case):
+    B, H, Hkv, Tq, Tk, dqk, dv, causal, sinks = case
+    inp = synth.randn_dense(B, H, Hkv, Tq, Tk, dqk, dv, dtype="bf16", sinks=sinks, seed=Tq * 31 + Tk)
+    dout = synth.randn_dout(B, H, Tq, dv, seed=Tq * 31 + Tk)
+    check_bwd(inp, dout, causal=causal, scale=1 / math.sqrt(dqk), label=str(case))
+
+
+def test_bwd_no_keys():
+    """Tk = 0: out = 0, so dq = 0 and the sink gradient is 0."""
+    announce("bwd Tk=0")
+    inp = synth.randn_dense(1, 4, 2, 9, 0, 128, 128, dtype="bf16", sinks=True, seed=5)
+    dout = synth.randn_dout(1, 4, 9, 128, seed=5)
+    dq, dk, dv, ds = run_fwd_bwd(inp, dout, causal=True, scale=0.1)
+    assert float(dq.float().abs().max()) == 0.0
+    assert float(ds.abs().max()) == 0.0
+
+
+def test_bwd_deterministic_and_strided():
+    """Two calls give identical bits; BSHD views (strided heads and tokens) give the same gradients."""
+    announce("bwd determinism + strided")
+    inp = synth.randn_dense(2, 8, 2, 150, 150, 128, 128, dtype="bf16", sinks=True, seed=11)
+    dout = synth.randn_dout(2, 8, 150, 128, seed=11)
+    a = run_fwd_bwd(inp, dout, causal=True, scale=0.09)
+    b = run_fwd_bwd(inp, dout, causal=True, scale=0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # the same tensors as BSHD storage viewed as BHSD
+    q, k, v = (inp[n].cuda().transpose(1, 2).contiguous().transpose(1, 2) for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda()
+    out, lse = A.dense(q, k, v, causal=True, scale=0.09, sinks=sk)
+    d = dout.cuda().transpose(1, 2).contiguous().transpose(1, 2)
+    dq = torch.empty_like(q.transpose(1, 2).contiguous()).transpose(1, 2)
+    r = A.dense_backward(q, k, v, out, d, lse, causal=True, scale=0.09, sinks=sk, dq=dq)
+    torch.cuda.synchronize()
+    for x, y in zip(a, r):
+        assert torch.equal(x, y)
+
+
+def test_bwd_rejects_bad_arguments():
+    inp = synth.randn_dense(1, 4, 2, 8, 8, 128, 128, dtype="bf16", sinks=False, seed=1)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    out, lse = A.dense(q, k, v, causal=True, scale=0.1)
+    with pytest.raises(A.AttnInvalidArgument):   # dsinks without sinks
+        A.dense_backward(q, k, v, out, out, lse, causal=True, scale=0.1,
+                         dsinks=torch.empty(4, device="cuda"))
+    with pytest.raises(A.AttnInvalidArgument):   # workspace too small
+        A.dense_backward(q, k, v, out, out, lse, causal=True, scale=0.1,
+                         workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    q5 = torch.zeros(1, 4, 8, 256, dtype=torch.bfloat16, device="cuda")
+    k5 = torch.zeros(1, 2, 8, 256, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(A.AttnUnsupported):       # head dims without a compiled backward
+        A.dense_backward(q5, k5, k5, q5, q5, lse, causal=True, scale=0.1)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ full benchmark shapes, one kv group sampled
+@pytest.mark.parametrize("wl,group", [(2, (1, 5)), (3, (3, 9))])
+def test_bwd_full_workload_sampled_group(wl, group):
+    """The benchmark's launch at full size; the oracle checks one (batch, kv head) group
+    (every dq row of its heads, every dk/dv row of the kv head): the gradient of a group
+    depends on that group's inputs only."""
+    s = synth.spec(wl)
+    announce(f"bwd full workload {s.name} group {group}")
+    inp = synth.make(wl)
+    dout = synth.make_dout(s)
+    dq, dk, dv, _ = run_fwd_bwd(inp, dout, causal=s.causal, scale=s.scale)
+    b, kvh = group
+    g = s.H // s.Hkv
+    hs = slice(kvh * g, (kvh + 1) * g)
+    rq, rk, rv, _ = oracle.dense_attention_backward(
+        inp["q"][b:b + 1, hs], inp["k"][b:b + 1, kvh:kvh + 1], inp["v"][b:b + 1, kvh:kvh + 1], dout[b:b + 1, hs],
+        scale=s.scale, causal=s.causal)
+    errs = {"dq": _rel_err(_np(dq[b:b + 1, hs]), rq), "dk": _rel_err(_np(dk[b:b + 1, kvh:kvh + 1]), rk),
+            "dv": _rel_err(_np(dv[b:b + 1, kvh:kvh + 1]), rv)}
+    assert max(errs.values()) <= TOL_REL, f"{s.name} group {group}: {errs}"
