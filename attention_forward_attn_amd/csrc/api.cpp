@@ -471,7 +471,10 @@ attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (bwd_path(a->d_qk, a->d_v) < 0)
     return fail(ATTN_UNSUPPORTED, "no compiled dense backward for (d_qk, d_v) = (%d, %d)", a->d_qk, a->d_v);
-  if ((int64_t)a->B * a->Hkv > 65535) return fail(ATTN_UNSUPPORTED, "B * Hkv above 65535 (grid y)");
+  // one-dimensional grids: (key blocks or row tiles) x B x Hkv workgroups
+  const int64_t groups = (int64_t)a->B * a->Hkv;
+  const int64_t tiles = std::max<int64_t>((a->Tk + 127) / 128, ((int64_t)(a->H / a->Hkv) * a->Tq + 127) / 128);
+  if (groups * tiles > 0x7fffffff) return fail(ATTN_UNSUPPORTED, "problem too large for one launch");
   return ATTN_OK;
 }
 
@@ -492,6 +495,8 @@ attn_status validate_bwd(const attn_dense_bwd_args* a) {
   for (int64_t s : strides)
     if (s < 0 || s % 8 != 0)
       return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and keep rows 16-byte aligned (multiple of 8 elements)");
+  if (a->q_st >= (1 << 24) || a->do_st >= (1 << 24) || a->k_st >= (1 << 24) || a->v_st >= (1 << 24))
+    return fail(ATTN_INVALID_ARGUMENT, "q, dout, k, v token strides must be below 2^24 elements");
   if (a->Tq > 1 && (a->q_st < a->d_qk || a->dq_st < a->d_qk || a->o_st < a->d_v || a->do_st < a->d_v))
     return fail(ATTN_INVALID_ARGUMENT, "query-side token stride smaller than the head dim");
   if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v || a->dk_st < a->d_qk || a->dv_st < a->d_v))

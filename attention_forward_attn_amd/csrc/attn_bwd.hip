@@ -171,26 +171,94 @@ __global__ void __launch_bounds__(256) bwd_dsink_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Tile loads: global_load_lds moves 16 (or 4) bytes per lane from global
+// memory straight into LDS at m0 + lane * size, from a wave-uniform base in
+// scalar registers plus a per-lane 32-bit byte offset. The waits are explicit
+// (vmcnt), since the compiler does not see these loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_u32(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kPF = 4;  // LDS operand reads kept ahead of the MFMAs
+
+// N MFMAs each fed by R LDS reads: keep PF MFMAs' reads in flight ahead
+template <int N, int R>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int PD = N < kPF ? N : kPF;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R * PD, 0);
+#pragma unroll
+  for (int k = 0; k < N - PD; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, PD, 0);
+}
+
+// DMA of BR rows (starting at row r0 of a row-major source with element row
+// stride `st`, rows past `rmax` clamped onto it) into a swizzled LDS tile of
+// CPR chunks per row: wave instruction j fills LDS slots 64j .. 64j+63, and
+// slot (r, c') receives logical chunk c' ^ swz(r) of row r.
+template <int CPR, int BR, int NW>
+__device__ __forceinline__ void dma_tile(const bf16_t* base, int64_t st, int r0, int rmax, uint32_t lds, int wave,
+                                         int lane) {
+  constexpr int NI = BR * CPR / 64;
+  static_assert(NI % NW == 0, "tile instructions split evenly over the waves");
+  const void* sb = uniform_ptr(base + (int64_t)r0 * st);
+#pragma unroll
+  for (int m = 0; m < NI / NW; ++m) {
+    const int j = wave + NW * m;
+    const int sl = 64 * j + lane, r = sl / CPR, c = (sl % CPR) ^ swz<CPR>(sl / CPR);
+    const int rr = min(r0 + r, rmax) - r0;
+    dma16(sb, 2u * (uint32_t)(rr * (int32_t)st + c * 8), lds + 1024u * j);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dK, dV: one workgroup per 32*NW keys of one (b, kv head)
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, int NW, int BQ>
 __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BNK = 32 * NW;  // keys per workgroup; BQ query rows per step (32-row sub-blocks)
-  constexpr int NT = NW * 64;
   constexpr int CPQ = DQK / 8, CPO = DV / 8;
   constexpr int KS = DQK / 16, VS = DV / 16, DTK = DQK / 32, DTV = DV / 32;
-  constexpr int QCH = BQ * CPQ / NT, OCH = BQ * CPO / NT;  // 16-byte chunks per thread per step
-  static_assert(BQ * CPQ % NT == 0 && BQ * CPO % NT == 0, "tiles split evenly over the threads");
+  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2, STAGE = QT_BYTES + OT_BYTES + 2 * BQ * 4;
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims are whole 32-column tiles");
-  __shared__ __attribute__((aligned(16))) bf16_t qt[BQ * DQK];
-  __shared__ __attribute__((aligned(16))) bf16_t ot[BQ * DV];
-  __shared__ __attribute__((aligned(16))) float rl[BQ];  // lse * log2(e) (+inf: row sees nothing)
-  __shared__ __attribute__((aligned(16))) float rd[BQ];  // D
-  __shared__ __attribute__((aligned(16))) int rlim[BQ];  // last visible key (-1: padding row)
+  static_assert(BQ <= 64, "one row statistic per lane");
+  // two stages: [Q tile | dO tile | lse | D]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
-  const int grp = blockIdx.y, b = grp / p.Hkv, kvh = grp % p.Hkv;
-  const int kb0 = blockIdx.x * BNK;
+  // key block 0 of every group first: under a causal mask the first key
+  // blocks are seen by the most query rows
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int kb0 = (blockIdx.x / n_groups) * BNK;
   const int key = kb0 + wave * 32 + lq;  // the key column this lane holds
   const int keyc = min(key, p.Tk - 1);
 
@@ -220,66 +288,42 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
   const int tb0 = min(t_first / BQ, ntb);
   const int per_head = ntb - tb0;
   const int n_it = p.g * per_head;
+  const uint32_t smem_s = lds_u32(smem);
 
-  u32x4 qreg[QCH], oreg[OCH];
-  float rl_r = INFINITY, rd_r = 0.f;
-  int rlim_r = -1;
-  auto load = [&](int it) {
-    const int hl = it / per_head, tb = tb0 + it % per_head;
+  auto issue = [&](int it) {
+    const int hl = it / per_head, t0 = (tb0 + it % per_head) * BQ;
     const int h = kvh * p.g + hl;
-    const bf16_t* qb = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
-    const bf16_t* ob = reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
-#pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPQ, c = sl % CPQ;
-      const int t = min(tb * BQ + r, p.Tq - 1);
-      qreg[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)t * p.q_st + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < OCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPO, c = sl % CPO;
-      const int t = min(tb * BQ + r, p.Tq - 1);
-      oreg[i] = *reinterpret_cast<const u32x4*>(ob + (int64_t)t * p.do_st + c * 8);
-    }
-    if (tid < BQ) {
-      const int t = tb * BQ + tid;
-      if (t < p.Tq) {
-        const int64_t row = ((int64_t)b * p.H + h) * p.Tq + t;
-        const float l = p.lse[row];
-        rl_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        rd_r = p.D[row];
-        rlim_r = p.causal ? min(t + off, p.Tk - 1) : p.Tk - 1;
-      } else {
-        rl_r = INFINITY;
-        rd_r = 0.f;
-        rlim_r = -1;
+    const uint32_t st = smem_s + (uint32_t)((it & 1) * STAGE);
+    dma_tile<CPQ, BQ, NW>(reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh, p.q_st, t0, p.Tq - 1, st,
+                          wave, lane);
+    dma_tile<CPO, BQ, NW>(reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh, p.do_st, t0,
+                          p.Tq - 1, st + QT_BYTES, wave, lane);
+    if (wave == NW - 1) {
+      // row statistics: lane l < BQ gets row t0 + l (clamped), 4 bytes each
+      const int64_t rb = ((int64_t)b * p.H + h) * p.Tq + t0;
+      const void* lb = uniform_ptr(p.lse + rb);
+      const void* db = uniform_ptr(p.D + rb);
+      const uint32_t vo = 4u * (uint32_t)(min(t0 + lane, p.Tq - 1) - t0);
+      if (lane < BQ) {
+        dma4(lb, vo, st + QT_BYTES + OT_BYTES);
+        dma4(db, vo, st + QT_BYTES + OT_BYTES + BQ * 4);
       }
     }
   };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPQ, c = sl % CPQ;
-      *reinterpret_cast<u32x4*>(qt + chunk_at<CPQ>(r, c)) = qreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < OCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPO, c = sl % CPO;
-      *reinterpret_cast<u32x4*>(ot + chunk_at<CPO>(r, c)) = oreg[i];
-    }
-    if (tid < BQ) {
-      rl[tid] = rl_r;
-      rd[tid] = rd_r;
-      rlim[tid] = rlim_r;
-    }
-  };
 
-  if (n_it > 0) load(0);
+  if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();  // every wave is done with the previous tile
-    store();
-    __syncthreads();
-    if (it + 1 < n_it) load(it + 1);  // in flight while this tile is multiplied
+    wait_all_loads();  // this wave's loads of tile it have landed
+    barrier();         // ... and everyone's; nobody reads the other stage any more
+    if (it + 1 < n_it) issue(it + 1);
+    const unsigned char* sp = smem + (it & 1) * STAGE;
+    const bf16_t* qt = reinterpret_cast<const bf16_t*>(sp);
+    const bf16_t* ot = reinterpret_cast<const bf16_t*>(sp + QT_BYTES);
+    const float* rl = reinterpret_cast<const float*>(sp + QT_BYTES + OT_BYTES);
+    const float* rd = rl + BQ;
+    const int t0 = (tb0 + it % per_head) * BQ;
+    // every (row, key) pair of the tile visible: no per-score mask
+    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (!p.causal || t0 + off >= kb0 + BNK - 1);
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
       f32x16 S, dP;
@@ -290,9 +334,11 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
       }
       const int r = qs * 32 + lq;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) S = mfma32(row_frag<CPQ>(qt, r, s, lh), kf[s], S);
-#pragma unroll
-      for (int s = 0; s < VS; ++s) dP = mfma32(row_frag<CPO>(ot, r, s, lh), vf[s], dP);
+      for (int s = 0; s < (KS > VS ? KS : VS); ++s) {
+        if (s < KS) S = mfma32(row_frag<CPQ>(qt, r, s, lh), kf[s], S);
+        if (s < VS) dP = mfma32(row_frag<CPO>(ot, r, s, lh), vf[s], dP);
+      }
+      pipeline_reads<KS + VS, 1>();
       // accumulator element i holds query row qs*32 + lh*4 + 8*(i/4) + i%4 of key `key`
       float P[16], dS[16];
 #pragma unroll
@@ -300,11 +346,15 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
         const int r0 = qs * 32 + lh * 4 + 8 * g4;
         const f32x4 L = *reinterpret_cast<const f32x4*>(rl + r0);
         const f32x4 Dv = *reinterpret_cast<const f32x4*>(rd + r0);
-        const i32x4 lim = *reinterpret_cast<const i32x4*>(rlim + r0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = g4 * 4 + j;
-          const float pr = (key <= lim[j]) ? __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j])) : 0.f;
+          float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j] * kLog2e));
+          if (!full) {
+            const int t = t0 + r0 + j;
+            const int lim = t >= p.Tq ? -1 : (p.causal ? t + off : p.Tk - 1);
+            pr = (key <= lim) ? pr : 0.f;
+          }
           P[i] = pr;
           dS[i] = pr * (dP[i] - Dv[j]);
         }
@@ -321,6 +371,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
         ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32, dt * 32, lane), db0, ak[dt]);
         ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32 + 16, dt * 32, lane), db1, ak[dt]);
       }
+      pipeline_reads<2 * (DTV + DTK), 2>();
     }
   }
 
@@ -353,19 +404,18 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
 template <int DQK, int DV, int NW, int BN>
 __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
   constexpr int CPK = DQK / 8, CPV = DV / 8;
   constexpr int KS = DQK / 16, VS = DV / 16, DT = DQK / 32, MT = BN / 32, PKS = BN / 16;
-  constexpr int KCH = BN * CPK / NT, VCH = BN * CPV / NT;
-  static_assert(BN * CPK % NT == 0 && BN * CPV % NT == 0, "tiles split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) bf16_t kt[BN * DQK];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[BN * DV];
+  constexpr int KT_BYTES = BN * DQK * 2, STAGE = KT_BYTES + BN * DV * 2;
+  // two stages: [K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
-  const int grp = blockIdx.y, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int rows = p.g * p.Tq;  // folded rows of the group
   const int n_rt = (rows + BM - 1) / BM;
-  const int tb = n_rt - 1 - (int)blockIdx.x;  // longest causal tiles first
+  const int tb = n_rt - 1 - (int)(blockIdx.x / n_groups);  // longest causal tiles first, every group
   const int f0 = tb * BM;
   const int f = f0 + wave * 32 + lq;
   const bool valid = f < rows;
@@ -388,43 +438,25 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
     for (int s = 0; s < VS; ++s) dof[s] = *reinterpret_cast<const bf16x8*>(dp + s * 16 + lh * 8);
   }
 
-  // keys this tile can see
-  int kend = p.Tk;
+  // keys this tile can see (kend), and keys every row of it sees (kfull)
+  int kend = p.Tk, kfull = (f0 + BM <= rows) ? p.Tk : 0;
   if (p.causal) {
     const int f_last = min(f0 + BM, rows) - 1;
-    const int t_hi = (f_last / p.Tq != f0 / p.Tq) ? p.Tq - 1 : f_last % p.Tq;
+    const bool one_head = f_last / p.Tq == f0 / p.Tq;
+    const int t_hi = one_head ? f_last % p.Tq : p.Tq - 1;
+    const int t_lo = one_head ? f0 % p.Tq : 0;
     kend = max(0, min(p.Tk, t_hi + off + 1));
+    kfull = min(kfull, max(0, t_lo + off + 1));
   }
   const int nb = (kend + BN - 1) / BN;
 
   const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
-  u32x4 kreg[KCH], vreg[VCH];
-  auto load = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPK, c = sl % CPK;
-      const int kk = min(j * BN + r, p.Tk - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kk * p.k_st + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPV, c = sl % CPV;
-      const int kk = min(j * BN + r, p.Tk - 1);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)kk * p.v_st + c * 8);
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPK, c = sl % CPK;
-      *reinterpret_cast<u32x4*>(kt + chunk_at<CPK>(r, c)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int sl = i * NT + tid, r = sl / CPV, c = sl % CPV;
-      *reinterpret_cast<u32x4*>(vt + chunk_at<CPV>(r, c)) = vreg[i];
-    }
+  const uint32_t smem_s = lds_u32(smem);
+  auto issue = [&](int j) {
+    const uint32_t st = smem_s + (uint32_t)((j & 1) * STAGE);
+    dma_tile<CPK, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, st, wave, lane);
+    dma_tile<CPV, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1, st + KT_BYTES, wave, lane);
   };
 
   f32x16 acc[DT];
@@ -433,12 +465,13 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  if (nb > 0) load(0);
+  if (nb > 0) issue(0);
   for (int j = 0; j < nb; ++j) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (j + 1 < nb) load(j + 1);
+    wait_all_loads();
+    barrier();
+    if (j + 1 < nb) issue(j + 1);
+    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
+    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
     f32x16 S[MT], dP[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -450,18 +483,24 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) S[mt] = mfma32(row_frag<CPK>(kt, mt * 32 + lq, s, lh), qf[s], S[mt]);
-#pragma unroll
-      for (int s = 0; s < VS; ++s) dP[mt] = mfma32(row_frag<CPV>(vt, mt * 32 + lq, s, lh), dof[s], dP[mt]);
+      for (int s = 0; s < (KS > VS ? KS : VS); ++s) {
+        if (s < KS) S[mt] = mfma32(row_frag<CPK>(kt, mt * 32 + lq, s, lh), qf[s], S[mt]);
+        if (s < VS) dP[mt] = mfma32(row_frag<CPV>(vt, mt * 32 + lq, s, lh), dof[s], dP[mt]);
+      }
     }
+    pipeline_reads<MT * (KS + VS), 1>();
     // S^T element i of tile mt is key j*BN + mt*32 + lh*4 + 8*(i/4) + i%4 of this lane's row
     float dS[MT * 16];
+    const bool full = (j + 1) * BN <= kfull;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
-        const float pr = (kk <= row_lim) ? __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -l2)) : 0.f;
+        float pr = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -l2));
+        if (!full) {
+          const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
+          pr = (kk <= row_lim) ? pr : 0.f;
+        }
         dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
       }
 #pragma unroll
@@ -470,6 +509,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_frag<CPK>(kt, ks * 16, dt * 32, lane), db, acc[dt]);
     }
+    pipeline_reads<PKS * DT, 2>();
   }
 
   if (valid) {
@@ -501,14 +541,14 @@ int launch_bwd_cfg(const BwdParams& p, void* stream) {
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   if (p.Tk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3((p.Tk + 32 * NW_KV - 1) / (32 * NW_KV), p.B * p.Hkv),
-                       dim3(NW_KV * 64), 0, st, p);
+    const int nkb = (p.Tk + 32 * NW_KV - 1) / (32 * NW_KV);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3(nkb * p.B * p.Hkv), dim3(NW_KV * 64), 0, st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   if (p.Tq > 0) {
     const int rows = p.g * p.Tq;
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, NW_Q, BN_Q>), dim3((rows + 32 * NW_Q - 1) / (32 * NW_Q), p.B * p.Hkv),
-                       dim3(NW_Q * 64), 0, st, p);
+    const int nrt = (rows + 32 * NW_Q - 1) / (32 * NW_Q);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, NW_Q, BN_Q>), dim3(nrt * p.B * p.Hkv), dim3(NW_Q * 64), 0, st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   return 0;

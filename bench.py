@@ -269,6 +269,60 @@ def measure(n: int, steps: int, warmup: int, split: bool = False) -> dict:
             "verdict": "Measured"}
 
 
+def bwd_flops(n: int) -> int:
+    """Algorithmic flops of the backward: five products per visible pair (S recomputed,
+    dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K), i.e. 2 * pairs * (3 d_qk + 2 d_v)."""
+    import synth
+
+    s = synth.spec(n)
+    return 2 * visible_pairs(s.B, s.H, s.Tq, s.Tk, s.causal) * (3 * s.d_qk + 2 * s.d_v)
+
+
+def bwd_path_name(d_qk: int, d_v: int) -> str:
+    return f"dense_bwd_bf16_d{d_qk}" + ("" if d_qk == d_v else f"_v{d_v}")
+
+
+def measure_bwd(n: int, steps: int, warmup: int) -> dict:
+    """The dense backward (all four launches) on workload n, after one forward that
+    supplies out and lse; dL/dO is the seeded synthetic gradient."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(n)
+    inp = synth.make(n)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    out, lse = A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk)
+    dout = synth.make_dout(s).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsk = torch.empty_like(sk) if sk is not None else None
+    ws = torch.empty(max(16, A.bwd_workspace_bytes(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v)), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        A.dense_backward(q, k, v, out, dout, lse, causal=s.causal, scale=s.scale, sinks=sk, dq=dq, dk=dk, dv=dv,
+                         dsinks=dsk, workspace=ws)
+
+    path = bwd_path_name(s.d_qk, s.d_v)
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != steps + warmup:
+        raise RuntimeError(f"NotEngaged: expected {steps + warmup} launches of {path}, saw {A.dispatch_count(path)}")
+    fl = bwd_flops(n)
+    ach = fl / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    value = fl / (t["ms_per_step"] * 1e-3) / 1e12
+    log(f"[bench] backward {describe(n)} | path {path} | {t['kernel_ms_mean']:.4f} ms per backward (4 launches) "
+        f"| {rl['achieved']} TFLOP/s = {100 * rl['frac']:.1f}% of peak")
+    return {"row": "dense backward (attn_bwd_dense)", "workload": describe(n), "path": path,
+            "value": round(value, 3), "unit": "TFLOP/s", "kernel_ms": round(t["kernel_ms_mean"], 5),
+            "roofline": rl, "verdict": "Measured"}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -484,6 +538,10 @@ def main():
                                          "kernel_ms": round(rp["timing"]["kernel_ms_mean"], 5)}})
         del r, rp
         torch.cuda.empty_cache()
+        # the dense backward on the two prefill workloads it is compiled for
+        for m in (2, 3):
+            next_rows.append(measure_bwd(m, st, wu))
+            torch.cuda.empty_cache()
     ceil = None
     if not args.no_ceilings:
         ceil = ceilings()
