@@ -205,7 +205,7 @@ __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-constexpr int kPF = 4;  // LDS operand reads kept ahead of the MFMAs
+constexpr int kPF = 2;  // LDS operand reads kept ahead of the MFMAs (2 measured best)
 
 // N MFMAs each fed by R LDS reads: keep PF MFMAs' reads in flight ahead
 template <int N, int R>
@@ -399,6 +399,181 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 3b. dK, dV with two waves per SIMD (d_qk + d_v <= 256): eight waves own 128
+// keys of one (b, kv head). Waves w and w+4 hold the same 32 keys and take
+// the two 32-row halves of every 64-row query tile; K and V of the block sit
+// in LDS for the whole kernel (the B operands of S and dP are read from there,
+// which leaves the registers for the dK/dV accumulators), and the two partial
+// sums of each key are added through LDS at the end.
+// ---------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
+  constexpr int NW = 8, BNK = 128, BQ = 64;
+  constexpr int CPQ = DQK / 8, CPO = DV / 8;
+  constexpr int KS = DQK / 16, VS = DV / 16, DTK = DQK / 32, DTV = DV / 32;
+  constexpr int KT_BYTES = BNK * DQK * 2, VT_BYTES = BNK * DV * 2;
+  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2, STAGE = QT_BYTES + OT_BYTES + 2 * BQ * 4;
+  constexpr int LDS_BYTES = KT_BYTES + VT_BYTES + 2 * STAGE;
+  constexpr int RED_BYTES = 4 * (DTK + DTV) * 16 * 64 * 4;  // partial sums of waves 4..7
+  static_assert(RED_BYTES <= LDS_BYTES && LDS_BYTES <= 160 * 1024, "LDS budget");
+  // [K tile | V tile | stage 0 | stage 1], each stage [Q tile | dO tile | lse | D]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int cg = wave & 3, half = wave >> 2;  // key columns, query half
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int kb0 = (blockIdx.x / n_groups) * BNK;
+  const int key = kb0 + cg * 32 + lq;
+  const uint32_t smem_s = lds_u32(smem);
+  const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem);
+  const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + KT_BYTES);
+
+  f32x16 ak[DTK], av[DTV];
+#pragma unroll
+  for (int dt = 0; dt < DTK; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ak[dt][i] = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) av[dt][i] = 0.f;
+
+  const int off = p.Tk - p.Tq;
+  const int t_first = p.causal ? max(0, kb0 - off) : 0;
+  const int ntb = (p.Tq + BQ - 1) / BQ;
+  const int tb0 = min(t_first / BQ, ntb);
+  const int per_head = ntb - tb0;
+  const int n_it = p.g * per_head;
+
+  auto issue = [&](int it) {
+    const int hl = it / per_head, t0 = (tb0 + it % per_head) * BQ;
+    const int h = kvh * p.g + hl;
+    const uint32_t st = smem_s + (uint32_t)(KT_BYTES + VT_BYTES + (it & 1) * STAGE);
+    dma_tile<CPQ, BQ, NW>(reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh, p.q_st, t0, p.Tq - 1, st,
+                          wave, lane);
+    dma_tile<CPO, BQ, NW>(reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh, p.do_st, t0,
+                          p.Tq - 1, st + QT_BYTES, wave, lane);
+    if (wave == NW - 1) {
+      const int64_t rb = ((int64_t)b * p.H + h) * p.Tq + t0;
+      const void* lb = uniform_ptr(p.lse + rb);
+      const void* db = uniform_ptr(p.D + rb);
+      const uint32_t vo = 4u * (uint32_t)(min(t0 + lane, p.Tq - 1) - t0);
+      dma4(lb, vo, st + QT_BYTES + OT_BYTES);
+      dma4(db, vo, st + QT_BYTES + OT_BYTES + BQ * 4);
+    }
+  };
+
+  // K and V of the block, once (rows past Tk clamped: they are masked)
+  dma_tile<CPQ, BNK, NW>(reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh, p.k_st, kb0, p.Tk - 1,
+                         smem_s, wave, lane);
+  dma_tile<CPO, BNK, NW>(reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh, p.v_st, kb0, p.Tk - 1,
+                         smem_s + KT_BYTES, wave, lane);
+  if (n_it > 0) issue(0);
+  for (int it = 0; it < n_it; ++it) {
+    wait_all_loads();
+    barrier();
+    if (it + 1 < n_it) issue(it + 1);
+    const unsigned char* sp = smem + KT_BYTES + VT_BYTES + (it & 1) * STAGE;
+    const bf16_t* qt = reinterpret_cast<const bf16_t*>(sp);
+    const bf16_t* ot = reinterpret_cast<const bf16_t*>(sp + QT_BYTES);
+    const float* rl = reinterpret_cast<const float*>(sp + QT_BYTES + OT_BYTES);
+    const float* rd = rl + BQ;
+    const int t0 = (tb0 + it % per_head) * BQ;
+    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (!p.causal || t0 + off >= kb0 + BNK - 1);
+    const int qs = half;
+    f32x16 S, dP;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+    const int r = qs * 32 + lq, kr = cg * 32 + lq;
+#pragma unroll
+    for (int s = 0; s < (KS > VS ? KS : VS); ++s) {
+      if (s < KS) S = mfma32(row_frag<CPQ>(qt, r, s, lh), row_frag<CPQ>(kt, kr, s, lh), S);
+      if (s < VS) dP = mfma32(row_frag<CPO>(ot, r, s, lh), row_frag<CPO>(vt, kr, s, lh), dP);
+    }
+    pipeline_reads<KS + VS, 2>();
+    float P[16], dS[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = qs * 32 + lh * 4 + 8 * g4;
+      const f32x4 L = *reinterpret_cast<const f32x4*>(rl + r0);
+      const f32x4 Dv = *reinterpret_cast<const f32x4*>(rd + r0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = g4 * 4 + j;
+        float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j] * kLog2e));
+        if (!full) {
+          const int t = t0 + r0 + j;
+          const int lim = t >= p.Tq ? -1 : (p.causal ? t + off : p.Tk - 1);
+          pr = (key <= lim) ? pr : 0.f;
+        }
+        P[i] = pr;
+        dS[i] = pr * (dP[i] - Dv[j]);
+      }
+    }
+    const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
+    const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+#pragma unroll
+    for (int dt = 0; dt < DTV; ++dt) {
+      av[dt] = mfma32(tr_frag<CPO>(ot, qs * 32, dt * 32, lane), pb0, av[dt]);
+      av[dt] = mfma32(tr_frag<CPO>(ot, qs * 32 + 16, dt * 32, lane), pb1, av[dt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DTK; ++dt) {
+      ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32, dt * 32, lane), db0, ak[dt]);
+      ak[dt] = mfma32(tr_frag<CPQ>(qt, qs * 32 + 16, dt * 32, lane), db1, ak[dt]);
+    }
+    pipeline_reads<2 * (DTV + DTK), 2>();
+  }
+
+  // waves 4..7 hand their partial sums to waves 0..3 through LDS
+  wait_all_loads();
+  barrier();
+  float* red = reinterpret_cast<float*>(smem) + cg * (DTK + DTV) * 16 * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DTK; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(red + ((dt * 4 + g4) * 64 + lane) * 4) =
+            f32x4{ak[dt][g4 * 4], ak[dt][g4 * 4 + 1], ak[dt][g4 * 4 + 2], ak[dt][g4 * 4 + 3]};
+#pragma unroll
+    for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(red + (((DTK + dt) * 4 + g4) * 64 + lane) * 4) =
+            f32x4{av[dt][g4 * 4], av[dt][g4 * 4 + 1], av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3]};
+  }
+  barrier();
+  if (half == 0 && key < p.Tk) {
+    bf16_t* dkp = reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st;
+    bf16_t* dvp = reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st;
+#pragma unroll
+    for (int dt = 0; dt < DTK; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + ((dt * 4 + g4) * 64 + lane) * 4);
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dkp + d) =
+            u32x2{pack2((ak[dt][g4 * 4] + o[0]) * p.scale, (ak[dt][g4 * 4 + 1] + o[1]) * p.scale),
+                  pack2((ak[dt][g4 * 4 + 2] + o[2]) * p.scale, (ak[dt][g4 * 4 + 3] + o[3]) * p.scale)};
+      }
+#pragma unroll
+    for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(red + (((DTK + dt) * 4 + g4) * 64 + lane) * 4);
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dvp + d) = u32x2{pack2(av[dt][g4 * 4] + o[0], av[dt][g4 * 4 + 1] + o[1]),
+                                                   pack2(av[dt][g4 * 4 + 2] + o[2], av[dt][g4 * 4 + 3] + o[3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 4. dQ: one workgroup per 32*NW folded query rows of one (b, kv head)
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, int NW, int BN>
@@ -527,7 +702,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 
 template <int DQK, int DV>
 int launch_bwd_cfg(const BwdParams& p, void* stream) {
-  constexpr int NW_KV = 4, NW_Q = 4, BN_Q = 64;
+  // dQ: two waves per SIMD where the registers allow it (d_qk + d_v <= 256)
+  constexpr int NW_KV = 4, NW_Q = DQK + DV > 256 ? 4 : 8, BN_Q = 64;
   constexpr int BQ_KV = DQK + DV > 256 ? 32 : 64;  // wide heads: one 32-row sub-block per step (registers)
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t R = (int64_t)p.B * p.H * p.Tq;
@@ -541,8 +717,14 @@ int launch_bwd_cfg(const BwdParams& p, void* stream) {
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   if (p.Tk > 0) {
-    const int nkb = (p.Tk + 32 * NW_KV - 1) / (32 * NW_KV);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3(nkb * p.B * p.Hkv), dim3(NW_KV * 64), 0, st, p);
+    if constexpr (DQK + DV <= 256) {
+      const int nkb = (p.Tk + 127) / 128;
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<DQK, DV>), dim3(nkb * p.B * p.Hkv), dim3(512), 0, st, p);
+    } else {
+      const int nkb = (p.Tk + 32 * NW_KV - 1) / (32 * NW_KV);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3(nkb * p.B * p.Hkv), dim3(NW_KV * 64), 0, st,
+                         p);
+    }
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   if (p.Tq > 0) {
