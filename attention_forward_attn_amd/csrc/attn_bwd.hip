@@ -228,11 +228,12 @@ template <int CPR, int BR, int NW>
 __device__ __forceinline__ void dma_tile(const bf16_t* base, int64_t st, int r0, int rmax, uint32_t lds, int wave,
                                          int lane) {
   constexpr int NI = BR * CPR / 64;
-  static_assert(NI % NW == 0, "tile instructions split evenly over the waves");
+  static_assert(BR * CPR % 64 == 0, "whole wave instructions");
   const void* sb = uniform_ptr(base + (int64_t)r0 * st);
 #pragma unroll
-  for (int m = 0; m < NI / NW; ++m) {
+  for (int m = 0; m < (NI + NW - 1) / NW; ++m) {
     const int j = wave + NW * m;
+    if (NI % NW != 0 && j >= NI) break;
     const int sl = 64 * j + lane, r = sl / CPR, c = (sl % CPR) ^ swz<CPR>(sl / CPR);
     const int rr = min(r0 + r, rmax) - r0;
     dma16(sb, 2u * (uint32_t)(rr * (int32_t)st + c * 8), lds + 1024u * j);
