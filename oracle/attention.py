@@ -95,6 +95,24 @@ def _causal_mask(ts, Tq: int, Tk: int) -> np.ndarray:
     return j <= t + (Tk - Tq)
 
 
+def _window_mask(ts, Tq: int, Tk: int, left: int, right: int) -> np.ndarray:
+    """Boolean [len(ts), Tk]: True where key j lies in the sliding window of token t.
+
+    The window is centred on the bottom-right diagonal position t + (Tk - Tq):
+    ``left`` keys before it and ``right`` keys after it, a negative value
+    meaning unbounded on that side (the (left, right) window arguments that
+    TransformerEngine's FA4 path forwards, TE page "Summary").
+    """
+    j = np.arange(Tk)[None, :]
+    c = np.asarray(ts)[:, None] + (Tk - Tq)
+    keep = np.ones((len(ts), Tk), dtype=bool)
+    if left >= 0:
+        keep &= j >= c - left
+    if right >= 0:
+        keep &= j <= c + right
+    return keep
+
+
 def _tile_row_token(f: np.ndarray, f0: int, Tq: int) -> np.ndarray:
     """Token index of folded rows ``f`` (a tile starting at folded row ``f0``).
 
@@ -132,7 +150,7 @@ def _softmax_rows(S: np.ndarray, sink: Optional[float]) -> Tuple[np.ndarray, np.
 
 
 def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
-                    rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+                    rows: Optional[Iterable[Tuple[int, int, int]]] = None, window: Tuple[int, int] = (-1, -1)):
     """Dense attention forward in fp64.
 
     q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v], sinks [H] or None.
@@ -142,7 +160,12 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
     Steps (explicit, in the order of the definition):
       1. K, V expanded to H heads by repeat_kv (kv-major).
       2. S = scale * q . K^T, an explicit [Tq, Tk] score matrix per (b, h).
-      3. Causal: S[t, j] = -inf where j > t + (Tk - Tq).
+      3. Causal: S[t, j] = -inf where j > t + (Tk - Tq). Sliding window
+         (left, right): also -inf outside [c - left, c + right] with
+         c = t + (Tk - Tq); a negative bound is no bound. The window never
+         widens the causal mask (the ArcFlash page, "What this does NOT do",
+         names a window clamp that turned causal attention into full
+         attention as a defect).
       4. Row softmax with the sink (if any) added to the denominator only.
       5. O = P . V;  lse = m + ln(denominator).
     """
@@ -160,6 +183,8 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
         S = scale * (q[b, h, ts] @ K[b, h].T)
         if causal:
             S = np.where(_causal_mask(ts, Tq, Tk), S, NEG_INF)
+        if window[0] >= 0 or window[1] >= 0:
+            S = np.where(_window_mask(ts, Tq, Tk, window[0], window[1]), S, NEG_INF)
         P, lse = _softmax_rows(S, None if sk is None else float(sk[h]))
         return P @ V[b, h], lse
 

@@ -28,8 +28,10 @@ def _attend(scores, values, sink):
     return o, math.log(math.fsum(tot))
 
 
-def brute_dense(q, k, v, scale, causal, sinks=None):
-    """q [B][H][Tq][Dqk], k [B][Hkv][Tk][Dqk], v [B][Hkv][Tk][Dv] (nested lists or arrays)."""
+def brute_dense(q, k, v, scale, causal, sinks=None, window=(-1, -1)):
+    """q [B][H][Tq][Dqk], k [B][Hkv][Tk][Dqk], v [B][Hkv][Tk][Dv] (nested lists or arrays).
+    window (left, right): key j kept iff left < 0 or j >= t + Tk - Tq - left, and
+    right < 0 or j <= t + Tk - Tq + right (tested key by key)."""
     B, H, Tq, Dqk = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv, Tk, Dv = len(k[0]), len(k[0][0]), len(v[0][0][0])
     g = H // Hkv
@@ -42,6 +44,10 @@ def brute_dense(q, k, v, scale, causal, sinks=None):
                 sc, vals = [], []
                 for j in range(Tk):
                     if causal and j > t + (Tk - Tq):
+                        continue
+                    if window[0] >= 0 and t + (Tk - Tq) - j > window[0]:
+                        continue
+                    if window[1] >= 0 and j - (t + (Tk - Tq)) > window[1]:
                         continue
                     sc.append(scale * math.fsum(float(q[b][h][t][d]) * float(k[b][kvh][j][d])
                                                 for d in range(Dqk)))

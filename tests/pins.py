@@ -150,6 +150,38 @@ def check_closed_forms(orc=oracle):
     return worst
 
 
+def check_window(orc=oracle):
+    """Sliding windows: brute force (different formulation), the diagonal-only
+    closed form, wide windows equal no window, and a window never widens causal."""
+    worst = 0.0
+    for i, (B, H, Hkv, Tq, Tk, d) in enumerate([(1, 4, 2, 9, 9, 5), (2, 2, 1, 5, 11, 3), (1, 2, 2, 8, 4, 4)]):
+        q = _rand((B, H, Tq, d), 700 + i, 0.7)
+        k = _rand((B, Hkv, Tk, d), 710 + i, 0.7)
+        v = _rand((B, Hkv, Tk, d), 720 + i)
+        sinks = _rand((H,), 730 + i)
+        for causal in (False, True):
+            for win in ((0, -1), (2, -1), (3, 1), (-1, 2), (1, 0), (0, 0)):
+                for sk in (None, sinks):
+                    o, l = orc.dense_attention(q, k, v, scale=0.5, causal=causal, sinks=sk, window=win)
+                    bo, bl = brute_dense(q, k, v, 0.5, causal, sk, window=win)
+                    worst = max(worst, _err(o, bo), _err(l, bl))
+    # left = 0 with causal: each row sees only its diagonal key (Tq = Tk)
+    q, k, v = _rand((1, 2, 6, 4), 740), _rand((1, 1, 6, 4), 741), _rand((1, 1, 6, 3), 742)
+    o, l = orc.dense_attention(q, k, v, scale=0.5, causal=True, window=(0, -1))
+    for h in range(2):
+        for t in range(6):
+            worst = max(worst, _err(o[0, h, t], v[0, 0, t]), _err(l[0, h, t], 0.5 * float(q[0, h, t] @ k[0, 0, t])))
+    # windows wider than the keys are no window; with causal, any right bound is causal
+    for causal in (False, True):
+        base = orc.dense_attention(q, k, v, scale=0.5, causal=causal)
+        wide = orc.dense_attention(q, k, v, scale=0.5, causal=causal, window=(6, 6))
+        worst = max(worst, _err(base[0], wide[0]), _err(base[1], wide[1]))
+    c = orc.dense_attention(q, k, v, scale=0.5, causal=True)
+    cw = orc.dense_attention(q, k, v, scale=0.5, causal=True, window=(-1, 3))
+    worst = max(worst, _err(c[0], cw[0]), _err(c[1], cw[1]))
+    return worst
+
+
 def check_causal_differs(orc=oracle):
     """Causal must not silently equal full attention (returns 0 when it differs)."""
     q, k, v = _rand((1, 2, 8, 4), 11), _rand((1, 1, 8, 4), 12), _rand((1, 1, 8, 4), 13)
@@ -302,6 +334,7 @@ def check_lse_logsumexp(orc=oracle):
 
 
 ALL_CHECKS = {
+    "window": check_window,
     "brute_dense": check_brute_dense,
     "brute_sparse": check_brute_sparse,
     "library_dense": check_library_dense,

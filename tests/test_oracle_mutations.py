@@ -74,3 +74,19 @@ def test_lse_base2_caught(monkeypatch):
 def test_sparse_value_columns_caught(monkeypatch):
     monkeypatch.setattr(OA, "_value_rows", lambda G, d_v: G[:, G.shape[1] - d_v:][:, ::-1])
     _assert_caught(_caught(["brute_sparse", "sparse_equals_dense_mqa"]))
+
+
+def test_window_ignored_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_window_mask", lambda ts, Tq, Tk, left, right: np.ones((len(ts), Tk), dtype=bool))
+    _assert_caught(_caught(["window"]))
+
+
+def test_window_rewrites_causal_caught(monkeypatch):
+    """The defect the ArcFlash page names: a window clamp that turns causal into full attention."""
+    orig = OA.dense_attention
+
+    def clamp(q, k, v, *, causal, window=(-1, -1), **kw):
+        return orig(q, k, v, causal=causal and window == (-1, -1), window=window, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention", clamp)
+    _assert_caught(_caught(["window"]))
