@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -39,6 +39,8 @@ class AttnDenseArgs(ctypes.Structure):
         ("out", ctypes.c_void_p), ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_st", ctypes.c_int64),
         ("lse", ctypes.c_void_p),
         ("sinks", ctypes.c_void_p),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -193,7 +195,8 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
-def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None) -> AttnDenseArgs:
+def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
+               window: Tuple[int, int] = (-1, -1)) -> AttnDenseArgs:
     """Fill the C argument struct from tensors (BHSD or any strided view with unit last stride)."""
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
@@ -213,17 +216,20 @@ def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None) -> 
     a.out, (a.o_sb, a.o_sh, a.o_st) = out.data_ptr(), out.stride()[:3]
     a.lse = lse.data_ptr()
     a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.window_left, a.window_right = int(window[0]), int(window[1])
     return a
 
 
 def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
-          out=None, lse=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+          out=None, lse=None, stream=None, window: Tuple[int, int] = (-1, -1)) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Fused dense attention forward on the GPU.
 
     q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v] (bf16, or fp32 for the
-    split-bf16 path), sinks [H] fp32 or None. Returns (out [B,H,Tq,d_v] in the
-    input dtype, lse [B,H,Tq] fp32). Launches on ``stream`` (default: torch's
-    current stream) and does not synchronise.
+    split-bf16 path), sinks [H] fp32 or None. ``window`` = (left, right) keys
+    around each row's diagonal position t + Tk - Tq (-1: unbounded; bf16 only;
+    it never widens the causal mask). Returns (out [B,H,Tq,d_v] in the input
+    dtype, lse [B,H,Tq] fp32). Launches on ``stream`` (default: torch's current
+    stream) and does not synchronise.
     """
     import torch
 
@@ -240,13 +246,14 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
     if not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
-    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks)
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
     _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
 
 
 def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
-                  n_splits: int = 0, out=None, lse=None, workspace=None, stream=None):
+                  n_splits: int = 0, out=None, lse=None, workspace=None, stream=None,
+                  window: Tuple[int, int] = (-1, -1)):
     """Split-KV dense forward (decode and other few-row shapes): same inputs
     and results as :func:`dense`. The keys are cut into ``n_splits`` ranges
     (0: the library's choice); the fp32 partials go to ``workspace``, a uint8
@@ -268,7 +275,7 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
     if not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
-    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks)
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
     need = int(lib.attn_splitkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
     if need < 0:
         _check(ATTN_INVALID_ARGUMENT)
@@ -294,6 +301,7 @@ def _shape_args(B, H, Hkv, Tq, Tk, d_qk, d_v, dtype, causal, sinks, scale) -> At
     a.out, a.o_sb, a.o_sh, a.o_st = _FAKE_PTR, H * Tq * d_v, Tq * d_v, d_v
     a.lse = _FAKE_PTR
     a.sinks = _FAKE_PTR if sinks else None
+    a.window_left = a.window_right = -1
     return a
 
 

@@ -103,6 +103,10 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   if (a->d_qk < 1 || a->d_v < 1) return fail(ATTN_INVALID_ARGUMENT, "head dims must be >= 1");
   if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (a->window_left < -1 || a->window_right < -1)
+    return fail(ATTN_INVALID_ARGUMENT, "window bounds must be >= -1 (-1: unbounded)");
+  if (a->dtype != ATTN_BF16 && (a->window_left >= 0 || a->window_right >= 0))
+    return fail(ATTN_UNSUPPORTED, "sliding windows are compiled for bf16 inputs only");
   const attn::KernelConfig* cfg = find_config(a->dtype, a->d_qk, a->d_v, 0);
   if (!cfg)
     return fail(ATTN_UNSUPPORTED, "no compiled dense kernel for dtype %d with (d_qk, d_v) = (%d, %d)", a->dtype,
@@ -139,6 +143,8 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
   p.npool = 0;
   p.causal = a->causal;
+  p.win_left = a->window_left;
+  p.win_right = a->window_right;
   p.scale = a->scale;
   p.c = a->scale * 1.4426950408889634f;
   const int BM = cfg->block_rows;
@@ -222,6 +228,7 @@ attn_status validate_sparse(const attn_sparse_args* a, DensePlan* out) {
   p.idx_ss = a->idx_ss;
   p.B = a->Sq; p.H = a->Hq; p.Hkv = 1; p.Tq = 1; p.Tk = a->topk; p.g = 1;
   p.npool = a->N;
+  p.win_left = p.win_right = -1;
   p.causal = 0;
   p.scale = a->scale;
   p.c = a->scale * 1.4426950408889634f;

@@ -879,27 +879,41 @@ attn_fwd_dma_kernel(const KernelParams p) {
       }
     }
   }
-  int kend = p.Tk, kfull = p.Tk;
-  if (!SPARSE && p.causal) {
-    const int off = p.Tk - p.Tq;
-    kend = min(p.Tk, max(0, t_hi + off + 1));
-    kfull = min(p.Tk, max(0, t_lo + off + 1));
+  // keys [0, kend) are needed and no row of the tile masks a key below
+  // kfull; with a sliding window, none masks a key from klfull on and no row
+  // sees a key before kstart. `up` = keys after a row's diagonal position it
+  // may see (-1: unbounded); the window never widens the causal bound.
+  int kend = p.Tk, kfull = p.Tk, kstart = 0, klfull = 0;
+  const int off = p.Tk - p.Tq;
+  const int up = p.causal ? 0 : p.win_right;
+  if (!SPARSE && up >= 0) {
+    kend = min(p.Tk, max(0, t_hi + off + up + 1));
+    kfull = min(p.Tk, max(0, t_lo + off + up + 1));
   }
-  // split-KV: this workgroup sees keys [k_lo, k_hi) only; from here on key
-  // positions (kend, kfull, the row limits, the K/V bases) are relative to k_lo
-  int k_lo = 0;
+  if (!SPARSE && p.win_left >= 0) {
+    kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
+    klfull = min(p.Tk, max(0, t_hi + off - p.win_left));
+  }
+  // this workgroup sees keys [k_lo, k_hi) only (split-KV: one range; sliding
+  // window: from the block holding kstart); from here on key positions
+  // (kend, kfull, klfull, the row limits, the K/V bases) are relative to k_lo
+  int k_lo = 0, k_hi = p.Tk;
   if (!SPARSE && p.n_splits > 1) {
     k_lo = blockIdx.y * p.split_keys;
-    const int k_hi = min(p.Tk, k_lo + p.split_keys);
+    k_hi = min(p.Tk, k_lo + p.split_keys);
+  }
+  if (!SPARSE) {
+    k_lo = max(k_lo, (kstart / BN) * BN);
     kend = max(0, min(kend, k_hi) - k_lo);
     kfull = max(0, min(kfull, k_hi) - k_lo);
+    klfull = max(0, klfull - k_lo);
   }
 
   // ---------------------------------------------------------------- the query row of this lane
   const int r = qg * 32 + lq;
   const bool row_ok = r < nrows;
   const int rr = row_ok ? r : 0;
-  int row_lim, row_h;
+  int row_lim, row_lo = -(1 << 30), row_h;
   int64_t q_off, o_off, l_off;
   if constexpr (SPARSE) {
     row_h = rr;
@@ -911,8 +925,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
     const int f = f0 + rr;
     row_h = kvh * p.g + f / p.Tq;
     const int t = f % p.Tq;
-    row_lim = p.causal ? min(p.Tk - 1, t + p.Tk - p.Tq) : p.Tk - 1;
-    row_lim = min(row_lim - k_lo, kend - 1);  // split-KV: relative to the range
+    row_lim = up >= 0 ? min(p.Tk - 1, t + off + up) : p.Tk - 1;
+    row_lim = min(row_lim - k_lo, kend - 1);  // relative to the range
+    if (p.win_left >= 0) row_lo = t + off - p.win_left - k_lo;
     q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (int64_t)t * p.q_st;
     o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (int64_t)t * p.o_st;
     l_off = ((int64_t)b * p.H + row_h) * p.Tq + t;
@@ -1291,6 +1306,17 @@ attn_fwd_dma_kernel(const KernelParams p) {
           for (int i = 0; i < 16; ++i) {
             const int over = (lim - (mt * 32 + (i >> 2) * 8 + (i & 3))) >> 31;  // all ones past the limit
             S[mt][i] = __int_as_float((__float_as_int(S[mt][i]) & ~over) | (int)(0xff800000u & (uint32_t)over));
+          }
+      }
+      if (key0 < klfull) {
+        // sliding window: mask keys before the row's window (offset below lo)
+        const int lo = row_lo - key0 - lh * 4;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int under = ((mt * 32 + (i >> 2) * 8 + (i & 3)) - lo) >> 31;  // all ones before the window
+            S[mt][i] = __int_as_float((__float_as_int(S[mt][i]) & ~under) | (int)(0xff800000u & (uint32_t)under));
           }
       }
     }

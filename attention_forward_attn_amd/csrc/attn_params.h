@@ -24,6 +24,7 @@ struct KernelParams {
   int32_t B, H, Hkv, Tq, Tk, g;  // sparse: B = Sq, H = Hq, Hkv = 1, Tk = topk
   int32_t npool;                 // sparse: rows in the pool
   int32_t causal;
+  int32_t win_left, win_right;   // sliding window around the diagonal (-1: unbounded side); dense bf16
   float scale;                   // softmax scale
   float c;                       // scale * log2(e)
 

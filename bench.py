@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak); sparse top-k GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-WORKLOAD_IDS = {"tiny": 1, "gqa": 2, "mla": 3, "mqa512": 4, "sparse": 5, "decode512": 6}
+WORKLOAD_IDS = {"tiny": 1, "gqa": 2, "mla": 3, "mqa512": 4, "sparse": 5, "decode512": 6, "swa1024": 7}
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 KERNEL_SOURCES = ("attention_forward_attn_amd/csrc/attn_kernels.hip",
                   "attention_forward_attn_amd/csrc/attn_params.h")
@@ -60,13 +60,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def visible_pairs(B, H, Tq, Tk, causal) -> int:
-    if not causal:
+def visible_pairs(B, H, Tq, Tk, causal, window=(-1, -1)) -> int:
+    """(row, key) pairs the mask keeps: causal bottom-right, and a sliding window
+    of (left, right) keys around the diagonal (-1: unbounded)."""
+    if not causal and window == (-1, -1):
         return B * H * Tq * Tk
     off = Tk - Tq
+    up = 0 if causal else window[1]
     tot = 0
     for t in range(Tq):
-        tot += max(0, min(Tk, t + off + 1))
+        hi = Tk - 1 if up < 0 else min(Tk - 1, t + off + up)
+        lo = 0 if window[0] < 0 else max(0, t + off - window[0])
+        tot += max(0, hi - lo + 1)
     return B * H * tot
 
 
@@ -76,8 +81,9 @@ def describe(n: int) -> str:
     s = synth.spec(n)
     if s.kind == "dense":
         t = f"T={s.Tq}" if s.Tq == s.Tk else f"Tq={s.Tq} Tk={s.Tk}"
+        w = "" if s.window == (-1, -1) else f" window=({s.window[0]},{s.window[1]})"
         return (f"{s.name}: dense causal B={s.B} H={s.H} Hkv={s.Hkv} {t} d_qk={s.d_qk} d_v={s.d_v} "
-                f"{s.dtype}" + (" sinks" if s.sinks else ""))
+                f"{s.dtype}" + (" sinks" if s.sinks else "") + w)
     return f"{s.name}: sparse top-k Sq={s.Sq} Hq={s.Hq} N={s.N} d_qk={s.d_qk} d_v={s.d_v} topk={s.topk} bf16"
 
 
@@ -87,7 +93,7 @@ def work(n: int) -> dict:
     s = synth.spec(n)
     if s.kind == "dense":
         elt = 2 if s.dtype == "bf16" else 4
-        pairs = visible_pairs(s.B, s.H, s.Tq, s.Tk, s.causal)
+        pairs = visible_pairs(s.B, s.H, s.Tq, s.Tk, s.causal, s.window)
         flops = 2 * pairs * (s.d_qk + s.d_v)
         nbytes = elt * (s.B * s.H * s.Tq * s.d_qk + s.B * s.Hkv * s.Tk * (s.d_qk + s.d_v)
                         + s.B * s.H * s.Tq * s.d_v) + 4 * s.B * s.H * s.Tq + (4 * s.H if s.sinks else 0)
@@ -123,9 +129,10 @@ def make_call(n: int, split: bool = False):
 
         def step():
             if split:
-                A.dense_splitkv(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse, workspace=ws)
+                A.dense_splitkv(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse, workspace=ws,
+                                window=s.window)
             else:
-                A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse)
+                A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, out=out, lse=lse, window=s.window)
 
         path = A.plan_dense(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v, dtype=s.dtype, sinks=s.sinks)["path"]
     else:
@@ -215,8 +222,9 @@ def cpu_baseline(n: int, inp: dict, budget_s: float = 12.0) -> dict:
                 kvh = h // g
                 oracle.dense_attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, kvh:kvh + 1],
                                        inp["v"][b:b + 1, kvh:kvh + 1], scale=s.scale, causal=s.causal,
-                                       sinks=None if inp["sinks"] is None else inp["sinks"][h:h + 1])
-                done_flops += 2 * visible_pairs(1, 1, s.Tq, s.Tk, s.causal) * (s.d_qk + s.d_v)
+                                       sinks=None if inp["sinks"] is None else inp["sinks"][h:h + 1],
+                                       window=s.window)
+                done_flops += 2 * visible_pairs(1, 1, s.Tq, s.Tk, s.causal, s.window) * (s.d_qk + s.d_v)
                 units += 1
                 if time.perf_counter() - t0 > budget_s:
                     break
@@ -542,6 +550,14 @@ def main():
         for m in (2, 3):
             next_rows.append(measure_bwd(m, st, wu))
             torch.cuda.empty_cache()
+        # the sliding-window forward
+        r = measure(7, st, wu)
+        next_rows.append({"row": "sliding-window forward (window_left = 1024)", "workload": describe(7),
+                          "path": r["path"], "value": round(r["value"], 3), "unit": r["unit"],
+                          "kernel_ms": round(r["timing"]["kernel_ms_mean"], 5), "roofline": r["roofline"],
+                          "verdict": r["verdict"]})
+        del r
+        torch.cuda.empty_cache()
     ceil = None
     if not args.no_ceilings:
         ceil = ceilings()

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -86,6 +86,15 @@ typedef enum attn_dtype {
  *        (256,256), (512,512) in bf16; (64,64) and (128,128) in f32.
  *   Sizes: B, H, Hkv >= 1, H % Hkv == 0; Tq, Tk >= 0 (Tq == 0 launches nothing;
  *        Tk == 0 writes out = 0 and lse = -inf, or sink).
+ *   window_left, window_right: sliding window around each row's diagonal
+ *        position c = t + (Tk - Tq): key j is visible only if
+ *        j >= c - window_left and j <= c + window_right; -1 leaves that side
+ *        unbounded (the window arguments of the FA4 wrappers in
+ *        TransformerEngine pull request 3259, "Summary"). The window only
+ *        narrows the mask: with causal = 1, window_right has no effect (a
+ *        window clamp that widened causal attention to full attention is a
+ *        defect the ArcFlash pull request lists under "What this does NOT
+ *        do"). bf16 only; (-1, -1) for float32 inputs.
  */
 typedef struct attn_dense_args {
   uint32_t struct_size; /* = sizeof(attn_dense_args) */
@@ -103,6 +112,8 @@ typedef struct attn_dense_args {
   int64_t o_sb, o_sh, o_st;
   float* lse;
   const float* sinks;
+  int32_t window_left;  /* -1: no left bound */
+  int32_t window_right; /* -1: no right bound */
 } attn_dense_args;
 
 /*

@@ -24,6 +24,9 @@ One more workload measures the split-KV forward (a "next" step beyond the
 five): ``decode512`` -- one new token per sequence (Tq=1) of the MQA d=512
 layer with sinks (the absorbed-MQA decode the ArcFlash page discusses at
 t_q = 1), B=8 sequences, a 32768-token cache, bf16; seed 6, same recipe.
+And one measures the sliding-window forward: ``swa1024`` -- the GQA layer of
+``gqa`` at 8192 tokens where each query also sees the 1024 keys before its
+own (causal, window_left = 1024), seed 7.
 
 Generation recipe (fixed so that every consumer sees identical bits):
 ``torch.Generator('cpu').manual_seed(seed)`` with seed = workload number (1..5);
@@ -57,6 +60,7 @@ class DenseSpec:
     dtype: str          # "bf16" or "f32"
     causal: bool
     sinks: bool
+    window: tuple = (-1, -1)  # sliding window (left, right) keys around the diagonal; -1: unbounded
 
     @property
     def scale(self) -> float:
@@ -110,6 +114,8 @@ WORKLOADS = {
 NEXT_WORKLOADS = {
     6: DenseSpec("decode512", 6, B=8, H=64, Hkv=1, Tq=1, Tk=32768, d_qk=512, d_v=512,
                  dtype="bf16", causal=True, sinks=True),
+    7: DenseSpec("swa1024", 7, B=2, H=32, Hkv=8, Tq=8192, Tk=8192, d_qk=128, d_v=128,
+                 dtype="bf16", causal=True, sinks=False, window=(1024, -1)),
 }
 
 
