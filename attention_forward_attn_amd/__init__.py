@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -94,6 +94,8 @@ class AttnDenseBwdArgs(ctypes.Structure):
         ("dk", ctypes.c_void_p), ("dk_sb", ctypes.c_int64), ("dk_sh", ctypes.c_int64), ("dk_st", ctypes.c_int64),
         ("dv", ctypes.c_void_p), ("dv_sb", ctypes.c_int64), ("dv_sh", ctypes.c_int64), ("dv_st", ctypes.c_int64),
         ("dsinks", ctypes.c_void_p),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -425,7 +427,7 @@ def abi_version() -> int:
 
 
 def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: float, sinks=None,
-                   dsinks=None) -> AttnDenseBwdArgs:
+                   dsinks=None, window: Tuple[int, int] = (-1, -1)) -> AttnDenseBwdArgs:
     """Fill the backward's C argument struct from tensors (unit last stride)."""
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
@@ -449,11 +451,13 @@ def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: 
     a.lse = lse.data_ptr()
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.dsinks = dsinks.data_ptr() if dsinks is not None else None
+    a.window_left, a.window_right = int(window[0]), int(window[1])
     return a
 
 
 def dense_backward(q, k, v, out, dout, lse, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
-                   dq=None, dk=None, dv=None, dsinks=None, workspace=None, stream=None):
+                   dq=None, dk=None, dv=None, dsinks=None, workspace=None, stream=None,
+                   window: Tuple[int, int] = (-1, -1)):
     """Dense attention backward on the GPU (bf16): returns (dq, dk, dv, dsinks).
 
     ``out`` and ``lse`` are the forward's results for (q, k, v, sinks); ``dout``
@@ -482,7 +486,7 @@ def dense_backward(q, k, v, out, dout, lse, *, causal: bool = True, scale: Optio
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [B, H, Tq]")
     a = dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, causal=causal, scale=scale, sinks=sinks,
-                       dsinks=dsinks)
+                       dsinks=dsinks, window=window)
     # a negative size means invalid sizes or head dims: the call below then
     # reports the library's own status before launching anything
     need = int(lib.attn_bwd_dense_workspace_bytes(ctypes.byref(a)))
@@ -502,6 +506,7 @@ def bwd_workspace_bytes(B, H, Hkv, Tq, Tk, d_qk, d_v) -> int:
     a.dtype = ATTN_BF16
     a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = B, H, Hkv, Tq, Tk, d_qk, d_v
     a.causal, a.scale = 1, 1.0 / math.sqrt(d_qk)
+    a.window_left = a.window_right = -1
     n = int(load_library().attn_bwd_dense_workspace_bytes(ctypes.byref(a)))
     if n < 0:
         _check(ATTN_INVALID_ARGUMENT)

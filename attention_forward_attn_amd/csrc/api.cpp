@@ -476,6 +476,8 @@ attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
   if (a->d_qk < 1 || a->d_v < 1) return fail(ATTN_INVALID_ARGUMENT, "head dims must be >= 1");
   if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (a->window_left < -1 || a->window_right < -1)
+    return fail(ATTN_INVALID_ARGUMENT, "window bounds must be >= -1 (-1: unbounded)");
   if (bwd_path(a->d_qk, a->d_v) < 0)
     return fail(ATTN_UNSUPPORTED, "no compiled dense backward for (d_qk, d_v) = (%d, %d)", a->d_qk, a->d_v);
   // one-dimensional grids: (key blocks or row tiles) x B x Hkv workgroups
@@ -548,6 +550,8 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
   p.dv_sb = a->dv_sb; p.dv_sh = a->dv_sh; p.dv_st = a->dv_st;
   p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
   p.causal = a->causal;
+  p.win_left = a->window_left;
+  p.win_right = a->window_right;
   p.scale = a->scale;
   p.c = a->scale * 1.4426950408889634f;
   const int err = attn::launch_bwd(p, a->d_qk, a->d_v, stream);

@@ -283,11 +283,16 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) av[dt][i] = 0.f;
 
   const int off = p.Tk - p.Tq;
-  // query tokens that can see a key of this block start at kb0 - off (causal)
-  const int t_first = p.causal ? max(0, kb0 - off) : 0;
+  // keys after its diagonal position a row may see (-1: unbounded); the
+  // window never widens the causal bound
+  const int up = p.causal ? 0 : p.win_right;
+  // query tokens that can see a key of this block: from kb0 - off - up (the
+  // upper bound) to kb0 + BNK - 1 - off + win_left (the window's lower bound)
+  const int t_first = up >= 0 ? max(0, kb0 - off - up) : 0;
+  const int t_last = p.win_left >= 0 ? min(p.Tq - 1, kb0 + BNK - 1 - off + p.win_left) : p.Tq - 1;
   const int ntb = (p.Tq + BQ - 1) / BQ;
   const int tb0 = min(t_first / BQ, ntb);
-  const int per_head = ntb - tb0;
+  const int per_head = t_last < t_first ? 0 : max(0, min(ntb, t_last / BQ + 1) - tb0);
   const int n_it = p.g * per_head;
   const uint32_t smem_s = lds_u32(smem);
 
@@ -324,7 +329,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
     const float* rd = rl + BQ;
     const int t0 = (tb0 + it % per_head) * BQ;
     // every (row, key) pair of the tile visible: no per-score mask
-    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (!p.causal || t0 + off >= kb0 + BNK - 1);
+    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (up < 0 || t0 + off + up >= kb0 + BNK - 1) &&
+                      (p.win_left < 0 || t0 + BQ - 1 + off - p.win_left <= kb0);
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
       f32x16 S, dP;
@@ -353,8 +359,9 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
           float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j] * kLog2e));
           if (!full) {
             const int t = t0 + r0 + j;
-            const int lim = t >= p.Tq ? -1 : (p.causal ? t + off : p.Tk - 1);
-            pr = (key <= lim) ? pr : 0.f;
+            const int lim = t >= p.Tq ? -1 : (up >= 0 ? t + off + up : p.Tk - 1);
+            const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
+            pr = (key <= lim && key >= lo) ? pr : 0.f;
           }
           P[i] = pr;
           dS[i] = pr * (dP[i] - Dv[j]);
@@ -441,10 +448,16 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
     for (int i = 0; i < 16; ++i) av[dt][i] = 0.f;
 
   const int off = p.Tk - p.Tq;
-  const int t_first = p.causal ? max(0, kb0 - off) : 0;
+  // keys after its diagonal position a row may see (-1: unbounded); the
+  // window never widens the causal bound
+  const int up = p.causal ? 0 : p.win_right;
+  // query tokens that can see a key of this block: from kb0 - off - up (the
+  // upper bound) to kb0 + BNK - 1 - off + win_left (the window's lower bound)
+  const int t_first = up >= 0 ? max(0, kb0 - off - up) : 0;
+  const int t_last = p.win_left >= 0 ? min(p.Tq - 1, kb0 + BNK - 1 - off + p.win_left) : p.Tq - 1;
   const int ntb = (p.Tq + BQ - 1) / BQ;
   const int tb0 = min(t_first / BQ, ntb);
-  const int per_head = ntb - tb0;
+  const int per_head = t_last < t_first ? 0 : max(0, min(ntb, t_last / BQ + 1) - tb0);
   const int n_it = p.g * per_head;
 
   auto issue = [&](int it) {
@@ -481,7 +494,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
     const float* rl = reinterpret_cast<const float*>(sp + QT_BYTES + OT_BYTES);
     const float* rd = rl + BQ;
     const int t0 = (tb0 + it % per_head) * BQ;
-    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (!p.causal || t0 + off >= kb0 + BNK - 1);
+    const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (up < 0 || t0 + off + up >= kb0 + BNK - 1) &&
+                      (p.win_left < 0 || t0 + BQ - 1 + off - p.win_left <= kb0);
     const int qs = half;
     f32x16 S, dP;
 #pragma unroll
@@ -508,8 +522,9 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
         float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[j] * kLog2e));
         if (!full) {
           const int t = t0 + r0 + j;
-          const int lim = t >= p.Tq ? -1 : (p.causal ? t + off : p.Tk - 1);
-          pr = (key <= lim) ? pr : 0.f;
+          const int lim = t >= p.Tq ? -1 : (up >= 0 ? t + off + up : p.Tk - 1);
+          const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
+          pr = (key <= lim && key >= lo) ? pr : 0.f;
         }
         P[i] = pr;
         dS[i] = pr * (dP[i] - Dv[j]);
@@ -598,7 +613,9 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
   const int fc = valid ? f : rows - 1;
   const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
   const int off = p.Tk - p.Tq;
-  const int row_lim = !valid ? -1 : (p.causal ? min(t + off, p.Tk - 1) : p.Tk - 1);
+  const int up = p.causal ? 0 : p.win_right;  // keys after the diagonal a row may see (-1: unbounded)
+  const int row_lim = !valid ? -1 : (up >= 0 ? min(t + off + up, p.Tk - 1) : p.Tk - 1);
+  const int row_lo = p.win_left >= 0 ? t + off - p.win_left : 0;
   const int64_t lrow = ((int64_t)b * p.H + h) * p.Tq + t;
   const float lse = p.lse[lrow];
   const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
@@ -614,17 +631,24 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
     for (int s = 0; s < VS; ++s) dof[s] = *reinterpret_cast<const bf16x8*>(dp + s * 16 + lh * 8);
   }
 
-  // keys this tile can see (kend), and keys every row of it sees (kfull)
-  int kend = p.Tk, kfull = (f0 + BM <= rows) ? p.Tk : 0;
-  if (p.causal) {
+  // keys this tile can see ([kstart, kend)), and keys every row of it sees
+  // ([klfull, kfull)): blocks inside the latter need no per-score mask
+  int kend = p.Tk, kfull = (f0 + BM <= rows) ? p.Tk : 0, kstart = 0, klfull = 0;
+  {
     const int f_last = min(f0 + BM, rows) - 1;
     const bool one_head = f_last / p.Tq == f0 / p.Tq;
     const int t_hi = one_head ? f_last % p.Tq : p.Tq - 1;
     const int t_lo = one_head ? f0 % p.Tq : 0;
-    kend = max(0, min(p.Tk, t_hi + off + 1));
-    kfull = min(kfull, max(0, t_lo + off + 1));
+    if (up >= 0) {
+      kend = max(0, min(p.Tk, t_hi + off + up + 1));
+      kfull = min(kfull, max(0, t_lo + off + up + 1));
+    }
+    if (p.win_left >= 0) {
+      kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
+      klfull = max(0, t_hi + off - p.win_left);
+    }
   }
-  const int nb = (kend + BN - 1) / BN;
+  const int nb = (kend + BN - 1) / BN, jb0 = kstart / BN;
 
   const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
@@ -641,8 +665,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  if (nb > 0) issue(0);
-  for (int j = 0; j < nb; ++j) {
+  if (nb > jb0) issue(jb0);
+  for (int j = jb0; j < nb; ++j) {
     wait_all_loads();
     barrier();
     if (j + 1 < nb) issue(j + 1);
@@ -667,7 +691,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
     pipeline_reads<MT * (KS + VS), 1>();
     // S^T element i of tile mt is key j*BN + mt*32 + lh*4 + 8*(i/4) + i%4 of this lane's row
     float dS[MT * 16];
-    const bool full = (j + 1) * BN <= kfull;
+    const bool full = (j + 1) * BN <= kfull && j * BN >= klfull;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -675,7 +699,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
         float pr = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -l2));
         if (!full) {
           const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
-          pr = (kk <= row_lim) ? pr : 0.f;
+          pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
         }
         dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
       }

@@ -83,6 +83,7 @@ struct BwdParams {
   int64_t dq_sb, dq_sh, dq_st, dk_sb, dk_sh, dk_st, dv_sb, dv_sh, dv_st;
   int32_t B, H, Hkv, Tq, Tk, g;
   int32_t causal;
+  int32_t win_left, win_right;  // sliding window as in the forward (-1: unbounded side)
   float scale;
   float c;                // scale * log2(e)
 };

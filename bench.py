@@ -283,7 +283,7 @@ def bwd_flops(n: int) -> int:
     import synth
 
     s = synth.spec(n)
-    return 2 * visible_pairs(s.B, s.H, s.Tq, s.Tk, s.causal) * (3 * s.d_qk + 2 * s.d_v)
+    return 2 * visible_pairs(s.B, s.H, s.Tq, s.Tk, s.causal, s.window) * (3 * s.d_qk + 2 * s.d_v)
 
 
 def bwd_path_name(d_qk: int, d_v: int) -> str:
@@ -302,7 +302,7 @@ def measure_bwd(n: int, steps: int, warmup: int) -> dict:
     inp = synth.make(n)
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
     sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
-    out, lse = A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk)
+    out, lse = A.dense(q, k, v, causal=s.causal, scale=s.scale, sinks=sk, window=s.window)
     dout = synth.make_dout(s).cuda()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsk = torch.empty_like(sk) if sk is not None else None
@@ -312,7 +312,7 @@ def measure_bwd(n: int, steps: int, warmup: int) -> dict:
 
     def step():
         A.dense_backward(q, k, v, out, dout, lse, causal=s.causal, scale=s.scale, sinks=sk, dq=dq, dk=dk, dv=dv,
-                         dsinks=dsk, workspace=ws)
+                         dsinks=dsk, workspace=ws, window=s.window)
 
     path = bwd_path_name(s.d_qk, s.d_v)
     A.reset_dispatch_counts()
@@ -546,8 +546,8 @@ def main():
                                          "kernel_ms": round(rp["timing"]["kernel_ms_mean"], 5)}})
         del r, rp
         torch.cuda.empty_cache()
-        # the dense backward on the two prefill workloads it is compiled for
-        for m in (2, 3):
+        # the dense backward on the prefill workloads it is compiled for
+        for m in (2, 3, 7):
             next_rows.append(measure_bwd(m, st, wu))
             torch.cuda.empty_cache()
         # the sliding-window forward

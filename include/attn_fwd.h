@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -254,7 +254,8 @@ int32_t attn_splitkv_choose(const attn_dense_args* a);
  *   dv       [B, Hkv, Tk, d_v] written, strides dv_sb, dv_sh, dv_st
  *   dsinks   [H] float32 written, or NULL (not computed); must be NULL when
  *            sinks is NULL
- *   causal, scale, sizes: as in the forward; lse carries no gradient.
+ *   causal, scale, sizes, window_left, window_right: as in the forward (the
+ *            same values the forward ran with); lse carries no gradient.
  *
  * Gradients are accumulated in fp32 and rounded once to bf16 (dq, dk, dv).
  * No atomics: results are bitwise reproducible. Compiled head dims (d_qk,
@@ -285,6 +286,8 @@ typedef struct attn_dense_bwd_args {
   void* dv;
   int64_t dv_sb, dv_sh, dv_st;
   float* dsinks;
+  int32_t window_left;  /* -1: no left bound */
+  int32_t window_right; /* -1: no right bound */
 } attn_dense_bwd_args;
 
 /* Workspace bytes attn_bwd_dense needs: B*H*Tq*4 (the row dots

@@ -345,15 +345,17 @@ def sum_kv_groups(x: np.ndarray, g: int) -> np.ndarray:
     return y
 
 
-def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks=None):
+def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks=None,
+                             window: Tuple[int, int] = (-1, -1)):
     """Gradients of the dense forward in fp64: (dq, dk, dv, dsinks).
 
     ``dout`` = dL/dO [B,H,Tq,d_v] for a scalar loss L of the output; the lse
     output is a saved statistic and carries no gradient. dsinks is None when
     ``sinks`` is None. Steps, per (b, h), through the forward's definition:
 
-      1. Recompute the forward: S = scale * q . K_h^T (explicit, masked), the
-         row softmax P with the sink in the denominator, O = P . V_h.
+      1. Recompute the forward: S = scale * q . K_h^T (explicit, masked by the
+         causal bound and the sliding window as in the forward), the row
+         softmax P with the sink in the denominator, O = P . V_h.
       2. dV_h = P^T . dO                      (O is linear in V)
       3. dP = dO . V_h^T                      (O is linear in P)
       4. D = rowsum(dO * O)                   (= rowsum(P * dP))
@@ -385,6 +387,8 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
             S = scale * (q[b, h] @ K[b, h].T)
             if causal:
                 S = np.where(_causal_mask(ts, Tq, Tk), S, NEG_INF)
+            if window[0] >= 0 or window[1] >= 0:
+                S = np.where(_window_mask(ts, Tq, Tk, window[0], window[1]), S, NEG_INF)
             sink = None if sk is None else float(sk[h])
             P, lse = _softmax_rows(S, sink)
             O = P @ V[b, h]

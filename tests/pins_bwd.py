@@ -20,8 +20,8 @@ TOL = 1e-10      # exact comparisons (library autograd, closed forms, invariants
 TOL_FD = 1e-7    # central differences with h = 1e-5 in fp64
 
 
-def _loss(orc, q, k, v, sinks, G, scale, causal):
-    o, _ = orc.dense_attention(q, k, v, scale=scale, causal=causal, sinks=sinks)
+def _loss(orc, q, k, v, sinks, G, scale, causal, window=(-1, -1)):
+    o, _ = orc.dense_attention(q, k, v, scale=scale, causal=causal, sinks=sinks, window=window)
     return float((o * G).sum())
 
 
@@ -160,7 +160,26 @@ def check_bwd_masked_rows(orc=oracle):
     return max(_err(gq[:, :, :4], 0.0), _err(gk, gk2), _err(gv, gv2))
 
 
+def check_bwd_window_finite_differences(orc=oracle):
+    """Sliding windows: the gradients against central differences of the windowed forward."""
+    worst = 0.0
+    B, H, Hkv, Tq, Tk, dqk, dv = 1, 4, 2, 7, 9, 4, 3
+    q = _rand((B, H, Tq, dqk), 350, 0.8)
+    k = _rand((B, Hkv, Tk, dqk), 351, 0.8)
+    v = _rand((B, Hkv, Tk, dv), 352)
+    G = _rand((B, H, Tq, dv), 353)
+    sinks = _rand((H,), 354)
+    for causal, win in ((True, (2, -1)), (False, (1, 2)), (True, (0, -1))):
+        sk = sinks.copy()
+        gq, gk, gv, gs = orc.dense_attention_backward(q, k, v, G, scale=0.5, causal=causal, sinks=sk, window=win)
+        f = lambda: _loss(orc, q, k, v, sk, G, 0.5, causal, win)  # noqa: E731
+        worst = max(worst, _err(gq, _fd_grad(f, q)), _err(gk, _fd_grad(f, k)), _err(gv, _fd_grad(f, v)),
+                    _err(gs, _fd_grad(f, sk)))
+    return worst / TOL_FD * TOL
+
+
 ALL_CHECKS = {
+    "bwd_window_finite_differences": check_bwd_window_finite_differences,
     "bwd_finite_differences": check_bwd_finite_differences,
     "bwd_library_autograd": check_bwd_library_autograd,
     "bwd_invariants": check_bwd_invariants,

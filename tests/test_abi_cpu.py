@@ -212,6 +212,7 @@ def _fake_bwd(**over):
     a.dtype = A.ATTN_BF16
     a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = 1, 8, 2, 16, 16, 128, 128
     a.causal, a.scale = 1, 0.1
+    a.window_left = a.window_right = -1
     fake = 0x10000  # aligned, never dereferenced: validation fails first
     for n in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"):
         setattr(a, n, fake)

@@ -161,3 +161,36 @@ def test_bwd_full_workload_sampled_group(wl, group):
     errs = {"dq": _rel_err(_np(dq[b:b + 1, hs]), rq), "dk": _rel_err(_np(dk[b:b + 1, kvh:kvh + 1]), rk),
             "dv": _rel_err(_np(dv[b:b + 1, kvh:kvh + 1]), rv)}
     assert max(errs.values()) <= TOL_REL, f"{s.name} group {group}: {errs}"
+
+
+# ------------------------------------------------------------------ sliding windows
+WIN_CASES = [
+    # B, H, Hkv, Tq, Tk, d_qk, d_v, causal, sinks, window
+    (1, 8, 2, 300, 300, 128, 128, True, True, (50, -1)),
+    (1, 4, 2, 257, 257, 64, 64, False, False, (30, 90)),
+    (1, 4, 4, 200, 333, 192, 128, True, False, (100, -1)),
+    (2, 4, 1, 150, 150, 128, 128, True, False, (0, -1)),      # diagonal only
+    (1, 8, 2, 100, 400, 128, 128, False, True, (-1, 20)),
+]
+
+
+@pytest.mark.parametrize("case", WIN_CASES, ids=lambda c: f"T{c[3]}x{c[4]}d{c[5]}w{c[9][0]}_{c[9][1]}"
+                         f"{'c' if c[7] else 'n'}")
+def test_bwd_window(case):
+    B, H, Hkv, Tq, Tk, dqk, dv, causal, sinks, window = case
+    announce(f"bwd window {case}")
+    inp = synth.randn_dense(B, H, Hkv, Tq, Tk, dqk, dv, dtype="bf16", sinks=sinks, seed=Tq + 3 * Tk)
+    dout = synth.randn_dout(B, H, Tq, dv, seed=Tq + 3 * Tk)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    scale = 1 / math.sqrt(dqk)
+    out, lse = A.dense(q, k, v, causal=causal, scale=scale, sinks=sk, window=window)
+    dq, dk, dv_, ds = A.dense_backward(q, k, v, out, dout.cuda(), lse, causal=causal, scale=scale, sinks=sk,
+                                       window=window)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = oracle.dense_attention_backward(inp["q"], inp["k"], inp["v"], dout, scale=scale, causal=causal,
+                                                     sinks=inp["sinks"], window=window)
+    errs = {"dq": _rel_err(_np(dq), rq), "dk": _rel_err(_np(dk), rk), "dv": _rel_err(_np(dv_), rv)}
+    assert max(errs.values()) <= TOL_REL, f"{case}: {errs}"
+    if rs is not None:
+        assert _rel_err(_np(ds), rs) <= TOL_SINK
