@@ -298,6 +298,33 @@ def sparse_topk_attention(q, kv, idx, *, d_v: int, scale: float, sinks=None,
     return out, lse
 
 
+def dequantize_rows(raw, fmt: str) -> np.ndarray:
+    """Decode a quantized cache [..., row bytes] (uint8) into fp64 values [..., d].
+
+    The cache types the llama.cpp page names (q8_0 / q4_0 K/V, "Pins #303") are
+    ggml's block formats; the pages name them without spelling them out, so
+    this follows their public definition: blocks of 32 values, each an fp16
+    scale d then the codes. q8_0 (34 bytes): value i = d * int8 code i.
+    q4_0 (18 bytes): code i is the low nibble of byte i for i < 16 and the high
+    nibble of byte i - 16 otherwise, value = d * (code - 8).
+    """
+    a = np.asarray(raw.numpy() if hasattr(raw, "numpy") else raw, dtype=np.uint8)
+    bb = {"q8_0": 34, "q4_0": 18}[fmt]
+    lead, rb = a.shape[:-1], a.shape[-1]
+    assert rb % bb == 0
+    nb = rb // bb
+    blocks = a.reshape(-1, nb, bb)
+    d = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)  # [n, nb]
+    if fmt == "q8_0":
+        codes = blocks[..., 2:].view(np.int8).astype(np.float64)           # [n, nb, 32]
+    else:
+        bytes_ = blocks[..., 2:].astype(np.int64)                           # [n, nb, 16]
+        lo, hi = bytes_ & 0xF, bytes_ >> 4
+        codes = np.concatenate([lo, hi], axis=-1).astype(np.float64) - 8.0  # elements 0..15, 16..31
+    vals = d[..., None] * codes
+    return vals.reshape(*lead, nb * 32)
+
+
 def merge_partials(parts, sink: Optional[float] = None):
     """Merge (O_i, lse_i) computed over disjoint key sets into the full result.
 

@@ -153,6 +153,61 @@ def randn_dout(B, H, Tq, d_v, *, dtype="bf16", seed=0) -> torch.Tensor:
     return make_dout(DenseSpec("adhoc", seed, B, H, 1, Tq, 1, 1, d_v, dtype, True, False))
 
 
+# ---------------------------------------------------------------------------
+# Quantized K/V caches in llama.cpp's block formats (ggml's block_q8_0 and
+# block_q4_0): blocks of 32 consecutive values along the head dimension,
+# each stored as an fp16 scale followed by the codes. These functions only
+# produce cache bytes from seeded tensors (input generation); what the bytes
+# mean is decoded independently by the oracle and by the kernels.
+#   q8_0: 34 bytes = fp16 d, 32 x int8 q           (value = d * q)
+#   q4_0: 18 bytes = fp16 d, 16 bytes of nibbles   (byte i: element i in the
+#         low nibble, element i + 16 in the high nibble; value = d * (n - 8))
+# ---------------------------------------------------------------------------
+QK = 32
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18}
+
+
+def quantize_rows(x: torch.Tensor, fmt: str) -> torch.Tensor:
+    """x [..., d] float -> uint8 [..., d/32 * block bytes] in the given block format
+    (round-to-nearest codes; the scale is max|x| / 127 for q8_0 and -max/8 over the
+    signed maximum for q4_0, as llama.cpp's reference quantizers choose them)."""
+    a = x.detach().to(torch.float32).cpu().numpy()
+    lead, d = a.shape[:-1], a.shape[-1]
+    assert d % QK == 0
+    blk = a.reshape(-1, d // QK, QK)
+    n = blk.shape[0] * blk.shape[1]
+    flat = blk.reshape(n, QK)
+    out = np.zeros((n, BLOCK_BYTES[fmt]), dtype=np.uint8)
+    if fmt == "q8_0":
+        amax = np.abs(flat).max(axis=1)
+        dsc = (amax / 127.0).astype(np.float16)
+        inv = np.where(dsc.astype(np.float32) > 0, 1.0 / dsc.astype(np.float32), 0.0)
+        q = np.clip(np.rint(flat * inv[:, None]), -127, 127).astype(np.int8)
+        out[:, 0:2] = dsc.view(np.uint8).reshape(n, 2)
+        out[:, 2:] = q.view(np.uint8)
+    elif fmt == "q4_0":
+        idx = np.abs(flat).argmax(axis=1)
+        mx = flat[np.arange(n), idx]
+        dsc = (mx / -8.0).astype(np.float16)
+        inv = np.where(dsc.astype(np.float32) != 0, 1.0 / dsc.astype(np.float32), 0.0)
+        q = np.clip(np.floor(flat * inv[:, None] + 8.5), 0, 15).astype(np.uint8)
+        out[:, 0:2] = dsc.view(np.uint8).reshape(n, 2)
+        out[:, 2:] = q[:, :16] | (q[:, 16:] << 4)
+    else:
+        raise ValueError(fmt)
+    return torch.from_numpy(out.reshape(*lead, (d // QK) * BLOCK_BYTES[fmt]))
+
+
+def make_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, *, seed=0, sinks=False) -> dict:
+    """Seeded decode inputs with a quantized cache: q bf16 [B,H,Tq,d] and k, v as
+    uint8 [B,Hkv,Tk,row bytes] in ``fmt`` (the same recipe as the dense
+    workloads draws q, k, v, sinks in that order; k and v are then quantized)."""
+    s = DenseSpec("adhoc", seed, B, H, Hkv, Tq, Tk, d, d, "f32", True, sinks)
+    inp = make_dense(s)
+    return {"q": inp["q"].to(torch.bfloat16), "k": quantize_rows(inp["k"], fmt),
+            "v": quantize_rows(inp["v"], fmt), "sinks": inp["sinks"], "fmt": fmt}
+
+
 def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:
     """[Sq, topk] int32, each row topk distinct values of [0, N), unsorted."""
     rng = np.random.default_rng(seed)
