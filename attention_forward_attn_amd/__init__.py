@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -104,7 +104,27 @@ EXPORTS = (
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
+    "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes",
 )
+ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
+KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
+
+
+class AttnQkvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("kv_format", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_sb", ctypes.c_int64), ("k_sh", ctypes.c_int64), ("k_st", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_sb", ctypes.c_int64), ("v_sh", ctypes.c_int64), ("v_st", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_sb", ctypes.c_int64), ("o_sh", ctypes.c_int64), ("o_st", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+    ]
 
 _lib = None
 
@@ -147,6 +167,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_dense.restype = ctypes.c_int
     lib.attn_bwd_dense_workspace_bytes.argtypes = [ctypes.POINTER(AttnDenseBwdArgs)]
     lib.attn_bwd_dense_workspace_bytes.restype = ctypes.c_int64
+    lib.attn_fwd_dense_qkv.argtypes = [ctypes.POINTER(AttnQkvArgs), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p]
+    lib.attn_fwd_dense_qkv.restype = ctypes.c_int
+    lib.attn_qkv_workspace_bytes.argtypes = [ctypes.POINTER(AttnQkvArgs), ctypes.c_int32]
+    lib.attn_qkv_workspace_bytes.restype = ctypes.c_int64
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -511,3 +536,63 @@ def bwd_workspace_bytes(B, H, Hkv, Tq, Tk, d_qk, d_v) -> int:
     if n < 0:
         _check(ATTN_INVALID_ARGUMENT)
     return n
+
+
+def qkv_args(q, k, v, out, lse, *, fmt: str, causal: bool, scale: float, sinks=None) -> AttnQkvArgs:
+    """Fill the quantized-cache call's struct: q/out bf16 [B,H,T,d]; k, v uint8
+    [B,Hkv,Tk,row bytes] in llama.cpp's ``fmt`` ("q8_0" or "q4_0") blocks."""
+    import torch
+
+    B, H, Tq, d = q.shape
+    _, Hkv, Tk, _ = k.shape
+    if k.dtype != torch.uint8 or v.dtype != torch.uint8:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "k, v must be uint8 block data")
+    if fmt not in KV_FORMATS:
+        raise AttnUnsupported(ATTN_UNSUPPORTED, f"kv format {fmt!r}")
+    row_bytes = d // 32 * (34 if fmt == "q8_0" else 18)
+    if d % 32 != 0 or k.shape[-1] != row_bytes or v.shape[-1] != row_bytes:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"k, v rows must hold {row_bytes} bytes ({fmt}, d={d})")
+    a = AttnQkvArgs()
+    a.struct_size = ctypes.sizeof(AttnQkvArgs)
+    a.kv_format = KV_FORMATS[fmt]
+    a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d = B, H, Hkv, Tq, Tk, d
+    a.causal = 1 if causal else 0
+    a.scale = float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    a.q, (a.q_sb, a.q_sh, a.q_st) = q.data_ptr(), q.stride()[:3]
+    a.k, (a.k_sb, a.k_sh, a.k_st) = k.data_ptr(), k.stride()[:3]
+    a.v, (a.v_sb, a.v_sh, a.v_st) = v.data_ptr(), v.stride()[:3]
+    a.out, (a.o_sb, a.o_sh, a.o_st) = out.data_ptr(), out.stride()[:3]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    return a
+
+
+def dense_qkv(q, k, v, *, fmt: str, causal: bool = True, scale: Optional[float] = None, sinks=None,
+              n_splits: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Decode forward over a quantized K/V cache (q8_0 / q4_0 blocks, dequantized
+    tile by tile inside the kernel). Same results as :func:`dense` on the
+    decoded cache; returns (out bf16 [B,H,Tq,d], lse fp32 [B,H,Tq])."""
+    import torch
+
+    lib = load_library()
+    B, H, Tq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Tq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous():
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
+    a = qkv_args(q, k, v, out, lse, fmt=fmt, causal=causal, scale=scale, sinks=sinks)
+    need = int(lib.attn_qkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_fwd_dense_qkv(ctypes.byref(a), int(n_splits), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                  ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse

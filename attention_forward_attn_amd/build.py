@@ -34,7 +34,8 @@ COMMON = [
 
 
 def sources():
-    return [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_bwd.hip"), os.path.join(CSRC, "api.cpp")]
+    return [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_bwd.hip"),
+            os.path.join(CSRC, "attn_qkv.hip"), os.path.join(CSRC, "api.cpp")]
 
 
 def build(verbose: bool = False, resource_report: bool = False, defines=(), out: str = LIB) -> str:

@@ -47,9 +47,15 @@ constexpr const char* kMergePath = "splitkv_merge";
 // the dense backward paths have counters of their own, below the merge's
 constexpr const char* kBwdPaths[] = {"dense_bwd_bf16_d64", "dense_bwd_bf16_d128", "dense_bwd_bf16_d192_v128"};
 constexpr int kBwdSlot0 = kMergeSlot - 3;
+// and the quantized-cache decode paths below those
+constexpr const char* kQkvPaths[] = {"dense_qkv_q8_0_d128", "dense_qkv_q4_0_d128", "dense_qkv_q8_0_d256",
+                                     "dense_qkv_q4_0_d256"};
+constexpr int kQkvSlot0 = kBwdSlot0 - 4;
 
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
+  for (int i = 0; i < 4; ++i)
+    if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
     if (std::strcmp(path, kBwdPaths[i]) == 0) return kBwdSlot0 + i;
   int n = 0;
@@ -559,6 +565,148 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
     return fail(ATTN_HIP_ERROR, "launch of the dense backward failed: %s", hipGetErrorString((hipError_t)err));
   const int bp = bwd_path(a->d_qk, a->d_v);
   note_dispatch(kBwdSlot0 + bp, kBwdPaths[bp]);
+  return ATTN_OK;
+}
+
+// ---------------------------------------------------------------- quantized K/V decode
+namespace {
+
+int qkv_path(int fmt, int d) {
+  const int f = fmt == ATTN_KV_Q8_0 ? 0 : (fmt == ATTN_KV_Q4_0 ? 1 : -1);
+  if (f < 0 || d != 128) return -1;
+  return f;
+}
+
+attn_status validate_qkv_shape(const attn_qkv_args* a) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_qkv_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_qkv_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_qkv_args));
+  if (a->kv_format != ATTN_KV_Q8_0 && a->kv_format != ATTN_KV_Q4_0)
+    return fail(ATTN_UNSUPPORTED, "kv_format %d unsupported (q8_0 = 8, q4_0 = 2)", a->kv_format);
+  if (a->B < 1 || a->H < 1 || a->Hkv < 1) return fail(ATTN_INVALID_ARGUMENT, "B, H, Hkv must be >= 1");
+  if (a->Tq < 0 || a->Tk < 0) return fail(ATTN_INVALID_ARGUMENT, "Tq, Tk must be >= 0");
+  if (a->H % a->Hkv != 0) return fail(ATTN_INVALID_ARGUMENT, "H (%d) must be a multiple of Hkv (%d)", a->H, a->Hkv);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (qkv_path(a->kv_format, a->d) < 0) return fail(ATTN_UNSUPPORTED, "no compiled quantized-cache kernel for d = %d", a->d);
+  return ATTN_OK;
+}
+
+int64_t qkv_row_bytes(const attn_qkv_args* a) { return (int64_t)a->d / 32 * (a->kv_format == ATTN_KV_Q8_0 ? 34 : 18); }
+
+attn_status validate_qkv(const attn_qkv_args* a) {
+  const attn_status s = validate_qkv_shape(a);
+  if (s != ATTN_OK) return s;
+  if (a->Tq > 0 && (!a->q || !a->out || !a->lse)) return fail(ATTN_INVALID_ARGUMENT, "q, out, lse must be non-NULL");
+  if (a->Tk > 0 && (!a->k || !a->v)) return fail(ATTN_INVALID_ARGUMENT, "k, v must be non-NULL when Tk > 0");
+  if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->lse) || !aligned16(a->sinks))
+    return fail(ATTN_INVALID_ARGUMENT, "q, out, lse, sinks must be 16-byte aligned");
+  if (((uintptr_t)a->k | (uintptr_t)a->v) & 3u) return fail(ATTN_INVALID_ARGUMENT, "k, v must be 4-byte aligned");
+  const int64_t es[] = {a->q_sb, a->q_sh, a->q_st, a->o_sb, a->o_sh, a->o_st};
+  for (int64_t x : es)
+    if (x < 0 || x % 8 != 0) return fail(ATTN_INVALID_ARGUMENT, "q/out strides must be >= 0 multiples of 8 elements");
+  const int64_t bs[] = {a->k_sb, a->k_sh, a->k_st, a->v_sb, a->v_sh, a->v_st};
+  for (int64_t x : bs)
+    if (x < 0 || x % 4 != 0) return fail(ATTN_INVALID_ARGUMENT, "k/v byte strides must be >= 0 multiples of 4");
+  if (a->Tk > 1 && (a->k_st < qkv_row_bytes(a) || a->v_st < qkv_row_bytes(a)))
+    return fail(ATTN_INVALID_ARGUMENT, "k/v token stride smaller than a row (%lld bytes)", (long long)qkv_row_bytes(a));
+  if (a->Tq > 1 && (a->q_st < a->d || a->o_st < a->d))
+    return fail(ATTN_INVALID_ARGUMENT, "q/out token stride smaller than d");
+  return ATTN_OK;
+}
+
+struct QkvPlan {
+  int n, keys, n_rt;
+  int64_t bytes;
+};
+
+QkvPlan plan_qkv(const attn_qkv_args* a, int n_req) {
+  QkvPlan pl{1, a->Tk, (int)(((int64_t)(a->H / a->Hkv) * a->Tq + 31) / 32), 0};
+  const int nblocks = (a->Tk + 31) / 32;
+  if (nblocks <= 1 || a->Tq == 0) return pl;
+  int want = n_req;
+  if (want == 0) {
+    int occ = attn::occupancy_qkv(a->kv_format, a->d);
+    if (occ <= 0) occ = 4;
+    const int64_t tiles = (int64_t)pl.n_rt * a->B * a->Hkv;
+    want = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (int64_t)device_cus() * occ / tiles));
+  }
+  want = std::min(want, nblocks);
+  if (want <= 1) return pl;
+  const int per = (nblocks + want - 1) / want;
+  pl.keys = per * 32;
+  pl.n = (a->Tk + pl.keys - 1) / pl.keys;
+  if (pl.n <= 1) {
+    pl.n = 1;
+    pl.keys = a->Tk;
+    return pl;
+  }
+  pl.bytes = (int64_t)pl.n * a->B * a->H * a->Tq * ((int64_t)a->d + 1) * 4;
+  return pl;
+}
+
+}  // namespace
+
+int64_t attn_qkv_workspace_bytes(const attn_qkv_args* a, int32_t n_splits) {
+  g_last_error.clear();
+  if (validate_qkv_shape(a) != ATTN_OK) return -1;
+  if (n_splits < 0 || n_splits > kMaxSplits) {
+    fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+    return -1;
+  }
+  return plan_qkv(a, n_splits).bytes;
+}
+
+attn_status attn_fwd_dense_qkv(const attn_qkv_args* a, int32_t n_splits, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  g_last_error.clear();
+  attn_status s = validate_qkv(a);
+  if (s != ATTN_OK) return s;
+  if (n_splits < 0 || n_splits > kMaxSplits)
+    return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+  if (a->Tq == 0) return ATTN_OK;
+  const QkvPlan pl = plan_qkv(a, n_splits);
+  if (pl.n > 1) {
+    if (workspace == nullptr || workspace_bytes < pl.bytes)
+      return fail(ATTN_INVALID_ARGUMENT, "%d key ranges need a workspace of %lld bytes, got %lld", pl.n,
+                  (long long)pl.bytes, (long long)(workspace ? workspace_bytes : 0));
+    if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  attn::QkvParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = static_cast<const unsigned char*>(a->k); p.v = static_cast<const unsigned char*>(a->v);
+  p.out = a->out; p.lse = a->lse; p.sinks = a->sinks;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_st = a->q_st;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
+  p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_st = a->o_st;
+  p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
+  p.causal = a->causal;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  p.n_rt = pl.n_rt;
+  p.n_splits = pl.n;
+  p.split_keys = pl.keys;
+  if (pl.n > 1) {
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = p.part_o + (int64_t)pl.n * a->B * a->H * a->Tq * a->d;
+  }
+  int err = attn::launch_qkv(p, a->kv_format, a->d, stream);
+  if (err != 0)
+    return fail(ATTN_HIP_ERROR, "launch of the quantized-cache kernel failed: %s", hipGetErrorString((hipError_t)err));
+  const int qp = qkv_path(a->kv_format, a->d);
+  note_dispatch(kQkvSlot0 + qp, kQkvPaths[qp]);
+  if (pl.n > 1) {
+    attn::MergeParams m;
+    std::memset(&m, 0, sizeof(m));
+    m.part_o = p.part_o; m.part_lse = p.part_lse; m.sinks = a->sinks; m.out = a->out; m.lse = a->lse;
+    m.o_sb = a->o_sb; m.o_sh = a->o_sh; m.o_st = a->o_st;
+    m.B = a->B; m.H = a->H; m.Tq = a->Tq; m.d_v = a->d; m.n_splits = pl.n; m.f32 = 0;
+    err = attn::launch_merge(m, stream);
+    if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the split merge failed: %s", hipGetErrorString((hipError_t)err));
+    note_dispatch(kMergeSlot, kMergePath);
+  }
   return ATTN_OK;
 }
 

@@ -95,6 +95,35 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
 
+// Decode forward over a quantized K/V cache (q8_0 / q4_0 blocks, bf16 q and
+// out): the keys of one (b, kv head) and up to 32 folded query rows per
+// workgroup, key ranges on grid y as in split-KV.
+struct QkvParams {
+  const void* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  void* out;
+  float* lse;
+  const float* sinks;
+  int64_t q_sb, q_sh, q_st;  // elements
+  int64_t k_sb, k_sh, k_st;  // bytes
+  int64_t v_sb, v_sh, v_st;  // bytes
+  int64_t o_sb, o_sh, o_st;  // elements
+  int32_t B, H, Hkv, Tq, Tk, g;
+  int32_t causal;
+  float scale;
+  float c;                   // scale * log2(e)
+  int32_t n_rt;              // 32-row tiles per (b, kv head)
+  int32_t n_splits, split_keys;
+  float* part_o;             // [n_splits][B*H*Tq][d] when n_splits > 1
+  float* part_lse;
+};
+
+// 0 or the hipError_t of the launch; -1 when (format, d) is not compiled
+int launch_qkv(const QkvParams& p, int fmt, int d, void* stream);
+// workgroups of the (format, d) kernel resident on one CU (0: unknown)
+int occupancy_qkv(int fmt, int d);
+
 // Host-side launchers, one per compiled kernel configuration.
 // Return 0 on success, else the hipError_t of the launch.
 typedef int (*launch_fn)(const KernelParams& p, void* stream);

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -305,6 +305,62 @@ int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a);
  * Launches are recorded under the dispatch path "dense_bwd_bf16_d<d_qk>" (with
  * "_v<d_v>" when d_v differs). */
 attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Decode forward over a quantized K/V cache. llama.cpp's quantized-KV cache
+ * types q8_0 and q4_0 (the llama.cpp page, "Pins #303": the flash-attention
+ * kernel dequantizes q4_0 / q8_0 K/V tiles as it loads them, instead of
+ * converting the whole cache to f16 every step) are ggml's block formats:
+ * rows of d values in blocks of 32, each block an fp16 scale d followed by
+ *   ATTN_KV_Q8_0 (ggml type 8): 32 int8 codes q        value = d * q   (34 bytes)
+ *   ATTN_KV_Q4_0 (ggml type 2): 16 bytes, byte i holding code i in its low and
+ *                               code i + 16 in its high nibble, value = d * (code - 8)
+ *                                                                          (18 bytes)
+ * The type numbers are ggml's (the page's dispatch census names
+ * flash_attn_ext_f16 instances by (ggml_type)8 and (ggml_type)2).
+ *
+ *   q     [B, H, Tq, d] bf16, element strides q_sb, q_sh, q_st (16-byte rows);
+ *         values must lie in the fp16 range (the products run on f16 MFMA)
+ *   k, v  [B, Hkv, Tk, d/32 blocks] in kv_format, strides in BYTES (k_sb, k_sh,
+ *         k_st, ...; multiples of 4, token stride >= the row's bytes); base
+ *         pointers 4-byte aligned
+ *   out   [B, H, Tq, d] bf16 (written), lse [B, H, Tq] fp32 contiguous (written)
+ *   sinks [H] fp32 or NULL; causal bottom-right as in attn_dense_args.
+ *   Compiled: kv_format Q8_0 or Q4_0 (K and V alike), d = 128.
+ *
+ * Keys are cut into ranges as in attn_fwd_dense_splitkv (n_splits, 0 = the
+ * library's choice; workspace n * B*H*Tq * (d + 1) * 4 bytes from
+ * attn_qkv_workspace_bytes, NULL when one range is used) and merged. Errors as
+ * in the other calls, before any launch. Launches are recorded under
+ * "dense_qkv_q8_0_d128" / "dense_qkv_q4_0_d128" (and "splitkv_merge"); no
+ * conversion kernel exists.
+ */
+typedef enum attn_kv_format { ATTN_KV_Q4_0 = 2, ATTN_KV_Q8_0 = 8 } attn_kv_format;
+
+typedef struct attn_qkv_args {
+  uint32_t struct_size; /* = sizeof(attn_qkv_args) */
+  int32_t kv_format;    /* attn_kv_format of k and v */
+  int32_t B, H, Hkv, Tq, Tk, d;
+  int32_t causal;
+  float scale;
+  const void* q;
+  int64_t q_sb, q_sh, q_st; /* elements */
+  const void* k;
+  int64_t k_sb, k_sh, k_st; /* bytes */
+  const void* v;
+  int64_t v_sb, v_sh, v_st; /* bytes */
+  void* out;
+  int64_t o_sb, o_sh, o_st; /* elements */
+  float* lse;
+  const float* sinks;
+} attn_qkv_args;
+
+attn_status attn_fwd_dense_qkv(const attn_qkv_args* a, int32_t n_splits, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes of attn_fwd_dense_qkv for n_splits (0: the library's
+ * choice); 0 when one range suffices, -1 on invalid arguments. Host only. */
+int64_t attn_qkv_workspace_bytes(const attn_qkv_args* a, int32_t n_splits);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status s);

@@ -208,6 +208,13 @@ def make_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, *, seed=0, sinks=False) -> dict:
             "v": quantize_rows(inp["v"], fmt), "sinks": inp["sinks"], "fmt": fmt}
 
 
+# Multi-sequence decode over a q8_0 cache: 4 sequences decoding 4 tokens each
+# (the llama.cpp page's case: 3 to 16 tokens per ubatch over 4 streams, head
+# size 128), GQA 32/8 heads, a 16384-token cache; seed 8.
+QUANT_DECODE = {"name": "qdecode", "B": 4, "H": 32, "Hkv": 8, "Tq": 4, "Tk": 16384, "d": 128, "fmt": "q8_0",
+                "seed": 8}
+
+
 def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:
     """[Sq, topk] int32, each row topk distinct values of [0, N), unsorted."""
     rng = np.random.default_rng(seed)
