@@ -613,6 +613,8 @@ attn_status validate_qkv(const attn_qkv_args* a) {
     return fail(ATTN_INVALID_ARGUMENT, "k/v token stride smaller than a row (%lld bytes)", (long long)qkv_row_bytes(a));
   if (a->Tq > 1 && (a->q_st < a->d || a->o_st < a->d))
     return fail(ATTN_INVALID_ARGUMENT, "q/out token stride smaller than d");
+  if ((int64_t)a->Tk * std::max(a->k_st, a->v_st) >= ((int64_t)1 << 31))
+    return fail(ATTN_INVALID_ARGUMENT, "k/v of one head must span less than 2^31 bytes");
   return ATTN_OK;
 }
 

@@ -74,6 +74,26 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // wave's LDS operations then complete in order).
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+__device__ __forceinline__ uint32_t lds_u32(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 4 bytes per lane from global memory straight into LDS at m0 + 4 * lane
+// (wave-uniform base in scalar registers, per-lane 32-bit byte offset); the
+// compiler does not see these loads, so their waits are explicit
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // 16-byte chunk swizzle of a tile row with CPR chunks (64 LDS banks), as in
 // the bf16 kernels: 16 consecutive rows put one logical chunk in distinct bank
 // groups, aligned 4-row groups put a 4-chunk group in distinct groups.
@@ -117,31 +137,45 @@ __device__ __forceinline__ f16x8 tr_frag(const f16_t* tile, int r0, int c0, int 
 // Decode 8 consecutive values (elements w0..w0+7 of one block, w0 a multiple
 // of 8) of the raw block at byte `bb` of the LDS byte array `raw` into 4 words
 // of packed f16.
+//
+// Packed f16 arithmetic: a byte b (0..255) placed under the exponent bits
+// 0x64 is the f16 number 1024 + b exactly, so codes become f16 with one
+// byte permute and one OR per pair, the offset (1024 + 128 for int8 codes
+// stored with their sign bit flipped, 1024 + 8 for nibbles) goes with one
+// packed subtract, and the scale with one packed multiply (d * code rounded
+// once to f16, as a single f32 product rounded to f16 would be).
+typedef f16_t f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t scale_pair(uint32_t four_bytes_lo_hi, uint32_t sel, f16x2 offset, f16x2 d2) {
+  const uint32_t bits = __builtin_amdgcn_perm(0u, four_bytes_lo_hi, sel) | 0x64006400u;
+  const f16x2 v = (__builtin_bit_cast(f16x2, bits) - offset) * d2;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int FMT>
 __device__ __forceinline__ u32x4 decode8(const unsigned char* raw, int bb, int w0) {
-  const uint16_t dbits = *reinterpret_cast<const uint16_t*>(raw + bb);
-  const float d = (float)__builtin_bit_cast(f16_t, dbits);
-  float x[8];
+  const f16_t d = __builtin_bit_cast(f16_t, *reinterpret_cast<const uint16_t*>(raw + bb));
+  const f16x2 d2 = {d, d};
+  // the 8 code bytes (q8_0) or the 8 bytes holding the nibbles (q4_0), read as
+  // 2-byte halves (blocks are 2-byte aligned)
+  const uint16_t* cp = reinterpret_cast<const uint16_t*>(raw + bb + 2 + (FMT == kFmtQ8 ? w0 : (w0 & 15)));
+  uint32_t lo = (uint32_t)cp[0] | ((uint32_t)cp[1] << 16), hi = (uint32_t)cp[2] | ((uint32_t)cp[3] << 16);
+  f16x2 off;
   if constexpr (FMT == kFmtQ8) {
-    const uint16_t* cp = reinterpret_cast<const uint16_t*>(raw + bb + 2 + w0);  // 2-byte aligned
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t two = cp[i];
-      x[2 * i] = d * (float)(int)(int8_t)(two & 0xffu);
-      x[2 * i + 1] = d * (float)(int)(int8_t)(two >> 8);
-    }
+    lo ^= 0x80808080u;  // int8 q -> q + 128
+    hi ^= 0x80808080u;
+    off = f16x2{(f16_t)1152.f, (f16_t)1152.f};
   } else {
     // element e < 16: low nibble of byte e; element e >= 16: high nibble of byte e - 16
     const int sh = w0 >= 16 ? 4 : 0;
-    const uint16_t* cp = reinterpret_cast<const uint16_t*>(raw + bb + 2 + (w0 & 15));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t two = cp[i];
-      x[2 * i] = d * (float)((int)((two >> sh) & 0xfu) - 8);
-      x[2 * i + 1] = d * (float)((int)((two >> (8 + sh)) & 0xfu) - 8);
-    }
+    lo = (lo >> sh) & 0x0f0f0f0fu;
+    hi = (hi >> sh) & 0x0f0f0f0fu;
+    off = f16x2{(f16_t)1032.f, (f16_t)1032.f};
   }
-  return u32x4{pack_h2(x[0], x[1]), pack_h2(x[2], x[3]), pack_h2(x[4], x[5]), pack_h2(x[6], x[7])};
+  // byte k of the result pair: selector 0..3 picks byte k of the second
+  // operand, 0x0c gives 0
+  return u32x4{scale_pair(lo, 0x0c010c00u, off, d2), scale_pair(lo, 0x0c030c02u, off, d2),
+               scale_pair(hi, 0x0c010c00u, off, d2), scale_pair(hi, 0x0c030c02u, off, d2)};
 }
 
 template <int FMT, int D>
@@ -154,8 +188,9 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
   constexpr int CPR = D / 8, KS = D / 16, DT = D / 32;
   constexpr int CH_PL = BN * CPR / 64;            // decoded 8-value chunks per lane per tile
   static_assert(RB % 4 == 0 && RAW_DW % 64 == 0 && (BN * CPR) % 64 == 0, "tile shapes");
-  __shared__ __attribute__((aligned(16))) uint32_t rawk[RAW_DW];
-  __shared__ __attribute__((aligned(16))) uint32_t rawv[RAW_DW];
+  // raw tiles, two stages each (the next tile lands while this one is decoded)
+  __shared__ __attribute__((aligned(16))) uint32_t rawk[2][RAW_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t rawv[2][RAW_DW];
   __shared__ __attribute__((aligned(16))) f16_t kt[BN * D];
   __shared__ __attribute__((aligned(16))) f16_t vt[BN * D];
 
@@ -202,16 +237,33 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
 
   const unsigned char* kb = p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)k_lo * p.k_st;
   const unsigned char* vb = p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)k_lo * p.v_st;
-  uint32_t rk[RAW_PL], rv[RAW_PL];
   // raw dwords of tile j: dword w = i*64 + lane is byte 4w of the tile's
-  // rows laid end to end (row r = 4w / RB); rows past kend repeat row kend-1
+  // rows laid end to end (row r = 4w / RB); rows past kend repeat row kend-1.
+  // Byte offsets stay below 2^32: the host limits a range to 2^31 bytes.
+  const void* kbs = uniform_ptr(kb);
+  const void* vbs = uniform_ptr(vb);
+  // rows packed back to back (token stride == row bytes, the usual cache
+  // layout): a whole tile is one contiguous byte range, so every load is a
+  // scalar base plus the lane's fixed offset 4 * (64 i + lane)
+  const bool packed = p.k_st == RB && p.v_st == RB;
   auto load = [&](int j) {
+    const uint32_t lk = lds_u32(rawk[j & 1]), lv = lds_u32(rawv[j & 1]);
+    if (packed && (j + 1) * BN <= kend) {
+      const void* ks = uniform_ptr(kb + (int64_t)j * BN * RB);
+      const void* vs = uniform_ptr(vb + (int64_t)j * BN * RB);
+#pragma unroll
+      for (int i = 0; i < RAW_PL; ++i) {
+        dma4(ks, 4u * (uint32_t)(i * 64 + lane), lk + 256u * i);
+        dma4(vs, 4u * (uint32_t)(i * 64 + lane), lv + 256u * i);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RAW_PL; ++i) {
       const int w = i * 64 + lane, r = (4 * w) / RB, c = (4 * w) % RB;
       const int key = min(j * BN + r, kend - 1);
-      rk[i] = *reinterpret_cast<const uint32_t*>(kb + (int64_t)key * p.k_st + c);
-      rv[i] = *reinterpret_cast<const uint32_t*>(vb + (int64_t)key * p.v_st + c);
+      dma4(kbs, (uint32_t)(key * (uint32_t)p.k_st + c), lk + 256u * i);
+      dma4(vbs, (uint32_t)(key * (uint32_t)p.v_st + c), lv + 256u * i);
     }
   };
 
@@ -224,17 +276,13 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
 
   if (nb > 0) load(0);
   for (int j = 0; j < nb; ++j) {
-    lds_order();  // the previous tile's reads stay before these writes
-#pragma unroll
-    for (int i = 0; i < RAW_PL; ++i) {
-      rawk[i * 64 + lane] = rk[i];
-      rawv[i * 64 + lane] = rv[i];
-    }
-    lds_order();
+    // tile j has landed; every LDS read of the previous iteration has returned
+    // before the next tile's loads may overwrite the other stage
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     if (j + 1 < nb) load(j + 1);  // in flight while this tile is decoded and multiplied
     // decode: chunk c = (key r, 8 values from column 8 * (c % CPR))
-    const unsigned char* rkb = reinterpret_cast<const unsigned char*>(rawk);
-    const unsigned char* rvb = reinterpret_cast<const unsigned char*>(rawv);
+    const unsigned char* rkb = reinterpret_cast<const unsigned char*>(rawk[j & 1]);
+    const unsigned char* rvb = reinterpret_cast<const unsigned char*>(rawv[j & 1]);
 #pragma unroll
     for (int i = 0; i < CH_PL; ++i) {
       const int c = i * 64 + lane, r = c / CPR, kc = c % CPR;
@@ -259,15 +307,18 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+    // the running max moves only when a score exceeds it by more than 2^8
+    // (P <= 256 in f16 meanwhile), so the rescale of O is rare
     const float mnew = fmaxf(m_run, halves_max(mx));
-    if (mnew > m_run) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c);
+    const bool grow = (mnew - m_run) * p.c > 8.f;  // false when both are -inf
+    if (__any(grow)) {
+      const float alpha = grow ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c)) : 1.f;
+      if (grow) m_run = mnew;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-      m_run = mnew;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
     float P[16], rs = 0.f;

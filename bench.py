@@ -331,6 +331,55 @@ def measure_bwd(n: int, steps: int, warmup: int) -> dict:
             "roofline": rl, "verdict": "Measured"}
 
 
+def measure_qkv(fmt: str, steps: int, warmup: int) -> dict:
+    """Multi-sequence decode over a quantized cache (synth.QUANT_DECODE shape in
+    ``fmt``), memory bound: bytes = q + the cache's raw K/V bytes + out + lse. The
+    same shape over a bf16 cache (split-KV forward) is timed beside it."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = dict(synth.QUANT_DECODE, fmt=fmt)
+    inp = synth.make_quant_kv(s["B"], s["H"], s["Hkv"], s["Tq"], s["Tk"], s["d"], fmt, seed=s["seed"])
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    B, H, Tq, d = q.shape
+    out = torch.empty((B, H, Tq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device="cuda")
+    a = A.qkv_args(q, k, v, out, lse, fmt=fmt, causal=True, scale=1 / math.sqrt(d))
+    ws = torch.empty(max(16, int(A.load_library().attn_qkv_workspace_bytes(a, 0))), dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.dense_qkv(q, k, v, fmt=fmt, causal=True, out=out, lse=lse, workspace=ws)
+
+    path = f"dense_qkv_{fmt}_d{d}"
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != steps + warmup:
+        raise RuntimeError(f"NotEngaged: expected {steps + warmup} launches of {path}, saw {A.dispatch_count(path)}")
+    nbytes = (2 * B * H * Tq * d * 2 + k.numel() + v.numel() + 4 * B * H * Tq)
+    ach = nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+    rl = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    # the same decode over a bf16 cache, for context
+    g = torch.Generator("cpu").manual_seed(s["seed"])
+    kf = torch.randn((B, s["Hkv"], s["Tk"], d), generator=g).to(torch.bfloat16).cuda()
+    vf = torch.randn((B, s["Hkv"], s["Tk"], d), generator=g).to(torch.bfloat16).cuda()
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    ws2 = torch.empty(max(16, A.splitkv_workspace_bytes(B, H, s["Hkv"], Tq, s["Tk"], d, d)), dtype=torch.uint8,
+                      device="cuda")
+    t2 = time_steps(lambda: A.dense_splitkv(q, kf, vf, causal=True, out=out2, lse=lse2, workspace=ws2), steps, warmup)
+    log(f"[bench] qdecode {fmt}: B={B} H={H} Hkv={s['Hkv']} Tq={Tq} Tk={s['Tk']} d={d} | path {path} | "
+        f"{t['kernel_ms_mean']:.4f} ms | {rl['achieved']} GB/s = {100 * rl['frac']:.1f}% of peak | bf16 cache "
+        f"{t2['kernel_ms_mean']:.4f} ms")
+    return {"row": f"decode over a {fmt} K/V cache (attn_fwd_dense_qkv), in-kernel dequant",
+            "workload": f"qdecode: causal B={B} H={H} Hkv={s['Hkv']} Tq={Tq} Tk={s['Tk']} d={d} {fmt} K/V, bf16 q/out",
+            "path": path + " + splitkv_merge", "value": round(nbytes / (t["ms_per_step"] * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "bf16_cache": {"path": "dense_bf16_d128 split-KV", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -549,6 +598,10 @@ def main():
         # the dense backward on the prefill workloads it is compiled for
         for m in (2, 3, 7):
             next_rows.append(measure_bwd(m, st, wu))
+            torch.cuda.empty_cache()
+        # decode over quantized caches
+        for fmt in ("q8_0", "q4_0"):
+            next_rows.append(measure_qkv(fmt, st, wu))
             torch.cuda.empty_cache()
         # the sliding-window forward
         r = measure(7, st, wu)
