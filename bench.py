@@ -10,6 +10,10 @@ whole forward (fold, Q/K/V staging, QK^T, mask, online softmax, PV,
 epilogue). The primary line is the dense causal GQA prefill workload
 (B=2 H=32 Hkv=8 T=4096 d=128 bf16); the other workloads are measured in the
 same run and reported under "workloads" unless --primary-only is given.
+Rows beyond the five ("next_rows", skipped with --no-next-rows): split-KV
+decode (d512, beside the plain path), the dense backward on gqa / mla /
+swa1024 (algorithmic flops = five products per visible pair), decode over a
+q8_0 and a q4_0 cache (beside a bf16 cache), and the sliding-window forward.
 
 Prints ONE JSON line on stdout. Kernel durations come from HIP events
 recorded around each launch on the stream the kernel runs on; ms_per_step is
@@ -541,6 +545,8 @@ def main():
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA / copy ceilings")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the rows beyond the five workloads (split-KV decode, backward, quantized cache, window)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -583,7 +589,7 @@ def main():
     # rows beyond the five: the split-KV forward on a decode step (Tq = 1),
     # with the plain one-launch path on the same inputs for context
     next_rows = []
-    if not args.primary_only and n != 6:
+    if not args.primary_only and not args.no_next_rows and n != 6:
         st, wu = max(10, args.steps // 2), max(3, args.warmup // 2)
         r = measure(6, st, wu, split=True)
         rp = measure(6, st, wu, split=False)
