@@ -160,7 +160,16 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   // rows; otherwise the rows of several heads of one group share a tile
   // (the folded view), which is what makes small Tq (decode) efficient.
   const int64_t folded = (int64_t)p.g * a->Tq;
-  if (a->Tq >= BM) {
+  // bf16 kernels with several heads per kv head fold token-major (row
+  // t * g + head): the rows of a tile then span few tokens, so under a
+  // causal mask they share almost the same key range and only one key block
+  // per tile needs the per-score mask
+  p.fold_tm = (cfg->dtype == 0 && p.g > 1) ? 1 : 0;
+  if (p.fold_tm) {
+    p.aligned = 0;
+    p.tiles_per_head = 0;
+    p.tiles_per_group = (int)((folded + BM - 1) / BM);
+  } else if (a->Tq >= BM) {
     p.aligned = 1;
     p.tiles_per_head = (a->Tq + BM - 1) / BM;
     p.tiles_per_group = p.tiles_per_head * p.g;
@@ -175,14 +184,14 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
   // with its own L2. When the (batch, kv head) groups split evenly, every XCD
   // takes whole groups so that a group's K/V stays in one L2.
-  p.xcd_groups = (p.aligned && p.n_groups % 8 == 0) ? 1 : 0;
+  p.xcd_groups = ((p.aligned || p.fold_tm) && p.n_groups % 8 == 0) ? 1 : 0;
   if (p.xcd_groups) {
     // An XCD runs 32 workgroups at once (one per CU); it works through its
     // groups a chunk at a time, the chunk holding at least two rounds of its
     // CUs (so the longest-first order inside a chunk can balance them), so
     // that concurrent workgroups share their K/V in that XCD's L2.
     const int gpx = p.n_groups / 8;
-    const int per_group = p.g * p.tiles_per_head;
+    const int per_group = p.fold_tm ? p.tiles_per_group : p.g * p.tiles_per_head;
     const int want = (64 + per_group - 1) / per_group;
     int chunk = gpx;
     for (int c = 1; c <= gpx; ++c)

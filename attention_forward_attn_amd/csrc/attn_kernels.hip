@@ -836,7 +836,27 @@ attn_fwd_dma_kernel(const KernelParams p) {
     nrows = p.H;
   } else {
     const int tile = blockIdx.x;
-    if (p.aligned) {
+    if (p.fold_tm) {
+      // token-major fold: tile tb of a group holds folded rows
+      // [tb*BM, tb*BM + BM), row f = token f / g of head f % g
+      int tb, grp;
+      if (p.xcd_groups) {
+        const int x = tile & 7, i = tile >> 3;
+        const int per_chunk = p.xcd_chunk * p.tiles_per_group;
+        const int c = i / per_chunk, r = i % per_chunk;
+        tb = (p.tiles_per_group - 1) - r / p.xcd_chunk;  // longest causal tiles first
+        grp = (c * p.xcd_chunk + r % p.xcd_chunk) * 8 + x;
+      } else {
+        tb = (p.tiles_per_group - 1) - tile / p.n_groups;
+        grp = tile % p.n_groups;
+      }
+      b = grp / p.Hkv;
+      kvh = grp % p.Hkv;
+      f0 = tb * C::BM;
+      nrows = min(C::BM, p.g * p.Tq - f0);
+      t_lo = f0 / p.g;
+      t_hi = (f0 + nrows - 1) / p.g;
+    } else if (p.aligned) {
       int tb, grp, hl;
       if (p.xcd_groups) {
         // XCD x (= tile % 8) owns groups x, x+8, ...; it takes them xcd_chunk
@@ -923,8 +943,8 @@ attn_fwd_dma_kernel(const KernelParams p) {
     l_off = (int64_t)sq * p.H + rr;
   } else {
     const int f = f0 + rr;
-    row_h = kvh * p.g + f / p.Tq;
-    const int t = f % p.Tq;
+    row_h = kvh * p.g + (p.fold_tm ? f % p.g : f / p.Tq);
+    const int t = p.fold_tm ? f / p.g : f % p.Tq;
     row_lim = up >= 0 ? min(p.Tk - 1, t + off + up) : p.Tk - 1;
     row_lim = min(row_lim - k_lo, kend - 1);  // relative to the range
     if (p.win_left >= 0) row_lo = t + off - p.win_left - k_lo;

@@ -30,6 +30,7 @@ struct KernelParams {
 
   // workgroup -> tile decode (dense)
   int32_t aligned;        // 1: tiles never straddle heads (tiles_per_head per head)
+  int32_t fold_tm;        // 1 (bf16 kernels, g > 1): token-major fold, row f = t * g + head
   int32_t block_rows;     // folded rows per workgroup
   int32_t tiles_per_head; // aligned mode
   int32_t tiles_per_group;// tiles per (b, kv head)
