@@ -212,6 +212,37 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
     return out, lse
 
 
+def dense_attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool, sinks=None,
+                           window: Tuple[int, int] = (-1, -1)):
+    """Packed variable-length batch: sequence b owns query tokens
+    [cu_q[b], cu_q[b+1]) of q [total_q, H, d_qk] and key tokens
+    [cu_k[b], cu_k[b+1]) of k, v [total_k, Hkv, d]. Each sequence is an
+    independent dense attention (its own bottom-right causal alignment,
+    window and sinks); no token attends across a sequence boundary. The
+    ArcFlash page ("What this does NOT do") lists a varlen path that silently
+    dropped the causal mask as a defect; here the mask applies per sequence.
+    Returns (out [total_q, H, d_v], lse [H, total_q]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu_q = [int(x) for x in np.asarray(cu_q)]
+    cu_k = [int(x) for x in np.asarray(cu_k)]
+    total_q, H, _ = q.shape
+    Dv = v.shape[-1]
+    out = np.zeros((total_q, H, Dv))
+    lse = np.full((H, total_q), NEG_INF)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if qe <= qs:
+            continue
+        qb = q[qs:qe].transpose(1, 0, 2)[None]            # [1, H, Tq_b, d]
+        kb = k[ks:ke].transpose(1, 0, 2)[None]
+        vb = v[ks:ke].transpose(1, 0, 2)[None]
+        o, l = dense_attention(qb, kb, vb, scale=scale, causal=causal, sinks=sinks, window=window)
+        out[qs:qe] = o[0].transpose(1, 0, 2)
+        lse[:, qs:qe] = l[0]
+    return out, lse
+
+
 def tile_rows_for_budget(tile_bytes: int, Tk: int, elt_bytes: int) -> int:
     """Folded query rows per tile so that one tile's [rows, Tk] scores fit the budget.
 

@@ -182,6 +182,44 @@ def check_window(orc=oracle):
     return worst
 
 
+def check_varlen(orc=oracle):
+    """Packed sequences: equal lengths give the padded batch exactly; ragged lengths
+    (including an empty sequence and Tq != Tk) match brute force per sequence; and a
+    sequence's output ignores every other sequence's keys."""
+    worst = 0.0
+    B, H, Hkv, T, d = 3, 4, 2, 6, 5
+    q, k, v = _rand((B, H, T, d), 900), _rand((B, Hkv, T, d), 901), _rand((B, Hkv, T, 3), 902)
+    sinks = _rand((H,), 903)
+    cu = np.arange(B + 1) * T
+    pack = lambda x: np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(-1, x.shape[1], x.shape[3]))  # noqa: E731
+    for causal in (False, True):
+        o, l = orc.dense_attention(q, k, v, scale=0.4, causal=causal, sinks=sinks)
+        ov, lv = orc.dense_attention_varlen(pack(q), pack(k), pack(v), cu, cu, scale=0.4, causal=causal, sinks=sinks)
+        worst = max(worst, _err(ov, pack(o)), _err(lv, l.transpose(1, 0, 2).reshape(H, -1)))
+    lq, lk = [3, 0, 7, 1], [5, 2, 4, 1]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = _rand((cq[-1], H, d), 904)
+    k, v = _rand((ck[-1], Hkv, d), 905), _rand((ck[-1], Hkv, 3), 906)
+    for causal in (False, True):
+        for win in ((-1, -1), (1, -1)):
+            ov, lv = orc.dense_attention_varlen(q, k, v, cq, ck, scale=0.4, causal=causal, sinks=sinks, window=win)
+            for b in range(len(lq)):
+                if lq[b] == 0:
+                    continue
+                qb = q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]
+                kb = k[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+                vb = v[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+                bo, bl = brute_dense(qb, kb, vb, 0.4, causal, sinks, window=win)
+                worst = max(worst, _err(ov[cq[b]:cq[b + 1]], np.asarray(bo)[0].transpose(1, 0, 2)),
+                            _err(lv[:, cq[b]:cq[b + 1]], np.asarray(bl)[0]))
+            # isolation: scrambling sequence 3's keys leaves the others unchanged
+            k2 = k.copy()
+            k2[ck[3]:ck[4]] += 10.0
+            ov2, lv2 = orc.dense_attention_varlen(q, k2, v, cq, ck, scale=0.4, causal=causal, sinks=sinks, window=win)
+            worst = max(worst, _err(ov2[:cq[3]], ov[:cq[3]]), _err(lv2[:, :cq[3]], lv[:, :cq[3]]))
+    return worst
+
+
 def check_causal_differs(orc=oracle):
     """Causal must not silently equal full attention (returns 0 when it differs)."""
     q, k, v = _rand((1, 2, 8, 4), 11), _rand((1, 1, 8, 4), 12), _rand((1, 1, 8, 4), 13)
@@ -335,6 +373,7 @@ def check_lse_logsumexp(orc=oracle):
 
 ALL_CHECKS = {
     "window": check_window,
+    "varlen": check_varlen,
     "brute_dense": check_brute_dense,
     "brute_sparse": check_brute_sparse,
     "library_dense": check_library_dense,

@@ -90,3 +90,14 @@ def test_window_rewrites_causal_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "dense_attention", clamp)
     _assert_caught(_caught(["window"]))
+
+
+def test_varlen_mask_dropped_caught(monkeypatch):
+    """The varlen defect the ArcFlash page names: causal silently off for packed sequences."""
+    orig = OA.dense_attention_varlen
+
+    def non_causal(q, k, v, cu_q, cu_k, *, causal, **kw):
+        return orig(q, k, v, cu_q, cu_k, causal=False, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention_varlen", non_causal)
+    _assert_caught(_caught(["varlen"]))
