@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -104,10 +104,31 @@ EXPORTS = (
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
-    "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes",
+    "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen",
 )
 ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
 KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
+
+
+class AttnVarlenArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_st", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_st", ctypes.c_int64), ("k_sh", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_st", ctypes.c_int64), ("v_sh", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_st", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+    ]
 
 
 class AttnQkvArgs(ctypes.Structure):
@@ -172,6 +193,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_dense_qkv.restype = ctypes.c_int
     lib.attn_qkv_workspace_bytes.argtypes = [ctypes.POINTER(AttnQkvArgs), ctypes.c_int32]
     lib.attn_qkv_workspace_bytes.restype = ctypes.c_int64
+    lib.attn_fwd_varlen.argtypes = [ctypes.POINTER(AttnVarlenArgs), ctypes.c_void_p]
+    lib.attn_fwd_varlen.restype = ctypes.c_int
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -595,4 +618,53 @@ def dense_qkv(q, k, v, *, fmt: str, causal: bool = True, scale: Optional[float] 
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.attn_fwd_dense_qkv(ctypes.byref(a), int(n_splits), ctypes.c_void_p(ws_ptr), ws_bytes,
                                   ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+def dense_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *, causal: bool = True,
+                 scale: Optional[float] = None, sinks=None, window: Tuple[int, int] = (-1, -1), out=None, lse=None,
+                 stream=None):
+    """Packed variable-length forward (bf16): q [total_q, H, d_qk], k, v [total_k, Hkv, d],
+    cu_seqlens_* int32 device tensors [B + 1]. Returns (out [total_q, H, d_v], lse [H, total_q])."""
+    import torch
+
+    lib = load_library()
+    total_q, H, dqk = q.shape
+    total_k, Hkv, _ = k.shape
+    dv = v.shape[-1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must have the same length")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name} must be a contiguous int32 tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        out = torch.empty((total_q, H, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    if v.shape[:2] != k.shape[:2] or tuple(out.shape) != (total_q, H, dv) or out.dtype != q.dtype:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "v must be [total_k, Hkv, d_v] and out [total_q, H, d_v]")
+    if tuple(lse.shape) != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be a contiguous fp32 [H, total_q] tensor")
+    a = AttnVarlenArgs()
+    a.struct_size = ctypes.sizeof(AttnVarlenArgs)
+    a.dtype = _dtype_code(q)
+    a.B, a.H, a.Hkv, a.max_seqlen_q, a.total_q, a.total_k, a.d_qk, a.d_v = (B, H, Hkv, int(max_seqlen_q), total_q,
+                                                                           total_k, dqk, dv)
+    a.causal = 1 if causal else 0
+    a.scale = float(scale)
+    a.q, (a.q_st, a.q_sh) = q.data_ptr(), q.stride()[:2]
+    a.k, (a.k_st, a.k_sh) = k.data_ptr(), k.stride()[:2]
+    a.v, (a.v_st, a.v_sh) = v.data_ptr(), v.stride()[:2]
+    a.out, (a.o_st, a.o_sh) = out.data_ptr(), out.stride()[:2]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.cu_seqlens_q, a.cu_seqlens_k = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    a.window_left, a.window_right = int(window[0]), int(window[1])
+    _check(lib.attn_fwd_varlen(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse

@@ -97,6 +97,29 @@ struct DensePlan {
   attn::KernelParams kp;
 };
 
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
+// with its own L2. When the (batch, kv head) groups split evenly, every XCD
+// takes whole groups so that a group's K/V stays in one L2. An XCD runs 32
+// workgroups at once (one per CU); it works through its groups a chunk at a
+// time, the chunk holding at least two rounds of its CUs (so the
+// longest-first order inside a chunk can balance them), so that concurrent
+// workgroups share their K/V in that XCD's L2.
+void plan_xcd(attn::KernelParams& p) {
+  p.xcd_groups = ((p.aligned || p.fold_tm) && p.n_groups % 8 == 0) ? 1 : 0;
+  p.xcd_chunk = 0;
+  if (!p.xcd_groups) return;
+  const int gpx = p.n_groups / 8;
+  const int per_group = p.fold_tm ? p.tiles_per_group : p.g * p.tiles_per_head;
+  const int want = (64 + per_group - 1) / per_group;
+  int chunk = gpx;
+  for (int c = 1; c <= gpx; ++c)
+    if (gpx % c == 0 && c >= want) {
+      chunk = c;
+      break;
+    }
+  p.xcd_chunk = chunk;
+}
+
 attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
   if (a->struct_size != sizeof(attn_dense_args))
@@ -181,28 +204,7 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
   if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   p.n_tiles = (int)tiles;
-  // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
-  // with its own L2. When the (batch, kv head) groups split evenly, every XCD
-  // takes whole groups so that a group's K/V stays in one L2.
-  p.xcd_groups = ((p.aligned || p.fold_tm) && p.n_groups % 8 == 0) ? 1 : 0;
-  if (p.xcd_groups) {
-    // An XCD runs 32 workgroups at once (one per CU); it works through its
-    // groups a chunk at a time, the chunk holding at least two rounds of its
-    // CUs (so the longest-first order inside a chunk can balance them), so
-    // that concurrent workgroups share their K/V in that XCD's L2.
-    const int gpx = p.n_groups / 8;
-    const int per_group = p.fold_tm ? p.tiles_per_group : p.g * p.tiles_per_head;
-    const int want = (64 + per_group - 1) / per_group;
-    int chunk = gpx;
-    for (int c = 1; c <= gpx; ++c)
-      if (gpx % c == 0 && c >= want) {
-        chunk = c;
-        break;
-      }
-    p.xcd_chunk = chunk;
-  } else {
-    p.xcd_chunk = 0;
-  }
+  plan_xcd(p);
   return ATTN_OK;
 }
 
@@ -719,6 +721,58 @@ attn_status attn_fwd_dense_qkv(const attn_qkv_args* a, int32_t n_splits, void* w
     note_dispatch(kMergeSlot, kMergePath);
   }
   return ATTN_OK;
+}
+
+// ---------------------------------------------------------------- packed variable-length batches
+attn_status attn_fwd_varlen(const attn_varlen_args* a, void* stream) {
+  g_last_error.clear();
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_varlen_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_varlen_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_varlen_args));
+  if (a->dtype != ATTN_BF16) return fail(ATTN_UNSUPPORTED, "packed batches are compiled for bf16 only");
+  if (a->B < 1 || a->max_seqlen_q < 0 || a->total_q < 0 || a->total_k < 0)
+    return fail(ATTN_INVALID_ARGUMENT, "B >= 1 and max_seqlen_q, total_q, total_k >= 0 required");
+  if (a->total_q > 0 && (!a->cu_seqlens_q || !a->cu_seqlens_k))
+    return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (((uintptr_t)a->cu_seqlens_q | (uintptr_t)a->cu_seqlens_k) & 3u)
+    return fail(ATTN_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  // the dense validation on an equivalent strided view: B sequences of
+  // max_seqlen_q queries (batch strides 0) and up to total_k keys
+  attn_dense_args d;
+  std::memset(&d, 0, sizeof(d));
+  d.struct_size = sizeof(d);
+  d.dtype = a->dtype;
+  d.B = a->B; d.H = a->H; d.Hkv = a->Hkv; d.Tq = a->max_seqlen_q; d.Tk = a->total_k;
+  d.d_qk = a->d_qk; d.d_v = a->d_v; d.causal = a->causal; d.scale = a->scale;
+  d.q = a->q; d.q_sb = 0; d.q_sh = a->q_sh; d.q_st = a->q_st;
+  d.k = a->k; d.k_sb = 0; d.k_sh = a->k_sh; d.k_st = a->k_st;
+  d.v = a->v; d.v_sb = 0; d.v_sh = a->v_sh; d.v_st = a->v_st;
+  d.out = a->out; d.o_sb = 0; d.o_sh = a->o_sh; d.o_st = a->o_st;
+  d.lse = a->lse; d.sinks = a->sinks;
+  d.window_left = a->window_left; d.window_right = a->window_right;
+  DensePlan dp;
+  attn_status s = validate_dense(&d, &dp);
+  if (s != ATTN_OK) return s;
+  if (dp.cfg->dtype != 0 || a->d_qk > 256)
+    return fail(ATTN_UNSUPPORTED, "no packed-batch kernel for these head dims (bf16, d_qk <= 256)");
+  if (a->total_q == 0 || a->max_seqlen_q == 0) return ATTN_OK;
+  attn::KernelParams& p = dp.kp;
+  const int BM = dp.cfg->block_rows;
+  p.varlen = 1;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.total_q = a->total_q;
+  p.total_k = a->total_k;
+  p.fold_tm = 1;
+  p.aligned = 0;
+  p.tiles_per_head = 0;
+  p.tiles_per_group = (int)(((int64_t)p.g * a->max_seqlen_q + BM - 1) / BM);
+  const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
+  if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
+  p.n_tiles = (int)tiles;
+  plan_xcd(p);
+  return do_launch(dp, stream);
 }
 
 uint64_t attn_dispatch_count(const char* path) {

@@ -831,6 +831,13 @@ attn_fwd_dma_kernel(const KernelParams p) {
 
   // ---------------------------------------------------------------- tile of this workgroup
   int b = 0, kvh = 0, f0 = 0, nrows = 0, t_lo = 0, t_hi = 0, sq = 0;
+  // query / key counts of this workgroup's sequence, and (packed batches) the
+  // sequence's first query and key token
+  int Tq = p.Tq, Tk = p.Tk;
+  int64_t qtok0 = 0, ktok0 = 0;
+  // packed batches are compiled into the kernels up to 256-wide heads; the
+  // 512-wide kernel runs at its register limit and is left without the branch
+  constexpr bool kPacked = !SPARSE && DQK <= 256;
   if constexpr (SPARSE) {
     sq = blockIdx.x;
     nrows = p.H;
@@ -853,7 +860,19 @@ attn_fwd_dma_kernel(const KernelParams p) {
       b = grp / p.Hkv;
       kvh = grp % p.Hkv;
       f0 = tb * C::BM;
-      nrows = min(C::BM, p.g * p.Tq - f0);
+      if (kPacked && p.varlen) {
+        // packed batch: the tiles cover the longest sequence's rows; a tile
+        // past its own sequence's rows has nothing to do (every thread
+        // leaves here)
+        const int qs = min(max(p.cu_q[b], 0), p.total_q), qe = min(max(p.cu_q[b + 1], qs), p.total_q);
+        const int ks = min(max(p.cu_k[b], 0), p.total_k), ke = min(max(p.cu_k[b + 1], ks), p.total_k);
+        Tq = qe - qs;
+        Tk = ke - ks;
+        qtok0 = qs;
+        ktok0 = ks;
+        if (f0 >= p.g * Tq) return;
+      }
+      nrows = min(C::BM, p.g * Tq - f0);
       t_lo = f0 / p.g;
       t_hi = (f0 + nrows - 1) / p.g;
     } else if (p.aligned) {
@@ -903,24 +922,24 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // kfull; with a sliding window, none masks a key from klfull on and no row
   // sees a key before kstart. `up` = keys after a row's diagonal position it
   // may see (-1: unbounded); the window never widens the causal bound.
-  int kend = p.Tk, kfull = p.Tk, kstart = 0, klfull = 0;
-  const int off = p.Tk - p.Tq;
+  int kend = Tk, kfull = Tk, kstart = 0, klfull = 0;
+  const int off = Tk - Tq;
   const int up = p.causal ? 0 : p.win_right;
   if (!SPARSE && up >= 0) {
-    kend = min(p.Tk, max(0, t_hi + off + up + 1));
-    kfull = min(p.Tk, max(0, t_lo + off + up + 1));
+    kend = min(Tk, max(0, t_hi + off + up + 1));
+    kfull = min(Tk, max(0, t_lo + off + up + 1));
   }
   if (!SPARSE && p.win_left >= 0) {
-    kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
-    klfull = min(p.Tk, max(0, t_hi + off - p.win_left));
+    kstart = min(Tk, max(0, t_lo + off - p.win_left));
+    klfull = min(Tk, max(0, t_hi + off - p.win_left));
   }
   // this workgroup sees keys [k_lo, k_hi) only (split-KV: one range; sliding
   // window: from the block holding kstart); from here on key positions
   // (kend, kfull, klfull, the row limits, the K/V bases) are relative to k_lo
-  int k_lo = 0, k_hi = p.Tk;
+  int k_lo = 0, k_hi = Tk;
   if (!SPARSE && p.n_splits > 1) {
     k_lo = blockIdx.y * p.split_keys;
-    k_hi = min(p.Tk, k_lo + p.split_keys);
+    k_hi = min(Tk, k_lo + p.split_keys);
   }
   if (!SPARSE) {
     k_lo = max(k_lo, (kstart / BN) * BN);
@@ -937,20 +956,20 @@ attn_fwd_dma_kernel(const KernelParams p) {
   int64_t q_off, o_off, l_off;
   if constexpr (SPARSE) {
     row_h = rr;
-    row_lim = p.Tk - 1;
+    row_lim = Tk - 1;
     q_off = (int64_t)sq * p.q_sb + (int64_t)rr * p.q_sh;
     o_off = (int64_t)sq * p.o_sb + (int64_t)rr * p.o_sh;
     l_off = (int64_t)sq * p.H + rr;
   } else {
     const int f = f0 + rr;
-    row_h = kvh * p.g + (p.fold_tm ? f % p.g : f / p.Tq);
-    const int t = p.fold_tm ? f / p.g : f % p.Tq;
-    row_lim = up >= 0 ? min(p.Tk - 1, t + off + up) : p.Tk - 1;
+    row_h = kvh * p.g + (p.fold_tm ? f % p.g : f / Tq);
+    const int t = p.fold_tm ? f / p.g : f % Tq;
+    row_lim = up >= 0 ? min(Tk - 1, t + off + up) : Tk - 1;
     row_lim = min(row_lim - k_lo, kend - 1);  // relative to the range
     if (p.win_left >= 0) row_lo = t + off - p.win_left - k_lo;
-    q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (int64_t)t * p.q_st;
-    o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (int64_t)t * p.o_st;
-    l_off = ((int64_t)b * p.H + row_h) * p.Tq + t;
+    q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (qtok0 + t) * p.q_st;
+    o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (qtok0 + t) * p.o_st;
+    l_off = kPacked && p.varlen ? (int64_t)row_h * p.total_q + qtok0 + t : ((int64_t)b * p.H + row_h) * Tq + t;
   }
 
   // ---------------------------------------------------------------- Q fragments (B operand of S^T)
@@ -976,8 +995,8 @@ attn_fwd_dma_kernel(const KernelParams p) {
     kbase = reinterpret_cast<const bf16_t*>(p.k);
     vbase = kbase;
   } else {
-    kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)k_lo * p.k_st;
-    vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + (int64_t)k_lo * p.v_st;
+    kbase = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (ktok0 + k_lo) * p.k_st;
+    vbase = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh + (ktok0 + k_lo) * p.v_st;
   }
 
   // ---------------------------------------------------------------- loads of one key block

@@ -31,6 +31,15 @@ struct KernelParams {
   // workgroup -> tile decode (dense)
   int32_t aligned;        // 1: tiles never straddle heads (tiles_per_head per head)
   int32_t fold_tm;        // 1 (bf16 kernels, g > 1): token-major fold, row f = t * g + head
+
+  // packed variable-length batch (bf16 kernels): sequence b holds query
+  // tokens [cu_q[b], cu_q[b+1]) and key tokens [cu_k[b], cu_k[b+1]) (device
+  // arrays, clamped to the totals); Tq / Tk above are the maxima, the batch
+  // strides are 0 and lse is [H, total_q]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t varlen;
+  int32_t total_q, total_k;
   int32_t block_rows;     // folded rows per workgroup
   int32_t tiles_per_head; // aligned mode
   int32_t tiles_per_group;// tiles per (b, kv head)

@@ -13,7 +13,8 @@ same run and reported under "workloads" unless --primary-only is given.
 Rows beyond the five ("next_rows", skipped with --no-next-rows): split-KV
 decode (d512, beside the plain path), the dense backward on gqa / mla /
 swa1024 (algorithmic flops = five products per visible pair), decode over a
-q8_0 and a q4_0 cache (beside a bf16 cache), and the sliding-window forward.
+q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
+forward (beside the padded batch) and the sliding-window forward.
 
 Prints ONE JSON line on stdout. Kernel durations come from HIP events
 recorded around each launch on the stream the kernel runs on; ms_per_step is
@@ -384,6 +385,67 @@ def measure_qkv(fmt: str, steps: int, warmup: int) -> dict:
             "bf16_cache": {"path": "dense_bf16_d128 split-KV", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
 
 
+def measure_varlen(steps: int, warmup: int) -> dict:
+    """The packed variable-length forward on synth.VARLEN_PREFILL (the gqa layer over
+    sequences of mixed lengths); flops = 2 * (visible pairs summed over the sequences)
+    * (d_qk + d_v). The padded batch (every sequence at the longest length, one dense
+    call) is timed beside it."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.VARLEN_PREFILL
+    inp = synth.make_varlen(s)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    cu = torch.from_numpy(inp["cu"]).cuda()
+    lens = [int(x) for x in inp["lens"]]
+    H, Hkv, d = s["H"], s["Hkv"], s["d"]
+    scale = 1 / math.sqrt(d)
+    out = torch.empty((q.shape[0], H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, q.shape[0]), dtype=torch.float32, device="cuda")
+    mx = max(lens)
+
+    def step():
+        A.dense_varlen(q, k, v, cu, cu, mx, causal=True, scale=scale, out=out, lse=lse)
+
+    path = f"dense_bf16_d{d}"
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != steps + warmup:
+        raise RuntimeError(f"NotEngaged: expected {steps + warmup} launches of {path}, saw {A.dispatch_count(path)}")
+    fl = sum(2 * visible_pairs(1, H, L, L, True) * 2 * d for L in lens)
+    ach = fl / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    # the padded batch: [n, H, max, d], each sequence's rows first and N(0,1) padding
+    # after them (MFMA timing depends on the data, so no zero padding), one dense call
+    n = len(lens)
+    gp = torch.Generator("cpu").manual_seed(s["seed"] + 1)
+    pq = torch.randn((n, H, mx, d), generator=gp).to(torch.bfloat16)
+    pk = torch.randn((n, Hkv, mx, d), generator=gp).to(torch.bfloat16)
+    pv = torch.randn((n, Hkv, mx, d), generator=gp).to(torch.bfloat16)
+    for i, L in enumerate(lens):
+        a, e = int(inp["cu"][i]), int(inp["cu"][i + 1])
+        pq[i, :, :L] = inp["q"][a:e].transpose(0, 1)
+        pk[i, :, :L] = inp["k"][a:e].transpose(0, 1)
+        pv[i, :, :L] = inp["v"][a:e].transpose(0, 1)
+    pq, pk, pv = pq.cuda(), pk.cuda(), pv.cuda()
+    po = torch.empty_like(pq)
+    pl = torch.empty((n, H, mx), dtype=torch.float32, device="cuda")
+    t2 = time_steps(lambda: A.dense(pq, pk, pv, causal=True, scale=scale, out=po, lse=pl), steps, warmup)
+    del pq, pk, pv, po, pl
+    log(f"[bench] varlen: {n} sequences, lengths {lens}, H={H}/{Hkv} d={d} causal | path {path} (packed) | "
+        f"{t['kernel_ms_mean']:.4f} ms | {rl['achieved']} TFLOP/s = {100 * rl['frac']:.1f}% of peak | padded batch "
+        f"{t2['kernel_ms_mean']:.4f} ms")
+    return {"row": "packed variable-length forward (attn_fwd_varlen)",
+            "workload": f"varlen: causal packed batch of {n} sequences (lengths {lens}, total {sum(lens)}) "
+                        f"H={H} Hkv={Hkv} d={d} bf16",
+            "path": path + " (packed)", "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "padded_batch": {"path": path, "shape": f"B={n} T={mx}", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -609,6 +671,9 @@ def main():
         for fmt in ("q8_0", "q4_0"):
             next_rows.append(measure_qkv(fmt, st, wu))
             torch.cuda.empty_cache()
+        # packed variable-length batches
+        next_rows.append(measure_varlen(st, wu))
+        torch.cuda.empty_cache()
         # the sliding-window forward
         r = measure(7, st, wu)
         next_rows.append({"row": "sliding-window forward (window_left = 1024)", "workload": describe(7),

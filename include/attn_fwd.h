@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -361,6 +361,53 @@ attn_status attn_fwd_dense_qkv(const attn_qkv_args* a, int32_t n_splits, void* w
 /* Workspace bytes of attn_fwd_dense_qkv for n_splits (0: the library's
  * choice); 0 when one range suffices, -1 on invalid arguments. Host only. */
 int64_t attn_qkv_workspace_bytes(const attn_qkv_args* a, int32_t n_splits);
+
+/*
+ * Packed variable-length forward (bf16). The sequences of a batch are laid
+ * end to end: sequence b owns query tokens [cu_seqlens_q[b], cu_seqlens_q[b+1])
+ * and key tokens [cu_seqlens_k[b], cu_seqlens_k[b+1]). Each sequence is an
+ * independent dense attention (bottom-right causal alignment with its own
+ * lengths, the same window and sinks); no token attends across a sequence
+ * boundary. The ArcFlash pull request ("What this does NOT do") lists a
+ * varlen path whose window clamp silently made causal attention full as a
+ * defect; here causal applies per sequence.
+ *
+ *   q     [total_q, H, d_qk], element strides q_st (token), q_sh (head)
+ *   k, v  [total_k, Hkv, d], strides k_st, k_sh / v_st, v_sh
+ *   out   [total_q, H, d_v] (written), strides o_st, o_sh
+ *   lse   [H, total_q] fp32 contiguous (written)
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B + 1], non-decreasing, first
+ *         entry 0; entries are clamped to [0, total] on the device, so a
+ *         malformed array gives wrong rows, never an out-of-bounds access
+ *   max_seqlen_q: the longest query sequence (it sizes the grid; rows of a
+ *         longer sequence past it are not computed)
+ *   Compiled head dims as for attn_fwd_dense in bf16 with d_qk <= 256 (the
+ *   512-wide kernel is built without packed batches: ATTN_UNSUPPORTED); no
+ *   split-KV.
+ */
+typedef struct attn_varlen_args {
+  uint32_t struct_size; /* = sizeof(attn_varlen_args) */
+  int32_t dtype;        /* ATTN_BF16 */
+  int32_t B, H, Hkv, max_seqlen_q, total_q, total_k, d_qk, d_v;
+  int32_t causal;
+  float scale;
+  const void* q;
+  int64_t q_st, q_sh;
+  const void* k;
+  int64_t k_st, k_sh;
+  const void* v;
+  int64_t v_st, v_sh;
+  void* out;
+  int64_t o_st, o_sh;
+  float* lse;
+  const float* sinks;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t window_left;
+  int32_t window_right;
+} attn_varlen_args;
+
+attn_status attn_fwd_varlen(const attn_varlen_args* a, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status s);

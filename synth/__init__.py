@@ -215,6 +215,30 @@ QUANT_DECODE = {"name": "qdecode", "B": 4, "H": 32, "Hkv": 8, "Tq": 4, "Tk": 163
                 "seed": 8}
 
 
+# A packed prefill batch: the gqa layer (H32/Hkv8, d128, causal) over 8
+# sequences whose lengths are drawn uniformly from [64, 4096]
+# (numpy default_rng(seed)), queries = keys per sequence; seed 9.
+VARLEN_PREFILL = {"name": "varlen", "n_seqs": 8, "min_len": 64, "max_len": 4096, "H": 32, "Hkv": 8, "d": 128,
+                  "seed": 9}
+
+
+def varlen_lengths(n_seqs: int, min_len: int, max_len: int, seed: int) -> np.ndarray:
+    return np.random.default_rng(seed).integers(min_len, max_len + 1, size=n_seqs).astype(np.int64)
+
+
+def make_varlen(s: dict = VARLEN_PREFILL) -> dict:
+    """Packed CPU tensors q [total, H, d], k, v [total, Hkv, d] (bf16, drawn in that
+    order from torch.Generator(seed), N(0,1)), the lengths and cu_seqlens int32 [n + 1]."""
+    lens = varlen_lengths(s["n_seqs"], s["min_len"], s["max_len"], s["seed"])
+    total = int(lens.sum())
+    g = torch.Generator("cpu").manual_seed(s["seed"])
+    q = torch.randn((total, s["H"], s["d"]), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((total, s["Hkv"], s["d"]), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((total, s["Hkv"], s["d"]), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return {"q": q, "k": k, "v": v, "lens": lens, "cu": cu}
+
+
 def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:
     """[Sq, topk] int32, each row topk distinct values of [0, N), unsorted."""
     rng = np.random.default_rng(seed)
