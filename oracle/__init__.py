@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     dense_attention,
     dense_attention_backward,
     dense_attention_tiled,
+    dense_attention_two_part,
     dense_attention_varlen,
     dequantize_rows,
     gather_rows,

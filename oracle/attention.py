@@ -212,6 +212,24 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
     return out, lse
 
 
+def dense_attention_two_part(q_nope, q_rope, k_nope, k_rope, v, *, scale: float, causal: bool, sinks=None,
+                             window: Tuple[int, int] = (-1, -1)):
+    """MLA's two-part rows (pith-train page, "Issues resolved" item 2: the model
+    concatenates the no-rope and rope parts and feeds the result to the
+    attention): the query row is [q_nope || q_rope] and the key row
+    [k_nope || k_rope]. k_rope is [B, Hkv, Tk, r], or [B, 1, Tk, r] for one rope
+    key shared by every kv head (MLA's decoupled rope key), which is copied to
+    each kv head first. Then the dense definition on the concatenated rows.
+    """
+    q_nope, q_rope, k_nope, k_rope = _f64(q_nope), _f64(q_rope), _f64(k_nope), _f64(k_rope)
+    Hkv = k_nope.shape[1]
+    if k_rope.shape[1] == 1 and Hkv > 1:
+        k_rope = np.repeat(k_rope, Hkv, axis=1)
+    q = np.concatenate([q_nope, q_rope], axis=-1)
+    k = np.concatenate([k_nope, k_rope], axis=-1)
+    return dense_attention(q, k, v, scale=scale, causal=causal, sinks=sinks, window=window)
+
+
 def dense_attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool, sinks=None,
                            window: Tuple[int, int] = (-1, -1)):
     """Packed variable-length batch: sequence b owns query tokens

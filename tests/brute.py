@@ -74,3 +74,31 @@ def brute_sparse(q, kv, idx, d_v, scale, sinks=None):
             out[s][h] = o if o is not None else [0.0] * d_v
             lse[s][h] = l
     return out, lse
+
+
+def brute_two_part(qn, qr, kn, kr, v, scale, causal, sinks=None):
+    """Two-part rows without concatenation: score = scale * (sum over the no-rope
+    columns + sum over the rope columns), each part by its own loop; the rope key
+    of kv head kvh is kr[b][kvh], or kr[b][0] when kr has one head (shared)."""
+    B, H, Tq = len(qn), len(qn[0]), len(qn[0][0])
+    Hkv, Tk, Dv = len(kn[0]), len(kn[0][0]), len(v[0][0][0])
+    g = H // Hkv
+    out = [[[None] * Tq for _ in range(H)] for _ in range(B)]
+    lse = [[[0.0] * Tq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            kvh = h // g
+            rh = 0 if len(kr[b]) == 1 else kvh
+            for t in range(Tq):
+                sc, vals = [], []
+                for j in range(Tk):
+                    if causal and j > t + (Tk - Tq):
+                        continue
+                    a = math.fsum(float(x) * float(y) for x, y in zip(qn[b][h][t], kn[b][kvh][j]))
+                    r = math.fsum(float(x) * float(y) for x, y in zip(qr[b][h][t], kr[b][rh][j]))
+                    sc.append(scale * (a + r))
+                    vals.append([float(x) for x in v[b][kvh][j]])
+                o, l = _attend(sc, vals, None if sinks is None else float(sinks[h]))
+                out[b][h][t] = o if o is not None else [0.0] * Dv
+                lse[b][h][t] = l
+    return out, lse

@@ -18,7 +18,7 @@ from scipy.special import logsumexp
 
 import oracle
 from oracle import attention as OA
-from tests.brute import brute_dense, brute_sparse
+from tests.brute import brute_dense, brute_sparse, brute_two_part
 
 TOL = 1e-12
 
@@ -371,7 +371,32 @@ def check_lse_logsumexp(orc=oracle):
     return worst
 
 
+def check_two_part(orc=oracle):
+    """MLA's two-part rows: brute force that sums the two partial dot products in
+    separate loops (no concatenation), with a rope key per kv head and one shared
+    by all kv heads; and the shared case equals the concatenation with the rope
+    key copied to every head."""
+    worst = 0.0
+    for i, (B, H, Hkv, Tq, Tk, dn, dr, dv) in enumerate([(1, 4, 2, 5, 7, 4, 3, 2), (2, 3, 3, 4, 4, 2, 2, 3)]):
+        qn, qr = _rand((B, H, Tq, dn), 950 + i), _rand((B, H, Tq, dr), 951 + i)
+        kn, v = _rand((B, Hkv, Tk, dn), 952 + i), _rand((B, Hkv, Tk, dv), 953 + i)
+        sinks = _rand((H,), 954 + i)
+        for kr in (_rand((B, Hkv, Tk, dr), 955 + i), _rand((B, 1, Tk, dr), 956 + i)):
+            for causal in (False, True):
+                for sk in (None, sinks):
+                    o, l = orc.dense_attention_two_part(qn, qr, kn, kr, v, scale=0.6, causal=causal, sinks=sk)
+                    bo, bl = brute_two_part(qn, qr, kn, kr, v, 0.6, causal, sk)
+                    worst = max(worst, _err(o, bo), _err(l, bl))
+    qn, qr = _rand((1, 4, 6, 3), 960), _rand((1, 4, 6, 2), 961)
+    kn, kr, v = _rand((1, 2, 6, 3), 962), _rand((1, 1, 6, 2), 963), _rand((1, 2, 6, 2), 964)
+    o, l = orc.dense_attention_two_part(qn, qr, kn, kr, v, scale=0.6, causal=True)
+    kc = np.concatenate([kn, np.concatenate([kr, kr], axis=1)], axis=-1)
+    o2, l2 = orc.dense_attention(np.concatenate([qn, qr], axis=-1), kc, v, scale=0.6, causal=True)
+    return max(worst, _err(o, o2), _err(l, l2))
+
+
 ALL_CHECKS = {
+    "two_part": check_two_part,
     "window": check_window,
     "varlen": check_varlen,
     "brute_dense": check_brute_dense,

@@ -101,3 +101,23 @@ def test_varlen_mask_dropped_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "dense_attention_varlen", non_causal)
     _assert_caught(_caught(["varlen"]))
+
+
+def test_two_part_rope_head_caught(monkeypatch):
+    """Two-part rows with the rope key of kv head 0 used for every kv head."""
+    orig = OA.dense_attention_two_part
+
+    def head0(qn, qr, kn, kr, v, **kw):
+        return orig(qn, qr, kn, np.asarray(kr, dtype=np.float64)[:, :1], v, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention_two_part", head0)
+    _assert_caught(_caught(["two_part"]))
+
+
+def test_two_part_rope_dropped_caught(monkeypatch):
+    """Two-part rows with the rope part left out of the scores."""
+    def no_rope(qn, qr, kn, kr, v, **kw):
+        return OA.dense_attention(qn, kn, v, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention_two_part", no_rope)
+    _assert_caught(_caught(["two_part"]))
