@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -41,6 +41,9 @@ class AttnDenseArgs(ctypes.Structure):
         ("sinks", ctypes.c_void_p),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("q_rope", ctypes.c_void_p), ("qr_sb", ctypes.c_int64), ("qr_sh", ctypes.c_int64), ("qr_st", ctypes.c_int64),
+        ("k_rope", ctypes.c_void_p), ("kr_sb", ctypes.c_int64), ("kr_sh", ctypes.c_int64), ("kr_st", ctypes.c_int64),
     ]
 
 
@@ -246,11 +249,26 @@ def _stream_handle(stream) -> int:
 
 
 def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
-               window: Tuple[int, int] = (-1, -1)) -> AttnDenseArgs:
-    """Fill the C argument struct from tensors (BHSD or any strided view with unit last stride)."""
+               window: Tuple[int, int] = (-1, -1), q_rope=None, k_rope=None) -> AttnDenseArgs:
+    """Fill the C argument struct from tensors (BHSD or any strided view with unit last stride).
+
+    With ``q_rope`` [B,H,Tq,r] and ``k_rope`` [B,Hkv,Tk,r] the query and key rows are
+    [q || q_rope] and [k || k_rope] (d_qk = q's width + r), read in place; a rope key
+    shared by the kv heads is passed as an expanded view (head stride 0)."""
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
     dv = v.shape[-1]
+    rope = 0
+    if q_rope is not None or k_rope is not None:
+        if q_rope is None or k_rope is None:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "q_rope and k_rope go together")
+        rope = q_rope.shape[-1]
+        if (tuple(q_rope.shape) != (B, H, Tq, rope) or tuple(k_rope.shape) != (B, Hkv, Tk, rope)
+                or k.shape[-1] != dqk or q_rope.stride(-1) != 1 or k_rope.stride(-1) != 1
+                or q_rope.dtype != q.dtype or k_rope.dtype != q.dtype):
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT,
+                                      "q_rope [B,H,Tq,r] and k_rope [B,Hkv,Tk,r] with unit last stride, q's dtype")
+        dqk += rope
     a = AttnDenseArgs()
     a.struct_size = ctypes.sizeof(AttnDenseArgs)
     a.dtype = _dtype_code(q)
@@ -267,17 +285,23 @@ def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
     a.lse = lse.data_ptr()
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.window_left, a.window_right = int(window[0]), int(window[1])
+    a.rope_dim = rope
+    if rope:
+        a.q_rope, (a.qr_sb, a.qr_sh, a.qr_st) = q_rope.data_ptr(), q_rope.stride()[:3]
+        a.k_rope, (a.kr_sb, a.kr_sh, a.kr_st) = k_rope.data_ptr(), k_rope.stride()[:3]
     return a
 
 
 def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
-          out=None, lse=None, stream=None, window: Tuple[int, int] = (-1, -1)) -> Tuple["torch.Tensor", "torch.Tensor"]:
+          out=None, lse=None, stream=None, window: Tuple[int, int] = (-1, -1), q_rope=None,
+          k_rope=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Fused dense attention forward on the GPU.
 
     q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v] (bf16, or fp32 for the
     split-bf16 path), sinks [H] fp32 or None. ``window`` = (left, right) keys
     around each row's diagonal position t + Tk - Tq (-1: unbounded; bf16 only;
-    it never widens the causal mask). Returns (out [B,H,Tq,d_v] in the input
+    it never widens the causal mask). ``q_rope``/``k_rope``: MLA's rope parts
+    read in place (see :func:`dense_args`). Returns (out [B,H,Tq,d_v] in the input
     dtype, lse [B,H,Tq] fp32). Launches on ``stream`` (default: torch's current
     stream) and does not synchronise.
     """
@@ -287,7 +311,7 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
     B, H, Tq, dqk = q.shape
     dv = v.shape[-1]
     if scale is None:
-        scale = 1.0 / math.sqrt(dqk)
+        scale = 1.0 / math.sqrt(dqk + (q_rope.shape[-1] if q_rope is not None else 0))
     if out is None:
         out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -296,14 +320,15 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
     if not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
-    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window, q_rope=q_rope,
+                   k_rope=k_rope)
     _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
 
 
 def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
                   n_splits: int = 0, out=None, lse=None, workspace=None, stream=None,
-                  window: Tuple[int, int] = (-1, -1)):
+                  window: Tuple[int, int] = (-1, -1), q_rope=None, k_rope=None):
     """Split-KV dense forward (decode and other few-row shapes): same inputs
     and results as :func:`dense`. The keys are cut into ``n_splits`` ranges
     (0: the library's choice); the fp32 partials go to ``workspace``, a uint8
@@ -316,7 +341,7 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
     B, H, Tq, dqk = q.shape
     dv = v.shape[-1]
     if scale is None:
-        scale = 1.0 / math.sqrt(dqk)
+        scale = 1.0 / math.sqrt(dqk + (q_rope.shape[-1] if q_rope is not None else 0))
     if out is None:
         out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -325,7 +350,8 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
     if not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
-    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window, q_rope=q_rope,
+                   k_rope=k_rope)
     need = int(lib.attn_splitkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
     if need < 0:
         _check(ATTN_INVALID_ARGUMENT)

@@ -84,11 +84,12 @@ int64_t tile_budget_bytes() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }  // NULL passes
 
-const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse) {
+const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse, int rope = 0) {
   int n = 0;
   const attn::KernelConfig* t = attn::kernel_table(&n);
   for (int i = 0; i < n; ++i)
-    if (t[i].dtype == dtype && t[i].d_qk == d_qk && t[i].d_v == d_v && t[i].sparse == sparse) return &t[i];
+    if (t[i].dtype == dtype && t[i].d_qk == d_qk && t[i].d_v == d_v && t[i].sparse == sparse && t[i].rope == rope)
+      return &t[i];
   return nullptr;
 }
 
@@ -136,10 +137,27 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
     return fail(ATTN_INVALID_ARGUMENT, "window bounds must be >= -1 (-1: unbounded)");
   if (a->dtype != ATTN_BF16 && (a->window_left >= 0 || a->window_right >= 0))
     return fail(ATTN_UNSUPPORTED, "sliding windows are compiled for bf16 inputs only");
-  const attn::KernelConfig* cfg = find_config(a->dtype, a->d_qk, a->d_v, 0);
+  if (a->rope_dim < 0 || a->rope_dim >= a->d_qk)
+    return fail(ATTN_INVALID_ARGUMENT, "rope_dim must be 0 or in [1, d_qk)");
+  const attn::KernelConfig* cfg = find_config(a->dtype, a->d_qk, a->d_v, 0, a->rope_dim);
   if (!cfg)
-    return fail(ATTN_UNSUPPORTED, "no compiled dense kernel for dtype %d with (d_qk, d_v) = (%d, %d)", a->dtype,
-                a->d_qk, a->d_v);
+    return fail(ATTN_UNSUPPORTED, "no compiled dense kernel for dtype %d with (d_qk, d_v) = (%d, %d), rope_dim %d",
+                a->dtype, a->d_qk, a->d_v, a->rope_dim);
+  const int rope = a->rope_dim;
+  const int d_main = a->d_qk - rope;  // columns held by q and k
+  if (rope > 0) {
+    if (a->Tq > 0 && !a->q_rope) return fail(ATTN_INVALID_ARGUMENT, "q_rope must be non-NULL when Tq > 0");
+    if (a->Tk > 0 && !a->k_rope) return fail(ATTN_INVALID_ARGUMENT, "k_rope must be non-NULL when Tk > 0");
+    if (!aligned16(a->q_rope) || !aligned16(a->k_rope))
+      return fail(ATTN_INVALID_ARGUMENT, "q_rope, k_rope must be 16-byte aligned");
+    const int64_t rs[] = {a->qr_sb, a->qr_sh, a->qr_st, a->kr_sb, a->kr_sh, a->kr_st};
+    for (int64_t x : rs)
+      if (x < 0 || x % 8 != 0)
+        return fail(ATTN_INVALID_ARGUMENT, "rope strides must be >= 0 and multiples of 8 elements");
+    if (a->kr_st >= (1 << 24)) return fail(ATTN_INVALID_ARGUMENT, "k_rope token stride must be below 2^24 elements");
+    if (a->Tq > 1 && a->qr_st < rope) return fail(ATTN_INVALID_ARGUMENT, "q_rope token stride smaller than rope_dim");
+    if (a->Tk > 1 && a->kr_st < rope) return fail(ATTN_INVALID_ARGUMENT, "k_rope token stride smaller than rope_dim");
+  }
   // empty operands (Tq == 0 or Tk == 0) may come with NULL pointers; they are never read
   if (a->Tq > 0 && (!a->q || !a->out || !a->lse))
     return fail(ATTN_INVALID_ARGUMENT, "q, out, lse must be non-NULL when Tq > 0");
@@ -156,8 +174,8 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
                   (long long)vec);
   if (a->k_st >= (1 << 24) || a->v_st >= (1 << 24))
     return fail(ATTN_INVALID_ARGUMENT, "k/v token strides must be below 2^24 elements");
-  if (a->Tq > 1 && a->q_st < a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "q token stride smaller than d_qk");
-  if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v))
+  if (a->Tq > 1 && a->q_st < d_main) return fail(ATTN_INVALID_ARGUMENT, "q token stride smaller than its row");
+  if (a->Tk > 1 && (a->k_st < d_main || a->v_st < a->d_v))
     return fail(ATTN_INVALID_ARGUMENT, "k/v token stride smaller than the head dim");
   if (a->Tq > 1 && a->o_st < a->d_v) return fail(ATTN_INVALID_ARGUMENT, "out token stride smaller than d_v");
 
@@ -169,6 +187,10 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
   p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;
   p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_st = a->o_st;
+  if (rope > 0) {
+    p.q2 = a->q_rope; p.q2_sb = a->qr_sb; p.q2_sh = a->qr_sh; p.q2_st = a->qr_st;
+    p.k2 = a->k_rope; p.k2_sb = a->kr_sb; p.k2_sh = a->kr_sh; p.k2_st = a->kr_st;
+  }
   p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
   p.npool = 0;
   p.causal = a->causal;

@@ -701,6 +701,14 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
                : "memory");
 }
 
+// The same with a full 64-bit address per lane (no scalar base): the lanes of
+// one instruction may read from two different tensors.
+__device__ __forceinline__ void dma16v(uint64_t addr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(addr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // a pointer that is the same in every lane, moved to scalar registers
 __device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
   const uint64_t v = (uint64_t)(uintptr_t)ptr;
@@ -813,10 +821,14 @@ struct DCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG>
+// ROPE > 0: the last ROPE columns of q and k come from q2 / k2 (MLA's rope
+// part read in place); the other DQK - ROPE from q / k.
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, int ROPE = 0>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_dma_kernel(const KernelParams p) {
   using C = DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>;
+  static_assert(ROPE == 0 || (!SPARSE && DS == 1 && (DQK - ROPE) % 16 == 0 && ROPE % 16 == 0),
+                "two-part rows: one wave holds the whole row, both parts whole K steps");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
   bf16_t* const kring = reinterpret_cast<bf16_t*>(smem);
   bf16_t* const vring = reinterpret_cast<bf16_t*>(smem + C::KRING_BYTES);
@@ -953,7 +965,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   const bool row_ok = r < nrows;
   const int rr = row_ok ? r : 0;
   int row_lim, row_lo = -(1 << 30), row_h;
-  int64_t q_off, o_off, l_off;
+  int64_t q_off, o_off, l_off, q2_off = 0;
   if constexpr (SPARSE) {
     row_h = rr;
     row_lim = Tk - 1;
@@ -968,6 +980,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
     row_lim = min(row_lim - k_lo, kend - 1);  // relative to the range
     if (p.win_left >= 0) row_lo = t + off - p.win_left - k_lo;
     q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (qtok0 + t) * p.q_st;
+    if constexpr (ROPE > 0) q2_off = (int64_t)b * p.q2_sb + (int64_t)row_h * p.q2_sh + (qtok0 + t) * p.q2_st;
     o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (qtok0 + t) * p.o_st;
     l_off = kPacked && p.varlen ? (int64_t)row_h * p.total_q + qtok0 + t : ((int64_t)b * p.H + row_h) * Tq + t;
   }
@@ -976,10 +989,16 @@ attn_fwd_dma_kernel(const KernelParams p) {
   bf16x8 qf[C::KS];
   {
     const bf16_t* qb = reinterpret_cast<const bf16_t*>(p.q) + q_off;
+    const bf16_t* qb2 = ROPE > 0 ? reinterpret_cast<const bf16_t*>(p.q2) + q2_off : nullptr;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok) w = *reinterpret_cast<const u32x4*>(qb + dsi * C::DQW + s * 16 + lh * 8);
+      if (row_ok) {
+        if (ROPE > 0 && s * 16 >= DQK - ROPE)
+          w = *reinterpret_cast<const u32x4*>(qb2 + (s * 16 - (DQK - ROPE)) + lh * 8);
+        else
+          w = *reinterpret_cast<const u32x4*>(qb + dsi * C::DQW + s * 16 + lh * 8);
+      }
       qf[s] = as_bf16x8(w);
     }
     // use the fragments here so that the compiler waits for these loads before
@@ -991,6 +1010,10 @@ attn_fwd_dma_kernel(const KernelParams p) {
 
   const bf16_t* kbase;
   const bf16_t* vbase;
+  const bf16_t* k2base = nullptr;
+  if constexpr (ROPE > 0)
+    k2base = reinterpret_cast<const bf16_t*>(p.k2) + (int64_t)b * p.k2_sb + (int64_t)kvh * p.k2_sh +
+             (ktok0 + k_lo) * p.k2_st;
   if constexpr (SPARSE) {
     kbase = reinterpret_cast<const bf16_t*>(p.k);
     vbase = kbase;
@@ -1058,7 +1081,27 @@ attn_fwd_dma_kernel(const KernelParams p) {
     asm volatile("" : "+s"(kr));
     const uint32_t Kb = kr + (uint32_t)((blk % NBUF) * C::K_ELEMS * 2);
     const int key0 = blk * BN;
-    if constexpr (SPARSE) {
+    if constexpr (ROPE > 0) {
+      // two-part rows: the tile row is laid out as one DQK-wide row, chunk c
+      // < NC0 comes from the first tensor and the rest from the second; the
+      // lanes of one instruction cover both parts, so each carries its own
+      // 64-bit address. Rows past kend are clamped onto row kend-1.
+      constexpr int NC0 = (DQK - ROPE) / 8;
+      const int last = kend - 1 - key0;
+      const uint64_t nb = (uint64_t)(uintptr_t)(kbase + (int64_t)key0 * p.k_st);
+      const uint64_t rb = (uint64_t)(uintptr_t)(k2base + (int64_t)key0 * p.k2_st);
+#pragma unroll
+      for (int m = 0; m < NIK_L; ++m) {
+        const int j = lw_ + NLW_ * m;
+        if (C::NIK % NLW_ != 0 && j >= C::NIK) break;
+        const int sl = 64 * j + lane;
+        const int rw = sl / C::CPRK, cp = sl % C::CPRK, c = cp ^ swz<C::CPRK>(rw);
+        const int rr = min(rw, last);
+        const uint64_t a = cp < NC0 ? nb + 2u * (uint32_t)(rr * (int32_t)p.k_st + c * 8)
+                                    : rb + 2u * (uint32_t)(rr * (int32_t)p.k2_st + (c - NC0) * 8);
+        dma16v(a, Kb + 1024u * NLW_ * m);
+      }
+    } else if constexpr (SPARSE) {
       // one LDS read per lane for the block's indices; each wave instruction
       // loads one pool row (64 chunks) whose index is broadcast by readlane
       static_assert(C::CPRK == 64 && BN <= 64, "one gathered row per wave instruction");
@@ -1558,21 +1601,21 @@ attn_fwd_dma_kernel(const KernelParams p) {
   }
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0>
 int occupancy_dma() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>), NW * 64,
-          0) != hipSuccess) {
+          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE>),
+          NW * 64, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
   return n;
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0>
 int launch_dma(const KernelParams& p, void* stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>),
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE>),
                      dim3(p.n_tiles, p.n_splits > 1 ? p.n_splits : 1), dim3(NW * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
@@ -1640,6 +1683,13 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) 
   if (lane == 0) m.lse[row] = lse;
 }
 
+#define DMA_ENTRY_ROPE(NAME, DQK, DV, ROPE, DS, NW, BN, NBUF, PP)                                                  \
+  KernelConfig {                                                                                                 \
+    NAME, 0, DQK, DV, false, DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP>::BM, BN, NW,                               \
+        DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, ROPE>, \
+        &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, ROPE>, ROPE                                          \
+  }
+
 #define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
   KernelConfig {                                                                                                 \
     NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::BM, BN, NW,                           \
@@ -1676,6 +1726,7 @@ int launch(const KernelParams& p, void* stream) {
 // (DS, waves, BN, LDS ring slots, two wave groups) per head-dim configuration;
 // DMA_ENTRY_X expands them first
 #define DMA_ENTRY_X(...) DMA_ENTRY(__VA_ARGS__)
+#define DMA_ENTRY_ROPE_X(...) DMA_ENTRY_ROPE(__VA_ARGS__)
 #ifndef ATTN_CFG_D64
 #define ATTN_CFG_D64 1, 8, 64, 3, true
 #endif
@@ -1699,6 +1750,7 @@ const KernelConfig kTable[] = {
     DMA_ENTRY_X("dense_bf16_d64", 64, 64, ATTN_CFG_D64, false),
     DMA_ENTRY_X("dense_bf16_d128", 128, 128, ATTN_CFG_D128, false),
     DMA_ENTRY_X("dense_bf16_d192_v128", 192, 128, ATTN_CFG_D192, false),
+    DMA_ENTRY_ROPE_X("dense_bf16_d192_v128_rope64", 192, 128, 64, ATTN_CFG_D192),
     DMA_ENTRY_X("dense_bf16_d256", 256, 256, ATTN_CFG_D256, false),
     DMA_ENTRY_X("dense_bf16_d512", 512, 512, ATTN_CFG_D512, false),
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),

@@ -20,6 +20,12 @@ struct KernelParams {
   int64_t v_sb, v_sh, v_st;
   int64_t o_sb, o_sh, o_st;
   int64_t idx_ss;
+  // two-part q / k rows (kernels compiled with a rope width): the last
+  // columns of each row come from q2 / k2 with these strides
+  const void* q2;
+  const void* k2;
+  int64_t q2_sb, q2_sh, q2_st;
+  int64_t k2_sb, k2_sh, k2_st;
 
   int32_t B, H, Hkv, Tq, Tk, g;  // sparse: B = Sq, H = Hq, Hkv = 1, Tk = topk
   int32_t npool;                 // sparse: rows in the pool
@@ -148,6 +154,7 @@ struct KernelConfig {
   int block_rows, block_keys, waves, lds_bytes;
   launch_fn launch;
   occupancy_fn occupancy;
+  int rope;          // columns of q / k read from the second pointers (0: none)
 };
 
 // Table of compiled configurations (defined in attn_kernels.hip).

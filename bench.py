@@ -14,7 +14,8 @@ Rows beyond the five ("next_rows", skipped with --no-next-rows): split-KV
 decode (d512, beside the plain path), the dense backward on gqa / mla /
 swa1024 (algorithmic flops = five products per visible pair), decode over a
 q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
-forward (beside the padded batch) and the sliding-window forward.
+forward (beside the padded batch), MLA two-part rows (beside the concatenated
+call) and the sliding-window forward.
 
 Warmup: at least W untimed steps and at least 0.2 s of them (the clocks
 ramp over the first ~30 ms of load). Prints ONE JSON line on stdout. Kernel
@@ -464,6 +465,49 @@ def measure_varlen(steps: int, warmup: int) -> dict:
             "padded_batch": {"path": path, "shape": f"B={n} T={mx}", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
 
 
+def measure_two_part(steps: int, warmup: int) -> dict:
+    """The MLA workload (3) with the query and key rows in two parts read in place:
+    q / k no-rope [.., 128] and rope [.., 64] as strided views of the workload's
+    tensors, the rope key of kv head 0 shared by all heads (an expanded view).
+    Same algorithmic flops as workload 3; the concatenated call on the same values
+    is timed beside it."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(3)
+    inp = synth.make(3)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    dn = 128
+    qn, qr, kn = q[..., :dn], q[..., dn:], k[..., :dn]
+    kr = k[:, :1, :, dn:].expand(s.B, s.Hkv, s.Tk, s.d_qk - dn)
+    out = torch.empty((s.B, s.H, s.Tq, s.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((s.B, s.H, s.Tq), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.dense(qn, kn, v, causal=True, scale=s.scale, out=out, lse=lse, q_rope=qr, k_rope=kr)
+
+    path = "dense_bf16_d192_v128_rope64"
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != t["calls"]:
+        raise RuntimeError(f"NotEngaged: expected {t['calls']} launches of {path}, saw {A.dispatch_count(path)}")
+    fl = work(3)["flops"]
+    ach = fl / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    qc, kc = torch.cat([qn, qr], -1), torch.cat([kn, kr], -1)
+    t2 = time_steps(lambda: A.dense(qc, kc, v, causal=True, scale=s.scale, out=out, lse=lse), steps, warmup)
+    log(f"[bench] two-part mla: {describe(3)}, rope key shared | path {path} | {t['kernel_ms_mean']:.4f} ms | "
+        f"{rl['achieved']} TFLOP/s = {100 * rl['frac']:.1f}% of peak | concatenated rows {t2['kernel_ms_mean']:.4f} ms")
+    return {"row": "MLA two-part rows read in place (attn_fwd_dense with q_rope / k_rope)",
+            "workload": describe(3) + ", q/k as no-rope 128 + rope 64 views, rope key shared by the heads",
+            "path": path, "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "concatenated": {"path": "dense_bf16_d192_v128", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -691,6 +735,9 @@ def main():
             torch.cuda.empty_cache()
         # packed variable-length batches
         next_rows.append(measure_varlen(st, wu))
+        torch.cuda.empty_cache()
+        # MLA rows in two parts
+        next_rows.append(measure_two_part(st, wu))
         torch.cuda.empty_cache()
         # the sliding-window forward
         r = measure(7, st, wu)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -95,6 +95,18 @@ typedef enum attn_dtype {
  *        window clamp that widened causal attention to full attention is a
  *        defect the ArcFlash pull request lists under "What this does NOT
  *        do"). bf16 only; (-1, -1) for float32 inputs.
+ *   rope_dim, q_rope, k_rope: MLA's two-part query and key without the
+ *        concatenation (pith-train pull request 65, "Issues resolved" item
+ *        2, builds [q_nope || q_rope] and [k_nope || k_rope] in the model; here
+ *        the kernel reads the two parts in place). rope_dim = 0: q and k
+ *        hold all d_qk columns (q_rope, k_rope unused). rope_dim > 0: q and
+ *        k hold the first d_qk - rope_dim columns, and q_rope [B, H, Tq,
+ *        rope_dim] (strides qr_sb, qr_sh, qr_st) and k_rope [B, Hkv, Tk,
+ *        rope_dim] (strides kr_sb, kr_sh, kr_st) the last rope_dim; the
+ *        result is that of the concatenated rows. kr_sh (and kr_sb) may be
+ *        0: one rope key row shared by every kv head, as MLA's decoupled
+ *        rope key is. Compiled: bf16, d_qk = 192 with rope_dim = 64, d_v =
+ *        128; ATTN_UNSUPPORTED otherwise.
  */
 typedef struct attn_dense_args {
   uint32_t struct_size; /* = sizeof(attn_dense_args) */
@@ -114,6 +126,11 @@ typedef struct attn_dense_args {
   const float* sinks;
   int32_t window_left;  /* -1: no left bound */
   int32_t window_right; /* -1: no right bound */
+  int32_t rope_dim;     /* 0, or the columns held by q_rope / k_rope */
+  const void* q_rope;
+  int64_t qr_sb, qr_sh, qr_st;
+  const void* k_rope;
+  int64_t kr_sb, kr_sh, kr_st;
 } attn_dense_args;
 
 /*
