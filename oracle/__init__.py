@@ -14,7 +14,9 @@ from .attention import (  # noqa: F401
     gather_rows,
     merge_partials,
     repeat_kv,
+    scatter_add_rows,
     sparse_topk_attention,
+    sparse_topk_attention_backward,
     sum_kv_groups,
     tile_rows_for_budget,
 )

@@ -479,3 +479,67 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
                 p_sink = np.where(np.isfinite(lse), np.exp(sink - np.where(np.isfinite(lse), lse, 0.0)), 0.0)
                 dsk[h] -= float((p_sink * D).sum())
     return dq, sum_kv_groups(dK, g), sum_kv_groups(dV, g), dsk
+
+
+def scatter_add_rows(n_rows: int, idx: Sequence[int], rows: np.ndarray) -> np.ndarray:
+    """Adjoint of ``gather_rows``: y[n] = sum of rows[j] over the slots j with idx[j] == n
+    (slots whose index is outside [0, n_rows) contribute nothing, as they were skipped)."""
+    y = np.zeros((n_rows, rows.shape[1]))
+    for j, n in enumerate(idx):
+        n = int(n)
+        if 0 <= n < n_rows:
+            y[n] += rows[j]
+    return y
+
+
+def sparse_topk_attention_backward(q, kv, idx, dout, *, d_v: int, scale: float, sinks=None):
+    """Gradients of the sparse top-k forward in fp64: (dq, dkv, dsinks).
+
+    ``dout`` = dL/dO [Sq,Hq,d_v]; lse carries no gradient (as in the dense
+    backward). The pool plays both roles: its rows are the keys (all d_qk
+    columns) and their first d_v columns the values, so the pool's gradient is
+    the sum of the two. Per query s, through the forward's definition:
+
+      1. G = kv[idx[s]] (explicit gather, skipped slots dropped),
+         S = scale * q[s] . G^T, row softmax P (sink in the denominator),
+         O = P . G[:, :d_v].
+      2. dP = dO . G[:, :d_v]^T, D = rowsum(dO * O), dS = P * (dP - D).
+      3. dq[s] = scale * dS . G.
+      4. dG = scale * dS^T . q[s]            (key role, all d_qk columns)
+         dG[:, :d_v] += P^T . dO             (value role)
+      5. dkv += the scatter-add of dG into the rows idx[s] names (the adjoint
+         of the gather; a duplicated index receives both slots' gradients).
+      6. dsink_h = -sum over queries of exp(sink_h - lse) * D.
+    """
+    q, kv, dout = _f64(q), _f64(kv), _f64(dout)
+    idx = np.asarray(idx.numpy() if hasattr(idx, "numpy") else idx)
+    Sq, Hq, Dqk = q.shape
+    N = kv.shape[0]
+    sk = None if sinks is None else _f64(sinks)
+    dq = np.zeros_like(q)
+    dkv = np.zeros((N, Dqk))
+    dsk = None if sk is None else np.zeros(Hq)
+    for s in range(Sq):
+        keep = [int(n) for n in idx[s] if 0 <= int(n) < N]
+        G = gather_rows(kv, keep)
+        Vg = _value_rows(G, d_v)
+        S = scale * (q[s] @ G.T)                                  # [Hq, n]
+        P = np.empty_like(S)
+        lse = np.empty(Hq)
+        for h in range(Hq):
+            Ph, Lh = _softmax_rows(S[h:h + 1], None if sk is None else float(sk[h]))
+            P[h], lse[h] = Ph[0], Lh[0]
+        O = P @ Vg
+        dO = dout[s]
+        dP = dO @ Vg.T
+        dS = _softmax_backward(P, dP, dO, O)
+        dq[s] = scale * (dS @ G)
+        dG = scale * (dS.T @ q[s])
+        dG[:, :d_v] += P.T @ dO
+        dkv += scatter_add_rows(N, keep, dG)
+        if sk is not None:
+            D = (dO * O).sum(axis=1)
+            fin = np.isfinite(lse)
+            p_sink = np.where(fin, np.exp(sk - np.where(fin, lse, 0.0)), 0.0)
+            dsk -= p_sink * D
+    return dq, dkv, dsk

@@ -178,7 +178,78 @@ def check_bwd_window_finite_differences(orc=oracle):
     return worst / TOL_FD * TOL
 
 
+def _sparse_loss(orc, q, kv, idx, G, d_v, scale, sinks):
+    o, _ = orc.sparse_topk_attention(q, kv, idx, d_v=d_v, scale=scale, sinks=sinks)
+    return float((o * G).sum())
+
+
+SPARSE_IDX = np.array([[0, 3, 3, 5], [6, 1, -1, 2], [4, 4, 4, 0]])   # duplicates and a skipped slot
+
+
+def check_sparse_bwd_finite_differences(orc=oracle):
+    """dq, dkv, dsinks of the sparse forward against central differences: duplicated
+    indices, a skipped (-1) slot, V the first d_v < d_qk columns of the pool."""
+    worst = 0.0
+    Sq, Hq, N, dqk, dv = 3, 2, 7, 5, 3
+    q = _rand((Sq, Hq, dqk), 360, 0.8)
+    kv = _rand((N, dqk), 361, 0.8)
+    G = _rand((Sq, Hq, dv), 362)
+    sinks = _rand((Hq,), 363)
+    for sk in (None, sinks.copy()):
+        gq, gkv, gs = orc.sparse_topk_attention_backward(q, kv, SPARSE_IDX, G, d_v=dv, scale=0.6, sinks=sk)
+        f = lambda: _sparse_loss(orc, q, kv, SPARSE_IDX, G, dv, 0.6, sk)  # noqa: E731
+        worst = max(worst, _err(gq, _fd_grad(f, q)), _err(gkv, _fd_grad(f, kv)))
+        if sk is not None:
+            worst = max(worst, _err(gs, _fd_grad(f, sk)))
+    return worst / TOL_FD * TOL
+
+
+def check_sparse_bwd_library_autograd(orc=oracle):
+    """torch autograd (fp64) through index_select + softmax with an explicit sink column."""
+    worst = 0.0
+    Sq, Hq, N, d, topk = 4, 3, 9, 6, 5
+    q, kv = _rand((Sq, Hq, d), 370), _rand((N, d), 371)
+    rng = np.random.default_rng(372)
+    idx = np.stack([rng.choice(N, topk, replace=False) for _ in range(Sq)])
+    G = _rand((Sq, Hq, d), 373)
+    sinks = _rand((Hq,), 374)
+    for sk in (None, sinks):
+        Q, KV = torch.tensor(q, requires_grad=True), torch.tensor(kv, requires_grad=True)
+        S_ = torch.tensor(sk, requires_grad=True) if sk is not None else None
+        outs = []
+        for s in range(Sq):
+            g = KV.index_select(0, torch.from_numpy(idx[s]))
+            sc = 0.45 * Q[s] @ g.T
+            if S_ is not None:
+                p = torch.softmax(torch.cat([sc, S_[:, None]], dim=1), dim=1)[:, :topk]
+            else:
+                p = torch.softmax(sc, dim=1)
+            outs.append(p @ g)
+        (torch.stack(outs) * torch.from_numpy(G)).sum().backward()
+        gq, gkv, gs = orc.sparse_topk_attention_backward(q, kv, idx, G, d_v=d, scale=0.45, sinks=sk)
+        worst = max(worst, _err(gq, Q.grad.numpy()), _err(gkv, KV.grad.numpy()))
+        if sk is not None:
+            worst = max(worst, _err(gs, S_.grad.numpy()))
+    return worst
+
+
+def check_sparse_bwd_equals_dense_mqa(orc=oracle):
+    """Every query naming the whole pool (d_v = d_qk) is dense non-causal MQA with k = v =
+    the pool: dq equal, and the pool's gradient is the dense dk + dv."""
+    Sq, Hq, N, d = 5, 4, 6, 4
+    q, kv, G = _rand((Sq, Hq, d), 380), _rand((N, d), 381), _rand((Sq, Hq, d), 382)
+    sinks = _rand((Hq,), 383)
+    idx = np.tile(np.arange(N), (Sq, 1))
+    gq, gkv, gs = orc.sparse_topk_attention_backward(q, kv, idx, G, d_v=d, scale=0.5, sinks=sinks)
+    dq, dk, dv, ds = orc.dense_attention_backward(q.transpose(1, 0, 2)[None], kv[None, None], kv[None, None],
+                                                  G.transpose(1, 0, 2)[None], scale=0.5, causal=False, sinks=sinks)
+    return max(_err(gq, dq[0].transpose(1, 0, 2)), _err(gkv, dk[0, 0] + dv[0, 0]), _err(gs, ds))
+
+
 ALL_CHECKS = {
+    "sparse_bwd_finite_differences": check_sparse_bwd_finite_differences,
+    "sparse_bwd_library_autograd": check_sparse_bwd_library_autograd,
+    "sparse_bwd_equals_dense_mqa": check_sparse_bwd_equals_dense_mqa,
     "bwd_window_finite_differences": check_bwd_window_finite_differences,
     "bwd_finite_differences": check_bwd_finite_differences,
     "bwd_library_autograd": check_bwd_library_autograd,

@@ -63,3 +63,43 @@ def test_sink_gradient_sign_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "dense_attention_backward", flipped)
     _assert_caught(["bwd_finite_differences", "bwd_library_autograd"])
+
+
+def test_sparse_value_role_dropped_caught(monkeypatch):
+    """The pool's gradient without its value-role term P^T dO."""
+    orig = OA.sparse_topk_attention_backward
+
+    def key_only(q, kv, idx, dout, *, d_v, scale, sinks=None):
+        dq, dkv, ds = orig(q, kv, idx, dout, d_v=d_v, scale=scale, sinks=sinks)
+        # subtract the value-role part again, recomputed per query
+        qf, kvf, do = (np.asarray(x, np.float64) for x in (q, kv, dout))
+        for s in range(qf.shape[0]):
+            keep = [int(n) for n in idx[s] if 0 <= int(n) < kvf.shape[0]]
+            Gm = kvf[keep]
+            S = scale * (qf[s] @ Gm.T)
+            m = S.max(axis=1, keepdims=True)
+            if sinks is not None:
+                m = np.maximum(m, np.asarray(sinks)[:, None])
+            e = np.exp(S - m)
+            den = e.sum(axis=1, keepdims=True) + (0 if sinks is None else np.exp(np.asarray(sinks)[:, None] - m))
+            P = e / den
+            contrib = P.T @ do[s]
+            for j, n in enumerate(keep):
+                dkv[n, :d_v] -= contrib[j]
+        return dq, dkv, ds
+
+    monkeypatch.setattr(oracle, "sparse_topk_attention_backward", key_only)
+    _assert_caught(["sparse_bwd_finite_differences", "sparse_bwd_library_autograd"])
+
+
+def test_sparse_duplicates_collapsed_caught(monkeypatch):
+    """A scatter that overwrites instead of adding loses a duplicated index's second slot."""
+    def assign(n_rows, idx, rows):
+        y = np.zeros((n_rows, rows.shape[1]))
+        for j, n in enumerate(idx):
+            if 0 <= int(n) < n_rows:
+                y[int(n)] = rows[j]
+        return y
+
+    monkeypatch.setattr(OA, "scatter_add_rows", assign)
+    _assert_caught(["sparse_bwd_finite_differences"])
