@@ -481,15 +481,14 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
     return dq, sum_kv_groups(dK, g), sum_kv_groups(dV, g), dsk
 
 
-def scatter_add_rows(n_rows: int, idx: Sequence[int], rows: np.ndarray) -> np.ndarray:
-    """Adjoint of ``gather_rows``: y[n] = sum of rows[j] over the slots j with idx[j] == n
-    (slots whose index is outside [0, n_rows) contribute nothing, as they were skipped)."""
-    y = np.zeros((n_rows, rows.shape[1]))
+def scatter_add_rows(y: np.ndarray, idx: Sequence[int], rows: np.ndarray) -> None:
+    """Adjoint of ``gather_rows``, accumulated into ``y``: y[n] += rows[j] for every slot j
+    with idx[j] == n, in slot order (slots whose index is outside [0, len(y)) contribute
+    nothing, as they were skipped)."""
     for j, n in enumerate(idx):
         n = int(n)
-        if 0 <= n < n_rows:
+        if 0 <= n < y.shape[0]:
             y[n] += rows[j]
-    return y
 
 
 def sparse_topk_attention_backward(q, kv, idx, dout, *, d_v: int, scale: float, sinks=None):
@@ -536,7 +535,7 @@ def sparse_topk_attention_backward(q, kv, idx, dout, *, d_v: int, scale: float, 
         dq[s] = scale * (dS @ G)
         dG = scale * (dS.T @ q[s])
         dG[:, :d_v] += P.T @ dO
-        dkv += scatter_add_rows(N, keep, dG)
+        scatter_add_rows(dkv, keep, dG)
         if sk is not None:
             D = (dO * O).sum(axis=1)
             fin = np.isfinite(lse)

@@ -94,12 +94,13 @@ def test_sparse_value_role_dropped_caught(monkeypatch):
 
 def test_sparse_duplicates_collapsed_caught(monkeypatch):
     """A scatter that overwrites instead of adding loses a duplicated index's second slot."""
-    def assign(n_rows, idx, rows):
-        y = np.zeros((n_rows, rows.shape[1]))
+    def assign(y, idx, rows):
+        seen = {}
         for j, n in enumerate(idx):
-            if 0 <= int(n) < n_rows:
-                y[int(n)] = rows[j]
-        return y
+            if 0 <= int(n) < y.shape[0]:
+                seen[int(n)] = rows[j]       # the last slot wins: duplicates collapse
+        for n, r in seen.items():
+            y[n] += r
 
     monkeypatch.setattr(OA, "scatter_add_rows", assign)
     _assert_caught(["sparse_bwd_finite_differences"])
