@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -102,12 +102,33 @@ class AttnDenseBwdArgs(ctypes.Structure):
     ]
 
 
+class AttnSparseBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Hq", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_ss", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("kv", ctypes.c_void_p), ("kv_sn", ctypes.c_int64),
+        ("indices", ctypes.c_void_p), ("idx_ss", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_ss", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("dout", ctypes.c_void_p), ("do_ss", ctypes.c_int64), ("do_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dq_ss", ctypes.c_int64), ("dq_sh", ctypes.c_int64),
+        ("dkv", ctypes.c_void_p), ("dkv_sn", ctypes.c_int64),
+        ("dsinks", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = (
     "attn_abi_version", "attn_fwd_dense", "attn_fwd_sparse_topk", "attn_plan_dense",
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
-    "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen",
+    "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen", "attn_bwd_sparse_topk",
+    "attn_bwd_sparse_workspace_bytes",
 )
 ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
 KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
@@ -198,6 +219,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_qkv_workspace_bytes.restype = ctypes.c_int64
     lib.attn_fwd_varlen.argtypes = [ctypes.POINTER(AttnVarlenArgs), ctypes.c_void_p]
     lib.attn_fwd_varlen.restype = ctypes.c_int
+    lib.attn_bwd_sparse_topk.argtypes = [ctypes.POINTER(AttnSparseBwdArgs), ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p]
+    lib.attn_bwd_sparse_topk.restype = ctypes.c_int
+    lib.attn_bwd_sparse_workspace_bytes.argtypes = [ctypes.POINTER(AttnSparseBwdArgs)]
+    lib.attn_bwd_sparse_workspace_bytes.restype = ctypes.c_int64
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -445,6 +471,62 @@ def sparse_topk(q, kv, idx, *, d_v: Optional[int] = None, scale: Optional[float]
     a = sparse_args(q, kv, idx, out, lse, d_v=d_v, scale=scale, sinks=sinks)
     _check(lib.attn_fwd_sparse_topk(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
+
+
+def sparse_backward(q, kv, idx, out, dout, lse, *, d_v: Optional[int] = None, scale: Optional[float] = None,
+                    sinks=None, dq=None, dkv=None, dsinks=None, workspace=None, stream=None):
+    """Sparse top-k backward: q [Sq,Hq,d], kv [N,d], idx [Sq,topk] int32 as in
+    :func:`sparse_topk`, the forward's out and lse, dout = dL/dO. Returns
+    (dq [Sq,Hq,d] bf16, dkv [N,d] fp32 -- the pool's gradient, key and value
+    roles summed, overwritten --, dsinks [Hq] fp32 or None). ``workspace``: a
+    uint8 device tensor of at least the library's workspace size (allocated here
+    when None). Launches on ``stream`` and does not synchronise."""
+    import torch
+
+    lib = load_library()
+    Sq, Hq, dqk = q.shape
+    N = kv.shape[0]
+    d_v = dqk if d_v is None else d_v
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if idx.dtype != torch.int32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "indices must be int32")
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dkv is None:
+        dkv = torch.empty((N, dqk), dtype=torch.float32, device=q.device)
+    if sinks is not None and dsinks is None:
+        dsinks = torch.empty_like(sinks)
+    for name, t in (("q", q), ("kv", kv), ("indices", idx), ("out", out), ("dout", dout), ("dq", dq), ("dkv", dkv)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    if dkv.dtype != torch.float32 or tuple(dkv.shape) != (N, dqk):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "dkv must be fp32 [N, d_qk]")
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [Sq, Hq]")
+    a = AttnSparseBwdArgs()
+    a.struct_size = ctypes.sizeof(AttnSparseBwdArgs)
+    a.dtype = _dtype_code(q)
+    a.Sq, a.Hq, a.N, a.d_qk, a.d_v, a.topk = Sq, Hq, N, dqk, d_v, idx.shape[1]
+    a.scale = float(scale)
+    a.q, (a.q_ss, a.q_sh) = q.data_ptr(), q.stride()[:2]
+    a.kv, a.kv_sn = kv.data_ptr(), kv.stride(0)
+    a.indices, a.idx_ss = idx.data_ptr(), idx.stride(0)
+    a.out, (a.o_ss, a.o_sh) = out.data_ptr(), out.stride()[:2]
+    a.dout, (a.do_ss, a.do_sh) = dout.data_ptr(), dout.stride()[:2]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.dq, (a.dq_ss, a.dq_sh) = dq.data_ptr(), dq.stride()[:2]
+    a.dkv, a.dkv_sn = dkv.data_ptr(), dkv.stride(0)
+    a.dsinks = dsinks.data_ptr() if dsinks is not None else None
+    need = int(lib.attn_bwd_sparse_workspace_bytes(ctypes.byref(a)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_bwd_sparse_topk(ctypes.byref(a), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                    ctypes.c_void_p(_stream_handle(stream))))
+    return dq, dkv, dsinks
 
 
 _FAKE_PTR = 1 << 12  # never dereferenced: plans are computed on the host only

@@ -51,9 +51,13 @@ constexpr int kBwdSlot0 = kMergeSlot - 3;
 constexpr const char* kQkvPaths[] = {"dense_qkv_q8_0_d128", "dense_qkv_q4_0_d128", "dense_qkv_q8_0_d256",
                                      "dense_qkv_q4_0_d256"};
 constexpr int kQkvSlot0 = kBwdSlot0 - 4;
+// and the sparse backward below those
+constexpr const char* kSpBwdPath = "sparse_bwd_bf16_d512";
+constexpr int kSpBwdSlot = kQkvSlot0 - 1;
 
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
+  if (std::strcmp(path, kSpBwdPath) == 0) return kSpBwdSlot;
   for (int i = 0; i < 4; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
@@ -495,7 +499,7 @@ const char* attn_last_error(void) { return g_last_error.c_str(); }
 // ---------------------------------------------------------------- dense backward
 namespace {
 
-int bwd_path(int d_qk, int d_v) {
+static int bwd_path(int d_qk, int d_v) {
   if (d_qk == 64 && d_v == 64) return 0;
   if (d_qk == 128 && d_v == 128) return 1;
   if (d_qk == 192 && d_v == 128) return 2;
@@ -503,7 +507,7 @@ int bwd_path(int d_qk, int d_v) {
 }
 
 // sizes, dtype and head dims only (what the workspace size depends on)
-attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
+static attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
   if (a->struct_size != sizeof(attn_dense_bwd_args))
     return fail(ATTN_ABI_MISMATCH, "attn_dense_bwd_args.struct_size = %u, library expects %zu", a->struct_size,
@@ -526,7 +530,7 @@ attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
   return ATTN_OK;
 }
 
-attn_status validate_bwd(const attn_dense_bwd_args* a) {
+static attn_status validate_bwd(const attn_dense_bwd_args* a) {
   const attn_status s = validate_bwd_shape(a);
   if (s != ATTN_OK) return s;
   if (a->Tq > 0 && (!a->q || !a->out || !a->dout || !a->lse || !a->dq))
@@ -552,7 +556,7 @@ attn_status validate_bwd(const attn_dense_bwd_args* a) {
   return ATTN_OK;
 }
 
-int64_t bwd_workspace(const attn_dense_bwd_args* a) {
+static int64_t bwd_workspace(const attn_dense_bwd_args* a) {
   const int64_t rows = (int64_t)a->B * a->H * a->Tq;
   return (rows * 4 + 255) / 256 * 256;
 }
@@ -601,16 +605,95 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------- sparse top-k backward
+namespace {
+
+static attn_status validate_sparse_bwd_shape(const attn_sparse_bwd_args* a) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_sparse_bwd_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_sparse_bwd_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_sparse_bwd_args));
+  if (a->dtype != ATTN_BF16) return fail(ATTN_UNSUPPORTED, "the sparse backward is compiled for bf16 only");
+  if (a->Sq < 0 || a->Hq < 1 || a->N < 1 || a->topk < 0) return fail(ATTN_INVALID_ARGUMENT, "bad Sq/Hq/N/topk");
+  if (a->d_qk != 512 || a->d_v != 512 || a->Hq != 64)
+    return fail(ATTN_UNSUPPORTED, "the sparse backward is compiled for d_qk = d_v = 512 and Hq = 64 (got %d, %d, %d)",
+                a->d_qk, a->d_v, a->Hq);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  return ATTN_OK;
+}
+
+static int64_t sparse_bwd_workspace(const attn_sparse_bwd_args* a) {
+  const int64_t b = (int64_t)a->Sq * a->Hq * 4;
+  return b == 0 ? 0 : (b + 255) / 256 * 256;
+}
+
+}  // namespace
+
+int64_t attn_bwd_sparse_workspace_bytes(const attn_sparse_bwd_args* a) {
+  g_last_error.clear();
+  if (validate_sparse_bwd_shape(a) != ATTN_OK) return -1;
+  return sparse_bwd_workspace(a);
+}
+
+attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  g_last_error.clear();
+  attn_status st = validate_sparse_bwd_shape(a);
+  if (st != ATTN_OK) return st;
+  if (!a->kv || !a->dkv) return fail(ATTN_INVALID_ARGUMENT, "kv and dkv must be non-NULL");
+  if (a->Sq > 0 && (!a->q || !a->out || !a->dout || !a->lse || !a->dq || (a->topk > 0 && !a->indices)))
+    return fail(ATTN_INVALID_ARGUMENT, "q, out, dout, lse, dq (and indices when topk > 0) must be non-NULL");
+  if (a->dsinks && !a->sinks) return fail(ATTN_INVALID_ARGUMENT, "dsinks needs sinks");
+  if (!aligned16(a->q) || !aligned16(a->kv) || !aligned16(a->out) || !aligned16(a->dout) || !aligned16(a->lse) ||
+      !aligned16(a->dq) || !aligned16(a->dkv) || ((uintptr_t)a->indices & 3u) || !aligned16(a->sinks) ||
+      ((uintptr_t)a->dsinks & 3u))
+    return fail(ATTN_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (indices, dsinks 4-byte)");
+  const int64_t strides[] = {a->q_ss, a->q_sh, a->kv_sn, a->o_ss, a->o_sh, a->do_ss, a->do_sh, a->dq_ss, a->dq_sh};
+  for (int64_t x : strides)
+    if (x < 0 || x % 8 != 0)
+      return fail(ATTN_INVALID_ARGUMENT, "strides must be >= 0 and multiples of 8 elements");
+  if (a->kv_sn < a->d_qk) return fail(ATTN_INVALID_ARGUMENT, "kv row stride smaller than d_qk");
+  if (a->dkv_sn < a->d_qk || a->dkv_sn % 4 != 0)
+    return fail(ATTN_INVALID_ARGUMENT, "dkv row stride must be >= d_qk and a multiple of 4");
+  if (a->idx_ss < a->topk) return fail(ATTN_INVALID_ARGUMENT, "index row stride smaller than topk");
+  const int64_t need = sparse_bwd_workspace(a);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_INVALID_ARGUMENT, "the sparse backward needs a workspace of %lld bytes, got %lld",
+                (long long)need, (long long)(workspace ? workspace_bytes : 0));
+  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  attn::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->kv; p.v = a->kv; p.out = a->out; p.dout = a->dout; p.lse = a->lse; p.sinks = a->sinks;
+  p.dq = a->dq; p.dsinks = a->dsinks;
+  p.D = static_cast<float*>(workspace);
+  p.q_sb = a->q_ss; p.q_sh = a->q_sh;
+  p.k_st = a->kv_sn; p.v_st = a->kv_sn;
+  p.o_sb = a->o_ss; p.o_sh = a->o_sh;
+  p.do_sb = a->do_ss; p.do_sh = a->do_sh;
+  p.dq_sb = a->dq_ss; p.dq_sh = a->dq_sh;
+  p.B = a->Sq; p.H = a->Hq; p.Hkv = 1; p.Tq = 1; p.Tk = a->topk; p.g = a->Hq;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  p.idx = a->indices; p.idx_ss = a->idx_ss;
+  p.npool = a->N; p.topk = a->topk;
+  p.dkv = a->dkv; p.dkv_sn = a->dkv_sn;
+  const int err = attn::launch_bwd_sparse(p, stream);
+  if (err != 0)
+    return fail(ATTN_HIP_ERROR, "launch of the sparse backward failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kSpBwdSlot, kSpBwdPath);
+  return ATTN_OK;
+}
+
 // ---------------------------------------------------------------- quantized K/V decode
 namespace {
 
-int qkv_path(int fmt, int d) {
+static int qkv_path(int fmt, int d) {
   const int f = fmt == ATTN_KV_Q8_0 ? 0 : (fmt == ATTN_KV_Q4_0 ? 1 : -1);
   if (f < 0 || d != 128) return -1;
   return f;
 }
 
-attn_status validate_qkv_shape(const attn_qkv_args* a) {
+static attn_status validate_qkv_shape(const attn_qkv_args* a) {
   if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
   if (a->struct_size != sizeof(attn_qkv_args))
     return fail(ATTN_ABI_MISMATCH, "attn_qkv_args.struct_size = %u, library expects %zu", a->struct_size,
@@ -626,9 +709,9 @@ attn_status validate_qkv_shape(const attn_qkv_args* a) {
   return ATTN_OK;
 }
 
-int64_t qkv_row_bytes(const attn_qkv_args* a) { return (int64_t)a->d / 32 * (a->kv_format == ATTN_KV_Q8_0 ? 34 : 18); }
+static int64_t qkv_row_bytes(const attn_qkv_args* a) { return (int64_t)a->d / 32 * (a->kv_format == ATTN_KV_Q8_0 ? 34 : 18); }
 
-attn_status validate_qkv(const attn_qkv_args* a) {
+static attn_status validate_qkv(const attn_qkv_args* a) {
   const attn_status s = validate_qkv_shape(a);
   if (s != ATTN_OK) return s;
   if (a->Tq > 0 && (!a->q || !a->out || !a->lse)) return fail(ATTN_INVALID_ARGUMENT, "q, out, lse must be non-NULL");
@@ -656,7 +739,7 @@ struct QkvPlan {
   int64_t bytes;
 };
 
-QkvPlan plan_qkv(const attn_qkv_args* a, int n_req) {
+static QkvPlan plan_qkv(const attn_qkv_args* a, int n_req) {
   QkvPlan pl{1, a->Tk, (int)(((int64_t)(a->H / a->Hkv) * a->Tq + 31) / 32), 0};
   const int nblocks = (a->Tk + 31) / 32;
   if (nblocks <= 1 || a->Tq == 0) return pl;

@@ -35,6 +35,7 @@
 // Scores and probabilities never leave the CU; the only workspace is D.
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "attn_params.h"
@@ -761,6 +762,231 @@ int launch_bwd_cfg(const BwdParams& p, void* stream) {
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// 5. Sparse top-k backward, d_qk = d_v = 512 (the values are the pool rows
+//    themselves), 64 heads. For query s with gathered rows X (32 per step):
+//
+//      S^T = X q^T, dP^T = X dO^T         (keys x heads)
+//      P = exp(scale S - lse), dS = P (dP - D)
+//      dq^T += X^T dS^T                   (scaled at the end)
+//      C = [scale dS^T | P^T] [q ; dO]    (keys x columns): the pool rows'
+//                                          gradient, key role plus value role
+//      dkv[idx] += C                      (fp32 atomics)
+//
+//    One workgroup per (query, half of the 512 columns), four waves; wave
+//    (hg, sl) owns heads 32 hg .. 32 hg + 31. S and dP need all 512 columns:
+//    each wave multiplies over columns 256 sl .. 256 sl + 255 and adds its
+//    partner's (same heads, other columns) partial through LDS. The two
+//    halves of a query repeat S and dP but each adds only its own columns of
+//    C, so every (query, slot) adds one 512-column row once. The half's
+//    columns of [q ; dO] (128 rows) stay in LDS for the C product, whose B
+//    operand comes from transposed reads; its A operand [scale dS | P] is
+//    staged key-major in LDS with the rows of each 16-row group permuted into
+//    the order the transposed reads deliver ({0-3, 8-11} | {4-7, 12-15}).
+//    The atomics of step j are issued at the start of step j + 1, so that
+//    the wait for the next rows never waits on them.
+// ---------------------------------------------------------------------------
+constexpr int kSpD = 512, kSpH = 64, kSpBN = 32;
+
+__global__ void __launch_bounds__(256) bwd_zero_rows_kernel(float* y, int64_t rows, int cols, int64_t st) {
+  const int64_t per_row = cols / 4, n = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, c = i % per_row;
+    *reinterpret_cast<f32x4*>(y + r * st + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_sparse_kernel(const BwdParams p) {
+  constexpr int HD = kSpD / 2;                       // columns of one half
+  constexpr int CPX = kSpD / 8, CPW = HD / 8, CPY = 2 * kSpH / 8;
+  constexpr int WR = 2 * kSpH;                       // rows of [q ; dO]
+  constexpr int X_BYTES = kSpBN * kSpD * 2;          // gathered rows
+  constexpr int W_BYTES = WR * HD * 2;               // [q ; dO], this half's columns
+  constexpr int XB_BYTES = 4 * 2 * 16 * 64 * 4;      // partial S / dP exchange
+  constexpr int Y_BYTES = kSpBN * WR * 2;            // [scale dS | P], key-major
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[X_BYTES + W_BYTES + XB_BYTES + Y_BYTES + 2 * kSpBN * 4];
+  bf16_t* const xt = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* const wt = reinterpret_cast<bf16_t*>(smem + X_BYTES);
+  float* const xb = reinterpret_cast<float*>(smem + X_BYTES + W_BYTES);
+  bf16_t* const yt = reinterpret_cast<bf16_t*>(smem + X_BYTES + W_BYTES + XB_BYTES);
+  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + X_BYTES + W_BYTES + XB_BYTES + Y_BYTES);
+
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 1, sl = wave >> 1;
+  // both halves of a query run on one XCD, next to each other in dispatch order
+  const int bi = blockIdx.x;
+  const int s = (bi >> 4) * 8 + (bi & 7), e = (bi >> 3) & 1;
+  if (s >= p.B) return;
+  const int hd = hg * 32 + lq;  // this lane's head
+  const int64_t lrow = (int64_t)s * p.H + hd;
+  const float lse = p.lse[lrow];
+  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  const float Dr = p.D[lrow];
+  const bf16_t* const qs = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)s * p.q_sb;
+  const bf16_t* const ds = reinterpret_cast<const bf16_t*>(p.dout) + (int64_t)s * p.do_sb;
+
+  // B operands of S^T and dP^T: this lane's head, columns 256 sl + 16 k + 8 lh ..
+  bf16x8 qf[16], dof[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    qf[k] = *reinterpret_cast<const bf16x8*>(qs + (int64_t)hd * p.q_sh + sl * 256 + k * 16 + lh * 8);
+    dof[k] = *reinterpret_cast<const bf16x8*>(ds + (int64_t)hd * p.do_sh + sl * 256 + k * 16 + lh * 8);
+  }
+  // [q ; dO] restricted to this half's columns, row-major (swizzled) in LDS
+#pragma unroll
+  for (int m = 0; m < WR * CPW / 256; ++m) {
+    const int slot = m * 256 + tid, r = slot / CPW, c = slot % CPW;
+    const bf16_t* src = r < kSpH ? qs + (int64_t)r * p.q_sh : ds + (int64_t)(r - kSpH) * p.do_sh;
+    *reinterpret_cast<u32x4*>(wt + chunk_at<CPW>(r, c)) = *reinterpret_cast<const u32x4*>(src + e * HD + c * 8);
+  }
+
+  const int32_t* const ixrow = p.idx + (int64_t)s * p.idx_ss;
+  const bf16_t* const pool = reinterpret_cast<const bf16_t*>(p.k);
+  const uint32_t xt_s = lds_u32(xt);
+  const int nblk = (p.topk + kSpBN - 1) / kSpBN;
+  // Block j: lane k (< 32) reads slot j*32 + k; the slots are recorded (-1
+  // for a slot past topk or an index outside the pool) and the 32 rows are
+  // gathered into LDS, 8 per wave, one 1 KiB row per wave instruction
+  // (skipped slots load row 0, never used). Returns the skipped-slot mask.
+  auto issue = [&](int j) -> uint32_t {
+    const int kk = j * kSpBN + lq;
+    const int ix = kk < p.topk ? ixrow[kk] : -1;
+    const bool skip = ix < 0 || ix >= p.npool;
+    if (wave == 0 && lane < kSpBN) sidx[(j & 1) * kSpBN + lane] = skip ? -1 : ix;
+    const uint32_t lane16 = (uint32_t)lane << 4;
+#pragma unroll
+    for (int m = 0; m < kSpBN / 4; ++m) {
+      const int r = wave * (kSpBN / 4) + m;
+      const int rix = __builtin_amdgcn_readlane(ix, r);
+      const int rowp = (rix >= 0 && rix < p.npool) ? rix : 0;
+      dma16(uniform_ptr(pool + (int64_t)rowp * p.k_st), lane16 ^ (uint32_t)(swz<CPX>(r) << 4), xt_s + 1024u * r);
+    }
+    return (uint32_t)__ballot(skip);
+  };
+
+  f32x16 dq[4], C[2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[t][i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) C[t][i] = 0.f;
+
+  // C element i of this lane: key lh*4 + 8*(i/4) + i%4, column (2 wave + t)*32 + lq of the half
+  auto flush = [&](int j) {
+    const int32_t* sx = sidx + (j & 1) * kSpBN;
+    float* const base = p.dkv + e * HD + (2 * wave) * 32 + lq;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n = sx[lh * 4 + 8 * (i >> 2) + (i & 3)];
+      if (n >= 0) {
+        float* const row = base + (int64_t)n * p.dkv_sn;
+        unsafeAtomicAdd(row, C[0][i]);
+        unsafeAtomicAdd(row + 32, C[1][i]);
+      }
+    }
+  };
+
+  uint32_t skip_cur = 0;
+  if (nblk > 0) skip_cur = issue(0);
+  for (int j = 0; j < nblk; ++j) {
+    wait_all_loads();
+    barrier();  // rows and slots of block j (and [q ; dO]) visible to every wave
+    if (j > 0) flush(j - 1);
+    // partial S^T, dP^T over this wave's 256 columns (X is the A operand of both)
+    f32x16 S, dP;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bf16x8 a = row_frag<CPX>(xt, lq, sl * 16 + k, lh);
+      S = mfma32(a, qf[k], S);
+      dP = mfma32(a, dof[k], dP);
+    }
+    // add the partner's partials (same heads, the other 256 columns)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      *reinterpret_cast<f32x4*>(xb + (((wave * 2 + 0) * 4 + g4) * 64 + lane) * 4) =
+          f32x4{S[g4 * 4], S[g4 * 4 + 1], S[g4 * 4 + 2], S[g4 * 4 + 3]};
+      *reinterpret_cast<f32x4*>(xb + (((wave * 2 + 1) * 4 + g4) * 64 + lane) * 4) =
+          f32x4{dP[g4 * 4], dP[g4 * 4 + 1], dP[g4 * 4 + 2], dP[g4 * 4 + 3]};
+    }
+    barrier();
+    const int pw = wave ^ 2;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(xb + (((pw * 2 + 0) * 4 + g4) * 64 + lane) * 4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(xb + (((pw * 2 + 1) * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        S[g4 * 4 + q4] += a[q4];
+        dP[g4 * 4 + q4] += b[q4];
+      }
+    }
+    // probabilities and dS (skipped slots: P = 0)
+    float Pv[16], dSv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = lh * 4 + 8 * (i >> 2) + (i & 3);
+      const float pr = ((skip_cur >> key) & 1u) ? 0.f : __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -l2));
+      Pv[i] = pr;
+      dSv[i] = pr * (dP[i] - Dr);
+    }
+    // dq^T += X^T dS^T on this wave's four column tiles of the half
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 b = pack8(dSv + ks * 8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dq[t] = mfma32(tr_frag<CPX>(xt, ks * 16, e * HD + (4 * sl + t) * 32, lane), b, dq[t]);
+    }
+    // stage [scale dS | P] key-major: wave sl = 0 writes row hd (scale dS),
+    // sl = 1 row 64 + hd (P), at the permuted position of its 16-row group
+    {
+      const int r = sl == 0 ? hd : kSpH + hd;
+      const int q16 = r & 15, pos = (q16 & 3) | ((q16 & 4) << 1) | ((q16 & 8) >> 1);
+      const int c = 2 * (r >> 4) + (pos >> 3);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = lh * 4 + 8 * (i >> 2) + (i & 3);
+        const float val = sl == 0 ? p.scale * dSv[i] : Pv[i];
+        yt[chunk_at<CPY>(key, c) + (pos & 7)] = (bf16_t)val;
+      }
+    }
+    barrier();  // staging complete; the gathered rows and the exchange are free
+    if (j + 1 < nblk) skip_cur = issue(j + 1);
+    // C = [scale dS | P] [q ; dO] on this wave's two column tiles of the half
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) C[t][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < WR / 16; ++ks) {
+      const bf16x8 a = row_frag<CPY>(yt, lq, ks, lh);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) C[t] = mfma32(a, tr_frag<CPW>(wt, ks * 16, (2 * wave + t) * 32, lane), C[t]);
+    }
+  }
+  if (nblk > 0) flush(nblk - 1);
+
+  bf16_t* const qo = reinterpret_cast<bf16_t*>(p.dq) + (int64_t)s * p.dq_sb + (int64_t)hd * p.dq_sh;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = e * HD + (4 * sl + t) * 32 + g4 * 8 + lh * 4;
+      *reinterpret_cast<u32x2*>(qo + d) = u32x2{pack2(dq[t][g4 * 4] * p.scale, dq[t][g4 * 4 + 1] * p.scale),
+                                                pack2(dq[t][g4 * 4 + 2] * p.scale, dq[t][g4 * 4 + 3] * p.scale)};
+    }
+}
+
 }  // namespace
 
 bool bwd_supported(int d_qk, int d_v) {
@@ -772,6 +998,29 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
   if (d_qk == 128 && d_v == 128) return launch_bwd_cfg<128, 128>(p, stream);
   if (d_qk == 192 && d_v == 128) return launch_bwd_cfg<192, 128>(p, stream);
   return -1;
+}
+
+int launch_bwd_sparse(const BwdParams& p, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n4 = (int64_t)p.npool * (kSpD / 4);
+  if (n4 > 0) {
+    const int64_t grid = std::min<int64_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(bwd_zero_rows_kernel, dim3((unsigned)grid), dim3(256), 0, st, p.dkv, (int64_t)p.npool, kSpD,
+                       p.dkv_sn);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  const int64_t R = (int64_t)p.B * p.H;
+  if (R > 0) {
+    hipLaunchKernelGGL(bwd_dot_kernel<kSpD>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+    if (p.sinks != nullptr && p.dsinks != nullptr) {
+      hipLaunchKernelGGL(bwd_dsink_kernel, dim3(p.H), dim3(256), 0, st, p);
+      if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+    }
+    hipLaunchKernelGGL(bwd_sparse_kernel, dim3((unsigned)(((p.B + 7) / 8) * 16)), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  return 0;
 }
 
 }  // namespace attn

@@ -102,6 +102,14 @@ struct BwdParams {
   int32_t win_left, win_right;  // sliding window as in the forward (-1: unbounded side)
   float scale;
   float c;                // scale * log2(e)
+  // sparse top-k (launch_bwd_sparse): q, out, dout, dq are [Sq, Hq, 512] with
+  // strides (q_sb, q_sh) etc., the pool is k with row stride k_st (values =
+  // its first 512 columns), lse / D are [Sq, Hq] (B = Sq, H = Hq, Tq = 1)
+  const int32_t* idx;     // [Sq, topk], row stride idx_ss
+  int64_t idx_ss;
+  int32_t npool, topk;
+  float* dkv;             // pool gradient, fp32 [npool, 512], row stride dkv_sn (overwritten)
+  int64_t dkv_sn;
 };
 
 // Launches the whole backward (row dots, sink gradients, dK/dV, dQ) on
@@ -110,6 +118,9 @@ struct BwdParams {
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
+// Sparse top-k backward (d_qk = d_v = 512, 64 heads): zeroes dkv, then row
+// dots, sink gradients and the gradient kernel. 0 or a hipError_t.
+int launch_bwd_sparse(const BwdParams& p, void* stream);
 
 // Decode forward over a quantized K/V cache (q8_0 / q4_0 blocks, bf16 q and
 // out): the keys of one (b, kv head) and up to 32 folded query rows per

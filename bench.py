@@ -355,6 +355,52 @@ def measure_bwd(n: int, steps: int, warmup: int) -> dict:
             "roofline": rl, "verdict": "Measured"}
 
 
+def sparse_bwd_flops(n: int) -> int:
+    """Algorithmic flops of the sparse backward: five products per (query, head, slot)
+    (S recomputed, dP, dq, the key-role and value-role pool gradients)."""
+    import synth
+
+    s = synth.spec(n)
+    return 2 * s.Sq * s.Hq * s.topk * (3 * s.d_qk + 2 * s.d_v)
+
+
+def measure_sparse_bwd(steps: int, warmup: int) -> dict:
+    """The sparse top-k backward on workload 5 (after one forward for out and lse);
+    dL/dO is the seeded synthetic gradient. All four launches are timed."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(5)
+    inp = synth.make(5)
+    q, kv, idx = inp["q"].cuda(), inp["kv"].cuda(), inp["idx"].cuda()
+    out, lse = A.sparse_topk(q, kv, idx, d_v=s.d_v, scale=s.scale)
+    dout = synth.make_sparse_dout(s).cuda()
+    dq = torch.empty_like(q)
+    dkv = torch.empty((s.N, s.d_qk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(s.Sq * s.Hq * 4 + 256, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        A.sparse_backward(q, kv, idx, out, dout, lse, d_v=s.d_v, scale=s.scale, dq=dq, dkv=dkv, workspace=ws)
+
+    path = "sparse_bwd_bf16_d512"
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != t["calls"]:
+        raise RuntimeError(f"NotEngaged: expected {t['calls']} launches of {path}, saw {A.dispatch_count(path)}")
+    fl = sparse_bwd_flops(5)
+    ach = fl / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    log(f"[bench] sparse backward {describe(5)} | path {path} | {t['kernel_ms_mean']:.4f} ms per backward "
+        f"(4 launches) | {rl['achieved']} TFLOP/s = {100 * rl['frac']:.1f}% of peak")
+    return {"row": "sparse top-k backward (attn_bwd_sparse_topk)", "workload": describe(5), "path": path,
+            "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured"}
+
+
 def measure_qkv(fmt: str, steps: int, warmup: int) -> dict:
     """Multi-sequence decode over a quantized cache (synth.QUANT_DECODE shape in
     ``fmt``), memory bound: bytes = q + the cache's raw K/V bytes + out + lse. The
@@ -729,6 +775,9 @@ def main():
         for m in (2, 3, 7):
             next_rows.append(measure_bwd(m, st, wu))
             torch.cuda.empty_cache()
+        # the sparse backward
+        next_rows.append(measure_sparse_bwd(max(3, st // 4), 1))
+        torch.cuda.empty_cache()
         # decode over quantized caches
         for fmt in ("q8_0", "q4_0"):
             next_rows.append(measure_qkv(fmt, st, wu))

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 8
+#define ATTN_ABI_VERSION 9
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -322,6 +322,60 @@ int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a);
  * Launches are recorded under the dispatch path "dense_bwd_bf16_d<d_qk>" (with
  * "_v<d_v>" when d_v differs). */
 attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Sparse top-k backward: the gradients of attn_fwd_sparse_topk with respect
+ * to q, the shared pool and the sinks, from the forward's inputs, its out and
+ * lse, and dout = dL/dO (the training counterpart that the rank-1 backward of
+ * the pages names beside the dense one; the TensorRT-LLM page, "Description",
+ * fixes the forward's shape). With P = exp(scale * q.kv[idx] - lse) and
+ * V the pool rows' first d_v columns, the pool row n receives, summed over
+ * every (query, slot) whose index is n (a duplicated index twice):
+ *   scale * sum_h dS_h q_h  (key role)  +  sum_h P_h dO_h  (value role),
+ * with dS = P (dP - rowsum(dO * O)), dP = dO . v.
+ *
+ *   q, out, dout [Sq, Hq, d] bf16, element strides (q_ss, q_sh) etc.
+ *   kv [N, d] bf16 (row stride kv_sn), indices int32 [Sq, topk] (row
+ *        stride idx_ss; entries outside [0, N) are skipped as in the forward)
+ *   lse [Sq, Hq] fp32 (the forward's), sinks [Hq] fp32 or NULL
+ *   dq [Sq, Hq, d] bf16 (written; strides dq_ss, dq_sh)
+ *   dkv [N, d] fp32 (overwritten: zeroed, then every contribution added
+ *        with fp32 atomics, so the summation order, and the last bits, vary
+ *        from run to run); row stride dkv_sn, a multiple of 4
+ *   dsinks [Hq] fp32 or NULL (needs sinks)
+ *   Compiled: d_qk = d_v = 512, Hq = 64. Workspace: Sq*Hq*4 bytes
+ *   (attn_bwd_sparse_workspace_bytes), caller-owned, 16-byte aligned.
+ * Launches on `stream`: a fill of dkv, row dots, sink gradients, the
+ * gradient kernel (dispatch path "sparse_bwd_bf16_d512"). Errors as for
+ * attn_bwd_dense.
+ */
+typedef struct attn_sparse_bwd_args {
+  uint32_t struct_size; /* = sizeof(attn_sparse_bwd_args) */
+  int32_t dtype;        /* ATTN_BF16 */
+  int32_t Sq, Hq, N, d_qk, d_v, topk;
+  float scale;
+  const void* q;
+  int64_t q_ss, q_sh;
+  const void* kv;
+  int64_t kv_sn;
+  const int32_t* indices;
+  int64_t idx_ss;
+  const void* out;
+  int64_t o_ss, o_sh;
+  const void* dout;
+  int64_t do_ss, do_sh;
+  const float* lse;
+  const float* sinks;
+  void* dq;
+  int64_t dq_ss, dq_sh;
+  float* dkv;
+  int64_t dkv_sn;
+  float* dsinks;
+} attn_sparse_bwd_args;
+
+int64_t attn_bwd_sparse_workspace_bytes(const attn_sparse_bwd_args* a);
+attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace, int64_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Decode forward over a quantized K/V cache. llama.cpp's quantized-KV cache

@@ -261,6 +261,13 @@ def make_sparse(s: SparseSpec, *, seed: Optional[int] = None) -> dict:
     return {"q": q, "kv": kv, "idx": idx, "sinks": sinks}
 
 
+def make_sparse_dout(s: SparseSpec, *, seed: Optional[int] = None) -> torch.Tensor:
+    """dL/dO [Sq,Hq,d_v] for the sparse backward: its own generator seeded with
+    1000 + the workload's seed, one ``randn`` in fp32 cast to bf16."""
+    g = torch.Generator("cpu").manual_seed(1000 + (s.seed if seed is None else seed))
+    return torch.randn((s.Sq, s.Hq, s.d_v), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
 def make(n: int) -> dict:
     s = spec(n)
     return make_dense(s) if s.kind == "dense" else make_sparse(s)
