@@ -7,6 +7,7 @@ from .attention import (  # noqa: F401
     causal_visible,
     dense_attention,
     dense_attention_backward,
+    dense_attention_extras,
     dense_attention_tiled,
     dense_attention_two_part,
     dense_attention_varlen,

@@ -212,6 +212,40 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
     return out, lse
 
 
+def dense_attention_extras(q, k, *, scale: float, causal: bool, sinks=None, window: Tuple[int, int] = (-1, -1)):
+    """The two extra returns FA4 b19 added to its forward (pith-train page, "Issues
+    resolved" item 1: (out, lse) widened to (out, lse, p, row_max)), read as:
+
+      p       [B,H,Tq,Tk]  the softmax probabilities exp(S - lse) of the visible
+                           keys (0 where masked); the sink has no column, so with
+                           sinks a row sums to 1 - exp(sink - lse)
+      row_max [B,H,Tq]     the largest visible scaled score max_j S[t, j] (the
+                           sink is not a score; -inf for a row with no key)
+
+    with S = scale * q . K^T (repeat_kv, masks and lse as in ``dense_attention``).
+    """
+    q, k = _f64(q), _f64(k)
+    B, H, Tq, _ = q.shape
+    _, Hkv, Tk, _ = k.shape
+    g = H // Hkv
+    K = repeat_kv(k, g)
+    sk = None if sinks is None else _f64(sinks)
+    P = np.zeros((B, H, Tq, Tk))
+    row_max = np.full((B, H, Tq), NEG_INF)
+    ts = np.arange(Tq)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h] @ K[b, h].T)
+            if causal:
+                S = np.where(_causal_mask(ts, Tq, Tk), S, NEG_INF)
+            if window[0] >= 0 or window[1] >= 0:
+                S = np.where(_window_mask(ts, Tq, Tk, window[0], window[1]), S, NEG_INF)
+            P[b, h], _ = _softmax_rows(S, None if sk is None else float(sk[h]))
+            if Tk > 0:
+                row_max[b, h] = S.max(axis=1)
+    return P, row_max
+
+
 def dense_attention_two_part(q_nope, q_rope, k_nope, k_rope, v, *, scale: float, causal: bool, sinks=None,
                              window: Tuple[int, int] = (-1, -1)):
     """MLA's two-part rows (pith-train page, "Issues resolved" item 2: the model

@@ -102,3 +102,36 @@ def brute_two_part(qn, qr, kn, kr, v, scale, causal, sinks=None):
                 out[b][h][t] = o if o is not None else [0.0] * Dv
                 lse[b][h][t] = l
     return out, lse
+
+
+def brute_extras(q, k, scale, causal, sinks=None, window=(-1, -1)):
+    """Probabilities and row maxima by explicit loops: for each row, the visible
+    keys' scores by fsum, weight of key j = 1 / (sum_i exp(s_i - s_j) + exp(sink - s_j))
+    (0 for masked keys), row max = the largest visible score (-inf if none)."""
+    B, H, Tq = len(q), len(q[0]), len(q[0][0])
+    Hkv, Tk = len(k[0]), len(k[0][0])
+    g = H // Hkv
+    P = [[[[0.0] * Tk for _ in range(Tq)] for _ in range(H)] for _ in range(B)]
+    M = [[[-math.inf] * Tq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            kvh = h // g
+            for t in range(Tq):
+                keys, sc = [], []
+                for j in range(Tk):
+                    if causal and j > t + (Tk - Tq):
+                        continue
+                    if window[0] >= 0 and t + (Tk - Tq) - j > window[0]:
+                        continue
+                    if window[1] >= 0 and j - (t + (Tk - Tq)) > window[1]:
+                        continue
+                    keys.append(j)
+                    sc.append(scale * math.fsum(float(x) * float(y) for x, y in zip(q[b][h][t], k[b][kvh][j])))
+                for j, sj in zip(keys, sc):
+                    terms = [math.exp(si - sj) for si in sc]
+                    if sinks is not None:
+                        terms.append(math.exp(float(sinks[h]) - sj))
+                    P[b][h][t][j] = 1.0 / math.fsum(terms)
+                if sc:
+                    M[b][h][t] = max(sc)
+    return P, M

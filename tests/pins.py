@@ -18,7 +18,7 @@ from scipy.special import logsumexp
 
 import oracle
 from oracle import attention as OA
-from tests.brute import brute_dense, brute_sparse, brute_two_part
+from tests.brute import brute_dense, brute_extras, brute_sparse, brute_two_part
 
 TOL = 1e-12
 
@@ -371,6 +371,28 @@ def check_lse_logsumexp(orc=oracle):
     return worst
 
 
+def check_extras(orc=oracle):
+    """The extra returns (probabilities, row maxima): brute force, P . V = O of the
+    forward, and each row's probabilities plus the sink's share sum to 1."""
+    worst = 0.0
+    for i, (B, H, Hkv, Tq, Tk, d) in enumerate([(1, 4, 2, 5, 7, 3), (2, 2, 1, 6, 4, 4)]):
+        q, k = _rand((B, H, Tq, d), 970 + i, 0.8), _rand((B, Hkv, Tk, d), 971 + i, 0.8)
+        v = _rand((B, Hkv, Tk, 2), 972 + i)
+        sinks = _rand((H,), 973 + i)
+        for causal in (False, True):
+            for sk in (None, sinks):
+                for win in ((-1, -1), (1, 0)):
+                    P, M = orc.dense_attention_extras(q, k, scale=0.7, causal=causal, sinks=sk, window=win)
+                    bP, bM = brute_extras(q, k, 0.7, causal, sk, window=win)
+                    worst = max(worst, _err(P, bP), _err(M, bM))
+                    o, l = orc.dense_attention(q, k, v, scale=0.7, causal=causal, sinks=sk, window=win)
+                    worst = max(worst, _err(np.einsum("bhts,bhsd->bhtd", P, OA.repeat_kv(v, H // Hkv)), o))
+                    share = 0.0 if sk is None else np.exp(sk[None, :, None] - l)
+                    rows = P.sum(axis=-1) + np.where(np.isfinite(l), share, 0.0)
+                    worst = max(worst, _err(np.where(np.isfinite(l), rows, 1.0), 1.0))
+    return worst
+
+
 def check_two_part(orc=oracle):
     """MLA's two-part rows: brute force that sums the two partial dot products in
     separate loops (no concatenation), with a rope key per kv head and one shared
@@ -397,6 +419,7 @@ def check_two_part(orc=oracle):
 
 ALL_CHECKS = {
     "two_part": check_two_part,
+    "extras": check_extras,
     "window": check_window,
     "varlen": check_varlen,
     "brute_dense": check_brute_dense,

@@ -121,3 +121,30 @@ def test_two_part_rope_dropped_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "dense_attention_two_part", no_rope)
     _assert_caught(_caught(["two_part"]))
+
+
+def test_extras_sink_in_row_max_caught(monkeypatch):
+    """The row maximum taken over the scores and the sink."""
+    orig = OA.dense_attention_extras
+
+    def with_sink(q, k, *, sinks=None, **kw):
+        P, M = orig(q, k, sinks=sinks, **kw)
+        if sinks is not None:
+            M = np.maximum(M, np.asarray(sinks, dtype=np.float64)[None, :, None])
+        return P, M
+
+    monkeypatch.setattr(oracle, "dense_attention_extras", with_sink)
+    _assert_caught(_caught(["extras"]))
+
+
+def test_extras_rows_renormalised_caught(monkeypatch):
+    """Probabilities renormalised to sum to 1, dropping the sink's share."""
+    orig = OA.dense_attention_extras
+
+    def renorm(q, k, **kw):
+        P, M = orig(q, k, **kw)
+        tot = P.sum(axis=-1, keepdims=True)
+        return np.where(tot > 0, P / np.where(tot > 0, tot, 1.0), 0.0), M
+
+    monkeypatch.setattr(oracle, "dense_attention_extras", renorm)
+    _assert_caught(_caught(["extras"]))
