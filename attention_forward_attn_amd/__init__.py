@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -128,7 +128,7 @@ EXPORTS = (
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
     "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen", "attn_bwd_sparse_topk",
-    "attn_bwd_sparse_workspace_bytes",
+    "attn_bwd_sparse_workspace_bytes", "attn_fwd_dense_extras",
 )
 ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
 KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
@@ -224,6 +224,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_sparse_topk.restype = ctypes.c_int
     lib.attn_bwd_sparse_workspace_bytes.argtypes = [ctypes.POINTER(AttnSparseBwdArgs)]
     lib.attn_bwd_sparse_workspace_bytes.restype = ctypes.c_int64
+    lib.attn_fwd_dense_extras.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_dense_extras.restype = ctypes.c_int
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -350,6 +353,38 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
                    k_rope=k_rope)
     _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
+
+
+def dense_extras(q, k, v, out, lse, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
+                 window: Tuple[int, int] = (-1, -1), want_p: bool = True, want_row_max: bool = True, p=None,
+                 row_max=None, stream=None):
+    """The forward's extra returns after :func:`dense` on the same arguments (``lse``
+    is the forward's, read): (p [B,H,Tq,Tk] fp32 or None, row_max [B,H,Tq] fp32 or
+    None). p = exp(scale q.k - lse) on visible keys, 0 elsewhere; row_max = the
+    largest visible scaled score (-inf without keys)."""
+    import torch
+
+    lib = load_library()
+    B, H, Tq, dqk = q.shape
+    Tk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if want_p and p is None:
+        p = torch.empty((B, H, Tq, Tk), dtype=torch.float32, device=q.device)
+    if want_row_max and row_max is None:
+        row_max = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    if p is not None and (p.dtype != torch.float32 or tuple(p.shape) != (B, H, Tq, Tk) or p.stride(-1) != 1):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "p must be fp32 [B, H, Tq, Tk] with a contiguous last dim")
+    if row_max is not None and (row_max.dtype != torch.float32 or tuple(row_max.shape) != (B, H, Tq)
+                                or not row_max.is_contiguous()):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "row_max must be contiguous fp32 [B, H, Tq]")
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
+    ps = p.stride()[:3] if p is not None else (0, 0, 0)
+    _check(lib.attn_fwd_dense_extras(ctypes.byref(a), ctypes.c_void_p(p.data_ptr() if p is not None else None),
+                                     ps[0], ps[1], ps[2],
+                                     ctypes.c_void_p(row_max.data_ptr() if row_max is not None else None),
+                                     ctypes.c_void_p(_stream_handle(stream))))
+    return p, row_max
 
 
 def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,

@@ -54,10 +54,13 @@ constexpr int kQkvSlot0 = kBwdSlot0 - 4;
 // and the sparse backward below those
 constexpr const char* kSpBwdPath = "sparse_bwd_bf16_d512";
 constexpr int kSpBwdSlot = kQkvSlot0 - 1;
+constexpr const char* kExtrasPath = "dense_extras_bf16";
+constexpr int kExtrasSlot = kSpBwdSlot - 1;
 
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
   if (std::strcmp(path, kSpBwdPath) == 0) return kSpBwdSlot;
+  if (std::strcmp(path, kExtrasPath) == 0) return kExtrasSlot;
   for (int i = 0; i < 4; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
@@ -602,6 +605,36 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
     return fail(ATTN_HIP_ERROR, "launch of the dense backward failed: %s", hipGetErrorString((hipError_t)err));
   const int bp = bwd_path(a->d_qk, a->d_v);
   note_dispatch(kBwdSlot0 + bp, kBwdPaths[bp]);
+  return ATTN_OK;
+}
+
+// ---------------------------------------------------------------- the forward's extra returns
+attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p_out, int64_t p_sb, int64_t p_sh, int64_t p_st,
+                                  float* row_max, void* stream) {
+  g_last_error.clear();
+  DensePlan dp;
+  attn_status st = validate_dense(a, &dp);
+  if (st != ATTN_OK) return st;
+  if (a->dtype != ATTN_BF16 || a->rope_dim != 0 || !attn::extras_supported(a->d_qk))
+    return fail(ATTN_UNSUPPORTED, "the extra returns are compiled for bf16, d_qk in {64,128,192,256,512}, rope_dim 0");
+  if (((uintptr_t)p_out & 3u) || ((uintptr_t)row_max & 3u))
+    return fail(ATTN_INVALID_ARGUMENT, "p and row_max must be 4-byte aligned");
+  if (p_out && (p_sb < 0 || p_sh < 0 || p_st < 0 || (a->Tq > 1 && p_st < a->Tk)))
+    return fail(ATTN_INVALID_ARGUMENT, "p strides must be >= 0 with a token stride of at least Tk");
+  if (a->Tq == 0 || (!p_out && !row_max)) return ATTN_OK;
+  attn::ExtrasParams e;
+  std::memset(&e, 0, sizeof(e));
+  e.q = a->q; e.k = a->k; e.lse = a->lse; e.p = p_out; e.row_max = row_max;
+  e.q_sb = a->q_sb; e.q_sh = a->q_sh; e.q_st = a->q_st;
+  e.k_sb = a->k_sb; e.k_sh = a->k_sh; e.k_st = a->k_st;
+  e.p_sb = p_sb; e.p_sh = p_sh; e.p_st = p_st;
+  e.B = a->B; e.H = a->H; e.Hkv = a->Hkv; e.Tq = a->Tq; e.Tk = a->Tk; e.g = a->H / a->Hkv;
+  e.causal = a->causal; e.win_left = a->window_left; e.win_right = a->window_right;
+  e.scale = a->scale;
+  e.c = a->scale * 1.4426950408889634f;
+  const int err = attn::launch_extras(e, a->d_qk, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the extra returns failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kExtrasSlot, kExtrasPath);
   return ATTN_OK;
 }
 

@@ -987,6 +987,94 @@ bwd_sparse_kernel(const BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 6. The forward's extra returns (FA4's widened (out, lse, p, row_max)):
+//    p = exp(scale q.k - lse) for the visible keys (0 where masked) and the
+//    row maxima of the scaled scores, recomputed from q, k and the forward's
+//    lse in a second pass (the fused forward forms neither). One workgroup
+//    per 128 query rows of one (b, h); S = Q K^T with Q fragments in
+//    registers as the A operand and 32-key K tiles through LDS as the B
+//    operand, so that a lane holds one key of 16 rows and each store
+//    instruction writes 32 consecutive keys of two rows.
+// ---------------------------------------------------------------------------
+template <int DQK>
+__global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
+  constexpr int NW = 4, BM = 32 * NW, BN = 32, CPK = DQK / 8, KS = DQK / 16;
+  constexpr int KT_BYTES = BN * DQK * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * KT_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_rt = (p.Tq + BM - 1) / BM;
+  const int bh = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  const int b = bh / p.H, h = bh % p.H, kvh = h / p.g;
+  const int t0 = rt * BM + wave * 32;
+  bf16x8 qf[KS];
+  {
+    const int tq = min(t0 + lq, p.Tq - 1);
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)tq * p.q_st;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + lh * 8);
+  }
+  // C element r of this lane: row t0 + (r/4)*8 + lh*4 + r%4, key lq of the tile
+  const int off = p.Tk - p.Tq;
+  const int up = p.causal ? 0 : p.win_right;
+  const int64_t lbase = ((int64_t)b * p.H + h) * p.Tq;
+  float l2[16], rm[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
+    const float l = t < p.Tq ? p.lse[lbase + t] : -INFINITY;
+    l2[r] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    rm[r] = -INFINITY;
+  }
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  float* const pbase = p.p ? p.p + b * p.p_sb + h * p.p_sh : nullptr;
+  const uint32_t smem_s = lds_u32(smem);
+  const int nb = (p.Tk + BN - 1) / BN;
+  if (nb > 0) dma_tile<CPK, BN, NW>(kbase, p.k_st, 0, p.Tk - 1, smem_s, wave, lane);
+  for (int j = 0; j < nb; ++j) {
+    wait_all_loads();
+    barrier();
+    if (j + 1 < nb)
+      dma_tile<CPK, BN, NW>(kbase, p.k_st, (j + 1) * BN, p.Tk - 1, smem_s + ((j + 1) & 1) * KT_BYTES, wave, lane);
+    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * KT_BYTES);
+    f32x16 S;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) S = mfma32(qf[s], row_frag<CPK>(kt, lq, s, lh), S);
+    const int kk = j * BN + lq;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
+      const int lim = up >= 0 ? min(p.Tk - 1, t + off + up) : p.Tk - 1;
+      const bool vis = t < p.Tq && kk <= lim && (p.win_left < 0 || kk >= t + off - p.win_left);
+      if (vis) rm[r] = fmaxf(rm[r], S[r] * p.scale);
+      if (pbase != nullptr && t < p.Tq && kk < p.Tk)
+        pbase[(int64_t)t * p.p_st + kk] = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], p.c, -l2[r])) : 0.f;
+    }
+  }
+  if (p.row_max != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = rm[r];
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
+      if (lq == 0 && t < p.Tq) p.row_max[lbase + t] = v;
+    }
+  }
+}
+
+template <int DQK>
+int launch_extras_d(const ExtrasParams& p, void* stream) {
+  const int n_rt = (p.Tq + 127) / 128;
+  const int64_t grid = (int64_t)p.B * p.H * n_rt;
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL(extras_kernel<DQK>, dim3((unsigned)grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), p);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 bool bwd_supported(int d_qk, int d_v) {
@@ -1021,6 +1109,19 @@ int launch_bwd_sparse(const BwdParams& p, void* stream) {
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   return 0;
+}
+
+bool extras_supported(int d_qk) { return d_qk == 64 || d_qk == 128 || d_qk == 192 || d_qk == 256 || d_qk == 512; }
+
+int launch_extras(const ExtrasParams& p, int d_qk, void* stream) {
+  switch (d_qk) {
+    case 64: return launch_extras_d<64>(p, stream);
+    case 128: return launch_extras_d<128>(p, stream);
+    case 192: return launch_extras_d<192>(p, stream);
+    case 256: return launch_extras_d<256>(p, stream);
+    case 512: return launch_extras_d<512>(p, stream);
+    default: return -1;
+  }
 }
 
 }  // namespace attn

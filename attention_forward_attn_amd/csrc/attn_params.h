@@ -118,6 +118,22 @@ struct BwdParams {
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
+// The forward's extra returns (a second pass from q, k and the forward's
+// lse): probabilities of the visible keys and row maxima of the scaled scores.
+struct ExtrasParams {
+  const void* q;
+  const void* k;
+  const float* lse;       // [B, H, Tq] contiguous (read)
+  float* p;               // [B, H, Tq, Tk] with strides p_sb, p_sh, p_st, or nullptr
+  float* row_max;         // [B, H, Tq] contiguous, or nullptr
+  int64_t q_sb, q_sh, q_st, k_sb, k_sh, k_st, p_sb, p_sh, p_st;
+  int32_t B, H, Hkv, Tq, Tk, g;
+  int32_t causal, win_left, win_right;
+  float scale, c;
+};
+int launch_extras(const ExtrasParams& p, int d_qk, void* stream);
+bool extras_supported(int d_qk);
+
 // Sparse top-k backward (d_qk = d_v = 512, 64 heads): zeroes dkv, then row
 // dots, sink gradients and the gradient kernel. 0 or a hipError_t.
 int launch_bwd_sparse(const BwdParams& p, void* stream);

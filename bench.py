@@ -15,7 +15,8 @@ decode (d512, beside the plain path), the dense backward on gqa / mla /
 swa1024 (algorithmic flops = five products per visible pair), decode over a
 q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
 forward (beside the padded batch), MLA two-part rows (beside the concatenated
-call) and the sliding-window forward.
+call), the sparse backward, the forward's extra returns (p, row_max) and the
+sliding-window forward.
 
 Warmup: at least W untimed steps and at least 0.2 s of them (the clocks
 ramp over the first ~30 ms of load). Prints ONE JSON line on stdout. Kernel
@@ -554,6 +555,45 @@ def measure_two_part(steps: int, warmup: int) -> dict:
             "concatenated": {"path": "dense_bf16_d192_v128", "kernel_ms": round(t2["kernel_ms_mean"], 5)}}
 
 
+def measure_extras(steps: int, warmup: int) -> dict:
+    """The forward's extra returns on the gqa workload (2): probabilities (fp32, every
+    (row, key) pair written, masked ones as 0) and row maxima, from q, k and the
+    forward's lse. HBM bound: bytes = p + q + k + lse + row_max."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(2)
+    inp = synth.make(2)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    out, lse = A.dense(q, k, v, causal=True, scale=s.scale)
+    p = torch.empty((s.B, s.H, s.Tq, s.Tk), dtype=torch.float32, device="cuda")
+    rm = torch.empty((s.B, s.H, s.Tq), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.dense_extras(q, k, v, out, lse, causal=True, scale=s.scale, p=p, row_max=rm)
+
+    path = "dense_extras_bf16"
+    A.reset_dispatch_counts()
+    t = time_steps(step, steps, warmup)
+    if A.dispatch_count(path) != t["calls"]:
+        raise RuntimeError(f"NotEngaged: expected {t['calls']} launches of {path}, saw {A.dispatch_count(path)}")
+    nbytes = p.numel() * 4 + q.numel() * 2 + k.numel() * 2 + 2 * lse.numel() * 4
+    ach = nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+    rl = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    t2 = time_steps(lambda: A.dense_extras(q, k, v, out, lse, causal=True, scale=s.scale, want_p=False, row_max=rm),
+                    steps, warmup)
+    del p
+    log(f"[bench] extras: {describe(2)} | path {path} | p + row_max {t['kernel_ms_mean']:.4f} ms | "
+        f"{rl['achieved']} GB/s = {100 * rl['frac']:.1f}% of peak | row_max only {t2['kernel_ms_mean']:.4f} ms")
+    return {"row": "the forward's extra returns p, row_max (attn_fwd_dense_extras)", "workload": describe(2),
+            "path": path, "value": round(nbytes / (t["ms_per_step"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "row_max_only": {"kernel_ms": round(t2["kernel_ms_mean"], 5)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -787,6 +827,9 @@ def main():
         torch.cuda.empty_cache()
         # MLA rows in two parts
         next_rows.append(measure_two_part(st, wu))
+        torch.cuda.empty_cache()
+        # the forward's extra returns
+        next_rows.append(measure_extras(max(3, st // 4), 1))
         torch.cuda.empty_cache()
         # the sliding-window forward
         r = measure(7, st, wu)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 9
+#define ATTN_ABI_VERSION 10
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -322,6 +322,27 @@ int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a);
  * Launches are recorded under the dispatch path "dense_bwd_bf16_d<d_qk>" (with
  * "_v<d_v>" when d_v differs). */
 attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * The forward's extra returns, as a second pass after attn_fwd_dense: FA4 b19
+ * widened its forward's return from (out, lse) to (out, lse, p, row_max)
+ * (pith-train pull request 65, "Issues resolved" item 1). Read here as
+ *   p[b,h,t,j]    = exp(scale * q.k_j - lse[b,h,t]) for visible keys, 0 for
+ *                   masked ones (the sink has no column: with sinks a row sums
+ *                   to 1 - exp(sink - lse))
+ *   row_max[b,h,t] = the largest visible scaled score (the sink is not a
+ *                   score); -inf for a row that sees no key.
+ * `a` holds the forward's arguments; a->lse is READ here (the forward's lse);
+ * v, out and sinks are not used. Masks (causal, window) as in the forward.
+ *   p       fp32 [B, H, Tq, Tk] with element strides p_sb, p_sh, p_st (last
+ *           dimension contiguous), or NULL
+ *   row_max fp32 [B, H, Tq] contiguous, or NULL
+ * bf16, d_qk in {64, 128, 192, 256, 512}, rope_dim 0; otherwise
+ * ATTN_UNSUPPORTED. One launch on `stream` (dispatch path
+ * "dense_extras_bf16"); p costs B*H*Tq*Tk*4 bytes of writes.
+ */
+attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p, int64_t p_sb, int64_t p_sh, int64_t p_st,
+                                  float* row_max, void* stream);
 
 /*
  * Sparse top-k backward: the gradients of attn_fwd_sparse_topk with respect
