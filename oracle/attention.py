@@ -150,7 +150,8 @@ def _softmax_rows(S: np.ndarray, sink: Optional[float]) -> Tuple[np.ndarray, np.
 
 
 def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
-                    rows: Optional[Iterable[Tuple[int, int, int]]] = None, window: Tuple[int, int] = (-1, -1)):
+                    rows: Optional[Iterable[Tuple[int, int, int]]] = None, window: Tuple[int, int] = (-1, -1),
+                    keep=None, p_drop: float = 0.0):
     """Dense attention forward in fp64.
 
     q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v], sinks [H] or None.
@@ -168,6 +169,9 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
          attention as a defect).
       4. Row softmax with the sink (if any) added to the denominator only.
       5. O = P . V;  lse = m + ln(denominator).
+    Dropout (``keep`` [B,H,Tq,Tk] bool, probability ``p_drop``): the
+    probabilities are multiplied by keep / (1 - p_drop) before the product
+    with V; lse stays that of the softmax (the dropout acts after it).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Tq, Dqk = q.shape
@@ -178,6 +182,7 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
     K = repeat_kv(k, g)
     V = repeat_kv(v, g)
     sk = None if sinks is None else _f64(sinks)
+    keep = None if keep is None else np.asarray(keep, dtype=bool)
 
     def head(b, h, ts):
         S = scale * (q[b, h, ts] @ K[b, h].T)
@@ -186,6 +191,8 @@ def dense_attention(q, k, v, *, scale: float, causal: bool, sinks=None,
         if window[0] >= 0 or window[1] >= 0:
             S = np.where(_window_mask(ts, Tq, Tk, window[0], window[1]), S, NEG_INF)
         P, lse = _softmax_rows(S, None if sk is None else float(sk[h]))
+        if keep is not None:
+            P = _dropout(P, keep[b, h][ts], p_drop)
         return P @ V[b, h], lse
 
     if rows is None:
@@ -434,6 +441,14 @@ def merge_partials(parts, sink: Optional[float] = None):
     return out, lse
 
 
+def _dropout(P: np.ndarray, keep: np.ndarray, p_drop: float) -> np.ndarray:
+    """Attention dropout on the probabilities: kept entries scaled by 1 / (1 - p), the
+    others zeroed (the TransformerEngine page's review names dropout_p and the RNG
+    state that the forward and the backward must share; here the mask itself is the
+    shared input)."""
+    return np.where(keep, P / (1.0 - p_drop), 0.0)
+
+
 def _softmax_backward(P: np.ndarray, dP: np.ndarray, dO: np.ndarray, O: np.ndarray) -> np.ndarray:
     """dS = P * (dP - D) with D = rowsum(dO * O): the softmax Jacobian applied to dP.
 
@@ -456,7 +471,7 @@ def sum_kv_groups(x: np.ndarray, g: int) -> np.ndarray:
 
 
 def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks=None,
-                             window: Tuple[int, int] = (-1, -1)):
+                             window: Tuple[int, int] = (-1, -1), keep=None, p_drop: float = 0.0):
     """Gradients of the dense forward in fp64: (dq, dk, dv, dsinks).
 
     ``dout`` = dL/dO [B,H,Tq,d_v] for a scalar loss L of the output; the lse
@@ -477,6 +492,10 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
       7. dsink_h = -sum over rows of p_sink * D, with p_sink = exp(sink - lse)
       8. dk, dv of kv head kv = sum of dK_h, dV_h over the g heads that read
          it (the adjoint of repeat_kv's kv-major copy).
+    With dropout (``keep``, ``p_drop`` as in the forward) the product with V
+    takes Pd = P * keep / (1 - p): dV = Pd^T dO, O = Pd V, and the chain rule
+    through the mask gives dS = P * (dPd - D) with dPd = (dO V^T) * keep / (1 - p)
+    (D = rowsum(dO * O) of the dropped output, as before).
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, Tq, Dqk = q.shape
@@ -492,6 +511,7 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
     dV = np.zeros((B, H, Tk, Dv))
     dsk = None if sk is None else np.zeros(H)
     ts = np.arange(Tq)
+    keep = None if keep is None else np.asarray(keep, dtype=bool)
     for b in range(B):
         for h in range(H):
             S = scale * (q[b, h] @ K[b, h].T)
@@ -501,10 +521,13 @@ def dense_attention_backward(q, k, v, dout, *, scale: float, causal: bool, sinks
                 S = np.where(_window_mask(ts, Tq, Tk, window[0], window[1]), S, NEG_INF)
             sink = None if sk is None else float(sk[h])
             P, lse = _softmax_rows(S, sink)
-            O = P @ V[b, h]
+            Pd = P if keep is None else _dropout(P, keep[b, h], p_drop)
+            O = Pd @ V[b, h]
             dO = dout[b, h]
-            dV[b, h] = P.T @ dO
+            dV[b, h] = Pd.T @ dO
             dP = dO @ V[b, h].T
+            if keep is not None:
+                dP = _dropout(dP, keep[b, h], p_drop)
             dS = _softmax_backward(P, dP, dO, O)
             dq[b, h] = scale * (dS @ K[b, h])
             dK[b, h] = scale * (dS.T @ q[b, h])

@@ -28,7 +28,7 @@ def _attend(scores, values, sink):
     return o, math.log(math.fsum(tot))
 
 
-def brute_dense(q, k, v, scale, causal, sinks=None, window=(-1, -1)):
+def brute_dense(q, k, v, scale, causal, sinks=None, window=(-1, -1), keep=None, p_drop=0.0):
     """q [B][H][Tq][Dqk], k [B][Hkv][Tk][Dqk], v [B][Hkv][Tk][Dv] (nested lists or arrays).
     window (left, right): key j kept iff left < 0 or j >= t + Tk - Tq - left, and
     right < 0 or j <= t + Tk - Tq + right (tested key by key)."""
@@ -51,7 +51,9 @@ def brute_dense(q, k, v, scale, causal, sinks=None, window=(-1, -1)):
                         continue
                     sc.append(scale * math.fsum(float(q[b][h][t][d]) * float(k[b][kvh][j][d])
                                                 for d in range(Dqk)))
-                    vals.append([float(x) for x in v[b][kvh][j]])
+                    # dropout: a dropped key's value row is zero, a kept one is scaled
+                    z = 1.0 if keep is None else (1.0 / (1.0 - p_drop) if keep[b][h][t][j] else 0.0)
+                    vals.append([z * float(x) for x in v[b][kvh][j]])
                 o, l = _attend(sc, vals, None if sinks is None else float(sinks[h]))
                 out[b][h][t] = o if o is not None else [0.0] * Dv
                 lse[b][h][t] = l

@@ -371,6 +371,30 @@ def check_lse_logsumexp(orc=oracle):
     return worst
 
 
+def check_dropout(orc=oracle):
+    """Dropout on the probabilities: brute force with the mask applied to the value
+    rows (a different placement of the same factor), an all-kept mask with p = 0 is
+    no dropout, an all-kept mask with p > 0 scales O by 1 / (1 - p), and lse never
+    changes."""
+    worst = 0.0
+    rng = np.random.default_rng(990)
+    for i, (B, H, Hkv, Tq, Tk, d) in enumerate([(1, 4, 2, 5, 7, 3), (2, 2, 1, 6, 4, 4)]):
+        q, k, v = _rand((B, H, Tq, d), 991 + i, 0.8), _rand((B, Hkv, Tk, d), 992 + i, 0.8), _rand((B, Hkv, Tk, 2), 993 + i)
+        sinks = _rand((H,), 994 + i)
+        keep = rng.random((B, H, Tq, Tk)) > 0.3
+        for causal in (False, True):
+            for sk in (None, sinks):
+                o, l = orc.dense_attention(q, k, v, scale=0.7, causal=causal, sinks=sk, keep=keep, p_drop=0.3)
+                bo, bl = brute_dense(q, k, v, 0.7, causal, sk, keep=keep, p_drop=0.3)
+                o0, l0 = orc.dense_attention(q, k, v, scale=0.7, causal=causal, sinks=sk)
+                worst = max(worst, _err(o, bo), _err(l, bl), _err(l, l0))
+                ones = np.ones_like(keep)
+                o1, _ = orc.dense_attention(q, k, v, scale=0.7, causal=causal, sinks=sk, keep=ones, p_drop=0.0)
+                o2, _ = orc.dense_attention(q, k, v, scale=0.7, causal=causal, sinks=sk, keep=ones, p_drop=0.25)
+                worst = max(worst, _err(o1, o0), _err(o2, o0 / 0.75))
+    return worst
+
+
 def check_extras(orc=oracle):
     """The extra returns (probabilities, row maxima): brute force, P . V = O of the
     forward, and each row's probabilities plus the sink's share sum to 1."""
@@ -420,6 +444,7 @@ def check_two_part(orc=oracle):
 ALL_CHECKS = {
     "two_part": check_two_part,
     "extras": check_extras,
+    "dropout": check_dropout,
     "window": check_window,
     "varlen": check_varlen,
     "brute_dense": check_brute_dense,

@@ -178,6 +178,39 @@ def check_bwd_window_finite_differences(orc=oracle):
     return worst / TOL_FD * TOL
 
 
+def check_bwd_dropout(orc=oracle):
+    """Dropout in the backward: central differences of the forward with the same mask
+    (the forward and the backward share it), and torch autograd through an explicit
+    mask multiply."""
+    worst = 0.0
+    rng = np.random.default_rng(995)
+    B, H, Hkv, Tq, Tk, dqk, dv = 1, 4, 2, 6, 7, 4, 3
+    q, k, v = _rand((B, H, Tq, dqk), 996, 0.8), _rand((B, Hkv, Tk, dqk), 997, 0.8), _rand((B, Hkv, Tk, dv), 998)
+    G = _rand((B, H, Tq, dv), 999)
+    sinks = _rand((H,), 1000)
+    keep = rng.random((B, H, Tq, Tk)) > 0.35
+    for causal in (False, True):
+        sk = sinks.copy()
+        gq, gk, gv, gs = orc.dense_attention_backward(q, k, v, G, scale=0.5, causal=causal, sinks=sk, keep=keep,
+                                                      p_drop=0.35)
+
+        def f():
+            o, _ = orc.dense_attention(q, k, v, scale=0.5, causal=causal, sinks=sk, keep=keep, p_drop=0.35)
+            return float((o * G).sum())
+        worst = max(worst, _err(gq, _fd_grad(f, q)) / TOL_FD * TOL, _err(gk, _fd_grad(f, k)) / TOL_FD * TOL,
+                    _err(gv, _fd_grad(f, v)) / TOL_FD * TOL, _err(gs, _fd_grad(f, sk)) / TOL_FD * TOL)
+        Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        g = H // Hkv
+        s = torch.matmul(Q, K.repeat_interleave(g, dim=1).transpose(-1, -2)) * 0.5
+        if causal:
+            s = s.masked_fill(~torch.ones(Tq, Tk, dtype=torch.bool).tril(diagonal=Tk - Tq), float("-inf"))
+        p = torch.softmax(s, dim=-1) * torch.from_numpy(keep) / 0.65
+        (torch.matmul(p, V.repeat_interleave(g, dim=1)) * torch.from_numpy(G)).sum().backward()
+        gq, gk, gv, _ = orc.dense_attention_backward(q, k, v, G, scale=0.5, causal=causal, keep=keep, p_drop=0.35)
+        worst = max(worst, _err(gq, Q.grad.numpy()), _err(gk, K.grad.numpy()), _err(gv, V.grad.numpy()))
+    return worst
+
+
 def _sparse_loss(orc, q, kv, idx, G, d_v, scale, sinks):
     o, _ = orc.sparse_topk_attention(q, kv, idx, d_v=d_v, scale=scale, sinks=sinks)
     return float((o * G).sum())
@@ -247,6 +280,7 @@ def check_sparse_bwd_equals_dense_mqa(orc=oracle):
 
 
 ALL_CHECKS = {
+    "bwd_dropout": check_bwd_dropout,
     "sparse_bwd_finite_differences": check_sparse_bwd_finite_differences,
     "sparse_bwd_library_autograd": check_sparse_bwd_library_autograd,
     "sparse_bwd_equals_dense_mqa": check_sparse_bwd_equals_dense_mqa,

@@ -104,3 +104,15 @@ def test_sparse_duplicates_collapsed_caught(monkeypatch):
 
     monkeypatch.setattr(OA, "scatter_add_rows", assign)
     _assert_caught(["sparse_bwd_finite_differences"])
+
+
+def test_dropout_mask_ignored_in_backward_caught(monkeypatch):
+    """The TransformerEngine page's review: a backward that drops the dropout state
+    while the forward applied it."""
+    orig = OA.dense_attention_backward
+
+    def no_mask(*a, keep=None, p_drop=0.0, **kw):
+        return orig(*a, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention_backward", no_mask)
+    _assert_caught(["bwd_dropout"])

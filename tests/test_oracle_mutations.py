@@ -148,3 +148,14 @@ def test_extras_rows_renormalised_caught(monkeypatch):
 
     monkeypatch.setattr(oracle, "dense_attention_extras", renorm)
     _assert_caught(_caught(["extras"]))
+
+
+def test_dropout_ignored_caught(monkeypatch):
+    """The TransformerEngine page's review: dropout_p configured but not applied."""
+    orig = OA.dense_attention
+
+    def ignored(*a, keep=None, p_drop=0.0, **kw):
+        return orig(*a, **kw)
+
+    monkeypatch.setattr(oracle, "dense_attention", ignored)
+    _assert_caught(_caught(["dropout"]))
