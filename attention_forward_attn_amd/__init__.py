@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -44,6 +44,8 @@ class AttnDenseArgs(ctypes.Structure):
         ("rope_dim", ctypes.c_int32),
         ("q_rope", ctypes.c_void_p), ("qr_sb", ctypes.c_int64), ("qr_sh", ctypes.c_int64), ("qr_st", ctypes.c_int64),
         ("k_rope", ctypes.c_void_p), ("kr_sb", ctypes.c_int64), ("kr_sh", ctypes.c_int64), ("kr_st", ctypes.c_int64),
+        ("keep", ctypes.c_void_p), ("m_sb", ctypes.c_int64), ("m_sh", ctypes.c_int64), ("m_st", ctypes.c_int64),
+        ("p_drop", ctypes.c_float),
     ]
 
 
@@ -99,6 +101,8 @@ class AttnDenseBwdArgs(ctypes.Structure):
         ("dsinks", ctypes.c_void_p),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("keep", ctypes.c_void_p), ("m_sb", ctypes.c_int64), ("m_sh", ctypes.c_int64), ("m_st", ctypes.c_int64),
+        ("p_drop", ctypes.c_float),
     ]
 
 
@@ -277,8 +281,23 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _set_keep(a, keep, p_drop: float, B: int, H: int, Tq: int, Tk: int):
+    """Dropout fields: ``keep`` int32 [B,H,Tq,ceil(Tk/32)] bit-packed keep mask (bit i
+    of word w = key 32 w + i, as ``synth.pack_keep`` writes), or None."""
+    if keep is None:
+        return
+    import torch
+
+    if keep.dtype != torch.int32 or keep.dim() != 4 or tuple(keep.shape[:3]) != (B, H, Tq) or keep.stride(-1) != 1 \
+            or keep.shape[3] < (Tk + 31) // 32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "keep must be int32 [B, H, Tq, ceil(Tk/32)] (bit-packed)")
+    a.keep, (a.m_sb, a.m_sh, a.m_st) = keep.data_ptr(), keep.stride()[:3]
+    a.p_drop = float(p_drop)
+
+
 def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
-               window: Tuple[int, int] = (-1, -1), q_rope=None, k_rope=None) -> AttnDenseArgs:
+               window: Tuple[int, int] = (-1, -1), q_rope=None, k_rope=None, keep=None,
+               p_drop: float = 0.0) -> AttnDenseArgs:
     """Fill the C argument struct from tensors (BHSD or any strided view with unit last stride).
 
     With ``q_rope`` [B,H,Tq,r] and ``k_rope`` [B,Hkv,Tk,r] the query and key rows are
@@ -314,6 +333,7 @@ def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
     a.lse = lse.data_ptr()
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.window_left, a.window_right = int(window[0]), int(window[1])
+    _set_keep(a, keep, p_drop, B, H, Tq, Tk)
     a.rope_dim = rope
     if rope:
         a.q_rope, (a.qr_sb, a.qr_sh, a.qr_st) = q_rope.data_ptr(), q_rope.stride()[:3]
@@ -323,14 +343,16 @@ def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
 
 def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
           out=None, lse=None, stream=None, window: Tuple[int, int] = (-1, -1), q_rope=None,
-          k_rope=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+          k_rope=None, keep=None, p_drop: float = 0.0) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Fused dense attention forward on the GPU.
 
     q [B,H,Tq,d_qk], k [B,Hkv,Tk,d_qk], v [B,Hkv,Tk,d_v] (bf16, or fp32 for the
     split-bf16 path), sinks [H] fp32 or None. ``window`` = (left, right) keys
     around each row's diagonal position t + Tk - Tq (-1: unbounded; bf16 only;
     it never widens the causal mask). ``q_rope``/``k_rope``: MLA's rope parts
-    read in place (see :func:`dense_args`). Returns (out [B,H,Tq,d_v] in the input
+    read in place (see :func:`dense_args`). ``keep``/``p_drop``: attention dropout with
+    the caller's bit-packed keep mask (pass the same mask to :func:`dense_backward`).
+    Returns (out [B,H,Tq,d_v] in the input
     dtype, lse [B,H,Tq] fp32). Launches on ``stream`` (default: torch's current
     stream) and does not synchronise.
     """
@@ -350,7 +372,7 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
     if not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
     a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window, q_rope=q_rope,
-                   k_rope=k_rope)
+                   k_rope=k_rope, keep=keep, p_drop=p_drop)
     _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
 
@@ -618,7 +640,7 @@ def abi_version() -> int:
 
 
 def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: float, sinks=None,
-                   dsinks=None, window: Tuple[int, int] = (-1, -1)) -> AttnDenseBwdArgs:
+                   dsinks=None, window: Tuple[int, int] = (-1, -1), keep=None, p_drop: float = 0.0) -> AttnDenseBwdArgs:
     """Fill the backward's C argument struct from tensors (unit last stride)."""
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
@@ -643,12 +665,13 @@ def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: 
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.dsinks = dsinks.data_ptr() if dsinks is not None else None
     a.window_left, a.window_right = int(window[0]), int(window[1])
+    _set_keep(a, keep, p_drop, B, H, Tq, Tk)
     return a
 
 
 def dense_backward(q, k, v, out, dout, lse, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
                    dq=None, dk=None, dv=None, dsinks=None, workspace=None, stream=None,
-                   window: Tuple[int, int] = (-1, -1)):
+                   window: Tuple[int, int] = (-1, -1), keep=None, p_drop: float = 0.0):
     """Dense attention backward on the GPU (bf16): returns (dq, dk, dv, dsinks).
 
     ``out`` and ``lse`` are the forward's results for (q, k, v, sinks); ``dout``
@@ -677,7 +700,7 @@ def dense_backward(q, k, v, out, dout, lse, *, causal: bool = True, scale: Optio
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [B, H, Tq]")
     a = dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, causal=causal, scale=scale, sinks=sinks,
-                       dsinks=dsinks, window=window)
+                       dsinks=dsinks, window=window, keep=keep, p_drop=p_drop)
     # a negative size means invalid sizes or head dims: the call below then
     # reports the library's own status before launching anything
     need = int(lib.attn_bwd_dense_workspace_bytes(ctypes.byref(a)))

@@ -56,11 +56,14 @@ constexpr const char* kSpBwdPath = "sparse_bwd_bf16_d512";
 constexpr int kSpBwdSlot = kQkvSlot0 - 1;
 constexpr const char* kExtrasPath = "dense_extras_bf16";
 constexpr int kExtrasSlot = kSpBwdSlot - 1;
+constexpr const char* kDropPath = "dense_dropout_bf16";
+constexpr int kDropPathSlot = kExtrasSlot - 1;
 
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
   if (std::strcmp(path, kSpBwdPath) == 0) return kSpBwdSlot;
   if (std::strcmp(path, kExtrasPath) == 0) return kExtrasSlot;
+  if (std::strcmp(path, kDropPath) == 0) return kDropPathSlot;
   for (int i = 0; i < 4; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
@@ -103,7 +106,22 @@ const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse, 
 struct DensePlan {
   const attn::KernelConfig* cfg;
   attn::KernelParams kp;
+  bool drop = false;  // dropout: the separate dropout kernel, not cfg
 };
+
+// dropout mask fields shared by the forward and backward argument structs
+template <class Args>
+static attn_status validate_keep(const Args* a, int Tq, int Tk) {
+  if (!a->keep) return ATTN_OK;
+  if (a->dtype != ATTN_BF16 || !attn::bwd_supported(a->d_qk, a->d_v))
+    return fail(ATTN_UNSUPPORTED, "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128)}");
+  if (!(a->p_drop >= 0.f && a->p_drop < 1.f)) return fail(ATTN_INVALID_ARGUMENT, "p_drop must be in [0, 1)");
+  if ((uintptr_t)a->keep & 3u) return fail(ATTN_INVALID_ARGUMENT, "keep must be 4-byte aligned");
+  const int64_t nw = ((int64_t)Tk + 31) / 32;
+  if (a->m_sb < 0 || a->m_sh < 0 || a->m_st < 0 || (Tq > 1 && a->m_st < nw) || a->m_st >= (1 << 24))
+    return fail(ATTN_INVALID_ARGUMENT, "keep strides must be >= 0, m_st >= ceil(Tk/32) and below 2^24 words");
+  return ATTN_OK;
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
 // with its own L2. When the (batch, kv head) groups split evenly, every XCD
@@ -152,6 +170,11 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
                 a->dtype, a->d_qk, a->d_v, a->rope_dim);
   const int rope = a->rope_dim;
   const int d_main = a->d_qk - rope;  // columns held by q and k
+  {
+    const attn_status ks = validate_keep(a, a->Tq, a->Tk);
+    if (ks != ATTN_OK) return ks;
+    if (a->keep && rope != 0) return fail(ATTN_UNSUPPORTED, "dropout with two-part rows is not compiled");
+  }
   if (rope > 0) {
     if (a->Tq > 0 && !a->q_rope) return fail(ATTN_INVALID_ARGUMENT, "q_rope must be non-NULL when Tq > 0");
     if (a->Tk > 0 && !a->k_rope) return fail(ATTN_INVALID_ARGUMENT, "k_rope must be non-NULL when Tk > 0");
@@ -187,6 +210,7 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   if (a->Tq > 1 && a->o_st < a->d_v) return fail(ATTN_INVALID_ARGUMENT, "out token stride smaller than d_v");
 
   out->cfg = cfg;
+  out->drop = a->keep != nullptr;
   attn::KernelParams& p = out->kp;
   std::memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse; p.sinks = a->sinks; p.idx = nullptr;
@@ -383,12 +407,35 @@ extern "C" {
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
+static attn_status launch_dropout(const attn_dense_args* a, void* stream) {
+  attn::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.k = a->k; p.v = a->v; p.sinks = a->sinks;
+  p.fwd_out = a->out; p.fwd_lse = a->lse;
+  p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_st = a->q_st;
+  p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
+  p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;
+  p.o_sb = a->o_sb; p.o_sh = a->o_sh; p.o_st = a->o_st;
+  p.B = a->B; p.H = a->H; p.Hkv = a->Hkv; p.Tq = a->Tq; p.Tk = a->Tk; p.g = a->H / a->Hkv;
+  p.causal = a->causal; p.win_left = a->window_left; p.win_right = a->window_right;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  p.keep = a->keep; p.m_sb = a->m_sb; p.m_sh = a->m_sh; p.m_st = a->m_st;
+  p.nwords = (int)(((int64_t)a->Tk + 31) / 32);
+  p.inv_keep = 1.f / (1.f - a->p_drop);
+  const int err = attn::launch_fwd_dropout(p, a->d_qk, a->d_v, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the dropout forward failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kDropPathSlot, kDropPath);
+  return ATTN_OK;
+}
+
 attn_status attn_fwd_dense(const attn_dense_args* a, void* stream) {
   g_last_error.clear();
   DensePlan dp;
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
   if (a->Tq == 0) return ATTN_OK;
+  if (dp.drop) return launch_dropout(a, stream);
   return do_launch(dp, stream);
 }
 
@@ -408,6 +455,7 @@ attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p) {
   DensePlan dp;
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
+  if (dp.drop) return fail(ATTN_UNSUPPORTED, "plans describe the fused kernels; dropout runs a separate kernel");
   if (a->Tq == 0) dp.kp.n_tiles = 0;
   fill_plan(dp, a->H / a->Hkv, (int64_t)(a->H / a->Hkv) * a->Tq, a->Tk, a->dtype == ATTN_BF16 ? 2 : 4, p);
   return ATTN_OK;
@@ -417,6 +465,10 @@ int32_t attn_splitkv_choose(const attn_dense_args* a) {
   g_last_error.clear();
   DensePlan dp;
   if (validate_dense(a, &dp) != ATTN_OK) return -1;
+  if (dp.drop) {
+    fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
+    return -1;
+  }
   if (a->dtype != ATTN_BF16) return 1;
   return plan_split(dp, a, 0).n;
 }
@@ -425,6 +477,10 @@ int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits)
   g_last_error.clear();
   DensePlan dp;
   if (validate_dense(a, &dp) != ATTN_OK) return -1;
+  if (dp.drop) {
+    fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
+    return -1;
+  }
   if (n_splits < 0 || n_splits > kMaxSplits) {
     fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
     return -1;
@@ -439,6 +495,7 @@ attn_status attn_fwd_dense_splitkv(const attn_dense_args* a, int32_t n_splits, v
   DensePlan dp;
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
+  if (dp.drop) return fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
   if (n_splits < 0 || n_splits > kMaxSplits)
     return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
   if (a->Tq == 0) return ATTN_OK;
@@ -556,7 +613,7 @@ static attn_status validate_bwd(const attn_dense_bwd_args* a) {
     return fail(ATTN_INVALID_ARGUMENT, "query-side token stride smaller than the head dim");
   if (a->Tk > 1 && (a->k_st < a->d_qk || a->v_st < a->d_v || a->dk_st < a->d_qk || a->dv_st < a->d_v))
     return fail(ATTN_INVALID_ARGUMENT, "key-side token stride smaller than the head dim");
-  return ATTN_OK;
+  return validate_keep(a, a->Tq, a->Tk);
 }
 
 static int64_t bwd_workspace(const attn_dense_bwd_args* a) {
@@ -600,6 +657,11 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
   p.win_right = a->window_right;
   p.scale = a->scale;
   p.c = a->scale * 1.4426950408889634f;
+  if (a->keep) {
+    p.keep = a->keep; p.m_sb = a->m_sb; p.m_sh = a->m_sh; p.m_st = a->m_st;
+    p.nwords = (int)(((int64_t)a->Tk + 31) / 32);
+    p.inv_keep = 1.f / (1.f - a->p_drop);
+  }
   const int err = attn::launch_bwd(p, a->d_qk, a->d_v, stream);
   if (err != 0)
     return fail(ATTN_HIP_ERROR, "launch of the dense backward failed: %s", hipGetErrorString((hipError_t)err));
@@ -615,6 +677,7 @@ attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p_out, int64_
   DensePlan dp;
   attn_status st = validate_dense(a, &dp);
   if (st != ATTN_OK) return st;
+  if (dp.drop) return fail(ATTN_UNSUPPORTED, "the extra returns take no dropout mask");
   if (a->dtype != ATTN_BF16 || a->rope_dim != 0 || !attn::extras_supported(a->d_qk))
     return fail(ATTN_UNSUPPORTED, "the extra returns are compiled for bf16, d_qk in {64,128,192,256,512}, rope_dim 0");
   if (((uintptr_t)p_out & 3u) || ((uintptr_t)row_max & 3u))

@@ -244,12 +244,16 @@ __device__ __forceinline__ void dma_tile(const bf16_t* base, int64_t st, int r0,
 // ---------------------------------------------------------------------------
 // 3. dK, dV: one workgroup per 32*NW keys of one (b, kv head)
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int NW, int BQ>
+template <int DQK, int DV, int NW, int BQ, bool DROP>
 __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int BNK = 32 * NW;  // keys per workgroup; BQ query rows per step (32-row sub-blocks)
   constexpr int CPQ = DQK / 8, CPO = DV / 8;
   constexpr int KS = DQK / 16, VS = DV / 16, DTK = DQK / 32, DTV = DV / 32;
-  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2, STAGE = QT_BYTES + OT_BYTES + 2 * BQ * 4;
+  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2;
+  // with dropout a stage also holds the keep words of its rows, one column of
+  // 32 keys per wave: [wave][row]
+  constexpr int MOFF = QT_BYTES + OT_BYTES + 2 * BQ * 4;
+  constexpr int STAGE = MOFF + (DROP ? NW * BQ * 4 : 0);
   static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims are whole 32-column tiles");
   static_assert(BQ <= 64, "one row statistic per lane");
   // two stages: [Q tile | dO tile | lse | D]
@@ -316,6 +320,13 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
         dma4(db, vo, st + QT_BYTES + OT_BYTES + BQ * 4);
       }
     }
+    if constexpr (DROP) {
+      // keep words of rows t0 .. t0+BQ-1 for this wave's 32 keys
+      const int w = min(kb0 / 32 + wave, p.nwords - 1);
+      const void* mb = uniform_ptr(p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t0 * p.m_st + w);
+      const uint32_t mo = 4u * (uint32_t)((min(t0 + lane, p.Tq - 1) - t0) * p.m_st);
+      if (lane < BQ) dma4(mb, mo, st + MOFF + wave * BQ * 4);
+    }
   };
 
   if (n_it > 0) issue(0);
@@ -354,6 +365,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
         const int r0 = qs * 32 + lh * 4 + 8 * g4;
         const f32x4 L = *reinterpret_cast<const f32x4*>(rl + r0);
         const f32x4 Dv = *reinterpret_cast<const f32x4*>(rd + r0);
+        u32x4 M = {0u, 0u, 0u, 0u};
+        if constexpr (DROP) M = *reinterpret_cast<const u32x4*>(rl + 2 * BQ + wave * BQ + r0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = g4 * 4 + j;
@@ -364,8 +377,15 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
             const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
             pr = (key <= lim && key >= lo) ? pr : 0.f;
           }
-          P[i] = pr;
-          dS[i] = pr * (dP[i] - Dv[j]);
+          if constexpr (DROP) {
+            // dV takes the dropped probabilities; dS = P (Z dP - D)
+            const float z = ((M[j] >> lq) & 1u) ? p.inv_keep : 0.f;
+            P[i] = pr * z;
+            dS[i] = pr * (z * dP[i] - Dv[j]);
+          } else {
+            P[i] = pr;
+            dS[i] = pr * (dP[i] - Dv[j]);
+          }
         }
       }
       const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
@@ -415,13 +435,17 @@ __global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdParams p) {
 // which leaves the registers for the dK/dV accumulators), and the two partial
 // sums of each key are added through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV>
+template <int DQK, int DV, bool DROP>
 __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
   constexpr int NW = 8, BNK = 128, BQ = 64;
   constexpr int CPQ = DQK / 8, CPO = DV / 8;
   constexpr int KS = DQK / 16, VS = DV / 16, DTK = DQK / 32, DTV = DV / 32;
   constexpr int KT_BYTES = BNK * DQK * 2, VT_BYTES = BNK * DV * 2;
-  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2, STAGE = QT_BYTES + OT_BYTES + 2 * BQ * 4;
+  constexpr int QT_BYTES = BQ * DQK * 2, OT_BYTES = BQ * DV * 2;
+  // with dropout a stage also holds the keep words of its rows, one column of
+  // 32 keys per key group: [cg][row]
+  constexpr int MOFF = QT_BYTES + OT_BYTES + 2 * BQ * 4;
+  constexpr int STAGE = MOFF + (DROP ? 4 * BQ * 4 : 0);
   constexpr int LDS_BYTES = KT_BYTES + VT_BYTES + 2 * STAGE;
   constexpr int RED_BYTES = 4 * (DTK + DTV) * 16 * 64 * 4;  // partial sums of waves 4..7
   static_assert(RED_BYTES <= LDS_BYTES && LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -477,6 +501,15 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
       dma4(lb, vo, st + QT_BYTES + OT_BYTES);
       dma4(db, vo, st + QT_BYTES + OT_BYTES + BQ * 4);
     }
+    if constexpr (DROP) {
+      if (wave < 4) {
+        // keep words of rows t0 .. t0+63 for key group `wave` (32 keys)
+        const int w = min(kb0 / 32 + wave, p.nwords - 1);
+        const void* mb = uniform_ptr(p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t0 * p.m_st + w);
+        const uint32_t mo = 4u * (uint32_t)((min(t0 + lane, p.Tq - 1) - t0) * p.m_st);
+        dma4(mb, mo, st + MOFF + wave * BQ * 4);
+      }
+    }
   };
 
   // K and V of the block, once (rows past Tk clamped: they are masked)
@@ -517,6 +550,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
       const int r0 = qs * 32 + lh * 4 + 8 * g4;
       const f32x4 L = *reinterpret_cast<const f32x4*>(rl + r0);
       const f32x4 Dv = *reinterpret_cast<const f32x4*>(rd + r0);
+      u32x4 M = {0u, 0u, 0u, 0u};
+      if constexpr (DROP) M = *reinterpret_cast<const u32x4*>(rl + 2 * BQ + cg * BQ + r0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = g4 * 4 + j;
@@ -527,8 +562,14 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
           const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
           pr = (key <= lim && key >= lo) ? pr : 0.f;
         }
-        P[i] = pr;
-        dS[i] = pr * (dP[i] - Dv[j]);
+        if constexpr (DROP) {
+          const float z = ((M[j] >> lq) & 1u) ? p.inv_keep : 0.f;
+          P[i] = pr * z;
+          dS[i] = pr * (z * dP[i] - Dv[j]);
+        } else {
+          P[i] = pr;
+          dS[i] = pr * (dP[i] - Dv[j]);
+        }
       }
     }
     const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
@@ -593,7 +634,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // 4. dQ: one workgroup per 32*NW folded query rows of one (b, kv head)
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int NW, int BN>
+template <int DQK, int DV, int NW, int BN, bool DROP>
 __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
   constexpr int BM = 32 * NW;
   constexpr int CPK = DQK / 8, CPV = DV / 8;
@@ -666,11 +707,26 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
+  // dropout: this row's keep words of block j (MT words), loaded one block
+  // ahead so that their wait falls where the block's tiles are waited for
+  const uint32_t* mrow = DROP ? p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st : nullptr;
+  uint32_t mw[MT], mwn[MT];
+  auto load_mask = [&](int j, uint32_t* dst) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dst[mt] = (j * MT + mt < p.nwords) ? mrow[j * MT + mt] : 0u;
+  };
+  if constexpr (DROP) {
+    if (nb > jb0) load_mask(jb0, mw);
+  }
+
   if (nb > jb0) issue(jb0);
   for (int j = jb0; j < nb; ++j) {
     wait_all_loads();
     barrier();
     if (j + 1 < nb) issue(j + 1);
+    if constexpr (DROP) {
+      if (j + 1 < nb) load_mask(j + 1, mwn);
+    }
     const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
     const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
     f32x16 S[MT], dP[MT];
@@ -702,7 +758,12 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
           const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
           pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
         }
-        dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
+        if constexpr (DROP) {
+          const float z = ((mw[mt] >> (lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) ? p.inv_keep : 0.f;
+          dS[mt * 16 + i] = pr * (z * dP[mt][i] - Dr);
+        } else {
+          dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
+        }
       }
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
@@ -711,6 +772,10 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_frag<CPK>(kt, ks * 16, dt * 32, lane), db, acc[dt]);
     }
     pipeline_reads<PKS * DT, 2>();
+    if constexpr (DROP) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) mw[mt] = mwn[mt];
+    }
   }
 
   if (valid) {
@@ -726,7 +791,182 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 7. Forward with attention dropout. The keep mask is an input that the
+//    backward reads too, so the two cannot disagree on it (the
+//    TransformerEngine page's review names a context-parallel backward that
+//    lost the dropout probability and RNG state the forward used). The dQ
+//    kernel's tiling: 32 folded query rows per wave with Q in registers, 64-key
+//    K and V tiles through LDS, S^T = K Q^T, an online softmax per row (the
+//    two lane halves hold different keys of a row), O^T += V^T (P keep)^T.
+//    The denominator takes every visible probability; only the product with
+//    V sees the mask, and the kept ones are scaled by 1 / (1 - p) at the end.
+// ---------------------------------------------------------------------------
+constexpr float kLn2 = 0.6931471805599453f;
+
 template <int DQK, int DV>
+__global__ void __launch_bounds__(256) fwd_dropout_kernel(const BwdParams p) {
+  constexpr int NW = 4, BN = 64, BM = 32 * NW;
+  constexpr int CPK = DQK / 8, CPV = DV / 8;
+  constexpr int KS = DQK / 16, DT = DV / 32, MT = BN / 32, PKS = BN / 16;
+  constexpr int KT_BYTES = BN * DQK * 2, STAGE = KT_BYTES + BN * DV * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int rows = p.g * p.Tq;  // folded rows of the group
+  const int n_rt = (rows + BM - 1) / BM;
+  const int tb = n_rt - 1 - (int)(blockIdx.x / n_groups);  // longest causal tiles first
+  const int f0 = tb * BM;
+  const int f = f0 + wave * 32 + lq;
+  const bool valid = f < rows;
+  const int fc = valid ? f : rows - 1;
+  const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
+  const int off = p.Tk - p.Tq;
+  const int up = p.causal ? 0 : p.win_right;
+  const int row_lim = !valid ? -1 : (up >= 0 ? min(t + off + up, p.Tk - 1) : p.Tk - 1);
+  const int row_lo = p.win_left >= 0 ? t + off - p.win_left : 0;
+
+  bf16x8 qf[KS];
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + lh * 8);
+  }
+  int kend = p.Tk, kfull = (f0 + BM <= rows) ? p.Tk : 0, kstart = 0, klfull = 0;
+  {
+    const int f_last = min(f0 + BM, rows) - 1;
+    const bool one_head = f_last / p.Tq == f0 / p.Tq;
+    const int t_hi = one_head ? f_last % p.Tq : p.Tq - 1;
+    const int t_lo = one_head ? f0 % p.Tq : 0;
+    if (up >= 0) {
+      kend = max(0, min(p.Tk, t_hi + off + up + 1));
+      kfull = min(kfull, max(0, t_lo + off + up + 1));
+    }
+    if (p.win_left >= 0) {
+      kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
+      klfull = max(0, t_hi + off - p.win_left);
+    }
+  }
+  const int nb = (kend + BN - 1) / BN, jb0 = kstart / BN;
+
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
+  const uint32_t smem_s = lds_u32(smem);
+  auto issue = [&](int j) {
+    const uint32_t st = smem_s + (uint32_t)((j & 1) * STAGE);
+    dma_tile<CPK, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, st, wave, lane);
+    dma_tile<CPV, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1, st + KT_BYTES, wave, lane);
+  };
+  // this row's keep words of block j, loaded one block ahead
+  const uint32_t* mrow = p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st;
+  uint32_t mw[MT], mwn[MT];
+  auto load_mask = [&](int j, uint32_t* dst) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dst[mt] = (j * MT + mt < p.nwords) ? mrow[j * MT + mt] : 0u;
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (nb > jb0) {
+    load_mask(jb0, mw);
+    issue(jb0);
+  }
+  for (int j = jb0; j < nb; ++j) {
+    wait_all_loads();
+    barrier();
+    if (j + 1 < nb) {
+      issue(j + 1);
+      load_mask(j + 1, mwn);
+    }
+    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
+    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
+    f32x16 S[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[mt][i] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) S[mt] = mfma32(row_frag<CPK>(kt, mt * 32 + lq, s, lh), qf[s], S[mt]);
+    pipeline_reads<MT * KS, 1>();
+    // S^T element i of tile mt is key j*BN + mt*32 + lh*4 + 8*(i/4) + i%4 of this lane's row
+    const bool full = (j + 1) * BN <= kfull && j * BN >= klfull;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (!full) {
+          const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
+          if (!(kk <= row_lim && kk >= row_lo)) S[mt][i] = -INFINITY;
+        }
+        mx = fmaxf(mx, S[mt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the other half of the row's keys
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c);
+    m_run = mnew;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    const float mc = (mnew == -INFINITY) ? 0.f : mnew * p.c;
+    float pd[MT * 16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -mc));
+        l_run += e;
+        pd[mt * 16 + i] = ((mw[mt] >> (lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) ? e : 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      const bf16x8 pb = pack8(pd + ks * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_frag<CPV>(vt, ks * 16, dt * 32, lane), pb, acc[dt]);
+    }
+    pipeline_reads<PKS * DT, 2>();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) mw[mt] = mwn[mt];
+  }
+
+  // epilogue: the row's denominator (both halves, the sink), O and lse
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float sk = p.sinks != nullptr ? p.sinks[h] : -INFINITY;
+  float factor = 0.f, lse = sk;
+  if (m_run != -INFINITY) {
+    const float ms = m_run * p.scale;
+    const float mtot = fmaxf(ms, sk);
+    const float a = __builtin_amdgcn_exp2f((ms - mtot) * kLog2e);
+    const float den = l * a + (sk != -INFINITY ? __builtin_amdgcn_exp2f((sk - mtot) * kLog2e) : 0.f);
+    factor = a / den * p.inv_keep;
+    lse = mtot + __builtin_amdgcn_logf(den) * kLn2;
+  }
+  if (valid) {
+    bf16_t* op = reinterpret_cast<bf16_t*>(p.fwd_out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(op + d) = u32x2{pack2(acc[dt][g4 * 4] * factor, acc[dt][g4 * 4 + 1] * factor),
+                                                  pack2(acc[dt][g4 * 4 + 2] * factor, acc[dt][g4 * 4 + 3] * factor)};
+      }
+    if (lh == 0) p.fwd_lse[((int64_t)b * p.H + h) * p.Tq + t] = lse;
+  }
+}
+
+template <int DQK, int DV, bool DROP>
 int launch_bwd_cfg(const BwdParams& p, void* stream) {
   // dQ: two waves per SIMD where the registers allow it (d_qk + d_v <= 256)
   constexpr int NW_KV = 4, NW_Q = DQK + DV > 256 ? 4 : 8, BN_Q = 64;
@@ -745,18 +985,18 @@ int launch_bwd_cfg(const BwdParams& p, void* stream) {
   if (p.Tk > 0) {
     if constexpr (DQK + DV <= 256) {
       const int nkb = (p.Tk + 127) / 128;
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<DQK, DV>), dim3(nkb * p.B * p.Hkv), dim3(512), 0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<DQK, DV, DROP>), dim3(nkb * p.B * p.Hkv), dim3(512), 0, st, p);
     } else {
       const int nkb = (p.Tk + 32 * NW_KV - 1) / (32 * NW_KV);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV>), dim3(nkb * p.B * p.Hkv), dim3(NW_KV * 64), 0, st,
-                         p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, NW_KV, BQ_KV, DROP>), dim3(nkb * p.B * p.Hkv), dim3(NW_KV * 64), 0,
+                         st, p);
     }
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   if (p.Tq > 0) {
     const int rows = p.g * p.Tq;
     const int nrt = (rows + 32 * NW_Q - 1) / (32 * NW_Q);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, NW_Q, BN_Q>), dim3(nrt * p.B * p.Hkv), dim3(NW_Q * 64), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, NW_Q, BN_Q, DROP>), dim3(nrt * p.B * p.Hkv), dim3(NW_Q * 64), 0, st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   return 0;
@@ -1082,9 +1322,12 @@ bool bwd_supported(int d_qk, int d_v) {
 }
 
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
-  if (d_qk == 64 && d_v == 64) return launch_bwd_cfg<64, 64>(p, stream);
-  if (d_qk == 128 && d_v == 128) return launch_bwd_cfg<128, 128>(p, stream);
-  if (d_qk == 192 && d_v == 128) return launch_bwd_cfg<192, 128>(p, stream);
+  const bool drop = p.keep != nullptr;
+  if (d_qk == 64 && d_v == 64) return drop ? launch_bwd_cfg<64, 64, true>(p, stream) : launch_bwd_cfg<64, 64, false>(p, stream);
+  if (d_qk == 128 && d_v == 128)
+    return drop ? launch_bwd_cfg<128, 128, true>(p, stream) : launch_bwd_cfg<128, 128, false>(p, stream);
+  if (d_qk == 192 && d_v == 128)
+    return drop ? launch_bwd_cfg<192, 128, true>(p, stream) : launch_bwd_cfg<192, 128, false>(p, stream);
   return -1;
 }
 
@@ -1122,6 +1365,22 @@ int launch_extras(const ExtrasParams& p, int d_qk, void* stream) {
     case 512: return launch_extras_d<512>(p, stream);
     default: return -1;
   }
+}
+
+int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream) {
+  const int64_t n_rt = ((int64_t)p.g * p.Tq + 127) / 128;
+  const int64_t grid = n_rt * p.B * p.Hkv;
+  if (grid == 0) return 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (d_qk == 64 && d_v == 64)
+    hipLaunchKernelGGL((fwd_dropout_kernel<64, 64>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else if (d_qk == 128 && d_v == 128)
+    hipLaunchKernelGGL((fwd_dropout_kernel<128, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else if (d_qk == 192 && d_v == 128)
+    hipLaunchKernelGGL((fwd_dropout_kernel<192, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else
+    return -1;
+  return (int)hipGetLastError();
 }
 
 }  // namespace attn

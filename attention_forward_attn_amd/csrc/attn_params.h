@@ -102,6 +102,15 @@ struct BwdParams {
   int32_t win_left, win_right;  // sliding window as in the forward (-1: unbounded side)
   float scale;
   float c;                // scale * log2(e)
+  // dropout (kernels built with it): keep mask bits, word (b, h, t, w) at
+  // keep + b*m_sb + h*m_sh + t*m_st + w holds keys 32 w .. 32 w + 31 (bit i =
+  // key 32 w + i); kept probabilities are scaled by inv_keep = 1 / (1 - p)
+  const uint32_t* keep;
+  int64_t m_sb, m_sh, m_st;
+  int32_t nwords;         // ceil(Tk / 32)
+  float inv_keep;
+  void* fwd_out;          // the dropout forward's output [B, H, Tq, d_v] (o strides)
+  float* fwd_lse;         // and its lse [B, H, Tq]
   // sparse top-k (launch_bwd_sparse): q, out, dout, dq are [Sq, Hq, 512] with
   // strides (q_sb, q_sh) etc., the pool is k with row stride k_st (values =
   // its first 512 columns), lse / D are [Sq, Hq] (B = Sq, H = Hq, Tq = 1)
@@ -116,6 +125,9 @@ struct BwdParams {
 // `stream`; 0 or the hipError_t of a failed launch. Returns -1 when no
 // kernel is compiled for (d_qk, d_v).
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
+// Forward with dropout (p.keep set): one launch writing fwd_out and fwd_lse;
+// -1 when no kernel is compiled for (d_qk, d_v) (the backward's set).
+int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
 // The forward's extra returns (a second pass from q, k and the forward's

@@ -15,8 +15,8 @@ decode (d512, beside the plain path), the dense backward on gqa / mla /
 swa1024 (algorithmic flops = five products per visible pair), decode over a
 q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
 forward (beside the padded batch), MLA two-part rows (beside the concatenated
-call), the sparse backward, the forward's extra returns (p, row_max) and the
-sliding-window forward.
+call), the sparse backward, the forward's extra returns (p, row_max), attention
+dropout (forward and backward) and the sliding-window forward.
 
 Warmup: at least W untimed steps and at least 0.2 s of them (the clocks
 ramp over the first ~30 ms of load). Prints ONE JSON line on stdout. Kernel
@@ -594,6 +594,46 @@ def measure_extras(steps: int, warmup: int) -> dict:
             "row_max_only": {"kernel_ms": round(t2["kernel_ms_mean"], 5)}}
 
 
+def measure_dropout(steps: int, warmup: int) -> dict:
+    """Attention dropout (p = 0.1, the caller's keep mask) on the gqa workload (2): the
+    forward and the backward with the same mask. Flops as the dense paths (the mask
+    adds no products); the fused forward without dropout is the comparison."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(2)
+    inp = synth.make(2)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    kw = synth.pack_keep(synth.make_keep(s.B, s.H, s.Tq, s.Tk, 0.1, seed=2)).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.H, s.Tq), dtype=torch.float32, device="cuda")
+    A.reset_dispatch_counts()
+    t = time_steps(lambda: A.dense(q, k, v, causal=True, scale=s.scale, out=out, lse=lse, keep=kw, p_drop=0.1),
+                   steps, warmup)
+    if A.dispatch_count("dense_dropout_bf16") != t["calls"]:
+        raise RuntimeError("NotEngaged: the dropout forward did not run once per step")
+    dout = synth.make_dout(s).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, A.bwd_workspace_bytes(s.B, s.H, s.Hkv, s.Tq, s.Tk, s.d_qk, s.d_v)), dtype=torch.uint8,
+                     device="cuda")
+    tb = time_steps(lambda: A.dense_backward(q, k, v, out, dout, lse, causal=True, scale=s.scale, dq=dq, dk=dk,
+                                             dv=dv, workspace=ws, keep=kw, p_drop=0.1), steps, warmup)
+    fl = work(2)["flops"]
+    ach = fl / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    bach = bwd_flops(2) / (tb["kernel_ms_mean"] * 1e-3) / 1e12
+    log(f"[bench] dropout p=0.1: {describe(2)} | forward {t['kernel_ms_mean']:.4f} ms = {rl['achieved']} TFLOP/s | "
+        f"backward {tb['kernel_ms_mean']:.4f} ms = {bach:.1f} TFLOP/s")
+    return {"row": "attention dropout, keep mask shared by forward and backward", "workload": describe(2) + ", p=0.1",
+            "path": "dense_dropout_bf16", "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s", "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "backward": {"path": "dense_bwd_bf16_d128 (dropout)", "kernel_ms": round(tb["kernel_ms_mean"], 5),
+                         "tflops": round(bach, 2)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -830,6 +870,9 @@ def main():
         torch.cuda.empty_cache()
         # the forward's extra returns
         next_rows.append(measure_extras(max(3, st // 4), 1))
+        torch.cuda.empty_cache()
+        # attention dropout
+        next_rows.append(measure_dropout(st, wu))
         torch.cuda.empty_cache()
         # the sliding-window forward
         r = measure(7, st, wu)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 10
+#define ATTN_ABI_VERSION 11
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -107,6 +107,18 @@ typedef enum attn_dtype {
  *        0: one rope key row shared by every kv head, as MLA's decoupled
  *        rope key is. Compiled: bf16, d_qk = 192 with rope_dim = 64, d_v =
  *        128; ATTN_UNSUPPORTED otherwise.
+ *   keep, m_sb, m_sh, m_st, p_drop: attention dropout. keep = NULL: none.
+ *        Otherwise keep holds the keep bits of every (b, h, t, key): the
+ *        32-bit word at keep + b*m_sb + h*m_sh + t*m_st + w (strides in
+ *        words, m_st >= ceil(Tk/32)) has bit i set when key 32 w + i is kept.
+ *        out = (P * keep / (1 - p_drop)) V; lse is the softmax's, before the
+ *        dropout. The caller draws the mask and passes the same one to
+ *        attn_bwd_dense, so the two directions cannot disagree on it (the
+ *        TransformerEngine pull request 3259 review flags a backward that
+ *        lost the forward's dropout state). bf16 with the backward's head
+ *        dims (64,64), (128,128), (192,128); runs a separate, unfused-grade
+ *        kernel (dispatch path "dense_dropout_bf16"); the split-KV, packed,
+ *        plan and extra-return calls return ATTN_UNSUPPORTED for it.
  */
 typedef struct attn_dense_args {
   uint32_t struct_size; /* = sizeof(attn_dense_args) */
@@ -131,6 +143,9 @@ typedef struct attn_dense_args {
   int64_t qr_sb, qr_sh, qr_st;
   const void* k_rope;
   int64_t kr_sb, kr_sh, kr_st;
+  const uint32_t* keep; /* NULL: no dropout */
+  int64_t m_sb, m_sh, m_st;
+  float p_drop;         /* in [0, 1) */
 } attn_dense_args;
 
 /*
@@ -305,6 +320,9 @@ typedef struct attn_dense_bwd_args {
   float* dsinks;
   int32_t window_left;  /* -1: no left bound */
   int32_t window_right; /* -1: no right bound */
+  const uint32_t* keep; /* the forward's dropout mask (see attn_dense_args), or NULL */
+  int64_t m_sb, m_sh, m_st;
+  float p_drop;
 } attn_dense_bwd_args;
 
 /* Workspace bytes attn_bwd_dense needs: B*H*Tq*4 (the row dots

@@ -268,6 +268,25 @@ def make_sparse_dout(s: SparseSpec, *, seed: Optional[int] = None) -> torch.Tens
     return torch.randn((s.Sq, s.Hq, s.d_v), generator=g, dtype=torch.float32).to(torch.bfloat16)
 
 
+def make_keep(B: int, H: int, Tq: int, Tk: int, p_drop: float, *, seed: int = 0) -> torch.Tensor:
+    """A dropout keep mask [B,H,Tq,Tk] bool: each entry kept with probability
+    1 - p_drop, drawn by numpy default_rng(3000 + seed)."""
+    rng = np.random.default_rng(3000 + seed)
+    return torch.from_numpy(rng.random((B, H, Tq, Tk)) >= p_drop)
+
+
+def pack_keep(keep: torch.Tensor) -> torch.Tensor:
+    """Bit-pack a keep mask [..., Tk] into int32 words [..., ceil(Tk/32)]: bit i of
+    word w is entry 32 w + i (the layout the library reads)."""
+    Tk = keep.shape[-1]
+    nw = (Tk + 31) // 32
+    k = np.zeros(keep.shape[:-1] + (nw * 32,), dtype=np.uint64)
+    k[..., :Tk] = keep.numpy().astype(np.uint64)
+    k = k.reshape(keep.shape[:-1] + (nw, 32))
+    words = (k << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+    return torch.from_numpy(words.view(np.int32))
+
+
 def make(n: int) -> dict:
     s = spec(n)
     return make_dense(s) if s.kind == "dense" else make_sparse(s)
