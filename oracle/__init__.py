@@ -11,6 +11,8 @@ from .attention import (  # noqa: F401
     dense_attention_tiled,
     dense_attention_two_part,
     dense_attention_varlen,
+    decode_fp8_e4m3,
+    dequantize_fp8_rows,
     dequantize_rows,
     gather_rows,
     merge_partials,

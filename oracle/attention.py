@@ -415,6 +415,27 @@ def dequantize_rows(raw, fmt: str) -> np.ndarray:
     return vals.reshape(*lead, nb * 32)
 
 
+def decode_fp8_e4m3(codes) -> np.ndarray:
+    """OCP FP8 E4M3 bytes -> fp64, from the format's definition: sign bit 7, exponent
+    bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is subnormal (m / 8 * 2^-6);
+    the pattern S.1111.111 is NaN; there are no infinities (largest finite 448)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 0xF) & (m == 0x7), np.nan, val)
+    return sign * val
+
+
+def dequantize_fp8_rows(codes, scales, block: int = 128) -> np.ndarray:
+    """Pool rows stored as fp8 codes [N, d] with one scale per ``block`` columns
+    [N, d / block]: value = decode(code) * scale of its block."""
+    v = decode_fp8_e4m3(codes)
+    sc = np.repeat(_f64(scales), block, axis=1)
+    return v * sc
+
+
 def merge_partials(parts, sink: Optional[float] = None):
     """Merge (O_i, lse_i) computed over disjoint key sets into the full result.
 

@@ -239,6 +239,44 @@ def make_varlen(s: dict = VARLEN_PREFILL) -> dict:
     return {"q": q, "k": k, "v": v, "lens": lens, "cu": cu}
 
 
+# fp8 pool rows for the sparse decode: OCP e4m3 (1 sign, 4 exponent bits with
+# bias 7, 3 mantissa bits; largest finite 448) with one fp32 scale per
+# 128-column block of a row, scale = max|x| / 448 of the block, codes rounded
+# to nearest by torch's float8_e4m3fn conversion. Only the bytes and scales are
+# produced here; the oracle and the kernels decode them independently.
+FP8_BLOCK = 128
+FP8_MAX = 448.0
+
+
+def quantize_fp8_rows(x: torch.Tensor):
+    """x [N, d] float -> (codes uint8 [N, d], scales fp32 [N, d / 128])."""
+    a = x.detach().to(torch.float32).cpu()
+    N, d = a.shape
+    assert d % FP8_BLOCK == 0
+    blk = a.reshape(N, d // FP8_BLOCK, FP8_BLOCK)
+    sc = blk.abs().amax(dim=-1) / FP8_MAX
+    sc = torch.where(sc > 0, sc, torch.ones_like(sc))
+    codes = (blk / sc[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(N, d)
+    return codes.contiguous(), sc.contiguous()
+
+
+# The sparse decode over an fp8 pool: 128 decoding queries (one token each of
+# 128 sequences) x 64 heads, top-k 2048 of a 65536-row pool, d 512; seed 10.
+SPARSE_FP8_DECODE = {"name": "fp8decode", "Sq": 128, "Hq": 64, "N": 65536, "d": 512, "topk": 2048, "seed": 10}
+
+
+def make_sparse_fp8(Sq: int, Hq: int, N: int, d: int, topk: int, *, seed: int = 0, sinks: bool = False) -> dict:
+    """q [Sq,Hq,d] bf16, the pool quantized from N(0,1) rows (codes, scales), indices as
+    the sparse recipe draws them, sinks [Hq] or None; drawn in the order q, pool, sinks."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((Sq, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    pool = torch.randn((N, d), generator=g, dtype=torch.float32)
+    sk = torch.randn((Hq,), generator=g, dtype=torch.float32) if sinks else None
+    codes, scales = quantize_fp8_rows(pool)
+    idx = torch.from_numpy(make_indices(Sq, N, topk, seed))
+    return {"q": q, "codes": codes, "scales": scales, "idx": idx, "sinks": sk}
+
+
 def make_indices(Sq: int, N: int, topk: int, seed: int) -> np.ndarray:
     """[Sq, topk] int32, each row topk distinct values of [0, N), unsorted."""
     rng = np.random.default_rng(seed)

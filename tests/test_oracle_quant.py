@@ -63,3 +63,40 @@ def test_round_trip_within_one_step():
     y4 = oracle.dequantize_rows(synth.quantize_rows(x, "q4_0"), "q4_0").reshape(64, 4, 32)
     step4 = np.abs(xb).max(axis=2, keepdims=True) / 8
     assert (np.abs(y4 - xb) <= step4 * 1.01 + 1e-6).all()
+
+
+# ---------------------------------------------------------------------------- fp8 (OCP E4M3) pool rows
+FP8_CASES = [(0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0xB8, -1.0), (0x3C, 1.5),
+             (0x07, 7 / 8 * 2.0 ** -6), (0x00, 0.0), (0x46, 3.5), (0xFE, -448.0)]
+
+
+def test_fp8_decode_closed_forms():
+    """Values the E4M3 definition fixes: bias 7, subnormals below 2^-6, 448 the largest
+    finite value, S.1111.111 NaN."""
+    got = oracle.decode_fp8_e4m3(np.array([c for c, _ in FP8_CASES]))
+    assert np.array_equal(got, np.array([v for _, v in FP8_CASES]))
+    assert np.isnan(oracle.decode_fp8_e4m3(np.array([0x7F, 0xFF]))).all()
+
+
+def test_fp8_decode_equals_library():
+    """All 256 codes against torch's float8_e4m3fn (the same OCP format)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_fp8_e4m3(codes.numpy())
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_fp8_rows_blocks_and_quantizer():
+    """Each 128-column block takes its own scale; the quantizer's round trip stays within
+    half an E4M3 step (2^-4 relative) of the input."""
+    x = torch.randn(6, 512, generator=torch.Generator().manual_seed(3)) * torch.tensor([1.0, 10.0, 0.01, 3.0]
+                                                                                      ).repeat_interleave(128)
+    codes, scales = synth.quantize_fp8_rows(x)
+    y = oracle.dequantize_fp8_rows(codes.numpy(), scales.numpy())
+    for blk in range(4):
+        cols = slice(128 * blk, 128 * blk + 128)
+        assert np.allclose(y[:, cols], oracle.decode_fp8_e4m3(codes[:, cols].numpy()) * scales[:, blk:blk + 1].numpy())
+    err = np.abs(y - x.double().numpy())
+    assert (err <= np.abs(x.double().numpy()) * 2.0 ** -4 + scales.repeat_interleave(128, 1).double().numpy()
+            * 2.0 ** -10).all()
