@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -126,13 +126,30 @@ class AttnSparseBwdArgs(ctypes.Structure):
     ]
 
 
+class AttnSparseFp8Args(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("Sq", ctypes.c_int32), ("Hq", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_ss", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("codes", ctypes.c_void_p), ("c_sn", ctypes.c_int64),
+        ("scales", ctypes.c_void_p), ("s_sn", ctypes.c_int64),
+        ("indices", ctypes.c_void_p), ("idx_ss", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("o_ss", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = (
     "attn_abi_version", "attn_fwd_dense", "attn_fwd_sparse_topk", "attn_plan_dense",
     "attn_plan_sparse_topk", "attn_status_string", "attn_last_error", "attn_dispatch_count",
     "attn_reset_dispatch_counts", "attn_budget_tile_rows", "attn_fwd_dense_splitkv",
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
     "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen", "attn_bwd_sparse_topk",
-    "attn_bwd_sparse_workspace_bytes", "attn_fwd_dense_extras",
+    "attn_bwd_sparse_workspace_bytes", "attn_fwd_dense_extras", "attn_fwd_sparse_fp8",
+    "attn_sparse_fp8_workspace_bytes",
 )
 ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
 KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
@@ -231,6 +248,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_dense_extras.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_dense_extras.restype = ctypes.c_int
+    lib.attn_fwd_sparse_fp8.argtypes = [ctypes.POINTER(AttnSparseFp8Args), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    lib.attn_fwd_sparse_fp8.restype = ctypes.c_int
+    lib.attn_sparse_fp8_workspace_bytes.argtypes = [ctypes.POINTER(AttnSparseFp8Args), ctypes.c_int32]
+    lib.attn_sparse_fp8_workspace_bytes.restype = ctypes.c_int64
     v = lib.attn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"libattn_fwd.so ABI version {v}, binding expects {ABI_VERSION}")
@@ -584,6 +606,61 @@ def sparse_backward(q, kv, idx, out, dout, lse, *, d_v: Optional[int] = None, sc
     _check(lib.attn_bwd_sparse_topk(ctypes.byref(a), ctypes.c_void_p(ws_ptr), ws_bytes,
                                     ctypes.c_void_p(_stream_handle(stream))))
     return dq, dkv, dsinks
+
+
+def sparse_fp8(q, codes, scales, idx, *, scale: Optional[float] = None, sinks=None, n_splits: int = 0, out=None,
+               lse=None, workspace=None, stream=None):
+    """Sparse top-k decode over an fp8 pool: q [Sq,Hq,512] bf16, codes [N,512] uint8
+    (OCP E4M3), scales [N,4] fp32 (one per 128 columns), idx [Sq,topk] int32. Returns
+    (out [Sq,Hq,512] bf16, lse [Sq,Hq] fp32), the sparse forward over the decoded pool."""
+    import torch
+
+    lib = load_library()
+    Sq, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if idx.dtype != torch.int32 or codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "idx int32, codes uint8, scales fp32")
+    if out is None:
+        out = torch.empty((Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Sq, Hq), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("codes", codes), ("scales", scales), ("indices", idx), ("out", out)):
+        if t.stride(-1) != 1:
+            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
+    if not lse.is_contiguous() or tuple(lse.shape) != (Sq, Hq):
+        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [Sq, Hq]")
+    a = AttnSparseFp8Args()
+    a.struct_size = ctypes.sizeof(AttnSparseFp8Args)
+    a.Sq, a.Hq, a.N, a.d, a.topk = Sq, Hq, codes.shape[0], d, idx.shape[1]
+    a.scale = float(scale)
+    a.q, (a.q_ss, a.q_sh) = q.data_ptr(), q.stride()[:2]
+    a.codes, a.c_sn = codes.data_ptr(), codes.stride(0)
+    a.scales, a.s_sn = scales.data_ptr(), scales.stride(0)
+    a.indices, a.idx_ss = idx.data_ptr(), idx.stride(0)
+    a.out, (a.o_ss, a.o_sh) = out.data_ptr(), out.stride()[:2]
+    a.lse = lse.data_ptr()
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    need = int(lib.attn_sparse_fp8_workspace_bytes(ctypes.byref(a), int(n_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_fwd_sparse_fp8(ctypes.byref(a), int(n_splits), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                   ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+def sparse_fp8_workspace_bytes(Sq: int, Hq: int, N: int, d: int, topk: int, n_splits: int = 0) -> int:
+    """Workspace bytes of :func:`sparse_fp8` for these sizes (host only)."""
+    a = AttnSparseFp8Args()
+    a.struct_size = ctypes.sizeof(AttnSparseFp8Args)
+    a.Sq, a.Hq, a.N, a.d, a.topk = Sq, Hq, N, d, topk
+    a.scale = 1.0 / math.sqrt(d)
+    n = int(load_library().attn_sparse_fp8_workspace_bytes(ctypes.byref(a), int(n_splits)))
+    if n < 0:
+        _check(ATTN_INVALID_ARGUMENT)
+    return n
 
 
 _FAKE_PTR = 1 << 12  # never dereferenced: plans are computed on the host only

@@ -58,12 +58,15 @@ constexpr const char* kExtrasPath = "dense_extras_bf16";
 constexpr int kExtrasSlot = kSpBwdSlot - 1;
 constexpr const char* kDropPath = "dense_dropout_bf16";
 constexpr int kDropPathSlot = kExtrasSlot - 1;
+constexpr const char* kFp8Path = "sparse_fp8_d512";
+constexpr int kFp8Slot = kDropPathSlot - 1;
 
 int path_index(const char* path) {
   if (std::strcmp(path, kMergePath) == 0) return kMergeSlot;
   if (std::strcmp(path, kSpBwdPath) == 0) return kSpBwdSlot;
   if (std::strcmp(path, kExtrasPath) == 0) return kExtrasSlot;
   if (std::strcmp(path, kDropPath) == 0) return kDropPathSlot;
+  if (std::strcmp(path, kFp8Path) == 0) return kFp8Slot;
   for (int i = 0; i < 4; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
@@ -698,6 +701,105 @@ attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p_out, int64_
   const int err = attn::launch_extras(e, a->d_qk, stream);
   if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the extra returns failed: %s", hipGetErrorString((hipError_t)err));
   note_dispatch(kExtrasSlot, kExtrasPath);
+  return ATTN_OK;
+}
+
+// ---------------------------------------------------------------- sparse decode over an fp8 pool
+namespace {
+
+struct Fp8Plan {
+  int n, split_keys;
+  int64_t bytes;
+};
+
+static attn_status validate_fp8_shape(const attn_sparse_fp8_args* a) {
+  if (!a) return fail(ATTN_INVALID_ARGUMENT, "args is NULL");
+  if (a->struct_size != sizeof(attn_sparse_fp8_args))
+    return fail(ATTN_ABI_MISMATCH, "attn_sparse_fp8_args.struct_size = %u, library expects %zu", a->struct_size,
+                sizeof(attn_sparse_fp8_args));
+  if (a->Sq < 0 || a->Hq < 1 || a->N < 1 || a->topk < 0) return fail(ATTN_INVALID_ARGUMENT, "bad Sq/Hq/N/topk");
+  if (a->d != 512 || a->Hq != 64)
+    return fail(ATTN_UNSUPPORTED, "the fp8 sparse decode is compiled for d = 512 and Hq = 64 (got %d, %d)", a->d, a->Hq);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f)) return fail(ATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  return ATTN_OK;
+}
+
+// ranges of whole 32-slot steps: enough workgroups for two per CU, at most
+// 4096 slots (the kernel's index buffer) per range
+static Fp8Plan plan_fp8(const attn_sparse_fp8_args* a, int n_req) {
+  Fp8Plan pl;
+  const int steps = std::max(1, (a->topk + 31) / 32);
+  int n = n_req;
+  if (n <= 0) n = std::max(1, (512 + std::max(a->Sq, 1) - 1) / std::max(a->Sq, 1));
+  n = std::max(n, (a->topk + 4095) / 4096);
+  n = std::min(n, steps);
+  const int per = (steps + n - 1) / n;
+  pl.split_keys = per * 32;
+  pl.n = (steps + per - 1) / per;
+  const int64_t rows = (int64_t)a->Sq * a->Hq;
+  const int64_t b = (int64_t)pl.n * rows * (a->d + 1) * 4;
+  pl.bytes = b == 0 ? 0 : (b + 255) / 256 * 256;
+  return pl;
+}
+
+}  // namespace
+
+int64_t attn_sparse_fp8_workspace_bytes(const attn_sparse_fp8_args* a, int32_t n_splits) {
+  g_last_error.clear();
+  if (validate_fp8_shape(a) != ATTN_OK) return -1;
+  if (n_splits < 0 || n_splits > kMaxSplits) {
+    fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+    return -1;
+  }
+  return plan_fp8(a, n_splits).bytes;
+}
+
+attn_status attn_fwd_sparse_fp8(const attn_sparse_fp8_args* a, int32_t n_splits, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  attn_status st = validate_fp8_shape(a);
+  if (st != ATTN_OK) return st;
+  if (n_splits < 0 || n_splits > kMaxSplits)
+    return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+  if (a->Sq == 0) return ATTN_OK;
+  if (!a->q || !a->codes || !a->scales || !a->out || !a->lse || (a->topk > 0 && !a->indices))
+    return fail(ATTN_INVALID_ARGUMENT, "q, codes, scales, out, lse (and indices when topk > 0) must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->codes) || !aligned16(a->scales) || !aligned16(a->out) ||
+      !aligned16(a->lse) || !aligned16(a->sinks) || ((uintptr_t)a->indices & 3u))
+    return fail(ATTN_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (indices 4-byte)");
+  if (a->q_ss < 0 || a->q_sh < 0 || a->o_ss < 0 || a->o_sh < 0 || ((a->q_ss | a->q_sh | a->o_ss | a->o_sh) & 7))
+    return fail(ATTN_INVALID_ARGUMENT, "q and out strides must be >= 0 and multiples of 8 elements");
+  if (a->c_sn < a->d || (a->c_sn & 15) || a->s_sn < a->d / 128 || (a->s_sn & 3))
+    return fail(ATTN_INVALID_ARGUMENT, "code rows need >= d bytes (multiple of 16), scale rows >= d/128 floats (multiple of 4)");
+  if ((int64_t)a->N * a->c_sn >= ((int64_t)1 << 32) || (int64_t)a->N * a->s_sn * 4 >= ((int64_t)1 << 32))
+    return fail(ATTN_INVALID_ARGUMENT, "the pool must stay below 4 GiB of codes and of scales");
+  if (a->topk > 0 && a->idx_ss < a->topk) return fail(ATTN_INVALID_ARGUMENT, "index row stride smaller than topk");
+  const Fp8Plan pl = plan_fp8(a, n_splits);
+  if (pl.bytes > 0 && (workspace == nullptr || workspace_bytes < pl.bytes))
+    return fail(ATTN_INVALID_ARGUMENT, "the fp8 sparse decode needs a workspace of %lld bytes, got %lld",
+                (long long)pl.bytes, (long long)(workspace ? workspace_bytes : 0));
+  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  const int64_t rows = (int64_t)a->Sq * a->Hq;
+  attn::SpFp8Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.codes = a->codes; p.scales = a->scales; p.idx = a->indices;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + (int64_t)pl.n * rows * a->d;
+  p.q_ss = a->q_ss; p.q_sh = a->q_sh; p.c_sn = a->c_sn; p.s_sn = a->s_sn; p.idx_ss = a->idx_ss;
+  p.Sq = a->Sq; p.Hq = a->Hq; p.N = a->N; p.topk = a->topk; p.split_keys = pl.split_keys; p.n_splits = pl.n;
+  p.scale = a->scale;
+  p.c = a->scale * 1.4426950408889634f;
+  int err = attn::launch_sparse_fp8(p, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the fp8 sparse decode failed: %s", hipGetErrorString((hipError_t)err));
+  attn::MergeParams m;
+  std::memset(&m, 0, sizeof(m));
+  m.part_o = p.part_o; m.part_lse = p.part_lse; m.sinks = a->sinks; m.out = a->out; m.lse = a->lse;
+  m.o_sb = a->o_ss; m.o_sh = a->o_sh; m.o_st = 0;
+  m.B = a->Sq; m.H = a->Hq; m.Tq = 1; m.n_splits = pl.n; m.d_v = a->d; m.f32 = 0;
+  err = attn::launch_merge(m, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the merge failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kFp8Slot, kFp8Path);
+  note_dispatch(kMergeSlot, kMergePath);
   return ATTN_OK;
 }
 

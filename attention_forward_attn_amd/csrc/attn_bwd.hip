@@ -201,6 +201,20 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 }
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// vmcnt wait with a wave-uniform count (0..7)
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+  }
+}
 __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
@@ -966,6 +980,194 @@ __global__ void __launch_bounds__(256) fwd_dropout_kernel(const BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 8. Sparse top-k decode over an fp8 pool (the sparse fp8 decode the
+//    TensorRT-LLM page names among FlashMLA's kernels): pool rows of 512 OCP
+//    E4M3 codes with one fp32 scale per 128 columns, decoded in the kernel
+//    (only the gathered rows are ever converted, never the pool). One
+//    workgroup of 8 waves per (query, range of its slots); per step of 32
+//    slots the rows' codes and scales arrive by DMA into one of four staging
+//    buffers (three steps ahead, explicit vmcnt accounting) and the codes are
+//    decoded to a bf16 tile (exactly: an E4M3 value has 4 significant bits).
+//    Wave (hg, sq) forms S^T for heads 32 hg.. over columns 128 sq.., which
+//    is exactly one scale block, so it multiplies its partial by each key's
+//    scale of that block in fp32; the four partials are summed through LDS in
+//    a fixed order; the online softmax is per head; O^T += X^T (P s)^T on the
+//    wave's 128 output columns, the same block's scales applied to P before it
+//    is rounded for the product. No decoded value is ever rounded. Each range writes
+//    its normalised O and its lse without the sink; the split-KV merge adds
+//    the sink and combines the ranges.
+// ---------------------------------------------------------------------------
+constexpr int kFp8Stages = 4, kFp8IdxCap = 4096;
+
+__global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
+  constexpr int D = 512, BN = 32, CPX = D / 8;
+  constexpr int STG = BN * D;               // codes of one step
+  constexpr int SCB = BN * 16;              // scales of one step (4 per row)
+  constexpr int X_BYTES = BN * D * 2;       // the decoded bf16 tile
+  constexpr int XB_BYTES = 8 * 16 * 64 * 4; // partial S^T exchange
+  constexpr int NS = kFp8Stages, PD = NS - 1;
+  __shared__ __attribute__((aligned(1024))) unsigned char
+      smem[NS * STG + NS * SCB + X_BYTES + XB_BYTES + kFp8IdxCap * 4];
+  unsigned char* const stg = smem;
+  float* const scl = reinterpret_cast<float*>(smem + NS * STG);
+  bf16_t* const xt = reinterpret_cast<bf16_t*>(smem + NS * STG + NS * SCB);
+  float* const xb = reinterpret_cast<float*>(smem + NS * STG + NS * SCB + X_BYTES);
+  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + NS * STG + NS * SCB + X_BYTES + XB_BYTES);
+
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 1, sq = wave >> 1;
+  const int s = blockIdx.x, r = blockIdx.y;
+  const int hd = hg * 32 + lq;
+  const int k_lo = r * p.split_keys, k_hi = min(p.topk, k_lo + p.split_keys);
+  const int nk = max(0, k_hi - k_lo);
+  const int nblk = (nk + BN - 1) / BN;
+
+  // the range's slots into LDS (-1: past the range, or outside the pool)
+  const int32_t* ixrow = p.idx + (int64_t)s * p.idx_ss + k_lo;
+  for (int e = tid; e < nblk * BN; e += 512) {
+    const int ix = e < nk ? ixrow[e] : -1;
+    sidx[e] = (ix >= 0 && ix < p.N) ? ix : -1;
+  }
+  // B operands of S^T: this lane's head, columns 128 sq + 16 k + 8 lh
+  bf16x8 qf[8];
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)s * p.q_ss + (int64_t)hd * p.q_sh + sq * 128 + lh * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qp + k * 16);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) asm volatile("" ::"v"(qf[k]));  // wait for them here, not in the loop
+  }
+  __syncthreads();
+
+  // step j: wave w gathers rows 4w .. 4w+3 (two rows of 512 codes per
+  // instruction: lanes 0-31 the first, 32-63 the second); wave 0 also the 32
+  // rows' scales (16 bytes each, lanes 0-31). Skipped slots read row 0.
+  const uint32_t stg_s = lds_u32(stg), scl_s = lds_u32(scl);
+  auto issue = [&](int j) {
+    const uint32_t buf = (uint32_t)(j % NS);
+    const int myix = sidx[j * BN + lq];
+    const int myrow = myix < 0 ? 0 : myix;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r0 = wave * 4 + 2 * m;
+      const int ra = __builtin_amdgcn_readlane(myrow, r0), rb = __builtin_amdgcn_readlane(myrow, r0 + 1);
+      const int rowl = lh ? rb : ra;
+      dma16(p.codes, (uint32_t)rowl * (uint32_t)p.c_sn + 16u * (uint32_t)lq, stg_s + buf * STG + 512u * r0);
+    }
+    if (wave == 0 && lane < BN) dma16(p.scales, 4u * (uint32_t)myrow * (uint32_t)p.s_sn, scl_s + buf * SCB);
+  };
+  const int per_step = wave == 0 ? 3 : 2;  // this wave's loads of one step
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int j = 0; j < PD && j < nblk; ++j) issue(j);
+  for (int j = 0; j < nblk; ++j) {
+    // step j's loads have landed once at most the later steps' are in flight
+    wait_vmcnt_dyn(per_step * min(PD - 1, nblk - 1 - j));
+    barrier();
+    if (j + PD < nblk) issue(j + PD);
+    // decode step j: thread t takes row t/16, chunks t%16 + 16 i (i = scale block)
+    {
+      const uint32_t buf = (uint32_t)(j % NS);
+      const int row = tid >> 4, c0 = tid & 15;
+      const unsigned char* src = stg + buf * STG + row * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 16 * i;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(src + 8 * c);
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
+        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false), d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
+        *reinterpret_cast<u32x4*>(xt + chunk_at<CPX>(row, c)) =
+            u32x4{pack2(a[0], a[1]), pack2(b[0], b[1]), pack2(c2[0], c2[1]), pack2(d2[0], d2[1])};
+      }
+    }
+    barrier();
+    // partial S^T over columns 128 sq .. 128 sq + 127
+    f32x16 S;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) S = mfma32(row_frag<CPX>(xt, lq, sq * 8 + k, lh), qf[k], S);
+    // the scales of this lane's 16 keys for block sq (the wave's columns)
+    float ks[16];
+    {
+      const float* sc = scl + (j % NS) * (SCB / 4) + sq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ks[i] = sc[4 * (lh * 4 + 8 * (i >> 2) + (i & 3))];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] *= ks[i];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(xb + ((wave * 4 + g4) * 64 + lane) * 4) =
+          f32x4{S[g4 * 4], S[g4 * 4 + 1], S[g4 * 4 + 2], S[g4 * 4 + 3]};
+    barrier();
+    // the four partials of these heads, summed in the same order by all four waves
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 t4 = *reinterpret_cast<const f32x4*>(xb + (((hg + 0) * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+      for (int o = 1; o < 4; ++o) t4 += *reinterpret_cast<const f32x4*>(xb + (((hg + 2 * o) * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[g4 * 4 + e] = t4[e];
+    }
+    // S^T element i: slot j*32 + lh*4 + 8*(i/4) + i%4 of this lane's head
+    const uint32_t skip = (uint32_t)__ballot(sidx[j * BN + lq] < 0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((skip >> (lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) S[i] = -INFINITY;
+      mx = fmaxf(mx, S[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c);
+    m_run = mnew;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+    const float mc = (mnew == -INFINITY) ? 0.f : mnew * p.c;
+    float pr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -mc));
+      l_run += e;
+      pr[i] = e * ks[i];  // the values of these columns are code * scale
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pb = pack8(pr + ks * 8);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma32(tr_frag<CPX>(xt, ks * 16, sq * 128 + t * 32, lane), pb, acc[t]);
+    }
+  }
+
+  // this range's partial: O normalised by its own denominator, lse without the sink
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const bool any = m_run != -INFINITY && l > 0.f;
+  const float inv = any ? 1.f / l : 0.f;
+  const int64_t R = (int64_t)p.Sq * p.Hq, orow = (int64_t)r * R + (int64_t)s * p.Hq + hd;
+  float* const po = p.part_o + orow * D;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int col = sq * 128 + t * 32 + g4 * 8 + lh * 4;
+      *reinterpret_cast<f32x4*>(po + col) = f32x4{acc[t][g4 * 4] * inv, acc[t][g4 * 4 + 1] * inv,
+                                                  acc[t][g4 * 4 + 2] * inv, acc[t][g4 * 4 + 3] * inv};
+    }
+  if (sq == 0 && lh == 0) p.part_lse[orow] = any ? m_run * p.scale + __builtin_amdgcn_logf(l) * kLn2 : -INFINITY;
+}
+
 template <int DQK, int DV, bool DROP>
 int launch_bwd_cfg(const BwdParams& p, void* stream) {
   // dQ: two waves per SIMD where the registers allow it (d_qk + d_v <= 256)
@@ -1380,6 +1582,13 @@ int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream) {
     hipLaunchKernelGGL((fwd_dropout_kernel<192, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
   else
     return -1;
+  return (int)hipGetLastError();
+}
+
+int launch_sparse_fp8(const SpFp8Params& p, void* stream) {
+  if (p.Sq == 0) return 0;
+  hipLaunchKernelGGL(sparse_fp8_kernel, dim3((unsigned)p.Sq, (unsigned)p.n_splits), dim3(512), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 

@@ -146,6 +146,23 @@ struct ExtrasParams {
 int launch_extras(const ExtrasParams& p, int d_qk, void* stream);
 bool extras_supported(int d_qk);
 
+// Sparse top-k decode over an fp8 pool (OCP E4M3 codes, one fp32 scale per
+// 128 columns of a row; values = the decoded rows, d = 512, 64 heads): the
+// query's slots cut into ranges of split_keys (grid y), each writing its
+// normalised partial O and lse (no sink) for launch_merge.
+struct SpFp8Params {
+  const void* q;                 // bf16 [Sq, Hq, 512], strides q_ss, q_sh (elements)
+  const unsigned char* codes;    // [N, 512] bytes, row stride c_sn (bytes)
+  const float* scales;           // [N, 4], row stride s_sn (elements)
+  const int32_t* idx;            // [Sq, topk], row stride idx_ss
+  float* part_o;                 // [n_splits][Sq*Hq][512]
+  float* part_lse;               // [n_splits][Sq*Hq]
+  int64_t q_ss, q_sh, c_sn, s_sn, idx_ss;
+  int32_t Sq, Hq, N, topk, split_keys, n_splits;
+  float scale, c;
+};
+int launch_sparse_fp8(const SpFp8Params& p, void* stream);
+
 // Sparse top-k backward (d_qk = d_v = 512, 64 heads): zeroes dkv, then row
 // dots, sink gradients and the gradient kernel. 0 or a hipError_t.
 int launch_bwd_sparse(const BwdParams& p, void* stream);

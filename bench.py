@@ -634,6 +634,62 @@ def measure_dropout(steps: int, warmup: int) -> dict:
                          "tflops": round(bach, 2)}}
 
 
+def measure_sparse_fp8(steps: int, warmup: int) -> dict:
+    """Sparse top-k decode over an fp8 pool (synth.SPARSE_FP8_DECODE: 128 queries x 64
+    heads, top-k 2048 of 65536 rows), HBM bound: bytes = gathered codes (512 B per
+    slot) and scales (16 B per slot) + q + out + indices + lse. Beside it: the bf16
+    sparse path over the same pool decoded to bf16, and the sparse prefill shape
+    (workload 5's sizes) over an fp8 pool against the bf16 path."""
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.SPARSE_FP8_DECODE
+    res = {}
+    for tag, Sq in (("decode", s["Sq"]), ("prefill", synth.spec(5).Sq)):
+        inp = synth.make_sparse_fp8(Sq, s["Hq"], s["N"], s["d"], s["topk"] if tag == "decode" else synth.spec(5).topk,
+                                    seed=s["seed"])
+        q, codes, scales, idx = inp["q"].cuda(), inp["codes"].cuda(), inp["scales"].cuda(), inp["idx"].cuda()
+        topk = idx.shape[1]
+        scale = 1 / math.sqrt(s["d"])
+        out = torch.empty((Sq, s["Hq"], s["d"]), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((Sq, s["Hq"]), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, A.sparse_fp8_workspace_bytes(Sq, s["Hq"], s["N"], s["d"], topk)), dtype=torch.uint8,
+                         device="cuda")
+        A.reset_dispatch_counts()
+        t = time_steps(lambda: A.sparse_fp8(q, codes, scales, idx, scale=scale, out=out, lse=lse, workspace=ws),
+                       steps, warmup)
+        if A.dispatch_count("sparse_fp8_d512") != t["calls"]:
+            raise RuntimeError("NotEngaged: the fp8 sparse decode did not run once per step")
+        nbytes = Sq * topk * (s["d"] + 16) + 2 * q.numel() * 2 + idx.numel() * 4 + lse.numel() * 4
+        # the same attention over the pool decoded to bf16, on the bf16 sparse path
+        pool = (codes.cpu().view(torch.float8_e4m3fn).float()
+                * scales.cpu().repeat_interleave(128, dim=1)).to(torch.bfloat16).cuda()
+        t2 = time_steps(lambda: A.sparse_topk(q, pool, idx, d_v=s["d"], scale=scale, out=out, lse=lse), steps, warmup)
+        res[tag] = (t, nbytes, t2, Sq, topk)
+        del q, codes, scales, idx, out, lse, ws, pool
+        torch.cuda.empty_cache()
+    t, nbytes, t2, Sq, topk = res["decode"]
+    ach = nbytes / (t["kernel_ms_mean"] * 1e-3) / 1e9
+    rl = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    tp, nbp, t2p, Sqp, topkp = res["prefill"]
+    achp = nbp / (tp["kernel_ms_mean"] * 1e-3) / 1e9
+    log(f"[bench] sparse fp8 decode: Sq={Sq} Hq={s['Hq']} N={s['N']} topk={topk} | path sparse_fp8_d512 + merge | "
+        f"{t['kernel_ms_mean']:.4f} ms | {rl['achieved']} GB/s = {100 * rl['frac']:.1f}% of peak | bf16 pool "
+        f"{t2['kernel_ms_mean']:.4f} ms | prefill shape Sq={Sqp}: fp8 {tp['kernel_ms_mean']:.3f} ms ({achp:.0f} GB/s) "
+        f"vs bf16 {t2p['kernel_ms_mean']:.3f} ms")
+    return {"row": "sparse top-k decode over an fp8 pool (attn_fwd_sparse_fp8), in-kernel dequant",
+            "workload": f"fp8decode: Sq={Sq} Hq={s['Hq']} N={s['N']} d=512 topk={topk}, E4M3 codes + fp32 scale "
+                        f"per 128 columns",
+            "path": "sparse_fp8_d512 + splitkv_merge", "value": round(nbytes / (t["ms_per_step"] * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
+            "bf16_pool": {"path": "sparse_bf16_d512", "kernel_ms": round(t2["kernel_ms_mean"], 5)},
+            "prefill_shape": {"Sq": Sqp, "topk": topkp, "fp8_ms": round(tp["kernel_ms_mean"], 4),
+                              "fp8_GBps": round(achp, 1), "bf16_ms": round(t2p["kernel_ms_mean"], 4)}}
+
+
 def ceilings() -> dict:
     """Achievable MFMA and copy rates on this device (best of a few launches)."""
     import ctypes
@@ -857,6 +913,9 @@ def main():
             torch.cuda.empty_cache()
         # the sparse backward
         next_rows.append(measure_sparse_bwd(max(3, st // 4), 1))
+        torch.cuda.empty_cache()
+        # the sparse decode over an fp8 pool
+        next_rows.append(measure_sparse_fp8(max(5, st // 2), 2))
         torch.cuda.empty_cache()
         # decode over quantized caches
         for fmt in ("q8_0", "q4_0"):

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 11
+#define ATTN_ABI_VERSION 12
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -361,6 +361,47 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
  */
 attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p, int64_t p_sb, int64_t p_sh, int64_t p_st,
                                   float* row_max, void* stream);
+
+/*
+ * Sparse top-k decode over an fp8 pool: attn_fwd_sparse_topk's result with the
+ * pool stored as OCP FP8 E4M3 codes and one fp32 scale per 128 columns of a
+ * row (pool value = decoded code * scale; the sparse fp8 decode that the
+ * TensorRT-LLM page lists among FlashMLA's kernels). Only the gathered rows
+ * are decoded, inside the kernel; the values are the same decoded rows (V ==
+ * K, d_v = d). The query's slots are cut into n_splits ranges of whole
+ * 32-slot steps (0: the library's choice) whose normalised partial outputs
+ * and lse go to the workspace; one merge launch adds the sink and combines.
+ *
+ *   q      [Sq, Hq, d] bf16, strides q_ss, q_sh (elements)
+ *   codes  [N, d] uint8, row stride c_sn (bytes); scales [N, d/128] fp32,
+ *          row stride s_sn (elements); N * c_sn and N * s_sn * 4 below 2^32
+ *   indices, out, lse, sinks, scale as in attn_fwd_sparse_topk
+ *   workspace: attn_sparse_fp8_workspace_bytes(a, n_splits) bytes, 16-byte
+ *          aligned, caller-owned
+ * Compiled: d = 512, Hq = 64, topk <= 4096 per range. Dispatch path
+ * "sparse_fp8_d512" (+ "splitkv_merge").
+ */
+typedef struct attn_sparse_fp8_args {
+  uint32_t struct_size; /* = sizeof(attn_sparse_fp8_args) */
+  int32_t Sq, Hq, N, d, topk;
+  float scale;
+  const void* q;
+  int64_t q_ss, q_sh;
+  const uint8_t* codes;
+  int64_t c_sn;
+  const float* scales;
+  int64_t s_sn;
+  const int32_t* indices;
+  int64_t idx_ss;
+  void* out;
+  int64_t o_ss, o_sh;
+  float* lse;
+  const float* sinks;
+} attn_sparse_fp8_args;
+
+int64_t attn_sparse_fp8_workspace_bytes(const attn_sparse_fp8_args* a, int32_t n_splits);
+attn_status attn_fwd_sparse_fp8(const attn_sparse_fp8_args* a, int32_t n_splits, void* workspace,
+                                int64_t workspace_bytes, void* stream);
 
 /*
  * Sparse top-k backward: the gradients of attn_fwd_sparse_topk with respect
