@@ -1,4 +1,5 @@
-// Attention backward for AMD CDNA4 (gfx950 / MI355X), bf16 inputs.
+// Attention backward (and the kernels that share its tiling) for AMD CDNA4
+// (gfx950 / MI355X), bf16 inputs.
 //
 // Gradients of O = softmax(scale * Q K^T + mask [+ sink in the denominator]) V
 // with respect to q, k, v and the sinks, from the forward's inputs, its
@@ -33,6 +34,17 @@
 //                      are recomputed and dQ^T += K^T dS^T.
 //
 // Scores and probabilities never leave the CU; the only workspace is D.
+//
+// The file also holds the kernels built on the same tile helpers (row and
+// transposed fragment reads, DMA tile loads):
+//
+//  5. bwd_sparse_kernel   the sparse top-k backward (pool gradient by fp32
+//                         atomics), after a fill, the row dots and the sinks.
+//  6. extras_kernel       the forward's extra returns (probabilities, row
+//                         maxima) as a second pass from q, k and lse.
+//  7. fwd_dropout_kernel  the forward with a caller-drawn dropout mask (the
+//                         backward kernels above take the same mask).
+//  8. sparse_fp8_kernel   the sparse top-k decode over an fp8 pool.
 
 #include <hip/hip_runtime.h>
 #include <algorithm>
