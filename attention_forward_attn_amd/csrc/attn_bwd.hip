@@ -831,7 +831,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <int DQK, int DV>
-__global__ void __launch_bounds__(256) fwd_dropout_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+fwd_dropout_kernel(const BwdParams p) {
   constexpr int NW = 4, BN = 64, BM = 32 * NW;
   constexpr int CPK = DQK / 8, CPV = DV / 8;
   constexpr int KS = DQK / 16, DT = DV / 32, MT = BN / 32, PKS = BN / 16;
