@@ -130,16 +130,18 @@ static attn_status validate_keep(const Args* a, int Tq, int Tk) {
 // with its own L2. When the (batch, kv head) groups split evenly, every XCD
 // takes whole groups so that a group's K/V stays in one L2. An XCD runs 32
 // workgroups at once (one per CU); it works through its groups a chunk at a
-// time, the chunk holding at least two rounds of its CUs (so the
+// time, the chunk holding at least `rounds` rounds of its CUs (so the
 // longest-first order inside a chunk can balance them), so that concurrent
-// workgroups share their K/V in that XCD's L2.
-void plan_xcd(attn::KernelParams& p) {
+// workgroups share their K/V in that XCD's L2. Measured: four rounds for
+// dense launches (gqa +1.1% over two, mla unchanged), two for packed
+// batches, whose tiles past a short sequence are empty (four cost 11%).
+void plan_xcd(attn::KernelParams& p, int rounds = 4) {
   p.xcd_groups = ((p.aligned || p.fold_tm) && p.n_groups % 8 == 0) ? 1 : 0;
   p.xcd_chunk = 0;
   if (!p.xcd_groups) return;
   const int gpx = p.n_groups / 8;
   const int per_group = p.fold_tm ? p.tiles_per_group : p.g * p.tiles_per_head;
-  const int want = (64 + per_group - 1) / per_group;
+  const int want = (32 * rounds + per_group - 1) / per_group;
   int chunk = gpx;
   for (int c = 1; c <= gpx; ++c)
     if (gpx % c == 0 && c >= want) {
@@ -1074,7 +1076,7 @@ attn_status attn_fwd_varlen(const attn_varlen_args* a, void* stream) {
   const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
   if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   p.n_tiles = (int)tiles;
-  plan_xcd(p);
+  plan_xcd(p, 2);
   return do_launch(dp, stream);
 }
 
