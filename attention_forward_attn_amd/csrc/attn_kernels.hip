@@ -780,7 +780,11 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG>
+// XK (one wave group, DS > 1, dense): the K ring has one slot more than the
+// V ring and no separate score-exchange buffer; the partial scores of key
+// block j are exchanged in the K slot block j was read from, once every wave
+// has read it. The LDS saved keeps a second K block in flight.
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, bool XK = false>
 struct DCfg {
   static constexpr int NT = NW * 64;
   static constexpr int NQG = NW / DS;
@@ -802,16 +806,20 @@ struct DCfg {
   // V block j in the two halves of step j+1; with one group both are read in
   // step j. K block j+KD (V block j+VD) is loaded while step j runs, into the
   // ring slot of a block nobody reads any more.
-  static constexpr int KD = (PP && SPARSE) ? NBUF - 2 : NBUF - 1;
+  static constexpr int NBK = XK ? NBUF + 1 : NBUF;  // K ring slots
+  static constexpr int KD = XK ? NBK - 1 : (PP && SPARSE) ? NBUF - 2 : NBUF - 1;
   static constexpr int VD = PP ? NBUF - 2 : NBUF - 1;
   static constexpr int NIK = BN * CPRK / 64;     // wave instructions per K tile
   static constexpr int NIV = SPARSE ? 0 : BN * CPRV / 64;
-  static constexpr int SX_BYTES = (DS > 1) ? NW * MT * 16 * 64 * 4 : 0;
+  static constexpr int SX_PART_BYTES = NW * MT * 16 * 64 * 4;  // partial scores of one key block
+  static constexpr int SX_BYTES = (DS > 1 && !XK) ? SX_PART_BYTES : 0;
   static constexpr int IDX_CAP = SPARSE ? 4096 : 0;
-  static constexpr int KRING_BYTES = NBUF * K_ELEMS * 2;
+  static constexpr int KRING_BYTES = NBK * K_ELEMS * 2;
   static constexpr int VRING_BYTES = NBUF * V_ELEMS * 2;
   static constexpr int LDS_BYTES = KRING_BYTES + VRING_BYTES + SX_BYTES + IDX_CAP * 4;
   static_assert(KD >= 1, "at least one key step of prefetch");
+  static_assert(!XK || (!PP && !SPARSE && DS > 1 && SX_PART_BYTES <= K_ELEMS * 2),
+                "the exchange fits in a K slot of the one-group dense kernel");
   static constexpr int NLOADW = PP ? NW / 2 : NW;  // waves sharing one tile's loads
   static_assert((KD - 1) * ((NIK + NLOADW - 1) / NLOADW + (NIV + NLOADW - 1) / NLOADW) <= 31, "vmcnt wait range");
   static_assert(CPRK >= 8 && (SPARSE || CPRV >= 8), "swizzle needs 8 chunks per row");
@@ -823,10 +831,10 @@ struct DCfg {
 
 // ROPE > 0: the last ROPE columns of q and k come from q2 / k2 (MLA's rope
 // part read in place); the other DQK - ROPE from q / k.
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, int ROPE = 0>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, int ROPE = 0, bool XK = false>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_dma_kernel(const KernelParams p) {
-  using C = DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG>;
+  using C = DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, XK>;
   static_assert(ROPE == 0 || (!SPARSE && DS == 1 && (DQK - ROPE) % 16 == 0 && ROPE % 16 == 0),
                 "two-part rows: one wave holds the whole row, both parts whole K steps");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
@@ -1079,7 +1087,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
     const int blk = __builtin_amdgcn_readfirstlane(blk_in);
     uint32_t kr = kring_s + 1024u * lw_;  // this wave's first instruction slot
     asm volatile("" : "+s"(kr));
-    const uint32_t Kb = kr + (uint32_t)((blk % NBUF) * C::K_ELEMS * 2);
+    const uint32_t Kb = kr + (uint32_t)((blk % C::NBK) * C::K_ELEMS * 2);
     const int key0 = blk * BN;
     if constexpr (ROPE > 0) {
       // two-part rows: the tile row is laid out as one DQK-wide row, chunk c
@@ -1271,7 +1279,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // through LDS when DS > 1
   auto doS = [&](int blk) {
     {
-      const bf16_t* Kb = kring + (blk % NBUF) * C::K_ELEMS;
+      const bf16_t* Kb = kring + (blk % C::NBK) * C::K_ELEMS;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -1286,7 +1294,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
           S[mt] = mfma32(a, qf[s], S[mt]);
         }
       }
-      if constexpr (DS > 1) {
+      if constexpr (DS > 1 && !XK) {
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -1304,8 +1312,21 @@ attn_fwd_dma_kernel(const KernelParams p) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, PD, 0);
-      if constexpr (DS > 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4 * C::MT, 0);
+      if constexpr (DS > 1 && !XK) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4 * C::MT, 0);
     }
+  };
+  // XK: the partial scores of block blk go into the K slot it was read from
+  auto sx_of = [&](int blk) -> float* {
+    return XK ? reinterpret_cast<float*>(kring + (blk % C::NBK) * C::K_ELEMS) : sx;
+  };
+  auto publishS = [&](int blk) {
+    float* const d = sx_of(blk);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(d + (((wave * C::MT + mt) * 4 + g4) * 64 + lane) * 4) =
+            f32x4{S[mt][g4 * 4], S[mt][g4 * 4 + 1], S[mt][g4 * 4 + 2], S[mt][g4 * 4 + 3]};
   };
 
   // O += V(blk)^T P(blk), V^T fragments by transposed LDS reads; the output
@@ -1313,7 +1334,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // measured faster for the wide slices)
   auto doPV = [&](int blk) {
     {
-      const bf16_t* Vb = SPARSE ? kring + (blk % NBUF) * C::K_ELEMS : vring + (blk % NBUF) * C::V_ELEMS;
+      const bf16_t* Vb = SPARSE ? kring + (blk % C::NBK) * C::K_ELEMS : vring + (blk % NBUF) * C::V_ELEMS;
       if constexpr (LEAN) asm volatile("" : "+v"(v0[0]), "+v"(v0[1]), "+v"(vx[0]), "+v"(vx[1]));
 #pragma unroll
       for (int ks = 0; ks < C::PKS; ++ks) {
@@ -1349,6 +1370,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   auto phase2 = [&](int blk) {
     const int key0 = blk * BN;
     if constexpr (DS > 1) {
+      const float* const sxb = sx_of(blk);
 #pragma unroll
       for (int o = 1; o < DS; ++o) {
         const int w2 = qg * DS + (dsi + o) % DS;
@@ -1356,7 +1378,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sx + (((w2 * C::MT + mt) * 4 + g4) * 64 + lane) * 4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sxb + (((w2 * C::MT + mt) * 4 + g4) * 64 + lane) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[mt][g4 * 4 + e] += v[e];
           }
@@ -1488,8 +1510,14 @@ attn_fwd_dma_kernel(const KernelParams p) {
       issue_v(i);
     };
     for (int i = -C::KD; i < 0; ++i) {
-      if (!C::PP || wgrp == 0) issue_k(i);
-      if (!C::PP || wgrp == 1) issue_v(i);
+      if constexpr (XK) {
+        // issue order K 0, V 0, K 1: at step j only K block j+1 may stay in flight
+        issue_v(i);
+        issue_k(i);
+      } else {
+        if (!C::PP || wgrp == 0) issue_k(i);
+        if (!C::PP || wgrp == 1) issue_v(i);
+      }
     }
     // wait until K block i and V block i-1 (two groups) or V block i (one
     // group) have landed: they were issued at B(2(i-KD)), later loads may
@@ -1531,6 +1559,22 @@ attn_fwd_dma_kernel(const KernelParams p) {
             issue_v(t >> 1);
           if (j < nb) phase2(j);
         }
+      }
+    } else if constexpr (XK) {
+      // step j: V block j+1 and K block j+2 are issued (in that order) into
+      // the slots step j-1 finished with, before the S product; the partial
+      // scores are exchanged in K block j's slot between two barriers
+      for (int j = 0; j < nb; ++j) {
+        wait_vmcnt_dyn(j + 1 < nb ? myK : 0);  // K block j and V block j have landed
+        lds_barrier();
+        issue_v(j);
+        issue_k(j);
+        doS(j);
+        lds_barrier();  // every wave has read K block j
+        publishS(j);
+        lds_barrier();
+        phase2(j);
+        doPV(j);
       }
     } else {
       for (int j = 0; j < nb; ++j) {
@@ -1601,11 +1645,11 @@ attn_fwd_dma_kernel(const KernelParams p) {
   }
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false>
 int occupancy_dma() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE>),
+          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK>),
           NW * 64, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -1613,9 +1657,9 @@ int occupancy_dma() {
   return n;
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false>
 int launch_dma(const KernelParams& p, void* stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE>),
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK>),
                      dim3(p.n_tiles, p.n_splits > 1 ? p.n_splits : 1), dim3(NW * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
@@ -1690,6 +1734,13 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) 
         &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, ROPE>, ROPE                                          \
   }
 
+#define DMA_ENTRY_XK(NAME, DQK, DV, DS, NW, BN, NBUF, PP, XK)                                                    \
+  KernelConfig {                                                                                                 \
+    NAME, 0, DQK, DV, false, DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP, XK>::BM, BN, NW,                          \
+        DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP, XK>::LDS_BYTES, &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, 0, XK>, \
+        &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, 0, XK>                                              \
+  }
+
 #define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
   KernelConfig {                                                                                                 \
     NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::BM, BN, NW,                           \
@@ -1727,6 +1778,7 @@ int launch(const KernelParams& p, void* stream) {
 // DMA_ENTRY_X expands them first
 #define DMA_ENTRY_X(...) DMA_ENTRY(__VA_ARGS__)
 #define DMA_ENTRY_ROPE_X(...) DMA_ENTRY_ROPE(__VA_ARGS__)
+#define DMA_ENTRY_XK_X(...) DMA_ENTRY_XK(__VA_ARGS__)
 #ifndef ATTN_CFG_D64
 #define ATTN_CFG_D64 1, 8, 64, 3, true
 #endif
@@ -1742,6 +1794,9 @@ int launch(const KernelParams& p, void* stream) {
 #ifndef ATTN_CFG_D512
 #define ATTN_CFG_D512 2, 8, 32, 2, false
 #endif
+#ifndef ATTN_D512_XK
+#define ATTN_D512_XK true
+#endif
 #ifndef ATTN_CFG_SPARSE
 #define ATTN_CFG_SPARSE 4, 8, 32, 3, false
 #endif
@@ -1752,7 +1807,7 @@ const KernelConfig kTable[] = {
     DMA_ENTRY_X("dense_bf16_d192_v128", 192, 128, ATTN_CFG_D192, false),
     DMA_ENTRY_ROPE_X("dense_bf16_d192_v128_rope64", 192, 128, 64, ATTN_CFG_D192),
     DMA_ENTRY_X("dense_bf16_d256", 256, 256, ATTN_CFG_D256, false),
-    DMA_ENTRY_X("dense_bf16_d512", 512, 512, ATTN_CFG_D512, false),
+    DMA_ENTRY_XK_X("dense_bf16_d512", 512, 512, ATTN_CFG_D512, ATTN_D512_XK),
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
     CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
     DMA_ENTRY_X("sparse_bf16_d512", 512, 512, ATTN_CFG_SPARSE, true),
