@@ -83,6 +83,16 @@ def test_dense_bf16_sinks(dqk, dv):
     check_dense_full(inp, causal=True, scale=1 / math.sqrt(dqk), label=f"sinks d{dqk}")
 
 
+@pytest.mark.parametrize("Tk", [1, 32, 33, 65, 97, 129])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_d512_few_key_blocks(Tk, causal):
+    """The 512-wide kernel keeps up to two K blocks and one V block in flight ahead of
+    the block it reads: one to five 32-key blocks, whole and ragged, cover its prologue
+    and the steps where fewer loads are pending."""
+    inp = synth.randn_dense(1, 16, 1, 40, Tk, 512, 512, dtype="bf16", sinks=True, seed=900 + Tk)
+    check_dense_full(inp, causal=causal, scale=1 / math.sqrt(512), label=f"d512 Tk{Tk}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_dense_f32_split(d, causal):
