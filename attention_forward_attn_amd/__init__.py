@@ -303,6 +303,62 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _bad(msg: str):
+    raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, msg)
+
+
+def _expect(t, name: str, shape=None, dtype=None, contiguous: bool = False):
+    """A tensor argument: its shape (None entries are free), dtype and layout.
+    The C library sees only pointers and sizes, so a tensor that does not match
+    the sizes taken from the others would be read or written out of bounds."""
+    if t is None:
+        _bad(f"{name} is required")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and int(t.shape[i]) != int(s) for i, s in enumerate(shape)):
+            want = "[" + ", ".join("*" if s is None else str(int(s)) for s in shape) + "]"
+            _bad(f"{name} must have shape {want}, got {list(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        _bad(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        _bad(f"{name} must be contiguous")
+    if t.dim() > 0 and t.numel() > 0 and t.stride(-1) != 1:
+        _bad(f"{name}: last dimension must be contiguous")
+
+
+def _on_device(**tensors):
+    """Every given tensor lives on one GPU (a host tensor would hand the kernels a
+    host pointer)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            _bad(f"{name} must be a GPU tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            _bad(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _check_dense(q, k, v, out, lse, sinks, q_rope=None, k_rope=None, device=True):
+    """Shapes, dtypes and devices of a dense call: q [B,H,Tq,d], k [B,Hkv,Tk,d],
+    v [B,Hkv,Tk,d_v], out [B,H,Tq,d_v] in q's dtype, lse fp32 [B,H,Tq] contiguous,
+    sinks fp32 [H] contiguous."""
+    import torch
+
+    _expect(q, "q", (None, None, None, None))
+    B, H, Tq, dqk = q.shape
+    _expect(k, "k", (B, None, None, dqk), q.dtype)
+    Hkv, Tk = k.shape[1], k.shape[2]
+    _expect(v, "v", (B, Hkv, Tk, None), q.dtype)
+    _expect(out, "out", (B, H, Tq, v.shape[-1]), q.dtype)
+    _expect(lse, "lse", (B, H, Tq), torch.float32, contiguous=True)
+    if sinks is not None:
+        _expect(sinks, "sinks", (H,), torch.float32, contiguous=True)
+    if device:
+        _on_device(q=q, k=k, v=v, out=out, lse=lse, sinks=sinks, q_rope=q_rope, k_rope=k_rope)
+
+
 def _set_keep(a, keep, p_drop: float, B: int, H: int, Tq: int, Tk: int):
     """Dropout fields: ``keep`` int32 [B,H,Tq,ceil(Tk/32)] bit-packed keep mask (bit i
     of word w = key 32 w + i, as ``synth.pack_keep`` writes), or None."""
@@ -313,6 +369,7 @@ def _set_keep(a, keep, p_drop: float, B: int, H: int, Tq: int, Tk: int):
     if keep.dtype != torch.int32 or keep.dim() != 4 or tuple(keep.shape[:3]) != (B, H, Tq) or keep.stride(-1) != 1 \
             or keep.shape[3] < (Tk + 31) // 32:
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "keep must be int32 [B, H, Tq, ceil(Tk/32)] (bit-packed)")
+    _on_device(keep=keep)
     a.keep, (a.m_sb, a.m_sh, a.m_st) = keep.data_ptr(), keep.stride()[:3]
     a.p_drop = float(p_drop)
 
@@ -325,6 +382,7 @@ def dense_args(q, k, v, out, lse, *, causal: bool, scale: float, sinks=None,
     With ``q_rope`` [B,H,Tq,r] and ``k_rope`` [B,Hkv,Tk,r] the query and key rows are
     [q || q_rope] and [k || k_rope] (d_qk = q's width + r), read in place; a rope key
     shared by the kv heads is passed as an expanded view (head stride 0)."""
+    _check_dense(q, k, v, out, lse, sinks, q_rope, k_rope)
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
     dv = v.shape[-1]
@@ -381,6 +439,8 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
     import torch
 
     lib = load_library()
+    _expect(q, "q", (None, None, None, None))
+    _expect(v, "v", (None, None, None, None))
     B, H, Tq, dqk = q.shape
     dv = v.shape[-1]
     if scale is None:
@@ -389,10 +449,6 @@ def dense(q, k, v, *, causal: bool = True, scale: Optional[float] = None, sinks=
         out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
-    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
-    if not lse.is_contiguous():
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
     a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window, q_rope=q_rope,
                    k_rope=k_rope, keep=keep, p_drop=p_drop)
     _check(lib.attn_fwd_dense(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
@@ -409,6 +465,8 @@ def dense_extras(q, k, v, out, lse, *, causal: bool = True, scale: Optional[floa
     import torch
 
     lib = load_library()
+    _expect(q, "q", (None, None, None, None))
+    _expect(v, "v", (None, None, None, None))
     B, H, Tq, dqk = q.shape
     Tk = k.shape[2]
     if scale is None:
@@ -443,6 +501,8 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
     import torch
 
     lib = load_library()
+    _expect(q, "q", (None, None, None, None))
+    _expect(v, "v", (None, None, None, None))
     B, H, Tq, dqk = q.shape
     dv = v.shape[-1]
     if scale is None:
@@ -451,10 +511,6 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
         out = torch.empty((B, H, Tq, dv), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
-    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "sinks must be contiguous fp32 [H]")
-    if not lse.is_contiguous():
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous")
     a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window, q_rope=q_rope,
                    k_rope=k_rope)
     need = int(lib.attn_splitkv_workspace_bytes(ctypes.byref(a), int(n_splits)))
@@ -506,7 +562,27 @@ def splitkv_choose(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype: str = "bf16", causal:
     return n
 
 
+def _check_sparse(q, kv, idx, out, lse, sinks, d_v: int, device=True):
+    """q [Sq,Hq,d_qk], kv [N,>=d_qk] in q's dtype, idx int32 [Sq,topk],
+    out [Sq,Hq,d_v], lse fp32 [Sq,Hq] contiguous, sinks fp32 [Hq] contiguous."""
+    import torch
+
+    _expect(q, "q", (None, None, None))
+    Sq, Hq, dqk = q.shape
+    _expect(kv, "kv", (None, None), q.dtype)
+    if kv.shape[1] < dqk:
+        _bad(f"kv rows hold {kv.shape[1]} values, q rows {dqk}")
+    _expect(idx, "indices", (Sq, None), torch.int32)
+    _expect(out, "out", (Sq, Hq, d_v), q.dtype)
+    _expect(lse, "lse", (Sq, Hq), torch.float32, contiguous=True)
+    if sinks is not None:
+        _expect(sinks, "sinks", (Hq,), torch.float32, contiguous=True)
+    if device:
+        _on_device(q=q, kv=kv, indices=idx, out=out, lse=lse, sinks=sinks)
+
+
 def sparse_args(q, kv, idx, out, lse, *, d_v: int, scale: float, sinks=None) -> AttnSparseArgs:
+    _check_sparse(q, kv, idx, out, lse, sinks, d_v)
     Sq, Hq, dqk = q.shape
     N = kv.shape[0]
     a = AttnSparseArgs()
@@ -576,13 +652,13 @@ def sparse_backward(q, kv, idx, out, dout, lse, *, d_v: Optional[int] = None, sc
         dkv = torch.empty((N, dqk), dtype=torch.float32, device=q.device)
     if sinks is not None and dsinks is None:
         dsinks = torch.empty_like(sinks)
-    for name, t in (("q", q), ("kv", kv), ("indices", idx), ("out", out), ("dout", dout), ("dq", dq), ("dkv", dkv)):
-        if t.stride(-1) != 1:
-            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
-    if dkv.dtype != torch.float32 or tuple(dkv.shape) != (N, dqk):
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "dkv must be fp32 [N, d_qk]")
-    if not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [Sq, Hq]")
+    _check_sparse(q, kv, idx, out, lse, sinks, d_v, device=False)
+    _expect(dout, "dout", tuple(out.shape), out.dtype)
+    _expect(dq, "dq", tuple(q.shape), q.dtype)
+    _expect(dkv, "dkv", (N, dqk), torch.float32)
+    if dsinks is not None:
+        _expect(dsinks, "dsinks", (Hq,), torch.float32, contiguous=True)
+    _on_device(q=q, kv=kv, indices=idx, out=out, lse=lse, sinks=sinks, dout=dout, dq=dq, dkv=dkv, dsinks=dsinks)
     a = AttnSparseBwdArgs()
     a.struct_size = ctypes.sizeof(AttnSparseBwdArgs)
     a.dtype = _dtype_code(q)
@@ -625,11 +701,16 @@ def sparse_fp8(q, codes, scales, idx, *, scale: Optional[float] = None, sinks=No
         out = torch.empty((Sq, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((Sq, Hq), dtype=torch.float32, device=q.device)
-    for name, t in (("q", q), ("codes", codes), ("scales", scales), ("indices", idx), ("out", out)):
-        if t.stride(-1) != 1:
-            raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"{name}: last dimension must be contiguous")
-    if not lse.is_contiguous() or tuple(lse.shape) != (Sq, Hq):
-        raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be contiguous fp32 [Sq, Hq]")
+    _expect(q, "q", (Sq, Hq, d), torch.bfloat16)
+    _expect(codes, "codes", (None, d))
+    N = codes.shape[0]
+    _expect(scales, "scales", (N, d // 128))
+    _expect(idx, "indices", (Sq, None))
+    _expect(out, "out", (Sq, Hq, d), torch.bfloat16)
+    _expect(lse, "lse", (Sq, Hq), torch.float32, contiguous=True)
+    if sinks is not None:
+        _expect(sinks, "sinks", (Hq,), torch.float32, contiguous=True)
+    _on_device(q=q, codes=codes, scales=scales, indices=idx, out=out, lse=lse, sinks=sinks)
     a = AttnSparseFp8Args()
     a.struct_size = ctypes.sizeof(AttnSparseFp8Args)
     a.Sq, a.Hq, a.N, a.d, a.topk = Sq, Hq, codes.shape[0], d, idx.shape[1]
@@ -719,6 +800,16 @@ def abi_version() -> int:
 def dense_bwd_args(q, k, v, out, dout, lse, dq, dk, dv, *, causal: bool, scale: float, sinks=None,
                    dsinks=None, window: Tuple[int, int] = (-1, -1), keep=None, p_drop: float = 0.0) -> AttnDenseBwdArgs:
     """Fill the backward's C argument struct from tensors (unit last stride)."""
+    import torch
+
+    _check_dense(q, k, v, out, lse, sinks, device=False)
+    _expect(dout, "dout", tuple(out.shape), q.dtype)
+    _expect(dq, "dq", tuple(q.shape), q.dtype)
+    _expect(dk, "dk", tuple(k.shape), q.dtype)
+    _expect(dv, "dv", tuple(v.shape), q.dtype)
+    if dsinks is not None:
+        _expect(dsinks, "dsinks", (q.shape[1],), torch.float32, contiguous=True)
+    _on_device(q=q, k=k, v=v, out=out, lse=lse, sinks=sinks, dout=dout, dq=dq, dk=dk, dv=dv, dsinks=dsinks)
     B, H, Tq, dqk = q.shape
     _, Hkv, Tk, _ = k.shape
     a = AttnDenseBwdArgs()
@@ -809,15 +900,23 @@ def qkv_args(q, k, v, out, lse, *, fmt: str, causal: bool, scale: float, sinks=N
     [B,Hkv,Tk,row bytes] in llama.cpp's ``fmt`` ("q8_0" or "q4_0") blocks."""
     import torch
 
+    _expect(q, "q", (None, None, None, None), torch.bfloat16)
     B, H, Tq, d = q.shape
+    _expect(k, "k", (B, None, None, None))
     _, Hkv, Tk, _ = k.shape
     if k.dtype != torch.uint8 or v.dtype != torch.uint8:
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "k, v must be uint8 block data")
+    _expect(v, "v", (B, Hkv, Tk, None))
+    _expect(out, "out", (B, H, Tq, d), torch.bfloat16)
+    _expect(lse, "lse", (B, H, Tq), torch.float32, contiguous=True)
+    if sinks is not None:
+        _expect(sinks, "sinks", (H,), torch.float32, contiguous=True)
     if fmt not in KV_FORMATS:
         raise AttnUnsupported(ATTN_UNSUPPORTED, f"kv format {fmt!r}")
     row_bytes = d // 32 * (34 if fmt == "q8_0" else 18)
     if d % 32 != 0 or k.shape[-1] != row_bytes or v.shape[-1] != row_bytes:
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, f"k, v rows must hold {row_bytes} bytes ({fmt}, d={d})")
+    _on_device(q=q, k=k, v=v, out=out, lse=lse, sinks=sinks)
     a = AttnQkvArgs()
     a.struct_size = ctypes.sizeof(AttnQkvArgs)
     a.kv_format = KV_FORMATS[fmt]
@@ -894,6 +993,11 @@ def dense_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *, caus
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "v must be [total_k, Hkv, d_v] and out [total_q, H, d_v]")
     if tuple(lse.shape) != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise AttnInvalidArgument(ATTN_INVALID_ARGUMENT, "lse must be a contiguous fp32 [H, total_q] tensor")
+    _expect(k, "k", (None, None, dqk), q.dtype)
+    _expect(v, "v", (total_k, Hkv, None), q.dtype)
+    if sinks is not None:
+        _expect(sinks, "sinks", (H,), torch.float32, contiguous=True)
+    _on_device(q=q, k=k, v=v, out=out, lse=lse, sinks=sinks, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     a = AttnVarlenArgs()
     a.struct_size = ctypes.sizeof(AttnVarlenArgs)
     a.dtype = _dtype_code(q)

@@ -4,7 +4,6 @@ Importable by the tests, the package smoke check and the bench's CPU-baseline
 leg; never by the product path.
 """
 from .attention import (  # noqa: F401
-    causal_visible,
     dense_attention,
     dense_attention_backward,
     dense_attention_extras,

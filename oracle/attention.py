@@ -83,11 +83,6 @@ def repeat_kv(x: np.ndarray, n_rep: int) -> np.ndarray:
     return y
 
 
-def causal_visible(t: int, j: int, Tq: int, Tk: int) -> bool:
-    """Bottom-right aligned causal mask: key j visible to query row t."""
-    return j <= t + (Tk - Tq)
-
-
 def _causal_mask(ts, Tq: int, Tk: int) -> np.ndarray:
     """Boolean [len(ts), Tk]: True where key j is visible to query token t."""
     j = np.arange(Tk)[None, :]

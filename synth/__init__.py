@@ -347,3 +347,115 @@ def randn_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, *, dtype="bf16", sinks=False, seed
 def randn_sparse(Sq, Hq, N, d_qk, topk, *, seed=0, sinks=False):
     s = SparseSpec("adhoc", seed, Sq, Hq, N, d_qk, d_qk, topk, sinks)
     return make_sparse(s)
+
+
+# ---------------------------------------------------------------------------
+# Wide-dynamic-range inputs. With N(0,1) rows at scale 1/sqrt(d) a row's
+# largest score is reached in its first key blocks, so an online softmax
+# never has to move its running maximum later in the row. These variants
+# reshape the same seeded draws so that it must:
+#
+#   "qx16"   -- q multiplied by 16 (exact in bf16): scores ~ N(0, 256);
+#   "rising" -- q multiplied by 4 and key j (or pool row j) by
+#               1 + 7 j / n, so each row's maximum climbs along the keys;
+#   "jump"   -- every query row gains +1 in each coordinate and one late key
+#               (pool row) becomes (80 / sqrt(d)) in each coordinate, so a row
+#               that sees it scores it about 80 (natural units) above the rest.
+#
+# They only scale or overwrite input values; the attention itself is
+# computed by the oracle and by the kernels.
+# ---------------------------------------------------------------------------
+WIDE_MODES = ("qx16", "rising", "jump")
+
+
+def jump_key(n: int) -> int:
+    """Position of the overwritten key in the "jump" mode: late, but not in the last block."""
+    return max(0, n - 1 - n // 7)
+
+
+def _key_ramp(n: int) -> torch.Tensor:
+    return 1.0 + 7.0 * torch.arange(n, dtype=torch.float32) / max(n, 1)
+
+
+def widen_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, mode, *, dtype="bf16", sinks=False, seed=0) -> dict:
+    """Dense inputs of the usual recipe (fp32 draws), reshaped by ``mode`` before the cast."""
+    s = DenseSpec("adhoc", seed, B, H, Hkv, Tq, Tk, d_qk, d_v, "f32", True, sinks)
+    inp = make_dense(s)
+    q, k = inp["q"], inp["k"]
+    if mode == "qx16":
+        q = q * 16.0
+    elif mode == "rising":
+        q = q * 4.0
+        k = k * _key_ramp(Tk)[None, None, :, None]
+    elif mode == "jump":
+        q = q + 1.0
+        if Tk > 0:
+            k = k.clone()
+            k[:, :, jump_key(Tk), :] = 80.0 / float(np.sqrt(d_qk))
+    else:
+        raise ValueError(mode)
+    dt = _torch_dtype(dtype)
+    return {"q": q.to(dt), "k": k.to(dt), "v": inp["v"].to(dt), "sinks": inp["sinks"]}
+
+
+def widen_sparse(Sq, Hq, N, d_qk, topk, mode, *, sinks=False, seed=0) -> dict:
+    """Sparse inputs: q [Sq,Hq,d], pool [N,d] (bf16), idx [Sq,topk] int32.
+
+    "rising": pool row r scaled by 1 + 7 r / N and each index list sorted
+    ascending, so the gathered blocks come in order of growing norm.
+    "jump": the last pool row is the large row and sits in every list at
+    position ``jump_key(topk)`` (the other indices are drawn from [0, N-1)).
+    "qx16": q multiplied by 16, indices as drawn."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((Sq, Hq, d_qk), generator=g, dtype=torch.float32)
+    kv = torch.randn((N, d_qk), generator=g, dtype=torch.float32)
+    sk = torch.randn((Hq,), generator=g, dtype=torch.float32) if sinks else None
+    if mode == "jump":
+        idx = make_indices(Sq, N - 1, topk, seed)
+        idx[:, jump_key(topk)] = N - 1
+        q = q + 1.0
+        kv[N - 1, :] = 80.0 / float(np.sqrt(d_qk))
+    else:
+        idx = make_indices(Sq, N, topk, seed)
+        if mode == "rising":
+            q = q * 4.0
+            kv = kv * _key_ramp(N)[:, None]
+            idx = np.sort(idx, axis=1)
+        elif mode == "qx16":
+            q = q * 16.0
+        else:
+            raise ValueError(mode)
+    return {"q": q.to(torch.bfloat16), "kv": kv.to(torch.bfloat16), "idx": torch.from_numpy(idx.astype(np.int32)),
+            "sinks": sk}
+
+
+def widen_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, mode, *, sinks=False, seed=0) -> dict:
+    """make_quant_kv with the dense reshaping of ``mode`` applied before quantizing."""
+    inp = widen_dense(B, H, Hkv, Tq, Tk, d, d, mode, dtype="f32", sinks=sinks, seed=seed)
+    return {"q": inp["q"].to(torch.bfloat16), "k": quantize_rows(inp["k"], fmt), "v": quantize_rows(inp["v"], fmt),
+            "sinks": inp["sinks"], "fmt": fmt}
+
+
+def widen_sparse_fp8(Sq, Hq, N, d, topk, mode, *, sinks=False, seed=0) -> dict:
+    """make_sparse_fp8 with the sparse reshaping of ``mode`` applied before quantizing the pool."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((Sq, Hq, d), generator=g, dtype=torch.float32)
+    pool = torch.randn((N, d), generator=g, dtype=torch.float32)
+    sk = torch.randn((Hq,), generator=g, dtype=torch.float32) if sinks else None
+    if mode == "jump":
+        idx = make_indices(Sq, N - 1, topk, seed)
+        idx[:, jump_key(topk)] = N - 1
+        q = q + 1.0
+        pool[N - 1, :] = 80.0 / float(np.sqrt(d))
+    elif mode == "rising":
+        idx = np.sort(make_indices(Sq, N, topk, seed), axis=1)
+        q = q * 4.0
+        pool = pool * _key_ramp(N)[:, None]
+    elif mode == "qx16":
+        idx = make_indices(Sq, N, topk, seed)
+        q = q * 16.0
+    else:
+        raise ValueError(mode)
+    codes, scales = quantize_fp8_rows(pool)
+    return {"q": q.to(torch.bfloat16), "codes": codes, "scales": scales,
+            "idx": torch.from_numpy(idx.astype(np.int32)), "sinks": sk}

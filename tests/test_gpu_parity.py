@@ -198,7 +198,9 @@ def test_workload_tiny_full():
 
 
 @pytest.mark.parametrize("n", [2, 3, 4])
-def test_workload_dense_sampled(n):
+def test_workload_dense_full(n):
+    """The benchmark's launch of workload n (same planner, same kernel, same tile
+    order) compared with the oracle on every output element."""
     s = synth.spec(n)
     inp = synth.make(n)
     announce(f"workload {s.name}: B{s.B} H{s.H} Hkv{s.Hkv} T{s.Tq} d{s.d_qk}/{s.d_v} sinks={s.sinks}")
@@ -208,21 +210,41 @@ def test_workload_dense_sampled(n):
     assert A.dispatch_count(path) == 1
     # every element written (outputs were poisoned with NaN)
     assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
-    rows = _sample_rows(s.B, s.H, s.Tq, np.random.default_rng(n))
-    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=s.scale, causal=True,
-                                    sinks=inp["sinks"], rows=rows)
-    bi, hi, ti = (torch.tensor([r[i] for r in rows]) for i in range(3))
-    go = _np(out[bi, hi, ti])
-    gl = _np(lse[bi, hi, ti])
-    eo, el = _o_err(go, ro), _lse_err(gl, rl)
-    announce(f"workload {s.name}: {len(rows)} sampled rows, max|dO|={eo:.3e} max|dlse|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE
     # run-to-run bitwise determinism
     out2, lse2 = run_dense(inp, causal=True, scale=s.scale)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del out2, lse2
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=s.scale, causal=True, sinks=inp["sinks"])
+    go, gl = _np(out), _np(lse)
+    eo, el = _o_err(go, ro), _lse_err(gl, rl)
+    where = np.unravel_index(int(np.argmax(np.abs(go - ro))), go.shape)
+    announce(f"workload {s.name}: all {go.size} outputs, max|dO|={eo:.3e} at {tuple(int(x) for x in where)} "
+             f"max|dlse|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
 
 
-def test_workload_sparse_sampled():
+def test_fold_with_xcd_order_full():
+    """Token-major GQA fold (g = 4) with the XCD-chunked tile order (B*Hkv = 16, a
+    multiple of 8): the combination the gqa workload launches, at a size whose
+    every output the oracle checks."""
+    inp = synth.randn_dense(2, 32, 8, 512, 512, 128, 128, dtype="bf16", seed=2512)
+    p = A.plan_dense(2, 32, 8, 512, 512, 128, 128)
+    assert p["fold_g"] == 4 and p["path"] == "dense_bf16_d128"
+    check_dense_full(inp, causal=True, scale=1 / math.sqrt(128), label="fold g4 + xcd order, B2 H32/8 T512")
+
+
+@pytest.mark.parametrize("B,H,Hkv,T,dqk,dv", [(1, 8, 8, 700, 192, 128), (2, 64, 8, 300, 64, 64),
+                                              (4, 8, 4, 257, 256, 256)])
+def test_xcd_order_other_dims_full(B, H, Hkv, T, dqk, dv):
+    """XCD-chunked order (B*Hkv a multiple of 8) on the other kernels: one head per kv head
+    (row blocks aligned to heads) and folded groups."""
+    inp = synth.randn_dense(B, H, Hkv, T, T, dqk, dv, dtype="bf16", sinks=True, seed=B * H + T)
+    check_dense_full(inp, causal=True, scale=1 / math.sqrt(dqk), label=f"xcd order B{B} H{H}/{Hkv} d{dqk}")
+
+
+def test_workload_sparse_queries():
+    """The benchmark's sparse launch at full size; 1024 of its 13312 queries (the
+    first and last 256 and 512 more drawn at random) against the oracle."""
     s = synth.spec(5)
     inp = synth.make(5)
     announce(f"workload sparse: Sq{s.Sq} Hq{s.Hq} N{s.N} d{s.d_qk} topk{s.topk}")
@@ -234,19 +256,38 @@ def test_workload_sparse_sampled():
     torch.cuda.synchronize()
     assert A.dispatch_count("sparse_bf16_d512") == 1 and A.dispatch_count("dense_bf16_d512") == 0
     assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
-    rng = np.random.default_rng(5)
-    qs = sorted({0, 1, s.Sq - 1} | set(rng.integers(0, s.Sq, 13).tolist()))
-    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], inp["idx"], d_v=s.d_v, scale=s.scale,
-                                          queries=qs)
-    go, gl = _np(out[qs]), _np(lse[qs])
-    eo, el = _o_err(go, ro), _lse_err(gl, rl)
-    announce(f"workload sparse: {len(qs)} sampled queries, max|dO|={eo:.3e} max|dlse|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
     A.sparse_topk(q, kv, ix, d_v=s.d_v, scale=s.scale, out=out2, lse=lse2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del out2, lse2
+    rng = np.random.default_rng(5)
+    middle = rng.choice(np.arange(256, s.Sq - 256), 512, replace=False).tolist()
+    qs = sorted(set(range(256)) | set(range(s.Sq - 256, s.Sq)) | set(middle))
+    assert len(qs) == 1024
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], inp["idx"], d_v=s.d_v, scale=s.scale,
+                                          queries=qs)
+    go, gl = _np(out[qs]), _np(lse[qs])
+    eo, el = _o_err(go, ro), _lse_err(gl, rl)
+    announce(f"workload sparse: {len(qs)} queries, max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("topk", [4096, 4097, 9000])
+def test_sparse_index_segments(topk):
+    """Index lists longer than the kernel's LDS index buffer (4096 entries) are
+    read in segments: exactly one segment, one entry more, and three segments."""
+    inp = synth.randn_sparse(3, 64, 12000, 512, topk, seed=topk)
+    idx = inp["idx"].clone()
+    idx[0, 4096 % topk] = -1     # a skipped entry in the second segment (or the first)
+    idx[1, topk - 1] = idx[1, 0]  # a duplicate across segments
+    announce(f"sparse segments topk={topk}")
+    out, lse = A.sparse_topk(inp["q"].cuda(), inp["kv"].cuda(), idx.cuda(), d_v=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], idx, d_v=512, scale=1 / math.sqrt(512))
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"topk {topk}: max|dO|={eo:.3e} max|dlse|={el:.3e}"
 
 
 # ------------------------------------------------------------------ seeded random sweeps

@@ -1,0 +1,141 @@
+"""The online softmax's running maximum, moved mid-row, against the fp64 oracle.
+
+With N(0,1) inputs a row's largest score sits in its first key blocks, so the
+kernels' lazy rescale (the output accumulator and the row sum multiplied by
+alpha = exp(m_old - m_new) when the maximum grows by more than 8 log2 units)
+would only ever run on the step from "no key yet" to the first block. The
+inputs here come from ``synth.widen_*``: q scaled by 16, key norms rising
+along the keys (pool rows in index order), and one late key scoring about 80
+above the rest. ``tests/test_rescale_inputs.py`` shows on the CPU that these
+inputs move the maximum by more than 8 log2 units after a row's first block at
+every block size the kernels use. Every path with an online softmax is
+covered: the dense kernels of every compiled head dim (bf16 and the fp32
+split path), split-KV, the sparse top-k kernel (one and several index
+segments), the quantized-cache decode and the fp8 sparse decode.
+
+Tolerances as everywhere: max |O - O_ref| <= 2e-2, max |lse - lse_ref| <= 1e-3
+(the scores stay below about 1e3 before scaling, where fp32 accumulation
+keeps the lse error far below the bar).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_attn_amd as A
+import oracle
+import synth
+from test_gpu_parity import TOL_LSE, TOL_O, _lse_err, _np, _o_err, announce
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]
+
+
+def _check(label, out, lse, ro, rl):
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item(), f"{label}: NaN in the result"
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    announce(f"{label}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE, f"{label}: max|dO|={eo:.3e} max|dlse|={el:.3e}"
+
+
+def _dense(inp, *, causal, scale, split=None):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    B, H, Tq, _ = q.shape
+    out = torch.full((B, H, Tq, v.shape[-1]), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((B, H, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    if split is None:
+        A.dense(q, k, v, causal=causal, scale=scale, sinks=sk, out=out, lse=lse)
+    else:
+        A.dense_splitkv(q, k, v, causal=causal, scale=scale, sinks=sk, n_splits=split, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("dqk,dv", HEAD_DIMS)
+def test_dense_bf16_rescale(dqk, dv, mode):
+    # T = 300: several key blocks of every block size, a ragged last block
+    for causal, sinks in ((True, False), (False, True)):
+        inp = synth.widen_dense(1, 8, 2, 300, 300, dqk, dv, mode, sinks=sinks, seed=dqk + dv + len(mode))
+        label = f"dense bf16 d{dqk}/{dv} {mode} causal={causal} sinks={sinks}"
+        announce(label)
+        out, lse = _dense(inp, causal=causal, scale=1 / math.sqrt(dqk))
+        ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=1 / math.sqrt(dqk), causal=causal,
+                                        sinks=inp["sinks"])
+        _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_f32_rescale(d, mode):
+    inp = synth.widen_dense(1, 4, 1, 200, 200, d, d, mode, dtype="f32", seed=40 + d)
+    label = f"dense f32 d{d} {mode}"
+    announce(label)
+    out, lse = _dense(inp, causal=True, scale=1 / math.sqrt(d))
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=1 / math.sqrt(d), causal=True)
+    _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,dqk,dv,n", [
+    (2, 8, 2, 1, 2000, 128, 128, 4),      # GQA decode over four key ranges
+    (1, 64, 1, 1, 3000, 512, 512, 0),     # MQA d512 decode, the library's range count
+    (1, 4, 1, 37, 1300, 192, 128, 5),     # short prefill
+])
+def test_splitkv_rescale(B, H, Hkv, Tq, Tk, dqk, dv, n, mode):
+    inp = synth.widen_dense(B, H, Hkv, Tq, Tk, dqk, dv, mode, sinks=True, seed=Tk + dqk)
+    label = f"split-KV B{B} H{H}/{Hkv} {Tq}x{Tk} d{dqk}/{dv} n{n} {mode}"
+    announce(label)
+    A.reset_dispatch_counts()
+    out, lse = _dense(inp, causal=True, scale=1 / math.sqrt(dqk), split=n)
+    assert A.dispatch_count("splitkv_merge") == 1
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=1 / math.sqrt(dqk), causal=True,
+                                    sinks=inp["sinks"])
+    _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("Sq,N,topk", [(4, 3000, 300), (3, 12000, 9000)])
+def test_sparse_rescale(Sq, N, topk, mode):
+    """topk 9000: three index segments (4096 + 4096 + 808), the maximum moving in each."""
+    inp = synth.widen_sparse(Sq, 64, N, 512, topk, mode, sinks=(topk < 1000), seed=N + topk)
+    label = f"sparse Sq{Sq} N{N} topk{topk} {mode}"
+    announce(label)
+    out, lse = A.sparse_topk(inp["q"].cuda(), inp["kv"].cuda(), inp["idx"].cuda(), d_v=512,
+                             sinks=None if inp["sinks"] is None else inp["sinks"].cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], inp["idx"], d_v=512, scale=1 / math.sqrt(512),
+                                          sinks=inp["sinks"])
+    _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_qkv_rescale(fmt, mode):
+    inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, 128, fmt, mode, sinks=True, seed=77)
+    label = f"qkv {fmt} {mode}"
+    announce(label)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    out, lse = A.dense_qkv(q, k, v, fmt=fmt, causal=True, sinks=inp["sinks"].cuda())
+    torch.cuda.synchronize()
+    kd = oracle.dequantize_rows(inp["k"], fmt)
+    vd = oracle.dequantize_rows(inp["v"], fmt)
+    ro, rl = oracle.dense_attention(inp["q"], kd, vd, scale=1 / math.sqrt(128), causal=True, sinks=inp["sinks"])
+    _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+def test_sparse_fp8_rescale(mode):
+    inp = synth.widen_sparse_fp8(3, 64, 5000, 512, 2048, mode, sinks=True, seed=91)
+    label = f"sparse fp8 {mode}"
+    announce(label)
+    out, lse = A.sparse_fp8(inp["q"].cuda(), inp["codes"].cuda(), inp["scales"].cuda(), inp["idx"].cuda(),
+                            sinks=inp["sinks"].cuda())
+    torch.cuda.synchronize()
+    pool = oracle.dequantize_fp8_rows(inp["codes"].numpy(), inp["scales"].numpy())
+    ro, rl = oracle.sparse_topk_attention(inp["q"], pool, inp["idx"].numpy(), d_v=512, scale=1 / math.sqrt(512),
+                                          sinks=inp["sinks"])
+    _check(label, out, lse, ro, rl)
