@@ -736,7 +736,9 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
   // dropout: this row's keep words of block j (MT words), loaded one block
   // ahead so that their wait falls where the block's tiles are waited for
   const uint32_t* mrow = DROP ? p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st : nullptr;
-  uint32_t mw[MT], mwn[MT];
+  // (the words of block j+1 are loaded into mw once block j's have been used,
+  // so that no second set of registers holds them)
+  uint32_t mw[MT];
   auto load_mask = [&](int j, uint32_t* dst) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) dst[mt] = (j * MT + mt < p.nwords) ? mrow[j * MT + mt] : 0u;
@@ -750,9 +752,6 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
     wait_all_loads();
     barrier();
     if (j + 1 < nb) issue(j + 1);
-    if constexpr (DROP) {
-      if (j + 1 < nb) load_mask(j + 1, mwn);
-    }
     const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
     const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
     f32x16 S[MT], dP[MT];
@@ -791,6 +790,9 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
           dS[mt * 16 + i] = pr * (dP[mt][i] - Dr);
         }
       }
+    if constexpr (DROP) {
+      if (j + 1 < nb) load_mask(j + 1, mw);
+    }
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
       const bf16x8 db = pack8(dS + ks * 8);
@@ -798,10 +800,6 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
       for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(tr_frag<CPK>(kt, ks * 16, dt * 32, lane), db, acc[dt]);
     }
     pipeline_reads<PKS * DT, 2>();
-    if constexpr (DROP) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) mw[mt] = mwn[mt];
-    }
   }
 
   if (valid) {
@@ -1184,7 +1182,9 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
 template <int DQK, int DV, bool DROP>
 int launch_bwd_cfg(const BwdParams& p, void* stream) {
   // dQ: two waves per SIMD where the registers allow it (d_qk + d_v <= 256)
-  constexpr int NW_KV = 4, NW_Q = DQK + DV > 256 ? 4 : 8, BN_Q = 64;
+  // (the dQ kernel with dropout and 128-wide heads takes 32-key blocks: with 64
+  // its mask words put it one register over the two-wave budget)
+  constexpr int NW_KV = 4, NW_Q = DQK + DV > 256 ? 4 : 8, BN_Q = (DROP && DQK + DV == 256) ? 32 : 64;
   constexpr int BQ_KV = DQK + DV > 256 ? 32 : 64;  // wide heads: one 32-row sub-block per step (registers)
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t R = (int64_t)p.B * p.H * p.Tq;
@@ -1477,8 +1477,10 @@ __global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
   float l2[16], rm[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
+    // rows past Tq read the last row's lse (clamped, never out of bounds) and
+    // write nothing
     const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
-    const float l = t < p.Tq ? p.lse[lbase + t] : -INFINITY;
+    const float l = p.lse[lbase + min(t, p.Tq - 1)];
     l2[r] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     rm[r] = -INFINITY;
   }
@@ -1490,32 +1492,51 @@ __global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
   for (int j = 0; j < nb; ++j) {
     wait_all_loads();
     barrier();
-    if (j + 1 < nb)
-      dma_tile<CPK, BN, NW>(kbase, p.k_st, (j + 1) * BN, p.Tk - 1, smem_s + ((j + 1) & 1) * KT_BYTES, wave, lane);
+    if (j + 1 < nb) {
+      // the slot address is rebuilt every step (the empty asm), so the per-
+      // instruction LDS addresses derived from it are not kept in scalar
+      // registers across the loop
+      uint32_t slot = smem_s + ((j + 1) & 1) * KT_BYTES;
+      asm volatile("" : "+s"(slot));
+      dma_tile<CPK, BN, NW>(kbase, p.k_st, (j + 1) * BN, p.Tk - 1, slot, wave, lane);
+    }
     const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * KT_BYTES);
     f32x16 S;
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) S = mfma32(qf[s], row_frag<CPK>(kt, lq, s, lh), S);
+    // Row r of this lane is token tl + cr(r) with cr(r) = (r/4)*8 + r%4. With
+    // rel = key - (tl + off) the visible keys of row r are the rel in
+    // [cr - left, cr + up]; rows from nrow on do not exist. The bounds are
+    // rebuilt every step (the empty asm) and tested by sign, so no per-row
+    // lane mask is kept across the loop (those would sit in scalar registers).
     const int kk = j * BN + lq;
+    int tl = t0 + lh * 4, nrow = p.Tq - tl;
+    asm volatile("" : "+v"(tl), "+v"(nrow));
+    const int rel = kk - (tl + off);
+    const int hi = up >= 0 ? min(up, p.Tk - 1 - kk + rel) : p.Tk - 1 - kk + rel;  // rel <= cr + hi
+    const int lo = p.win_left >= 0 ? -p.win_left : -(1 << 30);                     // rel >= cr + lo
+    const bool kin = kk < p.Tk;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
-      const int lim = up >= 0 ? min(p.Tk - 1, t + off + up) : p.Tk - 1;
-      const bool vis = t < p.Tq && kk <= lim && (p.win_left < 0 || kk >= t + off - p.win_left);
-      if (vis) rm[r] = fmaxf(rm[r], S[r] * p.scale);
-      if (pbase != nullptr && t < p.Tq && kk < p.Tk)
-        pbase[(int64_t)t * p.p_st + kk] = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], p.c, -l2[r])) : 0.f;
+      const int cr = (r >> 2) * 8 + (r & 3);
+      const int ok = ((cr + hi - rel) | (rel - cr - lo) | (nrow - 1 - cr)) >= 0;  // visible and an existing row
+      const float sv = S[r] * p.scale;
+      rm[r] = fmaxf(rm[r], ok ? sv : -INFINITY);
+      if (pbase != nullptr && kin && cr < nrow)
+        pbase[(int64_t)(tl + cr) * p.p_st + kk] = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], p.c, -l2[r])) : 0.f;
     }
   }
   if (p.row_max != nullptr) {
+    int tl = t0 + lh * 4;
+    asm volatile("" : "+v"(tl));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = rm[r];
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-      const int t = t0 + (r >> 2) * 8 + lh * 4 + (r & 3);
+      const int t = tl + (r >> 2) * 8 + (r & 3);
       if (lq == 0 && t < p.Tq) p.row_max[lbase + t] = v;
     }
   }

@@ -51,6 +51,16 @@
 extern "C" {
 #endif
 
+/*
+ * Versioning. pith-train pull request 65 ("Issues resolved" item 1) records
+ * FA4 b19 widening its forward's return tuple from (out, lse) to (out, lse,
+ * p, row_max), which broke every caller that unpacked two values. Here no
+ * call returns more than a status: every argument struct starts with
+ * struct_size (the caller sets it to sizeof the struct it was compiled
+ * with; a library built with another layout refuses the call with
+ * ATTN_ABI_MISMATCH instead of reading past it), and ATTN_ABI_VERSION is
+ * raised whenever any struct or signature changes.
+ */
 #define ATTN_ABI_VERSION 12
 
 typedef enum attn_status {
@@ -207,7 +217,9 @@ typedef struct attn_plan {
   int64_t budget_tiles;
 } attn_plan;
 
-/* ABI version of the loaded library (ATTN_ABI_VERSION at build time). */
+/* ABI version of the loaded library (ATTN_ABI_VERSION at build time); a
+ * binding compares it with the version it was written for before any call
+ * (pith-train pull request 65, "Issues resolved" item 1, see above). */
 int attn_abi_version(void);
 
 /* Dense forward. Validates, plans and launches one kernel on `stream`. */
@@ -566,11 +578,14 @@ const char* attn_status_string(attn_status s);
 /* Message of the last failed call on this host thread ("" if none). */
 const char* attn_last_error(void);
 
-/* Number of launches of kernel path `path` in this process (engagement
- * record: a path that never launched reads 0). */
+/* Number of launches of kernel path `path` in this process; 0 for a path that
+ * never launched or an unknown name. The engagement record of the ArcFlash
+ * pull request (section "D18"): a test asserts both that the path it meant to
+ * exercise really ran and that the paths it did not mean did not, so a silent
+ * fallback cannot pass as the fast path. Counters are atomic and per process. */
 uint64_t attn_dispatch_count(const char* path);
 
-/* Reset every dispatch counter to 0. */
+/* Reset every dispatch counter to 0 (the same engagement record, "D18"). */
 void attn_reset_dispatch_counts(void);
 
 /* Folded query rows per tile when [rows, Tk] scores of elt_bytes each must fit
