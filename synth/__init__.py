@@ -356,11 +356,23 @@ def randn_sparse(Sq, Hq, N, d_qk, topk, *, seed=0, sinks=False):
 # reshape the same seeded draws so that it must:
 #
 #   "qx16"   -- q multiplied by 16 (exact in bf16): scores ~ N(0, 256);
-#   "rising" -- q multiplied by 4 and key j (or pool row j) by
-#               1 + 7 j / n, so each row's maximum climbs along the keys;
+#   "rising" -- q multiplied by 4 and key j by 1 + 7 j / n, so each row's
+#               maximum climbs along the keys. Sparse pools (whose rows are
+#               the values too) rise additively instead: pool row r gains
+#               0.5 r / N in each coordinate and q gains 7, which lifts the
+#               score of row r by about 80 r / N while |v| stays below 3;
 #   "jump"   -- every query row gains +1 in each coordinate and one late key
 #               (pool row) becomes (80 / sqrt(d)) in each coordinate, so a row
 #               that sees it scores it about 80 (natural units) above the rest.
+#
+# The value rows are halved in every mode. Such scores make the softmax
+# peaky, so an output row nearly copies one value row; N(0,1) value rows
+# reach |v| > 4, where one bf16 rounding of the output alone errs by up to
+# 2^-6 (half a unit in the last place of [4, 8)) and the bf16 rounding of
+# the probabilities adds up to 2^-9 |v|: together above the 2e-2 bar, for
+# any correct kernel. With |v| < 4 the same two roundings stay below it. For
+# the one-pool sparse inputs (values = the pool rows) the pool is halved
+# and q doubled, so the scores are those of the unhalved pool.
 #
 # They only scale or overwrite input values; the attention itself is
 # computed by the oracle and by the kernels.
@@ -395,14 +407,15 @@ def widen_dense(B, H, Hkv, Tq, Tk, d_qk, d_v, mode, *, dtype="bf16", sinks=False
     else:
         raise ValueError(mode)
     dt = _torch_dtype(dtype)
-    return {"q": q.to(dt), "k": k.to(dt), "v": inp["v"].to(dt), "sinks": inp["sinks"]}
+    return {"q": q.to(dt), "k": k.to(dt), "v": (inp["v"] * 0.5).to(dt), "sinks": inp["sinks"]}
 
 
 def widen_sparse(Sq, Hq, N, d_qk, topk, mode, *, sinks=False, seed=0) -> dict:
     """Sparse inputs: q [Sq,Hq,d], pool [N,d] (bf16), idx [Sq,topk] int32.
 
-    "rising": pool row r scaled by 1 + 7 r / N and each index list sorted
-    ascending, so the gathered blocks come in order of growing norm.
+    "rising": pool row r gains 0.5 r / N in each coordinate, q gains 7, and
+    each index list is sorted ascending, so the gathered blocks come in order
+    of growing score.
     "jump": the last pool row is the large row and sits in every list at
     position ``jump_key(topk)`` (the other indices are drawn from [0, N-1)).
     "qx16": q multiplied by 16, indices as drawn."""
@@ -418,15 +431,15 @@ def widen_sparse(Sq, Hq, N, d_qk, topk, mode, *, sinks=False, seed=0) -> dict:
     else:
         idx = make_indices(Sq, N, topk, seed)
         if mode == "rising":
-            q = q * 4.0
-            kv = kv * _key_ramp(N)[:, None]
+            q = q + 3.5
+            kv = kv + (torch.arange(N, dtype=torch.float32) / N)[:, None]
             idx = np.sort(idx, axis=1)
         elif mode == "qx16":
             q = q * 16.0
         else:
             raise ValueError(mode)
-    return {"q": q.to(torch.bfloat16), "kv": kv.to(torch.bfloat16), "idx": torch.from_numpy(idx.astype(np.int32)),
-            "sinks": sk}
+    return {"q": (q * 2.0).to(torch.bfloat16), "kv": (kv * 0.5).to(torch.bfloat16),
+            "idx": torch.from_numpy(idx.astype(np.int32)), "sinks": sk}
 
 
 def widen_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, mode, *, sinks=False, seed=0) -> dict:
@@ -449,13 +462,13 @@ def widen_sparse_fp8(Sq, Hq, N, d, topk, mode, *, sinks=False, seed=0) -> dict:
         pool[N - 1, :] = 80.0 / float(np.sqrt(d))
     elif mode == "rising":
         idx = np.sort(make_indices(Sq, N, topk, seed), axis=1)
-        q = q * 4.0
-        pool = pool * _key_ramp(N)[:, None]
+        q = q + 3.5
+        pool = pool + (torch.arange(N, dtype=torch.float32) / N)[:, None]
     elif mode == "qx16":
         idx = make_indices(Sq, N, topk, seed)
         q = q * 16.0
     else:
         raise ValueError(mode)
-    codes, scales = quantize_fp8_rows(pool)
-    return {"q": q.to(torch.bfloat16), "codes": codes, "scales": scales,
+    codes, scales = quantize_fp8_rows(pool * 0.5)
+    return {"q": (q * 2.0).to(torch.bfloat16), "codes": codes, "scales": scales,
             "idx": torch.from_numpy(idx.astype(np.int32)), "sinks": sk}

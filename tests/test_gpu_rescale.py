@@ -15,7 +15,12 @@ segments), the quantized-cache decode and the fp8 sparse decode.
 
 Tolerances as everywhere: max |O - O_ref| <= 2e-2, max |lse - lse_ref| <= 1e-3
 (the scores stay below about 1e3 before scaling, where fp32 accumulation
-keeps the lse error far below the bar).
+keeps the lse error far below the bar). The value rows of these inputs are
+halved: a peaky softmax copies one value row into the output, and with
+N(0,1) values an output above 4 in magnitude carries up to 2^-6 from its
+own bf16 rounding plus 2^-9 |v| from the probabilities' -- over the bar for
+any correct kernel (seen once at d 512 with q x 16: 2.045e-2, matched by a
+CPU emulation of those two roundings).
 """
 import math
 
@@ -123,8 +128,24 @@ def test_qkv_rescale(fmt, mode):
     torch.cuda.synchronize()
     kd = oracle.dequantize_rows(inp["k"], fmt)
     vd = oracle.dequantize_rows(inp["v"], fmt)
-    ro, rl = oracle.dense_attention(inp["q"], kd, vd, scale=1 / math.sqrt(128), causal=True, sinks=inp["sinks"])
-    _check(label, out, lse, ro, rl)
+    scale = 1 / math.sqrt(128)
+    ro, rl = oracle.dense_attention(inp["q"], kd, vd, scale=scale, causal=True, sinks=inp["sinks"])
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item(), f"{label}: NaN in the result"
+    # The kernel rounds every decoded key value d * code to f16 once (unit
+    # roundoff 2^-11), so a score errs by up to 2^-11 scale sum_i |q_i k_i|
+    # and the row's lse (a smooth maximum of its scores) by the largest such
+    # bound over the row's keys. With N(0,1) inputs that is ~1e-4; with these
+    # scores it reaches ~1e-2, so the lse bar here is 1e-3 plus that bound.
+    qa = np.abs(inp["q"].double().numpy())
+    ka = np.abs(kd)
+    g = qa.shape[1] // ka.shape[1]
+    bound = np.stack([np.stack([(qa[b, h] @ ka[b, h // g].T).max(axis=1) for h in range(qa.shape[1])])
+                      for b in range(qa.shape[0])]) * scale * 2.0 ** -11
+    eo = _o_err(_np(out), ro)
+    dl = np.abs(_np(lse) - rl)
+    announce(f"{label}: max|dO|={eo:.3e} max|dlse|={dl.max():.3e} (f16-decode bound up to {bound.max():.3e})")
+    assert eo <= TOL_O, f"{label}: max|dO|={eo:.3e}"
+    assert (dl <= TOL_LSE + bound).all(), f"{label}: lse error {dl.max():.3e} beyond 1e-3 + the f16 bound"
 
 
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
