@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_INVALID_ARGUMENT, ATTN_UNSUPPORTED, ATTN_ABI_MISMATCH, ATTN_HIP_ERROR = range(5)
 ATTN_BF16, ATTN_F32 = 0, 1
-ABI_VERSION = 12
+ABI_VERSION = 13
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the library's per-device scratch array (ATTN_NOALLOC_SCRATCH_BYTES)
 
 
 class AttnDenseArgs(ctypes.Structure):
@@ -149,7 +150,7 @@ EXPORTS = (
     "attn_splitkv_workspace_bytes", "attn_splitkv_choose", "attn_bwd_dense", "attn_bwd_dense_workspace_bytes",
     "attn_fwd_dense_qkv", "attn_qkv_workspace_bytes", "attn_fwd_varlen", "attn_bwd_sparse_topk",
     "attn_bwd_sparse_workspace_bytes", "attn_fwd_dense_extras", "attn_fwd_sparse_fp8",
-    "attn_sparse_fp8_workspace_bytes",
+    "attn_sparse_fp8_workspace_bytes", "attn_fwd_dense_splitkv_noalloc",
 )
 ATTN_KV_Q4_0, ATTN_KV_Q8_0 = 2, 8
 KV_FORMATS = {"q8_0": ATTN_KV_Q8_0, "q4_0": ATTN_KV_Q4_0}
@@ -225,6 +226,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_dense_splitkv.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_void_p]
     lib.attn_fwd_dense_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_dense_splitkv_noalloc.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_fwd_dense_splitkv_noalloc.restype = ctypes.c_int
     lib.attn_splitkv_workspace_bytes.argtypes = [ctypes.POINTER(AttnDenseArgs), ctypes.c_int32]
     lib.attn_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.attn_splitkv_choose.argtypes = [ctypes.POINTER(AttnDenseArgs)]
@@ -522,6 +525,23 @@ def dense_splitkv(q, k, v, *, causal: bool = True, scale: Optional[float] = None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.attn_fwd_dense_splitkv(ctypes.byref(a), int(n_splits), ctypes.c_void_p(ws_ptr), ws_bytes,
                                       ctypes.c_void_p(_stream_handle(stream))))
+    return out, lse
+
+
+def dense_splitkv_noalloc(q, k, v, out, lse, *, causal: bool = True, scale: Optional[float] = None, sinks=None,
+                          n_splits: int = 0, stream=None, window: Tuple[int, int] = (-1, -1)):
+    """:func:`dense_splitkv` for callers that cannot allocate: ``out`` [B,H,Tq,d_v] and
+    ``lse`` [B,H,Tq] fp32 are the caller's, and the partials go to the library's
+    per-device scratch array (``NOALLOC_SCRATCH_BYTES``) instead of a workspace.
+    Neither this function nor the library allocates. Calls that overlap on one
+    device share that array and must be ordered by the caller. A plan whose
+    partials exceed the array raises AttnInvalidArgument (ask for fewer ranges)."""
+    lib = load_library()
+    _expect(q, "q", (None, None, None, None))
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    a = dense_args(q, k, v, out, lse, causal=causal, scale=scale, sinks=sinks, window=window)
+    _check(lib.attn_fwd_dense_splitkv_noalloc(ctypes.byref(a), int(n_splits), ctypes.c_void_p(_stream_handle(stream))))
     return out, lse
 
 

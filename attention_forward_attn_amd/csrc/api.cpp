@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/attn_fwd.h"
@@ -408,6 +409,99 @@ attn_status do_launch(const DensePlan& dp, void* stream) {
   return ATTN_OK;
 }
 
+
+// ---------------------------------------------------------------- scratch for callers that cannot allocate
+// The partials of attn_fwd_dense_splitkv_noalloc live in this array. Each
+// device the library runs on holds its own copy from module load until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it is only a stand-in symbol): the device address is looked up once
+// per device with hipGetSymbolAddress, with that device current, and kept
+// below. Every call on a device shares that device's copy, so calls that
+// overlap on one device (two streams, two threads) race on it. The kernels
+// write every partial they read, so nothing is cleared between calls.
+__device__ __attribute__((aligned(256))) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+attn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return fail(ATTN_HIP_ERROR, "hipGetDevice failed: %s", hipGetErrorString(de));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_UNSUPPORTED, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || ptr == nullptr)
+        return fail(ATTN_HIP_ERROR, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return ATTN_OK;
+}
+
+// The split-KV forward: validate, plan the key ranges, launch the ranges and
+// the merge. The partials go to the caller's `workspace`
+// (attn_fwd_dense_splitkv) or, with `scratch`, to the library's scratch array
+// of this device (attn_fwd_dense_splitkv_noalloc; `workspace_bytes` is then
+// the array's size, checked before its address is looked up).
+attn_status splitkv_launch(const attn_dense_args* a, int32_t n_splits, void* workspace, int64_t workspace_bytes,
+                           void* stream, bool scratch) {
+  g_last_error.clear();
+  DensePlan dp;
+  attn_status s = validate_dense(a, &dp);
+  if (s != ATTN_OK) return s;
+  if (dp.drop) return fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
+  if (n_splits < 0 || n_splits > kMaxSplits)
+    return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
+  if (a->Tq == 0) return ATTN_OK;
+  if (a->dtype != ATTN_BF16) {
+    if (n_splits > 1) return fail(ATTN_UNSUPPORTED, "split-KV is compiled for bf16 inputs only");
+    return do_launch(dp, stream);
+  }
+  const SplitPlan sp = plan_split(dp, a, n_splits);
+  if (sp.n == 1) return do_launch(dp, stream);
+  if (scratch) {
+    if (sp.bytes > workspace_bytes)
+      return fail(ATTN_INVALID_ARGUMENT,
+                  "split-KV over %d key ranges needs %lld bytes of partials, more than the %lld bytes of the "
+                  "library's scratch array (ask for fewer ranges)",
+                  sp.n, (long long)sp.bytes, (long long)workspace_bytes);
+    s = scratch_of_current_device(&workspace);
+    if (s != ATTN_OK) return s;
+  }
+  if (workspace == nullptr || workspace_bytes < sp.bytes)
+    return fail(ATTN_INVALID_ARGUMENT, "split-KV over %d key ranges needs a workspace of %lld bytes, got %lld", sp.n,
+                (long long)sp.bytes, (long long)(workspace ? workspace_bytes : 0));
+  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  attn::KernelParams& p = dp.kp;
+  p.n_splits = sp.n;
+  p.split_keys = sp.keys;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + (int64_t)sp.n * sp.rows * a->d_v;
+  s = do_launch(dp, stream);
+  if (s != ATTN_OK) return s;
+  attn::MergeParams m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.sinks = a->sinks;
+  m.out = a->out;
+  m.lse = a->lse;
+  m.o_sb = a->o_sb; m.o_sh = a->o_sh; m.o_st = a->o_st;
+  m.B = a->B; m.H = a->H; m.Tq = a->Tq; m.d_v = a->d_v; m.n_splits = sp.n;
+  m.f32 = 0;
+  const int err = attn::launch_merge(m, stream);
+  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the split-KV merge failed: %s", hipGetErrorString((hipError_t)err));
+  note_dispatch(kMergeSlot, kMergePath);
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -498,44 +592,11 @@ int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits)
 
 attn_status attn_fwd_dense_splitkv(const attn_dense_args* a, int32_t n_splits, void* workspace,
                                    int64_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  DensePlan dp;
-  attn_status s = validate_dense(a, &dp);
-  if (s != ATTN_OK) return s;
-  if (dp.drop) return fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
-  if (n_splits < 0 || n_splits > kMaxSplits)
-    return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
-  if (a->Tq == 0) return ATTN_OK;
-  if (a->dtype != ATTN_BF16) {
-    if (n_splits > 1) return fail(ATTN_UNSUPPORTED, "split-KV is compiled for bf16 inputs only");
-    return do_launch(dp, stream);
-  }
-  const SplitPlan sp = plan_split(dp, a, n_splits);
-  if (sp.n == 1) return do_launch(dp, stream);
-  if (workspace == nullptr || workspace_bytes < sp.bytes)
-    return fail(ATTN_INVALID_ARGUMENT, "split-KV over %d key ranges needs a workspace of %lld bytes, got %lld", sp.n,
-                (long long)sp.bytes, (long long)(workspace ? workspace_bytes : 0));
-  if (!aligned16(workspace)) return fail(ATTN_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  attn::KernelParams& p = dp.kp;
-  p.n_splits = sp.n;
-  p.split_keys = sp.keys;
-  p.part_o = static_cast<float*>(workspace);
-  p.part_lse = p.part_o + (int64_t)sp.n * sp.rows * a->d_v;
-  s = do_launch(dp, stream);
-  if (s != ATTN_OK) return s;
-  attn::MergeParams m;
-  m.part_o = p.part_o;
-  m.part_lse = p.part_lse;
-  m.sinks = a->sinks;
-  m.out = a->out;
-  m.lse = a->lse;
-  m.o_sb = a->o_sb; m.o_sh = a->o_sh; m.o_st = a->o_st;
-  m.B = a->B; m.H = a->H; m.Tq = a->Tq; m.d_v = a->d_v; m.n_splits = sp.n;
-  m.f32 = 0;
-  const int err = attn::launch_merge(m, stream);
-  if (err != 0) return fail(ATTN_HIP_ERROR, "launch of the split-KV merge failed: %s", hipGetErrorString((hipError_t)err));
-  note_dispatch(kMergeSlot, kMergePath);
-  return ATTN_OK;
+  return splitkv_launch(a, n_splits, workspace, workspace_bytes, stream, false);
+}
+
+attn_status attn_fwd_dense_splitkv_noalloc(const attn_dense_args* a, int32_t n_splits, void* stream) {
+  return splitkv_launch(a, n_splits, nullptr, ATTN_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 attn_status attn_plan_sparse_topk(const attn_sparse_args* a, attn_plan* p) {

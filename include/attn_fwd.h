@@ -61,7 +61,7 @@ extern "C" {
  * ATTN_ABI_MISMATCH instead of reading past it), and ATTN_ABI_VERSION is
  * raised whenever any struct or signature changes.
  */
-#define ATTN_ABI_VERSION 12
+#define ATTN_ABI_VERSION 13
 
 typedef enum attn_status {
   ATTN_OK = 0,
@@ -272,6 +272,26 @@ attn_status attn_fwd_dense_splitkv(const attn_dense_args* a, int32_t n_splits, v
  * n_splits (0 = the library's choice): n * B*H*Tq * (d_v + 1) * 4 for n > 1
  * ranges, 0 when one range suffices, -1 on invalid arguments. Host only. */
 int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits);
+
+/*
+ * The split-KV forward without any allocation, for callers that cannot call
+ * hipMalloc or take a workspace from an allocator: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Arguments,
+ * range choice and results are those of attn_fwd_dense_splitkv; the partials
+ * go to a scratch array the library holds on each device instead of a caller
+ * workspace (the caller still passes every input and output). The array is
+ * ATTN_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held until the process
+ * ends; a plan whose partials need more (attn_splitkv_workspace_bytes)
+ * returns ATTN_INVALID_ARGUMENT before any launch -- ask for fewer ranges.
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (several streams or host threads) race and must be ordered by
+ * the caller. One range only (or f32 inputs with n_splits <= 1) launches the
+ * plain kernel and touches no scratch. The call allocates nothing; its first
+ * call on a device looks the array's address up (hipGetSymbolAddress), and
+ * a failure there returns ATTN_HIP_ERROR.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+attn_status attn_fwd_dense_splitkv_noalloc(const attn_dense_args* a, int32_t n_splits, void* stream);
 
 /* The number of key ranges the library would choose (n_splits = 0) for
  * these arguments on the current device; -1 on invalid arguments. Host only
