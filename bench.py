@@ -16,7 +16,12 @@ swa1024 (algorithmic flops = five products per visible pair), decode over a
 q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
 forward (beside the padded batch), MLA two-part rows (beside the concatenated
 call), the sparse backward, the forward's extra returns (p, row_max), attention
-dropout (forward and backward) and the sliding-window forward.
+dropout (forward and backward) and the sliding-window forward; and two
+diagnostics of where the sparse forward's bytes come from (the Infinity
+Cache cleared before each launch; a 1 GiB pool). Every workload line also
+carries the sha256 of its generated inputs and, unless --no-cpu-baseline,
+the fp64 oracle timed on the host over a bounded sample of it (the tiny
+workload single-threaded over 100 repeats of its full output).
 
 Warmup: at least W untimed steps and at least 0.2 s of them (the clocks
 ramp over the first ~30 ms of load). Prints ONE JSON line on stdout. Kernel
@@ -223,20 +228,46 @@ def traffic_for(n: int):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(n: int, inp: dict, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle on a bounded sample of the same workload, timed on this host."""
+    """The fp64 oracle on a bounded sample of the same workload, timed on this host
+    (BLAS on every core it is given; the tiny workload single-threaded over 100
+    repeats of its full output)."""
     import numpy as np
 
     import oracle
     import synth
 
+    s = synth.spec(n)
+    if n == 1:
+        from threadpoolctl import threadpool_limits
+
+        reps = 100
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=s.scale, causal=s.causal)
+            dt = time.perf_counter() - t0
+        w = work(1)
+        return {"value": round(w["flops"] * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                "sample": f"the full workload (B1 H4 T128), {reps} repeats, single-threaded BLAS",
+                "seconds": round(dt, 2), "ms_per_run": round(dt * 1e3 / reps, 3), "cpu_model": cpu_model()}
     try:
         from threadpoolctl import threadpool_info
 
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    s = synth.spec(n)
     done_flops = 0
     t0 = time.perf_counter()
     units = 0
@@ -273,7 +304,14 @@ def cpu_baseline(n: int, inp: dict, budget_s: float = 12.0) -> dict:
         w = work(n)
         value, unit = w["bytes"] * units / s.Sq / dt / 1e9, "GB/s"
     return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": cpu_model()}
+
+
+def inputs_sha256(inp: dict) -> dict:
+    """sha256 of every generated input tensor (reproducibility record)."""
+    import synth
+
+    return {k: synth.sha256(v) for k, v in inp.items() if hasattr(v, "dtype")}
 
 
 def measure(n: int, steps: int, warmup: int, split: bool = False) -> dict:
@@ -300,6 +338,85 @@ def measure(n: int, steps: int, warmup: int, split: bool = False) -> dict:
         f"= {100 * rl['frac']:.1f}% of peak")
     return {"n": n, "path": path, "timing": t, "value": value, "unit": unit, "roofline": rl, "inp": inp,
             "verdict": "Measured"}
+
+
+def _event_ms(fn, before=None, steps: int = 10) -> list:
+    """HIP-event durations of `fn` launches on torch's current stream (the stream the
+    library launches on); `before` runs untimed ahead of each launch."""
+    import torch
+
+    out = []
+    for _ in range(steps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+SCRUB_MIB = 512
+BIG_POOL_ROWS = 1 << 20
+
+
+def measure_sparse_diagnostic(kind: str, steps: int, warmup: int) -> dict:
+    """Where workload 5's bytes come from. Its 64 MiB pool fits the 256 MB Infinity
+    Cache, so its GB/s is an effective gather rate. Two diagnostics with the same
+    queries, top-k and algorithmic bytes (31.53 GB per launch):
+      scrub  -- 512 MiB written by a device fill before every timed launch, so each
+                launch starts with the pool, q and the indices out of the cache;
+      pool1g -- a pool of 2^20 rows (1 GiB, four times the cache), indices drawn
+                like the workload's from [0, 2^20) (numpy default_rng(5)), pool rows
+                N(0,1) from a device generator seeded with 5: most gathers miss."""
+    import numpy as np
+    import torch
+
+    import attention_forward_attn_amd as A
+    import synth
+
+    s = synth.spec(5)
+    w = work(5)
+    if kind == "scrub":
+        step, path, inp = make_call(5)
+        junk = torch.empty(SCRUB_MIB << 20, dtype=torch.uint8, device="cuda")
+        before = lambda: junk.fill_(1)  # noqa: E731
+        desc = describe(5) + f", {SCRUB_MIB} MiB written before each launch"
+    elif kind == "pool1g":
+        inp = synth.make(5)
+        q = inp["q"].cuda()
+        del inp
+        g = torch.Generator(device="cuda").manual_seed(5)
+        kv = torch.randn((BIG_POOL_ROWS, s.d_qk), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        idx = torch.from_numpy(synth.make_indices(s.Sq, BIG_POOL_ROWS, s.topk, 5)).cuda()
+        out = torch.empty((s.Sq, s.Hq, s.d_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((s.Sq, s.Hq), dtype=torch.float32, device="cuda")
+
+        def step():
+            A.sparse_topk(q, kv, idx, d_v=s.d_v, scale=s.scale, out=out, lse=lse)
+
+        path = A.plan_sparse_topk(s.Sq, s.Hq, BIG_POOL_ROWS, s.d_qk, s.d_v, s.topk)["path"]
+        before = None
+        desc = describe(5).replace(f"N={s.N}", f"N={BIG_POOL_ROWS}") + " (1 GiB pool)"
+    else:
+        raise ValueError(kind)
+    A.reset_dispatch_counts()
+    _event_ms(step, before, max(2, warmup))
+    t_end = time.perf_counter() + MIN_WARMUP_S
+    while time.perf_counter() < t_end:
+        _event_ms(step, before, 1)
+    ms = sorted(_event_ms(step, before, steps))
+    mean = sum(ms) / len(ms)
+    gbs = w["bytes"] / (mean * 1e-3) / 1e9
+    log(f"[bench] {desc} | kernel {mean:.4f} ms (median {ms[len(ms) // 2]:.4f}) | {gbs:.1f} GB/s = "
+        f"{100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s")
+    return {"row": f"sparse top-k diagnostic: {kind}", "workload": desc, "path": path, "value": round(gbs, 1),
+            "unit": "GB/s", "kernel_ms": round(mean, 5), "kernel_ms_median": round(ms[len(ms) // 2], 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "verdict": "Measured" if A.dispatch_count(path) > 0 else "NotEngaged"}
 
 
 def bwd_flops(n: int) -> int:
@@ -859,9 +976,24 @@ def main():
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/traffic.json")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--commands", default="", help="the profiling commands, recorded in traffic.json")
+    ap.add_argument("--traffic-of", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="HBM bytes per launch of every kernel in a FETCH_SIZE / WRITE_SIZE counter run, scaled "
+                         "by the copy calibration recorded in profiles/traffic.json")
+    ap.add_argument("--sparse-diagnostic", choices=("scrub", "pool1g"),
+                    help="only the sparse forward with the Infinity Cache cleared before each launch, or over a "
+                         "1 GiB pool (one JSON line; for counter runs)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from, args.copy_mib, args.commands)
+        return
+    if args.traffic_of:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            cal = json.load(f)
+        fetch, write = _counter_means(args.traffic_of[0], "FETCH_SIZE"), _counter_means(args.traffic_of[1], "WRITE_SIZE")
+        for k in fetch:
+            b = (fetch[k] * cal["fetch_scale"] + write.get(k, 0.0) * cal["write_scale"]) * 1024.0
+            print(json.dumps({"kernel": k, "fetch_kib_raw": round(fetch[k], 1), "write_kib_raw": round(write.get(k, 0.0), 1),
+                              "hbm_bytes_per_launch": int(b)}))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention forward "
@@ -879,17 +1011,26 @@ def main():
     import attention_forward_attn_amd as A
 
     A.load_library()
+    if args.sparse_diagnostic:
+        print(json.dumps(measure_sparse_diagnostic(args.sparse_diagnostic, args.steps, args.warmup)), flush=True)
+        return
     n = WORKLOAD_IDS[args.workload]
     prim = measure(n, args.steps, args.warmup, split=(n == 6))
     others = []
     if not args.primary_only:
-        for m in (2, 3, 4, 5):
+        for m in (1, 2, 3, 4, 5):
             if m == n:
                 continue
             r = measure(m, max(10, args.steps // 2), max(3, args.warmup // 2))
-            others.append({"workload": describe(m), "path": r["path"], "value": round(r["value"], 3),
-                           "unit": r["unit"], "kernel_ms": round(r["timing"]["kernel_ms_mean"], 5),
-                           "roofline": r["roofline"], "verdict": r["verdict"]})
+            ent = {"workload": describe(m), "path": r["path"], "value": round(r["value"], 3),
+                   "unit": r["unit"], "kernel_ms": round(r["timing"]["kernel_ms_mean"], 5),
+                   "roofline": r["roofline"], "verdict": r["verdict"], "inputs_sha256": inputs_sha256(r["inp"])}
+            if m == 1:
+                ent["verdict"] = "Measured (launch-latency bound: 8.4 MFLOP per launch)"
+            if not args.no_cpu_baseline:
+                ent["cpu_baseline"] = cpu_baseline(m, r["inp"], budget_s=6.0)
+                log(f"[bench] cpu oracle ({describe(m)}): {ent['cpu_baseline']}")
+            others.append(ent)
             del r
             torch.cuda.empty_cache()
     # rows beyond the five: the split-KV forward on a decode step (Tq = 1),
@@ -910,6 +1051,10 @@ def main():
         # the dense backward on the prefill workloads it is compiled for
         for m in (2, 3, 7):
             next_rows.append(measure_bwd(m, st, wu))
+            torch.cuda.empty_cache()
+        # where the sparse forward's bytes come from: cache cleared, 1 GiB pool
+        for kind in ("scrub", "pool1g"):
+            next_rows.append(measure_sparse_diagnostic(kind, 10, 2))
             torch.cuda.empty_cache()
         # the sparse backward
         next_rows.append(measure_sparse_bwd(max(3, st // 4), 1))
@@ -968,7 +1113,7 @@ def main():
         "dtype": "bf16" if s.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes; no dataset)",
         "config": {"workload": describe(n), "path": prim["path"], "kernel_ms": round(prim["timing"]["kernel_ms_mean"], 5),
-                   "verdict": prim["verdict"]},
+                   "verdict": prim["verdict"], "inputs_sha256": inputs_sha256(prim["inp"])},
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
         "ceilings": ceil,
