@@ -207,8 +207,12 @@ def roofline(n: int, kernel_ms: float) -> dict:
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(n)}
     ach = w["bytes"] / (kernel_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_for(n)}
+    r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_for(n)}
+    if w["kind"] == "sparse":
+        r["rate"] = ("effective: algorithmic bytes / kernel time; the 64 MiB pool is served partly from the "
+                     "Infinity Cache (1 GiB-pool diagnostic in next_rows)")
+    return r
 
 
 def traffic_for(n: int):
