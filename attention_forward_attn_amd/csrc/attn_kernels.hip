@@ -1811,6 +1811,9 @@ const KernelConfig kTable[] = {
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
     CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
     DMA_ENTRY_X("sparse_bf16_d512", 512, 512, ATTN_CFG_SPARSE, true),
+    DMA_ENTRY_X("sparse_bf16_d512_v384", 512, 384, ATTN_CFG_SPARSE, true),
+    DMA_ENTRY_X("sparse_bf16_d512_v256", 512, 256, ATTN_CFG_SPARSE, true),
+    DMA_ENTRY_X("sparse_bf16_d512_v128", 512, 128, ATTN_CFG_SPARSE, true),
 };
 
 }  // namespace

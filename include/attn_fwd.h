@@ -169,7 +169,11 @@ typedef struct attn_dense_args {
  *   out     [Sq, Hq, d_v] bf16, strides o_ss, o_sh (written)
  *   lse     [Sq, Hq] float32, contiguous (written)
  *   sinks   [Hq] float32 or NULL (same meaning as in the dense call)
- *   No mask beyond the index list. Compiled: d_qk = 512, d_v = 512, Hq = 64.
+ *   No mask beyond the index list. Compiled: d_qk = 512 with d_v = 512, 384,
+ *   256 or 128 (V is always the first d_v columns of the gathered rows, so each
+ *   pool row is still read once), Hq <= 64; other widths return
+ *   ATTN_UNSUPPORTED, d_v > d_qk ATTN_INVALID_ARGUMENT (TensorRT-LLM pull
+ *   request 22028, "Description": the sparse forward at d_qk 512).
  */
 typedef struct attn_sparse_args {
   uint32_t struct_size; /* = sizeof(attn_sparse_args) */

@@ -247,3 +247,18 @@ def test_bwd_workspace_and_validation():
     bad.struct_size = 8
     assert lib.attn_bwd_dense(ctypes.byref(bad), ws, 1 << 20, None) == A.ATTN_ABI_MISMATCH
     assert lib.attn_bwd_dense(ctypes.byref(_fake_bwd(dtype=A.ATTN_F32)), ws, 1 << 20, None) == A.ATTN_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d_v", [128, 256, 384])
+def test_sparse_value_prefix_widths_plan(d_v):
+    """V = the first d_v columns of each 512-wide pool row: d_v in {128, 256, 384} (and 512)
+    are compiled, one kernel path each; other prefixes are UNSUPPORTED."""
+    p = A.plan_sparse_topk(100, 64, 1000, 512, d_v, 300)
+    assert p["path"] == f"sparse_bf16_d512_v{d_v}" and p["grid"] == 100 and p["block_rows"] == 64
+
+
+@pytest.mark.parametrize("d_v", [64, 200, 448])
+def test_sparse_value_prefix_unsupported(d_v):
+    with pytest.raises(A.AttnUnsupported):
+        A.plan_sparse_topk(10, 64, 1000, 512, d_v, 30)
+

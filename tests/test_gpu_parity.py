@@ -338,3 +338,27 @@ def test_sparse_random_sweep(seed):
                                           sinks=inp["sinks"])
     eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
     assert eo <= TOL_O and el <= TOL_LSE, f"sparse sweep: max|dO|={eo:.3e} max|dlse|={el:.3e}"
+
+
+@pytest.mark.parametrize("d_v,Hq,topk,sinks", [(128, 64, 500, False), (256, 64, 500, True), (384, 64, 500, True),
+                                               (256, 16, 5000, False), (384, 64, 97, False)])
+def test_sparse_value_prefix(d_v, Hq, topk, sinks):
+    """V = the first d_v columns of each gathered 512-wide pool row (d_v < d_qk): the
+    kernel path of that width runs and matches the oracle's prefix reading."""
+    Sq, N = 5, 6000
+    inp = synth.randn_sparse(Sq, Hq, N, 512, topk, seed=d_v + topk, sinks=sinks)
+    idx = inp["idx"].clone()
+    idx[0, 3] = -1
+    idx[1, topk - 1] = N + 1
+    idx[2, 1] = idx[2, 0]
+    announce(f"sparse value prefix d_v={d_v} Hq={Hq} topk={topk} sinks={sinks}")
+    A.reset_dispatch_counts()
+    out, lse = A.sparse_topk(inp["q"].cuda(), inp["kv"].cuda(), idx.cuda(), d_v=d_v,
+                             sinks=inp["sinks"].cuda() if sinks else None)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (Sq, Hq, d_v)
+    assert A.dispatch_count(f"sparse_bf16_d512_v{d_v}") == 1 and A.dispatch_count("sparse_bf16_d512") == 0
+    ro, rl = oracle.sparse_topk_attention(inp["q"], inp["kv"], idx, d_v=d_v, scale=1 / math.sqrt(512),
+                                          sinks=inp["sinks"])
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"d_v {d_v}: max|dO|={eo:.3e} max|dlse|={el:.3e}"
