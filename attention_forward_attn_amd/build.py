@@ -46,7 +46,7 @@ def build(verbose: bool = False, resource_report: bool = False, defines=(), out:
         obj = os.path.join(ROOT, "_build", os.path.basename(src) + tag + ".o")
         cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + ["-c", src, "-o", obj]
         if src.endswith(".cpp"):
-            cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", src, "-o", obj]
+            cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + ["-x", "hip", "-c", src, "-o", obj]
         if resource_report and src.endswith(".hip"):
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
         if verbose:

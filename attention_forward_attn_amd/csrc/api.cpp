@@ -950,10 +950,11 @@ attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace,
 // ---------------------------------------------------------------- quantized K/V decode
 namespace {
 
+// index into kQkvPaths: (q8_0, q4_0) x (d 128, d 256)
 static int qkv_path(int fmt, int d) {
   const int f = fmt == ATTN_KV_Q8_0 ? 0 : (fmt == ATTN_KV_Q4_0 ? 1 : -1);
-  if (f < 0 || d != 128) return -1;
-  return f;
+  if (f < 0 || (d != 128 && d != 256)) return -1;
+  return f + (d == 256 ? 2 : 0);
 }
 
 static attn_status validate_qkv_shape(const attn_qkv_args* a) {

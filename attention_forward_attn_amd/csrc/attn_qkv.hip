@@ -289,6 +289,9 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
       const int d0 = kc * 8, bb = r * RB + (d0 / 32) * BB;
       *reinterpret_cast<u32x4*>(kt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rkb, bb, d0 % 32);
       *reinterpret_cast<u32x4*>(vt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rvb, bb, d0 % 32);
+      // decode two chunks at a time: hoisting every raw read of the tile ahead
+      // of its use would hold 8 registers per chunk (wide heads spill)
+      if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
     // one wave: its own LDS writes are visible to its later LDS reads
     lds_order();
@@ -315,10 +318,27 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
       const float alpha = grow ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c)) : 1.f;
       if (grow) m_run = mnew;
       l_run *= alpha;
+      if constexpr (DT >= 8) {
+        // wide heads: the accumulator fills the AGPRs; scale each value in
+        // place (read, multiply, write back) so that no copy of it is held in
+        // VGPRs. The wait covers the last MFMA that wrote an accumulator.
+        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+          for (int i = 0; i < 16; ++i) {
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\t"
+                         "v_accvgpr_write_b32 %0, %1"
+                         : "+a"(acc[dt][i]), "=&v"(tmp)
+                         : "v"(alpha));
+          }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+      }
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
     float P[16], rs = 0.f;
@@ -412,12 +432,16 @@ int occ_cfg() {
 int launch_qkv(const QkvParams& p, int fmt, int d, void* stream) {
   if (fmt == kFmtQ8 && d == 128) return launch_cfg<kFmtQ8, 128>(p, stream);
   if (fmt == kFmtQ4 && d == 128) return launch_cfg<kFmtQ4, 128>(p, stream);
+  if (fmt == kFmtQ8 && d == 256) return launch_cfg<kFmtQ8, 256>(p, stream);
+  if (fmt == kFmtQ4 && d == 256) return launch_cfg<kFmtQ4, 256>(p, stream);
   return -1;
 }
 
 int occupancy_qkv(int fmt, int d) {
   if (fmt == kFmtQ8 && d == 128) return occ_cfg<kFmtQ8, 128>();
   if (fmt == kFmtQ4 && d == 128) return occ_cfg<kFmtQ4, 128>();
+  if (fmt == kFmtQ8 && d == 256) return occ_cfg<kFmtQ8, 256>();
+  if (fmt == kFmtQ4 && d == 256) return occ_cfg<kFmtQ4, 256>();
   return 0;
 }
 

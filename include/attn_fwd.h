@@ -513,7 +513,10 @@ attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace,
  *         pointers 4-byte aligned
  *   out   [B, H, Tq, d] bf16 (written), lse [B, H, Tq] fp32 contiguous (written)
  *   sinks [H] fp32 or NULL; causal bottom-right as in attn_dense_args.
- *   Compiled: kv_format Q8_0 or Q4_0 (K and V alike), d = 128.
+ *   Compiled: kv_format Q8_0 or Q4_0 (K and V alike), d = 128 or 256 (the
+ *   llama.cpp page's "Overview" lists head sizes 128, 256 and 512; 512 is
+ *   ATTN_UNSUPPORTED: one wave would hold a 512-wide row's output and query,
+ *   more registers than a wave has).
  *
  * Keys are cut into ranges as in attn_fwd_dense_splitkv (n_splits, 0 = the
  * library's choice; workspace n * B*H*Tq * (d + 1) * 4 bytes from

@@ -48,14 +48,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}T{c[3]}x{c[4]}"
                          f"{'c' if c[5] else 'n'}{'s' if c[6] else ''}n{c[7]}")
-def test_qkv_matches_oracle(case, fmt):
+def test_qkv_matches_oracle(case, fmt, d):
     B, H, Hkv, Tq, Tk, causal, sinks, n = case
-    announce(f"qkv {fmt} {case}")
-    inp = synth.make_quant_kv(B, H, Hkv, Tq, Tk, 128, fmt, seed=Tq * 13 + Tk, sinks=sinks)
-    scale = 1 / math.sqrt(128)
+    announce(f"qkv {fmt} d{d} {case}")
+    inp = synth.make_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, seed=Tq * 13 + Tk + d, sinks=sinks)
+    scale = 1 / math.sqrt(d)
     out, lse = run(inp, causal=causal, scale=scale, n_splits=n)
     ro, rl = reference(inp, causal=causal, scale=scale)
     eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
@@ -74,6 +75,17 @@ def test_qkv_dispatch_no_conversion():
         assert A.dispatch_count(path) == 0
 
 
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_qkv_dispatch_d256(fmt):
+    """256-wide heads run their own kernel path (and no 128-wide one)."""
+    inp = synth.make_quant_kv(1, 8, 2, 2, 300, 256, fmt, seed=3)
+    A.reset_dispatch_counts()
+    out, lse = run(inp, causal=True, scale=1 / 16, n_splits=2)
+    assert A.dispatch_count(f"dense_qkv_{fmt}_d256") == 1 and A.dispatch_count(f"dense_qkv_{fmt}_d128") == 0
+    ro, rl = reference(inp, causal=True, scale=1 / 16)
+    assert _o_err(_np(out), ro) <= TOL_O and _lse_err(_np(lse), rl) <= TOL_LSE
+
+
 def test_qkv_rejects():
     inp = synth.make_quant_kv(1, 4, 2, 2, 64, 128, "q8_0", seed=2)
     q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
@@ -81,6 +93,9 @@ def test_qkv_rejects():
         A.dense_qkv(q, k, v, fmt="q5_0", causal=True)
     with pytest.raises(A.AttnInvalidArgument):   # row bytes do not match the format
         A.dense_qkv(q, k[..., :68], v[..., :68], fmt="q8_0", causal=True)
+    wide = synth.make_quant_kv(1, 4, 2, 2, 64, 512, "q8_0", seed=4)
+    with pytest.raises(A.AttnUnsupported):       # 512-wide heads are not compiled
+        A.dense_qkv(wide["q"].cuda(), wide["k"].cuda(), wide["v"].cuda(), fmt="q8_0", causal=True)
     torch.cuda.synchronize()
 
 

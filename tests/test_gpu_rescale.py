@@ -119,16 +119,17 @@ def test_sparse_rescale(Sq, N, topk, mode):
 
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
-def test_qkv_rescale(fmt, mode):
-    inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, 128, fmt, mode, sinks=True, seed=77)
-    label = f"qkv {fmt} {mode}"
+@pytest.mark.parametrize("d", [128, 256])
+def test_qkv_rescale(d, fmt, mode):
+    inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, d, fmt, mode, sinks=True, seed=77)
+    label = f"qkv {fmt} d{d} {mode}"
     announce(label)
     q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
     out, lse = A.dense_qkv(q, k, v, fmt=fmt, causal=True, sinks=inp["sinks"].cuda())
     torch.cuda.synchronize()
     kd = oracle.dequantize_rows(inp["k"], fmt)
     vd = oracle.dequantize_rows(inp["v"], fmt)
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     ro, rl = oracle.dense_attention(inp["q"], kd, vd, scale=scale, causal=True, sinks=inp["sinks"])
     assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item(), f"{label}: NaN in the result"
     # The kernel rounds every decoded key value d * code to f16 once (unit
