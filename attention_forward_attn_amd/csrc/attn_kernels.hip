@@ -1,48 +1,53 @@
 // Fused attention forward for AMD CDNA4 (gfx950 / MI355X).
 //
-// One workgroup owns a block of query rows and streams keys through LDS:
+// One workgroup owns a block of query rows and streams the keys through LDS:
 //
 //   S^T = K Q^T      on v_mfma_f32_32x32x16_bf16 (fp32 accumulate)
 //   online softmax   row max / row sum kept in registers, exp2 with the
-//                    scale*log2(e) factor folded into one FMA
+//                    scale*log2(e) factor folded into one FMA, lazy rescale
 //   O^T += V^T P^T   on the same MFMA, P taken straight from the S^T
 //                    accumulators after bf16 packing
 //
 // The scores are computed transposed (keys along the MFMA M dimension,
 // queries along N) so that every lane owns exactly one query row: lane l holds
 // query column l%32 and 16 of the 32 keys of a 32x32 tile, the other 16 being
-// in lane l^32. Row max and row sum are therefore in-lane reductions plus one
-// exchange with the partner half-wave, the rescale of the output accumulator
-// is a per-lane multiply, and the accumulator layout of S^T is already the B
-// operand layout that O^T = V^T P^T needs (no shuffle of P).
+// in lane l^32. Row max and row sum are in-lane reductions plus one exchange
+// with the partner half-wave (v_permlane32_swap), the rescale of the output
+// accumulator is a per-lane multiply, and the S^T accumulator is already laid
+// out as the B operand that O^T = V^T P^T needs (no shuffle of P).
 //
-// K is staged in LDS row-major ([key][d], rows padded by 16 bytes so that the
-// 32 rows read by one A-operand load fall in distinct banks). V is staged
-// transposed ([d][key]) because the PV contraction runs over keys: each
-// thread loads a 4-key x 8-d block with 16-byte global loads and transposes
-// it in registers before writing 8-byte rows. Keys inside each 16-key group
-// are stored in the order {0-3, 8-11, 4-7, 12-15}, which is the order in which
-// the S^T accumulator hands them to the B operand, so one lane's eight V^T
-// values are contiguous.
+// Two kernel families live here:
 //
-// Tiles are double-buffered in LDS with a register prefetch: the global loads
-// of tile i+2 are in flight while tile i is being multiplied.
+//   attn_fwd_dma_kernel (every bf16 path: dense, folded GQA/MQA, split-KV,
+//     windows, packed batches, two-part MLA rows, sparse top-k). K and V tiles
+//     go from global memory straight into LDS with global_load_lds_dwordx4
+//     (16 bytes per lane, no staging registers); the bank-conflict swizzle is
+//     applied on the global side, and the V^T operands of the PV product are
+//     read from the row-major V tile with ds_read_b64_tr_b16 (no transposed
+//     copy of V exists). Loads are issued from inline asm and waited for with
+//     exact per-wave vmcnt counts and plain s_barriers. Narrow heads (64, 128,
+//     192) run two wave groups per workgroup that alternate their MFMA half
+//     (S and PV) and their softmax half on each SIMD; 256- and 512-wide heads
+//     split d over DS waves of a query group and sum the partial scores
+//     through LDS. Described in detail above the kernel.
+//
+//   attn_fwd_kernel (fp32 inputs only, the tiny workload): the first kernel of
+//     this library, register-staged: 16-byte global loads into registers, V
+//     transposed in registers (4 keys x 8 columns per thread) and stored to
+//     LDS as V^T, each fp32 q/k value split into a bf16 hi + lo pair so that
+//     S = hi*hi + hi*lo + lo*hi keeps ~16 bits on the bf16 MFMA.
 //
 // GQA/MQA: the query rows of one (batch, kv head) are the folded view
 // [g*Tq, d] of q[B,H,Tq,d] with kv-major heads (ArcFlash pull request,
-// "What rung 0 does"): folded row f is head kv*g + f/Tq at token f%Tq. The
-// fold is pure index arithmetic; nothing is copied.
-//
-// d = 512: a group of DS waves shares each 32-row query block; wave i of the
-// group computes a partial S over d_qk/DS columns, the partials are summed
-// through LDS, and the wave keeps the output columns [i*d_v/DS, (i+1)*d_v/DS).
-// This keeps the fp32 output accumulator at 128 registers per lane.
+// "What rung 0 does"): pure index arithmetic, nothing is copied. The bf16
+// kernels order the folded rows token-major (row t*g + head) so that a causal
+// tile spans few tokens.
 //
 // Sparse top-k (TensorRT-LLM pull request 22028, "Description"): the rows of a
-// workgroup are the heads of one query; the keys are pool rows named by the
-// query's index list, gathered with 16-byte loads into the same LDS tiles. The
-// value rows are the first d_v columns of the same gathered rows, so every
-// gathered row is read from memory once and serves both products.
+// workgroup are the heads of one query; the keys are the pool rows named by
+// the query's index list, gathered into the same LDS tiles. The value rows are
+// the first d_v columns of the same gathered rows, so every gathered row is
+// read from memory once and serves both products.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
