@@ -289,9 +289,9 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
       const int d0 = kc * 8, bb = r * RB + (d0 / 32) * BB;
       *reinterpret_cast<u32x4*>(kt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rkb, bb, d0 % 32);
       *reinterpret_cast<u32x4*>(vt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rvb, bb, d0 % 32);
-      // decode two chunks at a time: hoisting every raw read of the tile ahead
-      // of its use would hold 8 registers per chunk (wide heads spill)
-      if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      // wide heads decode two chunks at a time: hoisting every raw read of the
+      // tile ahead of its use would hold 8 registers per chunk (they spill)
+      if (D >= 256 && i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
     // one wave: its own LDS writes are visible to its later LDS reads
     lds_order();
