@@ -1004,7 +1004,8 @@ struct QkvPlan {
 };
 
 static QkvPlan plan_qkv(const attn_qkv_args* a, int n_req) {
-  QkvPlan pl{1, a->Tk, (int)(((int64_t)(a->H / a->Hkv) * a->Tq + 31) / 32), 0};
+  // a workgroup owns 16 folded query rows of one (b, kv head)
+  QkvPlan pl{1, a->Tk, (int)(((int64_t)(a->H / a->Hkv) * a->Tq + 15) / 16), 0};
   const int nblocks = (a->Tk + 31) / 32;
   if (nblocks <= 1 || a->Tq == 0) return pl;
   int want = n_req;

@@ -185,7 +185,7 @@ struct QkvParams {
   int32_t causal;
   float scale;
   float c;                   // scale * log2(e)
-  int32_t n_rt;              // 32-row tiles per (b, kv head)
+  int32_t n_rt;              // 16-row tiles per (b, kv head)
   int32_t n_splits, split_keys;
   float* part_o;             // [n_splits][B*H*Tq][d] when n_splits > 1
   float* part_lse;

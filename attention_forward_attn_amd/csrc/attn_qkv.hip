@@ -4,22 +4,31 @@
 // values along the head dimension: an fp16 scale, then 32 int8 codes or 16
 // bytes of 4-bit codes). The llama.cpp page ("Pins #303") describes the point
 // of the in-kernel path: the attention kernel dequantizes the K/V tiles it
-// loads, instead of converting the whole cache to f16 on every step. Here each
-// 32-key tile goes from global memory into LDS as raw bytes (coalesced dword
-// loads), is decoded by the wave into f16 tiles in LDS, and feeds f16 MFMAs:
+// loads, instead of converting the whole cache to f16 on every step.
 //
-//   S^T = K Q^T      v_mfma_f32_32x32x16_f16, the lane owns one query row
-//   online softmax   as in the bf16 forward (base-2, lane-local row state)
-//   O^T += V^T P^T   V^T fragments by transposed LDS reads of the f16 tile
+// A wave owns 16 folded query rows (GQA: the g heads x Tq tokens of one kv
+// head, e.g. 4 heads x 4 tokens of a multi-sequence decode step) and walks
+// 32-key tiles with v_mfma_f32_16x16x32_f16:
+//
+//   raw bytes   each lane loads, straight into registers, the whole blocks it
+//               decodes: block (4i + lane/16) of two keys (lane%16 and
+//               16 + lane%16), so one lane decodes one key's block end to end
+//   S^T = K Q^T the decoded K block is the MFMA's A operand as it stands
+//               (the contraction order over d is permuted so that a lane's
+//               eight k-elements of step 4i + c are chunk c of its block;
+//               q is loaded in the same order); K never goes through LDS
+//   softmax     online, base 2, lazy rescale; a query's four lane groups
+//               reduce through permlane swaps
+//   O^T += V^T P^T  the decoded V block goes to the wave's f16 tile in LDS and
+//               comes back as V^T by transposed reads
 //
 // f16 keeps the decoded values to 11 significant bits (a q8_0 value d*q needs
 // up to 18) where bf16 would keep 8; q is converted from bf16 exactly.
 //
-// One wave per workgroup: a workgroup owns up to 32 folded query rows (GQA:
-// the g heads x Tq tokens of one kv head, e.g. 4 heads x 4 tokens of a
-// multi-sequence decode step) and one range of keys (grid y), writing the
-// range's partial result for the split-KV merge; with one range it writes
-// out and lse directly.
+// A workgroup holds NW waves on the same rows; they take the tiles of its key
+// range in turn and merge their (max, sum, O) through LDS at the end, so a
+// workgroup writes one result: the output, or with several key ranges (grid
+// y) the range's partial result for the split-KV merge.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,8 +42,8 @@ typedef _Float16 f16_t;
 typedef __bf16 bf16_t;
 typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef f16_t f16x2 __attribute__((ext_vector_type(2)));
 typedef f16_t f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -44,16 +53,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kFmtQ8 = 8, kFmtQ4 = 2;  // the ggml type numbers of q8_0 and q4_0
 
-__device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+// max / sum over a query's four lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float groups_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+__device__ __forceinline__ float groups_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -68,35 +82,13 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// The raw tiles are written as 32-bit words and read as 16-bit halves, the
-// f16 tiles written as 128-bit chunks and read as MFMA operands: a compiler
-// barrier keeps these differently typed LDS accesses in program order (the
-// wave's LDS operations then complete in order).
+// The V tile is written as 128-bit chunks and read back by transposed 64-bit
+// reads: a compiler barrier keeps these LDS accesses in program order (one
+// wave's LDS operations complete in order).
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t lds_u32(const void* ptr) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
-}
-
-__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
-  const uint64_t v = (uint64_t)(uintptr_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// 4 bytes per lane from global memory straight into LDS at m0 + 4 * lane
-// (wave-uniform base in scalar registers, per-lane 32-bit byte offset); the
-// compiler does not see these loads, so their waits are explicit
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-// 16-byte chunk swizzle of a tile row with CPR chunks (64 LDS banks), as in
-// the bf16 kernels: 16 consecutive rows put one logical chunk in distinct bank
-// groups, aligned 4-row groups put a 4-chunk group in distinct groups.
+// 16-byte chunk swizzle of a V tile row of CPR chunks (64 LDS banks): 16
+// consecutive rows put one logical chunk in 16 distinct bank groups.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
   static_assert(CPR % 16 == 0, "rows of whole 256-byte groups");
@@ -108,97 +100,116 @@ __device__ __forceinline__ int chunk_at(int r, int c) {
   return r * (CPR * 8) + ((c ^ swz<CPR>(r)) << 3);
 }
 
-// A operand rows: lane row `row`, columns 16s + 8lh .. +7
+// A operand V^T for output columns c0..c0+15 (lane%16) and keys {4g..4g+3,
+// 16+4g..16+4g+3} of the tile (g = lane/16, the keys of the lane's P values):
+// each 16-lane group reads a 4-key x 16-column block per transposed read and
+// lane i receives column i of it.
 template <int CPR>
-__device__ __forceinline__ f16x8 row_frag(const f16_t* tile, int row, int s, int lh) {
-  return *reinterpret_cast<const f16x8*>(tile + chunk_at<CPR>(row, 2 * s + lh));
-}
-
-// A operand X^T (32 columns by 16 rows r0..r0+15) by two transposed reads; the
-// rows arrive in the order the B operand built from a 32x32 accumulator takes
-// them (elements 8ks .. 8ks+7)
-template <int CPR>
-__device__ __forceinline__ f16x8 tr_frag(const f16_t* tile, int r0, int c0, int lane) {
-  const int vg = lane >> 4, vi = lane & 15;
-  const int vrow = (vg >> 1) * 4 + (vi >> 2);
-  const int col = c0 + (vg & 1) * 16 + 4 * (vi & 3);
+__device__ __forceinline__ f16x8 v_frag(const f16_t* tile, int c0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = c0 + 4 * (i & 3);
   uint32_t w[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = r0 + vrow + 8 * h;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = 16 * hh + 4 * g + (i >> 2);
     const f16_t* ptr = tile + row * (CPR * 8) + (((col >> 3) ^ swz<CPR>(row)) << 3) + (col & 7);
     const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)ptr);
-    w[2 * h] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
-    w[2 * h + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
+    w[2 * hh] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
+    w[2 * hh + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
   }
   return __builtin_bit_cast(f16x8, u32x4{w[0], w[1], w[2], w[3]});
 }
 
-// Decode 8 consecutive values (elements w0..w0+7 of one block, w0 a multiple
-// of 8) of the raw block at byte `bb` of the LDS byte array `raw` into 4 words
-// of packed f16.
-//
-// Packed f16 arithmetic: a byte b (0..255) placed under the exponent bits
-// 0x64 is the f16 number 1024 + b exactly, so codes become f16 with one
-// byte permute and one OR per pair, the offset (1024 + 128 for int8 codes
-// stored with their sign bit flipped, 1024 + 8 for nibbles) goes with one
-// packed subtract, and the scale with one packed multiply (d * code rounded
-// once to f16, as a single f32 product rounded to f16 would be).
-typedef f16_t f16x2 __attribute__((ext_vector_type(2)));
+// Block geometry. A block sits at byte 34 b (q8_0) or 18 b (q4_0) of a row
+// whose length is a multiple of 4, so even blocks start 4-byte aligned and odd
+// blocks 2 bytes past a dword. A lane loads WIN dwords from the dword at or
+// just before its block (2 bytes early for odd blocks, which stays inside the
+// row: the previous block's codes) and shifts them by those 2 bytes, which
+// gives n[x] = bytes 4x .. 4x+3 of the block: the scale in n[0]'s low half,
+// code byte k at byte 2 + k. The window of an even block runs 2 bytes into
+// the next block of the same row (the last block of a row is odd).
+template <int FMT>
+struct Blk {
+  static constexpr int BB = FMT == kFmtQ8 ? 34 : 18;  // bytes per block
+  static constexpr int WIN = (BB + 2 + 3) / 4;          // dwords loaded per block
+};
 
-__device__ __forceinline__ uint32_t scale_pair(uint32_t four_bytes_lo_hi, uint32_t sel, f16x2 offset, f16x2 d2) {
-  const uint32_t bits = __builtin_amdgcn_perm(0u, four_bytes_lo_hi, sel) | 0x64006400u;
-  const f16x2 v = (__builtin_bit_cast(f16x2, bits) - offset) * d2;
-  return __builtin_bit_cast(uint32_t, v);
+// Decode one block from its normalised dwords n[] into 16 words of packed f16
+// (word m = values 2m, 2m + 1).
+//
+// Packed f16 arithmetic: a byte b placed under the exponent byte 0x64 is the
+// f16 number 1024 + b exactly; one byte permute with 0x64 bytes as its other
+// source builds two such numbers, one packed subtract removes the offset
+// (1024 + 128 for int8 codes with their sign bit flipped, 1024 + 8 for
+// nibbles) and one packed multiply applies the scale (d * code rounded once
+// to f16, as the single f32 product rounded to f16 would be).
+__device__ __forceinline__ uint32_t code_pair(uint32_t word, int m, f16x2 off, f16x2 d2) {
+  // values 2m, 2m+1 sit at bytes 2 + 2m, 3 + 2m: byte 2 and 3 of the word for
+  // even m, bytes 0 and 1 for odd m; selector 4 takes byte 0 of the first
+  // source (0x64)
+  const uint32_t sel = (m & 1) ? 0x04010400u : 0x04030402u;
+  const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, word, sel);
+  return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, bits) - off) * d2);
 }
 
 template <int FMT>
-__device__ __forceinline__ u32x4 decode8(const unsigned char* raw, int bb, int w0) {
-  const f16_t d = __builtin_bit_cast(f16_t, *reinterpret_cast<const uint16_t*>(raw + bb));
-  const f16x2 d2 = {d, d};
-  // the 8 code bytes (q8_0) or the 8 bytes holding the nibbles (q4_0), read as
-  // 2-byte halves (blocks are 2-byte aligned)
-  const uint16_t* cp = reinterpret_cast<const uint16_t*>(raw + bb + 2 + (FMT == kFmtQ8 ? w0 : (w0 & 15)));
-  uint32_t lo = (uint32_t)cp[0] | ((uint32_t)cp[1] << 16), hi = (uint32_t)cp[2] | ((uint32_t)cp[3] << 16);
-  f16x2 off;
+__device__ __forceinline__ void decode_block(const uint32_t (&n)[Blk<FMT>::WIN], uint32_t (&dec)[16]) {
+  constexpr int WIN = Blk<FMT>::WIN;
+  const f16x2 d2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(n[0], n[0], 0x01000100u));
   if constexpr (FMT == kFmtQ8) {
-    lo ^= 0x80808080u;  // int8 q -> q + 128
-    hi ^= 0x80808080u;
-    off = f16x2{(f16_t)1152.f, (f16_t)1152.f};
+    uint32_t c[WIN];
+#pragma unroll
+    for (int x = 0; x < WIN; ++x) c[x] = n[x] ^ 0x80808080u;  // int8 q -> q + 128 (n[0]'s scale bytes unused)
+    const f16x2 off = {(f16_t)1152.f, (f16_t)1152.f};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) dec[m] = code_pair(c[(m + 1) >> 1], m, off, d2);
   } else {
-    // element e < 16: low nibble of byte e; element e >= 16: high nibble of byte e - 16
-    const int sh = w0 >= 16 ? 4 : 0;
-    lo = (lo >> sh) & 0x0f0f0f0fu;
-    hi = (hi >> sh) & 0x0f0f0f0fu;
-    off = f16x2{(f16_t)1032.f, (f16_t)1032.f};
+    // value e < 16: low nibble of code byte e; value e >= 16: high nibble of byte e - 16
+    uint32_t lo[WIN], hi[WIN];
+#pragma unroll
+    for (int x = 0; x < WIN; ++x) {
+      lo[x] = n[x] & 0x0f0f0f0fu;
+      hi[x] = (n[x] >> 4) & 0x0f0f0f0fu;
+    }
+    const f16x2 off = {(f16_t)1032.f, (f16_t)1032.f};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      dec[m] = code_pair(lo[(m + 1) >> 1], m, off, d2);
+      dec[m + 8] = code_pair(hi[(m + 1) >> 1], m, off, d2);
+    }
   }
-  // byte k of the result pair: selector 0..3 picks byte k of the second
-  // operand, 0x0c gives 0
-  return u32x4{scale_pair(lo, 0x0c010c00u, off, d2), scale_pair(lo, 0x0c030c02u, off, d2),
-               scale_pair(hi, 0x0c010c00u, off, d2), scale_pair(hi, 0x0c030c02u, off, d2)};
 }
 
-template <int FMT, int D>
-__global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
-  constexpr int BN = 32;                          // keys per tile
-  constexpr int BB = FMT == kFmtQ8 ? 34 : 18;     // bytes per 32-value block
-  constexpr int RB = D / 32 * BB;                 // bytes per cache row
-  constexpr int RAW_DW = BN * RB / 4;             // dwords of one raw tile
-  constexpr int RAW_PL = RAW_DW / 64;             // per lane
-  constexpr int CPR = D / 8, KS = D / 16, DT = D / 32;
-  constexpr int CH_PL = BN * CPR / 64;            // decoded 8-value chunks per lane per tile
-  static_assert(RB % 4 == 0 && RAW_DW % 64 == 0 && (BN * CPR) % 64 == 0, "tile shapes");
-  // raw tiles, two stages each (the next tile lands while this one is decoded)
-  __shared__ __attribute__((aligned(16))) uint32_t rawk[2][RAW_DW];
-  __shared__ __attribute__((aligned(16))) uint32_t rawv[2][RAW_DW];
-  __shared__ __attribute__((aligned(16))) f16_t kt[BN * D];
-  __shared__ __attribute__((aligned(16))) f16_t vt[BN * D];
+// raw window dwords -> block dwords (shift by sh = 0 or 2 bytes)
+template <int WIN>
+__device__ __forceinline__ void normalise(const uint32_t (&r)[WIN], uint32_t sh, uint32_t (&n)[WIN]) {
+#pragma unroll
+  for (int x = 0; x < WIN; ++x) n[x] = __builtin_amdgcn_alignbyte(r[x + 1 < WIN ? x + 1 : x], r[x], sh);
+}
 
-  const int lane = threadIdx.x, lq = lane & 31, lh = lane >> 5;
+template <int FMT, int D, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 2)))
+qkv_decode_kernel(const QkvParams p) {
+  constexpr int BN = 32;                   // keys per tile
+  constexpr int BB = Blk<FMT>::BB, WIN = Blk<FMT>::WIN;
+  constexpr int NBK = D / 32;              // blocks per row
+  constexpr int BPL = NBK / 4;             // blocks per key a lane decodes
+  constexpr int KS = D / 32;               // S MFMA steps
+  constexpr int DT = D / 16;               // 16-column output tiles
+  constexpr int CPR = D / 8;
+  static_assert(NBK % 4 == 0 && DT % NW == 0, "shapes");
+  // one f16 V tile per wave; after the key loop the same bytes hold the
+  // waves' partial outputs (NW x DT x 64 lanes x 16 bytes, the same size)
+  __shared__ __attribute__((aligned(16))) f16_t vt_all[NW * BN * D];
+  __shared__ float ml_all[NW][16][2];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ql = lane & 15, lg = lane >> 4;
+  f16_t* vt = vt_all + w * (BN * D);
   const int grp = blockIdx.x / p.n_rt, rt = blockIdx.x % p.n_rt;
   const int b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int rows = p.g * p.Tq;
-  const int f0 = rt * 32, f = f0 + lq;
+  const int f0 = rt * 16, f = f0 + ql;
   const bool valid = f < rows;
   const int fc = valid ? f : rows - 1;
   const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
@@ -207,7 +218,7 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
   // keys the tile's rows can see, then this workgroup's key range
   int kend = p.Tk;
   if (p.causal) {
-    const int f_last = min(f0 + 32, rows) - 1;
+    const int f_last = min(f0 + 16, rows) - 1;
     const int t_hi = (f_last / p.Tq != f0 / p.Tq) ? p.Tq - 1 : f_last % p.Tq;
     kend = min(p.Tk, max(0, t_hi + off + 1));
   }
@@ -221,206 +232,218 @@ __global__ void __launch_bounds__(64) qkv_decode_kernel(const QkvParams p) {
   row_lim = min(row_lim, kend - 1);
   const int nb = (kend + BN - 1) / BN;
 
-  // q row of this lane as f16 (exact for bf16 values within the f16 range)
+  // q row of this lane as f16, in the permuted contraction order: step s
+  // takes values 32 * (4 (s / 4) + lane/16) + 8 (s % 4) .. + 7
   f16x8 qf[KS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + s * 16 + lh * 8);
+      const int d0 = 32 * ((s / 4) * 4 + lg) + 8 * (s % 4);
+      const u32x4 wq = *reinterpret_cast<const u32x4*>(qp + d0);
       uint32_t o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_h2(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xffff0000u));
+      for (int e = 0; e < 4; ++e) o[e] = pack_h2(__uint_as_float(wq[e] << 16), __uint_as_float(wq[e] & 0xffff0000u));
       qf[s] = __builtin_bit_cast(f16x8, u32x4{o[0], o[1], o[2], o[3]});
     }
   }
 
   const unsigned char* kb = p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)k_lo * p.k_st;
   const unsigned char* vb = p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)k_lo * p.v_st;
-  // raw dwords of tile j: dword w = i*64 + lane is byte 4w of the tile's
-  // rows laid end to end (row r = 4w / RB); rows past kend repeat row kend-1.
-  // Byte offsets stay below 2^32: the host limits a range to 2^31 bytes.
-  const void* kbs = uniform_ptr(kb);
-  const void* vbs = uniform_ptr(vb);
-  // rows packed back to back (token stride == row bytes, the usual cache
-  // layout): a whole tile is one contiguous byte range, so every load is a
-  // scalar base plus the lane's fixed offset 4 * (64 i + lane)
-  const bool packed = p.k_st == RB && p.v_st == RB;
-  auto load = [&](int j) {
-    const uint32_t lk = lds_u32(rawk[j & 1]), lv = lds_u32(rawv[j & 1]);
-    if (packed && (j + 1) * BN <= kend) {
-      const void* ks = uniform_ptr(kb + (int64_t)j * BN * RB);
-      const void* vs = uniform_ptr(vb + (int64_t)j * BN * RB);
+  const uint32_t kst = (uint32_t)p.k_st, vst = (uint32_t)p.v_st;
+  const uint32_t sh = (lg & 1) * 2;
+  // window start of the lane's block i within a row
+  uint32_t boff[BPL];
 #pragma unroll
-      for (int i = 0; i < RAW_PL; ++i) {
-        dma4(ks, 4u * (uint32_t)(i * 64 + lane), lk + 256u * i);
-        dma4(vs, 4u * (uint32_t)(i * 64 + lane), lv + 256u * i);
+  for (int i = 0; i < BPL; ++i) boff[i] = (uint32_t)((i * 4 + lg) * BB) - sh;
+
+  // raw windows of tile j: [key half][block][dword]; keys past kend repeat
+  // key kend - 1 (their scores are masked). Byte offsets stay below 2^31: the
+  // host limits one head's rows to that.
+  uint32_t rk[2][BPL][WIN], rv[2][BPL][WIN];
+  auto load = [&](const unsigned char* base, uint32_t st, int j, uint32_t (&r)[2][BPL][WIN]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint32_t key = (uint32_t)min(j * BN + kh * 16 + ql, kend - 1);
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(base + (key * st + boff[i]));
+#pragma unroll
+        for (int x = 0; x < WIN; ++x) r[kh][i][x] = wp[x];
       }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < RAW_PL; ++i) {
-      const int w = i * 64 + lane, r = (4 * w) / RB, c = (4 * w) % RB;
-      const int key = min(j * BN + r, kend - 1);
-      dma4(kbs, (uint32_t)(key * (uint32_t)p.k_st + c), lk + 256u * i);
-      dma4(vbs, (uint32_t)(key * (uint32_t)p.v_st + c), lv + 256u * i);
     }
   };
 
-  f32x16 acc[DT];
+  f32x4 acc[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (nb > 0) load(0);
-  for (int j = 0; j < nb; ++j) {
-    // tile j has landed; every LDS read of the previous iteration has returned
-    // before the next tile's loads may overwrite the other stage
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    if (j + 1 < nb) load(j + 1);  // in flight while this tile is decoded and multiplied
-    // decode: chunk c = (key r, 8 values from column 8 * (c % CPR))
-    const unsigned char* rkb = reinterpret_cast<const unsigned char*>(rawk[j & 1]);
-    const unsigned char* rvb = reinterpret_cast<const unsigned char*>(rawv[j & 1]);
+  if (w < nb) {
+    load(kb, kst, w, rk);
+    load(vb, vst, w, rv);
+  }
+  for (int j = w; j < nb; j += NW) {
+    const bool more = j + NW < nb;
+    // S^T for the tile's two 16-key halves, K decoded straight into the A operand
+    f32x4 S[2];
 #pragma unroll
-    for (int i = 0; i < CH_PL; ++i) {
-      const int c = i * 64 + lane, r = c / CPR, kc = c % CPR;
-      const int d0 = kc * 8, bb = r * RB + (d0 / 32) * BB;
-      *reinterpret_cast<u32x4*>(kt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rkb, bb, d0 % 32);
-      *reinterpret_cast<u32x4*>(vt + chunk_at<CPR>(r, kc)) = decode8<FMT>(rvb, bb, d0 % 32);
-      // wide heads decode two chunks at a time: hoisting every raw read of the
-      // tile ahead of its use would hold 8 registers per chunk (they spill)
-      if (D >= 256 && i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    for (int kh = 0; kh < 2; ++kh) {
+      S[kh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        uint32_t n[WIN], dec[16];
+        normalise<WIN>(rk[kh][i], sh, n);
+        decode_block<FMT>(n, dec);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          S[kh] = mfma16(__builtin_bit_cast(f16x8, u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]}),
+                         qf[4 * i + c], S[kh]);
+      }
     }
-    // one wave: its own LDS writes are visible to its later LDS reads
+    if (more) load(kb, kst, j + NW, rk);  // in flight while V is decoded and multiplied
+    // V: decoded into the wave's f16 tile (row = key, the lane's blocks)
     lds_order();
-    f32x16 S;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) S = mfma16(row_frag<CPR>(kt, lq, s, lh), qf[s], S);
-    // S^T element i: key j*BN + lh*4 + 8*(i/4) + i%4 of this lane's row
+      for (int i = 0; i < BPL; ++i) {
+        uint32_t n[WIN], dec[16];
+        normalise<WIN>(rv[kh][i], sh, n);
+        decode_block<FMT>(n, dec);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<u32x4*>(vt + chunk_at<CPR>(kh * 16 + ql, 4 * (i * 4 + lg) + c)) =
+              u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]};
+      }
+    if (more) load(vb, vst, j + NW, rv);
+    // scores of this lane: query ql, keys j*BN + 16 kh + 4 lg + e
     const int key0 = j * BN;
     if (key0 + BN - 1 > row_lim) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (key0 + lh * 4 + 8 * (i >> 2) + (i & 3) > row_lim) S[i] = -INFINITY;
-    }
-    float mx = -INFINITY;
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+        for (int e = 0; e < 4; ++e)
+          if (key0 + 16 * kh + 4 * lg + e > row_lim) S[kh][e] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
     // the running max moves only when a score exceeds it by more than 2^8
     // (P <= 256 in f16 meanwhile), so the rescale of O is rare
-    const float mnew = fmaxf(m_run, halves_max(mx));
+    const float mnew = fmaxf(m_run, groups_max(mx));
     const bool grow = (mnew - m_run) * p.c > 8.f;  // false when both are -inf
     if (__any(grow)) {
       const float alpha = grow ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c)) : 1.f;
       if (grow) m_run = mnew;
       l_run *= alpha;
-      if constexpr (DT >= 8) {
-        // wide heads: the accumulator fills the AGPRs; scale each value in
-        // place (read, multiply, write back) so that no copy of it is held in
-        // VGPRs. The wait covers the last MFMA that wrote an accumulator.
-        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float tmp;
-            asm volatile("v_accvgpr_read_b32 %1, %0\n\ts_nop 1\n\tv_mul_f32 %1, %1, %2\n\ts_nop 1\n\t"
-                         "v_accvgpr_write_b32 %0, %1"
-                         : "+a"(acc[dt][i]), "=&v"(tmp)
-                         : "v"(alpha));
-          }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-      }
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
-    float P[16], rs = 0.f;
+    float P[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      P[i] = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -mc));
-      rs += P[i];
-    }
-    l_run += rs;
-    const f16x8 pb0 = __builtin_bit_cast(
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) P[4 * kh + e] = __builtin_amdgcn_exp2f(fmaf(S[kh][e], p.c, -mc));
+    l_run += ((P[0] + P[1]) + (P[2] + P[3])) + ((P[4] + P[5]) + (P[6] + P[7]));
+    const f16x8 pb = __builtin_bit_cast(
         f16x8, u32x4{pack_h2(P[0], P[1]), pack_h2(P[2], P[3]), pack_h2(P[4], P[5]), pack_h2(P[6], P[7])});
-    const f16x8 pb1 = __builtin_bit_cast(
-        f16x8, u32x4{pack_h2(P[8], P[9]), pack_h2(P[10], P[11]), pack_h2(P[12], P[13]), pack_h2(P[14], P[15])});
+    lds_order();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      acc[dt] = mfma16(tr_frag<CPR>(vt, 0, dt * 32, lane), pb0, acc[dt]);
-      acc[dt] = mfma16(tr_frag<CPR>(vt, 16, dt * 32, lane), pb1, acc[dt]);
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16(v_frag<CPR>(vt, dt * 16, lane), pb, acc[dt]);
+  }
+
+  // merge the waves: lane holds query ql, columns dt*16 + 4 lg .. +3
+  const float l_w = groups_sum(l_run);
+  float M = m_run, L = l_w;
+  constexpr int DW = DT / NW;  // output tiles each wave finishes
+  f32x4 o[DW];
+  if constexpr (NW == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = acc[dt];
+  } else {
+    f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][DT][64]
+    __syncthreads();  // every wave is done with its V tile
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) part[(w * DT + dt) * 64 + lane] = acc[dt];
+    if (lg == 0) {
+      ml_all[w][ql][0] = m_run;
+      ml_all[w][ql][1] = l_w;
+    }
+    __syncthreads();
+    M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) M = fmaxf(M, ml_all[u][ql][0]);
+    float fac[NW];
+    L = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const float mu = ml_all[u][ql][0];
+      fac[u] = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mu - M) * p.c);
+      L += fac[u] * ml_all[u][ql][1];
+    }
+#pragma unroll
+    for (int x = 0; x < DW; ++x) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NW; ++u) s += fac[u] * part[(u * DT + w * DW + x) * 64 + lane];
+      o[x] = s;
     }
   }
 
-  // epilogue: O^T tiles, lane holds row `f`, columns dt*32 + 8*g4 + 4*lh .. +3
-  const float lt = halves_sum(l_run);
-  const float ms = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
+  const float ms = (M == -INFINITY) ? -INFINITY : M * p.scale;
   if (!valid) return;
   const int64_t l_off = ((int64_t)b * p.H + h) * p.Tq + t;
+  const int dt0 = (NW == 1) ? 0 : w * DW;
   if (p.n_splits > 1) {
-    const float pinv = lt > 0.f ? 1.f / lt : 0.f;
+    const float pinv = L > 0.f ? 1.f / L : 0.f;
     const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
     float* po = p.part_o + prow * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = dt * 32 + g4 * 8 + lh * 4;
-        *reinterpret_cast<f32x4*>(po + d) = f32x4{acc[dt][g4 * 4] * pinv, acc[dt][g4 * 4 + 1] * pinv,
-                                                  acc[dt][g4 * 4 + 2] * pinv, acc[dt][g4 * 4 + 3] * pinv};
-      }
-    if (lh == 0) p.part_lse[prow] = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
+    for (int x = 0; x < DW; ++x) *reinterpret_cast<f32x4*>(po + (dt0 + x) * 16 + 4 * lg) = o[x] * pinv;
+    if (lg == 0 && w == 0) p.part_lse[prow] = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
     return;
   }
   float inv, lse;
   if (p.sinks != nullptr) {
     const float sk = p.sinks[h];
-    const float M = fmaxf(ms, sk);
-    if (M == -INFINITY) {
+    const float Mx = fmaxf(ms, sk);
+    if (Mx == -INFINITY) {
       inv = 0.f;
       lse = -INFINITY;
     } else {
-      const float fac = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - M) * kLog2e);
-      const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - M) * kLog2e);
-      const float den = lt * fac + es;
-      inv = den > 0.f ? fac / den : 0.f;
-      lse = den > 0.f ? M + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+      const float fa = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - Mx) * kLog2e);
+      const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - Mx) * kLog2e);
+      const float den = L * fa + es;
+      inv = den > 0.f ? fa / den : 0.f;
+      lse = den > 0.f ? Mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
     }
   } else {
-    inv = lt > 0.f ? 1.f / lt : 0.f;
-    lse = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
+    inv = L > 0.f ? 1.f / L : 0.f;
+    lse = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
   }
   uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = dt * 32 + g4 * 8 + lh * 4;
-      *reinterpret_cast<u32x2*>(ob + d) = u32x2{pack_bf2(acc[dt][g4 * 4] * inv, acc[dt][g4 * 4 + 1] * inv),
-                                                pack_bf2(acc[dt][g4 * 4 + 2] * inv, acc[dt][g4 * 4 + 3] * inv)};
-    }
-  if (lh == 0) p.lse[l_off] = lse;
+  for (int x = 0; x < DW; ++x)
+    *reinterpret_cast<u32x2*>(ob + (dt0 + x) * 16 + 4 * lg) =
+        u32x2{pack_bf2(o[x][0] * inv, o[x][1] * inv), pack_bf2(o[x][2] * inv, o[x][3] * inv)};
+  if (lg == 0 && w == 0) p.lse[l_off] = lse;
 }
+
+constexpr int kWaves = 4;
 
 template <int FMT, int D>
 int launch_cfg(const QkvParams& p, void* stream) {
-  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
-                     dim3(64), 0, reinterpret_cast<hipStream_t>(stream), p);
+  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, kWaves>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
+                     dim3(64 * kWaves), 0, reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
 template <int FMT, int D>
 int occ_cfg() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D>), 64,
-                                                   0) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, kWaves>), 64 * kWaves, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }

@@ -115,3 +115,31 @@ def test_qkv_full_workload_sampled():
     gl = np.array([float(lse[b, h, t]) for b, h, t in rows])
     eo, el = _o_err(go, ro), _lse_err(gl, rl)
     assert eo <= TOL_O and el <= TOL_LSE, f"max|dO|={eo:.3e} max|dlse|={el:.3e}"
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("layout", ["padded_rows", "token_major"])
+def test_qkv_strided_cache(fmt, layout):
+    """Caches that are not [B, Hkv, Tk, row] back to back: rows padded by 12
+    bytes, and the token-major [B, Tk, Hkv, row] layout viewed as [B, Hkv, Tk, row]."""
+    B, H, Hkv, Tq, Tk, d = 2, 8, 2, 3, 333, 128
+    announce(f"qkv strided {fmt} {layout}")
+    inp = synth.make_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, seed=17, sinks=True)
+    rb = inp["k"].shape[-1]
+
+    def restride(x):
+        if layout == "padded_rows":
+            buf = torch.zeros((B, Hkv, Tk, rb + 12), dtype=torch.uint8)
+            buf[..., :rb] = x
+            return buf.cuda()[..., :rb]
+        return x.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+
+    k, v = restride(inp["k"]), restride(inp["v"])
+    assert not k.is_contiguous()
+    out = torch.full((B, H, Tq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    A.dense_qkv(inp["q"].cuda(), k, v, fmt=fmt, causal=True, sinks=inp["sinks"].cuda(), out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = reference(inp, causal=True, scale=1 / math.sqrt(d))
+    eo, el = _o_err(_np(out), ro), _lse_err(_np(lse), rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"{fmt} {layout}: max|dO|={eo:.3e} max|dlse|={el:.3e}"
