@@ -1678,17 +1678,6 @@ int launch_dma(const KernelParams& p, void* stream) {
 // "Flowchart", done across workgroups of one device). Memory bound: it reads
 // n_splits * d_v floats per row once.
 // ===========================================================================
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) {
   const int lane = threadIdx.x & 63;
   const int64_t R = (int64_t)m.B * m.H * m.Tq;
@@ -1697,39 +1686,85 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) 
   const int t = (int)(row % m.Tq);
   const int h = (int)((row / m.Tq) % m.H);
   const int b = (int)(row / ((int64_t)m.Tq * m.H));
-  float mx = -INFINITY;
-  for (int i = lane; i < m.n_splits; i += 64) mx = fmaxf(mx, m.part_lse[i * R + row]);
-  mx = wave_max(mx);
+  const int n = m.n_splits, nc = m.d_v / 4;
   const float sk = m.sinks != nullptr ? m.sinks[h] : -INFINITY;
-  mx = fmaxf(mx, sk);
-  float den = 0.f;
-  if (mx != -INFINITY) {
-    for (int i = lane; i < m.n_splits; i += 64) {
-      const float li = m.part_lse[i * R + row];
-      den += li == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((li - mx) * kLog2e);
-    }
-    den = wave_sum(den);
-    if (sk != -INFINITY) den += __builtin_amdgcn_exp2f((sk - mx) * kLog2e);
-  }
-  const float lse = (den > 0.f) ? mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
   const int64_t obase = (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)t * m.o_st;
-  for (int c = lane; c < m.d_v / 4; c += 64) {
+  // The wave's lanes split into G groups of C lanes: lane (c, s) takes 4-float
+  // chunk c of ranges s, s + G, s + 2G, ..., U of them per batch, loading each
+  // range's partial and its lse together (one memory round trip per batch).
+  // C is the smallest of 16, 32, 64 that holds the row's d_v / 4 chunks; wider
+  // rows take several passes. Sums run relative to the running maximum M of
+  // the lse_i seen so far; the groups add up across lanes at the end.
+  constexpr int U = 16;
+  const int C = nc <= 16 ? 16 : (nc <= 32 ? 32 : 64), G = 64 / C;
+  const int s = lane / C;
+  for (int c0 = 0; c0 < nc; c0 += C) {
+    const int c = c0 + lane % C;
+    const bool on = c < nc;
+    const float* po = m.part_o + row * m.d_v + 4 * (on ? c : nc - 1);
+    float M = -INFINITY, den = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < m.n_splits; ++i) {
-      const float li = m.part_lse[i * R + row];
-      if (li == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f((li - lse) * kLog2e);
-      const f32x4 oi = *reinterpret_cast<const f32x4*>(m.part_o + (i * R + row) * m.d_v + 4 * c);
-      o += w * oi;
+    for (int i0 = 0; i0 < n; i0 += U * G) {
+      float li[U];
+      f32x4 oi[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + s + u * G;
+        if (i < n) {
+          li[u] = m.part_lse[i * R + row];
+          oi[u] = *reinterpret_cast<const f32x4*>(po + i * R * m.d_v);
+        } else {
+          li[u] = -INFINITY;
+          oi[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float bm = li[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, li[u]);
+      for (int x = C; x < 64; x <<= 1) bm = fmaxf(bm, __shfl_xor(bm, x, 64));
+      const float Mn = fmaxf(M, bm);
+      if (Mn == -INFINITY) continue;  // no range with keys yet
+      const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+      den *= a;
+      o *= a;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // an empty range (lse_i = -inf) adds nothing, whatever its partial holds
+        const bool empty = li[u] == -INFINITY;
+        const float w = empty ? 0.f : __builtin_amdgcn_exp2f((li[u] - Mn) * kLog2e);
+        den += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += empty ? 0.f : w * oi[u][e];
+      }
+      M = Mn;
     }
-    if (m.f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(m.out) + obase + 4 * c) = o;
-    } else {
-      *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(m.out) + obase + 4 * c) =
-          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    for (int x = C; x < 64; x <<= 1) {
+      den += __shfl_xor(den, x, 64);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], x, 64);
     }
+    // the sink joins the denominator
+    const float Mx = fmaxf(M, sk);
+    float lse = -INFINITY, f = 0.f;
+    if (Mx != -INFINITY) {
+      const float fa = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((M - Mx) * kLog2e);
+      const float dt = den * fa + ((sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - Mx) * kLog2e));
+      if (dt > 0.f) {
+        lse = Mx + __builtin_amdgcn_logf(dt) * kLn2;
+        f = fa / dt;
+      }
+    }
+    o *= f;
+    if (on && s == 0) {
+      if (m.f32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(m.out) + obase + 4 * c) = o;
+      } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(m.out) + obase + 4 * c) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    }
+    if (c0 == 0 && lane == 0) m.lse[row] = lse;
   }
-  if (lane == 0) m.lse[row] = lse;
 }
 
 #define DMA_ENTRY_ROPE(NAME, DQK, DV, ROPE, DS, NW, BN, NBUF, PP)                                                  \

@@ -188,7 +188,7 @@ __device__ __forceinline__ void normalise(const uint32_t (&r)[WIN], uint32_t sh,
 }
 
 template <int FMT, int D, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 2)))
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW < 4 ? 1 : NW / 4)))
 qkv_decode_kernel(const QkvParams p) {
   constexpr int BN = 32;                   // keys per tile
   constexpr int BB = Blk<FMT>::BB, WIN = Blk<FMT>::WIN;
@@ -197,7 +197,7 @@ qkv_decode_kernel(const QkvParams p) {
   constexpr int KS = D / 32;               // S MFMA steps
   constexpr int DT = D / 16;               // 16-column output tiles
   constexpr int CPR = D / 8;
-  static_assert(NBK % 4 == 0 && DT % NW == 0, "shapes");
+  static_assert(NBK % 4 == 0 && NW <= 16, "shapes");
   // one f16 V tile per wave; after the key loop the same bytes hold the
   // waves' partial outputs (NW x DT x 64 lanes x 16 bytes, the same size)
   __shared__ __attribute__((aligned(16))) f16_t vt_all[NW * BN * D];
@@ -353,16 +353,14 @@ qkv_decode_kernel(const QkvParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16(v_frag<CPR>(vt, dt * 16, lane), pb, acc[dt]);
   }
 
-  // merge the waves: lane holds query ql, columns dt*16 + 4 lg .. +3
+  // merge the waves: lane holds query ql, columns dt*16 + 4 lg .. +3; wave w
+  // finishes the output tiles dt = w, w + NW, ...
   const float l_w = groups_sum(l_run);
   float M = m_run, L = l_w;
-  constexpr int DW = DT / NW;  // output tiles each wave finishes
-  f32x4 o[DW];
-  if constexpr (NW == 1) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = acc[dt];
-  } else {
-    f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][DT][64]
+  constexpr int DW = (DT + NW - 1) / NW;
+  float fac[NW];
+  f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][DT][64]
+  if constexpr (NW > 1) {
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) part[(w * DT + dt) * 64 + lane] = acc[dt];
@@ -374,7 +372,6 @@ qkv_decode_kernel(const QkvParams p) {
     M = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NW; ++u) M = fmaxf(M, ml_all[u][ql][0]);
-    float fac[NW];
     L = 0.f;
 #pragma unroll
     for (int u = 0; u < NW; ++u) {
@@ -382,25 +379,31 @@ qkv_decode_kernel(const QkvParams p) {
       fac[u] = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mu - M) * p.c);
       L += fac[u] * ml_all[u][ql][1];
     }
-#pragma unroll
-    for (int x = 0; x < DW; ++x) {
+  }
+  // the x-th output tile of this wave, unnormalised
+  auto tile_sum = [&](int x) -> f32x4 {
+    if constexpr (NW == 1) {
+      return acc[x];
+    } else {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NW; ++u) s += fac[u] * part[(u * DT + w * DW + x) * 64 + lane];
-      o[x] = s;
+      for (int u = 0; u < NW; ++u) s += fac[u] * part[(u * DT + w + x * NW) * 64 + lane];
+      return s;
     }
-  }
+  };
 
   const float ms = (M == -INFINITY) ? -INFINITY : M * p.scale;
   if (!valid) return;
   const int64_t l_off = ((int64_t)b * p.H + h) * p.Tq + t;
-  const int dt0 = (NW == 1) ? 0 : w * DW;
   if (p.n_splits > 1) {
     const float pinv = L > 0.f ? 1.f / L : 0.f;
     const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
     float* po = p.part_o + prow * D;
 #pragma unroll
-    for (int x = 0; x < DW; ++x) *reinterpret_cast<f32x4*>(po + (dt0 + x) * 16 + 4 * lg) = o[x] * pinv;
+    for (int x = 0; x < DW; ++x) {
+      if (NW > 1 && w + x * NW >= DT) break;
+      *reinterpret_cast<f32x4*>(po + (w + x * NW) * 16 + 4 * lg) = tile_sum(x) * pinv;
+    }
     if (lg == 0 && w == 0) p.part_lse[prow] = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
     return;
   }
@@ -424,18 +427,27 @@ qkv_decode_kernel(const QkvParams p) {
   }
   uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st;
 #pragma unroll
-  for (int x = 0; x < DW; ++x)
-    *reinterpret_cast<u32x2*>(ob + (dt0 + x) * 16 + 4 * lg) =
-        u32x2{pack_bf2(o[x][0] * inv, o[x][1] * inv), pack_bf2(o[x][2] * inv, o[x][3] * inv)};
+  for (int x = 0; x < DW; ++x) {
+    if (NW > 1 && w + x * NW >= DT) break;
+    const f32x4 o = tile_sum(x);
+    *reinterpret_cast<u32x2*>(ob + (w + x * NW) * 16 + 4 * lg) =
+        u32x2{pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv)};
+  }
   if (lg == 0 && w == 0) p.lse[l_off] = lse;
 }
 
-constexpr int kWaves = 4;
+// waves per workgroup: every wave a CU can hold (three or four per SIMD at
+// d 128, two at d 256), so one workgroup per CU covers the longest key range
+template <int FMT, int D>
+constexpr int waves_of() {
+  return D == 128 ? (FMT == kFmtQ8 ? 12 : 16) : 8;
+}
 
 template <int FMT, int D>
 int launch_cfg(const QkvParams& p, void* stream) {
-  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, kWaves>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
-                     dim3(64 * kWaves), 0, reinterpret_cast<hipStream_t>(stream), p);
+  constexpr int NW = waves_of<FMT, D>();
+  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, NW>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
+                     dim3(64 * NW), 0, reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
@@ -443,7 +455,8 @@ template <int FMT, int D>
 int occ_cfg() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, kWaves>), 64 * kWaves, 0) != hipSuccess) {
+          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, waves_of<FMT, D>()>), 64 * waves_of<FMT, D>(),
+          0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }

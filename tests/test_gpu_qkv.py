@@ -45,6 +45,7 @@ CASES = [
     (1, 4, 4, 7, 65, False, False, 1),        # one range: direct output
     (1, 2, 1, 40, 30, True, False, 0),        # Tq > Tk: rows that see no key
     (3, 4, 2, 3, 33, True, True, 100),        # more ranges asked than key blocks
+    (1, 8, 2, 1, 6000, True, True, 70),       # many ranges: several merge batches
 ]
 
 

@@ -40,6 +40,8 @@ CASES = [
     (2, 4, 4, 5, 777, 64, 64, False, True, 7),        # non-causal, ragged last range
     (1, 8, 2, 40, 30, 128, 128, True, True, 2),       # Tq > Tk: rows that see no key
     (1, 8, 2, 3, 900, 256, 256, True, False, 4),      # d256 (one-group kernel)
+    (1, 4, 1, 1, 20000, 64, 64, True, True, 150),     # many ranges: several merge batches per lane
+    (1, 8, 1, 2, 12000, 512, 512, True, False, 40),   # wide rows: two merge passes, three batches
 ]
 
 
