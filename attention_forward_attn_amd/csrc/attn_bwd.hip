@@ -58,6 +58,7 @@ namespace {
 typedef __bf16 bf16_t;
 typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -998,33 +999,53 @@ fwd_dropout_kernel(const BwdParams p) {
 //    (only the gathered rows are ever converted, never the pool). One
 //    workgroup of 8 waves per (query, range of its slots); per step of 32
 //    slots the rows' codes and scales arrive by DMA into one of four staging
-//    buffers (three steps ahead, explicit vmcnt accounting) and the codes are
-//    decoded to a bf16 tile (exactly: an E4M3 value has 4 significant bits).
-//    Wave (hg, sq) forms S^T for heads 32 hg.. over columns 128 sq.., which
-//    is exactly one scale block, so it multiplies its partial by each key's
-//    scale of that block in fp32; the four partials are summed through LDS in
-//    a fixed order; the online softmax is per head; O^T += X^T (P s)^T on the
-//    wave's 128 output columns, the same block's scales applied to P before it
-//    is rounded for the product. No decoded value is ever rounded. Each range writes
-//    its normalised O and its lse without the sink; the split-KV merge adds
-//    the sink and combines the ranges.
+//    buffers (three steps ahead, explicit vmcnt accounting). The MFMA operands
+//    come straight from the staged codes: a lane converts the 8 codes of its
+//    operand to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, an E4M3
+//    value has 4 significant bits), row-wise for S^T and through the 8-bit
+//    transposed LDS read (lane i of a 16-lane group gets byte i of 8
+//    consecutive 16-byte rows) for X^T. Wave (hg, sq) forms S^T for heads
+//    32 hg.. over columns 128 sq.., which is exactly one scale block, so it
+//    multiplies its partial by each key's scale of that block in fp32; the
+//    four partials are summed through LDS in a fixed order; the online softmax
+//    is per head; O^T += X^T (P s)^T on the wave's 128 output columns, the
+//    same block's scales applied to P before it is rounded for the product.
+//    No decoded value is ever rounded. Each range writes its normalised O and
+//    its lse without the sink; the split-KV merge adds the sink and combines
+//    the ranges.
+//
+//    Staged row r keeps its 16-byte chunk c at position c ^ (r % 16) (the DMA
+//    lanes fetch the chunks in that order), so the 32 rows a read touches
+//    fall in distinct bank groups. S^T's MFMA row m reads staged row pi(m)
+//    (bits 2 and 3 of m swapped): then the 8 scores a lane hands to each
+//    X^T P^T product belong to 8 consecutive staged rows, the rows one
+//    transposed read returns.
 // ---------------------------------------------------------------------------
 constexpr int kFp8Stages = 4, kFp8IdxCap = 4096;
 
+// 8 E4M3 codes (two words) -> 8 bf16, exactly
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// staged row of S^T's MFMA row m: bits 2 and 3 swapped
+__device__ __forceinline__ int fp8_row_of(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
 __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
-  constexpr int D = 512, BN = 32, CPX = D / 8;
+  constexpr int D = 512, BN = 32;
   constexpr int STG = BN * D;               // codes of one step
   constexpr int SCB = BN * 16;              // scales of one step (4 per row)
-  constexpr int X_BYTES = BN * D * 2;       // the decoded bf16 tile
   constexpr int XB_BYTES = 8 * 16 * 64 * 4; // partial S^T exchange
   constexpr int NS = kFp8Stages, PD = NS - 1;
-  __shared__ __attribute__((aligned(1024))) unsigned char
-      smem[NS * STG + NS * SCB + X_BYTES + XB_BYTES + kFp8IdxCap * 4];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STG + NS * SCB + XB_BYTES + kFp8IdxCap * 4];
   unsigned char* const stg = smem;
   float* const scl = reinterpret_cast<float*>(smem + NS * STG);
-  bf16_t* const xt = reinterpret_cast<bf16_t*>(smem + NS * STG + NS * SCB);
-  float* const xb = reinterpret_cast<float*>(smem + NS * STG + NS * SCB + X_BYTES);
-  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + NS * STG + NS * SCB + X_BYTES + XB_BYTES);
+  float* const xb = reinterpret_cast<float*>(smem + NS * STG + NS * SCB);
+  int32_t* const sidx = reinterpret_cast<int32_t*>(smem + NS * STG + NS * SCB + XB_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1053,8 +1074,9 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
   __syncthreads();
 
   // step j: wave w gathers rows 4w .. 4w+3 (two rows of 512 codes per
-  // instruction: lanes 0-31 the first, 32-63 the second); wave 0 also the 32
-  // rows' scales (16 bytes each, lanes 0-31). Skipped slots read row 0.
+  // instruction: lanes 0-31 the first, 32-63 the second; lane lq fetches
+  // chunk lq ^ (row % 16)); wave 0 also the 32 rows' scales (16 bytes each,
+  // lanes 0-31). Skipped slots read row 0.
   const uint32_t stg_s = lds_u32(stg), scl_s = lds_u32(scl);
   auto issue = [&](int j) {
     const uint32_t buf = (uint32_t)(j % NS);
@@ -1065,11 +1087,17 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
       const int r0 = wave * 4 + 2 * m;
       const int ra = __builtin_amdgcn_readlane(myrow, r0), rb = __builtin_amdgcn_readlane(myrow, r0 + 1);
       const int rowl = lh ? rb : ra;
-      dma16(p.codes, (uint32_t)rowl * (uint32_t)p.c_sn + 16u * (uint32_t)lq, stg_s + buf * STG + 512u * r0);
+      const uint32_t chunk = (uint32_t)(lq ^ ((r0 + lh) & 15));
+      dma16(p.codes, (uint32_t)rowl * (uint32_t)p.c_sn + 16u * chunk, stg_s + buf * STG + 512u * r0);
     }
     if (wave == 0 && lane < BN) dma16(p.scales, 4u * (uint32_t)myrow * (uint32_t)p.s_sn, scl_s + buf * SCB);
   };
   const int per_step = wave == 0 ? 3 : 2;  // this wave's loads of one step
+
+  // this lane's staged row for S^T, and its rows / column chunk for X^T
+  const int srow = fp8_row_of(lq);
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int trow = 8 * (g16 >> 1) + (j16 >> 1);  // + 16 ks
 
   f32x16 acc[4];
 #pragma unroll
@@ -1084,34 +1112,25 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
     wait_vmcnt_dyn(per_step * min(PD - 1, nblk - 1 - j));
     barrier();
     if (j + PD < nblk) issue(j + PD);
-    // decode step j: thread t takes row t/16, chunks t%16 + 16 i (i = scale block)
-    {
-      const uint32_t buf = (uint32_t)(j % NS);
-      const int row = tid >> 4, c0 = tid & 15;
-      const unsigned char* src = stg + buf * STG + row * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = c0 + 16 * i;
-        const u32x2 w = *reinterpret_cast<const u32x2*>(src + 8 * c);
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
-        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false), d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
-        *reinterpret_cast<u32x4*>(xt + chunk_at<CPX>(row, c)) =
-            u32x4{pack2(a[0], a[1]), pack2(b[0], b[1]), pack2(c2[0], c2[1]), pack2(d2[0], d2[1])};
-      }
-    }
-    barrier();
-    // partial S^T over columns 128 sq .. 128 sq + 127
+    const unsigned char* st = stg + (j % NS) * STG;
+    // partial S^T over columns 128 sq .. 128 sq + 127 (chunks 8 sq + k)
     f32x16 S;
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    {
+      const unsigned char* rp = st + srow * D + 8 * lh;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) S = mfma32(row_frag<CPX>(xt, lq, sq * 8 + k, lh), qf[k], S);
-    // the scales of this lane's 16 keys for block sq (the wave's columns)
+      for (int k = 0; k < 8; ++k) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(rp + (((8 * sq + k) ^ (srow & 15)) << 4));
+        S = mfma32(fp8x8_to_bf16(w[0], w[1]), qf[k], S);
+      }
+    }
+    // S^T element i: MFMA row lh*4 + 8*(i/4) + i%4, staged row 16*(i/8) + 8*lh + i%8
     float ks[16];
     {
       const float* sc = scl + (j % NS) * (SCB / 4) + sq;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ks[i] = sc[4 * (lh * 4 + 8 * (i >> 2) + (i & 3))];
+      for (int i = 0; i < 16; ++i) ks[i] = sc[4 * (16 * (i >> 3) + 8 * lh + (i & 7))];
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] *= ks[i];
@@ -1129,12 +1148,11 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[g4 * 4 + e] = t4[e];
     }
-    // S^T element i: slot j*32 + lh*4 + 8*(i/4) + i%4 of this lane's head
     const uint32_t skip = (uint32_t)__ballot(sidx[j * BN + lq] < 0);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if ((skip >> (lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) S[i] = -INFINITY;
+      if ((skip >> (16 * (i >> 3) + 8 * lh + (i & 7))) & 1u) S[i] = -INFINITY;
       mx = fmaxf(mx, S[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -1154,11 +1172,19 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
       l_run += e;
       pr[i] = e * ks[i];  // the values of these columns are code * scale
     }
+    // X^T for output columns 128 sq + 32 t + (lane % 32), staged rows 16 ks + 8 lh + 0..7
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = pack8(pr + ks * 8);
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pb = pack8(pr + kk * 8);
+      const int row = 16 * kk + trow;
+      const unsigned char* rp = st + row * D + 8 * (j16 & 1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = mfma32(tr_frag<CPX>(xt, ks * 16, sq * 128 + t * 32, lane), pb, acc[t]);
+      for (int t = 0; t < 4; ++t) {
+        const int chunk = 8 * sq + 2 * t + (g16 & 1);
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(rp + ((chunk ^ (row & 15)) << 4)));
+        acc[t] = mfma32(fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]), pb, acc[t]);
+      }
     }
   }
 
