@@ -789,13 +789,15 @@ static attn_status validate_fp8_shape(const attn_sparse_fp8_args* a) {
   return ATTN_OK;
 }
 
-// ranges of whole 32-slot steps: enough workgroups for two per CU, at most
-// 4096 slots (the kernel's index buffer) per range
+// ranges of whole 32-slot steps: enough workgroups for one per CU (a
+// workgroup takes 146 KiB of LDS; measured at 128 queries: two ranges 103 us,
+// four 116 us, three 130 us), at most 4096 slots (the kernel's index buffer)
+// per range
 static Fp8Plan plan_fp8(const attn_sparse_fp8_args* a, int n_req) {
   Fp8Plan pl;
   const int steps = std::max(1, (a->topk + 31) / 32);
   int n = n_req;
-  if (n <= 0) n = std::max(1, (512 + std::max(a->Sq, 1) - 1) / std::max(a->Sq, 1));
+  if (n <= 0) n = std::max(1, (device_cus() + std::max(a->Sq, 1) - 1) / std::max(a->Sq, 1));
   n = std::max(n, (a->topk + 4095) / 4096);
   n = std::min(n, steps);
   const int per = (steps + n - 1) / n;
