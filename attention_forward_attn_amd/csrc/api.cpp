@@ -50,8 +50,9 @@ constexpr const char* kBwdPaths[] = {"dense_bwd_bf16_d64", "dense_bwd_bf16_d128"
 constexpr int kBwdSlot0 = kMergeSlot - 3;
 // and the quantized-cache decode paths below those
 constexpr const char* kQkvPaths[] = {"dense_qkv_q8_0_d128", "dense_qkv_q4_0_d128", "dense_qkv_q8_0_d256",
-                                     "dense_qkv_q4_0_d256"};
-constexpr int kQkvSlot0 = kBwdSlot0 - 4;
+                                     "dense_qkv_q4_0_d256", "dense_qkv_q8_0_d512", "dense_qkv_q4_0_d512"};
+constexpr int kQkvPathCount = 6;
+constexpr int kQkvSlot0 = kBwdSlot0 - kQkvPathCount;
 // and the sparse backward below those
 constexpr const char* kSpBwdPath = "sparse_bwd_bf16_d512";
 constexpr int kSpBwdSlot = kQkvSlot0 - 1;
@@ -68,7 +69,7 @@ int path_index(const char* path) {
   if (std::strcmp(path, kExtrasPath) == 0) return kExtrasSlot;
   if (std::strcmp(path, kDropPath) == 0) return kDropPathSlot;
   if (std::strcmp(path, kFp8Path) == 0) return kFp8Slot;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kQkvPathCount; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
   for (int i = 0; i < 3; ++i)
     if (std::strcmp(path, kBwdPaths[i]) == 0) return kBwdSlot0 + i;
@@ -952,11 +953,11 @@ attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace,
 // ---------------------------------------------------------------- quantized K/V decode
 namespace {
 
-// index into kQkvPaths: (q8_0, q4_0) x (d 128, d 256)
+// index into kQkvPaths: (q8_0, q4_0) x (d 128, d 256, d 512)
 static int qkv_path(int fmt, int d) {
   const int f = fmt == ATTN_KV_Q8_0 ? 0 : (fmt == ATTN_KV_Q4_0 ? 1 : -1);
-  if (f < 0 || (d != 128 && d != 256)) return -1;
-  return f + (d == 256 ? 2 : 0);
+  if (f < 0 || (d != 128 && d != 256 && d != 512)) return -1;
+  return f + (d == 256 ? 2 : (d == 512 ? 4 : 0));
 }
 
 static attn_status validate_qkv_shape(const attn_qkv_args* a) {

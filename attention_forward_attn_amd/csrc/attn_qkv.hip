@@ -187,25 +187,37 @@ __device__ __forceinline__ void normalise(const uint32_t (&r)[WIN], uint32_t sh,
   for (int x = 0; x < WIN; ++x) n[x] = __builtin_amdgcn_alignbyte(r[x + 1 < WIN ? x + 1 : x], r[x], sh);
 }
 
-template <int FMT, int D, int NW>
+// CS = 1: every wave covers all D columns. CS = 2 (512-wide heads, whose
+// accumulator, q and raw blocks do not fit one wave): waves come in pairs on
+// the same tiles, wave c of a pair takes columns c D/2 .. (c+1) D/2 - 1 for
+// both its partial S^T and its output; the pair adds its two partial scores
+// through LDS (double-buffered, one workgroup barrier per tile, both waves
+// summing in the same order, so they hold identical scores and run identical
+// softmax state).
+template <int FMT, int D, int NW, int CS>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW < 4 ? 1 : NW / 4)))
 qkv_decode_kernel(const QkvParams p) {
   constexpr int BN = 32;                   // keys per tile
   constexpr int BB = Blk<FMT>::BB, WIN = Blk<FMT>::WIN;
-  constexpr int NBK = D / 32;              // blocks per row
+  constexpr int DC = D / CS;               // columns of one wave
+  constexpr int NBK = DC / 32;             // blocks per row in those columns
   constexpr int BPL = NBK / 4;             // blocks per key a lane decodes
-  constexpr int KS = D / 32;               // S MFMA steps
-  constexpr int DT = D / 16;               // 16-column output tiles
-  constexpr int CPR = D / 8;
-  static_assert(NBK % 4 == 0 && NW <= 16, "shapes");
+  constexpr int KS = DC / 32;              // S MFMA steps
+  constexpr int DT = DC / 16;              // 16-column output tiles
+  constexpr int CPR = DC / 8;
+  constexpr int NP = NW / CS;              // waves (CS = 1) or pairs (CS = 2) taking tiles in turn
+  static_assert(NBK % 4 == 0 && NW <= 16 && NW % CS == 0 && (CS == 1 || CS == 2), "shapes");
   // one f16 V tile per wave; after the key loop the same bytes hold the
   // waves' partial outputs (NW x DT x 64 lanes x 16 bytes, the same size)
-  __shared__ __attribute__((aligned(16))) f16_t vt_all[NW * BN * D];
+  __shared__ __attribute__((aligned(16))) f16_t vt_all[NW * BN * DC];
   __shared__ float ml_all[NW][16][2];
+  // partial scores of the pairs (CS = 2): [tile parity][wave][lane] x 8 floats
+  __shared__ __attribute__((aligned(16))) f32x4 xs_all[CS == 2 ? 2 * NW * 64 * 2 : 1];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ql = lane & 15, lg = lane >> 4;
-  f16_t* vt = vt_all + w * (BN * D);
+  const int pr = w / CS, cs = w % CS;      // pair (or wave) and its column half
+  f16_t* vt = vt_all + w * (BN * DC);
   const int grp = blockIdx.x / p.n_rt, rt = blockIdx.x % p.n_rt;
   const int b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int rows = p.g * p.Tq;
@@ -233,10 +245,11 @@ qkv_decode_kernel(const QkvParams p) {
   const int nb = (kend + BN - 1) / BN;
 
   // q row of this lane as f16, in the permuted contraction order: step s
-  // takes values 32 * (4 (s / 4) + lane/16) + 8 (s % 4) .. + 7
+  // takes values DC cs + 32 (4 (s / 4) + lane/16) + 8 (s % 4) .. + 7
   f16x8 qf[KS];
   {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st;
+    const uint16_t* qp =
+        reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st + DC * cs;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int d0 = 32 * ((s / 4) * 4 + lg) + 8 * (s % 4);
@@ -255,7 +268,7 @@ qkv_decode_kernel(const QkvParams p) {
   // window start of the lane's block i within a row
   uint32_t boff[BPL];
 #pragma unroll
-  for (int i = 0; i < BPL; ++i) boff[i] = (uint32_t)((i * 4 + lg) * BB) - sh;
+  for (int i = 0; i < BPL; ++i) boff[i] = (uint32_t)((NBK * cs + i * 4 + lg) * BB) - sh;
 
   // raw windows of tile j: [key half][block][dword]; keys past kend repeat
   // key kend - 1 (their scores are masked). Byte offsets stay below 2^31: the
@@ -279,29 +292,52 @@ qkv_decode_kernel(const QkvParams p) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (w < nb) {
-    load(kb, kst, w, rk);
-    load(vb, vst, w, rv);
+  // With CS = 2 every wave runs the same number of iterations (the pair
+  // barrier is the workgroup's): iterations past nb do no work.
+  const int iters = CS == 1 ? (nb > pr ? (nb - pr + NP - 1) / NP : 0) : (nb + NP - 1) / NP;
+  if (pr < nb) {
+    load(kb, kst, pr, rk);
+    load(vb, vst, pr, rv);
   }
-  for (int j = w; j < nb; j += NW) {
-    const bool more = j + NW < nb;
+  for (int it = 0; it < iters; ++it) {
+    const int j = pr + it * NP;
+    const bool live = j < nb;  // always true with CS = 1
+    const bool more = j + NP < nb;
     // S^T for the tile's two 16-key halves, K decoded straight into the A operand
     f32x4 S[2];
+    S[0] = S[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (live) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      S[kh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        uint32_t n[WIN], dec[16];
-        normalise<WIN>(rk[kh][i], sh, n);
-        decode_block<FMT>(n, dec);
+        for (int i = 0; i < BPL; ++i) {
+          uint32_t n[WIN], dec[16];
+          normalise<WIN>(rk[kh][i], sh, n);
+          decode_block<FMT>(n, dec);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          S[kh] = mfma16(__builtin_bit_cast(f16x8, u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]}),
-                         qf[4 * i + c], S[kh]);
+          for (int c = 0; c < 4; ++c)
+            S[kh] = mfma16(__builtin_bit_cast(f16x8, u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]}),
+                           qf[4 * i + c], S[kh]);
+        }
+      }
+      if (more) load(kb, kst, j + NP, rk);  // in flight while V is decoded and multiplied
+    }
+    if constexpr (CS == 2) {
+      // the pair's scores: own half + partner half, always half 0 first
+      f32x4* xs = xs_all + (it & 1) * (NW * 64 * 2);
+      xs[(w * 64 + lane) * 2] = S[0];
+      xs[(w * 64 + lane) * 2 + 1] = S[1];
+      __syncthreads();
+      const f32x4 o0 = xs[((w ^ 1) * 64 + lane) * 2], o1 = xs[((w ^ 1) * 64 + lane) * 2 + 1];
+      if (cs == 0) {
+        S[0] += o0;
+        S[1] += o1;
+      } else {
+        S[0] = o0 + S[0];
+        S[1] = o1 + S[1];
       }
     }
-    if (more) load(kb, kst, j + NW, rk);  // in flight while V is decoded and multiplied
+    if (!live) continue;
     // V: decoded into the wave's f16 tile (row = key, the lane's blocks)
     lds_order();
 #pragma unroll
@@ -316,7 +352,7 @@ qkv_decode_kernel(const QkvParams p) {
           *reinterpret_cast<u32x4*>(vt + chunk_at<CPR>(kh * 16 + ql, 4 * (i * 4 + lg) + c)) =
               u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]};
       }
-    if (more) load(vb, vst, j + NW, rv);
+    if (more) load(vb, vst, j + NP, rv);
     // scores of this lane: query ql, keys j*BN + 16 kh + 4 lg + e
     const int key0 = j * BN;
     if (key0 + BN - 1 > row_lim) {
@@ -353,14 +389,16 @@ qkv_decode_kernel(const QkvParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16(v_frag<CPR>(vt, dt * 16, lane), pb, acc[dt]);
   }
 
-  // merge the waves: lane holds query ql, columns dt*16 + 4 lg .. +3; wave w
-  // finishes the output tiles dt = w, w + NW, ...
+  // merge the waves (pairs) over the key range: lane holds query ql, columns
+  // DC cs + dt*16 + 4 lg .. +3; wave (pr, cs) finishes the output tiles
+  // dt = pr, pr + NP, ... of its column half. The two waves of a pair hold
+  // the same row state.
   const float l_w = groups_sum(l_run);
   float M = m_run, L = l_w;
-  constexpr int DW = (DT + NW - 1) / NW;
-  float fac[NW];
+  constexpr int DW = (DT + NP - 1) / NP;
+  float fac[NP];
   f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][DT][64]
-  if constexpr (NW > 1) {
+  if constexpr (NP > 1) {
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) part[(w * DT + dt) * 64 + lane] = acc[dt];
@@ -371,23 +409,23 @@ qkv_decode_kernel(const QkvParams p) {
     __syncthreads();
     M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NW; ++u) M = fmaxf(M, ml_all[u][ql][0]);
+    for (int u = 0; u < NP; ++u) M = fmaxf(M, ml_all[u * CS + cs][ql][0]);
     L = 0.f;
 #pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      const float mu = ml_all[u][ql][0];
+    for (int u = 0; u < NP; ++u) {
+      const float mu = ml_all[u * CS + cs][ql][0];
       fac[u] = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mu - M) * p.c);
-      L += fac[u] * ml_all[u][ql][1];
+      L += fac[u] * ml_all[u * CS + cs][ql][1];
     }
   }
   // the x-th output tile of this wave, unnormalised
   auto tile_sum = [&](int x) -> f32x4 {
-    if constexpr (NW == 1) {
+    if constexpr (NP == 1) {
       return acc[x];
     } else {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NW; ++u) s += fac[u] * part[(u * DT + w + x * NW) * 64 + lane];
+      for (int u = 0; u < NP; ++u) s += fac[u] * part[((u * CS + cs) * DT + pr + x * NP) * 64 + lane];
       return s;
     }
   };
@@ -398,11 +436,11 @@ qkv_decode_kernel(const QkvParams p) {
   if (p.n_splits > 1) {
     const float pinv = L > 0.f ? 1.f / L : 0.f;
     const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
-    float* po = p.part_o + prow * D;
+    float* po = p.part_o + prow * D + DC * cs;
 #pragma unroll
     for (int x = 0; x < DW; ++x) {
-      if (NW > 1 && w + x * NW >= DT) break;
-      *reinterpret_cast<f32x4*>(po + (w + x * NW) * 16 + 4 * lg) = tile_sum(x) * pinv;
+      if (NP > 1 && pr + x * NP >= DT) break;
+      *reinterpret_cast<f32x4*>(po + (pr + x * NP) * 16 + 4 * lg) = tile_sum(x) * pinv;
     }
     if (lg == 0 && w == 0) p.part_lse[prow] = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
     return;
@@ -425,12 +463,12 @@ qkv_decode_kernel(const QkvParams p) {
     inv = L > 0.f ? 1.f / L : 0.f;
     lse = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
   }
-  uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st;
+  uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st + DC * cs;
 #pragma unroll
   for (int x = 0; x < DW; ++x) {
-    if (NW > 1 && w + x * NW >= DT) break;
+    if (NP > 1 && pr + x * NP >= DT) break;
     const f32x4 o = tile_sum(x);
-    *reinterpret_cast<u32x2*>(ob + (w + x * NW) * 16 + 4 * lg) =
+    *reinterpret_cast<u32x2*>(ob + (pr + x * NP) * 16 + 4 * lg) =
         u32x2{pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv)};
   }
   if (lg == 0 && w == 0) p.lse[l_off] = lse;
@@ -440,13 +478,19 @@ qkv_decode_kernel(const QkvParams p) {
 // d 128, two at d 256), so one workgroup per CU covers the longest key range
 template <int FMT, int D>
 constexpr int waves_of() {
-  return D == 128 ? (FMT == kFmtQ8 ? 12 : 16) : 8;
+  return D == 128 ? (FMT == kFmtQ8 ? 12 : 16) : (D == 256 ? 8 : 6);
+}
+
+// column halves per wave pair: 512-wide heads split their columns over two waves
+template <int D>
+constexpr int cs_of() {
+  return D == 512 ? 2 : 1;
 }
 
 template <int FMT, int D>
 int launch_cfg(const QkvParams& p, void* stream) {
   constexpr int NW = waves_of<FMT, D>();
-  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, NW>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
+  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, NW, cs_of<D>()>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
                      dim3(64 * NW), 0, reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
@@ -455,7 +499,8 @@ template <int FMT, int D>
 int occ_cfg() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, waves_of<FMT, D>()>), 64 * waves_of<FMT, D>(),
+          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, waves_of<FMT, D>(), cs_of<D>()>),
+          64 * waves_of<FMT, D>(),
           0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -470,6 +515,8 @@ int launch_qkv(const QkvParams& p, int fmt, int d, void* stream) {
   if (fmt == kFmtQ4 && d == 128) return launch_cfg<kFmtQ4, 128>(p, stream);
   if (fmt == kFmtQ8 && d == 256) return launch_cfg<kFmtQ8, 256>(p, stream);
   if (fmt == kFmtQ4 && d == 256) return launch_cfg<kFmtQ4, 256>(p, stream);
+  if (fmt == kFmtQ8 && d == 512) return launch_cfg<kFmtQ8, 512>(p, stream);
+  if (fmt == kFmtQ4 && d == 512) return launch_cfg<kFmtQ4, 512>(p, stream);
   return -1;
 }
 
@@ -478,6 +525,8 @@ int occupancy_qkv(int fmt, int d) {
   if (fmt == kFmtQ4 && d == 128) return occ_cfg<kFmtQ4, 128>();
   if (fmt == kFmtQ8 && d == 256) return occ_cfg<kFmtQ8, 256>();
   if (fmt == kFmtQ4 && d == 256) return occ_cfg<kFmtQ4, 256>();
+  if (fmt == kFmtQ8 && d == 512) return occ_cfg<kFmtQ8, 512>();
+  if (fmt == kFmtQ4 && d == 512) return occ_cfg<kFmtQ4, 512>();
   return 0;
 }
 

@@ -513,17 +513,16 @@ attn_status attn_bwd_sparse_topk(const attn_sparse_bwd_args* a, void* workspace,
  *         pointers 4-byte aligned
  *   out   [B, H, Tq, d] bf16 (written), lse [B, H, Tq] fp32 contiguous (written)
  *   sinks [H] fp32 or NULL; causal bottom-right as in attn_dense_args.
- *   Compiled: kv_format Q8_0 or Q4_0 (K and V alike), d = 128 or 256 (the
- *   llama.cpp page's "Overview" lists head sizes 128, 256 and 512; 512 is
- *   ATTN_UNSUPPORTED: one wave would hold a 512-wide row's output and query,
- *   more registers than a wave has).
+ *   Compiled: kv_format Q8_0 or Q4_0 (K and V alike), d = 128, 256 or 512
+ *   (the head sizes the llama.cpp page's "Overview" lists); other d return
+ *   ATTN_UNSUPPORTED.
  *
  * Keys are cut into ranges as in attn_fwd_dense_splitkv (n_splits, 0 = the
  * library's choice; workspace n * B*H*Tq * (d + 1) * 4 bytes from
  * attn_qkv_workspace_bytes, NULL when one range is used) and merged. Errors as
  * in the other calls, before any launch. Launches are recorded under
- * "dense_qkv_q8_0_d128" / "dense_qkv_q4_0_d128" (and "splitkv_merge"); no
- * conversion kernel exists.
+ * "dense_qkv_<format>_d<d>" ("dense_qkv_q8_0_d128" ... "dense_qkv_q4_0_d512",
+ * and "splitkv_merge"); no conversion kernel exists.
  */
 typedef enum attn_kv_format { ATTN_KV_Q4_0 = 2, ATTN_KV_Q8_0 = 8 } attn_kv_format;
 

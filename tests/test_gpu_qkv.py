@@ -49,7 +49,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}/{c[2]}T{c[3]}x{c[4]}"
                          f"{'c' if c[5] else 'n'}{'s' if c[6] else ''}n{c[7]}")
@@ -76,14 +76,16 @@ def test_qkv_dispatch_no_conversion():
         assert A.dispatch_count(path) == 0
 
 
+@pytest.mark.parametrize("d", [256, 512])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
-def test_qkv_dispatch_d256(fmt):
-    """256-wide heads run their own kernel path (and no 128-wide one)."""
-    inp = synth.make_quant_kv(1, 8, 2, 2, 300, 256, fmt, seed=3)
+def test_qkv_dispatch_wide(fmt, d):
+    """256- and 512-wide heads run their own kernel paths (and no other width's)."""
+    inp = synth.make_quant_kv(1, 8, 2, 2, 300, d, fmt, seed=3)
     A.reset_dispatch_counts()
-    out, lse = run(inp, causal=True, scale=1 / 16, n_splits=2)
-    assert A.dispatch_count(f"dense_qkv_{fmt}_d256") == 1 and A.dispatch_count(f"dense_qkv_{fmt}_d128") == 0
-    ro, rl = reference(inp, causal=True, scale=1 / 16)
+    out, lse = run(inp, causal=True, scale=1 / math.sqrt(d), n_splits=2)
+    for other in (128, 256, 512):
+        assert A.dispatch_count(f"dense_qkv_{fmt}_d{other}") == (1 if other == d else 0)
+    ro, rl = reference(inp, causal=True, scale=1 / math.sqrt(d))
     assert _o_err(_np(out), ro) <= TOL_O and _lse_err(_np(lse), rl) <= TOL_LSE
 
 
@@ -94,9 +96,9 @@ def test_qkv_rejects():
         A.dense_qkv(q, k, v, fmt="q5_0", causal=True)
     with pytest.raises(A.AttnInvalidArgument):   # row bytes do not match the format
         A.dense_qkv(q, k[..., :68], v[..., :68], fmt="q8_0", causal=True)
-    wide = synth.make_quant_kv(1, 4, 2, 2, 64, 512, "q8_0", seed=4)
-    with pytest.raises(A.AttnUnsupported):       # 512-wide heads are not compiled
-        A.dense_qkv(wide["q"].cuda(), wide["k"].cuda(), wide["v"].cuda(), fmt="q8_0", causal=True)
+    odd = synth.make_quant_kv(1, 4, 2, 2, 64, 384, "q8_0", seed=4)
+    with pytest.raises(A.AttnUnsupported):       # 384-wide heads are not compiled
+        A.dense_qkv(odd["q"].cuda(), odd["k"].cuda(), odd["v"].cuda(), fmt="q8_0", causal=True)
     torch.cuda.synchronize()
 
 

@@ -119,7 +119,7 @@ def test_sparse_rescale(Sq, N, topk, mode):
 
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 256, 512])
 def test_qkv_rescale(d, fmt, mode):
     inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, d, fmt, mode, sinks=True, seed=77)
     label = f"qkv {fmt} d{d} {mode}"
