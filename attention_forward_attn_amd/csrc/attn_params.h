@@ -168,8 +168,8 @@ int launch_sparse_fp8(const SpFp8Params& p, void* stream);
 int launch_bwd_sparse(const BwdParams& p, void* stream);
 
 // Decode forward over a quantized K/V cache (q8_0 / q4_0 blocks, bf16 q and
-// out): the keys of one (b, kv head) and up to 32 folded query rows per
-// workgroup, key ranges on grid y as in split-KV.
+// out): the keys of one (b, kv head) and 16 folded query rows per workgroup,
+// key ranges on grid y as in split-KV.
 struct QkvParams {
   const void* q;
   const unsigned char* k;
