@@ -1492,10 +1492,12 @@ attn_fwd_dma_kernel(const KernelParams p) {
       nb = (kend + BN - 1) / BN;
     }
     // Loads of key step i: K block i+KD and V block i+VD. With two groups the
-    // V block is loaded by group 1 right after B(2i) and the K block by group
-    // 0 right after B(2i+1), each at the start of its softmax half, so the
-    // issue never delays an MFMA half; with one group both are issued right
-    // after the S product of step i, while its MFMAs drain.
+    // V block is loaded by group 1 right after B(2i), at the start of its
+    // softmax half, and the K block by group 0 in the same half step, between
+    // the S and PV products of its MFMA half (measured 1% faster than at the
+    // start of its softmax half, which the VALU work makes the longer half);
+    // with one group both are issued right after the S product of step i,
+    // while its MFMAs drain.
     auto issue_k = [&](int i) {
       const int kj = i + C::KD;
       if (kj >= 0 && kj < nb) issueK(kj);
@@ -1551,17 +1553,17 @@ attn_fwd_dma_kernel(const KernelParams p) {
         }
         const int j = u >> 1;
         if ((u & 1) == 0) {
-          // MFMA half: S(j) and the PV product of block j-1
+          // MFMA half: S(j) and the PV product of block j-1; group 0's K
+          // loads of step t/2 go out between the two, while the S products
+          // drain
           if (j < nb) doS(j);
           // keep the V reads below the S product (register pressure)
           __builtin_amdgcn_sched_barrier(0);
+          if (wgrp == 0) issue_k(t >> 1);
           if (j >= 1) doPV(j - 1);
         } else {
-          // softmax half; this group's loads of step t/2 go first
-          if (wgrp == 0)
-            issue_k(t >> 1);
-          else
-            issue_v(t >> 1);
+          // softmax half; group 1's V loads of step t/2 go first
+          if (wgrp == 1) issue_v(t >> 1);
           if (j < nb) phase2(j);
         }
       }
