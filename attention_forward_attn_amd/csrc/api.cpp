@@ -46,8 +46,10 @@ constexpr int kMergeSlot = kMaxPaths - 1;
 constexpr const char* kMergePath = "splitkv_merge";
 
 // the dense backward paths have counters of their own, below the merge's
-constexpr const char* kBwdPaths[] = {"dense_bwd_bf16_d64", "dense_bwd_bf16_d128", "dense_bwd_bf16_d192_v128"};
-constexpr int kBwdSlot0 = kMergeSlot - 3;
+constexpr const char* kBwdPaths[] = {"dense_bwd_bf16_d64", "dense_bwd_bf16_d128", "dense_bwd_bf16_d192_v128",
+                                     "dense_bwd_bf16_d256", "dense_bwd_bf16_d512"};
+constexpr int kBwdPathCount = 5;
+constexpr int kBwdSlot0 = kMergeSlot - kBwdPathCount;
 // and the quantized-cache decode paths below those
 constexpr const char* kQkvPaths[] = {"dense_qkv_q8_0_d128", "dense_qkv_q4_0_d128", "dense_qkv_q8_0_d256",
                                      "dense_qkv_q4_0_d256", "dense_qkv_q8_0_d512", "dense_qkv_q4_0_d512"};
@@ -71,7 +73,7 @@ int path_index(const char* path) {
   if (std::strcmp(path, kFp8Path) == 0) return kFp8Slot;
   for (int i = 0; i < kQkvPathCount; ++i)
     if (std::strcmp(path, kQkvPaths[i]) == 0) return kQkvSlot0 + i;
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < kBwdPathCount; ++i)
     if (std::strcmp(path, kBwdPaths[i]) == 0) return kBwdSlot0 + i;
   int n = 0;
   const attn::KernelConfig* t = attn::kernel_table(&n);
@@ -118,7 +120,7 @@ struct DensePlan {
 template <class Args>
 static attn_status validate_keep(const Args* a, int Tq, int Tk) {
   if (!a->keep) return ATTN_OK;
-  if (a->dtype != ATTN_BF16 || !attn::bwd_supported(a->d_qk, a->d_v))
+  if (a->dtype != ATTN_BF16 || !attn::dropout_supported(a->d_qk, a->d_v))
     return fail(ATTN_UNSUPPORTED, "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128)}");
   if (!(a->p_drop >= 0.f && a->p_drop < 1.f)) return fail(ATTN_INVALID_ARGUMENT, "p_drop must be in [0, 1)");
   if ((uintptr_t)a->keep & 3u) return fail(ATTN_INVALID_ARGUMENT, "keep must be 4-byte aligned");
@@ -632,6 +634,8 @@ static int bwd_path(int d_qk, int d_v) {
   if (d_qk == 64 && d_v == 64) return 0;
   if (d_qk == 128 && d_v == 128) return 1;
   if (d_qk == 192 && d_v == 128) return 2;
+  if (d_qk == 256 && d_v == 256) return 3;
+  if (d_qk == 512 && d_v == 512) return 4;
   return -1;
 }
 
@@ -685,9 +689,21 @@ static attn_status validate_bwd(const attn_dense_bwd_args* a) {
   return validate_keep(a, a->Tq, a->Tk);
 }
 
-static int64_t bwd_workspace(const attn_dense_bwd_args* a) {
+// the row dots D (fp32 [B, H, Tq]), then, where the dK/dV kernel splits the
+// query heads of a kv group, its fp32 partials [n_split, B*Hkv, Tk, d_qk + d_v]
+static int64_t bwd_dots_bytes(const attn_dense_bwd_args* a) {
   const int64_t rows = (int64_t)a->B * a->H * a->Tq;
   return (rows * 4 + 255) / 256 * 256;
+}
+
+static int bwd_splits(const attn_dense_bwd_args* a) {
+  return attn::bwd_head_splits(a->B, a->Hkv, a->H / a->Hkv, a->Tk, a->d_qk, a->d_v);
+}
+
+static int64_t bwd_workspace(const attn_dense_bwd_args* a) {
+  const int ns = bwd_splits(a);
+  const int64_t part = ns > 1 ? (int64_t)ns * a->B * a->Hkv * a->Tk * (a->d_qk + a->d_v) * 4 : 0;
+  return bwd_dots_bytes(a) + part;
 }
 
 }  // namespace
@@ -712,6 +728,8 @@ attn_status attn_bwd_dense(const attn_dense_bwd_args* a, void* workspace, int64_
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.dout = a->dout; p.lse = a->lse; p.sinks = a->sinks;
   p.dq = a->dq; p.dk = a->dk; p.dv = a->dv; p.dsinks = a->dsinks;
   p.D = static_cast<float*>(workspace);
+  p.n_split = bwd_splits(a);
+  p.part = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dots_bytes(a)) : nullptr;
   p.q_sb = a->q_sb; p.q_sh = a->q_sh; p.q_st = a->q_st;
   p.k_sb = a->k_sb; p.k_sh = a->k_sh; p.k_st = a->k_st;
   p.v_sb = a->v_sb; p.v_sh = a->v_sh; p.v_st = a->v_st;

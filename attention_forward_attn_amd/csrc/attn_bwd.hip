@@ -817,6 +817,318 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 4b. dK/dV and dQ for 256- and 512-wide heads (d_qk = d_v = D). One wave
+//     cannot hold a D-wide accumulator next to its operands, so the columns
+//     are split: wave (group gi, column slice cs) owns columns 128 cs ..
+//     128 cs + 127 of its 32 keys (dK/dV) or 32 folded rows (dQ). S and dP
+//     need the whole contraction over D: each wave multiplies over its slice
+//     and the D/128 partial products of a group are added through LDS in a
+//     fixed order (every wave of the group then holds the same S and dP), two
+//     workgroup barriers per step. One wave per SIMD (the partial products,
+//     the slice's operands and accumulators take ~300 registers); the Q/dO
+//     (dK/dV) or K/V (dQ) tiles are double-buffered through LDS, 160 KiB per
+//     workgroup at D = 512.
+// ---------------------------------------------------------------------------
+template <int D, int NG>
+__global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dkdv_wide_kernel(const BwdParams p) {
+  constexpr int DS = D / 128, NW = NG * DS, DC = 128;
+  constexpr int BNK = 32 * NG, BQ = 32;
+  constexpr int CP = D / 8, KSC = DC / 16, DTC = DC / 32;
+  constexpr int QT_BYTES = BQ * D * 2, STAGE = 2 * QT_BYTES;  // [Q tile | dO tile]
+  constexpr int XS_FLOATS = NW * 2 * 16 * 64;                 // partial S and dP of every wave
+  static_assert(2 * STAGE + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XS_FLOATS * 4];
+  float* const xs = reinterpret_cast<float*>(smem + 2 * STAGE);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int gi = wave / DS, cs = wave % DS;
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int rsp = blockIdx.x / n_groups, sp = rsp % p.n_split;
+  const int kb0 = (rsp / p.n_split) * BNK;  // the longest causal key blocks first
+  const int h_lo = sp * p.g / p.n_split, h_hi = (sp + 1) * p.g / p.n_split;
+  const int key = kb0 + gi * 32 + lq;
+  const int keyc = min(key, p.Tk - 1);
+
+  // K and V of this lane's key over the wave's columns (B operands of S and dP)
+  bf16x8 kf[KSC], vf[KSC];
+  {
+    const bf16_t* kp = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh + (int64_t)keyc * p.k_st + cs * DC;
+    const bf16_t* vp = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh + (int64_t)keyc * p.v_st + cs * DC;
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(kp + s * 16 + lh * 8);
+      vf[s] = *reinterpret_cast<const bf16x8*>(vp + s * 16 + lh * 8);
+    }
+  }
+  f32x16 ak[DTC], av[DTC];
+#pragma unroll
+  for (int dt = 0; dt < DTC; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ak[dt][i] = 0.f;
+      av[dt][i] = 0.f;
+    }
+
+  const int off = p.Tk - p.Tq;
+  const int up = p.causal ? 0 : p.win_right;
+  const int t_first = up >= 0 ? max(0, kb0 - off - up) : 0;
+  const int t_last = p.win_left >= 0 ? min(p.Tq - 1, kb0 + BNK - 1 - off + p.win_left) : p.Tq - 1;
+  const int ntb = (p.Tq + BQ - 1) / BQ;
+  const int tb0 = min(t_first / BQ, ntb);
+  const int per_head = t_last < t_first ? 0 : max(0, min(ntb, t_last / BQ + 1) - tb0);
+  const int n_it = (h_hi - h_lo) * per_head;
+  const uint32_t smem_s = lds_u32(smem);
+
+  auto issue = [&](int it) {
+    const int hl = h_lo + it / per_head, t0 = (tb0 + it % per_head) * BQ;
+    const int h = kvh * p.g + hl;
+    const uint32_t st = smem_s + (uint32_t)((it & 1) * STAGE);
+    dma_tile<CP, BQ, NW>(reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh, p.q_st, t0, p.Tq - 1, st,
+                         wave, lane);
+    dma_tile<CP, BQ, NW>(reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh, p.do_st, t0, p.Tq - 1,
+                         st + QT_BYTES, wave, lane);
+  };
+
+  if (n_it > 0) issue(0);
+  for (int it = 0; it < n_it; ++it) {
+    wait_all_loads();
+    barrier();  // tile it has landed everywhere; nobody reads the other stage any more
+    if (it + 1 < n_it) issue(it + 1);
+    const int hl = h_lo + it / per_head, t0 = (tb0 + it % per_head) * BQ;
+    const int h = kvh * p.g + hl;
+    const bf16_t* qt = reinterpret_cast<const bf16_t*>(smem + (it & 1) * STAGE);
+    const bf16_t* ot = reinterpret_cast<const bf16_t*>(smem + (it & 1) * STAGE + QT_BYTES);
+    // lse and D of this lane's 16 rows (row lh*4 + 8*(i/4) + i%4 of the tile), clamped to the last row
+    const int64_t rb = ((int64_t)b * p.H + h) * p.Tq;
+    float L[16], Dv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = min(t0 + lh * 4 + 8 * (i >> 2) + (i & 3), p.Tq - 1);
+      L[i] = p.lse[rb + t];
+      Dv[i] = p.D[rb + t];
+    }
+    // partial S and dP over the wave's columns; accumulator element i holds
+    // query row lh*4 + 8*(i/4) + i%4 of key `key`
+    f32x16 S, dP;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      S = mfma32(row_frag<CP>(qt, lq, cs * KSC + s, lh), kf[s], S);
+      dP = mfma32(row_frag<CP>(ot, lq, cs * KSC + s, lh), vf[s], dP);
+    }
+    // the group's partial products, added in slice order
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xs[((wave * 2 + 0) * 16 + i) * 64 + lane] = S[i];
+      xs[((wave * 2 + 1) * 16 + i) * 64 + lane] = dP[i];
+    }
+    barrier();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float sv = xs[(((gi * DS) * 2 + 0) * 16 + i) * 64 + lane], dv = xs[(((gi * DS) * 2 + 1) * 16 + i) * 64 + lane];
+#pragma unroll
+      for (int c = 1; c < DS; ++c) {
+        sv += xs[(((gi * DS + c) * 2 + 0) * 16 + i) * 64 + lane];
+        dv += xs[(((gi * DS + c) * 2 + 1) * 16 + i) * 64 + lane];
+      }
+      S[i] = sv;
+      dP[i] = dv;
+    }
+    float P[16], dS[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + lh * 4 + 8 * (i >> 2) + (i & 3);
+      const int lim = t >= p.Tq ? -1 : (up >= 0 ? t + off + up : p.Tk - 1);
+      const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
+      float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[i] * kLog2e));
+      pr = (key <= lim && key >= lo) ? pr : 0.f;
+      P[i] = pr;
+      dS[i] = pr * (dP[i] - Dv[i]);
+    }
+    const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
+    const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+#pragma unroll
+    for (int dt = 0; dt < DTC; ++dt) {
+      av[dt] = mfma32(tr_frag<CP>(ot, 0, cs * DC + dt * 32, lane), pb0, av[dt]);
+      av[dt] = mfma32(tr_frag<CP>(ot, 16, cs * DC + dt * 32, lane), pb1, av[dt]);
+      ak[dt] = mfma32(tr_frag<CP>(qt, 0, cs * DC + dt * 32, lane), db0, ak[dt]);
+      ak[dt] = mfma32(tr_frag<CP>(qt, 16, cs * DC + dt * 32, lane), db1, ak[dt]);
+    }
+  }
+
+  // dK^T / dV^T tiles: lane holds key `key`, columns 128 cs + dt*32 + 8*g4 + 4*lh .. +3
+  if (key < p.Tk && p.n_split > 1) {
+    float* pp = p.part + ((int64_t)(sp * n_groups + grp) * p.Tk + key) * (2 * D) + cs * DC;
+#pragma unroll
+    for (int dt = 0; dt < DTC; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<f32x4*>(pp + d) =
+            f32x4{ak[dt][g4 * 4], ak[dt][g4 * 4 + 1], ak[dt][g4 * 4 + 2], ak[dt][g4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(pp + D + d) =
+            f32x4{av[dt][g4 * 4], av[dt][g4 * 4 + 1], av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3]};
+      }
+  } else if (key < p.Tk) {
+    bf16_t* dkp = reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st + cs * DC;
+    bf16_t* dvp = reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st + cs * DC;
+#pragma unroll
+    for (int dt = 0; dt < DTC; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(dkp + d) = u32x2{pack2(ak[dt][g4 * 4] * p.scale, ak[dt][g4 * 4 + 1] * p.scale),
+                                                   pack2(ak[dt][g4 * 4 + 2] * p.scale, ak[dt][g4 * 4 + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(dvp + d) =
+            u32x2{pack2(av[dt][g4 * 4], av[dt][g4 * 4 + 1]), pack2(av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3])};
+      }
+  }
+}
+
+template <int D, int NG>
+__global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const BwdParams p) {
+  constexpr int DS = D / 128, NW = NG * DS, DC = 128;
+  constexpr int BM = 32 * NG, BN = 32;
+  constexpr int CP = D / 8, KSC = DC / 16, DTC = DC / 32;
+  constexpr int KT_BYTES = BN * D * 2, STAGE = 2 * KT_BYTES;  // [K tile | V tile]
+  constexpr int XS_FLOATS = NW * 2 * 16 * 64;
+  static_assert(2 * STAGE + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XS_FLOATS * 4];
+  float* const xs = reinterpret_cast<float*>(smem + 2 * STAGE);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
+  const int gi = wave / DS, cs = wave % DS;
+  const int n_groups = p.B * p.Hkv;
+  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int rows = p.g * p.Tq;
+  const int n_rt = (rows + BM - 1) / BM;
+  const int tb = n_rt - 1 - (int)(blockIdx.x / n_groups);  // longest causal tiles first
+  const int f0 = tb * BM;
+  const int f = f0 + gi * 32 + lq;
+  const bool valid = f < rows;
+  const int fc = valid ? f : rows - 1;
+  const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
+  const int off = p.Tk - p.Tq;
+  const int up = p.causal ? 0 : p.win_right;
+  const int row_lim = !valid ? -1 : (up >= 0 ? min(t + off + up, p.Tk - 1) : p.Tk - 1);
+  const int row_lo = p.win_left >= 0 ? t + off - p.win_left : 0;
+  const int64_t lrow = ((int64_t)b * p.H + h) * p.Tq + t;
+  const float lse = p.lse[lrow];
+  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  const float Dr = p.D[lrow];
+
+  // q and dO of this lane's row over the wave's columns (B operands of S^T and dP^T)
+  bf16x8 qf[KSC], dof[KSC];
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st + cs * DC;
+    const bf16_t* dp =
+        reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)t * p.do_st + cs * DC;
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + lh * 8);
+      dof[s] = *reinterpret_cast<const bf16x8*>(dp + s * 16 + lh * 8);
+    }
+  }
+
+  // keys the workgroup's rows can see ([kstart, kend))
+  int kend = p.Tk, kstart = 0;
+  {
+    const int f_last = min(f0 + BM, rows) - 1;
+    const bool one_head = f_last / p.Tq == f0 / p.Tq;
+    const int t_hi = one_head ? f_last % p.Tq : p.Tq - 1;
+    const int t_lo = one_head ? f0 % p.Tq : 0;
+    if (up >= 0) kend = max(0, min(p.Tk, t_hi + off + up + 1));
+    if (p.win_left >= 0) kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
+  }
+  const int nb = (kend + BN - 1) / BN, jb0 = kstart / BN;
+
+  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
+  const uint32_t smem_s = lds_u32(smem);
+  auto issue = [&](int j) {
+    const uint32_t st = smem_s + (uint32_t)((j & 1) * STAGE);
+    dma_tile<CP, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, st, wave, lane);
+    dma_tile<CP, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1, st + KT_BYTES, wave, lane);
+  };
+
+  f32x16 acc[DTC];
+#pragma unroll
+  for (int dt = 0; dt < DTC; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  if (nb > jb0) issue(jb0);
+  for (int j = jb0; j < nb; ++j) {
+    wait_all_loads();
+    barrier();
+    if (j + 1 < nb) issue(j + 1);
+    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
+    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
+    // partial S^T and dP^T over the wave's columns; element i is key
+    // j*BN + lh*4 + 8*(i/4) + i%4 of this lane's row
+    f32x16 S, dP;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      S = mfma32(row_frag<CP>(kt, lq, cs * KSC + s, lh), qf[s], S);
+      dP = mfma32(row_frag<CP>(vt, lq, cs * KSC + s, lh), dof[s], dP);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xs[((wave * 2 + 0) * 16 + i) * 64 + lane] = S[i];
+      xs[((wave * 2 + 1) * 16 + i) * 64 + lane] = dP[i];
+    }
+    barrier();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float sv = xs[(((gi * DS) * 2 + 0) * 16 + i) * 64 + lane], dv = xs[(((gi * DS) * 2 + 1) * 16 + i) * 64 + lane];
+#pragma unroll
+      for (int c = 1; c < DS; ++c) {
+        sv += xs[(((gi * DS + c) * 2 + 0) * 16 + i) * 64 + lane];
+        dv += xs[(((gi * DS + c) * 2 + 1) * 16 + i) * 64 + lane];
+      }
+      S[i] = sv;
+      dP[i] = dv;
+    }
+    float dS[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = j * BN + lh * 4 + 8 * (i >> 2) + (i & 3);
+      float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -l2));
+      pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
+      dS[i] = pr * (dP[i] - Dr);
+    }
+    const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+#pragma unroll
+    for (int dt = 0; dt < DTC; ++dt) {
+      acc[dt] = mfma32(tr_frag<CP>(kt, 0, cs * DC + dt * 32, lane), db0, acc[dt]);
+      acc[dt] = mfma32(tr_frag<CP>(kt, 16, cs * DC + dt * 32, lane), db1, acc[dt]);
+    }
+  }
+
+  if (valid) {
+    bf16_t* qo = reinterpret_cast<bf16_t*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)t * p.dq_st + cs * DC;
+#pragma unroll
+    for (int dt = 0; dt < DTC; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + lh * 4;
+        *reinterpret_cast<u32x2*>(qo + d) = u32x2{pack2(acc[dt][g4 * 4] * p.scale, acc[dt][g4 * 4 + 1] * p.scale),
+                                                  pack2(acc[dt][g4 * 4 + 2] * p.scale, acc[dt][g4 * 4 + 3] * p.scale)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 7. Forward with attention dropout. The keep mask is an input that the
 //    backward reads too, so the two cannot disagree on it (the
 //    TransformerEngine page's review names a context-parallel backward that
@@ -1205,6 +1517,74 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
   if (sq == 0 && lh == 0) p.part_lse[orow] = any ? m_run * p.scale + __builtin_amdgcn_logf(l) * kLn2 : -INFINITY;
 }
 
+// dK and dV from the head-split partials: four columns a thread, the splits
+// added in order (so the result does not depend on the launch's timing)
+template <int D>
+__global__ void __launch_bounds__(256) bwd_wide_reduce_kernel(const BwdParams p) {
+  constexpr int C4 = 2 * D / 4;  // four-column units of one key's [dK | dV] row
+  const int64_t n_keys = (int64_t)p.B * p.Hkv * p.Tk;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n_keys * C4) return;
+  const int64_t row = u / C4;
+  const int c = (int)(u % C4) * 4;
+  const int grp = (int)(row / p.Tk), key = (int)(row % p.Tk), b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int64_t split_stride = n_keys * 2 * D;
+  const float* src = p.part + row * 2 * D + c;
+  f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  for (int s = 1; s < p.n_split; ++s) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + s * split_stride);
+    a[0] += x[0];
+    a[1] += x[1];
+    a[2] += x[2];
+    a[3] += x[3];
+  }
+  bf16_t* dst;
+  float m = 1.f;
+  if (c < D) {
+    dst = reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st + c;
+    m = p.scale;
+  } else {
+    dst = reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st + (c - D);
+  }
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack2(a[0] * m, a[1] * m), pack2(a[2] * m, a[3] * m)};
+}
+
+// 256- and 512-wide heads: column-split dK/dV and dQ kernels (four waves a workgroup)
+template <int D>
+int launch_bwd_wide(const BwdParams& p, void* stream) {
+  constexpr int NG = D == 512 ? 1 : 2, NW = NG * (D / 128);
+  if (p.n_split < 1 || p.n_split > p.g || (p.n_split > 1 && p.part == nullptr)) return (int)hipErrorInvalidValue;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t R = (int64_t)p.B * p.H * p.Tq;
+  if (R > 0) {
+    constexpr int RPB = 4 * (64 / (D / 8));  // rows per block of the dot kernel
+    hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((R + RPB - 1) / RPB)), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  if (p.sinks != nullptr && p.dsinks != nullptr) {
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3(p.H), dim3(256), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  if (p.Tk > 0) {
+    const int nkb = (p.Tk + 32 * NG - 1) / (32 * NG);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, NG>), dim3(nkb * p.n_split * p.B * p.Hkv), dim3(NW * 64), 0, st,
+                       p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+    if (p.n_split > 1) {
+      const int64_t units = (int64_t)p.B * p.Hkv * p.Tk * (2 * D / 4);
+      hipLaunchKernelGGL(bwd_wide_reduce_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, p);
+      if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+    }
+  }
+  if (p.Tq > 0) {
+    const int rows = p.g * p.Tq;
+    const int nrt = (rows + 32 * NG - 1) / (32 * NG);
+    hipLaunchKernelGGL((bwd_dq_wide_kernel<D, NG>), dim3(nrt * p.B * p.Hkv), dim3(NW * 64), 0, st, p);
+    if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
+  }
+  return 0;
+}
+
 template <int DQK, int DV, bool DROP>
 int launch_bwd_cfg(const BwdParams& p, void* stream) {
   // dQ: two waves per SIMD where the registers allow it (d_qk + d_v <= 256)
@@ -1580,7 +1960,23 @@ int launch_extras_d(const ExtrasParams& p, void* stream) {
 }  // namespace
 
 bool bwd_supported(int d_qk, int d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128) ||
+         (d_qk == 256 && d_v == 256) || (d_qk == 512 && d_v == 512);
+}
+
+bool dropout_supported(int d_qk, int d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+}
+
+int bwd_head_splits(int B, int Hkv, int g, int Tk, int d_qk, int d_v) {
+  if (d_qk != d_v || (d_qk != 256 && d_qk != 512) || Tk <= 0 || g <= 1) return 1;
+  const int bnk = d_qk == 512 ? 32 : 64;  // keys per dK/dV workgroup
+  const int64_t base = (int64_t)B * Hkv * ((Tk + bnk - 1) / bnk);
+  // one workgroup fits a CU: ask for about three per CU of the 256 so that the
+  // short causal key blocks fill in behind the long ones; at most 16 splits
+  // (the partials' traffic grows with their number)
+  if (base >= 512) return 1;
+  return (int)std::min<int64_t>({(int64_t)g, 16, (768 + base - 1) / base});
 }
 
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
@@ -1590,6 +1986,9 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
     return drop ? launch_bwd_cfg<128, 128, true>(p, stream) : launch_bwd_cfg<128, 128, false>(p, stream);
   if (d_qk == 192 && d_v == 128)
     return drop ? launch_bwd_cfg<192, 128, true>(p, stream) : launch_bwd_cfg<192, 128, false>(p, stream);
+  if (drop) return -1;  // no dropout kernels for the wide heads
+  if (d_qk == 256 && d_v == 256) return launch_bwd_wide<256>(p, stream);
+  if (d_qk == 512 && d_v == 512) return launch_bwd_wide<512>(p, stream);
   return -1;
 }
 

@@ -94,6 +94,12 @@ struct BwdParams {
   void* dv;
   float* dsinks;          // [H] or nullptr
   float* D;               // workspace: rowsum(dO * O), [B, H, Tq]
+  // 256- and 512-wide heads with few key blocks: the query heads of a kv group
+  // are split n_split ways over workgroups, each writing unscaled fp32 dK and dV
+  // partials to part, [n_split, B*Hkv, Tk, 2*d] (dK columns, then dV), summed in
+  // split order by a last kernel; n_split = 1 writes dk/dv directly
+  float* part;
+  int32_t n_split;
   int64_t q_sb, q_sh, q_st, k_sb, k_sh, k_st, v_sb, v_sh, v_st;
   int64_t o_sb, o_sh, o_st, do_sb, do_sh, do_st;
   int64_t dq_sb, dq_sh, dq_st, dk_sb, dk_sh, dk_st, dv_sb, dv_sh, dv_st;
@@ -130,6 +136,11 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
+// dropout (forward and backward) is compiled for (64,64), (128,128), (192,128)
+bool dropout_supported(int d_qk, int d_v);
+// how many ways the 256/512-wide dK/dV kernel splits a kv group's query heads
+// (1 for the other widths); the workspace holds the partials when it is > 1
+int bwd_head_splits(int B, int Hkv, int g, int Tk, int d_qk, int d_v);
 // The forward's extra returns (a second pass from q, k and the forward's
 // lse): probabilities of the visible keys and row maxima of the scaled scores.
 struct ExtrasParams {

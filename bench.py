@@ -11,7 +11,7 @@ epilogue). The primary line is the dense causal GQA prefill workload
 (B=2 H=32 Hkv=8 T=4096 d=128 bf16); the other workloads are measured in the
 same run and reported under "workloads" unless --primary-only is given.
 Rows beyond the five ("next_rows", skipped with --no-next-rows): split-KV
-decode (d512, beside the plain path), the dense backward on gqa / mla /
+decode (d512, beside the plain path), the dense backward on gqa / mla / mqa512 /
 swa1024 (algorithmic flops = five products per visible pair), decode over a
 q8_0 and a q4_0 cache (beside a bf16 cache), the packed variable-length
 forward (beside the padded batch), MLA two-part rows (beside the concatenated
@@ -1053,7 +1053,7 @@ def main():
         del r, rp
         torch.cuda.empty_cache()
         # the dense backward on the prefill workloads it is compiled for
-        for m in (2, 3, 7):
+        for m in (2, 3, 4, 7):
             next_rows.append(measure_bwd(m, st, wu))
             torch.cuda.empty_cache()
         # where the sparse forward's bytes come from: cache cleared, 1 GiB pool

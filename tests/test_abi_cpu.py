@@ -231,9 +231,18 @@ def test_bwd_workspace_and_validation():
     assert A.bwd_workspace_bytes(1, 8, 2, 3, 5, 64, 64) == 256          # rounded up to 256
     with pytest.raises(A.AttnInvalidArgument):
         A.bwd_workspace_bytes(1, 8, 3, 3, 5, 64, 64)                    # H % Hkv != 0
-    assert lib.attn_bwd_dense_workspace_bytes(ctypes.byref(_fake_bwd(d_qk=256, d_v=256))) == -1
+    assert lib.attn_bwd_dense_workspace_bytes(ctypes.byref(_fake_bwd(d_qk=384, d_v=384))) == -1
+    assert lib.attn_bwd_dense_workspace_bytes(ctypes.byref(_fake_bwd(d_qk=256, d_v=128))) == -1
+    assert lib.attn_bwd_dense_workspace_bytes(ctypes.byref(_fake_bwd(d_qk=512, d_v=512))) > 0
+    # 512-wide MQA, 1400 keys: 44 key blocks of 32, so the 64 query heads are split
+    # 16 ways and the workspace adds 16 fp32 [dK | dV] partials of the kv head
+    assert A.bwd_workspace_bytes(1, 64, 1, 1400, 1400, 512, 512) == 64 * 1400 * 4 + 16 * 1400 * 1024 * 4
+    # many key blocks (8 groups x 64 blocks of 64 keys): no split
+    assert A.bwd_workspace_bytes(2, 32, 8, 4096, 4096, 256, 256) == 2 * 32 * 4096 * 4
+    # the split never exceeds the heads of a group: 2 heads, 1 key block
+    assert A.bwd_workspace_bytes(1, 2, 1, 16, 16, 256, 256) == 256 + 2 * 16 * 512 * 4
     ws = ctypes.c_void_p(0x20000)
-    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(d_qk=512, d_v=512)), ws, 1 << 20, None)
+    st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(d_qk=384, d_v=384)), ws, 1 << 20, None)
     assert st == A.ATTN_UNSUPPORTED
     st = lib.attn_bwd_dense(ctypes.byref(_fake_bwd(dsinks=0x30000)), ws, 1 << 20, None)
     assert st == A.ATTN_INVALID_ARGUMENT and b"dsinks" in lib.attn_last_error()

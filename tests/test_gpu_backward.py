@@ -61,7 +61,7 @@ def check_bwd(inp, dout, *, causal, scale, label):
     return errs
 
 
-BWD_DIMS = [(64, 64), (128, 128), (192, 128)]
+BWD_DIMS = [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]
 
 
 @pytest.mark.parametrize("dqk,dv", BWD_DIMS)
@@ -81,6 +81,10 @@ CASES = [
     (2, 6, 3, 1, 257, 192, 128, True, True),       # one query row
     (1, 2, 1, 97, 1, 128, 128, False, False),      # one key: dq = dk = 0
     (1, 16, 16, 64, 64, 192, 128, True, False),    # MLA shape, exact tiles
+    (1, 8, 1, 130, 130, 512, 512, True, True),     # MQA, 512-wide heads, sinks
+    (1, 8, 2, 70, 333, 256, 256, True, True),      # GQA, 256-wide heads, Tq < Tk, sinks
+    (1, 4, 4, 150, 40, 512, 512, True, False),     # 512-wide, rows that see no key
+    (2, 6, 3, 1, 257, 256, 256, False, True),      # 256-wide, one query row
 ]
 
 
@@ -134,33 +138,57 @@ def test_bwd_rejects_bad_arguments():
     with pytest.raises(A.AttnInvalidArgument):   # workspace too small
         A.dense_backward(q, k, v, out, out, lse, causal=True, scale=0.1,
                          workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
-    q5 = torch.zeros(1, 4, 8, 256, dtype=torch.bfloat16, device="cuda")
-    k5 = torch.zeros(1, 2, 8, 256, dtype=torch.bfloat16, device="cuda")
+    q5 = torch.zeros(1, 4, 8, 384, dtype=torch.bfloat16, device="cuda")
+    k5 = torch.zeros(1, 2, 8, 384, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(A.AttnUnsupported):       # head dims without a compiled backward
         A.dense_backward(q5, k5, k5, q5, q5, lse, causal=True, scale=0.1)
     torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------ full benchmark shapes, one kv group sampled
-@pytest.mark.parametrize("wl,group", [(2, (1, 5)), (3, (3, 9))])
+@pytest.mark.parametrize("wl,group", [(2, (1, 5)), (3, (3, 9)), (4, (0, 0))])
 def test_bwd_full_workload_sampled_group(wl, group):
     """The benchmark's launch at full size; the oracle checks one (batch, kv head) group
-    (every dq row of its heads, every dk/dv row of the kv head): the gradient of a group
-    depends on that group's inputs only."""
+    (every dq row of its heads, every dk/dv row of the kv head, the sink gradients of
+    its heads): the gradient of a group depends on that group's inputs only. The
+    512-wide MQA workload is one group of 64 heads whose dK/dV kernel splits the
+    heads 16 ways."""
     s = synth.spec(wl)
     announce(f"bwd full workload {s.name} group {group}")
     inp = synth.make(wl)
     dout = synth.make_dout(s)
-    dq, dk, dv, _ = run_fwd_bwd(inp, dout, causal=s.causal, scale=s.scale)
+    dq, dk, dv, ds = run_fwd_bwd(inp, dout, causal=s.causal, scale=s.scale)
     b, kvh = group
     g = s.H // s.Hkv
     hs = slice(kvh * g, (kvh + 1) * g)
-    rq, rk, rv, _ = oracle.dense_attention_backward(
+    sk = inp["sinks"][hs] if inp["sinks"] is not None else None
+    rq, rk, rv, rs = oracle.dense_attention_backward(
         inp["q"][b:b + 1, hs], inp["k"][b:b + 1, kvh:kvh + 1], inp["v"][b:b + 1, kvh:kvh + 1], dout[b:b + 1, hs],
-        scale=s.scale, causal=s.causal)
+        scale=s.scale, causal=s.causal, sinks=sk)
     errs = {"dq": _rel_err(_np(dq[b:b + 1, hs]), rq), "dk": _rel_err(_np(dk[b:b + 1, kvh:kvh + 1]), rk),
             "dv": _rel_err(_np(dv[b:b + 1, kvh:kvh + 1]), rv)}
     assert max(errs.values()) <= TOL_REL, f"{s.name} group {group}: {errs}"
+    if rs is not None and s.B == 1:      # dsinks sums over the batch: one batch is the whole sum
+        es = _rel_err(_np(ds[hs]), rs)
+        assert es <= TOL_SINK, f"{s.name}: dsinks rel err {es:.3e}"
+
+
+def test_bwd_wide_many_key_blocks():
+    """256-wide heads with 64 groups x 8 key blocks = 512 dK/dV workgroups: the heads of a
+    group are not split (dk, dv written directly); two groups checked against the oracle."""
+    announce("bwd d256 B64 H2/1 T512 (no head split)")
+    B, H, Hkv, T, d = 64, 2, 1, 512, 256
+    assert A.bwd_workspace_bytes(B, H, Hkv, T, T, d, d) == B * H * T * 4
+    inp = synth.randn_dense(B, H, Hkv, T, T, d, d, dtype="bf16", sinks=True, seed=41)
+    dout = synth.randn_dout(B, H, T, d, seed=41)
+    dq, dk, dv, _ = run_fwd_bwd(inp, dout, causal=True, scale=1 / math.sqrt(d))
+    for b in (0, B - 1):
+        rq, rk, rv, _r = oracle.dense_attention_backward(
+            inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1], dout[b:b + 1], scale=1 / math.sqrt(d),
+            causal=True, sinks=inp["sinks"])
+        errs = {"dq": _rel_err(_np(dq[b:b + 1]), rq), "dk": _rel_err(_np(dk[b:b + 1]), rk),
+                "dv": _rel_err(_np(dv[b:b + 1]), rv)}
+        assert max(errs.values()) <= TOL_REL, f"batch {b}: {errs}"
 
 
 # ------------------------------------------------------------------ sliding windows
@@ -171,6 +199,8 @@ WIN_CASES = [
     (1, 4, 4, 200, 333, 192, 128, True, False, (100, -1)),
     (2, 4, 1, 150, 150, 128, 128, True, False, (0, -1)),      # diagonal only
     (1, 8, 2, 100, 400, 128, 128, False, True, (-1, 20)),
+    (1, 8, 1, 200, 200, 512, 512, True, True, (40, -1)),
+    (1, 4, 2, 150, 260, 256, 256, False, False, (70, 25)),
 ]
 
 

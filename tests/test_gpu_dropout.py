@@ -106,6 +106,9 @@ def test_dropout_rejects():
     kw = synth.pack_keep(synth.make_keep(1, 2, 8, 8, 0.5, seed=1)).cuda()
     with pytest.raises(A.AttnUnsupported):        # no dropout kernel for 256-wide heads
         A.dense(q, k, v, keep=kw, p_drop=0.5)
+    o256, l256 = A.dense(q, k, v, causal=True, scale=0.1)
+    with pytest.raises(A.AttnUnsupported):        # the 256-wide backward takes no mask either
+        A.dense_backward(q, k, v, o256, o256, l256, causal=True, scale=0.1, keep=kw, p_drop=0.5)
     q2, k2 = q[..., :128].contiguous(), k[..., :128].contiguous()
     out = torch.empty_like(q2)
     lse = torch.empty((1, 2, 8), device="cuda")
