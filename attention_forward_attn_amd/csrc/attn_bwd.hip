@@ -995,11 +995,15 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
   constexpr int DS = D / 128, NW = NG * DS, DC = 128;
   constexpr int BM = 32 * NG, BN = 32;
   constexpr int CP = D / 8, KSC = DC / 16, DTC = DC / 32;
-  constexpr int KT_BYTES = BN * D * 2, STAGE = 2 * KT_BYTES;  // [K tile | V tile]
+  constexpr int KT_BYTES = BN * D * 2;
   constexpr int XS_FLOATS = NW * 2 * 16 * 64;
-  static_assert(2 * STAGE + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XS_FLOATS * 4];
-  float* const xs = reinterpret_cast<float*>(smem + 2 * STAGE);
+  // K tiles are double-buffered; V tiles too where LDS allows, else one V
+  // stage is refilled as soon as every wave has taken its dP from it
+  constexpr int NVS = 4 * KT_BYTES + XS_FLOATS * 4 <= 160 * 1024 ? 2 : 1;
+  constexpr int V_OFF = 2 * KT_BYTES, XS_OFF = V_OFF + NVS * KT_BYTES;
+  static_assert(XS_OFF + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[XS_OFF + XS_FLOATS * 4];
+  float* const xs = reinterpret_cast<float*>(smem + XS_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
   const int gi = wave / DS, cs = wave % DS;
@@ -1050,10 +1054,12 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
   const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
   const uint32_t smem_s = lds_u32(smem);
-  auto issue = [&](int j) {
-    const uint32_t st = smem_s + (uint32_t)((j & 1) * STAGE);
-    dma_tile<CP, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, st, wave, lane);
-    dma_tile<CP, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1, st + KT_BYTES, wave, lane);
+  auto issue_k = [&](int j) {
+    dma_tile<CP, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, smem_s + (uint32_t)((j & 1) * KT_BYTES), wave, lane);
+  };
+  auto issue_v = [&](int j) {
+    dma_tile<CP, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1,
+                         smem_s + (uint32_t)(V_OFF + (NVS == 2 ? (j & 1) : 0) * KT_BYTES), wave, lane);
   };
 
   f32x16 acc[DTC];
@@ -1062,13 +1068,19 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  if (nb > jb0) issue(jb0);
+  if (nb > jb0) {
+    issue_k(jb0);
+    issue_v(jb0);
+  }
   for (int j = jb0; j < nb; ++j) {
     wait_all_loads();
-    barrier();
-    if (j + 1 < nb) issue(j + 1);
-    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE);
-    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * STAGE + KT_BYTES);
+    barrier();  // tile j has landed everywhere; nobody reads the stages it+1 refills any more
+    if (j + 1 < nb) {
+      issue_k(j + 1);
+      if constexpr (NVS == 2) issue_v(j + 1);
+    }
+    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * KT_BYTES);
+    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + V_OFF + (NVS == 2 ? (j & 1) : 0) * KT_BYTES);
     // partial S^T and dP^T over the wave's columns; element i is key
     // j*BN + lh*4 + 8*(i/4) + i%4 of this lane's row
     f32x16 S, dP;
@@ -1088,6 +1100,8 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
       xs[((wave * 2 + 1) * 16 + i) * 64 + lane] = dP[i];
     }
     barrier();
+    if constexpr (NVS == 1)  // every wave has its dP partial: the V stage is free
+      if (j + 1 < nb) issue_v(j + 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float sv = xs[(((gi * DS) * 2 + 0) * 16 + i) * 64 + lane], dv = xs[(((gi * DS) * 2 + 1) * 16 + i) * 64 + lane];
@@ -1549,10 +1563,11 @@ __global__ void __launch_bounds__(256) bwd_wide_reduce_kernel(const BwdParams p)
   *reinterpret_cast<u32x2*>(dst) = u32x2{pack2(a[0] * m, a[1] * m), pack2(a[2] * m, a[3] * m)};
 }
 
-// 256- and 512-wide heads: column-split dK/dV and dQ kernels (four waves a workgroup)
+// 256- and 512-wide heads: column-split dK/dV and dQ kernels (4 or 8 waves a workgroup)
 template <int D>
 int launch_bwd_wide(const BwdParams& p, void* stream) {
-  constexpr int NG = D == 512 ? 1 : 2, NW = NG * (D / 128);
+  constexpr int NG = D == 512 ? 1 : 2, NW = NG * (D / 128);  // dK/dV
+  constexpr int NGQ = 1024 / D, NWQ = NGQ * (D / 128);        // dQ: 8 waves
   if (p.n_split < 1 || p.n_split > p.g || (p.n_split > 1 && p.part == nullptr)) return (int)hipErrorInvalidValue;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t R = (int64_t)p.B * p.H * p.Tq;
@@ -1578,8 +1593,8 @@ int launch_bwd_wide(const BwdParams& p, void* stream) {
   }
   if (p.Tq > 0) {
     const int rows = p.g * p.Tq;
-    const int nrt = (rows + 32 * NG - 1) / (32 * NG);
-    hipLaunchKernelGGL((bwd_dq_wide_kernel<D, NG>), dim3(nrt * p.B * p.Hkv), dim3(NW * 64), 0, st, p);
+    const int nrt = (rows + 32 * NGQ - 1) / (32 * NGQ);
+    hipLaunchKernelGGL((bwd_dq_wide_kernel<D, NGQ>), dim3(nrt * p.B * p.Hkv), dim3(NWQ * 64), 0, st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   return 0;
