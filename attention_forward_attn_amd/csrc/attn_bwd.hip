@@ -819,29 +819,36 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // 4b. dK/dV and dQ for 256- and 512-wide heads (d_qk = d_v = D). One wave
 //     cannot hold a D-wide accumulator next to its operands, so the columns
-//     are split: wave (group gi, column slice cs) owns columns 128 cs ..
-//     128 cs + 127 of its 32 keys (dK/dV) or 32 folded rows (dQ). S and dP
-//     need the whole contraction over D: each wave multiplies over its slice
-//     and the D/128 partial products of a group are added through LDS in a
-//     fixed order (every wave of the group then holds the same S and dP), two
-//     workgroup barriers per step. One wave per SIMD (the partial products,
-//     the slice's operands and accumulators take ~300 registers); the Q/dO
-//     (dK/dV) or K/V (dQ) tiles are double-buffered through LDS, 160 KiB per
-//     workgroup at D = 512.
+//     are split into DS = D/128 slices of 128.
+//     dK/dV: a workgroup owns 32*NG keys in NG groups of 32; a group has 2*DS
+//     waves. K wave cs owns dK columns 128cs.. of the group's keys and forms
+//     the partial S = Q K^T over those columns; V wave cs owns the same dV
+//     columns and forms the partial dP = dO V^T. The partials go to LDS; each
+//     wave of the group then owns 16/(2*DS) of the 16 accumulator elements of
+//     every lane: it adds the partials of those elements in a fixed order,
+//     forms P and dS, and writes them as bf16 over the partials it consumed;
+//     after a barrier every wave reads the B operand it multiplies by (P for
+//     dV, dS for dK). Three workgroup barriers per 32-row step, two waves per
+//     SIMD; the Q and dO tiles are double-buffered through LDS.
+//     dQ: wave (group gi, slice cs) owns columns 128cs.. of 32 folded rows;
+//     S and dP partials are added through LDS in slice order (every wave of
+//     the group then holds the whole S and dP).
 // ---------------------------------------------------------------------------
 template <int D, int NG>
-__global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dkdv_wide_kernel(const BwdParams p) {
-  constexpr int DS = D / 128, NW = NG * DS, DC = 128;
+__global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(const BwdParams p) {
+  constexpr int DS = D / 128, GW = 2 * DS, NW = NG * GW, DC = 128;
+  constexpr int EP = 16 / GW;  // accumulator elements of every lane a wave reduces
   constexpr int BNK = 32 * NG, BQ = 32;
   constexpr int CP = D / 8, KSC = DC / 16, DTC = DC / 32;
   constexpr int QT_BYTES = BQ * D * 2, STAGE = 2 * QT_BYTES;  // [Q tile | dO tile]
-  constexpr int XS_FLOATS = NW * 2 * 16 * 64;                 // partial S and dP of every wave
-  static_assert(2 * STAGE + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XS_FLOATS * 4];
-  float* const xs = reinterpret_cast<float*>(smem + 2 * STAGE);
+  constexpr int XW_BYTES = 4 * 64 * 16;                       // one wave's partial: [q][lane][4 floats]
+  static_assert(EP == 2 || EP == 4, "two or four elements per wave");
+  static_assert(2 * STAGE + NW * XW_BYTES <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + NW * XW_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
-  const int gi = wave / DS, cs = wave % DS;
+  const int gi = wave / GW, gw = wave % GW;
+  const int role = gw / DS, cs = gw % DS;  // role 0: S and dK, role 1: dP and dV
   const int n_groups = p.B * p.Hkv;
   const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int rsp = blockIdx.x / n_groups, sp = rsp % p.n_split;
@@ -849,26 +856,25 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dkdv_wide_kernel(cons
   const int h_lo = sp * p.g / p.n_split, h_hi = (sp + 1) * p.g / p.n_split;
   const int key = kb0 + gi * 32 + lq;
   const int keyc = min(key, p.Tk - 1);
+  unsigned char* const xg = smem + 2 * STAGE + gi * GW * XW_BYTES;  // the group's partials
+  auto xat = [&](int w, int q) { return xg + w * XW_BYTES + (q * 64 + lane) * 16; };
 
-  // K and V of this lane's key over the wave's columns (B operands of S and dP)
-  bf16x8 kf[KSC], vf[KSC];
+  // K (role 0) or V (role 1) of this lane's key over the wave's columns: the B
+  // operand of the partial product
+  bf16x8 kvf[KSC];
   {
-    const bf16_t* kp = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh + (int64_t)keyc * p.k_st + cs * DC;
-    const bf16_t* vp = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh + (int64_t)keyc * p.v_st + cs * DC;
+    const bf16_t* src =
+        role ? reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh + (int64_t)keyc * p.v_st
+             : reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh + (int64_t)keyc * p.k_st;
+    src += cs * DC;
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(kp + s * 16 + lh * 8);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vp + s * 16 + lh * 8);
-    }
+    for (int s = 0; s < KSC; ++s) kvf[s] = *reinterpret_cast<const bf16x8*>(src + s * 16 + lh * 8);
   }
-  f32x16 ak[DTC], av[DTC];
+  f32x16 acc[DTC];
 #pragma unroll
   for (int dt = 0; dt < DTC; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ak[dt][i] = 0.f;
-      av[dt][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   const int off = p.Tk - p.Tq;
   const int up = p.causal ? 0 : p.win_right;
@@ -889,103 +895,144 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dkdv_wide_kernel(cons
     dma_tile<CP, BQ, NW>(reinterpret_cast<const bf16_t*>(p.dout) + b * p.do_sb + h * p.do_sh, p.do_st, t0, p.Tq - 1,
                          st + QT_BYTES, wave, lane);
   };
+  // lse and D of the rows of this wave's elements (element e of a lane is
+  // query row lh*4 + 8*(e/4) + e%4 of the tile), clamped to the last row;
+  // loaded one step ahead, before the step's tile loads are issued
+  float L[EP], Dv[EP];
+  auto load_rows = [&](int it) {
+    const int hl = h_lo + it / per_head, t0 = (tb0 + it % per_head) * BQ;
+    const int64_t rb = ((int64_t)b * p.H + kvh * p.g + hl) * p.Tq;
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+      const int e = gw * EP + k;
+      const int t = min(t0 + lh * 4 + 8 * (e >> 2) + (e & 3), p.Tq - 1);
+      L[k] = p.lse[rb + t];
+      Dv[k] = p.D[rb + t];
+    }
+  };
 
-  if (n_it > 0) issue(0);
+  if (n_it > 0) {
+    load_rows(0);
+    issue(0);
+  }
   for (int it = 0; it < n_it; ++it) {
     wait_all_loads();
-    barrier();  // tile it has landed everywhere; nobody reads the other stage any more
-    if (it + 1 < n_it) issue(it + 1);
-    const int hl = h_lo + it / per_head, t0 = (tb0 + it % per_head) * BQ;
-    const int h = kvh * p.g + hl;
-    const bf16_t* qt = reinterpret_cast<const bf16_t*>(smem + (it & 1) * STAGE);
-    const bf16_t* ot = reinterpret_cast<const bf16_t*>(smem + (it & 1) * STAGE + QT_BYTES);
-    // lse and D of this lane's 16 rows (row lh*4 + 8*(i/4) + i%4 of the tile), clamped to the last row
-    const int64_t rb = ((int64_t)b * p.H + h) * p.Tq;
-    float L[16], Dv[16];
+    barrier();  // tile it has landed everywhere; nobody reads the other stage or the partials any more
+    float Lc[EP], Dc[EP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = min(t0 + lh * 4 + 8 * (i >> 2) + (i & 3), p.Tq - 1);
-      L[i] = p.lse[rb + t];
-      Dv[i] = p.D[rb + t];
+    for (int k = 0; k < EP; ++k) {
+      Lc[k] = L[k];
+      Dc[k] = Dv[k];
     }
-    // partial S and dP over the wave's columns; accumulator element i holds
-    // query row lh*4 + 8*(i/4) + i%4 of key `key`
-    f32x16 S, dP;
+    if (it + 1 < n_it) {
+      load_rows(it + 1);
+      issue(it + 1);
+    }
+    const int t0 = (tb0 + it % per_head) * BQ;
+    const bf16_t* tl = reinterpret_cast<const bf16_t*>(smem + (it & 1) * STAGE + role * QT_BYTES);
+    // the partial S (role 0) or dP (role 1) over the wave's columns
+    f32x16 X;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      S[i] = 0.f;
-      dP[i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) X[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KSC; ++s) {
-      S = mfma32(row_frag<CP>(qt, lq, cs * KSC + s, lh), kf[s], S);
-      dP = mfma32(row_frag<CP>(ot, lq, cs * KSC + s, lh), vf[s], dP);
-    }
-    // the group's partial products, added in slice order
+    for (int s = 0; s < KSC; ++s) X = mfma32(row_frag<CP>(tl, lq, cs * KSC + s, lh), kvf[s], X);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      xs[((wave * 2 + 0) * 16 + i) * 64 + lane] = S[i];
-      xs[((wave * 2 + 1) * 16 + i) * 64 + lane] = dP[i];
-    }
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(xat(gw, q)) = f32x4{X[4 * q], X[4 * q + 1], X[4 * q + 2], X[4 * q + 3]};
     barrier();
+    // this wave's elements: the partials added in wave order, then P and dS
+    float sv[EP], dv[EP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float sv = xs[(((gi * DS) * 2 + 0) * 16 + i) * 64 + lane], dv = xs[(((gi * DS) * 2 + 1) * 16 + i) * 64 + lane];
+    for (int k = 0; k < EP; ++k) sv[k] = dv[k] = 0.f;
 #pragma unroll
-      for (int c = 1; c < DS; ++c) {
-        sv += xs[(((gi * DS + c) * 2 + 0) * 16 + i) * 64 + lane];
-        dv += xs[(((gi * DS + c) * 2 + 1) * 16 + i) * 64 + lane];
+    for (int c = 0; c < GW; ++c) {
+      float v[EP];
+      if constexpr (EP == 2) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(xat(c, gw >> 1) + (gw & 1) * 8);
+        v[0] = x[0];
+        v[1] = x[1];
+      } else {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(xat(c, gw));
+        v[0] = x[0];
+        v[1] = x[1];
+        v[2] = x[2];
+        v[3] = x[3];
       }
-      S[i] = sv;
-      dP[i] = dv;
-    }
-    float P[16], dS[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = t0 + lh * 4 + 8 * (i >> 2) + (i & 3);
+      for (int k = 0; k < EP; ++k) {
+        if (c < DS)
+          sv[k] += v[k];
+        else
+          dv[k] += v[k];
+      }
+    }
+    float P[EP], dS[EP];
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+      const int e = gw * EP + k;
+      const int t = t0 + lh * 4 + 8 * (e >> 2) + (e & 3);
       const int lim = t >= p.Tq ? -1 : (up >= 0 ? t + off + up : p.Tk - 1);
       const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
-      float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -L[i] * kLog2e));
+      float pr = __builtin_amdgcn_exp2f(fmaf(sv[k], p.c, -Lc[k] * kLog2e));
       pr = (key <= lim && key >= lo) ? pr : 0.f;
-      P[i] = pr;
-      dS[i] = pr * (dP[i] - Dv[i]);
+      P[k] = pr;
+      dS[k] = pr * (dv[k] - Dc[k]);
     }
-    const bf16x8 pb0 = pack8(P), pb1 = pack8(P + 8);
-    const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+    // written over wave 0's partial of these elements, which only this wave read
+    if constexpr (EP == 2) {
+      *reinterpret_cast<u32x2*>(xat(0, gw >> 1) + (gw & 1) * 8) = u32x2{pack2(P[0], P[1]), pack2(dS[0], dS[1])};
+    } else {
+      *reinterpret_cast<u32x4*>(xat(0, gw)) =
+          u32x4{pack2(P[0], P[1]), pack2(P[2], P[3]), pack2(dS[0], dS[1]), pack2(dS[2], dS[3])};
+    }
+    barrier();
+    // B operand: P for dV, dS for dK, elements 0..15 of this lane as bf16
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 c4 = *reinterpret_cast<const u32x4*>(xat(0, q));
+      if constexpr (EP == 2) {  // {P 4q,4q+1 | dS 4q,4q+1 | P 4q+2,4q+3 | dS 4q+2,4q+3}
+        w[2 * q] = role ? c4[0] : c4[1];
+        w[2 * q + 1] = role ? c4[2] : c4[3];
+      } else {  // {P 4q,4q+1 | P 4q+2,4q+3 | dS 4q,4q+1 | dS 4q+2,4q+3}
+        w[2 * q] = role ? c4[0] : c4[2];
+        w[2 * q + 1] = role ? c4[1] : c4[3];
+      }
+    }
+    const bf16x8 b0 = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
 #pragma unroll
     for (int dt = 0; dt < DTC; ++dt) {
-      av[dt] = mfma32(tr_frag<CP>(ot, 0, cs * DC + dt * 32, lane), pb0, av[dt]);
-      av[dt] = mfma32(tr_frag<CP>(ot, 16, cs * DC + dt * 32, lane), pb1, av[dt]);
-      ak[dt] = mfma32(tr_frag<CP>(qt, 0, cs * DC + dt * 32, lane), db0, ak[dt]);
-      ak[dt] = mfma32(tr_frag<CP>(qt, 16, cs * DC + dt * 32, lane), db1, ak[dt]);
+      acc[dt] = mfma32(tr_frag<CP>(tl, 0, cs * DC + dt * 32, lane), b0, acc[dt]);
+      acc[dt] = mfma32(tr_frag<CP>(tl, 16, cs * DC + dt * 32, lane), b1, acc[dt]);
     }
   }
 
-  // dK^T / dV^T tiles: lane holds key `key`, columns 128 cs + dt*32 + 8*g4 + 4*lh .. +3
+  // dK^T (role 0, scaled) or dV^T (role 1) tile: lane holds key `key`, columns
+  // 128 cs + dt*32 + 8*g4 + 4*lh .. +3
   if (key < p.Tk && p.n_split > 1) {
-    float* pp = p.part + ((int64_t)(sp * n_groups + grp) * p.Tk + key) * (2 * D) + cs * DC;
+    float* pp = p.part + ((int64_t)(sp * n_groups + grp) * p.Tk + key) * (2 * D) + role * D + cs * DC;
 #pragma unroll
     for (int dt = 0; dt < DTC; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = dt * 32 + g4 * 8 + lh * 4;
         *reinterpret_cast<f32x4*>(pp + d) =
-            f32x4{ak[dt][g4 * 4], ak[dt][g4 * 4 + 1], ak[dt][g4 * 4 + 2], ak[dt][g4 * 4 + 3]};
-        *reinterpret_cast<f32x4*>(pp + D + d) =
-            f32x4{av[dt][g4 * 4], av[dt][g4 * 4 + 1], av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3]};
+            f32x4{acc[dt][g4 * 4], acc[dt][g4 * 4 + 1], acc[dt][g4 * 4 + 2], acc[dt][g4 * 4 + 3]};
       }
   } else if (key < p.Tk) {
-    bf16_t* dkp = reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st + cs * DC;
-    bf16_t* dvp = reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st + cs * DC;
+    bf16_t* dst =
+        role ? reinterpret_cast<bf16_t*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_st
+             : reinterpret_cast<bf16_t*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_st;
+    dst += cs * DC;
+    const float m = role ? 1.f : p.scale;
 #pragma unroll
     for (int dt = 0; dt < DTC; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = dt * 32 + g4 * 8 + lh * 4;
-        *reinterpret_cast<u32x2*>(dkp + d) = u32x2{pack2(ak[dt][g4 * 4] * p.scale, ak[dt][g4 * 4 + 1] * p.scale),
-                                                   pack2(ak[dt][g4 * 4 + 2] * p.scale, ak[dt][g4 * 4 + 3] * p.scale)};
-        *reinterpret_cast<u32x2*>(dvp + d) =
-            u32x2{pack2(av[dt][g4 * 4], av[dt][g4 * 4 + 1]), pack2(av[dt][g4 * 4 + 2], av[dt][g4 * 4 + 3])};
+        *reinterpret_cast<u32x2*>(dst + d) = u32x2{pack2(acc[dt][g4 * 4] * m, acc[dt][g4 * 4 + 1] * m),
+                                                   pack2(acc[dt][g4 * 4 + 2] * m, acc[dt][g4 * 4 + 3] * m)};
       }
   }
 }
@@ -1566,7 +1613,7 @@ __global__ void __launch_bounds__(256) bwd_wide_reduce_kernel(const BwdParams p)
 // 256- and 512-wide heads: column-split dK/dV and dQ kernels (4 or 8 waves a workgroup)
 template <int D>
 int launch_bwd_wide(const BwdParams& p, void* stream) {
-  constexpr int NG = D == 512 ? 1 : 2, NW = NG * (D / 128);  // dK/dV
+  constexpr int NG = 512 / D, NW = NG * 2 * (D / 128);          // dK/dV: 8 waves
   constexpr int NGQ = 1024 / D, NWQ = NGQ * (D / 128);        // dQ: 8 waves
   if (p.n_split < 1 || p.n_split > p.g || (p.n_split > 1 && p.part == nullptr)) return (int)hipErrorInvalidValue;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
