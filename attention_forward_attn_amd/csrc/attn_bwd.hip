@@ -1050,12 +1050,16 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
   constexpr int V_OFF = 2 * KT_BYTES, XS_OFF = V_OFF + NVS * KT_BYTES;
   static_assert(XS_OFF + XS_FLOATS * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[XS_OFF + XS_FLOATS * 4];
-  float* const xs = reinterpret_cast<float*>(smem + XS_OFF);
+  constexpr int EP = 16 / DS;                // accumulator elements of every lane a wave reduces
+  constexpr int XW_BYTES = 2 * 4 * 64 * 16;  // one wave's partials: [S | dP][q][lane][4 floats]
+  static_assert(NW * XW_BYTES == XS_FLOATS * 4, "partials area");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
   const int gi = wave / DS, cs = wave % DS;
   const int n_groups = p.B * p.Hkv;
   const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  unsigned char* const xg = smem + XS_OFF + gi * DS * XW_BYTES;  // the group's partials
+  auto xat = [&](int w, int m, int q) { return xg + w * XW_BYTES + ((m * 4 + q) * 64 + lane) * 16; };
   const int rows = p.g * p.Tq;
   const int n_rt = (rows + BM - 1) / BM;
   const int tb = n_rt - 1 - (int)(blockIdx.x / n_groups);  // longest causal tiles first
@@ -1142,33 +1146,72 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
       dP = mfma32(row_frag<CP>(vt, lq, cs * KSC + s, lh), dof[s], dP);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      xs[((wave * 2 + 0) * 16 + i) * 64 + lane] = S[i];
-      xs[((wave * 2 + 1) * 16 + i) * 64 + lane] = dP[i];
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<f32x4*>(xat(cs, 0, q)) = f32x4{S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]};
+      *reinterpret_cast<f32x4*>(xat(cs, 1, q)) = f32x4{dP[4 * q], dP[4 * q + 1], dP[4 * q + 2], dP[4 * q + 3]};
     }
     barrier();
     if constexpr (NVS == 1)  // every wave has its dP partial: the V stage is free
       if (j + 1 < nb) issue_v(j + 1);
+    // this wave's elements (keys) of the lane's row: the partials added in
+    // slice order, then dS, written as bf16 over slice 0's S partial of
+    // those elements (read by this wave only)
+    float sv[EP], dv[EP];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float sv = xs[(((gi * DS) * 2 + 0) * 16 + i) * 64 + lane], dv = xs[(((gi * DS) * 2 + 1) * 16 + i) * 64 + lane];
+    for (int k = 0; k < EP; ++k) sv[k] = dv[k] = 0.f;
 #pragma unroll
-      for (int c = 1; c < DS; ++c) {
-        sv += xs[(((gi * DS + c) * 2 + 0) * 16 + i) * 64 + lane];
-        dv += xs[(((gi * DS + c) * 2 + 1) * 16 + i) * 64 + lane];
+    for (int c = 0; c < DS; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < EP / 4; ++q4) {
+        const f32x4 xsv = *reinterpret_cast<const f32x4*>(xat(c, 0, cs * (EP / 4) + q4));
+        const f32x4 xdv = *reinterpret_cast<const f32x4*>(xat(c, 1, cs * (EP / 4) + q4));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          sv[q4 * 4 + k] += xsv[k];
+          dv[q4 * 4 + k] += xdv[k];
+        }
       }
-      S[i] = sv;
-      dP[i] = dv;
-    }
-    float dS[16];
+    uint32_t dw[EP / 2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = j * BN + lh * 4 + 8 * (i >> 2) + (i & 3);
-      float pr = __builtin_amdgcn_exp2f(fmaf(S[i], p.c, -l2));
-      pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
-      dS[i] = pr * (dP[i] - Dr);
+    for (int k = 0; k < EP; k += 2) {
+      float d2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = cs * EP + k + u;
+        const int kk = j * BN + lh * 4 + 8 * (e >> 2) + (e & 3);
+        float pr = __builtin_amdgcn_exp2f(fmaf(sv[k + u], p.c, -l2));
+        pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
+        d2[u] = pr * (dv[k + u] - Dr);
+      }
+      dw[k / 2] = pack2(d2[0], d2[1]);
     }
-    const bf16x8 db0 = pack8(dS), db1 = pack8(dS + 8);
+    if constexpr (EP == 4) {
+      *reinterpret_cast<u32x2*>(xat(0, 0, cs)) = u32x2{dw[0], dw[1]};
+    } else {
+      *reinterpret_cast<u32x4*>(xat(0, 0, 2 * cs)) = u32x4{dw[0], dw[1], dw[2], dw[3]};
+    }
+    barrier();
+    // dS of elements 0..15 of this lane as bf16 (the B operand)
+    uint32_t w[8];
+    if constexpr (EP == 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 c2 = *reinterpret_cast<const u32x2*>(xat(0, 0, q));
+        w[2 * q] = c2[0];
+        w[2 * q + 1] = c2[1];
+      }
+    } else {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const u32x4 c4 = *reinterpret_cast<const u32x4*>(xat(0, 0, 2 * o));
+        w[4 * o] = c4[0];
+        w[4 * o + 1] = c4[1];
+        w[4 * o + 2] = c4[2];
+        w[4 * o + 3] = c4[3];
+      }
+    }
+    const bf16x8 db0 = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    const bf16x8 db1 = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
 #pragma unroll
     for (int dt = 0; dt < DTC; ++dt) {
       acc[dt] = mfma32(tr_frag<CP>(kt, 0, cs * DC + dt * 32, lane), db0, acc[dt]);
