@@ -327,7 +327,10 @@ int32_t attn_splitkv_choose(const attn_dense_args* a);
  *
  * Gradients are accumulated in fp32 and rounded once to bf16 (dq, dk, dv).
  * No atomics: results are bitwise reproducible. Compiled head dims (d_qk,
- * d_v): (64,64), (128,128), (192,128); others return ATTN_UNSUPPORTED.
+ * d_v): (64,64), (128,128), (192,128), (256,256), (512,512); others return
+ * ATTN_UNSUPPORTED. The dropout mask (keep) is taken for the first three
+ * only; with the 256- and 512-wide heads a non-NULL keep returns
+ * ATTN_UNSUPPORTED.
  */
 typedef struct attn_dense_bwd_args {
   uint32_t struct_size; /* = sizeof(attn_dense_bwd_args) */
@@ -362,12 +365,17 @@ typedef struct attn_dense_bwd_args {
 } attn_dense_bwd_args;
 
 /* Workspace bytes attn_bwd_dense needs: B*H*Tq*4 (the row dots
- * rowsum(dO * O)), rounded up to 256; -1 on invalid sizes, dtype or head
+ * rowsum(dO * O)), rounded up to 256; for the 256- and 512-wide heads, where
+ * the shape gives fewer than 512 dK/dV workgroups (B*Hkv*ceil(Tk/32) at 512,
+ * B*Hkv*ceil(Tk/64) at 256), the query heads of a kv group are split n ways
+ * (n = min(H/Hkv, 16, ceil(768 / that count))) and n*B*Hkv*Tk*(d_qk+d_v)*4
+ * bytes of fp32 dK/dV partials follow (none when n = 1). -1 on invalid sizes, dtype or head
  * dims (pointers are not examined). Host only. */
 int64_t attn_bwd_dense_workspace_bytes(const attn_dense_bwd_args* a);
 
 /* Dense backward: four launches on `stream` (row dots, sink gradients when
- * dsinks != NULL, dK/dV, dQ). `workspace` is caller-owned device memory,
+ * dsinks != NULL, dK/dV, dQ; a fifth that adds the dK/dV partials in a fixed
+ * order when the heads are split, see above). `workspace` is caller-owned device memory,
  * 16-byte aligned, of at least attn_bwd_dense_workspace_bytes(a) bytes; its
  * contents on return are unspecified and calls sharing it must be ordered on
  * one stream. Argument errors (NULL or misaligned pointers, bad strides, a
