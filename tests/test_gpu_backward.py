@@ -128,6 +128,37 @@ def test_bwd_deterministic_and_strided():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d,Hkv", [(512, 1), (256, 2)])
+def test_bwd_wide_deterministic_and_strided(d, Hkv):
+    """256/512-wide heads with the query heads split over workgroups (few key blocks):
+    two calls give identical bits (the partials are added in a fixed order), and BSHD
+    views with padded rows give the same gradients."""
+    announce(f"bwd d{d} Hkv{Hkv} determinism + strided")
+    B, H, T = 1, 16, 300
+    inp = synth.randn_dense(B, H, Hkv, T, T, d, d, dtype="bf16", sinks=True, seed=d + Hkv)
+    dout = synth.randn_dout(B, H, T, d, seed=d + Hkv)
+    a = run_fwd_bwd(inp, dout, causal=True, scale=0.05)
+    b = run_fwd_bwd(inp, dout, causal=True, scale=0.05)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+    def bshd_padded(x):  # [B, N, T, d] -> a view of [B, T, N, d + 8] storage
+        Bx, N, Tx, dx = x.shape
+        store = torch.zeros(Bx, Tx, N, dx + 8, dtype=x.dtype, device="cuda")
+        store[..., :dx] = x.cuda().transpose(1, 2)
+        return store[..., :dx].transpose(1, 2)
+
+    q, k, v = (bshd_padded(inp[n]) for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda()
+    out, lse = A.dense(q, k, v, causal=True, scale=0.05, sinks=sk)
+    r = A.dense_backward(q, k, v, out, bshd_padded(dout), lse, causal=True, scale=0.05, sinks=sk,
+                         dq=bshd_padded(torch.zeros_like(inp["q"])), dk=bshd_padded(torch.zeros_like(inp["k"])),
+                         dv=bshd_padded(torch.zeros_like(inp["v"])))
+    torch.cuda.synchronize()
+    for x, y in zip(a, r):
+        assert torch.equal(x, y)
+
+
 def test_bwd_rejects_bad_arguments():
     inp = synth.randn_dense(1, 4, 2, 8, 8, 128, 128, dtype="bf16", sinks=False, seed=1)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
