@@ -107,6 +107,29 @@ def test_bwd_no_keys():
     assert float(ds.abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("d", [256, 512])
+def test_bwd_wide_empty(d):
+    """256/512-wide heads at the edges: no keys (dq = 0, dsinks = 0), no queries
+    (dk = dv = 0, with the heads split), one query row per head."""
+    announce(f"bwd d{d} empty edges")
+    inp = synth.randn_dense(1, 8, 1, 9, 0, d, d, dtype="bf16", sinks=True, seed=d + 1)
+    dout = synth.randn_dout(1, 8, 9, d, seed=d + 1)
+    dq, dk, dv, ds = run_fwd_bwd(inp, dout, causal=True, scale=0.05)
+    assert float(dq.float().abs().max()) == 0.0 and float(ds.abs().max()) == 0.0
+    q = torch.zeros(1, 8, 0, d, dtype=torch.bfloat16, device="cuda")
+    k = synth.randn_dense(1, 8, 1, 1, 40, d, d, dtype="bf16", sinks=False, seed=3)["k"].cuda()
+    out = torch.zeros_like(q)
+    lse = torch.zeros(1, 8, 0, device="cuda")
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    A.dense_backward(q, k, k, out, out, lse, causal=False, scale=0.05, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert float(dk.float().abs().max()) == 0.0 and float(dv.float().abs().max()) == 0.0
+    inp = synth.randn_dense(1, 8, 1, 1, 70, d, d, dtype="bf16", sinks=True, seed=d + 2)
+    dout = synth.randn_dout(1, 8, 1, d, seed=d + 2)
+    check_bwd(inp, dout, causal=True, scale=1 / math.sqrt(d), label=f"d{d} Tq=1")
+
+
 def test_bwd_deterministic_and_strided():
     """Two calls give identical bits; BSHD views (strided heads and tokens) give the same gradients."""
     announce("bwd determinism + strided")
