@@ -482,8 +482,17 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
   const int cg = wave & 3, half = wave >> 2;  // key columns, query half
   const int n_groups = p.B * p.Hkv;
-  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
-  const int kb0 = (blockIdx.x / n_groups) * BNK;
+  // whole (b, kv head) groups on one XCD where the group count allows it
+  // (workgroups are dealt to the 8 XCDs in turn), key block 0 of every
+  // group first: under a causal mask the first key blocks see the most rows
+  int grp_ = blockIdx.x % n_groups, kbi_ = blockIdx.x / n_groups;
+  if (n_groups % 8 == 0) {
+    const int slot = blockIdx.x / 8, gpx = n_groups / 8;
+    grp_ = (blockIdx.x % 8) * gpx + slot % gpx;
+    kbi_ = slot / gpx;
+  }
+  const int grp = grp_, b = grp / p.Hkv, kvh = grp % p.Hkv;
+  const int kb0 = kbi_ * BNK;
   const int key = kb0 + cg * 32 + lq;
   const uint32_t smem_s = lds_u32(smem);
   const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem);
@@ -511,9 +520,12 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
   const int tb0 = min(t_first / BQ, ntb);
   const int per_head = t_last < t_first ? 0 : max(0, min(ntb, t_last / BQ + 1) - tb0);
   const int n_it = p.g * per_head;
+  // step it: query tile per_head-1-it/g (counted from tb0), head it%g of the
+  // group; the tiles run downwards so that the workgroups of a group, which
+  // share an XCD, read the same tile at about the same time (measured 1.5%)
 
   auto issue = [&](int it) {
-    const int hl = it / per_head, t0 = (tb0 + it % per_head) * BQ;
+    const int hl = it % p.g, t0 = (tb0 + per_head - 1 - it / p.g) * BQ;
     const int h = kvh * p.g + hl;
     const uint32_t st = smem_s + (uint32_t)(KT_BYTES + VT_BYTES + (it & 1) * STAGE);
     dma_tile<CPQ, BQ, NW>(reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh, p.q_st, t0, p.Tq - 1, st,
@@ -553,7 +565,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_pair_kernel(const BwdParams p) {
     const bf16_t* ot = reinterpret_cast<const bf16_t*>(sp + QT_BYTES);
     const float* rl = reinterpret_cast<const float*>(sp + QT_BYTES + OT_BYTES);
     const float* rd = rl + BQ;
-    const int t0 = (tb0 + it % per_head) * BQ;
+    const int t0 = (tb0 + per_head - 1 - it / p.g) * BQ;
     const bool full = t0 + BQ <= p.Tq && kb0 + BNK <= p.Tk && (up < 0 || t0 + off + up >= kb0 + BNK - 1) &&
                       (p.win_left < 0 || t0 + BQ - 1 + off - p.win_left <= kb0);
     const int qs = half;
