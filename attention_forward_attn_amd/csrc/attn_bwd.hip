@@ -850,9 +850,12 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 //     after a barrier every wave reads the B operand it multiplies by (P for
 //     dV, dS for dK). Three workgroup barriers per 32-row step, two waves per
 //     SIMD; the Q and dO tiles are double-buffered through LDS.
-//     dQ: wave (group gi, slice cs) owns columns 128cs.. of 32 folded rows;
-//     S and dP partials are added through LDS in slice order (every wave of
-//     the group then holds the whole S and dP).
+//     dQ: 8 waves, groups of DS; wave (group gi, slice cs) owns columns
+//     128cs.. of the group's 32 folded rows and forms partial S and dP over
+//     them. The same reduce-scatter: wave cs adds the partials of 16/DS of
+//     the elements in slice order, forms dS and writes it as bf16 over slice
+//     0's partial of those elements; after a barrier every wave reads the
+//     whole dS of its rows for dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D, int NG>
 __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(const BwdParams p) {
@@ -1673,7 +1676,7 @@ __global__ void __launch_bounds__(256) bwd_wide_reduce_kernel(const BwdParams p)
   *reinterpret_cast<u32x2*>(dst) = u32x2{pack2(a[0] * m, a[1] * m), pack2(a[2] * m, a[3] * m)};
 }
 
-// 256- and 512-wide heads: column-split dK/dV and dQ kernels (4 or 8 waves a workgroup)
+// 256- and 512-wide heads: column-split dK/dV and dQ kernels (8 waves a workgroup each)
 template <int D>
 int launch_bwd_wide(const BwdParams& p, void* stream) {
   constexpr int NG = 512 / D, NW = NG * 2 * (D / 128);          // dK/dV: 8 waves
