@@ -1020,18 +1020,20 @@ static attn_status validate_qkv(const attn_qkv_args* a) {
 }
 
 struct QkvPlan {
-  int n, keys, n_rt;
+  int n, keys, n_rt, rt;
   int64_t bytes;
 };
 
 static QkvPlan plan_qkv(const attn_qkv_args* a, int n_req) {
-  // a workgroup owns 16 folded query rows of one (b, kv head)
-  QkvPlan pl{1, a->Tk, (int)(((int64_t)(a->H / a->Hkv) * a->Tq + 15) / 16), 0};
+  // a workgroup owns 16 rt folded query rows of one (b, kv head)
+  const int64_t rows = (int64_t)(a->H / a->Hkv) * a->Tq;
+  const int rt = attn::qkv_row_tiles(a->kv_format, a->d, (int)std::min<int64_t>(rows, 1 << 30));
+  QkvPlan pl{1, a->Tk, (int)((rows + 16 * rt - 1) / (16 * rt)), rt, 0};
   const int nblocks = (a->Tk + 31) / 32;
   if (nblocks <= 1 || a->Tq == 0) return pl;
   int want = n_req;
   if (want == 0) {
-    int occ = attn::occupancy_qkv(a->kv_format, a->d);
+    int occ = attn::occupancy_qkv(a->kv_format, a->d, pl.rt);
     if (occ <= 0) occ = 4;
     const int64_t tiles = (int64_t)pl.n_rt * a->B * a->Hkv;
     want = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (int64_t)device_cus() * occ / tiles));
@@ -1096,7 +1098,7 @@ attn_status attn_fwd_dense_qkv(const attn_qkv_args* a, int32_t n_splits, void* w
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)pl.n * a->B * a->H * a->Tq * a->d;
   }
-  int err = attn::launch_qkv(p, a->kv_format, a->d, stream);
+  int err = attn::launch_qkv(p, a->kv_format, a->d, pl.rt, stream);
   if (err != 0)
     return fail(ATTN_HIP_ERROR, "launch of the quantized-cache kernel failed: %s", hipGetErrorString((hipError_t)err));
   const int qp = qkv_path(a->kv_format, a->d);

@@ -196,16 +196,19 @@ struct QkvParams {
   int32_t causal;
   float scale;
   float c;                   // scale * log2(e)
-  int32_t n_rt;              // 16-row tiles per (b, kv head)
+  int32_t n_rt;              // row tiles (16 RT folded rows) per (b, kv head)
   int32_t n_splits, split_keys;
   float* part_o;             // [n_splits][B*H*Tq][d] when n_splits > 1
   float* part_lse;
 };
 
-// 0 or the hipError_t of the launch; -1 when (format, d) is not compiled
-int launch_qkv(const QkvParams& p, int fmt, int d, void* stream);
-// workgroups of the (format, d) kernel resident on one CU (0: unknown)
-int occupancy_qkv(int fmt, int d);
+// 16-row tiles a workgroup of the quantized-cache kernel takes (RT) for
+// `rows` = g * Tq folded rows of a kv head, format fmt and head dim d
+int qkv_row_tiles(int fmt, int d, int rows);
+// 0 or the hipError_t of the launch; -1 when (format, d, rt) is not compiled
+int launch_qkv(const QkvParams& p, int fmt, int d, int rt, void* stream);
+// workgroups of the (format, d, rt) kernel resident on one CU (0: unknown)
+int occupancy_qkv(int fmt, int d, int rt);
 
 // Host-side launchers, one per compiled kernel configuration.
 // Return 0 on success, else the hipError_t of the launch.

@@ -7,8 +7,10 @@
 // loads, instead of converting the whole cache to f16 on every step.
 //
 // A wave owns 16 folded query rows (GQA: the g heads x Tq tokens of one kv
-// head, e.g. 4 heads x 4 tokens of a multi-sequence decode step) and walks
-// 32-key tiles with v_mfma_f32_16x16x32_f16:
+// head, e.g. 4 heads x 4 tokens of a multi-sequence decode step), or two such
+// row tiles where a kv head has more rows (each decoded K block then feeds
+// both tiles' products, so the cache is read and decoded once per 32 rows),
+// and walks 32-key tiles with v_mfma_f32_16x16x32_f16:
 //
 //   raw bytes   each lane loads, straight into registers, the whole blocks it
 //               decodes: block (4i + lane/16) of two keys (lane%16 and
@@ -194,10 +196,11 @@ __device__ __forceinline__ void normalise(const uint32_t (&r)[WIN], uint32_t sh,
 // through LDS (double-buffered, one workgroup barrier per tile, both waves
 // summing in the same order, so they hold identical scores and run identical
 // softmax state).
-template <int FMT, int D, int NW, int CS>
+template <int FMT, int D, int NW, int CS, int RT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW < 4 ? 1 : NW / 4)))
 qkv_decode_kernel(const QkvParams p) {
   constexpr int BN = 32;                   // keys per tile
+  constexpr int RB = 16 * RT;              // folded rows of the workgroup
   constexpr int BB = Blk<FMT>::BB, WIN = Blk<FMT>::WIN;
   constexpr int DC = D / CS;               // columns of one wave
   constexpr int NBK = DC / 32;             // blocks per row in those columns
@@ -207,10 +210,12 @@ qkv_decode_kernel(const QkvParams p) {
   constexpr int CPR = DC / 8;
   constexpr int NP = NW / CS;              // waves (CS = 1) or pairs (CS = 2) taking tiles in turn
   static_assert(NBK % 4 == 0 && NW <= 16 && NW % CS == 0 && (CS == 1 || CS == 2), "shapes");
+  static_assert(CS == 1 || RT == 1, "column pairs hold one row tile");
   // one f16 V tile per wave; after the key loop the same bytes hold the
-  // waves' partial outputs (NW x DT x 64 lanes x 16 bytes, the same size)
-  __shared__ __attribute__((aligned(16))) f16_t vt_all[NW * BN * DC];
-  __shared__ float ml_all[NW][16][2];
+  // waves' partial outputs (NW x RT x DT x 64 lanes x 16 bytes)
+  constexpr int VT_ELEMS = NW * BN * DC, PART_ELEMS = NW * RT * DT * 64 * 8;
+  __shared__ __attribute__((aligned(16))) f16_t vt_all[VT_ELEMS > PART_ELEMS ? VT_ELEMS : PART_ELEMS];
+  __shared__ float ml_all[NW][RB][2];
   // partial scores of the pairs (CS = 2): [tile parity][wave][lane] x 8 floats
   __shared__ __attribute__((aligned(16))) f32x4 xs_all[CS == 2 ? 2 * NW * 64 * 2 : 1];
 
@@ -221,16 +226,22 @@ qkv_decode_kernel(const QkvParams p) {
   const int grp = blockIdx.x / p.n_rt, rt = blockIdx.x % p.n_rt;
   const int b = grp / p.Hkv, kvh = grp % p.Hkv;
   const int rows = p.g * p.Tq;
-  const int f0 = rt * 16, f = f0 + ql;
-  const bool valid = f < rows;
-  const int fc = valid ? f : rows - 1;
-  const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
+  const int f0 = rt * RB;
   const int off = p.Tk - p.Tq;
+  // row tile r: folded row f0 + 16 r + ql of this lane (head and token
+  // recomputed where needed rather than held across the key loop)
+  auto row_of = [&](int r, int& h, int& t) -> bool {
+    const int f = f0 + 16 * r + ql;
+    const int fc = f < rows ? f : rows - 1;
+    h = kvh * p.g + fc / p.Tq;
+    t = fc % p.Tq;
+    return f < rows;
+  };
 
-  // keys the tile's rows can see, then this workgroup's key range
+  // keys the workgroup's rows can see, then this workgroup's key range
   int kend = p.Tk;
   if (p.causal) {
-    const int f_last = min(f0 + 16, rows) - 1;
+    const int f_last = min(f0 + RB, rows) - 1;
     const int t_hi = (f_last / p.Tq != f0 / p.Tq) ? p.Tq - 1 : f_last % p.Tq;
     kend = min(p.Tk, max(0, t_hi + off + 1));
   }
@@ -240,14 +251,23 @@ qkv_decode_kernel(const QkvParams p) {
     k_hi = min(p.Tk, k_lo + p.split_keys);
   }
   kend = max(0, min(kend, k_hi) - k_lo);
-  int row_lim = valid ? (p.causal ? min(p.Tk - 1, t + off) : p.Tk - 1) - k_lo : -1;
-  row_lim = min(row_lim, kend - 1);
+  int row_lim[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int h, t;
+    const bool v = row_of(r, h, t);
+    row_lim[r] = v ? (p.causal ? min(p.Tk - 1, t + off) : p.Tk - 1) - k_lo : -1;
+    row_lim[r] = min(row_lim[r], kend - 1);
+  }
   const int nb = (kend + BN - 1) / BN;
 
-  // q row of this lane as f16, in the permuted contraction order: step s
+  // q rows of this lane as f16, in the permuted contraction order: step s
   // takes values DC cs + 32 (4 (s / 4) + lane/16) + 8 (s % 4) .. + 7
-  f16x8 qf[KS];
-  {
+  f16x8 qf[RT][KS];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int h, t;
+    row_of(r, h, t);
     const uint16_t* qp =
         reinterpret_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st + DC * cs;
 #pragma unroll
@@ -257,7 +277,7 @@ qkv_decode_kernel(const QkvParams p) {
       uint32_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = pack_h2(__uint_as_float(wq[e] << 16), __uint_as_float(wq[e] & 0xffff0000u));
-      qf[s] = __builtin_bit_cast(f16x8, u32x4{o[0], o[1], o[2], o[3]});
+      qf[r][s] = __builtin_bit_cast(f16x8, u32x4{o[0], o[1], o[2], o[3]});
     }
   }
 
@@ -287,10 +307,15 @@ qkv_decode_kernel(const QkvParams p) {
     }
   };
 
-  f32x4 acc[DT];
+  f32x4 acc[RT][DT];
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int r = 0; r < RT; ++r) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
 
   // With CS = 2 every wave runs the same number of iterations (the pair
   // barrier is the workgroup's): iterations past nb do no work.
@@ -303,9 +328,11 @@ qkv_decode_kernel(const QkvParams p) {
     const int j = pr + it * NP;
     const bool live = j < nb;  // always true with CS = 1
     const bool more = j + NP < nb;
-    // S^T for the tile's two 16-key halves, K decoded straight into the A operand
-    f32x4 S[2];
-    S[0] = S[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // S^T for the tile's two 16-key halves and every row tile, K decoded
+    // once straight into the A operand
+    f32x4 S[RT][2];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) S[r][0] = S[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (live) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -315,9 +342,11 @@ qkv_decode_kernel(const QkvParams p) {
           normalise<WIN>(rk[kh][i], sh, n);
           decode_block<FMT>(n, dec);
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            S[kh] = mfma16(__builtin_bit_cast(f16x8, u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]}),
-                           qf[4 * i + c], S[kh]);
+          for (int c = 0; c < 4; ++c) {
+            const f16x8 ka = __builtin_bit_cast(f16x8, u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]});
+#pragma unroll
+            for (int r = 0; r < RT; ++r) S[r][kh] = mfma16(ka, qf[r][4 * i + c], S[r][kh]);
+          }
         }
       }
       if (more) load(kb, kst, j + NP, rk);  // in flight while V is decoded and multiplied
@@ -325,16 +354,16 @@ qkv_decode_kernel(const QkvParams p) {
     if constexpr (CS == 2) {
       // the pair's scores: own half + partner half, always half 0 first
       f32x4* xs = xs_all + (it & 1) * (NW * 64 * 2);
-      xs[(w * 64 + lane) * 2] = S[0];
-      xs[(w * 64 + lane) * 2 + 1] = S[1];
+      xs[(w * 64 + lane) * 2] = S[0][0];
+      xs[(w * 64 + lane) * 2 + 1] = S[0][1];
       __syncthreads();
       const f32x4 o0 = xs[((w ^ 1) * 64 + lane) * 2], o1 = xs[((w ^ 1) * 64 + lane) * 2 + 1];
       if (cs == 0) {
-        S[0] += o0;
-        S[1] += o1;
+        S[0][0] += o0;
+        S[0][1] += o1;
       } else {
-        S[0] = o0 + S[0];
-        S[1] = o1 + S[1];
+        S[0][0] = o0 + S[0][0];
+        S[0][1] = o1 + S[0][1];
       }
     }
     if (!live) continue;
@@ -353,132 +382,160 @@ qkv_decode_kernel(const QkvParams p) {
               u32x4{dec[4 * c], dec[4 * c + 1], dec[4 * c + 2], dec[4 * c + 3]};
       }
     if (more) load(vb, vst, j + NP, rv);
-    // scores of this lane: query ql, keys j*BN + 16 kh + 4 lg + e
+    // scores of this lane: query ql of each row tile, keys j*BN + 16 kh + 4 lg + e
     const int key0 = j * BN;
-    if (key0 + BN - 1 > row_lim) {
+    f16x8 pb[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      if (key0 + BN - 1 > row_lim[r]) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (key0 + 16 * kh + 4 * lg + e > row_lim[r]) S[r][kh][e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(S[r][0][0], S[r][0][1]), fmaxf(S[r][0][2], S[r][0][3])),
+                       fmaxf(fmaxf(S[r][1][0], S[r][1][1]), fmaxf(S[r][1][2], S[r][1][3])));
+      // the running max moves only when a score exceeds it by more than 2^8
+      // (P <= 256 in f16 meanwhile), so the rescale of O is rare
+      const float mnew = fmaxf(m_run[r], groups_max(mx));
+      const bool grow = (mnew - m_run[r]) * p.c > 8.f;  // false when both are -inf
+      if (__any(grow)) {
+        const float alpha =
+            grow ? ((m_run[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[r] - mnew) * p.c)) : 1.f;
+        if (grow) m_run[r] = mnew;
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[r][dt] *= alpha;
+      }
+      const float mc = (m_run[r] == -INFINITY) ? 0.f : m_run[r] * p.c;
+      float P[8];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key0 + 16 * kh + 4 * lg + e > row_lim) S[kh][e] = -INFINITY;
+        for (int e = 0; e < 4; ++e) P[4 * kh + e] = __builtin_amdgcn_exp2f(fmaf(S[r][kh][e], p.c, -mc));
+      l_run[r] += ((P[0] + P[1]) + (P[2] + P[3])) + ((P[4] + P[5]) + (P[6] + P[7]));
+      pb[r] = __builtin_bit_cast(
+          f16x8, u32x4{pack_h2(P[0], P[1]), pack_h2(P[2], P[3]), pack_h2(P[4], P[5]), pack_h2(P[6], P[7])});
     }
-    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-    // the running max moves only when a score exceeds it by more than 2^8
-    // (P <= 256 in f16 meanwhile), so the rescale of O is rare
-    const float mnew = fmaxf(m_run, groups_max(mx));
-    const bool grow = (mnew - m_run) * p.c > 8.f;  // false when both are -inf
-    if (__any(grow)) {
-      const float alpha = grow ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c)) : 1.f;
-      if (grow) m_run = mnew;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
-    float P[8];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) P[4 * kh + e] = __builtin_amdgcn_exp2f(fmaf(S[kh][e], p.c, -mc));
-    l_run += ((P[0] + P[1]) + (P[2] + P[3])) + ((P[4] + P[5]) + (P[6] + P[7]));
-    const f16x8 pb = __builtin_bit_cast(
-        f16x8, u32x4{pack_h2(P[0], P[1]), pack_h2(P[2], P[3]), pack_h2(P[4], P[5]), pack_h2(P[6], P[7])});
     lds_order();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16(v_frag<CPR>(vt, dt * 16, lane), pb, acc[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const f16x8 va = v_frag<CPR>(vt, dt * 16, lane);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r][dt] = mfma16(va, pb[r], acc[r][dt]);
+    }
   }
 
-  // merge the waves (pairs) over the key range: lane holds query ql, columns
-  // DC cs + dt*16 + 4 lg .. +3; wave (pr, cs) finishes the output tiles
-  // dt = pr, pr + NP, ... of its column half. The two waves of a pair hold
-  // the same row state.
-  const float l_w = groups_sum(l_run);
-  float M = m_run, L = l_w;
+  // merge the waves (pairs) over the key range: lane holds query ql of each
+  // row tile, columns DC cs + dt*16 + 4 lg .. +3; wave (pr, cs) finishes the
+  // output tiles dt = pr, pr + NP, ... of its column half for every row
+  // tile. The two waves of a pair hold the same row state.
+  float M[RT], L[RT];
   constexpr int DW = (DT + NP - 1) / NP;
-  float fac[NP];
-  f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][DT][64]
+  float fac[RT][NP];
+  f32x4* part = reinterpret_cast<f32x4*>(vt_all);  // [NW][RT][DT][64]
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    M[r] = m_run[r];
+    L[r] = groups_sum(l_run[r]);
+  }
   if constexpr (NP > 1) {
     __syncthreads();  // every wave is done with its V tile
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) part[(w * DT + dt) * 64 + lane] = acc[dt];
-    if (lg == 0) {
-      ml_all[w][ql][0] = m_run;
-      ml_all[w][ql][1] = l_w;
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) part[((w * RT + r) * DT + dt) * 64 + lane] = acc[r][dt];
+      if (lg == 0) {
+        ml_all[w][16 * r + ql][0] = m_run[r];
+        ml_all[w][16 * r + ql][1] = L[r];
+      }
     }
     __syncthreads();
-    M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NP; ++u) M = fmaxf(M, ml_all[u * CS + cs][ql][0]);
-    L = 0.f;
+    for (int r = 0; r < RT; ++r) {
+      float Mr = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const float mu = ml_all[u * CS + cs][ql][0];
-      fac[u] = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mu - M) * p.c);
-      L += fac[u] * ml_all[u * CS + cs][ql][1];
+      for (int u = 0; u < NP; ++u) Mr = fmaxf(Mr, ml_all[u * CS + cs][16 * r + ql][0]);
+      float Lr = 0.f;
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const float mu = ml_all[u * CS + cs][16 * r + ql][0];
+        fac[r][u] = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mu - Mr) * p.c);
+        Lr += fac[r][u] * ml_all[u * CS + cs][16 * r + ql][1];
+      }
+      M[r] = Mr;
+      L[r] = Lr;
     }
   }
-  // the x-th output tile of this wave, unnormalised
-  auto tile_sum = [&](int x) -> f32x4 {
+  // the x-th output tile of this wave for row tile r, unnormalised
+  auto tile_sum = [&](int r, int x) -> f32x4 {
     if constexpr (NP == 1) {
-      return acc[x];
+      return acc[r][x];
     } else {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NP; ++u) s += fac[u] * part[((u * CS + cs) * DT + pr + x * NP) * 64 + lane];
+      for (int u = 0; u < NP; ++u) s += fac[r][u] * part[(((u * CS + cs) * RT + r) * DT + pr + x * NP) * 64 + lane];
       return s;
     }
   };
 
-  const float ms = (M == -INFINITY) ? -INFINITY : M * p.scale;
-  if (!valid) return;
-  const int64_t l_off = ((int64_t)b * p.H + h) * p.Tq + t;
-  if (p.n_splits > 1) {
-    const float pinv = L > 0.f ? 1.f / L : 0.f;
-    const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
-    float* po = p.part_o + prow * D + DC * cs;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int h, t;
+    if (!row_of(r, h, t)) continue;
+    const float ms = (M[r] == -INFINITY) ? -INFINITY : M[r] * p.scale;
+    const int64_t l_off = ((int64_t)b * p.H + h) * p.Tq + t;
+    if (p.n_splits > 1) {
+      const float pinv = L[r] > 0.f ? 1.f / L[r] : 0.f;
+      const int64_t prow = (int64_t)blockIdx.y * ((int64_t)p.B * p.H * p.Tq) + l_off;
+      float* po = p.part_o + prow * D + DC * cs;
+#pragma unroll
+      for (int x = 0; x < DW; ++x) {
+        if (NP > 1 && pr + x * NP >= DT) break;
+        *reinterpret_cast<f32x4*>(po + (pr + x * NP) * 16 + 4 * lg) = tile_sum(r, x) * pinv;
+      }
+      if (lg == 0 && w == 0) p.part_lse[prow] = L[r] > 0.f ? ms + __builtin_amdgcn_logf(L[r]) * kLn2 : -INFINITY;
+      continue;
+    }
+    float inv, lse;
+    if (p.sinks != nullptr) {
+      const float sk = p.sinks[h];
+      const float Mx = fmaxf(ms, sk);
+      if (Mx == -INFINITY) {
+        inv = 0.f;
+        lse = -INFINITY;
+      } else {
+        const float fa = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - Mx) * kLog2e);
+        const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - Mx) * kLog2e);
+        const float den = L[r] * fa + es;
+        inv = den > 0.f ? fa / den : 0.f;
+        lse = den > 0.f ? Mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
+      }
+    } else {
+      inv = L[r] > 0.f ? 1.f / L[r] : 0.f;
+      lse = L[r] > 0.f ? ms + __builtin_amdgcn_logf(L[r]) * kLn2 : -INFINITY;
+    }
+    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st + DC * cs;
 #pragma unroll
     for (int x = 0; x < DW; ++x) {
       if (NP > 1 && pr + x * NP >= DT) break;
-      *reinterpret_cast<f32x4*>(po + (pr + x * NP) * 16 + 4 * lg) = tile_sum(x) * pinv;
+      const f32x4 o = tile_sum(r, x);
+      *reinterpret_cast<u32x2*>(ob + (pr + x * NP) * 16 + 4 * lg) =
+          u32x2{pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv)};
     }
-    if (lg == 0 && w == 0) p.part_lse[prow] = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
-    return;
+    if (lg == 0 && w == 0) p.lse[l_off] = lse;
   }
-  float inv, lse;
-  if (p.sinks != nullptr) {
-    const float sk = p.sinks[h];
-    const float Mx = fmaxf(ms, sk);
-    if (Mx == -INFINITY) {
-      inv = 0.f;
-      lse = -INFINITY;
-    } else {
-      const float fa = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - Mx) * kLog2e);
-      const float es = (sk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sk - Mx) * kLog2e);
-      const float den = L * fa + es;
-      inv = den > 0.f ? fa / den : 0.f;
-      lse = den > 0.f ? Mx + __builtin_amdgcn_logf(den) * kLn2 : -INFINITY;
-    }
-  } else {
-    inv = L > 0.f ? 1.f / L : 0.f;
-    lse = L > 0.f ? ms + __builtin_amdgcn_logf(L) * kLn2 : -INFINITY;
-  }
-  uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st + DC * cs;
-#pragma unroll
-  for (int x = 0; x < DW; ++x) {
-    if (NP > 1 && pr + x * NP >= DT) break;
-    const f32x4 o = tile_sum(x);
-    *reinterpret_cast<u32x2*>(ob + (pr + x * NP) * 16 + 4 * lg) =
-        u32x2{pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv)};
-  }
-  if (lg == 0 && w == 0) p.lse[l_off] = lse;
 }
 
-// waves per workgroup: every wave a CU can hold (three or four per SIMD at
-// d 128, two at d 256), so one workgroup per CU covers the longest key range
-template <int FMT, int D>
+// waves per workgroup: every wave a CU can hold (three per SIMD at d 128, two
+// at d 256), so one workgroup per CU covers the longest key range; with more
+// row tiles a wave holds more accumulators and fewer waves fit
+template <int FMT, int D, int RT>
 constexpr int waves_of() {
-  return D == 128 ? (FMT == kFmtQ8 ? 12 : 16) : (D == 256 ? 8 : 6);
+  if constexpr (D == 128) return RT == 1 ? 12 : 8;
+  else if constexpr (D == 256) return RT == 1 ? 8 : 4;
+  else return 6;
 }
 
 // column halves per wave pair: 512-wide heads split their columns over two waves
@@ -487,46 +544,81 @@ constexpr int cs_of() {
   return D == 512 ? 2 : 1;
 }
 
-template <int FMT, int D>
+template <int FMT, int D, int RT>
 int launch_cfg(const QkvParams& p, void* stream) {
-  constexpr int NW = waves_of<FMT, D>();
-  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, NW, cs_of<D>()>), dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1),
-                     dim3(64 * NW), 0, reinterpret_cast<hipStream_t>(stream), p);
+  constexpr int NW = waves_of<FMT, D, RT>();
+  hipLaunchKernelGGL((qkv_decode_kernel<FMT, D, NW, cs_of<D>(), RT>),
+                     dim3(p.n_rt * p.B * p.Hkv, p.n_splits > 1 ? p.n_splits : 1), dim3(64 * NW), 0,
+                     reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
-template <int FMT, int D>
+template <int FMT, int D, int RT>
 int occ_cfg() {
   int n = 0;
+  constexpr int NW = waves_of<FMT, D, RT>();
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, waves_of<FMT, D>(), cs_of<D>()>),
-          64 * waves_of<FMT, D>(),
-          0) != hipSuccess) {
+          &n, reinterpret_cast<const void*>(&qkv_decode_kernel<FMT, D, NW, cs_of<D>(), RT>), 64 * NW, 0) !=
+      hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
   return n;
 }
 
+template <int FMT, int D>
+int launch_rt(const QkvParams& p, int rt, void* stream) {
+  if constexpr (D == 512) {
+    return rt == 1 ? launch_cfg<FMT, D, 1>(p, stream) : -1;
+  } else {
+    if (rt == 1) return launch_cfg<FMT, D, 1>(p, stream);
+    if constexpr (D == 128 || FMT == kFmtQ4)
+      if (rt == 2) return launch_cfg<FMT, D, 2>(p, stream);
+    return -1;
+  }
+}
+
+template <int FMT, int D>
+int occ_rt(int rt) {
+  if constexpr (D == 512) {
+    return rt == 1 ? occ_cfg<FMT, D, 1>() : 0;
+  } else {
+    if (rt == 1) return occ_cfg<FMT, D, 1>();
+    if constexpr (D == 128 || FMT == kFmtQ4)
+      if (rt == 2) return occ_cfg<FMT, D, 2>();
+    return 0;
+  }
+}
+
 }  // namespace
 
-int launch_qkv(const QkvParams& p, int fmt, int d, void* stream) {
-  if (fmt == kFmtQ8 && d == 128) return launch_cfg<kFmtQ8, 128>(p, stream);
-  if (fmt == kFmtQ4 && d == 128) return launch_cfg<kFmtQ4, 128>(p, stream);
-  if (fmt == kFmtQ8 && d == 256) return launch_cfg<kFmtQ8, 256>(p, stream);
-  if (fmt == kFmtQ4 && d == 256) return launch_cfg<kFmtQ4, 256>(p, stream);
-  if (fmt == kFmtQ8 && d == 512) return launch_cfg<kFmtQ8, 512>(p, stream);
-  if (fmt == kFmtQ4 && d == 512) return launch_cfg<kFmtQ4, 512>(p, stream);
+int qkv_row_tiles(int fmt, int d, int rows) {
+  // two row tiles (8 waves, two per SIMD) where a kv head has more than 16
+  // folded rows; four (4 waves, one per SIMD) measured slower on long caches.
+  // q8_0's wider raw blocks leave no room for two at d 256, the column pairs
+  // of d 512 none at all
+  if (d == 512 || rows <= 16) return 1;
+  if (d == 256 && fmt != kFmtQ4) return 1;
+  return 2;
+}
+
+int launch_qkv(const QkvParams& p, int fmt, int d, int rt, void* stream) {
+  if (fmt == kFmtQ8 && d == 128) return launch_rt<kFmtQ8, 128>(p, rt, stream);
+  if (fmt == kFmtQ4 && d == 128) return launch_rt<kFmtQ4, 128>(p, rt, stream);
+  if (fmt == kFmtQ8 && d == 256) return launch_rt<kFmtQ8, 256>(p, rt, stream);
+  if (fmt == kFmtQ4 && d == 256) return launch_rt<kFmtQ4, 256>(p, rt, stream);
+  if (fmt == kFmtQ8 && d == 512) return launch_rt<kFmtQ8, 512>(p, rt, stream);
+  if (fmt == kFmtQ4 && d == 512) return launch_rt<kFmtQ4, 512>(p, rt, stream);
   return -1;
 }
 
-int occupancy_qkv(int fmt, int d) {
-  if (fmt == kFmtQ8 && d == 128) return occ_cfg<kFmtQ8, 128>();
-  if (fmt == kFmtQ4 && d == 128) return occ_cfg<kFmtQ4, 128>();
-  if (fmt == kFmtQ8 && d == 256) return occ_cfg<kFmtQ8, 256>();
-  if (fmt == kFmtQ4 && d == 256) return occ_cfg<kFmtQ4, 256>();
-  if (fmt == kFmtQ8 && d == 512) return occ_cfg<kFmtQ8, 512>();
-  if (fmt == kFmtQ4 && d == 512) return occ_cfg<kFmtQ4, 512>();
+int occupancy_qkv(int fmt, int d, int rt) {
+  if (fmt == kFmtQ8 && d == 128) return occ_rt<kFmtQ8, 128>(rt);
+  if (fmt == kFmtQ4 && d == 128) return occ_rt<kFmtQ4, 128>(rt);
+  if (fmt == kFmtQ8 && d == 256) return occ_rt<kFmtQ8, 256>(rt);
+  if (fmt == kFmtQ4 && d == 256) return occ_rt<kFmtQ4, 256>(rt);
+  if (fmt == kFmtQ8 && d == 512) return occ_rt<kFmtQ8, 512>(rt);
+  if (fmt == kFmtQ4 && d == 512) return occ_rt<kFmtQ4, 512>(rt);
   return 0;
 }
 

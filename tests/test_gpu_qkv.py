@@ -46,6 +46,9 @@ CASES = [
     (1, 2, 1, 40, 30, True, False, 0),        # Tq > Tk: rows that see no key
     (3, 4, 2, 3, 33, True, True, 100),        # more ranges asked than key blocks
     (1, 8, 2, 1, 6000, True, True, 70),       # many ranges: several merge batches
+    (2, 64, 1, 1, 700, True, True, 0),        # MQA decode: 64 rows of one kv head, one workgroup's tiles
+    (1, 32, 1, 1, 500, True, False, 3),       # 32 rows: two row tiles
+    (1, 8, 1, 5, 300, True, False, 0),        # 40 rows: a partly filled row tile, one empty
 ]
 
 
