@@ -656,9 +656,11 @@ static attn_status validate_bwd_shape(const attn_dense_bwd_args* a) {
     return fail(ATTN_INVALID_ARGUMENT, "window bounds must be >= -1 (-1: unbounded)");
   if (bwd_path(a->d_qk, a->d_v) < 0)
     return fail(ATTN_UNSUPPORTED, "no compiled dense backward for (d_qk, d_v) = (%d, %d)", a->d_qk, a->d_v);
-  // one-dimensional grids: (key blocks or row tiles) x B x Hkv workgroups
+  // one-dimensional grids: (key blocks or row tiles) x B x Hkv workgroups;
+  // counted with the smallest blocks of any path (32 keys, up to 16 head
+  // splits; 32 folded rows)
   const int64_t groups = (int64_t)a->B * a->Hkv;
-  const int64_t tiles = std::max<int64_t>((a->Tk + 127) / 128, ((int64_t)(a->H / a->Hkv) * a->Tq + 127) / 128);
+  const int64_t tiles = std::max<int64_t>((a->Tk + 31) / 32 * 16, ((int64_t)(a->H / a->Hkv) * a->Tq + 31) / 32);
   if (groups * tiles > 0x7fffffff) return fail(ATTN_UNSUPPORTED, "problem too large for one launch");
   return ATTN_OK;
 }
