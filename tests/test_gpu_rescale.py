@@ -120,9 +120,12 @@ def test_sparse_rescale(Sq, N, topk, mode):
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
 @pytest.mark.parametrize("d", [128, 256, 512])
-def test_qkv_rescale(d, fmt, mode):
-    inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, d, fmt, mode, sinks=True, seed=77)
-    label = f"qkv {fmt} d{d} {mode}"
+@pytest.mark.parametrize("shape", [(2, 8, 2, 3, 1500), (1, 32, 1, 2, 1500)], ids=["gqa12rows", "mqa64rows"])
+def test_qkv_rescale(d, fmt, mode, shape):
+    # 12 folded rows a kv head: one 16-row tile; 64: two tiles a wave at d 128 (and q4_0 at d 256)
+    B, H, Hkv, Tq, Tk = shape
+    inp = synth.widen_quant_kv(B, H, Hkv, Tq, Tk, d, fmt, mode, sinks=True, seed=77)
+    label = f"qkv {fmt} d{d} {mode} {shape}"
     announce(label)
     q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
     out, lse = A.dense_qkv(q, k, v, fmt=fmt, causal=True, sinks=inp["sinks"].cuda())

@@ -100,8 +100,10 @@ def test_sparse_inputs_move_the_maximum(mode):
 
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
-def test_quantized_inputs_move_the_maximum(fmt, mode):
-    inp = synth.widen_quant_kv(2, 8, 2, 3, 1500, 128, fmt, mode, sinks=True, seed=77)
+@pytest.mark.parametrize("shape", [(2, 8, 2, 3, 1500), (1, 32, 1, 2, 1500)], ids=["gqa12rows", "mqa64rows"])
+def test_quantized_inputs_move_the_maximum(fmt, mode, shape):
+    B, H, Hkv, Tq, Tk = shape
+    inp = synth.widen_quant_kv(B, H, Hkv, Tq, Tk, 128, fmt, mode, sinks=True, seed=77)
     kd = oracle.dequantize_rows(inp["k"], fmt)
     S2 = dense_scores(_f64(inp["q"]), kd, 1 / math.sqrt(128), True)
     _assert_fires(S2, f"qkv {fmt} {mode}", 0.9 if mode != "qx16" else 0.05)
