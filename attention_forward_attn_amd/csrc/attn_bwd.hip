@@ -17,7 +17,8 @@
 // GQA/MQA: the keys of kv head kvh are read by the g query heads kvh*g ..
 // kvh*g + g-1 (kv-major), so dK and dV sum over those heads.
 //
-// Four launches, none with atomics (the result does not depend on timing):
+// Four launches (five with a head split), none with atomics (the result does
+// not depend on timing):
 //
 //  1. bwd_dot_kernel   D for every row, several rows per wave.
 //  2. bwd_dsink_kernel one workgroup per head sums its rows' sink terms.
@@ -33,7 +34,14 @@
 //                      while K and V blocks stream through LDS; S^T and dP^T
 //                      are recomputed and dQ^T += K^T dS^T.
 //
-// Scores and probabilities never leave the CU; the only workspace is D.
+// (Steps 3 and 4 for 64/128-wide heads: bwd_dkdv_pair_kernel, K and V in LDS
+// and two waves per SIMD; for 256/512-wide heads: bwd_dkdv_wide_kernel and
+// bwd_dq_wide_kernel, the columns split over waves whose partial products
+// meet in LDS, see section 4b.)
+//
+// Scores and probabilities never leave the CU; the workspace holds D and, for
+// 256/512-wide heads with few key blocks, fp32 dK/dV partials of head splits
+// that a fifth kernel (bwd_wide_reduce_kernel) adds in a fixed order.
 //
 // The file also holds the kernels built on the same tile helpers (row and
 // transposed fragment reads, DMA tile loads):
