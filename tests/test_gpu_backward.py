@@ -278,3 +278,50 @@ def test_bwd_window(case):
     assert max(errs.values()) <= TOL_REL, f"{case}: {errs}"
     if rs is not None:
         assert _rel_err(_np(ds), rs) <= TOL_SINK
+
+
+# ------------------------------------------------------------------ seeded random sweep
+def _bwd_sweep_cases(n, seed):
+    """Shapes drawn at random (seeded) over every compiled head-dim pair: GQA group
+    (up to 16 heads a kv head, so the 256/512-wide kernels split heads), lengths
+    with ragged tails, Tq != Tk, causal / sink / window switches."""
+    rng = np.random.default_rng(seed)
+    dims = [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]
+    cases = []
+    for i in range(n):
+        dqk, dv = dims[i % len(dims)]
+        Hkv = int(rng.integers(1, 3))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        Tq = int(rng.integers(1, 260))
+        Tk = Tq if rng.random() < 0.5 else int(rng.integers(1, 260))
+        causal = bool(rng.random() < 0.7)
+        win = (-1, -1)
+        if rng.random() < 0.3:
+            win = (int(rng.integers(0, 80)), -1 if causal else int(rng.integers(0, 80)))
+        cases.append(dict(B=int(rng.integers(1, 3)), H=g * Hkv, Hkv=Hkv, Tq=Tq, Tk=Tk, dqk=dqk, dv=dv, causal=causal,
+                          sinks=bool(rng.random() < 0.4), window=win, seed=2000 * seed + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _bwd_sweep_cases(15, 11), ids=lambda c: (
+    f"B{c['B']}H{c['H']}/{c['Hkv']}T{c['Tq']}x{c['Tk']}d{c['dqk']}/{c['dv']}"
+    f"{'c' if c['causal'] else 'n'}{'s' if c['sinks'] else ''}w{c['window'][0]}_{c['window'][1]}"))
+def test_bwd_random_sweep(case):
+    c = case
+    announce(f"bwd sweep {c}")
+    inp = synth.randn_dense(c["B"], c["H"], c["Hkv"], c["Tq"], c["Tk"], c["dqk"], c["dv"], dtype="bf16",
+                            sinks=c["sinks"], seed=c["seed"])
+    dout = synth.randn_dout(c["B"], c["H"], c["Tq"], c["dv"], seed=c["seed"])
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
+    scale = 1 / math.sqrt(c["dqk"])
+    out, lse = A.dense(q, k, v, causal=c["causal"], scale=scale, sinks=sk, window=c["window"])
+    dq, dk, dv_, ds = A.dense_backward(q, k, v, out, dout.cuda(), lse, causal=c["causal"], scale=scale, sinks=sk,
+                                       window=c["window"])
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = oracle.dense_attention_backward(inp["q"], inp["k"], inp["v"], dout, scale=scale,
+                                                     causal=c["causal"], sinks=inp["sinks"], window=c["window"])
+    errs = {"dq": _rel_err(_np(dq), rq), "dk": _rel_err(_np(dk), rk), "dv": _rel_err(_np(dv_), rv)}
+    assert max(errs.values()) <= TOL_REL, f"{c}: {errs}"
+    if rs is not None:
+        assert _rel_err(_np(ds), rs) <= TOL_SINK, f"{c}: dsinks"
