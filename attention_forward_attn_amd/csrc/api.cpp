@@ -121,7 +121,8 @@ template <class Args>
 static attn_status validate_keep(const Args* a, int Tq, int Tk) {
   if (!a->keep) return ATTN_OK;
   if (a->dtype != ATTN_BF16 || !attn::dropout_supported(a->d_qk, a->d_v))
-    return fail(ATTN_UNSUPPORTED, "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128)}");
+    return fail(ATTN_UNSUPPORTED,
+                "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128), (256,256)}");
   if (!(a->p_drop >= 0.f && a->p_drop < 1.f)) return fail(ATTN_INVALID_ARGUMENT, "p_drop must be in [0, 1)");
   if ((uintptr_t)a->keep & 3u) return fail(ATTN_INVALID_ARGUMENT, "keep must be 4-byte aligned");
   const int64_t nw = ((int64_t)Tk + 31) / 32;

@@ -865,7 +865,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdParams p) {
 //     0's partial of those elements; after a barrier every wave reads the
 //     whole dS of its rows for dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
-template <int D, int NG>
+template <int D, int NG, bool DROP>
 __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(const BwdParams p) {
   constexpr int DS = D / 128, GW = 2 * DS, NW = NG * GW, DC = 128;
   constexpr int EP = 16 / GW;  // accumulator elements of every lane a wave reduces
@@ -927,18 +927,23 @@ __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(
                          st + QT_BYTES, wave, lane);
   };
   // lse and D of the rows of this wave's elements (element e of a lane is
-  // query row lh*4 + 8*(e/4) + e%4 of the tile), clamped to the last row;
-  // loaded one step ahead, before the step's tile loads are issued
+  // query row lh*4 + 8*(e/4) + e%4 of the tile), clamped to the last row, and
+  // with dropout the keep word of each such row that holds the group's 32
+  // keys; loaded one step ahead, before the step's tile loads are issued
   float L[EP], Dv[EP];
+  uint32_t Mw[EP];
+  const int wkey = min((kb0 + gi * 32) / 32, max(p.nwords - 1, 0));
   auto load_rows = [&](int it) {
     const int hl = h_lo + it / per_head, t0 = (tb0 + it % per_head) * BQ;
-    const int64_t rb = ((int64_t)b * p.H + kvh * p.g + hl) * p.Tq;
+    const int h = kvh * p.g + hl;
+    const int64_t rb = ((int64_t)b * p.H + h) * p.Tq;
 #pragma unroll
     for (int k = 0; k < EP; ++k) {
       const int e = gw * EP + k;
       const int t = min(t0 + lh * 4 + 8 * (e >> 2) + (e & 3), p.Tq - 1);
       L[k] = p.lse[rb + t];
       Dv[k] = p.D[rb + t];
+      if constexpr (DROP) Mw[k] = p.keep[b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st + wkey];
     }
   };
 
@@ -950,10 +955,12 @@ __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(
     wait_all_loads();
     barrier();  // tile it has landed everywhere; nobody reads the other stage or the partials any more
     float Lc[EP], Dc[EP];
+    uint32_t Mc[EP];
 #pragma unroll
     for (int k = 0; k < EP; ++k) {
       Lc[k] = L[k];
       Dc[k] = Dv[k];
+      if constexpr (DROP) Mc[k] = Mw[k];
     }
     if (it + 1 < n_it) {
       load_rows(it + 1);
@@ -1006,8 +1013,15 @@ __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(
       const int lo = p.win_left >= 0 ? t + off - p.win_left : 0;
       float pr = __builtin_amdgcn_exp2f(fmaf(sv[k], p.c, -Lc[k] * kLog2e));
       pr = (key <= lim && key >= lo) ? pr : 0.f;
-      P[k] = pr;
-      dS[k] = pr * (dv[k] - Dc[k]);
+      if constexpr (DROP) {
+        // dV takes the dropped probabilities; dS = P (Z dP - D)
+        const float z = ((Mc[k] >> lq) & 1u) ? p.inv_keep : 0.f;
+        P[k] = pr * z;
+        dS[k] = pr * (z * dv[k] - Dc[k]);
+      } else {
+        P[k] = pr;
+        dS[k] = pr * (dv[k] - Dc[k]);
+      }
     }
     // written over wave 0's partial of these elements, which only this wave read
     if constexpr (EP == 2) {
@@ -1068,7 +1082,7 @@ __global__ void __launch_bounds__(NG * 2 * (D / 128) * 64) bwd_dkdv_wide_kernel(
   }
 }
 
-template <int D, int NG>
+template <int D, int NG, bool DROP>
 __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const BwdParams p) {
   constexpr int DS = D / 128, NW = NG * DS, DC = 128;
   constexpr int BM = 32 * NG, BN = 32;
@@ -1150,6 +1164,14 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
+  // dropout: the keep word of this lane's row for key block j (32 keys),
+  // loaded a block ahead so that its wait falls where the block's tiles are
+  // waited for
+  const uint32_t* mrow = DROP ? p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st : nullptr;
+  uint32_t mw = 0u;
+  if constexpr (DROP) {
+    if (nb > jb0) mw = jb0 < p.nwords ? mrow[jb0] : 0u;
+  }
   if (nb > jb0) {
     issue_k(jb0);
     issue_v(jb0);
@@ -1212,9 +1234,17 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
         const int kk = j * BN + lh * 4 + 8 * (e >> 2) + (e & 3);
         float pr = __builtin_amdgcn_exp2f(fmaf(sv[k + u], p.c, -l2));
         pr = (kk <= row_lim && kk >= row_lo) ? pr : 0.f;
-        d2[u] = pr * (dv[k + u] - Dr);
+        if constexpr (DROP) {
+          const float z = ((mw >> (lh * 4 + 8 * (e >> 2) + (e & 3))) & 1u) ? p.inv_keep : 0.f;
+          d2[u] = pr * (z * dv[k + u] - Dr);
+        } else {
+          d2[u] = pr * (dv[k + u] - Dr);
+        }
       }
       dw[k / 2] = pack2(d2[0], d2[1]);
+    }
+    if constexpr (DROP) {
+      if (j + 1 < nb) mw = j + 1 < p.nwords ? mrow[j + 1] : 0u;
     }
     if constexpr (EP == 4) {
       *reinterpret_cast<u32x2*>(xat(0, 0, cs)) = u32x2{dw[0], dw[1]};
@@ -1685,7 +1715,7 @@ __global__ void __launch_bounds__(256) bwd_wide_reduce_kernel(const BwdParams p)
 }
 
 // 256- and 512-wide heads: column-split dK/dV and dQ kernels (8 waves a workgroup each)
-template <int D>
+template <int D, bool DROP>
 int launch_bwd_wide(const BwdParams& p, void* stream) {
   constexpr int NG = 512 / D, NW = NG * 2 * (D / 128);          // dK/dV: 8 waves
   constexpr int NGQ = 1024 / D, NWQ = NGQ * (D / 128);        // dQ: 8 waves
@@ -1703,8 +1733,8 @@ int launch_bwd_wide(const BwdParams& p, void* stream) {
   }
   if (p.Tk > 0) {
     const int nkb = (p.Tk + 32 * NG - 1) / (32 * NG);
-    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, NG>), dim3(nkb * p.n_split * p.B * p.Hkv), dim3(NW * 64), 0, st,
-                       p);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<D, NG, DROP>), dim3(nkb * p.n_split * p.B * p.Hkv), dim3(NW * 64), 0,
+                       st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
     if (p.n_split > 1) {
       const int64_t units = (int64_t)p.B * p.Hkv * p.Tk * (2 * D / 4);
@@ -1715,7 +1745,7 @@ int launch_bwd_wide(const BwdParams& p, void* stream) {
   if (p.Tq > 0) {
     const int rows = p.g * p.Tq;
     const int nrt = (rows + 32 * NGQ - 1) / (32 * NGQ);
-    hipLaunchKernelGGL((bwd_dq_wide_kernel<D, NGQ>), dim3(nrt * p.B * p.Hkv), dim3(NWQ * 64), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_wide_kernel<D, NGQ, DROP>), dim3(nrt * p.B * p.Hkv), dim3(NWQ * 64), 0, st, p);
     if (hipPeekAtLastError() != hipSuccess) return (int)hipGetLastError();
   }
   return 0;
@@ -2105,7 +2135,8 @@ bool bwd_supported(int d_qk, int d_v) {
 }
 
 bool dropout_supported(int d_qk, int d_v) {
-  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128) ||
+         (d_qk == 256 && d_v == 256);
 }
 
 int bwd_head_splits(int B, int Hkv, int g, int Tk, int d_qk, int d_v) {
@@ -2126,10 +2157,10 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream) {
     return drop ? launch_bwd_cfg<128, 128, true>(p, stream) : launch_bwd_cfg<128, 128, false>(p, stream);
   if (d_qk == 192 && d_v == 128)
     return drop ? launch_bwd_cfg<192, 128, true>(p, stream) : launch_bwd_cfg<192, 128, false>(p, stream);
-  if (drop) return -1;  // no dropout kernels for the wide heads
-  if (d_qk == 256 && d_v == 256) return launch_bwd_wide<256>(p, stream);
-  if (d_qk == 512 && d_v == 512) return launch_bwd_wide<512>(p, stream);
-  return -1;
+  if (d_qk == 256 && d_v == 256)
+    return drop ? launch_bwd_wide<256, true>(p, stream) : launch_bwd_wide<256, false>(p, stream);
+  if (d_qk == 512 && d_v == 512 && !drop) return launch_bwd_wide<512, false>(p, stream);
+  return -1;  // no dropout kernels for 512-wide heads
 }
 
 int launch_bwd_sparse(const BwdParams& p, void* stream) {
@@ -2179,6 +2210,8 @@ int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream) {
     hipLaunchKernelGGL((fwd_dropout_kernel<128, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
   else if (d_qk == 192 && d_v == 128)
     hipLaunchKernelGGL((fwd_dropout_kernel<192, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  else if (d_qk == 256 && d_v == 256)
+    hipLaunchKernelGGL((fwd_dropout_kernel<256, 256>), dim3((unsigned)grid), dim3(256), 0, st, p);
   else
     return -1;
   return (int)hipGetLastError();
