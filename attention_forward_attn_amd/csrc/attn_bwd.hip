@@ -1307,7 +1307,7 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <int DQK, int DV>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQK + DV > 320 ? 1 : 2)))
 fwd_dropout_kernel(const BwdParams p) {
   constexpr int NW = 4, BN = 64, BM = 32 * NW;
   constexpr int CPK = DQK / 8, CPV = DV / 8;
