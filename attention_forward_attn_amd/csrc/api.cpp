@@ -122,7 +122,7 @@ static attn_status validate_keep(const Args* a, int Tq, int Tk) {
   if (!a->keep) return ATTN_OK;
   if (a->dtype != ATTN_BF16 || !attn::dropout_supported(a->d_qk, a->d_v))
     return fail(ATTN_UNSUPPORTED,
-                "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128), (256,256)}");
+                "dropout is compiled for bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128), (256,256), (512,512)}");
   if (!(a->p_drop >= 0.f && a->p_drop < 1.f)) return fail(ATTN_INVALID_ARGUMENT, "p_drop must be in [0, 1)");
   if ((uintptr_t)a->keep & 3u) return fail(ATTN_INVALID_ARGUMENT, "keep must be 4-byte aligned");
   const int64_t nw = ((int64_t)Tk + 31) / 32;
@@ -540,7 +540,15 @@ attn_status attn_fwd_dense(const attn_dense_args* a, void* stream) {
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
   if (a->Tq == 0) return ATTN_OK;
-  if (dp.drop) return launch_dropout(a, stream);
+  if (dp.drop) {
+    // 512-wide heads: the plain forward gives lse (the dropout leaves it as it
+    // is), then a second pass forms the dropped output from it
+    if (a->d_qk == 512) {
+      s = do_launch(dp, stream);
+      if (s != ATTN_OK) return s;
+    }
+    return launch_dropout(a, stream);
+  }
   return do_launch(dp, stream);
 }
 

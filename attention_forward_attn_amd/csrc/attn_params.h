@@ -136,7 +136,7 @@ int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream);
 // (d_qk, d_v) pairs with a compiled backward
 bool bwd_supported(int d_qk, int d_v);
-// dropout (forward and backward) is compiled for (64,64), (128,128), (192,128), (256,256)
+// dropout (forward and backward) is compiled for the backward's head dims
 bool dropout_supported(int d_qk, int d_v);
 // how many ways the 256/512-wide dK/dV kernel splits a kv group's query heads
 // (1 for the other widths); the workspace holds the partials when it is > 1

@@ -126,9 +126,11 @@ typedef enum attn_dtype {
  *        attn_bwd_dense, so the two directions cannot disagree on it (the
  *        TransformerEngine pull request 3259 review flags a backward that
  *        lost the forward's dropout state). bf16 with head dims (64,64),
- *        (128,128), (192,128), (256,256); runs a separate, unfused-grade
- *        kernel (dispatch path "dense_dropout_bf16"); the split-KV, packed,
- *        plan and extra-return calls return ATTN_UNSUPPORTED for it.
+ *        (128,128), (192,128), (256,256), (512,512); runs a separate,
+ *        unfused-grade kernel (dispatch path "dense_dropout_bf16"; for
+ *        (512,512) after the plain forward, whose lse it reads and whose
+ *        output it overwrites); the split-KV, packed, plan and extra-return
+ *        calls return ATTN_UNSUPPORTED for it.
  */
 typedef struct attn_dense_args {
   uint32_t struct_size; /* = sizeof(attn_dense_args) */
@@ -328,8 +330,7 @@ int32_t attn_splitkv_choose(const attn_dense_args* a);
  * Gradients are accumulated in fp32 and rounded once to bf16 (dq, dk, dv).
  * No atomics: results are bitwise reproducible. Compiled head dims (d_qk,
  * d_v): (64,64), (128,128), (192,128), (256,256), (512,512); others return
- * ATTN_UNSUPPORTED. The dropout mask (keep) is taken for all but (512,512),
- * where a non-NULL keep returns ATTN_UNSUPPORTED.
+ * ATTN_UNSUPPORTED. The dropout mask (keep) is taken for all of them.
  */
 typedef struct attn_dense_bwd_args {
   uint32_t struct_size; /* = sizeof(attn_dense_bwd_args) */

@@ -30,6 +30,8 @@ CASES = [
     (1, 4, 2, 257, 257, 128, 128, True, False, (50, -1)),    # sliding window
     (1, 8, 2, 150, 190, 256, 256, True, True, (-1, -1)),     # 256-wide heads (dK/dV heads split)
     (2, 4, 1, 97, 97, 256, 256, False, False, (30, 20)),     # 256-wide, window both sides
+    (1, 8, 1, 130, 150, 512, 512, True, True, (-1, -1)),     # 512-wide: plain forward, then the dropout pass
+    (1, 4, 2, 70, 70, 512, 512, False, False, (25, -1)),     # 512-wide with a window
 ]
 
 
@@ -103,15 +105,12 @@ def test_dropout_full_workload_sampled():
 
 
 def test_dropout_rejects():
-    inp = synth.randn_dense(1, 2, 1, 8, 8, 512, 512, dtype="bf16", seed=1)
+    inp = synth.randn_dense(1, 2, 1, 8, 8, 128, 128, dtype="bf16", seed=1)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     kw = synth.pack_keep(synth.make_keep(1, 2, 8, 8, 0.5, seed=1)).cuda()
-    with pytest.raises(A.AttnUnsupported):        # no dropout kernel for 512-wide heads
-        A.dense(q, k, v, keep=kw, p_drop=0.5)
-    o512, l512 = A.dense(q, k, v, causal=True, scale=0.1)
-    with pytest.raises(A.AttnUnsupported):        # the 512-wide backward takes no mask either
-        A.dense_backward(q, k, v, o512, o512, l512, causal=True, scale=0.1, keep=kw, p_drop=0.5)
-    q2, k2 = q[..., :128].contiguous(), k[..., :128].contiguous()
+    with pytest.raises(A.AttnUnsupported):        # dropout is compiled for bf16 inputs only
+        A.dense(q.float(), k.float(), v.float(), keep=kw, p_drop=0.5)
+    q2, k2 = q, k
     out = torch.empty_like(q2)
     lse = torch.empty((1, 2, 8), device="cuda")
     a = A.dense_args(q2, k2, k2, out, lse, causal=True, scale=0.1, keep=kw, p_drop=0.5)
