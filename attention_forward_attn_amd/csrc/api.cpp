@@ -138,10 +138,12 @@ static attn_status validate_keep(const Args* a, int Tq, int Tk) {
 // time, the chunk holding at least `rounds` rounds of its CUs (so the
 // longest-first order inside a chunk can balance them), so that concurrent
 // workgroups share their K/V in that XCD's L2. Measured: four rounds for
-// folded GQA launches (gqa +1.1% over two); two for one-head groups (mla:
-// same time, and four heads' K/V at a time per L2 instead of eight fetch
-// 1.8x instead of 2.7x the algorithmic bytes) and for packed batches, whose
-// tiles past a short sequence are empty (four cost 11%).
+// folded GQA launches (gqa +1.1% over two); one for one-head groups (mla:
+// two heads' K/V at a time per L2 fetch 1.55x the algorithmic bytes, four
+// 1.8x and eight 2.7x, all in the same time; one head at a time fetches
+// 1.0x but runs 10% longer, the last head's longest tiles starting late);
+// two for packed batches, whose tiles past a short sequence are empty (four
+// cost 11%).
 void plan_xcd(attn::KernelParams& p, int rounds = 4) {
   p.xcd_groups = ((p.aligned || p.fold_tm) && p.n_groups % 8 == 0) ? 1 : 0;
   p.xcd_chunk = 0;
@@ -269,7 +271,7 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
   if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   p.n_tiles = (int)tiles;
-  plan_xcd(p, p.fold_tm ? 4 : 2);
+  plan_xcd(p, p.fold_tm ? 4 : 1);
   return ATTN_OK;
 }
 
