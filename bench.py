@@ -57,8 +57,11 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 WORKLOAD_IDS = {"tiny": 1, "gqa": 2, "mla": 3, "mqa512": 4, "sparse": 5, "decode512": 6, "swa1024": 7}
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+# the forward kernels and the planner that orders their workgroups (which
+# decides what shares an L2); recorded traffic counts only while these match
 KERNEL_SOURCES = ("attention_forward_attn_amd/csrc/attn_kernels.hip",
-                  "attention_forward_attn_amd/csrc/attn_params.h")
+                  "attention_forward_attn_amd/csrc/attn_params.h",
+                  "attention_forward_attn_amd/csrc/api.cpp")
 
 
 def log(msg):
