@@ -2321,7 +2321,9 @@ int bwd_head_splits(int B, int Hkv, int g, int Tk, int d_qk, int d_v) {
   const int64_t base = (int64_t)B * Hkv * ((Tk + bnk - 1) / bnk);
   // one workgroup fits a CU: ask for about three per CU of the 256 so that the
   // short causal key blocks fill in behind the long ones; at most 16 splits
-  // (the partials' traffic grows with their number)
+  // (the partials' traffic grows with their number). Measured on the MQA
+  // d512 shape (44 key blocks): 8 splits 12% and 12 splits 2% slower than
+  // 16; 32 the same time with twice the workspace
   if (base >= 512) return 1;
   return (int)std::min<int64_t>({(int64_t)g, 16, (768 + base - 1) / base});
 }
