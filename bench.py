@@ -719,9 +719,10 @@ def measure_extras(steps: int, warmup: int) -> dict:
 
 
 def measure_dropout(steps: int, warmup: int) -> dict:
-    """Attention dropout (p = 0.1, the caller's keep mask) on the gqa workload (2): the
-    forward and the backward with the same mask. Flops as the dense paths (the mask
-    adds no products); the fused forward without dropout is the comparison."""
+    """Attention dropout (p = 0.1, the caller's keep mask) on the gqa workload (2), and
+    beside it on the 512-wide MQA workload (4): the forward and the backward with the
+    same mask. Flops as the dense paths (the mask adds no products); the fused forward
+    without dropout is the comparison."""
     import torch
 
     import attention_forward_attn_amd as A
@@ -751,11 +752,38 @@ def measure_dropout(steps: int, warmup: int) -> dict:
     bach = bwd_flops(2) / (tb["kernel_ms_mean"] * 1e-3) / 1e12
     log(f"[bench] dropout p=0.1: {describe(2)} | forward {t['kernel_ms_mean']:.4f} ms = {rl['achieved']} TFLOP/s | "
         f"backward {tb['kernel_ms_mean']:.4f} ms = {bach:.1f} TFLOP/s")
+    # the same on the 512-wide MQA workload (4, with sinks): the plain forward and
+    # the dropout's second pass, then the 512-wide backward kernels with the mask
+    s4 = synth.spec(4)
+    inp4 = synth.make(4)
+    q4, k4, v4 = (inp4[x].cuda() for x in ("q", "k", "v"))
+    sk4 = inp4["sinks"].cuda()
+    kw4 = synth.pack_keep(synth.make_keep(s4.B, s4.H, s4.Tq, s4.Tk, 0.1, seed=4)).cuda()
+    out4 = torch.empty((s4.B, s4.H, s4.Tq, s4.d_v), dtype=torch.bfloat16, device="cuda")
+    lse4 = torch.empty((s4.B, s4.H, s4.Tq), dtype=torch.float32, device="cuda")
+    t4 = time_steps(lambda: A.dense(q4, k4, v4, causal=True, scale=s4.scale, sinks=sk4, out=out4, lse=lse4, keep=kw4,
+                                    p_drop=0.1), steps, warmup)
+    dout4 = synth.make_dout(s4).cuda()
+    dq4, dk4, dv4, dsk4 = torch.empty_like(q4), torch.empty_like(k4), torch.empty_like(v4), torch.empty_like(sk4)
+    ws4 = torch.empty(max(16, A.bwd_workspace_bytes(s4.B, s4.H, s4.Hkv, s4.Tq, s4.Tk, s4.d_qk, s4.d_v)),
+                      dtype=torch.uint8, device="cuda")
+    tb4 = time_steps(lambda: A.dense_backward(q4, k4, v4, out4, dout4, lse4, causal=True, scale=s4.scale, sinks=sk4,
+                                              dq=dq4, dk=dk4, dv=dv4, dsinks=dsk4, workspace=ws4, keep=kw4,
+                                              p_drop=0.1), steps, warmup)
+    f4 = work(4)["flops"] / (t4["kernel_ms_mean"] * 1e-3) / 1e12
+    b4 = bwd_flops(4) / (tb4["kernel_ms_mean"] * 1e-3) / 1e12
+    log(f"[bench] dropout p=0.1: {describe(4)} | forward (two passes) {t4['kernel_ms_mean']:.4f} ms = {f4:.1f} TFLOP/s"
+        f" | backward {tb4['kernel_ms_mean']:.4f} ms = {b4:.1f} TFLOP/s")
     return {"row": "attention dropout, keep mask shared by forward and backward", "workload": describe(2) + ", p=0.1",
             "path": "dense_dropout_bf16", "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3),
             "unit": "TFLOP/s", "kernel_ms": round(t["kernel_ms_mean"], 5), "roofline": rl, "verdict": "Measured",
             "backward": {"path": "dense_bwd_bf16_d128 (dropout)", "kernel_ms": round(tb["kernel_ms_mean"], 5),
-                         "tflops": round(bach, 2)}}
+                         "tflops": round(bach, 2)},
+            "mqa512": {"workload": describe(4) + ", p=0.1",
+                       "forward": {"path": "dense_bf16_d512 + dropout pass", "kernel_ms": round(t4["kernel_ms_mean"], 5),
+                                   "tflops": round(f4, 2)},
+                       "backward": {"path": "dense_bwd_bf16_d512 (dropout)", "kernel_ms": round(tb4["kernel_ms_mean"], 5),
+                                    "tflops": round(b4, 2)}}}
 
 
 def measure_sparse_fp8(steps: int, warmup: int) -> dict:

@@ -32,6 +32,7 @@ CASES = [
     (2, 4, 1, 97, 97, 256, 256, False, False, (30, 20)),     # 256-wide, window both sides
     (1, 8, 1, 130, 150, 512, 512, True, True, (-1, -1)),     # 512-wide: plain forward, then the dropout pass
     (1, 4, 2, 70, 70, 512, 512, False, False, (25, -1)),     # 512-wide with a window
+    (1, 4, 1, 90, 40, 512, 512, True, True, (-1, -1)),       # 512-wide, Tq > Tk: rows that see no key
 ]
 
 
