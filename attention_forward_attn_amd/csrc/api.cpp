@@ -255,21 +255,25 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   // causal mask they share almost the same key range and only one key block
   // per tile needs the per-score mask
   p.fold_tm = (cfg->dtype == 0 && p.g > 1) ? 1 : 0;
+  // counted in 64 bits before anything is narrowed; the dropout kernels tile
+  // the folded rows by 128 (64 for 512-wide heads), so their grids are
+  // checked as well
+  const int64_t tpg = (!p.fold_tm && a->Tq >= BM) ? (int64_t)((a->Tq + BM - 1) / BM) * p.g : (folded + BM - 1) / BM;
+  const int64_t tiles = (int64_t)p.n_groups * tpg;
+  const int64_t drop_tiles = out->drop ? (int64_t)p.n_groups * ((folded + 63) / 64) : 0;
+  if (tiles > 0x7fffffff || drop_tiles > 0x7fffffff)
+    return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   if (p.fold_tm) {
     p.aligned = 0;
     p.tiles_per_head = 0;
-    p.tiles_per_group = (int)((folded + BM - 1) / BM);
   } else if (a->Tq >= BM) {
     p.aligned = 1;
     p.tiles_per_head = (a->Tq + BM - 1) / BM;
-    p.tiles_per_group = p.tiles_per_head * p.g;
   } else {
     p.aligned = 0;
     p.tiles_per_head = 0;
-    p.tiles_per_group = (int)((folded + BM - 1) / BM);
   }
-  const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
-  if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
+  p.tiles_per_group = (int)tpg;
   p.n_tiles = (int)tiles;
   plan_xcd(p, p.fold_tm ? 4 : 1);
   return ATTN_OK;
@@ -1173,9 +1177,10 @@ attn_status attn_fwd_varlen(const attn_varlen_args* a, void* stream) {
   p.fold_tm = 1;
   p.aligned = 0;
   p.tiles_per_head = 0;
-  p.tiles_per_group = (int)(((int64_t)p.g * a->max_seqlen_q + BM - 1) / BM);
-  const int64_t tiles = (int64_t)p.n_groups * p.tiles_per_group;
+  const int64_t tpg = ((int64_t)p.g * a->max_seqlen_q + BM - 1) / BM;
+  const int64_t tiles = (int64_t)p.n_groups * tpg;
   if (tiles > 0x7fffffff) return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
+  p.tiles_per_group = (int)tpg;
   p.n_tiles = (int)tiles;
   plan_xcd(p, 2);
   return do_launch(dp, stream);

@@ -111,6 +111,41 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.attn_fwd_dense(ctypes.byref(a), None) == A.ATTN_INVALID_ARGUMENT
 
 
+def test_oversized_grids_rejected_before_narrowing():
+    """Tile counts are formed in 64 bits and checked before they are narrowed to a
+    32-bit launch size, also for the dropout kernels' smaller row tiles."""
+    lib = A.load_library()
+
+    def args(H, Tq, d, keep=False):
+        a = A.AttnDenseArgs()
+        a.struct_size = ctypes.sizeof(A.AttnDenseArgs)
+        a.dtype = A.ATTN_BF16
+        a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = 1, H, 1, Tq, 64, d, d
+        a.scale, a.causal = 0.1, 1
+        a.q = a.k = a.v = a.out = a.lse = 4096
+        a.q_sb, a.q_sh, a.q_st = H * Tq * d, Tq * d, d
+        a.k_sb, a.k_sh, a.k_st = 64 * d, 64 * d, d
+        a.v_sb, a.v_sh, a.v_st = 64 * d, 64 * d, d
+        a.o_sb, a.o_sh, a.o_st = H * Tq * d, Tq * d, d
+        if keep:
+            a.keep, a.p_drop = 4096, 0.1
+            a.m_sb, a.m_sh, a.m_st = H * Tq * 2, Tq * 2, 2
+        return a
+
+    def plan(a):
+        p = A.AttnPlan()
+        p.struct_size = ctypes.sizeof(A.AttnPlan)
+        return lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p))
+
+    # 2^16 heads x 2^26 tokens: 2^34 row tiles of one group, past a 32-bit count
+    assert plan(args(1 << 16, 1 << 26, 128)) == A.ATTN_INVALID_ARGUMENT
+    assert b"too large" in lib.attn_last_error()
+    # 512-wide: 3 * 2^29 tiles of 128 rows fit, the dropout's 64-row tiles do not
+    assert plan(args(1 << 16, 3 << 20, 512)) == A.ATTN_OK
+    assert plan(args(1 << 16, 3 << 20, 512, keep=True)) == A.ATTN_INVALID_ARGUMENT
+    assert b"too large" in lib.attn_last_error()
+
+
 def test_sparse_validation_errors():
     with pytest.raises(A.AttnInvalidArgument):
         A.plan_sparse_topk(4, 64, 100, 512, 513, 16)           # d_v > d_qk
