@@ -2215,7 +2215,10 @@ __global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_rt = (p.Tq + BM - 1) / BM;
-  const int bh = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  // the row tiles with the most visible key blocks of every head go first
+  // (under a causal mask a tile's work grows with its index)
+  const int n_bh = p.B * p.H;
+  const int bh = blockIdx.x % n_bh, rt = n_rt - 1 - (int)(blockIdx.x / n_bh);
   const int b = bh / p.H, h = bh % p.H, kvh = h / p.g;
   const int t0 = rt * BM + wave * 32;
   bf16x8 qf[KS];
@@ -2243,11 +2246,21 @@ __global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
   float* const pbase = p.p ? p.p + b * p.p_sb + h * p.p_sh : nullptr;
   const uint32_t smem_s = lds_u32(smem);
   const int nb = (p.Tk + BN - 1) / BN;
-  if (nb > 0) dma_tile<CPK, BN, NW>(kbase, p.k_st, 0, p.Tk - 1, smem_s, wave, lane);
-  for (int j = 0; j < nb; ++j) {
+  // key blocks [jb0, jb1) hold a key some row of the workgroup sees; the
+  // blocks outside are masked for all of its rows, so they take no product:
+  // p gets zeros there and row_max nothing
+  int jb0 = 0, jb1 = nb;
+  {
+    const int t_lo = rt * BM, t_hi = min(rt * BM + BM - 1, p.Tq - 1);
+    if (up >= 0) jb1 = (max(0, min(p.Tk, t_hi + off + up + 1)) + BN - 1) / BN;
+    if (p.win_left >= 0) jb0 = min(p.Tk, max(0, t_lo + off - p.win_left)) / BN;
+    jb0 = min(jb0, jb1);
+  }
+  if (jb0 < jb1) dma_tile<CPK, BN, NW>(kbase, p.k_st, jb0 * BN, p.Tk - 1, smem_s + (jb0 & 1) * KT_BYTES, wave, lane);
+  for (int j = jb0; j < jb1; ++j) {
     wait_all_loads();
     barrier();
-    if (j + 1 < nb) {
+    if (j + 1 < jb1) {
       // the slot address is rebuilt every step (the empty asm), so the per-
       // instruction LDS addresses derived from it are not kept in scalar
       // registers across the loop
@@ -2281,6 +2294,23 @@ __global__ void __launch_bounds__(256) extras_kernel(const ExtrasParams p) {
       rm[r] = fmaxf(rm[r], ok ? sv : -INFINITY);
       if (pbase != nullptr && kin && cr < nrow)
         pbase[(int64_t)(tl + cr) * p.p_st + kk] = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], p.c, -l2[r])) : 0.f;
+    }
+  }
+  if (pbase != nullptr && (jb0 > 0 || jb1 < nb)) {
+    // zeros for the blocks the product loop skipped: lane lq writes key
+    // j * BN + lq of this wave's rows tl + cr, the product loop's layout
+    const int tl = t0 + lh * 4, nrow = p.Tq - tl;
+    for (int j = 0; j < nb; ++j) {
+      if (j == jb0) j = jb1;
+      if (j >= nb) break;
+      const int kk = j * BN + lq;
+      if (kk < p.Tk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = (r >> 2) * 8 + (r & 3);
+          if (cr < nrow) pbase[(int64_t)(tl + cr) * p.p_st + kk] = 0.f;
+        }
+      }
     }
   }
   if (p.row_max != nullptr) {

@@ -30,6 +30,7 @@ CASES = [
     (1, 2, 1, 97, 33, 256, 256, True, False, (-1, -1)),     # Tq > Tk: rows that see no key
     (1, 8, 1, 70, 70, 512, 512, True, True, (-1, -1)),
     (1, 2, 2, 64, 257, 128, 128, False, False, (10, 20)),
+    (1, 2, 1, 300, 300, 64, 64, True, False, (50, -1)),     # tiles whose first and last key blocks are all masked
 ]
 
 
