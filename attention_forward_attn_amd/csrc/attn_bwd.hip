@@ -1305,6 +1305,7 @@ __global__ void __launch_bounds__(NG * (D / 128) * 64) bwd_dq_wide_kernel(const 
 //    V sees the mask, and the kept ones are scaled by 1 / (1 - p) at the end.
 // ---------------------------------------------------------------------------
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold of the online softmax (log2 units)
 
 template <int DQK, int DV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQK + DV > 320 ? 1 : 2)))
@@ -1402,7 +1403,8 @@ fwd_dropout_kernel(const BwdParams p) {
     pipeline_reads<MT * KS, 1>();
     // S^T element i of tile mt is key j*BN + mt*32 + lh*4 + 8*(i/4) + i%4 of this lane's row
     const bool full = (j + 1) * BN <= kfull && j * BN >= klfull;
-    float mx = -INFINITY;
+    // four partial maxima and sums keep the dependency chains short
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -1411,27 +1413,36 @@ fwd_dropout_kernel(const BwdParams p) {
           const int kk = j * BN + mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3);
           if (!(kk <= row_lim && kk >= row_lo)) S[mt][i] = -INFINITY;
         }
-        mx = fmaxf(mx, S[mt][i]);
+        mx4[i & 3] = fmaxf(mx4[i & 3], S[mt][i]);
       }
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the other half of the row's keys
+    // lazy rescale: the running maximum only moves when a score exceeds it by
+    // more than kRescaleLog2 (log2 units), so the exp2 arguments stay below
+    // that bound and the accumulator is rescaled on the first blocks only
     const float mnew = fmaxf(m_run, mx);
-    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - mnew) * p.c);
-    m_run = mnew;
-    l_run *= alpha;
+    const bool grow = (mnew - m_run) * p.c > kRescaleLog2;  // false when both are -inf
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mnew) * p.c) : 1.f;
+      if (grow) m_run = mnew;
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-    const float mc = (mnew == -INFINITY) ? 0.f : mnew * p.c;
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * p.c;
     float pd[MT * 16];
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -mc));
-        l_run += e;
+        rs4[i & 3] += e;
         pd[mt * 16 + i] = ((mw[mt] >> (lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) ? e : 0.f;
       }
+    l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
       const bf16x8 pb = pack8(pd + ks * 8);

@@ -10,8 +10,8 @@ above the rest. ``tests/test_rescale_inputs.py`` shows on the CPU that these
 inputs move the maximum by more than 8 log2 units after a row's first block at
 every block size the kernels use. Every path with an online softmax is
 covered: the dense kernels of every compiled head dim (bf16 and the fp32
-split path), split-KV, the sparse top-k kernel (one and several index
-segments), the quantized-cache decode and the fp8 sparse decode.
+split path), the dropout forward, split-KV, the sparse top-k kernel (one and
+several index segments), the quantized-cache decode and the fp8 sparse decode.
 
 Tolerances as everywhere: max |O - O_ref| <= 2e-2, max |lse - lse_ref| <= 1e-3
 (the scores stay below about 1e3 before scaling, where fp32 accumulation
@@ -71,6 +71,26 @@ def test_dense_bf16_rescale(dqk, dv, mode):
         ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=1 / math.sqrt(dqk), causal=causal,
                                         sinks=inp["sinks"])
         _check(label, out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mode", synth.WIDE_MODES)
+@pytest.mark.parametrize("dqk,dv", HEAD_DIMS)
+def test_dropout_rescale(dqk, dv, mode):
+    """The dropout forward's own online softmax (and, at d 512, the second pass
+    that reads the plain forward's lse) with the running maximum moved mid-row."""
+    inp = synth.widen_dense(1, 4, 2, 300, 300, dqk, dv, mode, sinks=True, seed=7 + dqk + dv + len(mode))
+    keep = synth.make_keep(1, 4, 300, 300, 0.2, seed=dqk + len(mode))
+    q, k, v, sk = (inp[n].cuda() for n in ("q", "k", "v", "sinks"))
+    label = f"dropout d{dqk}/{dv} {mode}"
+    announce(label)
+    out = torch.full((1, 4, 300, dv), float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full((1, 4, 300), float("nan"), dtype=torch.float32, device="cuda")
+    A.dense(q, k, v, causal=True, scale=1 / math.sqrt(dqk), sinks=sk, out=out, lse=lse,
+            keep=synth.pack_keep(keep).cuda(), p_drop=0.2)
+    torch.cuda.synchronize()
+    ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=1 / math.sqrt(dqk), causal=True,
+                                    sinks=inp["sinks"], keep=keep.numpy(), p_drop=0.2)
+    _check(label, out, lse, ro, rl)
 
 
 @pytest.mark.parametrize("mode", synth.WIDE_MODES)
