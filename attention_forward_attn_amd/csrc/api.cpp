@@ -101,19 +101,24 @@ int64_t tile_budget_bytes() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }  // NULL passes
 
-const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse, int rope = 0) {
+const attn::KernelConfig* find_config(int dtype, int d_qk, int d_v, int sparse, int rope = 0, int drop = 0) {
   int n = 0;
   const attn::KernelConfig* t = attn::kernel_table(&n);
   for (int i = 0; i < n; ++i)
-    if (t[i].dtype == dtype && t[i].d_qk == d_qk && t[i].d_v == d_v && t[i].sparse == sparse && t[i].rope == rope)
+    if (t[i].dtype == dtype && t[i].d_qk == d_qk && t[i].d_v == d_v && t[i].sparse == sparse && t[i].rope == rope &&
+        t[i].drop == drop)
       return &t[i];
   return nullptr;
 }
 
+// Dropout runs inside the fused kernel for 512-wide heads and as a separate
+// kernel for the narrower ones.
+bool fused_dropout(const attn_dense_args* a) { return a->keep != nullptr && a->d_qk == 512 && a->d_v == 512; }
+
 struct DensePlan {
   const attn::KernelConfig* cfg;
   attn::KernelParams kp;
-  bool drop = false;  // dropout: the separate dropout kernel, not cfg
+  bool drop = false;  // dropout by the separate dropout kernel, not cfg
 };
 
 // dropout mask fields shared by the forward and backward argument structs
@@ -178,7 +183,8 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
     return fail(ATTN_UNSUPPORTED, "sliding windows are compiled for bf16 inputs only");
   if (a->rope_dim < 0 || a->rope_dim >= a->d_qk)
     return fail(ATTN_INVALID_ARGUMENT, "rope_dim must be 0 or in [1, d_qk)");
-  const attn::KernelConfig* cfg = find_config(a->dtype, a->d_qk, a->d_v, 0, a->rope_dim);
+  const attn::KernelConfig* cfg =
+      find_config(a->dtype, a->d_qk, a->d_v, 0, a->rope_dim, a->dtype == ATTN_BF16 && fused_dropout(a) ? 1 : 0);
   if (!cfg)
     return fail(ATTN_UNSUPPORTED, "no compiled dense kernel for dtype %d with (d_qk, d_v) = (%d, %d), rope_dim %d",
                 a->dtype, a->d_qk, a->d_v, a->rope_dim);
@@ -224,7 +230,7 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   if (a->Tq > 1 && a->o_st < a->d_v) return fail(ATTN_INVALID_ARGUMENT, "out token stride smaller than d_v");
 
   out->cfg = cfg;
-  out->drop = a->keep != nullptr;
+  out->drop = a->keep != nullptr && !cfg->drop;
   attn::KernelParams& p = out->kp;
   std::memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse; p.sinks = a->sinks; p.idx = nullptr;
@@ -243,6 +249,11 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   p.win_right = a->window_right;
   p.scale = a->scale;
   p.c = a->scale * 1.4426950408889634f;
+  if (cfg->drop) {
+    p.keep = a->keep;
+    p.m_sb = a->m_sb; p.m_sh = a->m_sh; p.m_st = a->m_st;
+    p.inv_keep = 1.f / (1.f - a->p_drop);
+  }
   const int BM = cfg->block_rows;
   p.block_rows = BM;
   p.n_groups = a->B * a->Hkv;
@@ -255,12 +266,11 @@ attn_status validate_dense(const attn_dense_args* a, DensePlan* out) {
   // causal mask they share almost the same key range and only one key block
   // per tile needs the per-score mask
   p.fold_tm = (cfg->dtype == 0 && p.g > 1) ? 1 : 0;
-  // counted in 64 bits before anything is narrowed; the dropout kernels tile
-  // the folded rows by 128 (64 for 512-wide heads), so their grids are
-  // checked as well
+  // counted in 64 bits before anything is narrowed; the separate dropout
+  // kernel tiles the folded rows by 128, so its grid is checked as well
   const int64_t tpg = (!p.fold_tm && a->Tq >= BM) ? (int64_t)((a->Tq + BM - 1) / BM) * p.g : (folded + BM - 1) / BM;
   const int64_t tiles = (int64_t)p.n_groups * tpg;
-  const int64_t drop_tiles = out->drop ? (int64_t)p.n_groups * ((folded + 63) / 64) : 0;
+  const int64_t drop_tiles = out->drop ? (int64_t)p.n_groups * ((folded + 127) / 128) : 0;
   if (tiles > 0x7fffffff || drop_tiles > 0x7fffffff)
     return fail(ATTN_INVALID_ARGUMENT, "problem too large for one launch");
   if (p.fold_tm) {
@@ -467,7 +477,7 @@ attn_status splitkv_launch(const attn_dense_args* a, int32_t n_splits, void* wor
   DensePlan dp;
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
-  if (dp.drop) return fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
+  if (a->keep) return fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
   if (n_splits < 0 || n_splits > kMaxSplits)
     return fail(ATTN_INVALID_ARGUMENT, "n_splits must be in [0, %d], got %d", kMaxSplits, n_splits);
   if (a->Tq == 0) return ATTN_OK;
@@ -546,15 +556,7 @@ attn_status attn_fwd_dense(const attn_dense_args* a, void* stream) {
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
   if (a->Tq == 0) return ATTN_OK;
-  if (dp.drop) {
-    // 512-wide heads: the plain forward gives lse (the dropout leaves it as it
-    // is), then a second pass forms the dropped output from it
-    if (a->d_qk == 512) {
-      s = do_launch(dp, stream);
-      if (s != ATTN_OK) return s;
-    }
-    return launch_dropout(a, stream);
-  }
+  if (dp.drop) return launch_dropout(a, stream);
   return do_launch(dp, stream);
 }
 
@@ -574,7 +576,7 @@ attn_status attn_plan_dense(const attn_dense_args* a, attn_plan* p) {
   DensePlan dp;
   attn_status s = validate_dense(a, &dp);
   if (s != ATTN_OK) return s;
-  if (dp.drop) return fail(ATTN_UNSUPPORTED, "plans describe the fused kernels; dropout runs a separate kernel");
+  if (dp.drop) return fail(ATTN_UNSUPPORTED, "plans describe the fused kernels; dropout at this width runs a separate kernel");
   if (a->Tq == 0) dp.kp.n_tiles = 0;
   fill_plan(dp, a->H / a->Hkv, (int64_t)(a->H / a->Hkv) * a->Tq, a->Tk, a->dtype == ATTN_BF16 ? 2 : 4, p);
   return ATTN_OK;
@@ -584,7 +586,7 @@ int32_t attn_splitkv_choose(const attn_dense_args* a) {
   g_last_error.clear();
   DensePlan dp;
   if (validate_dense(a, &dp) != ATTN_OK) return -1;
-  if (dp.drop) {
+  if (a->keep) {
     fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
     return -1;
   }
@@ -596,7 +598,7 @@ int64_t attn_splitkv_workspace_bytes(const attn_dense_args* a, int32_t n_splits)
   g_last_error.clear();
   DensePlan dp;
   if (validate_dense(a, &dp) != ATTN_OK) return -1;
-  if (dp.drop) {
+  if (a->keep) {
     fail(ATTN_UNSUPPORTED, "split-KV with dropout is not compiled");
     return -1;
   }
@@ -781,7 +783,7 @@ attn_status attn_fwd_dense_extras(const attn_dense_args* a, float* p_out, int64_
   DensePlan dp;
   attn_status st = validate_dense(a, &dp);
   if (st != ATTN_OK) return st;
-  if (dp.drop) return fail(ATTN_UNSUPPORTED, "the extra returns take no dropout mask");
+  if (a->keep) return fail(ATTN_UNSUPPORTED, "the extra returns take no dropout mask");
   if (a->dtype != ATTN_BF16 || a->rope_dim != 0 || !attn::extras_supported(a->d_qk))
     return fail(ATTN_UNSUPPORTED, "the extra returns are compiled for bf16, d_qk in {64,128,192,256,512}, rope_dim 0");
   if (((uintptr_t)p_out & 3u) || ((uintptr_t)row_max & 3u))

@@ -50,8 +50,10 @@
 //                         atomics), after a fill, the row dots and the sinks.
 //  6. extras_kernel       the forward's extra returns (probabilities, row
 //                         maxima) as a second pass from q, k and lse.
-//  7. fwd_dropout_kernel  the forward with a caller-drawn dropout mask (the
-//                         backward kernels above take the same mask).
+//  7. fwd_dropout_kernel  the forward with a caller-drawn dropout mask, heads
+//                         up to 256 wide (512-wide heads take the mask inside
+//                         the fused forward); the backward kernels above take
+//                         the same mask.
 //  8. sparse_fp8_kernel   the sparse top-k decode over an fp8 pool.
 
 #include <hip/hip_runtime.h>
@@ -1693,185 +1695,6 @@ __global__ void __launch_bounds__(512) sparse_fp8_kernel(const SpFp8Params p) {
   if (sq == 0 && lh == 0) p.part_lse[orow] = any ? m_run * p.scale + __builtin_amdgcn_logf(l) * kLn2 : -INFINITY;
 }
 
-// ---------------------------------------------------------------------------
-// 7b. The dropout forward for 512-wide heads, as a second pass after the
-//     plain forward: the dropout leaves lse as it is (it is the softmax's),
-//     so with P = exp(scale q.k - lse) known, this pass only forms
-//     O = (P keep / (1 - p)) V and overwrites the plain output. The wide dQ
-//     kernel's tiling: 8 waves, groups of DS = D/128; wave (gi, cs) owns
-//     output columns 128 cs.. of 32 folded rows and forms the partial S over
-//     its 128 columns of Q and K; the partials are reduce-scattered through
-//     LDS, the owner of an element forms P keep and writes it as bf16 over
-//     slice 0's partial, and O^T += V^T (P keep)^T takes V^T from the V tile
-//     by transposed reads.
-// ---------------------------------------------------------------------------
-template <int D, int NG>
-__global__ void __launch_bounds__(NG * (D / 128) * 64) fwd_dropout_pv_wide_kernel(const BwdParams p) {
-  constexpr int DS = D / 128, NW = NG * DS, DC = 128;
-  constexpr int BM = 32 * NG, BN = 32;
-  constexpr int CP = D / 8, KSC = DC / 16, DTC = DC / 32;
-  constexpr int KT_BYTES = BN * D * 2;
-  constexpr int EP = 16 / DS;               // accumulator elements of every lane a wave reduces
-  constexpr int XW_BYTES = 4 * 64 * 16;     // one wave's partial S: [q][lane][4 floats]
-  constexpr int ST_OFF = 2 * KT_BYTES, XS_OFF = 4 * KT_BYTES;  // [K stage 0 | K stage 1 | V stage 0 | V stage 1 | S]
-  static_assert(XS_OFF + NW * XW_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(EP == 4 || EP == 8, "four or eight elements per wave");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[XS_OFF + NW * XW_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lq = lane & 31, lh = lane >> 5;
-  const int gi = wave / DS, cs = wave % DS;
-  const int n_groups = p.B * p.Hkv;
-  const int grp = blockIdx.x % n_groups, b = grp / p.Hkv, kvh = grp % p.Hkv;
-  unsigned char* const xg = smem + XS_OFF + gi * DS * XW_BYTES;  // the group's partials
-  auto xat = [&](int w, int q) { return xg + w * XW_BYTES + (q * 64 + lane) * 16; };
-  const int rows = p.g * p.Tq;
-  const int n_rt = (rows + BM - 1) / BM;
-  const int tb = n_rt - 1 - (int)(blockIdx.x / n_groups);  // longest causal tiles first
-  const int f0 = tb * BM;
-  const int f = f0 + gi * 32 + lq;
-  const bool valid = f < rows;
-  const int fc = valid ? f : rows - 1;
-  const int h = kvh * p.g + fc / p.Tq, t = fc % p.Tq;
-  const int off = p.Tk - p.Tq;
-  const int up = p.causal ? 0 : p.win_right;
-  const int row_lim = !valid ? -1 : (up >= 0 ? min(t + off + up, p.Tk - 1) : p.Tk - 1);
-  const int row_lo = p.win_left >= 0 ? t + off - p.win_left : 0;
-  const int64_t lrow = ((int64_t)b * p.H + h) * p.Tq + t;
-  const float lse = p.fwd_lse[lrow];
-  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-
-  // q of this lane's row over the wave's columns (the B operand of S^T)
-  bf16x8 qf[KSC];
-  {
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)t * p.q_st + cs * DC;
-#pragma unroll
-    for (int s = 0; s < KSC; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + lh * 8);
-  }
-
-  // keys the workgroup's rows can see ([kstart, kend))
-  int kend = p.Tk, kstart = 0;
-  {
-    const int f_last = min(f0 + BM, rows) - 1;
-    const bool one_head = f_last / p.Tq == f0 / p.Tq;
-    const int t_hi = one_head ? f_last % p.Tq : p.Tq - 1;
-    const int t_lo = one_head ? f0 % p.Tq : 0;
-    if (up >= 0) kend = max(0, min(p.Tk, t_hi + off + up + 1));
-    if (p.win_left >= 0) kstart = min(p.Tk, max(0, t_lo + off - p.win_left));
-  }
-  const int nb = (kend + BN - 1) / BN, jb0 = kstart / BN;
-
-  const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + b * p.k_sb + kvh * p.k_sh;
-  const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + b * p.v_sb + kvh * p.v_sh;
-  const uint32_t smem_s = lds_u32(smem);
-  auto issue = [&](int j) {
-    dma_tile<CP, BN, NW>(kbase, p.k_st, j * BN, p.Tk - 1, smem_s + (uint32_t)((j & 1) * KT_BYTES), wave, lane);
-    dma_tile<CP, BN, NW>(vbase, p.v_st, j * BN, p.Tk - 1, smem_s + (uint32_t)(ST_OFF + (j & 1) * KT_BYTES), wave,
-                         lane);
-  };
-  // the keep word of this lane's row for key block j, loaded a block ahead
-  const uint32_t* mrow = p.keep + b * p.m_sb + h * p.m_sh + (int64_t)t * p.m_st;
-  uint32_t mw = (nb > jb0 && jb0 < p.nwords) ? mrow[jb0] : 0u;
-
-  f32x16 acc[DTC];
-#pragma unroll
-  for (int dt = 0; dt < DTC; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-
-  if (nb > jb0) issue(jb0);
-  for (int j = jb0; j < nb; ++j) {
-    wait_all_loads();
-    barrier();  // block j has landed everywhere; nobody reads the stages j+1 refills any more
-    if (j + 1 < nb) issue(j + 1);
-    const bf16_t* kt = reinterpret_cast<const bf16_t*>(smem + (j & 1) * KT_BYTES);
-    const bf16_t* vt = reinterpret_cast<const bf16_t*>(smem + ST_OFF + (j & 1) * KT_BYTES);
-    // partial S^T over the wave's columns; element i is key
-    // j*BN + lh*4 + 8*(i/4) + i%4 of this lane's row
-    f32x16 S;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KSC; ++s) S = mfma32(row_frag<CP>(kt, lq, cs * KSC + s, lh), qf[s], S);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(xat(cs, q)) = f32x4{S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]};
-    barrier();
-    // this wave's elements: the partials added in slice order, then P keep,
-    // written as bf16 over slice 0's partial of those elements
-    float sv[EP];
-#pragma unroll
-    for (int k = 0; k < EP; ++k) sv[k] = 0.f;
-#pragma unroll
-    for (int c = 0; c < DS; ++c)
-#pragma unroll
-      for (int q4 = 0; q4 < EP / 4; ++q4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(xat(c, cs * (EP / 4) + q4));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sv[q4 * 4 + k] += x[k];
-      }
-    uint32_t pw[EP / 2];
-#pragma unroll
-    for (int k = 0; k < EP; k += 2) {
-      float p2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = cs * EP + k + u;
-        const int ko = lh * 4 + 8 * (e >> 2) + (e & 3), kk = j * BN + ko;
-        float pr = __builtin_amdgcn_exp2f(fmaf(sv[k + u], p.c, -l2));
-        pr = (kk <= row_lim && kk >= row_lo && ((mw >> ko) & 1u)) ? pr : 0.f;
-        p2[u] = pr;
-      }
-      pw[k / 2] = pack2(p2[0], p2[1]);
-    }
-    if (j + 1 < nb) mw = j + 1 < p.nwords ? mrow[j + 1] : 0u;
-    if constexpr (EP == 4) {
-      *reinterpret_cast<u32x2*>(xat(0, cs)) = u32x2{pw[0], pw[1]};
-    } else {
-      *reinterpret_cast<u32x4*>(xat(0, 2 * cs)) = u32x4{pw[0], pw[1], pw[2], pw[3]};
-    }
-    barrier();
-    // P keep of elements 0..15 of this lane as bf16 (the B operand)
-    uint32_t w[8];
-    if constexpr (EP == 4) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 c2 = *reinterpret_cast<const u32x2*>(xat(0, q));
-        w[2 * q] = c2[0];
-        w[2 * q + 1] = c2[1];
-      }
-    } else {
-#pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        const u32x4 c4 = *reinterpret_cast<const u32x4*>(xat(0, 2 * o));
-        w[4 * o] = c4[0];
-        w[4 * o + 1] = c4[1];
-        w[4 * o + 2] = c4[2];
-        w[4 * o + 3] = c4[3];
-      }
-    }
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
-#pragma unroll
-    for (int dt = 0; dt < DTC; ++dt) {
-      acc[dt] = mfma32(tr_frag<CP>(vt, 0, cs * DC + dt * 32, lane), pb0, acc[dt]);
-      acc[dt] = mfma32(tr_frag<CP>(vt, 16, cs * DC + dt * 32, lane), pb1, acc[dt]);
-    }
-  }
-
-  if (valid) {
-    bf16_t* op = reinterpret_cast<bf16_t*>(p.fwd_out) + b * p.o_sb + h * p.o_sh + (int64_t)t * p.o_st + cs * DC;
-    const float m = p.inv_keep;
-#pragma unroll
-    for (int dt = 0; dt < DTC; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = dt * 32 + g4 * 8 + lh * 4;
-        *reinterpret_cast<u32x2*>(op + d) = u32x2{pack2(acc[dt][g4 * 4] * m, acc[dt][g4 * 4 + 1] * m),
-                                                  pack2(acc[dt][g4 * 4 + 2] * m, acc[dt][g4 * 4 + 3] * m)};
-      }
-  }
-}
-
 // dK and dV from the head-split partials: four columns a thread, the splits
 // added in order (so the result does not depend on the launch's timing)
 template <int D>
@@ -2432,12 +2255,8 @@ int launch_fwd_dropout(const BwdParams& p, int d_qk, int d_v, void* stream) {
     hipLaunchKernelGGL((fwd_dropout_kernel<192, 128>), dim3((unsigned)grid), dim3(256), 0, st, p);
   else if (d_qk == 256 && d_v == 256)
     hipLaunchKernelGGL((fwd_dropout_kernel<256, 256>), dim3((unsigned)grid), dim3(256), 0, st, p);
-  else if (d_qk == 512 && d_v == 512) {
-    // the second pass after the plain forward (section 7b): 64 folded rows a workgroup
-    const int64_t grid2 = ((int64_t)p.g * p.Tq + 63) / 64 * p.B * p.Hkv;
-    hipLaunchKernelGGL((fwd_dropout_pv_wide_kernel<512, 2>), dim3((unsigned)grid2), dim3(512), 0, st, p);
-  } else
-    return -1;
+  else
+    return -1;  // (512-wide heads take the mask inside the fused forward)
   return (int)hipGetLastError();
 }
 

@@ -29,7 +29,8 @@
 //     192) run two wave groups per workgroup that alternate their MFMA half
 //     (S and PV) and their softmax half on each SIMD; 256- and 512-wide heads
 //     split d over DS waves of a query group and sum the partial scores
-//     through LDS. Described in detail above the kernel.
+//     through LDS; the 512-wide instance also comes with the caller's dropout
+//     keep mask applied inside (DROP). Described in detail above the kernel.
 //
 //   attn_fwd_kernel (fp32 inputs only, the tiny workload): the first kernel of
 //     this library, register-staged: 16-byte global loads into registers, V
@@ -836,12 +837,15 @@ struct DCfg {
 
 // ROPE > 0: the last ROPE columns of q and k come from q2 / k2 (MLA's rope
 // part read in place); the other DQK - ROPE from q / k.
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, int ROPE = 0, bool XK = false>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool SPARSE, bool PINGPONG, int ROPE = 0, bool XK = false,
+          bool DROP = false>
 __global__ void __launch_bounds__(NW * 64)
 attn_fwd_dma_kernel(const KernelParams p) {
   using C = DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, XK>;
   static_assert(ROPE == 0 || (!SPARSE && DS == 1 && (DQK - ROPE) % 16 == 0 && ROPE % 16 == 0),
                 "two-part rows: one wave holds the whole row, both parts whole K steps");
+  static_assert(!DROP || (XK && !SPARSE && ROPE == 0 && BN == 32),
+                "dropout: the one-group 512-wide kernel, one keep word per row and key block");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
   bf16_t* const kring = reinterpret_cast<bf16_t*>(smem);
   bf16_t* const vring = reinterpret_cast<bf16_t*>(smem + C::KRING_BYTES);
@@ -849,7 +853,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
   int32_t* const sidx = reinterpret_cast<int32_t*>(smem + C::KRING_BYTES + C::VRING_BYTES + C::SX_BYTES);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // (the dropout instance holds the wave index in a scalar register: its key
+  // loop has no vector register to spare)
+  const int lane = tid & 63, wave = DROP ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int lq = lane & 31, lh = lane >> 5;
   const int qg = wave / DS, dsi = wave % DS;
   const int wgrp = C::PP ? (wave >= NW / 2 ? 1 : 0) : 0;  // wave group
@@ -979,6 +985,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   const int rr = row_ok ? r : 0;
   int row_lim, row_lo = -(1 << 30), row_h;
   int64_t q_off, o_off, l_off, q2_off = 0;
+  int t_row = 0;  // the row's query token (dense)
   if constexpr (SPARSE) {
     row_h = rr;
     row_lim = Tk - 1;
@@ -995,6 +1002,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
     q_off = (int64_t)b * p.q_sb + (int64_t)row_h * p.q_sh + (qtok0 + t) * p.q_st;
     if constexpr (ROPE > 0) q2_off = (int64_t)b * p.q2_sb + (int64_t)row_h * p.q2_sh + (qtok0 + t) * p.q2_st;
     o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (qtok0 + t) * p.o_st;
+    t_row = t;
     l_off = kPacked && p.varlen ? (int64_t)row_h * p.total_q + qtok0 + t : ((int64_t)b * p.H + row_h) * Tq + t;
   }
 
@@ -1279,6 +1287,16 @@ attn_fwd_dma_kernel(const KernelParams p) {
 
   f32x16 S[C::MT];
   bf16x8 pb[C::PKS];
+  // dropout: the keep word of this lane's row for the current 32-key block
+  // (the next block's is loaded into it once the softmax has used it); its
+  // address is rebuilt per load from the row's head and token, which keeps
+  // the registers of the 512-wide loop free of a 64-bit pointer
+  uint32_t mw = 0u;
+  auto keep_word = [&](int blk) -> uint32_t {
+    int th = t_row, hh = row_h;
+    asm volatile("" : "+v"(th), "+v"(hh));  // not hoisted: a 64-bit row base would stay live
+    return p.keep[(int64_t)b * p.m_sb + (int64_t)hh * p.m_sh + (int64_t)th * p.m_st + (k_lo >> 5) + blk];
+  };
 
   // S(blk) = K(blk) Q^T, partial over this wave's d_qk columns and published
   // through LDS when DS > 1
@@ -1454,8 +1472,11 @@ attn_fwd_dma_kernel(const KernelParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(S[mt][i], p.c, -mc));
-        S[mt][i] = e;
         rs4[i & 3] += e;
+        // dropout: the denominator takes every probability, the product with
+        // V only the kept ones (key mt*32 + lh*4 + 8*(i/4) + i%4 of the block)
+        if constexpr (DROP) S[mt][i] = ((mw >> (mt * 32 + lh * 4 + 8 * (i >> 2) + (i & 3))) & 1u) ? e : 0.f;
+        else S[mt][i] = e;
       }
     l_run += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
 #pragma unroll
@@ -1516,6 +1537,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
       issue_k(i);
       issue_v(i);
     };
+    if constexpr (DROP) {
+      if (nb > 0) mw = keep_word(0);
+    }
     for (int i = -C::KD; i < 0; ++i) {
       if constexpr (XK) {
         // issue order K 0, V 0, K 1: at step j only K block j+1 may stay in flight
@@ -1570,10 +1594,18 @@ attn_fwd_dma_kernel(const KernelParams p) {
     } else if constexpr (XK) {
       // step j: V block j+1 and K block j+2 are issued (in that order) into
       // the slots step j-1 finished with, before the S product; the partial
-      // scores are exchanged in K block j's slot between two barriers
+      // scores are exchanged in K block j's slot between two barriers. With
+      // dropout every step drains the loads (K block j+1 included): the keep
+      // word of block j+1 is an ordinary load, issued once the softmax of
+      // block j has used the register, and the compiler's wait for it then
+      // falls after the drain
       for (int j = 0; j < nb; ++j) {
-        wait_vmcnt_dyn(j + 1 < nb ? myK : 0);  // K block j and V block j have landed
+        if constexpr (DROP)
+          wait_vmcnt_dyn(0);
+        else
+          wait_vmcnt_dyn(j + 1 < nb ? myK : 0);  // K block j and V block j have landed
         lds_barrier();
+        if constexpr (DROP) asm volatile("" ::"v"(mw));  // the compiler's wait for the word lands here
         issue_v(j);
         issue_k(j);
         doS(j);
@@ -1581,6 +1613,9 @@ attn_fwd_dma_kernel(const KernelParams p) {
         publishS(j);
         lds_barrier();
         phase2(j);
+        if constexpr (DROP) {
+          if (j + 1 < nb) mw = keep_word(j + 1);
+        }
         doPV(j);
       }
     } else {
@@ -1600,7 +1635,7 @@ attn_fwd_dma_kernel(const KernelParams p) {
   // ---------------------------------------------------------------- epilogue
   const float lt = halves_sum(l_run);
   const float ms = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
-  if (!SPARSE && p.n_splits > 1) {
+  if (!SPARSE && !DROP && p.n_splits > 1) {  // (the host never splits a dropout launch)
     // split-KV partial: O over this key range normalised by the range's own
     // denominator (fp32), lse of the range without the sink
     if (row_ok) {
@@ -1637,6 +1672,12 @@ attn_fwd_dma_kernel(const KernelParams p) {
     inv = lt > 0.f ? 1.f / lt : 0.f;
     lse = lt > 0.f ? ms + __builtin_amdgcn_logf(lt) * kLn2 : -INFINITY;
   }
+  if constexpr (DROP) {
+    inv *= p.inv_keep;  // the kept probabilities are scaled by 1 / (1 - p)
+    // rebuilt here rather than kept live through the key loop (registers)
+    o_off = (int64_t)b * p.o_sb + (int64_t)row_h * p.o_sh + (int64_t)t_row * p.o_st;
+    l_off = ((int64_t)b * p.H + row_h) * Tq + t_row;
+  }
   if (row_ok) {
     bf16_t* ob = reinterpret_cast<bf16_t*>(p.out) + o_off;
 #pragma unroll
@@ -1648,15 +1689,19 @@ attn_fwd_dma_kernel(const KernelParams p) {
             u32x2{pack_bf16x2(acc[dt][g4 * 4] * inv, acc[dt][g4 * 4 + 1] * inv),
                   pack_bf16x2(acc[dt][g4 * 4 + 2] * inv, acc[dt][g4 * 4 + 3] * inv)};
       }
-    if (lh == 0 && dsi == 0) p.lse[l_off] = lse;
+    // both lane halves of a row hold the same lse; the dropout instance lets
+    // both store it (the lane half is not kept live through its key loop)
+    if ((DROP || lh == 0) && dsi == 0) p.lse[l_off] = lse;
   }
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false,
+          bool DROP = false>
 int occupancy_dma() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK>),
+          &n,
+          reinterpret_cast<const void*>(&attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK, DROP>),
           NW * 64, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -1664,9 +1709,10 @@ int occupancy_dma() {
   return n;
 }
 
-template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false>
+template <int DQK, int DV, int DS, int NW, int BN, int NBUF, bool PINGPONG, bool SPARSE, int ROPE = 0, bool XK = false,
+          bool DROP = false>
 int launch_dma(const KernelParams& p, void* stream) {
-  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK>),
+  hipLaunchKernelGGL((attn_fwd_dma_kernel<DQK, DV, DS, NW, BN, NBUF, SPARSE, PINGPONG, ROPE, XK, DROP>),
                      dim3(p.n_tiles, p.n_splits > 1 ? p.n_splits : 1), dim3(NW * 64), 0,
                      reinterpret_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
@@ -1783,6 +1829,14 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const MergeParams m) 
         &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, 0, XK>                                              \
   }
 
+#define DMA_ENTRY_XK_DROP(NAME, DQK, DV, DS, NW, BN, NBUF, PP, XK)                                               \
+  KernelConfig {                                                                                                 \
+    NAME, 0, DQK, DV, false, DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP, XK>::BM, BN, NW,                          \
+        DCfg<DQK, DV, DS, NW, BN, NBUF, false, PP, XK>::LDS_BYTES,                                               \
+        &launch_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, 0, XK, true>,                                          \
+        &occupancy_dma<DQK, DV, DS, NW, BN, NBUF, PP, false, 0, XK, true>, 0, 1                                  \
+  }
+
 #define DMA_ENTRY(NAME, DQK, DV, DS, NW, BN, NBUF, PP, SPARSE)                                                   \
   KernelConfig {                                                                                                 \
     NAME, 0, DQK, DV, SPARSE, DCfg<DQK, DV, DS, NW, BN, NBUF, SPARSE, PP>::BM, BN, NW,                           \
@@ -1821,6 +1875,7 @@ int launch(const KernelParams& p, void* stream) {
 #define DMA_ENTRY_X(...) DMA_ENTRY(__VA_ARGS__)
 #define DMA_ENTRY_ROPE_X(...) DMA_ENTRY_ROPE(__VA_ARGS__)
 #define DMA_ENTRY_XK_X(...) DMA_ENTRY_XK(__VA_ARGS__)
+#define DMA_ENTRY_XK_DROP_X(...) DMA_ENTRY_XK_DROP(__VA_ARGS__)
 #ifndef ATTN_CFG_D64
 #define ATTN_CFG_D64 1, 8, 64, 3, true
 #endif
@@ -1850,6 +1905,7 @@ const KernelConfig kTable[] = {
     DMA_ENTRY_ROPE_X("dense_bf16_d192_v128_rope64", 192, 128, 64, ATTN_CFG_D192),
     DMA_ENTRY_X("dense_bf16_d256", 256, 256, ATTN_CFG_D256, false),
     DMA_ENTRY_XK_X("dense_bf16_d512", 512, 512, ATTN_CFG_D512, ATTN_D512_XK),
+    DMA_ENTRY_XK_DROP_X("dense_bf16_d512_dropout", 512, 512, ATTN_CFG_D512, ATTN_D512_XK),
     CFG_ENTRY("dense_f32split_d64", 1, 64, 64, 1, 1, 4, 32, true, false),
     CFG_ENTRY("dense_f32split_d128", 1, 128, 128, 1, 1, 4, 32, true, false),
     DMA_ENTRY_X("sparse_bf16_d512", 512, 512, ATTN_CFG_SPARSE, true),

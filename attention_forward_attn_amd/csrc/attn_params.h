@@ -26,6 +26,12 @@ struct KernelParams {
   const void* k2;
   int64_t q2_sb, q2_sh, q2_st;
   int64_t k2_sb, k2_sh, k2_st;
+  // attention dropout inside the fused kernel (512-wide heads): bit k % 32 of
+  // keep[b * m_sb + h * m_sh + t * m_st + k / 32] keeps key k of row (b, h, t)
+  // in the product with V; the kept probabilities are scaled by inv_keep
+  const uint32_t* keep;
+  int64_t m_sb, m_sh, m_st;
+  float inv_keep;
 
   int32_t B, H, Hkv, Tq, Tk, g;  // sparse: B = Sq, H = Hq, Hkv = 1, Tk = topk
   int32_t npool;                 // sparse: rows in the pool
@@ -225,6 +231,7 @@ struct KernelConfig {
   launch_fn launch;
   occupancy_fn occupancy;
   int rope;          // columns of q / k read from the second pointers (0: none)
+  int drop;          // 1: applies the caller's dropout keep mask (KernelParams::keep)
 };
 
 // Table of compiled configurations (defined in attn_kernels.hip).

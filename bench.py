@@ -752,8 +752,8 @@ def measure_dropout(steps: int, warmup: int) -> dict:
     bach = bwd_flops(2) / (tb["kernel_ms_mean"] * 1e-3) / 1e12
     log(f"[bench] dropout p=0.1: {describe(2)} | forward {t['kernel_ms_mean']:.4f} ms = {rl['achieved']} TFLOP/s | "
         f"backward {tb['kernel_ms_mean']:.4f} ms = {bach:.1f} TFLOP/s")
-    # the same on the 512-wide MQA workload (4, with sinks): the plain forward and
-    # the dropout's second pass, then the 512-wide backward kernels with the mask
+    # the same on the 512-wide MQA workload (4, with sinks): the fused 512-wide
+    # forward with the mask applied inside, then the 512-wide backward kernels
     s4 = synth.spec(4)
     inp4 = synth.make(4)
     q4, k4, v4 = (inp4[x].cuda() for x in ("q", "k", "v"))
@@ -772,7 +772,7 @@ def measure_dropout(steps: int, warmup: int) -> dict:
                                               p_drop=0.1), steps, warmup)
     f4 = work(4)["flops"] / (t4["kernel_ms_mean"] * 1e-3) / 1e12
     b4 = bwd_flops(4) / (tb4["kernel_ms_mean"] * 1e-3) / 1e12
-    log(f"[bench] dropout p=0.1: {describe(4)} | forward (two passes) {t4['kernel_ms_mean']:.4f} ms = {f4:.1f} TFLOP/s"
+    log(f"[bench] dropout p=0.1: {describe(4)} | forward {t4['kernel_ms_mean']:.4f} ms = {f4:.1f} TFLOP/s"
         f" | backward {tb4['kernel_ms_mean']:.4f} ms = {b4:.1f} TFLOP/s")
     return {"row": "attention dropout, keep mask shared by forward and backward", "workload": describe(2) + ", p=0.1",
             "path": "dense_dropout_bf16", "value": round(fl / (t["ms_per_step"] * 1e-3) / 1e12, 3),
@@ -780,7 +780,7 @@ def measure_dropout(steps: int, warmup: int) -> dict:
             "backward": {"path": "dense_bwd_bf16_d128 (dropout)", "kernel_ms": round(tb["kernel_ms_mean"], 5),
                          "tflops": round(bach, 2)},
             "mqa512": {"workload": describe(4) + ", p=0.1",
-                       "forward": {"path": "dense_bf16_d512 + dropout pass", "kernel_ms": round(t4["kernel_ms_mean"], 5),
+                       "forward": {"path": "dense_bf16_d512_dropout", "kernel_ms": round(t4["kernel_ms_mean"], 5),
                                    "tflops": round(f4, 2)},
                        "backward": {"path": "dense_bwd_bf16_d512 (dropout)", "kernel_ms": round(tb4["kernel_ms_mean"], 5),
                                     "tflops": round(b4, 2)}}}

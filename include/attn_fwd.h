@@ -126,11 +126,12 @@ typedef enum attn_dtype {
  *        attn_bwd_dense, so the two directions cannot disagree on it (the
  *        TransformerEngine pull request 3259 review flags a backward that
  *        lost the forward's dropout state). bf16 with head dims (64,64),
- *        (128,128), (192,128), (256,256), (512,512); runs a separate,
- *        unfused-grade kernel (dispatch path "dense_dropout_bf16"; for
- *        (512,512) after the plain forward, whose lse it reads and whose
- *        output it overwrites); the split-KV, packed, plan and extra-return
- *        calls return ATTN_UNSUPPORTED for it.
+ *        (128,128), (192,128), (256,256), (512,512). Heads up to 256 wide
+ *        run a separate, unfused-grade kernel (dispatch path
+ *        "dense_dropout_bf16"); (512,512) applies the mask inside the fused
+ *        kernel (path "dense_bf16_d512_dropout"). The split-KV, packed and
+ *        extra-return calls return ATTN_UNSUPPORTED for it, and so does
+ *        attn_plan_dense where the separate kernel would run.
  */
 typedef struct attn_dense_args {
   uint32_t struct_size; /* = sizeof(attn_dense_args) */

@@ -140,10 +140,13 @@ def test_oversized_grids_rejected_before_narrowing():
     # 2^16 heads x 2^26 tokens: 2^34 row tiles of one group, past a 32-bit count
     assert plan(args(1 << 16, 1 << 26, 128)) == A.ATTN_INVALID_ARGUMENT
     assert b"too large" in lib.attn_last_error()
-    # 512-wide: 3 * 2^29 tiles of 128 rows fit, the dropout's 64-row tiles do not
-    assert plan(args(1 << 16, 3 << 20, 512)) == A.ATTN_OK
-    assert plan(args(1 << 16, 3 << 20, 512, keep=True)) == A.ATTN_INVALID_ARGUMENT
+    # 128-wide: 3 * 2^29 tiles of 256 rows fit, the separate dropout kernel's
+    # 128-row tiles do not
+    assert plan(args(1 << 16, 3 << 21, 128)) == A.ATTN_OK
+    assert plan(args(1 << 16, 3 << 21, 128, keep=True)) == A.ATTN_INVALID_ARGUMENT
     assert b"too large" in lib.attn_last_error()
+    # 512-wide heads take the mask inside the fused kernel, on its own tiles
+    assert plan(args(1 << 16, 3 << 20, 512, keep=True)) == A.ATTN_OK
 
 
 def test_sparse_validation_errors():

@@ -52,7 +52,12 @@ def test_dropout_forward(case):
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     sk = inp["sinks"].cuda() if inp["sinks"] is not None else None
     scale = 1 / math.sqrt(dqk)
+    A.reset_dispatch_counts()
     out, lse = A.dense(q, k, v, causal=causal, scale=scale, sinks=sk, window=window, keep=kw, p_drop=P_DROP)
+    if dqk == 512:  # the mask is applied inside the fused 512-wide kernel, in one launch
+        assert A.dispatch_count("dense_bf16_d512_dropout") == 1 and A.dispatch_count("dense_dropout_bf16") == 0
+    else:
+        assert A.dispatch_count("dense_dropout_bf16") == 1
     plain, _ = A.dense(q, k, v, causal=causal, scale=scale, sinks=sk, window=window)
     torch.cuda.synchronize()
     ro, rl = oracle.dense_attention(inp["q"], inp["k"], inp["v"], scale=scale, causal=causal, sinks=inp["sinks"],
