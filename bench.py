@@ -761,8 +761,11 @@ def measure_dropout(steps: int, warmup: int) -> dict:
     kw4 = synth.pack_keep(synth.make_keep(s4.B, s4.H, s4.Tq, s4.Tk, 0.1, seed=4)).cuda()
     out4 = torch.empty((s4.B, s4.H, s4.Tq, s4.d_v), dtype=torch.bfloat16, device="cuda")
     lse4 = torch.empty((s4.B, s4.H, s4.Tq), dtype=torch.float32, device="cuda")
+    A.reset_dispatch_counts()
     t4 = time_steps(lambda: A.dense(q4, k4, v4, causal=True, scale=s4.scale, sinks=sk4, out=out4, lse=lse4, keep=kw4,
                                     p_drop=0.1), steps, warmup)
+    if A.dispatch_count("dense_bf16_d512_dropout") != t4["calls"]:
+        raise RuntimeError("NotEngaged: the fused 512-wide dropout forward did not run once per step")
     dout4 = synth.make_dout(s4).cuda()
     dq4, dk4, dv4, dsk4 = torch.empty_like(q4), torch.empty_like(k4), torch.empty_like(v4), torch.empty_like(sk4)
     ws4 = torch.empty(max(16, A.bwd_workspace_bytes(s4.B, s4.H, s4.Hkv, s4.Tq, s4.Tk, s4.d_qk, s4.d_v)),
