@@ -149,6 +149,43 @@ def test_oversized_grids_rejected_before_narrowing():
     assert plan(args(1 << 16, 3 << 20, 512, keep=True)) == A.ATTN_OK
 
 
+def test_dropout_plans():
+    """A keep mask with 512-wide heads plans the fused kernel's dropout instance (the
+    mask applied inside, on the plain kernel's tiles); narrower heads run the separate
+    dropout kernel, which plans do not describe."""
+    lib = A.load_library()
+
+    def args(d, keep):
+        a = A.AttnDenseArgs()
+        a.struct_size = ctypes.sizeof(A.AttnDenseArgs)
+        a.dtype = A.ATTN_BF16
+        a.B, a.H, a.Hkv, a.Tq, a.Tk, a.d_qk, a.d_v = 1, 64, 1, 1400, 1400, d, d
+        a.scale, a.causal = 0.05, 1
+        a.q = a.k = a.v = a.out = a.lse = 4096
+        a.q_sb, a.q_sh, a.q_st = 64 * 1400 * d, 1400 * d, d
+        a.k_sb, a.k_sh, a.k_st = 1400 * d, 1400 * d, d
+        a.v_sb, a.v_sh, a.v_st = 1400 * d, 1400 * d, d
+        a.o_sb, a.o_sh, a.o_st = 64 * 1400 * d, 1400 * d, d
+        if keep:
+            a.keep, a.p_drop = 4096, 0.1
+            a.m_sb, a.m_sh, a.m_st = 64 * 1400 * 44, 1400 * 44, 44
+        return a
+
+    def plan(a):
+        p = A.AttnPlan()
+        p.struct_size = ctypes.sizeof(A.AttnPlan)
+        st = lib.attn_plan_dense(ctypes.byref(a), ctypes.byref(p))
+        return st, p
+
+    st, plain = plan(args(512, False))
+    assert st == A.ATTN_OK and plain.path == b"dense_bf16_d512"
+    st, drop = plan(args(512, True))
+    assert st == A.ATTN_OK and drop.path == b"dense_bf16_d512_dropout"
+    assert (drop.block_rows, drop.grid, drop.waves) == (plain.block_rows, plain.grid, plain.waves)
+    st, _ = plan(args(128, True))
+    assert st == A.ATTN_UNSUPPORTED and b"separate kernel" in lib.attn_last_error()
+
+
 def test_sparse_validation_errors():
     with pytest.raises(A.AttnInvalidArgument):
         A.plan_sparse_topk(4, 64, 100, 512, 513, 16)           # d_v > d_qk
